@@ -1,0 +1,220 @@
+"""CPU oracle for tree-indexed sparse attention decode (fp64 numpy).
+
+TEST INFRASTRUCTURE ONLY. This module is the slow, plain reference the GPU
+path is checked against. Only the test suite, the smoke check and the CPU
+baseline leg of the benchmark may import it; the product path never does, and
+it shares no code with the HIP library or its Python binding.
+
+What is computed, and where it comes from
+-----------------------------------------
+"Subquadratic Attention with a Hierarchical Tree-Structured Indexer" (ZHA),
+Abstract: a tree of recursively compressed key summaries is built over the KV
+cache; future queries traverse it from the top down to retrieve a sparse
+subset of keys; the cost counted is routing plus the final attention over that
+subset.  "Vdev-Ctrl Releases ALHR", Technical Breakthrough and Core Features:
+the tree is static and keys/values are routed hierarchically.  Progressive
+Sparse Attention related-papers page (the NSA / InfLLMv2 abstract): blocks are
+chosen by coarse scores and fine softmax attention runs on the selected tokens.
+
+Readings taken where the pages are silent (each is listed with its reason in
+the design notes of the repository):
+  * summary of a node = arithmetic mean of the keys under it, computed exactly
+    and rounded once to float32 (the stored summary);
+  * levels = branchings below the root; leaves = branching**levels contiguous
+    blocks of leaf_block keys; the root is implicit and never scored;
+  * node score = plain dot product q . summary (fp64, no scale);
+  * beam = global top-`beam` over all children of all kept nodes at a level,
+    ordered by (score descending, node index ascending);
+  * selection is per query head; GQA maps q head h to KV head h // (Hq/Hkv);
+  * final attention = exact softmax over the union of the selected leaf
+    blocks with scale 1/sqrt(d), no mask; output float64 here.
+
+Every function below is written from those definitions, not from any listing.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+__all__ = ["widen", "tree_build", "tree_route", "tree_attend", "decode"]
+
+
+# ---------------------------------------------------------------------------
+# exact widening of the stored inputs
+# ---------------------------------------------------------------------------
+
+def widen(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact conversion of stored inputs to float64.
+
+    dtype "f32": float32 values; "bf16": uint16 arrays of bf16 bit patterns
+    (the bf16 value is the float32 whose high half is the pattern)."""
+    if dtype == "f32":
+        return np.asarray(x, dtype=np.float32).astype(np.float64)
+    if dtype == "bf16":
+        hi = np.asarray(x, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+        return hi.view(np.float32).astype(np.float64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def _check_geometry(n_keys: int, branching: int, leaf_block: int, levels: int) -> None:
+    if branching < 2 or leaf_block < 1 or levels < 1:
+        raise ValueError("need branching >= 2, leaf_block >= 1, levels >= 1")
+    if n_keys != branching ** levels * leaf_block:
+        raise ValueError("n_keys must equal branching**levels * leaf_block")
+
+
+# ---------------------------------------------------------------------------
+# build: node summary = mean of the keys under the node
+# ---------------------------------------------------------------------------
+
+def tree_build(K: np.ndarray, dtype: str, branching: int, leaf_block: int,
+               levels: int) -> Dict[str, List[np.ndarray]]:
+    """Summaries of every node at levels 1..levels (ZHA Abstract: recursively
+    compressed key summaries over the KV cache).
+
+    K: [B, Hkv, N, d] stored keys. Level l has n_l = branching**l nodes; node
+    n of level l covers the M_l = N / n_l contiguous keys [n*M_l, (n+1)*M_l).
+    Its summary is the mean of those keys. Because all children of a node are
+    equal-sized, this equals the recursive mean of child means.
+
+    Returns {"mean": [fp64 [B,Hkv,n_l,d] for l=1..levels],
+             "stored": [the same rounded once to float32]}.
+    """
+    B, H, N, d = K.shape
+    _check_geometry(N, branching, leaf_block, levels)
+    means = [np.empty((B, H, branching ** l, d), dtype=np.float64)
+             for l in range(1, levels + 1)]
+    for bi in range(B):
+        for h in range(H):
+            k64 = widen(K[bi, h], dtype)                      # [N, d]
+            for l in range(1, levels + 1):
+                n_l = branching ** l
+                M_l = N // n_l
+                node_sums = k64.reshape(n_l, M_l, d).sum(axis=1)
+                means[l - 1][bi, h] = node_sums / M_l
+            del k64
+    stored = [m.astype(np.float32) for m in means]
+    return {"mean": means, "stored": stored}
+
+
+# ---------------------------------------------------------------------------
+# route: top-down beam traversal
+# ---------------------------------------------------------------------------
+
+def tree_route(Q: np.ndarray, dtype: str, stored: Sequence[np.ndarray],
+               branching: int, beam: int) -> Dict[str, np.ndarray]:
+    """Top-down traversal that keeps a fixed beam of nodes per level (ZHA
+    Abstract: queries traverse the tree from the top down to retrieve a sparse
+    subset of keys; ALHR post: keys are routed hierarchically).
+
+    Q: [B, Hq, d] stored queries; stored[l-1]: float32 [B, Hkv, n_l, d].
+    Level 1 candidates are the `branching` children of the implicit root; at
+    level l the candidates are all children of the nodes kept at level l-1.
+    Each candidate is scored q . summary in fp64, candidates are ordered by
+    (score desc, node index asc) and the first min(beam, #candidates) kept.
+
+    Returns
+      indices : int32 [B, Hq, min(beam, n_leaves)] selected leaves, ascending
+      trace   : int32 [B, Hq, levels, beam] kept nodes per level, ascending,
+                padded with -1
+      gap     : fp64 [B, Hq, levels] relative score gap at the cut
+                (sigma_W - sigma_W+1) / max(|sigma_W|, |sigma_W+1|),
+                0 if both are 0, +inf where nothing was cut
+      scored  : int64 [B, Hq] number of candidate summaries scored
+    """
+    B, Hq, d = Q.shape
+    levels = len(stored)
+    Hkv = stored[0].shape[1]
+    if Hq % Hkv != 0:
+        raise ValueError("q_heads must be a multiple of kv_heads")
+    G = Hq // Hkv
+    n_leaves = branching ** levels
+    if not 1 <= beam <= n_leaves:
+        raise ValueError("beam must lie in [1, branching**levels]")
+    q64 = widen(Q, dtype)
+    W_out = min(beam, n_leaves)
+    indices = np.empty((B, Hq, W_out), dtype=np.int32)
+    trace = np.full((B, Hq, levels, beam), -1, dtype=np.int32)
+    gap = np.full((B, Hq, levels), np.inf, dtype=np.float64)
+    scored = np.zeros((B, Hq), dtype=np.int64)
+    children = np.arange(branching, dtype=np.int64)
+    for bi in range(B):
+        for hq in range(Hq):
+            hk = hq // G
+            q = q64[bi, hq]
+            kept = None
+            for l in range(1, levels + 1):
+                if kept is None:
+                    cand = children.copy()
+                else:
+                    cand = (kept[:, None] * branching + children[None, :]).ravel()
+                summ = stored[l - 1][bi, hk][cand].astype(np.float64)
+                sigma = summ @ q
+                scored[bi, hq] += len(cand)
+                order = np.lexsort((cand, -sigma))
+                n_keep = min(beam, len(cand))
+                if len(cand) > n_keep:
+                    a, c = sigma[order[n_keep - 1]], sigma[order[n_keep]]
+                    den = max(abs(a), abs(c))
+                    gap[bi, hq, l - 1] = 0.0 if den == 0.0 else (a - c) / den
+                kept = cand[order[:n_keep]]
+                trace[bi, hq, l - 1, :n_keep] = np.sort(kept)
+            indices[bi, hq] = np.sort(kept)
+    return {"indices": indices, "trace": trace, "gap": gap, "scored": scored}
+
+
+# ---------------------------------------------------------------------------
+# attend: exact softmax over the keys of the selected leaf blocks
+# ---------------------------------------------------------------------------
+
+def tree_attend(Q: np.ndarray, K: np.ndarray, V: np.ndarray, dtype: str,
+                indices: np.ndarray, leaf_block: int,
+                scale: Optional[float] = None) -> np.ndarray:
+    """Final attention restricted to the retrieved keys (ZHA Abstract: routing
+    plus final attention; NSA/InfLLMv2 abstract on the Progressive Sparse
+    Attention page: fine-grained softmax attention on the selected tokens).
+
+    The key set of a query is the union of the leaf blocks named in its row of
+    `indices` ([B, Hq, W], any order; negative entries are empty slots;
+    repeated entries count once). Scores s_t = scale * q . k_t, scale defaults
+    to 1/sqrt(d); o = sum_t softmax(s)_t v_t, in fp64. A query whose set is
+    empty gets a zero row. An entry >= N / leaf_block raises ValueError.
+    Returns fp64 [B, Hq, d].
+    """
+    B, Hq, d = Q.shape
+    _, Hkv, N, _ = K.shape
+    G = Hq // Hkv
+    n_blocks = N // leaf_block
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    q64 = widen(Q, dtype)
+    out = np.zeros((B, Hq, d), dtype=np.float64)
+    for bi in range(B):
+        for hq in range(Hq):
+            hk = hq // G
+            sel = np.asarray(indices[bi, hq], dtype=np.int64)
+            if np.any(sel >= n_blocks):
+                raise ValueError("leaf index out of range")
+            blocks = np.unique(sel[sel >= 0])
+            if blocks.size == 0:
+                continue
+            rows = (blocks[:, None] * leaf_block
+                    + np.arange(leaf_block)[None, :]).ravel()
+            k = widen(K[bi, hk, rows], dtype)
+            v = widen(V[bi, hk, rows], dtype)
+            s = scale * (k @ q64[bi, hq])
+            p = np.exp(s - s.max())
+            out[bi, hq] = (p @ v) / p.sum()
+    return out
+
+
+def decode(Q, K, V, dtype: str, branching: int, leaf_block: int, levels: int,
+           beam: int, scale: Optional[float] = None) -> Dict[str, object]:
+    """Build, route and attend in sequence (one decode step after a build)."""
+    tree = tree_build(K, dtype, branching, leaf_block, levels)
+    r = tree_route(Q, dtype, tree["stored"], branching, beam)
+    o = tree_attend(Q, K, V, dtype, r["indices"], leaf_block, scale)
+    return {"tree": tree, "route": r, "out": o}
+
