@@ -1,0 +1,200 @@
+#!/usr/bin/env python3
+"""Throughput of tree-indexed sparse attention decode on one MI355X.
+
+A step is one pass of the whole hot path over one batch: tree_build over the
+KV cache, then tree_route and tree_attend for every query head (one decode
+step).  The default workload is GQA decode in bf16 with 32,768 keys per KV
+head (batch 4, 32 query / 8 KV heads, d = 128, branching 8, leaf block 64,
+3 levels, beam 8), inputs drawn from the seeded generator and resident in
+HBM before timing starts.
+
+Prints ONE JSON line on stdout; details go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(w):
+    """Bytes the method must move (see the byte model in the design notes)."""
+    s = w.elem_bytes
+    d, b, W, L = w.head_dim, w.branching, w.beam, w.leaf_block
+    heads = w.batch * w.kv_heads
+    nodes = sum(b ** l for l in range(1, w.levels + 1))
+    build = heads * (w.n_keys * d * s + nodes * d * 4)
+    cand = b + sum(min(W, b ** (l - 1)) * b for l in range(2, w.levels + 1))
+    route_q = cand * d * 4 + d * s + 4 * W
+    attend_q = W * L * d * s * 2 + d * s + 4 * W + 4 * d
+    return {"build": build, "route": w.queries * route_q, "attend": w.queries * attend_q,
+            "candidates_per_query": cand}
+
+
+def cpu_baseline(w, x, min_seconds: float = 10.0, max_reps: int = 20):
+    """The CPU oracle, as it stands, on whole steps of the same workload."""
+    from oracle import tis_oracle as O
+    from threadpoolctl import threadpool_limits
+    reps = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while True:
+            O.decode(x["Q"], x["K"], x["V"], w.dtype, w.branching, w.leaf_block, w.levels,
+                     w.beam)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= min_seconds or reps >= max_reps:
+                break
+    return {"value": reps * w.queries / el, "unit": "queries/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} whole steps (build over all {w.batch * w.kv_heads} KV heads, "
+                      f"route + attend of all {w.queries} queries) of the same workload, "
+                      f"numpy fp64, BLAS limited to 1 thread, {el:.1f} s"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="gqa_32k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic", default=None,
+                    help="JSON file with measured HBM bytes per build launch")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); every tree is "
+              "independent per (batch, KV head), so N GPUs would each run their own share "
+              "with no exchange", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    import workloads
+    import tree_indexed_sparse_build_amd as tis
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        return 1
+    w = workloads.get(args.workload)
+    t0 = time.time()
+    x = workloads.generate(w)
+    log(f"workload {w.name}: generated in {time.time() - t0:.1f}s; {tis.version()}; "
+        f"device {torch.cuda.get_device_name(0)}")
+    dev = torch.device("cuda", 0)
+    Q = tis.from_storage(x["Q"], w.dtype, dev)
+    K = tis.from_storage(x["K"], w.dtype, dev)
+    V = tis.from_storage(x["V"], w.dtype, dev)
+    plan = tis.DecodePlan(Q, K, V, w.branching, w.leaf_block, w.levels, w.beam)
+
+    def step():
+        plan.build()
+        plan.route()
+        plan.attend()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K_ = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K_)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    start.record()
+    for i in range(K_):
+        e = ev[i]
+        e[0].record()
+        plan.build()
+        e[1].record()
+        plan.route()
+        e[2].record()
+        plan.attend()
+        e[3].record()
+    end.record()
+    h1 = time.perf_counter()
+    torch.cuda.synchronize()
+    h2 = time.perf_counter()
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / K_
+    t_build = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e-3
+    t_route = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e-3
+    t_attend = np.array([e[2].elapsed_time(e[3]) for e in ev]) * 1e-3
+
+    by = algorithmic_bytes(w)
+    build_gbs = by["build"] / t_build.mean() / 1e9
+    decode_s = (t_route + t_attend).mean()
+    idx = plan.indices.cpu().numpy()
+    uniq = 0
+    for bb in range(w.batch):
+        for h in range(w.kv_heads):
+            uniq += len(np.unique(idx[bb, h * w.group:(h + 1) * w.group]))
+    attend_dedup = uniq * w.leaf_block * w.head_dim * w.elem_bytes * 2
+    log(f"step {ms_step * 1e3:.1f} us (host enqueue {(h1 - h0) / K_ * 1e6:.1f} us/step, "
+        f"wall {(h2 - h0) / K_ * 1e6:.1f} us/step)")
+    log(f"build  {t_build.mean() * 1e6:8.2f} us  {build_gbs:8.1f} GB/s "
+        f"({build_gbs / HBM_PEAK_GBS:.1%} of 8 TB/s) on {by['build'] / 1e6:.1f} MB")
+    log(f"route  {t_route.mean() * 1e6:8.2f} us  {by['route'] / t_route.mean() / 1e9:8.1f} GB/s "
+        f"on {by['route'] / 1e6:.2f} MB ({by['candidates_per_query']} candidates/query)")
+    log(f"attend {t_attend.mean() * 1e6:8.2f} us  {by['attend'] / t_attend.mean() / 1e9:8.1f} "
+        f"GB/s on {by['attend'] / 1e6:.2f} MB per-query sum; "
+        f"{attend_dedup / t_attend.mean() / 1e9:.1f} GB/s on {attend_dedup / 1e6:.2f} MB of "
+        f"distinct blocks per KV head")
+    log(f"decode (route + attend) {decode_s * 1e6:.2f} us -> {w.queries / decode_s:.3e} queries/s")
+
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            traffic = json.load(f).get("build_bytes_per_launch")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle ...")
+        cpu = cpu_baseline(w, x)
+        log(f"cpu oracle {cpu['value']:.2f} queries/s ({cpu['sample']})")
+
+    line = {
+        "metric": "decode queries/sec + achieved HBM GB/s (% roofline) at N=32K\u20131M keys",
+        "value": w.queries / (ms_step * 1e-3),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": K_,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 inputs; fp64 build sums and route scores; fp32 attention"
+        if w.dtype == "bf16" else "f32 inputs; fp64 build sums and route scores; fp32 attention",
+        "data": "synthetic (seeded clustered-Gaussian keys, see workloads.py)",
+        "config": {"workload": w.name, "batch": w.batch, "q_heads": w.q_heads,
+                   "kv_heads": w.kv_heads, "head_dim": w.head_dim, "n_keys": w.n_keys,
+                   "branching": w.branching, "leaf_block": w.leaf_block, "levels": w.levels,
+                   "beam": w.beam, "step": "tree_build + tree_route + tree_attend"},
+        "roofline": {"kernel": "tree_build", "bound": "hbm", "achieved": build_gbs,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": build_gbs / HBM_PEAK_GBS,
+                     "traffic": traffic},
+        "decode": {"us": decode_s * 1e6, "queries_per_s": w.queries / decode_s,
+                   "route_us": t_route.mean() * 1e6, "attend_us": t_attend.mean() * 1e6,
+                   "attend_gbs_per_query_bytes": by["attend"] / t_attend.mean() / 1e9,
+                   "attend_gbs_distinct_blocks": attend_dedup / t_attend.mean() / 1e9},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,161 @@
+/*
+ * tis.h -- tree-indexed sparse attention decode on AMD Instinct MI355X (gfx950).
+ *
+ * The method (ZHA abstract, "Subquadratic Attention with a Hierarchical
+ * Tree-Structured Indexer"): build a tree of recursively compressed key
+ * summaries over the KV cache; each decode query walks it from the top down
+ * to retrieve a sparse subset of keys; final softmax attention runs over that
+ * subset only.  The tree is static and routing is hierarchical, as in the ALHR
+ * post ("Vdev-Ctrl Releases ALHR", Technical Breakthrough and Core Features).
+ *
+ * Geometry used by every call
+ *   B  batch, Hkv KV heads, Hq query heads (Hq % Hkv == 0, G = Hq / Hkv),
+ *   d  head dim (64 or 128), b branching (2..64), L leaf_block (keys per leaf),
+ *   lv levels (1..16): branchings below the implicit root, so a head has
+ *   b^lv leaves and N = b^lv * L keys.  Level l (1..lv) has n_l = b^l nodes;
+ *   node n of level l covers the M_l = N / n_l contiguous keys
+ *   [n*M_l, (n+1)*M_l).  The children of node n are n*b .. n*b+b-1.
+ *   A query head h reads KV head h / G (contiguous groups).
+ *
+ * Memory
+ *   Every data pointer is a DEVICE pointer (HBM), 16-byte aligned, owned by
+ *   the caller.  The library allocates, frees and synchronises nothing; all
+ *   work is enqueued on `stream` (a hipStream_t; NULL = the default stream).
+ *   Layouts are dense row-major:
+ *     K, V       [B][Hkv][N][d]   element type `dtype`
+ *     Q          [B][Hq][d]       element type `dtype`
+ *     summaries  float32, level-major: for l = 1..lv a block [B][Hkv][n_l][d],
+ *                block l starting at element offset d*B*Hkv*(n_1+...+n_{l-1})
+ *     indices    int32 [B][Hq][W]
+ *     O          float32 [B][Hq][d]
+ *
+ * Errors
+ *   Every argument is checked on the host before anything is enqueued; a call
+ *   that returns non-TIS_OK has written nothing.  A launch failure returns
+ *   TIS_E_HIP.  Faults inside kernels surface at the caller's next
+ *   synchronisation.  tis_last_error() gives a message for the last non-OK
+ *   status of the calling thread.  No C++ exception crosses this interface.
+ *
+ * Workspaces
+ *   tis_tree_build and tis_tree_attend take a caller-owned device workspace
+ *   whose size the *_workspace_bytes query returns.  It holds partial sums and
+ *   arrival counters.  It must be ZERO-FILLED before its first use; every call
+ *   that completes leaves the counters at zero again, so one zero-fill serves
+ *   any number of later calls.  Calls that share a workspace must be ordered
+ *   (same stream or synchronised); concurrent calls on one workspace race.
+ */
+#ifndef TIS_H_
+#define TIS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tis_status {
+  TIS_OK = 0,
+  TIS_E_NULL = 1,        /* a required pointer is NULL                        */
+  TIS_E_SHAPE = 2,       /* sizes inconsistent (e.g. N != b^lv * L)           */
+  TIS_E_DTYPE = 3,       /* unknown element type                              */
+  TIS_E_ALIGN = 4,       /* a data pointer is not 16-byte aligned            */
+  TIS_E_UNSUPPORTED = 5, /* valid but outside what is compiled (d, b, beam..)  */
+  TIS_E_WORKSPACE = 6,   /* workspace missing or smaller than required        */
+  TIS_E_HIP = 7          /* the HIP runtime reported an error                 */
+} tis_status;
+
+typedef enum tis_dtype { TIS_F32 = 0, TIS_BF16 = 1 } tis_dtype;
+
+/* Largest candidate set one level may score: beam * branching <= 256. */
+#define TIS_MAX_CANDIDATES 256
+
+/* A built tree: plain descriptor (no hidden state).  The caller sets
+ * `summaries` (device, tis_tree_summary_bytes() bytes) before
+ * tis_tree_build; the build fills in the geometry fields. */
+typedef struct tis_tree {
+  int32_t batch, kv_heads, n_keys, head_dim, branching, leaf_block, levels;
+  float *summaries;
+} tis_tree;
+
+/* Bytes of the summaries buffer: 4 * d * B * Hkv * (n_1 + ... + n_lv).
+ * Returns 0 if the geometry is invalid or the size overflows. */
+size_t tis_tree_summary_bytes(int batch, int kv_heads, int head_dim, int branching,
+                              int levels);
+
+/* Bytes of workspace tis_tree_build needs for this geometry (>= 256). */
+size_t tis_build_workspace_bytes(int batch, int kv_heads, int n_keys, int head_dim,
+                                 int branching, int leaf_block, int levels);
+
+/*
+ * tis_tree_build -- node summaries for every level (ZHA abstract: recursively
+ * compressed key summaries over the KV cache; the summary of a node is the
+ * mean of the keys under it).
+ *
+ * K        [B][Hkv][N][d] keys, dtype TIS_F32 or TIS_BF16 (read once).
+ * tree     in: tree->summaries; out: geometry fields filled in.
+ * Each summary is the exact mean of the node's keys (sums accumulated in
+ * fp64, in a fixed order), rounded once to float32.  Deterministic.
+ * Requires N == b^lv * L, lv >= 1, b >= 2, d in {64,128}.
+ */
+tis_status tis_tree_build(const void *K, tis_dtype dtype, int batch, int kv_heads,
+                          int n_keys, int head_dim, int branching, int leaf_block,
+                          int levels, tis_tree *tree, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/*
+ * tis_tree_route -- top-down beam traversal (ZHA abstract: queries traverse
+ * the tree from the top down to retrieve a sparse subset of keys).
+ *
+ * Q        [B][Hq][d], dtype TIS_F32 or TIS_BF16; tree->batch is B.
+ * For every query: the candidates of level 1 are the b children of the
+ * root; those of level l are all children of the nodes kept at level l-1.
+ * A candidate's score is q . summary, computed in fp64 from the stored fp32
+ * summary.  The kept set is the first min(beam, #candidates) candidates in
+ * (score descending, node index ascending) order.
+ * indices  out: int32 [B][Hq][beam], the kept leaves in ascending order.
+ * trace    optional (NULL to skip): int32 [B][Hq][lv][beam], the kept nodes
+ *          of every level in ascending order, padded with -1.
+ * Requires 1 <= beam <= b^lv and beam * b <= TIS_MAX_CANDIDATES.
+ */
+tis_status tis_tree_route(const void *Q, tis_dtype dtype, int q_heads,
+                          const tis_tree *tree, int beam, int32_t *indices,
+                          int32_t *trace, void *stream);
+
+/* Bytes of workspace tis_tree_attend needs for this geometry (>= 256). */
+size_t tis_attend_workspace_bytes(int batch, int q_heads, int head_dim, int beam,
+                                  int leaf_block);
+
+/*
+ * tis_tree_attend -- exact softmax attention over the keys of the selected
+ * leaf blocks (ZHA abstract: the final attention after routing; the NSA /
+ * InfLLMv2 abstract on the Progressive Sparse Attention related-papers page:
+ * fine-grained softmax attention on the selected tokens).
+ *
+ * Q [B][Hq][d], K and V [B][Hkv][N][d], all of type `dtype`.
+ * indices  int32 [B][Hq][beam] leaf-block numbers, any order.  A negative
+ *          entry is an empty slot; a repeated entry counts once; an entry
+ *          >= N / L makes that query's output row NaN (never read out of
+ *          bounds).  A query whose set is empty gets a zero row.
+ * scale    softmax scale; <= 0 selects 1/sqrt(d).
+ * O        out: float32 [B][Hq][d], o = sum_t softmax(scale*q.k_t) v_t over
+ *          the union of the selected blocks; fp32 accumulation.
+ * Requires N % L == 0 and 1 <= beam <= TIS_MAX_CANDIDATES.
+ */
+tis_status tis_tree_attend(const void *Q, const void *K, const void *V, tis_dtype dtype,
+                           int batch, int q_heads, int kv_heads, int n_keys,
+                           int head_dim, int leaf_block, const int32_t *indices,
+                           int beam, float scale, float *O, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+/* Message for the last non-OK status returned on the calling thread. */
+const char *tis_last_error(void);
+
+/* Library version string, e.g. "tis 0.1.0 gfx950". */
+const char *tis_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TIS_H_ */

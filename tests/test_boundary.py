@@ -1,0 +1,151 @@
+"""The C-ABI library: it loads, exports every entry point include/tis.h
+declares, and its host-side checks reject bad arguments before anything is
+enqueued.  No compute call is made: every call below fails a check first,
+and the pointers passed are never dereferenced."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from tree_indexed_sparse_build_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tis.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tis_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert {"tis_tree_build", "tis_tree_route", "tis_tree_attend"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.SIGNATURES), "binding and header disagree"
+
+
+def test_version(lib):
+    assert lib.tis_version().decode().startswith("tis ")
+
+
+def test_summary_bytes(lib):
+    # 4 * d * B * Hkv * (8 + 64 + 512) for the 32K-key GQA workload
+    assert lib.tis_tree_summary_bytes(4, 8, 128, 8, 3) == 4 * 128 * 32 * 584
+    assert lib.tis_tree_summary_bytes(1, 1, 64, 2, 6) == 4 * 64 * 126
+    assert lib.tis_tree_summary_bytes(1, 1, 64, 1, 6) == 0
+    assert lib.tis_tree_summary_bytes(1, 1, 64, 2, 0) == 0
+    assert lib.tis_tree_summary_bytes(1, 1, 64, 2, 17) == 0
+
+
+def test_workspace_bytes(lib):
+    assert lib.tis_build_workspace_bytes(4, 8, 32768, 128, 8, 64, 3) >= 256
+    # invalid geometry -> 0 and the last error of the thread is untouched
+    assert lib.tis_build_workspace_bytes(4, 8, 1000, 128, 8, 64, 3) == 0
+    assert lib.tis_attend_workspace_bytes(4, 32, 128, 8, 64) >= 4 * 32 * 8 * 132 * 4
+    assert lib.tis_attend_workspace_bytes(0, 32, 128, 8, 64) == 0
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: each call fails a check first
+
+
+def _tree(summ=FAKE, b=2, L=16, lv=3, d=64, B=1, H=1):
+    return _lib.TisTree(B, H, b ** lv * L, d, b, L, lv, summ)
+
+
+def _build(lib, **kw):
+    a = dict(K=FAKE, dt=_lib.TIS_BF16, B=1, H=1, N=128, d=64, b=2, L=16, lv=3,
+             tree=_lib.TisTree(0, 0, 0, 0, 0, 0, 0, FAKE), ws=FAKE, wsb=0)
+    a.update(kw)
+    return lib.tis_tree_build(a["K"], a["dt"], a["B"], a["H"], a["N"], a["d"], a["b"], a["L"],
+                              a["lv"], ctypes.byref(a["tree"]), a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=None), _lib.TIS_E_NULL),
+    (dict(ws=None), _lib.TIS_E_NULL),
+    (dict(tree=_lib.TisTree(0, 0, 0, 0, 0, 0, 0, None)), _lib.TIS_E_NULL),
+    (dict(dt=7), _lib.TIS_E_DTYPE),
+    (dict(N=96), _lib.TIS_E_SHAPE),
+    (dict(b=1), _lib.TIS_E_SHAPE),
+    (dict(b=65, N=65 ** 3 * 16), _lib.TIS_E_UNSUPPORTED),
+    (dict(lv=0), _lib.TIS_E_SHAPE),
+    (dict(lv=17), _lib.TIS_E_UNSUPPORTED),
+    (dict(L=0), _lib.TIS_E_SHAPE),
+    (dict(d=96), _lib.TIS_E_UNSUPPORTED),
+    (dict(d=0), _lib.TIS_E_SHAPE),
+    (dict(B=0), _lib.TIS_E_SHAPE),
+    (dict(K=FAKE + 2, wsb=1 << 20), _lib.TIS_E_ALIGN),
+    (dict(ws=FAKE + 8, wsb=1 << 20), _lib.TIS_E_ALIGN),
+    (dict(wsb=255), _lib.TIS_E_WORKSPACE),
+])
+def test_build_rejects(lib, kw, status):
+    assert _build(lib, **kw) == status
+    assert lib.tis_last_error().decode()
+
+
+def test_build_rejects_overflowing_geometry(lib):
+    assert _build(lib, b=64, lv=16, N=0) == _lib.TIS_E_SHAPE
+
+
+def _route(lib, Q=FAKE, dt=_lib.TIS_F32, Hq=2, tree=None, beam=2, idx=FAKE, trace=None):
+    t = tree if tree is not None else _tree(H=1)
+    return lib.tis_tree_route(Q, dt, Hq, ctypes.byref(t), beam, idx, trace, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Q=None), _lib.TIS_E_NULL),
+    (dict(idx=None), _lib.TIS_E_NULL),
+    (dict(tree=_tree(summ=None)), _lib.TIS_E_NULL),
+    (dict(dt=3), _lib.TIS_E_DTYPE),
+    (dict(tree=_tree(H=2), Hq=3), _lib.TIS_E_SHAPE),
+    (dict(Hq=0), _lib.TIS_E_SHAPE),
+    (dict(beam=0), _lib.TIS_E_SHAPE),
+    (dict(beam=9), _lib.TIS_E_SHAPE),
+    (dict(tree=_tree(b=64, lv=2, L=1), beam=5), _lib.TIS_E_UNSUPPORTED),
+    (dict(tree=_lib.TisTree(1, 1, 100, 64, 2, 16, 3, FAKE)), _lib.TIS_E_SHAPE),
+    (dict(Q=FAKE + 4), _lib.TIS_E_ALIGN),
+    (dict(idx=FAKE + 2), _lib.TIS_E_ALIGN),
+    (dict(trace=FAKE + 1), _lib.TIS_E_ALIGN),
+])
+def test_route_rejects(lib, kw, status):
+    assert _route(lib, **kw) == status
+    assert lib.tis_last_error().decode()
+
+
+def _attend(lib, **kw):
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, dt=_lib.TIS_BF16, B=1, Hq=4, Hkv=2, N=256, d=128, L=16,
+             idx=FAKE, beam=4, scale=0.0, O=FAKE, ws=FAKE, wsb=0)
+    a.update(kw)
+    return lib.tis_tree_attend(a["Q"], a["K"], a["V"], a["dt"], a["B"], a["Hq"], a["Hkv"], a["N"],
+                               a["d"], a["L"], a["idx"], a["beam"], a["scale"], a["O"], a["ws"],
+                               a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(V=None), _lib.TIS_E_NULL),
+    (dict(O=None), _lib.TIS_E_NULL),
+    (dict(dt=-1), _lib.TIS_E_DTYPE),
+    (dict(Hq=3), _lib.TIS_E_SHAPE),
+    (dict(N=250), _lib.TIS_E_SHAPE),
+    (dict(L=0), _lib.TIS_E_SHAPE),
+    (dict(beam=0), _lib.TIS_E_SHAPE),
+    (dict(beam=257), _lib.TIS_E_UNSUPPORTED),
+    (dict(d=32), _lib.TIS_E_UNSUPPORTED),
+    (dict(scale=float("nan")), _lib.TIS_E_SHAPE),
+    (dict(scale=float("inf")), _lib.TIS_E_SHAPE),
+    (dict(K=FAKE + 8, wsb=1 << 20), _lib.TIS_E_ALIGN),
+    (dict(O=FAKE + 4, wsb=1 << 20), _lib.TIS_E_ALIGN),
+    (dict(wsb=100), _lib.TIS_E_WORKSPACE),
+])
+def test_attend_rejects(lib, kw, status):
+    assert _attend(lib, **kw) == status
+    assert lib.tis_last_error().decode()

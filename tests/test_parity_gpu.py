@@ -1,0 +1,228 @@
+"""Parity of the HIP path (through the C-ABI) with the CPU oracle.
+
+Every case draws seeded inputs from `workloads`, runs tree_build, tree_route
+(with trace) and tree_attend on the GPU, and compares with the oracle under
+the rules in tests/parity.py.  Reduced cases keep each workload's generator,
+branching, leaf block, beam and head grouping at fewer levels / heads; the
+full-size cases run the five page-shaped workloads at their real sizes in
+the launch configuration the benchmark times.
+"""
+from __future__ import annotations
+
+import math
+import sys
+import time
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import tis_oracle as O
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _say(*a):
+    print("[parity]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def tis():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import tree_indexed_sparse_build_amd as t
+    t.version()  # raises if libtis.so is missing
+    return t
+
+
+def run_gpu(t, w, x, oracle_idx=None):
+    dev = "cuda"
+    K = t.from_storage(x["K"], w.dtype, dev)
+    V = t.from_storage(x["V"], w.dtype, dev)
+    Q = t.from_storage(x["Q"], w.dtype, dev)
+    tree = t.tree_build(K, w.branching, w.leaf_block, w.levels)
+    idx, tr = t.tree_route(Q, tree, w.beam, trace=True)
+    out = t.tree_attend(Q, K, V, idx, w.leaf_block)
+    res = {"tree": tree, "idx": idx, "trace": tr, "out": out}
+    if oracle_idx is not None:
+        oi = torch.from_numpy(np.ascontiguousarray(oracle_idx, dtype=np.int32)).to(dev)
+        res["out_oracle_idx"] = t.tree_attend(Q, K, V, oi, w.leaf_block)
+    torch.cuda.synchronize()
+    res["levels"] = [tree.level(l).cpu().numpy() for l in range(1, w.levels + 1)]
+    for k in ("idx", "trace", "out", "out_oracle_idx"):
+        if k in res:
+            res[k] = res[k].cpu().numpy()
+    return res
+
+
+def check_case(t, w, x=None, label=""):
+    t0 = time.time()
+    if x is None:
+        x = workloads.generate(w)
+    _say(f"{label or w.name}: generated in {time.time() - t0:.1f}s "
+         f"(B={w.batch} Hq={w.q_heads} Hkv={w.kv_heads} d={w.head_dim} N={w.n_keys} "
+         f"b={w.branching} L={w.leaf_block} lv={w.levels} W={w.beam} {w.dtype})")
+    ob = O.tree_build(x["K"], w.dtype, w.branching, w.leaf_block, w.levels)
+    orr = O.tree_route(x["Q"], w.dtype, ob["stored"], w.branching, w.beam)
+    _say(f"{label or w.name}: oracle build+route done at {time.time() - t0:.1f}s")
+    g = run_gpu(t, w, x, oracle_idx=orr["indices"])
+    eq, tot, worst = parity.compare_summaries(g["levels"], ob["stored"])
+    exact, tie, nq = parity.compare_indices(g["idx"], orr)
+    parity.compare_trace(g["trace"], orr)
+    o_or = O.tree_attend(x["Q"], x["K"], x["V"], w.dtype, orr["indices"], w.leaf_block)
+    err1 = parity.compare_outputs(g["out_oracle_idx"], o_or, w.dtype)
+    # every query's output is also checked on the leaves the GPU chose
+    o_g = O.tree_attend(x["Q"], x["K"], x["V"], w.dtype, g["idx"], w.leaf_block)
+    err2 = parity.compare_outputs(g["out"], o_g, w.dtype)
+    _say(f"{label or w.name}: summaries bit-equal {eq}/{tot} (worst {worst} ulp); "
+         f"indices exact {exact}/{nq}, tie-exposed mismatches {tie}; "
+         f"attend max-abs {err1:.2e} (oracle idx) {err2:.2e} (gpu idx); "
+         f"min cut gap {float(np.min(orr['gap'])):.2e}; {time.time() - t0:.1f}s")
+    return x, ob, orr, g
+
+
+# ---------------------------------------------------------------- reduced --
+REDUCED = [
+    ("alhr_1k", None, None),          # the full 1,024-key case is already small
+    ("gqa_32k", 2, 2),
+    ("gqa_256k", 2, 2),
+    ("long_1m", 3, 1),
+    ("deep_planted", 4, 2),
+]
+
+
+@pytest.mark.parametrize("name,levels,kvh", REDUCED, ids=[r[0] for r in REDUCED])
+def test_reduced_workload(tis, name, levels, kvh):
+    w = workloads.get(name) if levels is None else workloads.small(name, levels=levels,
+                                                                   kv_heads=kvh)
+    check_case(tis, w)
+
+
+def _custom(name, dtype, b, L, lv, W, d=128, B=1, Hkv=2, G=3, gen="normal", seed=11):
+    return workloads.Workload(name, dtype, B, Hkv * G, Hkv, d, b, L, lv, W, gen, seed=seed)
+
+
+EDGE = [
+    # ragged leaf blocks against the 2/4/8 rows one wave-wide load covers
+    _custom("ragged_f32_d64", "f32", 3, 5, 3, 4, d=64),
+    _custom("ragged_bf16_d64", "bf16", 3, 5, 3, 4, d=64),
+    _custom("ragged_bf16_d128", "bf16", 3, 7, 3, 5, d=128, B=2),
+    _custom("ragged_f32_d128", "f32", 5, 3, 2, 7, d=128),
+    # one level: block top-k then softmax on the kept blocks
+    _custom("single_level", "bf16", 16, 8, 1, 5),
+    _custom("single_level_wide", "f32", 64, 4, 1, 4, d=64),
+    # widest candidate set (beam * branching = 256) and beam 1
+    _custom("cand_256", "bf16", 16, 4, 2, 16),
+    _custom("beam_1", "bf16", 4, 16, 4, 1),
+    # beam = every leaf: the final attention is dense
+    _custom("full_beam", "f32", 2, 8, 4, 16, d=64),
+    # long leaf blocks (several batches of rows per wave)
+    _custom("long_leaf", "bf16", 2, 200, 2, 2),
+    # deep binary tree whose chunks climb through the arrival counters
+    _custom("deep_binary", "bf16", 2, 4, 9, 6, d=64, Hkv=3, G=1),
+    # many heads, GQA group 8, batch 3
+    _custom("gqa8_batch3", "bf16", 4, 32, 3, 6, B=3, Hkv=2, G=8),
+]
+
+
+@pytest.mark.parametrize("w", EDGE, ids=[w.name for w in EDGE])
+def test_edge_geometry(tis, w):
+    check_case(tis, w)
+
+
+def test_full_beam_is_dense_attention(tis):
+    w = _custom("dense_check", "bf16", 4, 16, 2, 16, d=128)
+    x = workloads.generate(w)
+    g = run_gpu(tis, w, x)
+    assert np.all(g["idx"] == np.arange(16, dtype=np.int32))
+    k = O.widen(x["K"], w.dtype)
+    v = O.widen(x["V"], w.dtype)
+    q = O.widen(x["Q"], w.dtype)
+    for hq in range(w.q_heads):
+        kk, vv = k[0, hq // w.group], v[0, hq // w.group]
+        s = kk @ q[0, hq] / math.sqrt(w.head_dim)
+        p = np.exp(s - s.max())
+        want = p @ vv / p.sum()
+        assert np.max(np.abs(g["out"][0, hq] - want)) <= parity.ATTEND_TOL["bf16"]
+
+
+def test_attend_slot_rules(tis):
+    """Duplicates count once, negative slots are empty, an all-empty row is
+    zero, an out-of-range block makes the row NaN (and nothing else)."""
+    w = _custom("slots", "bf16", 4, 16, 2, 4, Hkv=1, G=6)
+    x = workloads.generate(w)
+    n_blocks = w.n_keys // w.leaf_block
+    idx = np.array([[[3, 3, 7, -1],
+                     [-1, -1, -1, -1],
+                     [0, 1, 2, 15],
+                     [5, n_blocks, 1, 2],
+                     [9, -5, 9, 9],
+                     [15, 14, 13, 12]]], dtype=np.int32)
+    K = tis.from_storage(x["K"], w.dtype)
+    V = tis.from_storage(x["V"], w.dtype)
+    Q = tis.from_storage(x["Q"], w.dtype)
+    out = tis.tree_attend(Q, K, V, torch.from_numpy(idx).cuda(), w.leaf_block).cpu().numpy()
+    safe = idx.copy()
+    safe[0, 3] = -1  # the oracle refuses out-of-range blocks; compare the other rows
+    want = O.tree_attend(x["Q"], x["K"], x["V"], w.dtype, safe, w.leaf_block)
+    for r in (0, 2, 4, 5):
+        assert np.max(np.abs(out[0, r] - want[0, r])) <= parity.ATTEND_TOL["bf16"]
+    assert np.all(out[0, 1] == 0.0)
+    assert np.all(np.isnan(out[0, 3]))
+
+
+def test_deterministic(tis):
+    w = workloads.small("gqa_256k", levels=2, kv_heads=2)
+    x = workloads.generate(w)
+    a = run_gpu(tis, w, x)
+    b = run_gpu(tis, w, x)
+    for la, lb in zip(a["levels"], b["levels"]):
+        assert np.array_equal(la.view(np.uint32), lb.view(np.uint32))
+    assert np.array_equal(a["idx"], b["idx"])
+    assert np.array_equal(a["out"].view(np.uint32), b["out"].view(np.uint32))
+
+
+def test_planted_blocks_retrieved(tis):
+    w = workloads.small("deep_planted", levels=4, kv_heads=2)
+    x = workloads.generate(w)
+    g = run_gpu(tis, w, x)
+    hit = [x["planted"][0, h] in g["idx"][0, h] for h in range(w.q_heads)]
+    assert all(hit), f"planted block missed by {hit.count(False)} queries"
+
+
+def test_errors_through_binding(tis):
+    K = torch.zeros((1, 1, 96, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(tis.TisError, match="TIS_E_SHAPE"):
+        tis.tree_build(K, 2, 16, 3)  # 2^3 * 16 = 128 != 96
+    K = torch.zeros((1, 1, 128, 96), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(tis.TisError, match="TIS_E_UNSUPPORTED"):
+        tis.tree_build(K, 2, 16, 3)
+    K = torch.zeros((1, 2, 128, 64), dtype=torch.float32, device="cuda")
+    tree = tis.tree_build(K, 2, 16, 3)
+    Q = torch.zeros((1, 3, 64), dtype=torch.float32, device="cuda")
+    with pytest.raises(tis.TisError, match="TIS_E_SHAPE"):
+        tis.tree_route(Q, tree, 2)  # 3 q heads over 2 KV heads
+    Q = torch.zeros((1, 4, 64), dtype=torch.float32, device="cuda")
+    with pytest.raises(tis.TisError, match="TIS_E_SHAPE"):
+        tis.tree_route(Q, tree, 9)  # beam > 8 leaves
+    torch.cuda.synchronize()
+
+
+# -------------------------------------------------------------- full size --
+FULL = ["alhr_1k", "gqa_32k", "gqa_256k", "deep_planted", "long_1m"]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_workload(tis, name):
+    w = workloads.get(name)
+    x, ob, orr, g = check_case(tis, w, label=f"{name} (full size)")
+    if w.generator == "planted":
+        hit = np.array([[x["planted"][bb, h] in g["idx"][bb, h] for h in range(w.q_heads)]
+                        for bb in range(w.batch)])
+        _say(f"{name}: planted blocks retrieved by {int(hit.sum())}/{hit.size} queries")
+        assert hit.all()

@@ -1,0 +1,11 @@
+"""Tree-indexed sparse attention decode on AMD Instinct MI355X (gfx950).
+
+A tree of mean key summaries is built over each KV head's cache; each decode
+query walks it top-down keeping a fixed beam of nodes per level, then runs
+exact softmax attention over the keys of its selected leaf blocks
+("Subquadratic Attention with a Hierarchical Tree-Structured Indexer",
+Abstract).  The three calls run as hand-written HIP kernels in libtis.so.
+"""
+from .ops import (Tree, tree_build, tree_route, tree_attend, decode, version,  # noqa: F401
+                  from_storage, DecodePlan)
+from ._lib import TisError  # noqa: F401

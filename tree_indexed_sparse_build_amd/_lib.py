@@ -1,0 +1,82 @@
+"""ctypes view of libtis.so: the C-ABI declared in include/tis.h.
+
+Argument marshalling only.  The library must be built (see ``_build``); when
+it is missing, loading raises instead of falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtis.so")
+
+TIS_OK, TIS_E_NULL, TIS_E_SHAPE, TIS_E_DTYPE, TIS_E_ALIGN, TIS_E_UNSUPPORTED, \
+    TIS_E_WORKSPACE, TIS_E_HIP = range(8)
+TIS_F32, TIS_BF16 = 0, 1
+TIS_MAX_CANDIDATES = 256
+
+STATUS_NAMES = {
+    TIS_OK: "TIS_OK", TIS_E_NULL: "TIS_E_NULL", TIS_E_SHAPE: "TIS_E_SHAPE",
+    TIS_E_DTYPE: "TIS_E_DTYPE", TIS_E_ALIGN: "TIS_E_ALIGN",
+    TIS_E_UNSUPPORTED: "TIS_E_UNSUPPORTED", TIS_E_WORKSPACE: "TIS_E_WORKSPACE",
+    TIS_E_HIP: "TIS_E_HIP",
+}
+
+
+class TisTree(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("kv_heads", ctypes.c_int32),
+                ("n_keys", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("branching", ctypes.c_int32), ("leaf_block", ctypes.c_int32),
+                ("levels", ctypes.c_int32), ("summaries", ctypes.c_void_p)]
+
+
+class TisError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+_c_int, _c_size, _vp, _c_float = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+
+SIGNATURES = {
+    "tis_tree_summary_bytes": (_c_size, [_c_int] * 5),
+    "tis_build_workspace_bytes": (_c_size, [_c_int] * 7),
+    "tis_tree_build": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                _c_int, ctypes.POINTER(TisTree), _vp, _c_size, _vp]),
+    "tis_tree_route": (_c_int, [_vp, _c_int, _c_int, ctypes.POINTER(TisTree), _c_int, _vp, _vp,
+                                _vp]),
+    "tis_attend_workspace_bytes": (_c_size, [_c_int] * 5),
+    "tis_tree_attend": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                 _c_int, _vp, _c_int, _c_float, _vp, _vp, _c_size, _vp]),
+    "tis_last_error": (ctypes.c_char_p, []),
+    "tis_version": (ctypes.c_char_p, []),
+}
+
+_lock = threading.Lock()
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    f"libtis.so not found at {LIB_PATH}; build it with "
+                    "`python -m tree_indexed_sparse_build_amd._build`")
+            h = ctypes.CDLL(LIB_PATH)
+            for name, (res, args) in SIGNATURES.items():
+                f = getattr(h, name)
+                f.restype = res
+                f.argtypes = args
+            _lib = h
+        return _lib
+
+
+def check(status: int) -> None:
+    if status != TIS_OK:
+        msg = lib().tis_last_error().decode(errors="replace")
+        raise TisError(status, msg)

@@ -1,0 +1,175 @@
+// tree_route: top-down beam traversal ("Subquadratic Attention with a
+// Hierarchical Tree-Structured Indexer", Abstract: queries traverse the tree
+// of key summaries from the top down to retrieve a sparse subset of keys).
+//
+// One workgroup (4 waves) walks one query through every level in a single
+// launch.  Per level: gather the candidate summary rows (half a wave per
+// fp32 row of d = 128, 16-byte loads), dot them with the query in fp64,
+// rank the candidates in LDS and compact the kept set in ascending node
+// order, which is also candidate order for the next level.
+#include "tis_device.hpp"
+#include "tis_internal.hpp"
+
+namespace tis {
+namespace {
+
+constexpr int kRouteWaves = 4;
+constexpr int kRouteThreads = kRouteWaves * 64;
+static_assert(kMaxCandidates <= kRouteThreads, "one thread per candidate");
+
+// Ordered key of a candidate: the fp64 score mapped to an unsigned integer
+// whose order is the score order, with its 8 lowest bits replaced by
+// (255 - position).  Larger key = better.  Positions run in ascending node
+// order, so equal scores go to the lower node index.  Scores closer than
+// 2^-44 relative also fall to the index order; that is far inside the
+// relative cut gap of 1e-5 below which a selection counts as a tie.
+__device__ inline uint64_t score_key(double s, int pos) {
+  s = s + 0.0;  // -0 -> +0
+  uint64_t u = static_cast<uint64_t>(__double_as_longlong(s));
+  u = (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+  return (u & ~0xffull) | static_cast<uint64_t>(255 - pos);
+}
+
+template <typename T, int D> __device__ inline void load_q(const T *q, int col, double *out);
+template <> __device__ inline void load_q<float, 128>(const float *q, int col, double *out) {
+  const float4 v = *reinterpret_cast<const float4 *>(q + col);
+  out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+}
+template <> __device__ inline void load_q<float, 64>(const float *q, int col, double *out) {
+  load_q<float, 128>(q, col, out);
+}
+template <> __device__ inline void load_q<bf16_bits, 128>(const bf16_bits *q, int col, double *out) {
+  const uint2 v = *reinterpret_cast<const uint2 *>(q + col);
+  out[0] = __uint_as_float(v.x << 16);
+  out[1] = __uint_as_float(v.x & 0xffff0000u);
+  out[2] = __uint_as_float(v.y << 16);
+  out[3] = __uint_as_float(v.y & 0xffff0000u);
+}
+template <> __device__ inline void load_q<bf16_bits, 64>(const bf16_bits *q, int col, double *out) {
+  load_q<bf16_bits, 128>(q, col, out);
+}
+
+template <typename T, int D> __global__ void __launch_bounds__(kRouteThreads) k_route(RouteArgs a) {
+  constexpr int LPR = D / 4;          // lanes per fp32 summary row
+  constexpr int RPI = 64 / LPR;       // rows per wave-wide load
+  constexpr int U = 8;                // loads in flight per lane
+  constexpr int REP = LPR / U;        // lanes sharing one reduced score
+  constexpr int ROWS = U * kRouteWaves * RPI;
+  __shared__ uint64_t keys[kMaxCandidates];
+  __shared__ int rank[kMaxCandidates];
+  __shared__ int front[2][kMaxCandidates];
+  __shared__ int wcount[kRouteWaves];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int64_t qi = blockIdx.x;
+  const int64_t bi = qi / a.q_heads;
+  const int hq = static_cast<int>(qi - bi * a.q_heads);
+  const int64_t head = bi * a.kv_heads + hq / a.group;
+  const int b = a.branching;
+  const int W = a.beam;
+  const int lv = a.levels;
+  const int col = (lane % LPR) * 4;
+  const int rsub = lane / LPR;
+
+  double q[4];
+  load_q<T, D>(static_cast<const T *>(a.Q) + qi * D, col, q);
+
+  int cur = 0;
+  int nf = 1;
+  for (int l = 1; l <= lv; ++l) {
+    const int C = l == 1 ? b : nf * b;
+    const float *sl = a.summ + a.summ_off[l] + head * a.n_at[l] * D + col;
+    for (int base = 0; base < C; base += ROWS) {
+      float4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int pos = base + (u * kRouteWaves + w) * RPI + rsub;
+        if (pos < C) {
+          const int64_t node = l == 1 ? pos : static_cast<int64_t>(front[cur][pos / b]) * b + pos % b;
+          v[u] = *reinterpret_cast<const float4 *>(sl + node * D);
+        } else {
+          v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+      double part[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        // fp32 x (fp32 or bf16) products are exact in fp64
+        double s = q[0] * static_cast<double>(v[u].x);
+        s = fma(q[1], static_cast<double>(v[u].y), s);
+        s = fma(q[2], static_cast<double>(v[u].z), s);
+        s = fma(q[3], static_cast<double>(v[u].w), s);
+        part[u] = s;
+      }
+      const double s = group_transpose_reduce<U, LPR>(part, lane);
+      const int k = (lane % LPR) / REP;
+      const int pos = base + (k * kRouteWaves + w) * RPI + rsub;
+      if ((lane % REP) == 0 && pos < C) keys[pos] = score_key(s, pos);
+    }
+    if (C > W) {
+      for (int i = tid; i < C; i += kRouteThreads) rank[i] = 0;
+    }
+    __syncthreads();
+    if (C > W) {
+      // rank_i = number of candidates with a larger key; the threads left
+      // over when C < 256 split the comparison range
+      int cp = 1;
+      while (cp < C) cp <<= 1;
+      const int parts = kRouteThreads / cp;
+      const int span = (C + parts - 1) / parts;
+      const int i = tid % cp;
+      const int part = tid / cp;
+      if (i < C && part < parts) {
+        const uint64_t ki = keys[i];
+        const int j0 = part * span;
+        const int j1 = min(C, j0 + span);
+        int cnt = 0;
+        for (int j = j0; j < j1; ++j) cnt += keys[j] > ki ? 1 : 0;
+        if (cnt) atomicAdd(&rank[i], cnt);
+      }
+      __syncthreads();
+    }
+    // compact the kept candidates in position (= node) order
+    const bool keep = tid < C && (C <= W || rank[tid] < W);
+    const uint64_t mask = __ballot(keep);
+    if (lane == 0) wcount[w] = __popcll(mask);
+    __syncthreads();
+    int off = 0;
+    for (int ww = 0; ww < w; ++ww) off += wcount[ww];
+    if (keep) {
+      const int below = __popcll(mask & ((1ull << lane) - 1ull));
+      front[cur ^ 1][off + below] =
+          l == 1 ? tid : front[cur][tid / b] * b + tid % b;
+    }
+    __syncthreads();
+    cur ^= 1;
+    nf = C < W ? C : W;
+    if (a.trace) {
+      int32_t *tr = a.trace + (qi * lv + (l - 1)) * W;
+      for (int k = tid; k < W; k += kRouteThreads) tr[k] = k < nf ? front[cur][k] : -1;
+    }
+  }
+  for (int k = tid; k < W; k += kRouteThreads) a.indices[qi * W + k] = front[cur][k];
+}
+
+}  // namespace
+
+hipError_t launch_route(Dt dt, int head_dim, const RouteArgs &a, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(a.queries));
+  const dim3 block(kRouteThreads);
+  if (dt == Dt::BF16 && head_dim == 128)
+    hipLaunchKernelGGL((k_route<bf16_bits, 128>), grid, block, 0, s, a);
+  else if (dt == Dt::BF16 && head_dim == 64)
+    hipLaunchKernelGGL((k_route<bf16_bits, 64>), grid, block, 0, s, a);
+  else if (dt == Dt::F32 && head_dim == 128)
+    hipLaunchKernelGGL((k_route<float, 128>), grid, block, 0, s, a);
+  else if (dt == Dt::F32 && head_dim == 64)
+    hipLaunchKernelGGL((k_route<float, 64>), grid, block, 0, s, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace tis

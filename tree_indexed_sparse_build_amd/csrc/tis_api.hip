@@ -1,0 +1,297 @@
+// C-ABI of libtis: argument checks, launch geometry and error mapping.
+// Every check runs on the host before anything is enqueued, so a call that
+// fails a check touches neither the device nor the HIP runtime.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "tis.h"
+#include "tis_internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+tis_status fail(tis_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// b^e with overflow detection (limit: INT32 range).
+bool ipow(int64_t b, int e, int64_t *out) {
+  int64_t r = 1;
+  for (int i = 0; i < e; ++i) {
+    r *= b;
+    if (r > 0x7fffffffLL) return false;
+  }
+  *out = r;
+  return true;
+}
+
+struct Geometry {
+  int64_t n_at[tis::kMaxLevels + 1];
+  int64_t summ_off[tis::kMaxLevels + 1];
+  int64_t summ_elems;
+};
+
+// Checks the tree geometry shared by build and route and fills level sizes.
+tis_status check_tree(int batch, int kv_heads, int n_keys, int head_dim, int branching,
+                      int leaf_block, int levels, Geometry *g) {
+  if (batch < 1 || kv_heads < 1) return fail(TIS_E_SHAPE, "batch and kv_heads must be >= 1");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(head_dim < 1 ? TIS_E_SHAPE : TIS_E_UNSUPPORTED,
+                "head_dim %d: only 64 and 128 are compiled", head_dim);
+  if (branching < 2) return fail(TIS_E_SHAPE, "branching %d < 2", branching);
+  if (branching > tis::kMaxBranching)
+    return fail(TIS_E_UNSUPPORTED, "branching %d > %d", branching, tis::kMaxBranching);
+  if (levels < 1) return fail(TIS_E_SHAPE, "levels %d < 1", levels);
+  if (levels > tis::kMaxLevels)
+    return fail(TIS_E_UNSUPPORTED, "levels %d > %d", levels, tis::kMaxLevels);
+  if (leaf_block < 1) return fail(TIS_E_SHAPE, "leaf_block %d < 1", leaf_block);
+  int64_t leaves;
+  if (!ipow(branching, levels, &leaves) || leaves * leaf_block != static_cast<int64_t>(n_keys))
+    return fail(TIS_E_SHAPE, "n_keys %d != branching^levels * leaf_block (%d^%d * %d)", n_keys,
+                branching, levels, leaf_block);
+  const int64_t heads = static_cast<int64_t>(batch) * kv_heads;
+  int64_t off = 0;
+  g->n_at[0] = 1;
+  g->summ_off[0] = 0;
+  for (int l = 1; l <= levels; ++l) {
+    g->n_at[l] = g->n_at[l - 1] * branching;
+    g->summ_off[l] = off;
+    off += heads * g->n_at[l] * head_dim;
+  }
+  for (int l = levels + 1; l <= tis::kMaxLevels; ++l) g->n_at[l] = g->summ_off[l] = 0;
+  g->summ_elems = off;
+  return TIS_OK;
+}
+
+tis_status check_dtype(tis_dtype dt) {
+  if (dt != TIS_F32 && dt != TIS_BF16) return fail(TIS_E_DTYPE, "unknown dtype %d", (int)dt);
+  return TIS_OK;
+}
+
+tis_status hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return TIS_OK;
+  return fail(TIS_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t tis_tree_summary_bytes(int batch, int kv_heads, int head_dim, int branching, int levels) {
+  if (batch < 1 || kv_heads < 1 || head_dim < 1 || branching < 2 || levels < 1 ||
+      levels > tis::kMaxLevels)
+    return 0;
+  int64_t n = 1, total = 0;
+  for (int l = 1; l <= levels; ++l) {
+    n *= branching;
+    if (n > 0x7fffffffLL) return 0;
+    total += n;
+  }
+  const double bytes = 4.0 * head_dim * (double)batch * kv_heads * (double)total;
+  if (bytes > 9.0e18) return 0;
+  return static_cast<size_t>(4) * head_dim * static_cast<size_t>(batch) * kv_heads *
+         static_cast<size_t>(total);
+}
+
+size_t tis_build_workspace_bytes(int batch, int kv_heads, int n_keys, int head_dim,
+                                 int branching, int leaf_block, int levels) {
+  Geometry g;
+  char saved[sizeof g_err];
+  memcpy(saved, g_err, sizeof saved);
+  const tis_status st =
+      check_tree(batch, kv_heads, n_keys, head_dim, branching, leaf_block, levels, &g);
+  memcpy(g_err, saved, sizeof saved);
+  if (st != TIS_OK) return 0;
+  tis::BuildPlan p;
+  if (!tis::plan_build(static_cast<int64_t>(batch) * kv_heads, head_dim, branching, leaf_block,
+                       levels, &p))
+    return 0;
+  return p.workspace_bytes;
+}
+
+tis_status tis_tree_build(const void *K, tis_dtype dtype, int batch, int kv_heads, int n_keys,
+                          int head_dim, int branching, int leaf_block, int levels, tis_tree *tree,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+  if (!K || !tree || !tree->summaries || !workspace)
+    return fail(TIS_E_NULL, "tis_tree_build: K, tree, tree->summaries and workspace are required");
+  tis_status st = check_dtype(dtype);
+  if (st != TIS_OK) return st;
+  Geometry g;
+  st = check_tree(batch, kv_heads, n_keys, head_dim, branching, leaf_block, levels, &g);
+  if (st != TIS_OK) return st;
+  if (!aligned(K, 16) || !aligned(tree->summaries, 16) || !aligned(workspace, 16))
+    return fail(TIS_E_ALIGN, "tis_tree_build: K, summaries and workspace must be 16-byte aligned");
+  const int64_t heads = static_cast<int64_t>(batch) * kv_heads;
+  tis::BuildPlan p;
+  if (!tis::plan_build(heads, head_dim, branching, leaf_block, levels, &p))
+    return fail(TIS_E_UNSUPPORTED, "tis_tree_build: grid too large");
+  if (workspace_bytes < p.workspace_bytes)
+    return fail(TIS_E_WORKSPACE, "tis_tree_build: workspace %zu bytes < %zu required",
+                workspace_bytes, p.workspace_bytes);
+
+  tis::BuildArgs a{};
+  a.K = K;
+  a.summ = tree->summaries;
+  char *ws = static_cast<char *>(workspace);
+  a.ws_cnt = reinterpret_cast<int *>(ws);
+  a.ws_sum = reinterpret_cast<double *>(ws + tis::align_up(p.cnt_elems * sizeof(int), 256));
+  a.n_keys = n_keys;
+  a.chunks = p.chunks;
+  a.branching = branching;
+  a.leaf_block = leaf_block;
+  a.levels = levels;
+  a.root_level = p.root_level;
+  int64_t cnt_off = 0, sum_off = 0;
+  for (int l = 0; l <= tis::kMaxLevels; ++l) {
+    a.n_at[l] = g.n_at[l];
+    a.summ_off[l] = g.summ_off[l];
+    a.ws_off[l] = a.cnt_off[l] = 0;
+  }
+  for (int l = 1; l <= p.root_level; ++l) {
+    if (l <= p.root_level - 1) {
+      a.cnt_off[l] = cnt_off;
+      cnt_off += heads * g.n_at[l];
+    }
+    if (l >= 2) {
+      a.ws_off[l] = sum_off;
+      sum_off += heads * g.n_at[l] * head_dim;
+    }
+  }
+  const tis::Dt dt = dtype == TIS_BF16 ? tis::Dt::BF16 : tis::Dt::F32;
+  st = hip_status(tis::launch_build(dt, head_dim, heads, a, p, static_cast<hipStream_t>(stream)),
+                  "tis_tree_build launch");
+  if (st != TIS_OK) return st;
+  tree->batch = batch;
+  tree->kv_heads = kv_heads;
+  tree->n_keys = n_keys;
+  tree->head_dim = head_dim;
+  tree->branching = branching;
+  tree->leaf_block = leaf_block;
+  tree->levels = levels;
+  return TIS_OK;
+}
+
+tis_status tis_tree_route(const void *Q, tis_dtype dtype, int q_heads, const tis_tree *tree,
+                          int beam, int32_t *indices, int32_t *trace, void *stream) {
+  if (!Q || !tree || !tree->summaries || !indices)
+    return fail(TIS_E_NULL, "tis_tree_route: Q, tree, tree->summaries and indices are required");
+  tis_status st = check_dtype(dtype);
+  if (st != TIS_OK) return st;
+  Geometry g;
+  st = check_tree(tree->batch, tree->kv_heads, tree->n_keys, tree->head_dim, tree->branching,
+                  tree->leaf_block, tree->levels, &g);
+  if (st != TIS_OK) return st;
+  if (q_heads < 1 || q_heads % tree->kv_heads != 0)
+    return fail(TIS_E_SHAPE, "tis_tree_route: q_heads %d is not a positive multiple of kv_heads %d",
+                q_heads, tree->kv_heads);
+  const int64_t leaves = g.n_at[tree->levels];
+  if (beam < 1 || beam > leaves)
+    return fail(TIS_E_SHAPE, "tis_tree_route: beam %d outside [1, %lld]", beam, (long long)leaves);
+  if (static_cast<int64_t>(beam) * tree->branching > TIS_MAX_CANDIDATES)
+    return fail(TIS_E_UNSUPPORTED, "tis_tree_route: beam * branching = %lld > %d",
+                (long long)beam * tree->branching, TIS_MAX_CANDIDATES);
+  if (!aligned(Q, 16) || !aligned(tree->summaries, 16) || !aligned(indices, 4) ||
+      (trace && !aligned(trace, 4)))
+    return fail(TIS_E_ALIGN, "tis_tree_route: Q and summaries need 16-byte, indices 4-byte alignment");
+  const int64_t queries = static_cast<int64_t>(tree->batch) * q_heads;
+  if (queries > 0x7fffffffLL) return fail(TIS_E_UNSUPPORTED, "tis_tree_route: too many queries");
+
+  tis::RouteArgs a{};
+  a.Q = Q;
+  a.summ = tree->summaries;
+  a.indices = indices;
+  a.trace = trace;
+  a.queries = queries;
+  a.q_heads = q_heads;
+  a.kv_heads = tree->kv_heads;
+  a.group = q_heads / tree->kv_heads;
+  a.branching = tree->branching;
+  a.levels = tree->levels;
+  a.beam = beam;
+  for (int l = 0; l <= tis::kMaxLevels; ++l) {
+    a.n_at[l] = g.n_at[l];
+    a.summ_off[l] = g.summ_off[l];
+  }
+  const tis::Dt dt = dtype == TIS_BF16 ? tis::Dt::BF16 : tis::Dt::F32;
+  return hip_status(tis::launch_route(dt, tree->head_dim, a, static_cast<hipStream_t>(stream)),
+                    "tis_tree_route launch");
+}
+
+size_t tis_attend_workspace_bytes(int batch, int q_heads, int head_dim, int beam, int leaf_block) {
+  (void)leaf_block;
+  if (batch < 1 || q_heads < 1 || head_dim < 1 || beam < 1) return 0;
+  tis::AttendPlan p;
+  tis::plan_attend(static_cast<int64_t>(batch) * q_heads, head_dim, beam, &p);
+  return p.workspace_bytes;
+}
+
+tis_status tis_tree_attend(const void *Q, const void *K, const void *V, tis_dtype dtype, int batch,
+                           int q_heads, int kv_heads, int n_keys, int head_dim, int leaf_block,
+                           const int32_t *indices, int beam, float scale, float *O,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+  if (!Q || !K || !V || !indices || !O || !workspace)
+    return fail(TIS_E_NULL, "tis_tree_attend: Q, K, V, indices, O and workspace are required");
+  tis_status st = check_dtype(dtype);
+  if (st != TIS_OK) return st;
+  if (batch < 1 || kv_heads < 1 || q_heads < 1 || q_heads % kv_heads != 0)
+    return fail(TIS_E_SHAPE, "tis_tree_attend: need batch, kv_heads >= 1 and q_heads a multiple of kv_heads");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(head_dim < 1 ? TIS_E_SHAPE : TIS_E_UNSUPPORTED,
+                "tis_tree_attend: head_dim %d: only 64 and 128 are compiled", head_dim);
+  if (leaf_block < 1 || n_keys < 1 || n_keys % leaf_block != 0)
+    return fail(TIS_E_SHAPE, "tis_tree_attend: n_keys %d is not a positive multiple of leaf_block %d",
+                n_keys, leaf_block);
+  if (beam < 1) return fail(TIS_E_SHAPE, "tis_tree_attend: beam %d < 1", beam);
+  if (beam > TIS_MAX_CANDIDATES)
+    return fail(TIS_E_UNSUPPORTED, "tis_tree_attend: beam %d > %d", beam, TIS_MAX_CANDIDATES);
+  if (!(scale == scale) || isinf(scale))
+    return fail(TIS_E_SHAPE, "tis_tree_attend: scale must be finite");
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) ||
+      !aligned(workspace, 16) || !aligned(indices, 4))
+    return fail(TIS_E_ALIGN, "tis_tree_attend: Q, K, V, O and workspace need 16-byte alignment");
+  const int64_t queries = static_cast<int64_t>(batch) * q_heads;
+  if (queries * beam > 0x7fffffffLL) return fail(TIS_E_UNSUPPORTED, "tis_tree_attend: grid too large");
+  tis::AttendPlan p;
+  tis::plan_attend(queries, head_dim, beam, &p);
+  if (workspace_bytes < p.workspace_bytes)
+    return fail(TIS_E_WORKSPACE, "tis_tree_attend: workspace %zu bytes < %zu required",
+                workspace_bytes, p.workspace_bytes);
+
+  const double sc = scale > 0.f ? static_cast<double>(scale) : 1.0 / sqrt(static_cast<double>(head_dim));
+  tis::AttendArgs a{};
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.indices = indices;
+  a.O = O;
+  char *ws = static_cast<char *>(workspace);
+  a.cnt = reinterpret_cast<int *>(ws);
+  a.part = reinterpret_cast<float *>(ws + tis::align_up(p.cnt_elems * sizeof(int), 256));
+  a.queries = queries;
+  a.n_keys = n_keys;
+  a.q_heads = q_heads;
+  a.kv_heads = kv_heads;
+  a.group = q_heads / kv_heads;
+  a.leaf_block = leaf_block;
+  a.beam = beam;
+  a.n_blocks = n_keys / leaf_block;
+  a.scale_log2 = static_cast<float>(sc * 1.4426950408889634);
+  const tis::Dt dt = dtype == TIS_BF16 ? tis::Dt::BF16 : tis::Dt::F32;
+  return hip_status(tis::launch_attend(dt, head_dim, a, p, static_cast<hipStream_t>(stream)),
+                    "tis_tree_attend launch");
+}
+
+const char *tis_last_error(void) { return g_err; }
+
+const char *tis_version(void) { return "tis 0.1.0 gfx950"; }
+
+}  // extern "C"

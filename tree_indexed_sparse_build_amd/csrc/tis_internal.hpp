@@ -1,0 +1,98 @@
+// Internal declarations shared by the translation units of libtis.
+// Kernel argument blocks are passed by value; all offsets are in elements.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tis {
+
+constexpr int kMaxLevels = 16;
+constexpr int kMaxCandidates = 256;   // beam * branching scored per level
+constexpr int kMaxBranching = 64;
+
+enum class Dt : int { F32 = 0, BF16 = 1 };
+
+// ---------------------------------------------------------------- build --
+// Work split.  A wave reduces the b leaves of one level-(lv-1) node.  A
+// workgroup of nw = b^kg waves owns the subtree of one node at level
+// r = lv - 1 - kg (a "chunk") and finishes its inner levels in LDS.  When
+// r >= 2 the chunk root's fp64 sum goes to the workspace and the last of the
+// b sibling chunks to arrive (counted with an atomic) climbs one level, and
+// so on up to level 1, so the whole tree takes one launch.
+struct BuildArgs {
+  const void *K;
+  float *summ;
+  double *ws_sum;        // fp64 node sums of levels 2..r
+  int *ws_cnt;           // arrival counters of levels 1..r-1
+  int64_t n_keys;        // N
+  int64_t chunks;        // b^r chunks per head
+  int branching, leaf_block, levels;
+  int root_level;        // r
+  int64_t n_at[kMaxLevels + 1];     // b^l
+  int64_t summ_off[kMaxLevels + 1]; // element offset of level l in summ
+  int64_t ws_off[kMaxLevels + 1];   // element offset of level l in ws_sum
+  int64_t cnt_off[kMaxLevels + 1];  // element offset of level l in ws_cnt
+};
+
+struct BuildPlan {
+  int root_level;
+  int waves;             // nw
+  int64_t chunks;        // b^r per head
+  size_t lds_bytes;
+  size_t cnt_elems, sum_elems;
+  size_t workspace_bytes;
+};
+
+bool plan_build(int64_t heads, int head_dim, int branching, int leaf_block, int levels,
+                BuildPlan *plan);
+hipError_t launch_build(Dt dt, int head_dim, int64_t heads, const BuildArgs &a,
+                        const BuildPlan &p, hipStream_t s);
+
+// ---------------------------------------------------------------- route --
+struct RouteArgs {
+  const void *Q;
+  const float *summ;
+  int32_t *indices;
+  int32_t *trace;        // may be null
+  int64_t queries;       // B * Hq
+  int q_heads, kv_heads, group;
+  int branching, levels, beam;
+  int64_t n_at[kMaxLevels + 1];
+  int64_t summ_off[kMaxLevels + 1];
+};
+
+hipError_t launch_route(Dt dt, int head_dim, const RouteArgs &a, hipStream_t s);
+
+// --------------------------------------------------------------- attend --
+// One wave per (query, index slot): it gathers the slot's leaf block, runs
+// an online softmax over its keys and leaves (m, l, acc[d]) in the
+// workspace; the last wave of a query to arrive merges the beam's partials.
+struct AttendArgs {
+  const void *Q, *K, *V;
+  const int32_t *indices;
+  float *O;
+  float *part;           // [queries][beam][d + 4]: m, l, -, -, acc[d]
+  int *cnt;              // [queries] arrival counters
+  int64_t queries;       // B * Hq
+  int64_t n_keys;
+  int q_heads, kv_heads, group;
+  int leaf_block, beam;
+  int64_t n_blocks;      // N / L
+  float scale_log2;      // softmax scale * log2(e)
+};
+
+struct AttendPlan {
+  size_t part_elems;
+  size_t cnt_elems;
+  size_t workspace_bytes;
+};
+
+void plan_attend(int64_t queries, int head_dim, int beam, AttendPlan *p);
+hipError_t launch_attend(Dt dt, int head_dim, const AttendArgs &a, const AttendPlan &p,
+                         hipStream_t s);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace tis

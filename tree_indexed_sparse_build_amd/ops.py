@@ -1,0 +1,239 @@
+"""Python binding of the three calls: tree_build, tree_route, tree_attend.
+
+Torch supplies device memory and the stream; every step of the computation
+runs in libtis's HIP kernels.  Tensors must live on a ROCm device; float32
+and bfloat16 are the accepted element types.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+from typing import Dict, Optional, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import TisTree, check, lib
+
+_DTYPES = {torch.float32: _lib.TIS_F32, torch.bfloat16: _lib.TIS_BF16}
+
+__all__ = ["Tree", "DecodePlan", "tree_build", "tree_route", "tree_attend", "decode", "version", "from_storage",
+           "summary_offsets"]
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16") from None
+
+
+def _need_device(*ts: torch.Tensor) -> None:
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must be on a ROCm device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+# Zero-filled workspaces, one per (device, size class).  Every completed call
+# returns its counters to zero, so a workspace is reused without clearing.
+_workspaces: Dict[Tuple[int, str], torch.Tensor] = {}
+
+
+def _workspace(device: torch.device, kind: str, nbytes: int) -> torch.Tensor:
+    key = (device.index if device.index is not None else torch.cuda.current_device(), kind)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        size = max(nbytes, 256)
+        ws = torch.zeros(size, dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+@dataclasses.dataclass
+class Tree:
+    """A built tree: fp32 summaries, level-major ([B, Hkv, n_l, d] blocks for
+    l = 1..levels, concatenated), plus its geometry."""
+    summaries: torch.Tensor
+    batch: int
+    kv_heads: int
+    n_keys: int
+    head_dim: int
+    branching: int
+    leaf_block: int
+    levels: int
+
+    def c_struct(self) -> TisTree:
+        return TisTree(self.batch, self.kv_heads, self.n_keys, self.head_dim, self.branching,
+                       self.leaf_block, self.levels, self.summaries.data_ptr())
+
+    def level(self, l: int) -> torch.Tensor:
+        """Summaries of level l (1..levels) as a [B, Hkv, b**l, d] view."""
+        off = summary_offsets(self.batch, self.kv_heads, self.head_dim, self.branching,
+                              self.levels)
+        n = self.branching ** l
+        return self.summaries[off[l - 1]:off[l - 1] + self.batch * self.kv_heads * n *
+                              self.head_dim].view(self.batch, self.kv_heads, n, self.head_dim)
+
+
+def summary_offsets(batch, kv_heads, head_dim, branching, levels):
+    off, out = 0, []
+    for l in range(1, levels + 1):
+        out.append(off)
+        off += batch * kv_heads * branching ** l * head_dim
+    out.append(off)
+    return out
+
+
+def tree_build(K: torch.Tensor, branching: int, leaf_block: int, levels: int) -> Tree:
+    """Summaries of every node: K [B, Hkv, N, d] with N = branching**levels * leaf_block."""
+    _need_device(K)
+    if K.dim() != 4:
+        raise ValueError("K must be [B, Hkv, N, d]")
+    B, H, N, d = K.shape
+    L = lib()
+    nbytes = L.tis_tree_summary_bytes(B, H, d, branching, levels)
+    if nbytes == 0:
+        raise _lib.TisError(_lib.TIS_E_SHAPE, "invalid tree geometry")
+    summ = torch.empty(nbytes // 4, dtype=torch.float32, device=K.device)
+    wsb = L.tis_build_workspace_bytes(B, H, N, d, branching, leaf_block, levels)
+    ws = _workspace(K.device, "build", wsb)
+    t = TisTree(0, 0, 0, 0, 0, 0, 0, summ.data_ptr())
+    check(L.tis_tree_build(K.data_ptr(), _dtype_code(K), B, H, N, d, branching, leaf_block,
+                           levels, ctypes.byref(t), ws.data_ptr(), ws.numel(),
+                           _stream(K.device)))
+    return Tree(summ, t.batch, t.kv_heads, t.n_keys, t.head_dim, t.branching, t.leaf_block,
+                t.levels)
+
+
+def tree_route(Q: torch.Tensor, tree: Tree, beam: int, trace: bool = False):
+    """Leaf blocks each query keeps: int32 [B, Hq, beam], ascending.  With
+    trace=True also returns the kept nodes of every level, int32
+    [B, Hq, levels, beam] padded with -1."""
+    _need_device(Q, tree.summaries)
+    if Q.dim() != 3:
+        raise ValueError("Q must be [B, Hq, d]")
+    B, Hq, d = Q.shape
+    if B != tree.batch or d != tree.head_dim:
+        raise ValueError("Q does not match the tree's batch / head_dim")
+    idx = torch.empty((B, Hq, beam), dtype=torch.int32, device=Q.device)
+    tr = (torch.empty((B, Hq, tree.levels, beam), dtype=torch.int32, device=Q.device)
+          if trace else None)
+    t = tree.c_struct()
+    check(lib().tis_tree_route(Q.data_ptr(), _dtype_code(Q), Hq, ctypes.byref(t), beam,
+                               idx.data_ptr(), tr.data_ptr() if tr is not None else None,
+                               _stream(Q.device)))
+    return (idx, tr) if trace else idx
+
+
+def tree_attend(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, indices: torch.Tensor,
+                leaf_block: int, scale: Optional[float] = None) -> torch.Tensor:
+    """Softmax attention of each query over the keys of its selected leaf
+    blocks.  Q [B, Hq, d]; K, V [B, Hkv, N, d]; indices int32 [B, Hq, W].
+    Returns float32 [B, Hq, d]."""
+    _need_device(Q, K, V, indices)
+    if indices.dtype != torch.int32:
+        raise TypeError("indices must be int32")
+    if K.dtype != Q.dtype or V.dtype != Q.dtype:
+        raise TypeError("Q, K and V must share one dtype")
+    B, Hq, d = Q.shape
+    _, Hkv, N, _ = K.shape
+    if tuple(V.shape) != tuple(K.shape) or K.shape[0] != B or K.shape[3] != d:
+        raise ValueError("shape mismatch between Q, K and V")
+    if indices.dim() != 3 or indices.shape[0] != B or indices.shape[1] != Hq:
+        raise ValueError("indices must be [B, Hq, W]")
+    W = indices.shape[2]
+    O = torch.empty((B, Hq, d), dtype=torch.float32, device=Q.device)
+    L = lib()
+    wsb = L.tis_attend_workspace_bytes(B, Hq, d, W, leaf_block)
+    ws = _workspace(Q.device, "attend", wsb)
+    check(L.tis_tree_attend(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q), B, Hq,
+                            Hkv, N, d, leaf_block, indices.data_ptr(), W,
+                            0.0 if scale is None else float(scale), O.data_ptr(),
+                            ws.data_ptr(), ws.numel(), _stream(Q.device)))
+    return O
+
+
+def decode(Q, K, V, branching: int, leaf_block: int, levels: int, beam: int,
+           scale: Optional[float] = None):
+    """Build, route and attend on the current stream (no host sync between)."""
+    tree = tree_build(K, branching, leaf_block, levels)
+    idx = tree_route(Q, tree, beam)
+    return tree, idx, tree_attend(Q, K, V, idx, leaf_block, scale)
+
+
+def version() -> str:
+    return lib().tis_version().decode()
+
+
+def from_storage(arr, dtype: str, device="cuda") -> torch.Tensor:
+    """Device tensor from a host storage array: float32 values ("f32") or
+    uint16 bf16 bit patterns ("bf16"), bits unchanged."""
+    import numpy as np
+    if dtype == "f32":
+        t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32))
+    elif dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.uint16).view(np.int16)).view(
+            torch.bfloat16)
+    else:
+        raise ValueError(f"unknown storage dtype {dtype!r}")
+    return t.to(device)
+
+
+class DecodePlan:
+    """Pre-allocated buffers and C-ABI arguments for repeated build / route /
+    attend over fixed device tensors, so a call costs one C-ABI call and no
+    allocation (used by timing loops)."""
+
+    def __init__(self, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, branching: int,
+                 leaf_block: int, levels: int, beam: int, scale: Optional[float] = None):
+        _need_device(Q, K, V)
+        L = lib()
+        self._lib = L
+        B, H, N, d = K.shape
+        Hq = Q.shape[1]
+        self.Q, self.K, self.V = Q, K, V
+        self.dt = _dtype_code(K)
+        self.geom = (B, H, N, d, branching, leaf_block, levels)
+        self.q_heads, self.beam, self.scale = Hq, beam, 0.0 if scale is None else float(scale)
+        nbytes = L.tis_tree_summary_bytes(B, H, d, branching, levels)
+        if nbytes == 0:
+            raise _lib.TisError(_lib.TIS_E_SHAPE, "invalid tree geometry")
+        self.summaries = torch.empty(nbytes // 4, dtype=torch.float32, device=K.device)
+        self.ws_build = torch.zeros(max(256, L.tis_build_workspace_bytes(*self.geom)),
+                                    dtype=torch.uint8, device=K.device)
+        self.ws_attend = torch.zeros(max(256, L.tis_attend_workspace_bytes(B, Hq, d, beam,
+                                                                           leaf_block)),
+                                     dtype=torch.uint8, device=K.device)
+        self.indices = torch.empty((B, Hq, beam), dtype=torch.int32, device=K.device)
+        self.out = torch.empty((B, Hq, d), dtype=torch.float32, device=K.device)
+        self.tree_c = TisTree(0, 0, 0, 0, 0, 0, 0, self.summaries.data_ptr())
+        self.stream = _stream(K.device)
+
+    def build(self) -> None:
+        B, H, N, d, b, Lb, lv = self.geom
+        check(self._lib.tis_tree_build(self.K.data_ptr(), self.dt, B, H, N, d, b, Lb, lv,
+                                       ctypes.byref(self.tree_c), self.ws_build.data_ptr(),
+                                       self.ws_build.numel(), self.stream))
+
+    def route(self) -> None:
+        check(self._lib.tis_tree_route(self.Q.data_ptr(), self.dt, self.q_heads,
+                                       ctypes.byref(self.tree_c), self.beam,
+                                       self.indices.data_ptr(), None, self.stream))
+
+    def attend(self) -> None:
+        B, H, N, d, b, Lb, lv = self.geom
+        check(self._lib.tis_tree_attend(self.Q.data_ptr(), self.K.data_ptr(), self.V.data_ptr(),
+                                        self.dt, B, self.q_heads, H, N, d, Lb,
+                                        self.indices.data_ptr(), self.beam, self.scale,
+                                        self.out.data_ptr(), self.ws_attend.data_ptr(),
+                                        self.ws_attend.numel(), self.stream))
+
+    def tree(self) -> Tree:
+        B, H, N, d, b, Lb, lv = self.geom
+        return Tree(self.summaries, B, H, N, d, b, Lb, lv)
