@@ -38,11 +38,12 @@
  *
  * Workspaces
  *   tis_tree_build and tis_tree_attend take a caller-owned device workspace
- *   whose size the *_workspace_bytes query returns.  It holds partial sums and
- *   arrival counters.  It must be ZERO-FILLED before its first use; every call
- *   that completes leaves the counters at zero again, so one zero-fill serves
- *   any number of later calls.  Calls that share a workspace must be ordered
- *   (same stream or synchronised); concurrent calls on one workspace race.
+ *   of at least the size the matching *_workspace_bytes query returns.  It
+ *   holds partial results and arrival counters.  It must be ALL ZERO before
+ *   its first use; every call that completes leaves it all zero again,
+ *   whatever the geometry, so one zero-fill serves any number of later calls
+ *   of any shapes.  Calls that share a workspace must be ordered (same stream
+ *   or synchronised); concurrent calls on one workspace race.
  */
 #ifndef TIS_H_
 #define TIS_H_

@@ -226,3 +226,22 @@ def test_full_size_workload(tis, name):
                         for bb in range(w.batch)])
         _say(f"{name}: planted blocks retrieved by {int(hit.sum())}/{hit.size} queries")
         assert hit.all()
+
+
+def test_workspace_reuse_across_geometries(tis):
+    """One cached workspace serves calls of different shapes in turn: each
+    completed call leaves it all zero, so arrival counters of a call never
+    start from another call's partial results."""
+    cases = [
+        _custom("ws_a", "bf16", 4, 16, 4, 16, Hkv=2, G=2, seed=21),   # few queries, wide beam
+        _custom("ws_b", "bf16", 4, 16, 4, 8, Hkv=2, G=16, seed=22),   # many queries
+        _custom("ws_c", "bf16", 2, 8, 8, 4, d=64, Hkv=1, G=4, seed=23),  # deep: build climbs
+        _custom("ws_d", "bf16", 8, 8, 3, 16, Hkv=4, G=8, seed=24),
+        _custom("ws_a2", "bf16", 4, 16, 4, 16, Hkv=2, G=2, seed=25),
+    ]
+    for w in cases:
+        check_case(tis, w)
+    for kind in ("build", "attend"):
+        for (dev, k), ws in tis.ops._workspaces.items():
+            if k == kind:
+                assert int(torch.count_nonzero(ws)) == 0, f"{kind} workspace left dirty"

@@ -145,7 +145,9 @@ template <typename T, int D> __global__ void __launch_bounds__(64) k_attend(Atte
   if (!s_last) return;
   __threadfence();
 
-  const float *pq = a.part + qi * W * PS;
+  // The merge reads every partial of the query with independent loads,
+  // then clears them so the workspace is all zero again when the call ends.
+  float *pq = a.part + qi * W * PS;
   float mx = -INFINITY;
   bool anybad = false;
   for (int j = lane; j < W; j += 64) {
@@ -159,13 +161,25 @@ template <typename T, int D> __global__ void __launch_bounds__(64) k_attend(Atte
 #pragma unroll
   for (int c = 0; c < CPL; ++c) num[c] = 0.f;
   if (mx != -INFINITY) {
-    for (int j = 0; j < W; ++j) {
-      const float mj = pq[j * PS];
-      if (mj == -INFINITY) continue;
-      const float wj = exp2f(mj - mx);
-      den = fmaf(wj, pq[j * PS + 1], den);
+    for (int j0 = 0; j0 < W; j0 += 64) {
+      // weight of slot j0 + lane, shared with the wave through shuffles
+      const int j = j0 + lane;
+      const float mj = j < W ? pq[j * PS] : -INFINITY;
+      const float wj = exp2f(mj - mx);  // 0 for empty slots
+      den += wave_sum(j < W ? wj * pq[j * PS + 1] : 0.f);
+      const int n = min(64, W - j0);
+      for (int k0 = 0; k0 < n; k0 += 8) {
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) num[c] = fmaf(wj, pq[j * PS + kPartHeader + lane * CPL + c], num[c]);
+        for (int kk = 0; kk < 8; ++kk) {
+          const int k = k0 + kk;
+          const float wk = __shfl(wj, k & 63, 64);
+          if (k < n) {
+            const float *row = pq + (j0 + k) * PS + kPartHeader + lane * CPL;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) num[c] = fmaf(wk, row[c], num[c]);
+          }
+        }
+      }
     }
   }
   float *o = a.O + qi * D + lane * CPL;
@@ -175,6 +189,8 @@ template <typename T, int D> __global__ void __launch_bounds__(64) k_attend(Atte
     if (anybad) r = NAN;
     o[c] = r;
   }
+  for (int i = lane * 4; i < W * PS; i += 64 * 4)
+    *reinterpret_cast<float4 *>(pq + i) = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
 }  // namespace

@@ -146,6 +146,10 @@ template <typename T, int D> __global__ void __launch_bounds__(512) k_build(Buil
           static_cast<float>(s / M);
     }
     __syncthreads();
+    // every sibling sum has been read: clear them, so a completed call leaves
+    // the workspace all zero whatever geometry used it before
+    double *sibw = a.ws_sum + a.ws_off[r] + (head * a.n_at[r] + parent * b) * D;
+    for (int i = tid; i < b * D; i += blockDim.x) sibw[i] = 0.0;
     --r;
     node = parent;
   }
