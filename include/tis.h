@@ -37,13 +37,14 @@
  *   status of the calling thread.  No C++ exception crosses this interface.
  *
  * Workspaces
- *   tis_tree_build and tis_tree_attend take a caller-owned device workspace
- *   of at least the size the matching *_workspace_bytes query returns.  It
- *   holds partial results and arrival counters.  It must be ALL ZERO before
- *   its first use; every call that completes leaves it all zero again,
- *   whatever the geometry, so one zero-fill serves any number of later calls
- *   of any shapes.  Calls that share a workspace must be ordered (same stream
- *   or synchronised); concurrent calls on one workspace race.
+ *   tis_tree_build takes a caller-owned device workspace of at least the size
+ *   tis_build_workspace_bytes returns (0 when the tree is shallow enough for
+ *   one kernel; then NULL is accepted).  It holds fp64 node sums passed
+ *   between the build's two kernels; its contents on entry do not matter.
+ *   Calls that share a workspace must be ordered (same stream or
+ *   synchronised).  tis_tree_attend keeps workspace arguments for a split
+ *   mode; this version needs none (tis_attend_workspace_bytes returns 0) and
+ *   ignores them.
  */
 #ifndef TIS_H_
 #define TIS_H_
@@ -84,7 +85,8 @@ typedef struct tis_tree {
 size_t tis_tree_summary_bytes(int batch, int kv_heads, int head_dim, int branching,
                               int levels);
 
-/* Bytes of workspace tis_tree_build needs for this geometry (>= 256). */
+/* Bytes of workspace tis_tree_build needs for this geometry; 0 if none or if
+ * the geometry is invalid. */
 size_t tis_build_workspace_bytes(int batch, int kv_heads, int n_keys, int head_dim,
                                  int branching, int leaf_block, int levels);
 
@@ -123,7 +125,8 @@ tis_status tis_tree_route(const void *Q, tis_dtype dtype, int q_heads,
                           const tis_tree *tree, int beam, int32_t *indices,
                           int32_t *trace, void *stream);
 
-/* Bytes of workspace tis_tree_attend needs for this geometry (>= 256). */
+/* Bytes of workspace tis_tree_attend needs for this geometry: 0 in this
+ * version, which finishes each query inside one workgroup. */
 size_t tis_attend_workspace_bytes(int batch, int q_heads, int head_dim, int beam,
                                   int leaf_block);
 
@@ -138,9 +141,11 @@ size_t tis_attend_workspace_bytes(int batch, int q_heads, int head_dim, int beam
  *          entry is an empty slot; a repeated entry counts once; an entry
  *          >= N / L makes that query's output row NaN (never read out of
  *          bounds).  A query whose set is empty gets a zero row.
- * scale    softmax scale; <= 0 selects 1/sqrt(d).
+ * scale    softmax scale; <= 0 selects 1/sqrt(d); NaN or infinite is
+ *          rejected (TIS_E_SHAPE).
  * O        out: float32 [B][Hq][d], o = sum_t softmax(scale*q.k_t) v_t over
  *          the union of the selected blocks; fp32 accumulation.
+ * workspace, workspace_bytes: unused in this version (may be NULL / 0).
  * Requires N % L == 0 and 1 <= beam <= TIS_MAX_CANDIDATES.
  */
 tis_status tis_tree_attend(const void *Q, const void *K, const void *V, tis_dtype dtype,

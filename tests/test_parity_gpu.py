@@ -229,9 +229,8 @@ def test_full_size_workload(tis, name):
 
 
 def test_workspace_reuse_across_geometries(tis):
-    """One cached workspace serves calls of different shapes in turn: each
-    completed call leaves it all zero, so arrival counters of a call never
-    start from another call's partial results."""
+    """One cached workspace serves calls of different shapes in turn, and
+    contents left by earlier calls never leak into later results."""
     cases = [
         _custom("ws_a", "bf16", 4, 16, 4, 16, Hkv=2, G=2, seed=21),   # few queries, wide beam
         _custom("ws_b", "bf16", 4, 16, 4, 8, Hkv=2, G=16, seed=22),   # many queries
@@ -240,8 +239,6 @@ def test_workspace_reuse_across_geometries(tis):
         _custom("ws_a2", "bf16", 4, 16, 4, 16, Hkv=2, G=2, seed=25),
     ]
     for w in cases:
+        for ws in tis.ops._workspaces.values():
+            ws.fill_(0x7F)  # garbage (large finite doubles) must not matter
         check_case(tis, w)
-    for kind in ("build", "attend"):
-        for (dev, k), ws in tis.ops._workspaces.items():
-            if k == kind:
-                assert int(torch.count_nonzero(ws)) == 0, f"{kind} workspace left dirty"

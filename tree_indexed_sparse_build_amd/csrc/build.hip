@@ -1,11 +1,15 @@
-// tree_build: node summaries = mean of the keys under each node, every level
-// in one launch ("Subquadratic Attention with a Hierarchical Tree-Structured
+// tree_build: node summaries = mean of the keys under each node, for every
+// level ("Subquadratic Attention with a Hierarchical Tree-Structured
 // Indexer", Abstract: a tree of recursively compressed key summaries over
 // the KV cache).
 //
 // HBM-bound: K is read exactly once with 16-byte coalesced loads (a wave
-// reads whole 1 KB stretches of a leaf block), each summary row is written
-// once.  Sums are carried in fp64 in a fixed order and rounded once to fp32.
+// reads whole 1 KB stretches of a leaf block, 16 KB in flight per wave),
+// each summary row is written once.  Sums are carried in fp64 in a fixed
+// order and rounded once to fp32.  The first kernel finishes every level up
+// to the roots of its chunks; when those sit below level 1 a second, small
+// kernel climbs the rest from their fp64 sums (a kernel boundary instead of
+// device-scope fences between workgroups).
 #include "tis_device.hpp"
 #include "tis_internal.hpp"
 
@@ -26,9 +30,8 @@ template <typename T, int D> __global__ void __launch_bounds__(512) k_build(Buil
   constexpr int E = G::kElemsPerLane;
   constexpr int LPR = G::kLanesPerRow;
   constexpr int R = G::kRowsPerInstr;
-  constexpr int U = 8;  // 16-byte loads in flight per lane
+  constexpr int U = 16;  // 16-byte loads in flight per lane
   extern __shared__ double lds[];
-  __shared__ int s_last;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -71,10 +74,7 @@ template <typename T, int D> __global__ void __launch_bounds__(512) k_build(Buil
     }
     // rows of one leaf are spread over the R lane groups of the wave
 #pragma unroll
-    for (int m = LPR; m < 64; m <<= 1) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] += shfl_xor_f64(acc[e], m);
-    }
+    for (int e = 0; e < E; ++e) acc[e] = group_sum<LPR, 32>(acc[e], lane);
     if (lane < LPR)
       store_mean<E>(a.summ + a.summ_off[lv] + (head * a.n_at[lv] + leaf) * D + col, acc,
                     static_cast<double>(L));
@@ -117,41 +117,39 @@ template <typename T, int D> __global__ void __launch_bounds__(512) k_build(Buil
     nxt = t;
   }
 
-  // ---- levels above the chunk root: the last sibling to arrive climbs
-  int r = lvl;
-  int64_t node = base;
-  while (r >= 2) {
-    double *mine = a.ws_sum + a.ws_off[r] + (head * a.n_at[r] + node) * D;
+  // ---- the chunk root: its fp64 sum feeds the levels above (second kernel)
+  if (lvl >= 2) {
+    double *mine = a.ws_sum + a.ws_off[lvl] + (head * a.n_at[lvl] + base) * D;
     for (int i = tid; i < D; i += blockDim.x) mine[i] = cur[i];
-    __threadfence();
-    __syncthreads();
-    const int64_t parent = node / b;
-    int *ctr = a.ws_cnt + a.cnt_off[r - 1] + head * a.n_at[r - 1] + parent;
-    if (tid == 0) {
-      const int old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-      const int last = old == b - 1;
-      if (last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_last = last;
+  }
+}
+
+// Levels r-1 .. 1 from the fp64 sums of the level-r chunk roots.  One
+// workgroup per level-1 node, one thread per column: each thread carries its
+// column up through every level of the subtree on its own, so there is no
+// barrier; a workgroup's reads of a node row are one coalesced stretch.
+template <int D> __global__ void __launch_bounds__(D) k_build_top(BuildArgs a) {
+  const int t = threadIdx.x;
+  const int b = a.branching;
+  const int r = a.root_level;
+  const int64_t head = blockIdx.x / b;
+  const int64_t n1 = blockIdx.x - head * b;
+  for (int l = r - 1; l >= 1; --l) {
+    // level l of the subtree holds the b^(l-1) nodes from n1 * b^(l-1) on
+    int64_t first = n1;
+    int64_t span = 1;
+    for (int k = 1; k < l; ++k) {
+      first *= b;
+      span *= b;
     }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    const double M = static_cast<double>(a.n_keys / a.n_at[r - 1]);
-    const double *sib = a.ws_sum + a.ws_off[r] + (head * a.n_at[r] + parent * b) * D;
-    for (int i = tid; i < D; i += blockDim.x) {
+    const double M = static_cast<double>(a.n_keys / a.n_at[l]);
+    const double *child = a.ws_sum + a.ws_off[l + 1] + head * a.n_at[l + 1] * D + t;
+    for (int64_t n = first; n < first + span; ++n) {
       double s = 0.0;
-      for (int c = 0; c < b; ++c) s += sib[c * D + i];
-      cur[i] = s;
-      a.summ[a.summ_off[r - 1] + (head * a.n_at[r - 1] + parent) * D + i] =
-          static_cast<float>(s / M);
+      for (int c = 0; c < b; ++c) s += child[(n * b + c) * D];
+      a.summ[a.summ_off[l] + (head * a.n_at[l] + n) * D + t] = static_cast<float>(s / M);
+      if (l >= 2) a.ws_sum[a.ws_off[l] + (head * a.n_at[l] + n) * D + t] = s;
     }
-    __syncthreads();
-    // every sibling sum has been read: clear them, so a completed call leaves
-    // the workspace all zero whatever geometry used it before
-    double *sibw = a.ws_sum + a.ws_off[r] + (head * a.n_at[r] + parent * b) * D;
-    for (int i = tid; i < b * D; i += blockDim.x) sibw[i] = 0.0;
-    --r;
-    node = parent;
   }
 }
 
@@ -170,21 +168,18 @@ bool plan_build(int64_t heads, int head_dim, int branching, int leaf_block, int 
   int64_t chunks = 1;
   for (int i = 0; i < r; ++i) chunks *= branching;
   if (heads * chunks > 0x7fffffffLL) return false;
-  size_t cnt = 0, sum = 0;
+  size_t sum = 0;
   int64_t n = 1;
   for (int l = 1; l <= r; ++l) {
     n *= branching;
-    if (l <= r - 1) cnt += static_cast<size_t>(heads * n);
     if (l >= 2) sum += static_cast<size_t>(heads * n) * head_dim;
   }
   p->root_level = r;
   p->waves = static_cast<int>(nw);
   p->chunks = chunks;
   p->lds_bytes = static_cast<size_t>(2 * nw * head_dim) * sizeof(double);
-  p->cnt_elems = cnt;
   p->sum_elems = sum;
-  p->workspace_bytes = align_up(cnt * sizeof(int), 256) + sum * sizeof(double);
-  if (p->workspace_bytes < 256) p->workspace_bytes = 256;
+  p->workspace_bytes = sum * sizeof(double);
   return true;
 }
 
@@ -202,6 +197,13 @@ hipError_t launch_build(Dt dt, int head_dim, int64_t heads, const BuildArgs &a,
     hipLaunchKernelGGL((k_build<float, 64>), grid, block, p.lds_bytes, s, a);
   else
     return hipErrorInvalidValue;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.root_level < 2) return e;
+  const dim3 grid2(static_cast<unsigned>(heads * a.branching));
+  if (head_dim == 128)
+    hipLaunchKernelGGL((k_build_top<128>), grid2, dim3(128), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_build_top<64>), grid2, dim3(64), 0, s, a);
   return hipGetLastError();
 }
 

@@ -2,20 +2,21 @@
 // Hierarchical Tree-Structured Indexer", Abstract: queries traverse the tree
 // of key summaries from the top down to retrieve a sparse subset of keys).
 //
-// One workgroup (4 waves) walks one query through every level in a single
+// One workgroup (8 waves) walks one query through every level in a single
 // launch.  Per level: gather the candidate summary rows (half a wave per
-// fp32 row of d = 128, 16-byte loads), dot them with the query in fp64,
-// rank the candidates in LDS and compact the kept set in ascending node
-// order, which is also candidate order for the next level.
+// fp32 row of d = 128, 16-byte loads, every row of the level in flight at
+// once), dot them with the query in fp64, rank the candidates in LDS and
+// compact the kept set in ascending node order; the kept nodes' children,
+// in that order, are the next level's candidates.
 #include "tis_device.hpp"
 #include "tis_internal.hpp"
 
 namespace tis {
 namespace {
 
-constexpr int kRouteWaves = 4;
+constexpr int kRouteWaves = 8;
 constexpr int kRouteThreads = kRouteWaves * 64;
-static_assert(kMaxCandidates <= kRouteThreads, "one thread per candidate");
+static_assert(kMaxCandidates <= kRouteThreads / 2, "two or more threads per candidate");
 
 // Ordered key of a candidate: the fp64 score mapped to an unsigned integer
 // whose order is the score order, with its 8 lowest bits replaced by
@@ -56,8 +57,9 @@ template <typename T, int D> __global__ void __launch_bounds__(kRouteThreads) k_
   constexpr int REP = LPR / U;        // lanes sharing one reduced score
   constexpr int ROWS = U * kRouteWaves * RPI;
   __shared__ uint64_t keys[kMaxCandidates];
-  __shared__ int rank[kMaxCandidates];
-  __shared__ int front[2][kMaxCandidates];
+  __shared__ int pcnt[kRouteThreads];      // partial rank counts, one per thread
+  __shared__ int cand[2][kMaxCandidates];  // node id of every candidate, this level / next
+  __shared__ int front[kMaxCandidates];    // kept nodes of the level, ascending
   __shared__ int wcount[kRouteWaves];
 
   const int tid = threadIdx.x;
@@ -73,25 +75,24 @@ template <typename T, int D> __global__ void __launch_bounds__(kRouteThreads) k_
   const int col = (lane % LPR) * 4;
   const int rsub = lane / LPR;
 
+  // the query row is loaded together with the first level's summaries
   double q[4];
   load_q<T, D>(static_cast<const T *>(a.Q) + qi * D, col, q);
 
   int cur = 0;
   int nf = 1;
   for (int l = 1; l <= lv; ++l) {
-    const int C = l == 1 ? b : nf * b;
+    const int C = nf * b;
     const float *sl = a.summ + a.summ_off[l] + head * a.n_at[l] * D + col;
     for (int base = 0; base < C; base += ROWS) {
       float4 v[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int pos = base + (u * kRouteWaves + w) * RPI + rsub;
-        if (pos < C) {
-          const int64_t node = l == 1 ? pos : static_cast<int64_t>(front[cur][pos / b]) * b + pos % b;
-          v[u] = *reinterpret_cast<const float4 *>(sl + node * D);
-        } else {
-          v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
+        // level 1: the candidates are the root's children 0..b-1
+        const int node = l == 1 ? pos : cand[cur][pos < C ? pos : 0];
+        v[u] = pos < C ? *reinterpret_cast<const float4 *>(sl + static_cast<int64_t>(node) * D)
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
       }
       double part[U];
 #pragma unroll
@@ -108,50 +109,64 @@ template <typename T, int D> __global__ void __launch_bounds__(kRouteThreads) k_
       const int pos = base + (k * kRouteWaves + w) * RPI + rsub;
       if ((lane % REP) == 0 && pos < C) keys[pos] = score_key(s, pos);
     }
-    if (C > W) {
-      for (int i = tid; i < C; i += kRouteThreads) rank[i] = 0;
-    }
     __syncthreads();
+    // rank of candidate i = number of candidates with a larger key.  Threads
+    // are split into `parts` groups of cp (the power of two >= C); group p
+    // compares every candidate with one slice of the keys.
+    int lcp = 0, lparts = 0;
     if (C > W) {
-      // rank_i = number of candidates with a larger key; the threads left
-      // over when C < 256 split the comparison range
-      int cp = 1;
-      while (cp < C) cp <<= 1;
-      const int parts = kRouteThreads / cp;
-      const int span = (C + parts - 1) / parts;
-      const int i = tid % cp;
-      const int part = tid / cp;
-      if (i < C && part < parts) {
+      lcp = 32 - __clz(C - 1);
+      lparts = min(9 - lcp, 3);
+      const int span = (((C + (1 << lparts) - 1) >> lparts) + 7) & ~7;
+      const int i = tid & ((1 << lcp) - 1);
+      const int part = tid >> lcp;
+      int cnt = 0;
+      if (i < C && part < (1 << lparts)) {
         const uint64_t ki = keys[i];
-        const int j0 = part * span;
-        const int j1 = min(C, j0 + span);
-        int cnt = 0;
-        for (int j = j0; j < j1; ++j) cnt += keys[j] > ki ? 1 : 0;
-        if (cnt) atomicAdd(&rank[i], cnt);
+        int j = part * span;
+        const int j1 = min(C, j + span);
+        for (; j + 8 <= j1; j += 8) {
+          uint64_t kj[8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) kj[t] = keys[j + t];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) cnt += kj[t] > ki ? 1 : 0;
+        }
+        for (; j < j1; ++j) cnt += keys[j] > ki ? 1 : 0;
       }
+      pcnt[tid] = cnt;
       __syncthreads();
     }
-    // compact the kept candidates in position (= node) order
-    const bool keep = tid < C && (C <= W || rank[tid] < W);
+    // compact the kept candidates in position (= node) order and lay out
+    // the next level's candidates: the children of each kept node
+    bool keep = tid < C;
+    if (keep && C > W) {
+      int r = 0;
+      for (int p = 0; p < (1 << lparts); ++p) r += pcnt[(p << lcp) + tid];
+      keep = r < W;
+    }
     const uint64_t mask = __ballot(keep);
     if (lane == 0) wcount[w] = __popcll(mask);
     __syncthreads();
-    int off = 0;
-    for (int ww = 0; ww < w; ++ww) off += wcount[ww];
     if (keep) {
-      const int below = __popcll(mask & ((1ull << lane) - 1ull));
-      front[cur ^ 1][off + below] =
-          l == 1 ? tid : front[cur][tid / b] * b + tid % b;
+      int off = 0;
+      for (int ww = 0; ww < w; ++ww) off += wcount[ww];
+      const int kpos = off + __popcll(mask & ((1ull << lane) - 1ull));
+      const int node = l == 1 ? tid : cand[cur][tid];
+      front[kpos] = node;
+      if (l < lv) {
+        for (int c = 0; c < b; ++c) cand[cur ^ 1][kpos * b + c] = node * b + c;
+      }
     }
     __syncthreads();
     cur ^= 1;
     nf = C < W ? C : W;
     if (a.trace) {
       int32_t *tr = a.trace + (qi * lv + (l - 1)) * W;
-      for (int k = tid; k < W; k += kRouteThreads) tr[k] = k < nf ? front[cur][k] : -1;
+      for (int k = tid; k < W; k += kRouteThreads) tr[k] = k < nf ? front[k] : -1;
     }
   }
-  for (int k = tid; k < W; k += kRouteThreads) a.indices[qi * W + k] = front[cur][k];
+  for (int k = tid; k < W; k += kRouteThreads) a.indices[qi * W + k] = front[k];
 }
 
 }  // namespace

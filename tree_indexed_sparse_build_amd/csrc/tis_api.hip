@@ -121,8 +121,8 @@ size_t tis_build_workspace_bytes(int batch, int kv_heads, int n_keys, int head_d
 tis_status tis_tree_build(const void *K, tis_dtype dtype, int batch, int kv_heads, int n_keys,
                           int head_dim, int branching, int leaf_block, int levels, tis_tree *tree,
                           void *workspace, size_t workspace_bytes, void *stream) {
-  if (!K || !tree || !tree->summaries || !workspace)
-    return fail(TIS_E_NULL, "tis_tree_build: K, tree, tree->summaries and workspace are required");
+  if (!K || !tree || !tree->summaries)
+    return fail(TIS_E_NULL, "tis_tree_build: K, tree and tree->summaries are required");
   tis_status st = check_dtype(dtype);
   if (st != TIS_OK) return st;
   Geometry g;
@@ -134,37 +134,30 @@ tis_status tis_tree_build(const void *K, tis_dtype dtype, int batch, int kv_head
   tis::BuildPlan p;
   if (!tis::plan_build(heads, head_dim, branching, leaf_block, levels, &p))
     return fail(TIS_E_UNSUPPORTED, "tis_tree_build: grid too large");
-  if (workspace_bytes < p.workspace_bytes)
-    return fail(TIS_E_WORKSPACE, "tis_tree_build: workspace %zu bytes < %zu required",
-                workspace_bytes, p.workspace_bytes);
+  if (p.workspace_bytes > 0 && (!workspace || workspace_bytes < p.workspace_bytes))
+    return fail(workspace ? TIS_E_WORKSPACE : TIS_E_NULL,
+                "tis_tree_build: workspace of %zu bytes required, %zu given", p.workspace_bytes,
+                workspace ? workspace_bytes : (size_t)0);
 
   tis::BuildArgs a{};
   a.K = K;
   a.summ = tree->summaries;
-  char *ws = static_cast<char *>(workspace);
-  a.ws_cnt = reinterpret_cast<int *>(ws);
-  a.ws_sum = reinterpret_cast<double *>(ws + tis::align_up(p.cnt_elems * sizeof(int), 256));
+  a.ws_sum = static_cast<double *>(workspace);
   a.n_keys = n_keys;
   a.chunks = p.chunks;
   a.branching = branching;
   a.leaf_block = leaf_block;
   a.levels = levels;
   a.root_level = p.root_level;
-  int64_t cnt_off = 0, sum_off = 0;
+  int64_t sum_off = 0;
   for (int l = 0; l <= tis::kMaxLevels; ++l) {
     a.n_at[l] = g.n_at[l];
     a.summ_off[l] = g.summ_off[l];
-    a.ws_off[l] = a.cnt_off[l] = 0;
+    a.ws_off[l] = 0;
   }
-  for (int l = 1; l <= p.root_level; ++l) {
-    if (l <= p.root_level - 1) {
-      a.cnt_off[l] = cnt_off;
-      cnt_off += heads * g.n_at[l];
-    }
-    if (l >= 2) {
-      a.ws_off[l] = sum_off;
-      sum_off += heads * g.n_at[l] * head_dim;
-    }
+  for (int l = 2; l <= p.root_level; ++l) {
+    a.ws_off[l] = sum_off;
+    sum_off += heads * g.n_at[l] * head_dim;
   }
   const tis::Dt dt = dtype == TIS_BF16 ? tis::Dt::BF16 : tis::Dt::F32;
   st = hip_status(tis::launch_build(dt, head_dim, heads, a, p, static_cast<hipStream_t>(stream)),
@@ -227,19 +220,22 @@ tis_status tis_tree_route(const void *Q, tis_dtype dtype, int q_heads, const tis
 }
 
 size_t tis_attend_workspace_bytes(int batch, int q_heads, int head_dim, int beam, int leaf_block) {
+  (void)batch;
+  (void)q_heads;
+  (void)head_dim;
+  (void)beam;
   (void)leaf_block;
-  if (batch < 1 || q_heads < 1 || head_dim < 1 || beam < 1) return 0;
-  tis::AttendPlan p;
-  tis::plan_attend(static_cast<int64_t>(batch) * q_heads, head_dim, beam, &p);
-  return p.workspace_bytes;
+  return 0;  // each query is finished inside one workgroup
 }
 
 tis_status tis_tree_attend(const void *Q, const void *K, const void *V, tis_dtype dtype, int batch,
                            int q_heads, int kv_heads, int n_keys, int head_dim, int leaf_block,
                            const int32_t *indices, int beam, float scale, float *O,
                            void *workspace, size_t workspace_bytes, void *stream) {
-  if (!Q || !K || !V || !indices || !O || !workspace)
-    return fail(TIS_E_NULL, "tis_tree_attend: Q, K, V, indices, O and workspace are required");
+  (void)workspace;
+  (void)workspace_bytes;
+  if (!Q || !K || !V || !indices || !O)
+    return fail(TIS_E_NULL, "tis_tree_attend: Q, K, V, indices and O are required");
   tis_status st = check_dtype(dtype);
   if (st != TIS_OK) return st;
   if (batch < 1 || kv_heads < 1 || q_heads < 1 || q_heads % kv_heads != 0)
@@ -256,15 +252,10 @@ tis_status tis_tree_attend(const void *Q, const void *K, const void *V, tis_dtyp
   if (!(scale == scale) || isinf(scale))
     return fail(TIS_E_SHAPE, "tis_tree_attend: scale must be finite");
   if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) ||
-      !aligned(workspace, 16) || !aligned(indices, 4))
-    return fail(TIS_E_ALIGN, "tis_tree_attend: Q, K, V, O and workspace need 16-byte alignment");
+      !aligned(indices, 4))
+    return fail(TIS_E_ALIGN, "tis_tree_attend: Q, K, V and O need 16-byte alignment, indices 4-byte");
   const int64_t queries = static_cast<int64_t>(batch) * q_heads;
-  if (queries * beam > 0x7fffffffLL) return fail(TIS_E_UNSUPPORTED, "tis_tree_attend: grid too large");
-  tis::AttendPlan p;
-  tis::plan_attend(queries, head_dim, beam, &p);
-  if (workspace_bytes < p.workspace_bytes)
-    return fail(TIS_E_WORKSPACE, "tis_tree_attend: workspace %zu bytes < %zu required",
-                workspace_bytes, p.workspace_bytes);
+  if (queries > 0x7fffffffLL) return fail(TIS_E_UNSUPPORTED, "tis_tree_attend: too many queries");
 
   const double sc = scale > 0.f ? static_cast<double>(scale) : 1.0 / sqrt(static_cast<double>(head_dim));
   tis::AttendArgs a{};
@@ -273,9 +264,6 @@ tis_status tis_tree_attend(const void *Q, const void *K, const void *V, tis_dtyp
   a.V = V;
   a.indices = indices;
   a.O = O;
-  char *ws = static_cast<char *>(workspace);
-  a.cnt = reinterpret_cast<int *>(ws);
-  a.part = reinterpret_cast<float *>(ws + tis::align_up(p.cnt_elems * sizeof(int), 256));
   a.queries = queries;
   a.n_keys = n_keys;
   a.q_heads = q_heads;
@@ -286,7 +274,7 @@ tis_status tis_tree_attend(const void *Q, const void *K, const void *V, tis_dtyp
   a.n_blocks = n_keys / leaf_block;
   a.scale_log2 = static_cast<float>(sc * 1.4426950408889634);
   const tis::Dt dt = dtype == TIS_BF16 ? tis::Dt::BF16 : tis::Dt::F32;
-  return hip_status(tis::launch_attend(dt, head_dim, a, p, static_cast<hipStream_t>(stream)),
+  return hip_status(tis::launch_attend(dt, head_dim, a, static_cast<hipStream_t>(stream)),
                     "tis_tree_attend launch");
 }
 

@@ -53,20 +53,79 @@ template <typename T, int D> struct RowGeom {
   static_assert(kLanesPerRow <= 64 && 64 % kLanesPerRow == 0, "row must tile a wave");
 };
 
-__device__ inline double shfl_xor_f64(double v, int mask) {
-  return __shfl_xor(v, mask, 64);
+// ---- cross-lane exchange without the LDS crossbar ----------------------
+// xor_lane<M>(v, lane): lane l receives v of lane l ^ M.  M = 1, 2: one DPP
+// quad permutation; M = 4, 8: two DPP row permutations (xor 4 = xor 3 then
+// mirror in 8 lanes, xor 8 = mirror in 16 then mirror in 8); M = 16, 32:
+// one permlane swap (gfx950) and a select.
+template <int CTRL> __device__ inline uint32_t dpp(uint32_t v) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_mov_dpp(static_cast<int>(v), CTRL, 0xF, 0xF, false));
 }
 
+template <int M> __device__ inline uint32_t xor_lane(uint32_t v, int lane) {
+  static_assert(M == 1 || M == 2 || M == 4 || M == 8 || M == 16 || M == 32, "lane mask");
+  if constexpr (M == 1) {
+    return dpp<0xB1>(v);  // quad_perm [1,0,3,2]
+  } else if constexpr (M == 2) {
+    return dpp<0x4E>(v);  // quad_perm [2,3,0,1]
+  } else if constexpr (M == 4) {
+    return dpp<0x141>(dpp<0x1B>(v));  // quad_perm [3,2,1,0], row_half_mirror
+  } else if constexpr (M == 8) {
+    return dpp<0x141>(dpp<0x140>(v));  // row_mirror, row_half_mirror
+  } else if constexpr (M == 16) {
+    const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (lane & 16) ? p[0] : p[1];
+  } else {
+    const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (lane & 32) ? p[0] : p[1];
+  }
+}
+template <int M> __device__ inline float xor_lane(float v, int lane) {
+  return __uint_as_float(xor_lane<M>(__float_as_uint(v), lane));
+}
+template <int M> __device__ inline double xor_lane(double v, int lane) {
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
+  const uint32_t lo = xor_lane<M>(static_cast<uint32_t>(u), lane);
+  const uint32_t hi = xor_lane<M>(static_cast<uint32_t>(u >> 32), lane);
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
+// v + (v of lane ^ M), the same on both lanes of each pair.
+template <int M, typename F> __device__ inline F xor_sum(F v, int lane) {
+  return v + xor_lane<M>(v, lane);
+}
+
+// Butterfly reductions over all 64 lanes (every lane gets the result).
 __device__ inline float wave_max(float v) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-  return v;
+  const int lane = __lane_id();
+  v = fmaxf(v, xor_lane<1>(v, lane));
+  v = fmaxf(v, xor_lane<2>(v, lane));
+  v = fmaxf(v, xor_lane<4>(v, lane));
+  v = fmaxf(v, xor_lane<8>(v, lane));
+  v = fmaxf(v, xor_lane<16>(v, lane));
+  return fmaxf(v, xor_lane<32>(v, lane));
 }
 
 __device__ inline float wave_sum(float v) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
-  return v;
+  const int lane = __lane_id();
+  v = xor_sum<1>(v, lane);
+  v = xor_sum<2>(v, lane);
+  v = xor_sum<4>(v, lane);
+  v = xor_sum<8>(v, lane);
+  v = xor_sum<16>(v, lane);
+  return xor_sum<32>(v, lane);
+}
+
+// Sum over lane groups: every lane gets the sum over the lanes that differ
+// from it only in the bits FIRST, 2*FIRST, ..., LAST.
+template <int FIRST, int LAST, typename F> __device__ inline F group_sum(F v, int lane) {
+  if constexpr (FIRST <= LAST) {
+    v = xor_sum<FIRST>(v, lane);
+    return group_sum<FIRST * 2, LAST>(v, lane);
+  } else {
+    return v;
+  }
 }
 
 // Transposed reduction over lane groups of LPR consecutive lanes.
@@ -75,26 +134,26 @@ __device__ inline float wave_sum(float v) {
 // / (LPR / U); the LPR / U lanes sharing a k all return the same total.
 // Each halving step exchanges half of the remaining values, so U values cost
 // U - 1 + log2(LPR / U) exchanges instead of U * log2(LPR).
-template <int U, int LPR, typename F> __device__ inline F group_transpose_reduce(F (&v)[U], int lane) {
-  static_assert(U >= 1 && U <= LPR, "need U <= LPR");
-#pragma unroll
-  for (int step = 0; (U >> (step + 1)) >= 1; ++step) {
-    const int h = U >> (step + 1);
-    const int m = LPR >> (step + 1);
+template <int U, int LPR, int STEP, typename F>
+__device__ inline void transpose_steps(F (&v)[U], int lane) {
+  constexpr int h = U >> (STEP + 1);
+  if constexpr (h >= 1) {
+    constexpr int m = LPR >> (STEP + 1);
     const bool sel = (lane & m) != 0;
 #pragma unroll
-    for (int k = 0; k < U / 2; ++k) {
-      if (k < h) {
-        const F keep = sel ? v[k + h] : v[k];
-        const F send = sel ? v[k] : v[k + h];
-        v[k] = keep + __shfl_xor(send, m, 64);
-      }
+    for (int k = 0; k < h; ++k) {
+      const F keep = sel ? v[k + h] : v[k];
+      const F send = sel ? v[k] : v[k + h];
+      v[k] = keep + xor_lane<m>(send, lane);
     }
+    transpose_steps<U, LPR, STEP + 1>(v, lane);
   }
-  F s = v[0];
-#pragma unroll
-  for (int m = LPR / U / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
-  return s;
+}
+
+template <int U, int LPR, typename F> __device__ inline F group_transpose_reduce(F (&v)[U], int lane) {
+  static_assert(U >= 1 && U <= LPR, "need U <= LPR");
+  transpose_steps<U, LPR, 0>(v, lane);
+  return group_sum<1, LPR / U / 2>(v[0], lane);
 }
 
 }  // namespace tis

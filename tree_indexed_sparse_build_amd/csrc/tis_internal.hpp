@@ -18,14 +18,12 @@ enum class Dt : int { F32 = 0, BF16 = 1 };
 // Work split.  A wave reduces the b leaves of one level-(lv-1) node.  A
 // workgroup of nw = b^kg waves owns the subtree of one node at level
 // r = lv - 1 - kg (a "chunk") and finishes its inner levels in LDS.  When
-// r >= 2 the chunk root's fp64 sum goes to the workspace and the last of the
-// b sibling chunks to arrive (counted with an atomic) climbs one level, and
-// so on up to level 1, so the whole tree takes one launch.
+// r >= 2 the chunk roots leave fp64 sums in the workspace and a second
+// kernel computes levels r-1 .. 1 from them.
 struct BuildArgs {
   const void *K;
   float *summ;
   double *ws_sum;        // fp64 node sums of levels 2..r
-  int *ws_cnt;           // arrival counters of levels 1..r-1
   int64_t n_keys;        // N
   int64_t chunks;        // b^r chunks per head
   int branching, leaf_block, levels;
@@ -33,7 +31,6 @@ struct BuildArgs {
   int64_t n_at[kMaxLevels + 1];     // b^l
   int64_t summ_off[kMaxLevels + 1]; // element offset of level l in summ
   int64_t ws_off[kMaxLevels + 1];   // element offset of level l in ws_sum
-  int64_t cnt_off[kMaxLevels + 1];  // element offset of level l in ws_cnt
 };
 
 struct BuildPlan {
@@ -41,7 +38,7 @@ struct BuildPlan {
   int waves;             // nw
   int64_t chunks;        // b^r per head
   size_t lds_bytes;
-  size_t cnt_elems, sum_elems;
+  size_t sum_elems;
   size_t workspace_bytes;
 };
 
@@ -66,15 +63,14 @@ struct RouteArgs {
 hipError_t launch_route(Dt dt, int head_dim, const RouteArgs &a, hipStream_t s);
 
 // --------------------------------------------------------------- attend --
-// One wave per (query, index slot): it gathers the slot's leaf block, runs
-// an online softmax over its keys and leaves (m, l, acc[d]) in the
-// workspace; the last wave of a query to arrive merges the beam's partials.
+// One workgroup per query: its waves split the selected leaf blocks into
+// row units, keep online-softmax partials and merge them in LDS.
+constexpr int kAttendMaxWaves = 16;
+
 struct AttendArgs {
   const void *Q, *K, *V;
   const int32_t *indices;
   float *O;
-  float *part;           // [queries][beam][d + 4]: m, l, -, -, acc[d]
-  int *cnt;              // [queries] arrival counters
   int64_t queries;       // B * Hq
   int64_t n_keys;
   int q_heads, kv_heads, group;
@@ -83,15 +79,8 @@ struct AttendArgs {
   float scale_log2;      // softmax scale * log2(e)
 };
 
-struct AttendPlan {
-  size_t part_elems;
-  size_t cnt_elems;
-  size_t workspace_bytes;
-};
-
-void plan_attend(int64_t queries, int head_dim, int beam, AttendPlan *p);
-hipError_t launch_attend(Dt dt, int head_dim, const AttendArgs &a, const AttendPlan &p,
-                         hipStream_t s);
+int attend_waves(int head_dim, Dt dt, int beam, int leaf_block);
+hipError_t launch_attend(Dt dt, int head_dim, const AttendArgs &a, hipStream_t s);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

@@ -40,8 +40,8 @@ def _stream(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-# Zero-filled workspaces, one per (device, size class).  Every completed call
-# returns its counters to zero, so a workspace is reused without clearing.
+# Workspaces, one per (device, kind), grown on demand and reused: calls are
+# ordered on the caller's stream, and no call expects particular contents.
 _workspaces: Dict[Tuple[int, str], torch.Tensor] = {}
 
 
@@ -49,8 +49,7 @@ def _workspace(device: torch.device, kind: str, nbytes: int) -> torch.Tensor:
     key = (device.index if device.index is not None else torch.cuda.current_device(), kind)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        size = max(nbytes, 256)
-        ws = torch.zeros(size, dtype=torch.uint8, device=device)
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
 
@@ -102,11 +101,11 @@ def tree_build(K: torch.Tensor, branching: int, leaf_block: int, levels: int) ->
         raise _lib.TisError(_lib.TIS_E_SHAPE, "invalid tree geometry")
     summ = torch.empty(nbytes // 4, dtype=torch.float32, device=K.device)
     wsb = L.tis_build_workspace_bytes(B, H, N, d, branching, leaf_block, levels)
-    ws = _workspace(K.device, "build", wsb)
+    ws = _workspace(K.device, "build", wsb) if wsb else None
     t = TisTree(0, 0, 0, 0, 0, 0, 0, summ.data_ptr())
     check(L.tis_tree_build(K.data_ptr(), _dtype_code(K), B, H, N, d, branching, leaf_block,
-                           levels, ctypes.byref(t), ws.data_ptr(), ws.numel(),
-                           _stream(K.device)))
+                           levels, ctypes.byref(t), ws.data_ptr() if ws is not None else None,
+                           ws.numel() if ws is not None else 0, _stream(K.device)))
     return Tree(summ, t.batch, t.kv_heads, t.n_keys, t.head_dim, t.branching, t.leaf_block,
                 t.levels)
 
@@ -151,11 +150,12 @@ def tree_attend(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, indices: torc
     O = torch.empty((B, Hq, d), dtype=torch.float32, device=Q.device)
     L = lib()
     wsb = L.tis_attend_workspace_bytes(B, Hq, d, W, leaf_block)
-    ws = _workspace(Q.device, "attend", wsb)
+    ws = _workspace(Q.device, "attend", wsb) if wsb else None
     check(L.tis_tree_attend(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q), B, Hq,
                             Hkv, N, d, leaf_block, indices.data_ptr(), W,
                             0.0 if scale is None else float(scale), O.data_ptr(),
-                            ws.data_ptr(), ws.numel(), _stream(Q.device)))
+                            ws.data_ptr() if ws is not None else None,
+                            ws.numel() if ws is not None else 0, _stream(Q.device)))
     return O
 
 
@@ -205,11 +205,12 @@ class DecodePlan:
         if nbytes == 0:
             raise _lib.TisError(_lib.TIS_E_SHAPE, "invalid tree geometry")
         self.summaries = torch.empty(nbytes // 4, dtype=torch.float32, device=K.device)
-        self.ws_build = torch.zeros(max(256, L.tis_build_workspace_bytes(*self.geom)),
-                                    dtype=torch.uint8, device=K.device)
-        self.ws_attend = torch.zeros(max(256, L.tis_attend_workspace_bytes(B, Hq, d, beam,
-                                                                           leaf_block)),
-                                     dtype=torch.uint8, device=K.device)
+        wsb = L.tis_build_workspace_bytes(*self.geom)
+        self.ws_build = (torch.empty(wsb, dtype=torch.uint8, device=K.device) if wsb
+                         else None)
+        wsa = L.tis_attend_workspace_bytes(B, Hq, d, beam, leaf_block)
+        self.ws_attend = (torch.zeros(wsa, dtype=torch.uint8, device=K.device) if wsa
+                          else None)
         self.indices = torch.empty((B, Hq, beam), dtype=torch.int32, device=K.device)
         self.out = torch.empty((B, Hq, d), dtype=torch.float32, device=K.device)
         self.tree_c = TisTree(0, 0, 0, 0, 0, 0, 0, self.summaries.data_ptr())
@@ -217,9 +218,11 @@ class DecodePlan:
 
     def build(self) -> None:
         B, H, N, d, b, Lb, lv = self.geom
+        ws = self.ws_build
         check(self._lib.tis_tree_build(self.K.data_ptr(), self.dt, B, H, N, d, b, Lb, lv,
-                                       ctypes.byref(self.tree_c), self.ws_build.data_ptr(),
-                                       self.ws_build.numel(), self.stream))
+                                       ctypes.byref(self.tree_c),
+                                       None if ws is None else ws.data_ptr(),
+                                       0 if ws is None else ws.numel(), self.stream))
 
     def route(self) -> None:
         check(self._lib.tis_tree_route(self.Q.data_ptr(), self.dt, self.q_heads,
@@ -231,8 +234,11 @@ class DecodePlan:
         check(self._lib.tis_tree_attend(self.Q.data_ptr(), self.K.data_ptr(), self.V.data_ptr(),
                                         self.dt, B, self.q_heads, H, N, d, Lb,
                                         self.indices.data_ptr(), self.beam, self.scale,
-                                        self.out.data_ptr(), self.ws_attend.data_ptr(),
-                                        self.ws_attend.numel(), self.stream))
+                                        self.out.data_ptr(),
+                                        None if self.ws_attend is None
+                                        else self.ws_attend.data_ptr(),
+                                        0 if self.ws_attend is None
+                                        else self.ws_attend.numel(), self.stream))
 
     def tree(self) -> Tree:
         B, H, N, d, b, Lb, lv = self.geom
