@@ -3,11 +3,12 @@
 // of key summaries from the top down to retrieve a sparse subset of keys).
 //
 // One workgroup (8 waves) walks one query through every level in a single
-// launch.  Per level: gather the candidate summary rows (half a wave per
-// fp32 row of d = 128, 16-byte loads, every row of the level in flight at
-// once), dot them with the query in fp64, rank the candidates in LDS and
-// compact the kept set in ascending node order; the kept nodes' children,
-// in that order, are the next level's candidates.
+// launch.  Levels with no more candidates than the beam keep everything and
+// are not scored.  Per scored level: gather the candidate summary rows (half
+// a wave per fp32 row of d = 128, 16-byte loads, every row of the level in
+// flight at once), dot them with the query in fp64, rank the candidates in
+// LDS and put the W best at their rank; their children are the next level's
+// candidates.  The kept leaves are written in ascending order.
 #include "tis_device.hpp"
 #include "tis_internal.hpp"
 
@@ -19,16 +20,18 @@ constexpr int kRouteThreads = kRouteWaves * 64;
 static_assert(kMaxCandidates <= kRouteThreads / 2, "two or more threads per candidate");
 
 // Ordered key of a candidate: the fp64 score mapped to an unsigned integer
-// whose order is the score order, with its 8 lowest bits replaced by
-// (255 - position).  Larger key = better.  Positions run in ascending node
-// order, so equal scores go to the lower node index.  Scores closer than
-// 2^-44 relative also fall to the index order; that is far inside the
-// relative cut gap of 1e-5 below which a selection counts as a tie.
-__device__ inline uint64_t score_key(double s, int pos) {
+// whose order is the score order, with its `bits` lowest bits replaced by
+// (2^bits - 1 - node), bits = enough bits for every node index of the level.
+// Larger key = better, and equal scores go to the lower node index.  Scores
+// closer than 2^(bits - 52) relative (at most 2^-21 for levels of up to 2^31
+// nodes) also fall to the index order; that is far inside the relative cut
+// gap of 1e-5 below which a selection counts as a tie.
+__device__ inline uint64_t score_key(double s, int node, int bits) {
   s = s + 0.0;  // -0 -> +0
   uint64_t u = static_cast<uint64_t>(__double_as_longlong(s));
   u = (u >> 63) ? ~u : (u | 0x8000000000000000ull);
-  return (u & ~0xffull) | static_cast<uint64_t>(255 - pos);
+  const uint64_t mask = (1ull << bits) - 1ull;
+  return (u & ~mask) | (mask - static_cast<uint64_t>(node));
 }
 
 template <typename T, int D> __device__ inline void load_q(const T *q, int col, double *out);
@@ -59,8 +62,7 @@ template <typename T, int D> __global__ void __launch_bounds__(kRouteThreads) k_
   __shared__ uint64_t keys[kMaxCandidates];
   __shared__ int pcnt[kRouteThreads];      // partial rank counts, one per thread
   __shared__ int cand[2][kMaxCandidates];  // node id of every candidate, this level / next
-  __shared__ int front[kMaxCandidates];    // kept nodes of the level, ascending
-  __shared__ int wcount[kRouteWaves];
+  __shared__ int front[kMaxCandidates];    // kept nodes of the level, in rank order
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -75,98 +77,129 @@ template <typename T, int D> __global__ void __launch_bounds__(kRouteThreads) k_
   const int col = (lane % LPR) * 4;
   const int rsub = lane / LPR;
 
-  // the query row is loaded together with the first level's summaries
+  // Levels whose candidate set is no larger than the beam keep every node,
+  // whatever the scores: the walk starts at the first level l0 that cuts,
+  // whose candidates are all of its nodes (so its loads need no selection).
+  int l0 = 1;
+  while (l0 < lv && a.n_at[l0] <= W) ++l0;
+  if (a.trace) {
+    for (int l = 1; l < l0; ++l) {
+      int32_t *tr = a.trace + (qi * lv + (l - 1)) * W;
+      for (int k = tid; k < W; k += kRouteThreads) tr[k] = k < a.n_at[l] ? k : -1;
+    }
+  }
+
+  // the query row is loaded together with the first scored level's summaries
   double q[4];
   load_q<T, D>(static_cast<const T *>(a.Q) + qi * D, col, q);
 
   int cur = 0;
-  int nf = 1;
-  for (int l = 1; l <= lv; ++l) {
+  int nf = static_cast<int>(a.n_at[l0 - 1]);
+  for (int l = l0; l <= lv; ++l) {
     const int C = nf * b;
-    const float *sl = a.summ + a.summ_off[l] + head * a.n_at[l] * D + col;
-    for (int base = 0; base < C; base += ROWS) {
-      float4 v[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int pos = base + (u * kRouteWaves + w) * RPI + rsub;
-        // level 1: the candidates are the root's children 0..b-1
-        const int node = l == 1 ? pos : cand[cur][pos < C ? pos : 0];
-        v[u] = pos < C ? *reinterpret_cast<const float4 *>(sl + static_cast<int64_t>(node) * D)
-                       : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-      double part[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        // fp32 x (fp32 or bf16) products are exact in fp64
-        double s = q[0] * static_cast<double>(v[u].x);
-        s = fma(q[1], static_cast<double>(v[u].y), s);
-        s = fma(q[2], static_cast<double>(v[u].z), s);
-        s = fma(q[3], static_cast<double>(v[u].w), s);
-        part[u] = s;
-      }
-      const double s = group_transpose_reduce<U, LPR>(part, lane);
-      const int k = (lane % LPR) / REP;
-      const int pos = base + (k * kRouteWaves + w) * RPI + rsub;
-      if ((lane % REP) == 0 && pos < C) keys[pos] = score_key(s, pos);
-    }
-    __syncthreads();
-    // rank of candidate i = number of candidates with a larger key.  Threads
-    // are split into `parts` groups of cp (the power of two >= C); group p
-    // compares every candidate with one slice of the keys.
-    int lcp = 0, lparts = 0;
+    const bool all = l == l0;  // candidates are nodes 0..C-1 of level l
     if (C > W) {
-      lcp = 32 - __clz(C - 1);
-      lparts = min(9 - lcp, 3);
-      const int span = (((C + (1 << lparts) - 1) >> lparts) + 7) & ~7;
-      const int i = tid & ((1 << lcp) - 1);
-      const int part = tid >> lcp;
-      int cnt = 0;
-      if (i < C && part < (1 << lparts)) {
-        const uint64_t ki = keys[i];
-        int j = part * span;
-        const int j1 = min(C, j + span);
-        for (; j + 8 <= j1; j += 8) {
-          uint64_t kj[8];
+      const int bits = 32 - __clz(static_cast<int>(a.n_at[l]) - 1);
+      const float *sl = a.summ + a.summ_off[l] + head * a.n_at[l] * D + col;
+      for (int base = 0; base < C; base += ROWS) {
+        float4 v[U];
 #pragma unroll
-          for (int t = 0; t < 8; ++t) kj[t] = keys[j + t];
-#pragma unroll
-          for (int t = 0; t < 8; ++t) cnt += kj[t] > ki ? 1 : 0;
+        for (int u = 0; u < U; ++u) {
+          const int pos = base + (u * kRouteWaves + w) * RPI + rsub;
+          const int node = all ? pos : cand[cur][pos < C ? pos : 0];
+          v[u] = pos < C ? *reinterpret_cast<const float4 *>(sl + static_cast<int64_t>(node) * D)
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
         }
-        for (; j < j1; ++j) cnt += keys[j] > ki ? 1 : 0;
+        double part[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          // fp32 x (fp32 or bf16) products are exact in fp64
+          double s = q[0] * static_cast<double>(v[u].x);
+          s = fma(q[1], static_cast<double>(v[u].y), s);
+          s = fma(q[2], static_cast<double>(v[u].z), s);
+          s = fma(q[3], static_cast<double>(v[u].w), s);
+          part[u] = s;
+        }
+        const double s = group_transpose_reduce<U, LPR>(part, lane);
+        const int k = (lane % LPR) / REP;
+        const int pos = base + (k * kRouteWaves + w) * RPI + rsub;
+        if ((lane % REP) == 0 && pos < C) keys[pos] = score_key(s, all ? pos : cand[cur][pos], bits);
       }
-      pcnt[tid] = cnt;
       __syncthreads();
-    }
-    // compact the kept candidates in position (= node) order and lay out
-    // the next level's candidates: the children of each kept node
-    bool keep = tid < C;
-    if (keep && C > W) {
-      int r = 0;
-      for (int p = 0; p < (1 << lparts); ++p) r += pcnt[(p << lcp) + tid];
-      keep = r < W;
-    }
-    const uint64_t mask = __ballot(keep);
-    if (lane == 0) wcount[w] = __popcll(mask);
-    __syncthreads();
-    if (keep) {
-      int off = 0;
-      for (int ww = 0; ww < w; ++ww) off += wcount[ww];
-      const int kpos = off + __popcll(mask & ((1ull << lane) - 1ull));
-      const int node = l == 1 ? tid : cand[cur][tid];
-      front[kpos] = node;
-      if (l < lv) {
-        for (int c = 0; c < b; ++c) cand[cur ^ 1][kpos * b + c] = node * b + c;
+      // rank of candidate i = number of candidates with a larger key.
+      // Threads form `parts` groups of cp (the power of two >= C); group p
+      // compares every candidate with one slice of the keys.
+      const int lcp = 32 - __clz(C - 1);
+      const int lparts = min(9 - lcp, 3);
+      const int span = (((C + (1 << lparts) - 1) >> lparts) + 7) & ~7;
+      {
+        const int i = tid & ((1 << lcp) - 1);
+        const int part = tid >> lcp;
+        int cnt = 0;
+        if (i < C && part < (1 << lparts)) {
+          const uint64_t ki = keys[i];
+          int j = part * span;
+          const int j1 = min(C, j + span);
+          for (; j + 8 <= j1; j += 8) {
+            uint64_t kj[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) kj[t] = keys[j + t];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) cnt += kj[t] > ki ? 1 : 0;
+          }
+          for (; j < j1; ++j) cnt += keys[j] > ki ? 1 : 0;
+        }
+        pcnt[tid] = cnt;
+      }
+      __syncthreads();
+      // the W best go to front[] at their rank; their children, in the same
+      // order, are the next level's candidates
+      if (tid < C) {
+        int r = 0;
+        for (int p = 0; p < (1 << lparts); ++p) r += pcnt[(p << lcp) + tid];
+        if (r < W) {
+          const int node = all ? tid : cand[cur][tid];
+          front[r] = node;
+          if (l < lv) {
+            for (int c = 0; c < b; ++c) cand[cur ^ 1][r * b + c] = node * b + c;
+          }
+        }
+      }
+    } else {
+      // no cut: every candidate is kept
+      if (tid < C) {
+        const int node = all ? tid : cand[cur][tid];
+        front[tid] = node;
+        if (l < lv) {
+          for (int c = 0; c < b; ++c) cand[cur ^ 1][tid * b + c] = node * b + c;
+        }
       }
     }
     __syncthreads();
     cur ^= 1;
     nf = C < W ? C : W;
     if (a.trace) {
+      // kept nodes of the level in ascending order
       int32_t *tr = a.trace + (qi * lv + (l - 1)) * W;
-      for (int k = tid; k < W; k += kRouteThreads) tr[k] = k < nf ? front[k] : -1;
+      for (int k = tid; k < W; k += kRouteThreads) {
+        if (k < nf) {
+          const int node = front[k];
+          int r = 0;
+          for (int j = 0; j < nf; ++j) r += front[j] < node ? 1 : 0;
+          tr[r] = node;
+        } else {
+          tr[k] = -1;
+        }
+      }
     }
   }
-  for (int k = tid; k < W; k += kRouteThreads) a.indices[qi * W + k] = front[k];
+  // the kept leaves, ascending
+  for (int k = tid; k < W; k += kRouteThreads) {
+    const int node = front[k];
+    int r = 0;
+    for (int j = 0; j < W; ++j) r += front[j] < node ? 1 : 0;
+    a.indices[qi * W + r] = node;
+  }
 }
 
 }  // namespace
