@@ -47,10 +47,15 @@ def test_summary_bytes(lib):
 
 
 def test_workspace_bytes(lib):
-    # 3 levels of branching 8: one kernel, no workspace
+    # the build keeps fp64 sums of levels 2..r, r = the level of its chunk roots
+    # 32K keys, 4 x 8 heads: chunks are level-1 nodes (8 leaves per wave, 8 waves)
     assert lib.tis_build_workspace_bytes(4, 8, 32768, 128, 8, 64, 3) == 0
-    # 5 levels: chunk roots at level 3 pass fp64 sums of levels 2..3
-    assert lib.tis_build_workspace_bytes(1, 8, 1 << 20, 128, 8, 32, 5) == 8 * (64 + 512) * 128 * 8
+    # 256K keys, 2 x 8 heads: chunks at level 2
+    assert lib.tis_build_workspace_bytes(2, 8, 262144, 128, 8, 64, 4) == 16 * 64 * 128 * 8
+    # 1M keys, 8 heads: chunks at level 2 (64 leaves per wave, 8 waves per workgroup)
+    assert lib.tis_build_workspace_bytes(1, 8, 1 << 20, 128, 8, 32, 5) == 8 * 64 * 128 * 8
+    # a single-level tree needs none
+    assert lib.tis_build_workspace_bytes(1, 1, 64, 128, 16, 4, 1) == 0
     # invalid geometry -> 0
     assert lib.tis_build_workspace_bytes(4, 8, 1000, 128, 8, 64, 3) == 0
     # attend finishes each query inside one workgroup: no workspace

@@ -6,31 +6,66 @@
 // HBM-bound: K is read exactly once with 16-byte coalesced loads (a wave
 // reads whole 1 KB stretches of a leaf block, 16 KB in flight per wave),
 // each summary row is written once.  Sums are carried in fp64 in a fixed
-// order and rounded once to fp32.  The first kernel finishes every level up
-// to the roots of its chunks; when those sit below level 1 a second, small
-// kernel climbs the rest from their fp64 sums (a kernel boundary instead of
-// device-scope fences between workgroups).
+// order and rounded once to fp32.  A wave reduces a subtree of b^kw leaves
+// (a stack of open node sums in registers); a workgroup of b^kg waves
+// finishes its chunk's inner levels in LDS.  When the chunk roots sit below
+// level 1, one small kernel per remaining level climbs from their fp64 sums
+// (kernel boundaries instead of device-scope fences between workgroups).
 #include "tis_device.hpp"
 #include "tis_internal.hpp"
 
 namespace tis {
 namespace {
 
-template <int E> __device__ inline void store_mean(float *dst, const double *s, double M) {
-  float f[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) f[e] = static_cast<float>(s[e] / M);
-#pragma unroll
-  for (int e = 0; e < E; e += 4)
-    *reinterpret_cast<float4 *>(dst + e) = make_float4(f[e], f[e + 1], f[e + 2], f[e + 3]);
+// Mean of a node from its fp64 sum over M keys, rounded once to fp32.  When M
+// is a power of two the product with 1/M is exact, the same value as s / M.
+__device__ inline float node_mean(const BuildArgs &a, int level, double s) {
+  return static_cast<float>(((a.pow2_levels >> level) & 1) ? s * a.mean_inv[level]
+                                                          : s / a.mean_div[level]);
 }
 
-template <typename T, int D> __global__ void __launch_bounds__(512) k_build(BuildArgs a) {
+// Transposed reduction of a lane's E column sums over the R = 64 / LPR row
+// groups of the wave (lane bits LPR .. 32).  Each step keeps half of the
+// remaining columns, so afterwards the lane holds E / R finished columns
+// v[0 .. E/R), starting at column rowgroup_offset() of its E-column slice.
+template <int E, int LPR, int M, int STEP>
+__device__ inline void rowgroup_steps(double (&v)[E], int lane) {
+  if constexpr (M >= LPR) {
+    constexpr int h = E >> (STEP + 1);
+    const bool sel = (lane & M) != 0;
+#pragma unroll
+    for (int k = 0; k < h; ++k) {
+      const double keep = sel ? v[k + h] : v[k];
+      const double send = sel ? v[k] : v[k + h];
+      v[k] = keep + xor_lane<M>(send, lane);
+    }
+    rowgroup_steps<E, LPR, M / 2, STEP + 1>(v, lane);
+  }
+}
+
+template <int E, int LPR> __device__ inline int rowgroup_offset(int lane) {
+  int off = 0;
+  int h = E / 2;
+#pragma unroll
+  for (int m = 32; m >= LPR; m >>= 1, h >>= 1) off += (lane & m) ? h : 0;
+  return off;
+}
+
+template <int CPL> __device__ inline void store_cols(float *dst, const float *f) {
+  if constexpr (CPL == 2)
+    *reinterpret_cast<float2 *>(dst) = make_float2(f[0], f[1]);
+  else
+    dst[0] = f[0];
+}
+
+template <typename T, int D> __global__ void __launch_bounds__(1024) k_build(BuildArgs a) {
   using G = RowGeom<T, D>;
   constexpr int E = G::kElemsPerLane;
   constexpr int LPR = G::kLanesPerRow;
   constexpr int R = G::kRowsPerInstr;
-  constexpr int U = 16;  // 16-byte loads in flight per lane
+  constexpr int CPL = E / R;  // finished columns per lane (D / 64)
+  constexpr int U = 16;       // 16-byte loads in flight per lane
+  static_assert(CPL * 64 == D, "one finished column block per lane");
   extern __shared__ double lds[];
 
   const int tid = threadIdx.x;
@@ -40,19 +75,38 @@ template <typename T, int D> __global__ void __launch_bounds__(512) k_build(Buil
   const int b = a.branching;
   const int L = a.leaf_block;
   const int lv = a.levels;
+  const int kw = a.wave_depth;
   const int64_t head = blockIdx.x / a.chunks;
   const int64_t chunk = blockIdx.x - head * a.chunks;
   const int col = (lane % LPR) * E;
+  const int colf = col + rowgroup_offset<E, LPR>(lane);  // this lane's finished columns
   const int rsub = lane / LPR;
   const T *kh = static_cast<const T *>(a.K) + head * a.n_keys * D + col;
 
-  // ---- this wave: the b leaves under one node of level lv-1
-  const int64_t node1 = chunk * nw + w;
-  double pacc[E];
+  // ---- this wave: the subtree of b^kw leaves under one node of level lv-kw
+  const int64_t wnode = chunk * nw + w;
+  const int64_t leaf0 = wnode * a.wave_leaves;
+  double st[kMaxWaveDepth][CPL];  // running sums of the open node at level lv-k
+  int ctr[kMaxWaveDepth];
+  int64_t nid[kMaxWaveDepth];     // index of that node within its level
+  double root[CPL];
 #pragma unroll
-  for (int e = 0; e < E; ++e) pacc[e] = 0.0;
-  for (int c = 0; c < b; ++c) {
-    const int64_t leaf = node1 * b + c;
+  for (int k = 0; k < kMaxWaveDepth; ++k) {
+    ctr[k] = 0;
+    nid[k] = wnode;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) st[k][j] = 0.0;
+  }
+  for (int k = kMaxWaveDepth - 1; k >= 0; --k) {
+    // node of level lv-k-1 that holds the first leaf: wnode * b^(kw-k-1)
+    if (k < kw) {
+      int64_t n = wnode;
+      for (int j = k + 1; j < kw; ++j) n *= b;
+      nid[k] = n;
+    }
+  }
+  for (int64_t c = 0; c < a.wave_leaves; ++c) {
+    const int64_t leaf = leaf0 + c;
     const T *kl = kh + leaf * static_cast<int64_t>(L) * D;
     double acc[E];
 #pragma unroll
@@ -72,35 +126,52 @@ template <typename T, int D> __global__ void __launch_bounds__(512) k_build(Buil
         for (int e = 0; e < E; ++e) acc[e] += static_cast<double>(f[e]);
       }
     }
-    // rows of one leaf are spread over the R lane groups of the wave
+    rowgroup_steps<E, LPR, 32, 0>(acc, lane);
+    {
+      float f[CPL];
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = group_sum<LPR, 32>(acc[e], lane);
-    if (lane < LPR)
-      store_mean<E>(a.summ + a.summ_off[lv] + (head * a.n_at[lv] + leaf) * D + col, acc,
-                    static_cast<double>(L));
+      for (int j = 0; j < CPL; ++j) f[j] = node_mean(a, lv, acc[j]);
+      store_cols<CPL>(a.summ + a.summ_off[lv] + (head * a.n_at[lv] + leaf) * D + colf, f);
+    }
+    double carry[CPL];
 #pragma unroll
-    for (int e = 0; e < E; ++e) pacc[e] += acc[e];
+    for (int j = 0; j < CPL; ++j) carry[j] = root[j] = acc[j];
+    // close every level whose node this leaf completes
+#pragma unroll
+    for (int k = 0; k < kMaxWaveDepth; ++k) {
+      if (k >= kw) break;
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) st[k][j] += carry[j];
+      if (++ctr[k] < b) break;
+      const int lvl = lv - k - 1;
+      if (lvl >= 1) {
+        float f[CPL];
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) f[j] = node_mean(a, lvl, st[k][j]);
+        store_cols<CPL>(a.summ + a.summ_off[lvl] + (head * a.n_at[lvl] + nid[k]) * D + colf, f);
+      }
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        carry[j] = root[j] = st[k][j];
+        st[k][j] = 0.0;
+      }
+      ctr[k] = 0;
+      ++nid[k];
+    }
   }
 
-  int lvl = lv - 1;  // level of the wave's node
-  if (lvl >= 1 && lane < LPR)
-    store_mean<E>(a.summ + a.summ_off[lvl] + (head * a.n_at[lvl] + node1) * D + col, pacc,
-                  static_cast<double>(a.n_keys / a.n_at[lvl]));
-
-  // ---- the workgroup's inner levels, from the waves' fp64 sums in LDS
+  // ---- the workgroup's inner levels, from the waves' fp64 root sums in LDS
+  int lvl = lv - kw;  // level of the wave's root
   double *cur = lds;
   double *nxt = lds + nw * D;
-  if (lane < LPR) {
 #pragma unroll
-    for (int e = 0; e < E; ++e) cur[w * D + col + e] = pacc[e];
-  }
+  for (int j = 0; j < CPL; ++j) cur[w * D + colf + j] = root[j];
   __syncthreads();
   int64_t base = chunk * nw;  // index of cur[0]'s node within its level
   for (int ncur = nw; ncur > 1; ncur /= b) {
     const int nn = ncur / b;
     --lvl;
     base /= b;
-    const double M = lvl >= 1 ? static_cast<double>(a.n_keys / a.n_at[lvl]) : 1.0;
     for (int i = tid; i < nn * D; i += blockDim.x) {
       const int n = i / D;
       const int dd = i % D;
@@ -108,8 +179,7 @@ template <typename T, int D> __global__ void __launch_bounds__(512) k_build(Buil
       for (int c = 0; c < b; ++c) s += cur[(n * b + c) * D + dd];
       nxt[n * D + dd] = s;
       if (lvl >= 1)
-        a.summ[a.summ_off[lvl] + (head * a.n_at[lvl] + base + n) * D + dd] =
-            static_cast<float>(s / M);
+        a.summ[a.summ_off[lvl] + (head * a.n_at[lvl] + base + n) * D + dd] = node_mean(a, lvl, s);
     }
     __syncthreads();
     double *t = cur;
@@ -117,40 +187,29 @@ template <typename T, int D> __global__ void __launch_bounds__(512) k_build(Buil
     nxt = t;
   }
 
-  // ---- the chunk root: its fp64 sum feeds the levels above (second kernel)
+  // ---- the chunk root: its fp64 sum feeds the levels above (later kernels)
   if (lvl >= 2) {
     double *mine = a.ws_sum + a.ws_off[lvl] + (head * a.n_at[lvl] + base) * D;
     for (int i = tid; i < D; i += blockDim.x) mine[i] = cur[i];
   }
 }
 
-// Levels r-1 .. 1 from the fp64 sums of the level-r chunk roots.  One
-// workgroup per level-1 node, one thread per column: each thread carries its
-// column up through every level of the subtree on its own, so there is no
-// barrier; a workgroup's reads of a node row are one coalesced stretch.
-template <int D> __global__ void __launch_bounds__(D) k_build_top(BuildArgs a) {
-  const int t = threadIdx.x;
+// One level l above the chunk roots: node sum = sum of its b children's fp64
+// sums (level l+1), one thread per (node, column), every load independent.
+// Launched once per level, from r-1 down to 1; the kernel boundary between
+// levels orders the writes of one level before the reads of the next.
+template <int D> __global__ void __launch_bounds__(256) k_build_level(BuildArgs a, int l) {
+  const int64_t item = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t nodes = a.chunks_at_level[l];  // B*Hkv*n_l
+  if (item >= nodes * D) return;
+  const int64_t node = item / D;  // (head, node) flattened: head * n_l + n
+  const int t = static_cast<int>(item - node * D);
   const int b = a.branching;
-  const int r = a.root_level;
-  const int64_t head = blockIdx.x / b;
-  const int64_t n1 = blockIdx.x - head * b;
-  for (int l = r - 1; l >= 1; --l) {
-    // level l of the subtree holds the b^(l-1) nodes from n1 * b^(l-1) on
-    int64_t first = n1;
-    int64_t span = 1;
-    for (int k = 1; k < l; ++k) {
-      first *= b;
-      span *= b;
-    }
-    const double M = static_cast<double>(a.n_keys / a.n_at[l]);
-    const double *child = a.ws_sum + a.ws_off[l + 1] + head * a.n_at[l + 1] * D + t;
-    for (int64_t n = first; n < first + span; ++n) {
-      double s = 0.0;
-      for (int c = 0; c < b; ++c) s += child[(n * b + c) * D];
-      a.summ[a.summ_off[l] + (head * a.n_at[l] + n) * D + t] = static_cast<float>(s / M);
-      if (l >= 2) a.ws_sum[a.ws_off[l] + (head * a.n_at[l] + n) * D + t] = s;
-    }
-  }
+  const double *child = a.ws_sum + a.ws_off[l + 1] + node * b * D + t;
+  double s = 0.0;
+  for (int c = 0; c < b; ++c) s += child[static_cast<int64_t>(c) * D];
+  a.summ[a.summ_off[l] + node * D + t] = node_mean(a, l, s);
+  if (l >= 2) a.ws_sum[a.ws_off[l] + node * D + t] = s;
 }
 
 }  // namespace
@@ -158,26 +217,57 @@ template <int D> __global__ void __launch_bounds__(D) k_build_top(BuildArgs a) {
 bool plan_build(int64_t heads, int head_dim, int branching, int leaf_block, int levels,
                 BuildPlan *p) {
   (void)leaf_block;
-  int kg = 0;
-  int64_t nw = 1;
-  while (kg + 1 <= levels - 1 && nw * branching <= 8) {
-    nw *= branching;
-    ++kg;
+  // Choose the wave subtree depth kw (b^kw leaves per wave) and the
+  // workgroup depth kg (b^kg <= 16 waves).  Each level left above the chunk
+  // roots costs one more small launch (~5 us), so: (1) a plan that finishes
+  // in the first kernel (r <= 1) wins if it still has >= 2048 waves;
+  // (2) otherwise plans with >= 4096 waves and >= 512 workgroups (enough
+  // loads in flight on 256 CUs), fewest levels left first; (3) otherwise the
+  // most waves.  Ties go to bigger workgroups.
+  struct Cand { int kw, kg, r; int64_t waves, wgs; };
+  auto ipow = [](int64_t x, int e) {
+    int64_t v = 1;
+    for (int i = 0; i < e; ++i) v *= x;
+    return v;
+  };
+  auto tier = [](const Cand &c) {
+    if (c.r <= 1 && c.waves >= 2048) return 0;
+    if (c.waves >= 4096 && c.wgs >= 512) return 1;
+    return 2;
+  };
+  auto better = [&](const Cand &c, const Cand &o) {
+    const int tc = tier(c), to = tier(o);
+    if (tc != to) return tc < to;
+    if (tc == 0) return c.waves > o.waves || (c.waves == o.waves && c.kg > o.kg);
+    if (tc == 1) return c.r < o.r || (c.r == o.r && c.kg > o.kg);
+    return c.waves > o.waves || (c.waves == o.waves && c.r < o.r);
+  };
+  bool have = false;
+  Cand best{};
+  for (int kw = 0; kw <= kMaxWaveDepth && kw <= levels; ++kw) {
+    for (int kg = 0; kw + kg <= levels; ++kg) {
+      const int64_t nw = ipow(branching, kg);
+      if (nw > 16) break;
+      const int r = levels - kw - kg;
+      const Cand c{kw, kg, r, heads * ipow(branching, levels - kw), heads * ipow(branching, r)};
+      if (c.wgs > 0x7fffffffLL) continue;
+      if (!have || better(c, best)) best = c;
+      have = true;
+    }
   }
-  const int r = levels - 1 - kg;
-  int64_t chunks = 1;
-  for (int i = 0; i < r; ++i) chunks *= branching;
-  if (heads * chunks > 0x7fffffffLL) return false;
+  if (!have) return false;
+  const int64_t nw = ipow(branching, best.kg);
+  p->wave_depth = best.kw;
+  p->root_level = best.r;
+  p->waves = static_cast<int>(nw);
+  p->chunks = ipow(branching, best.r);
+  p->lds_bytes = static_cast<size_t>(2 * nw * head_dim) * sizeof(double);
   size_t sum = 0;
   int64_t n = 1;
-  for (int l = 1; l <= r; ++l) {
+  for (int l = 1; l <= best.r; ++l) {
     n *= branching;
     if (l >= 2) sum += static_cast<size_t>(heads * n) * head_dim;
   }
-  p->root_level = r;
-  p->waves = static_cast<int>(nw);
-  p->chunks = chunks;
-  p->lds_bytes = static_cast<size_t>(2 * nw * head_dim) * sizeof(double);
   p->sum_elems = sum;
   p->workspace_bytes = sum * sizeof(double);
   return true;
@@ -198,13 +288,16 @@ hipError_t launch_build(Dt dt, int head_dim, int64_t heads, const BuildArgs &a,
   else
     return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.root_level < 2) return e;
-  const dim3 grid2(static_cast<unsigned>(heads * a.branching));
-  if (head_dim == 128)
-    hipLaunchKernelGGL((k_build_top<128>), grid2, dim3(128), 0, s, a);
-  else
-    hipLaunchKernelGGL((k_build_top<64>), grid2, dim3(64), 0, s, a);
-  return hipGetLastError();
+  for (int l = p.root_level - 1; e == hipSuccess && l >= 1; --l) {
+    const int64_t items = a.chunks_at_level[l] * head_dim;
+    const dim3 g(static_cast<unsigned>((items + 255) / 256));
+    if (head_dim == 128)
+      hipLaunchKernelGGL((k_build_level<128>), g, dim3(256), 0, s, a, l);
+    else
+      hipLaunchKernelGGL((k_build_level<64>), g, dim3(256), 0, s, a, l);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 }  // namespace tis

@@ -149,11 +149,25 @@ tis_status tis_tree_build(const void *K, tis_dtype dtype, int batch, int kv_head
   a.leaf_block = leaf_block;
   a.levels = levels;
   a.root_level = p.root_level;
+  a.wave_depth = p.wave_depth;
+  a.wave_leaves = 1;
+  for (int i = 0; i < p.wave_depth; ++i) a.wave_leaves *= branching;
+  a.pow2_levels = 0;
   int64_t sum_off = 0;
   for (int l = 0; l <= tis::kMaxLevels; ++l) {
     a.n_at[l] = g.n_at[l];
+    a.chunks_at_level[l] = heads * g.n_at[l];
     a.summ_off[l] = g.summ_off[l];
     a.ws_off[l] = 0;
+    a.mean_div[l] = a.mean_inv[l] = 1.0;
+    if (l >= 1 && l <= levels) {
+      const int64_t M = static_cast<int64_t>(n_keys) / g.n_at[l];
+      a.mean_div[l] = static_cast<double>(M);
+      if ((M & (M - 1)) == 0) {
+        a.pow2_levels |= 1u << l;
+        a.mean_inv[l] = 1.0 / static_cast<double>(M);
+      }
+    }
   }
   for (int l = 2; l <= p.root_level; ++l) {
     a.ws_off[l] = sum_off;

@@ -15,26 +15,35 @@ constexpr int kMaxBranching = 64;
 enum class Dt : int { F32 = 0, BF16 = 1 };
 
 // ---------------------------------------------------------------- build --
-// Work split.  A wave reduces the b leaves of one level-(lv-1) node.  A
-// workgroup of nw = b^kg waves owns the subtree of one node at level
-// r = lv - 1 - kg (a "chunk") and finishes its inner levels in LDS.  When
-// r >= 2 the chunk roots leave fp64 sums in the workspace and a second
-// kernel computes levels r-1 .. 1 from them.
+// Work split.  A wave reduces the b^kw leaves under one node of level lv-kw
+// (kw <= kMaxWaveDepth).  A workgroup of nw = b^kg waves owns the subtree of
+// one node at level r = lv - kw - kg (a "chunk") and finishes its inner
+// levels in LDS.  When r >= 2 the chunk roots leave fp64 sums in the
+// workspace and one small kernel per level computes levels r-1 .. 1.
+constexpr int kMaxWaveDepth = 3;
+
 struct BuildArgs {
   const void *K;
   float *summ;
   double *ws_sum;        // fp64 node sums of levels 2..r
   int64_t n_keys;        // N
   int64_t chunks;        // b^r chunks per head
+  int64_t wave_leaves;   // b^kw
   int branching, leaf_block, levels;
   int root_level;        // r
-  int64_t n_at[kMaxLevels + 1];     // b^l
-  int64_t summ_off[kMaxLevels + 1]; // element offset of level l in summ
-  int64_t ws_off[kMaxLevels + 1];   // element offset of level l in ws_sum
+  int wave_depth;        // kw
+  uint32_t pow2_levels;  // bit l set: M_l = N / n_l is a power of two
+  int64_t n_at[kMaxLevels + 1];            // b^l
+  int64_t chunks_at_level[kMaxLevels + 1]; // B*Hkv*b^l
+  int64_t summ_off[kMaxLevels + 1];        // element offset of level l in summ
+  int64_t ws_off[kMaxLevels + 1];          // element offset of level l in ws_sum
+  double mean_div[kMaxLevels + 1];         // M_l
+  double mean_inv[kMaxLevels + 1];         // 1 / M_l when a power of two
 };
 
 struct BuildPlan {
-  int root_level;
+  int root_level;        // r
+  int wave_depth;        // kw
   int waves;             // nw
   int64_t chunks;        // b^r per head
   size_t lds_bytes;
