@@ -43,6 +43,78 @@ def algorithmic_bytes(w):
             "candidates_per_query": cand}
 
 
+COPY_BYTES = 256 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{}.json")
+BUILD_SOURCE = os.path.join(ROOT, "tree_indexed_sparse_build_amd", "csrc", "build.hip")
+
+
+def _source_digest() -> str:
+    import hashlib
+    with open(BUILD_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM bytes per tree_build launch from the committed counter summary,
+    or None when there is none or the build kernel changed since."""
+    path = TRAFFIC_FILE.format(workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("build_source_sha256_16") != _source_digest():
+        return None
+    return t.get("build_bytes_per_launch")
+
+
+def traffic_from_counters(workload: str, fetch_csv: str, write_csv: str) -> dict:
+    """Scales rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the
+    k_build dispatches by what the same counters read for the 256 MiB
+    reference copy (COPY_BYTES read and written), and writes the summary."""
+    import csv
+
+    def per_kernel(path, counter):
+        vals = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") != counter:
+                    continue
+                name = r["Kernel_Name"]
+                vals.setdefault(name, []).append(float(r["Counter_Value"]))
+        return vals
+
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+
+    def pick(vals, key, how="mean"):
+        ks = [k for k in vals if key in k]
+        if not ks:
+            raise SystemExit(f"no dispatch matching {key!r} in the counter file")
+        xs = [v for k in ks for v in vals[k]]
+        return (max(xs) if how == "max" else sum(xs) / len(xs)), ks
+
+    # the reference copy is the largest copy dispatch (input uploads are smaller)
+    f_copy, _ = pick(fetch, "copyBuffer", "max")
+    w_copy, _ = pick(write, "copyBuffer", "max")
+    f_build, _ = pick(fetch, "k_build<")
+    w_build, _ = pick(write, "k_build<")
+    f_scale = COPY_BYTES / (f_copy * 1024.0)
+    w_scale = COPY_BYTES / (w_copy * 1024.0)
+    out = {
+        "workload": workload,
+        "kernel": "k_build (first kernel of tree_build)",
+        "fetch_kib_per_dispatch": f_build, "write_kib_per_dispatch": w_build,
+        "copy_fetch_kib": f_copy, "copy_write_kib": w_copy,
+        "fetch_scale": f_scale, "write_scale": w_scale,
+        "build_bytes_per_launch": f_build * 1024.0 * f_scale + w_build * 1024.0 * w_scale,
+        "build_source_sha256_16": _source_digest(),
+    }
+    with open(TRAFFIC_FILE.format(workload), "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    return out
+
+
 def cpu_baseline(w, x, min_seconds: float = 10.0, max_reps: int = 20):
     """The CPU oracle, as it stands, on whole steps of the same workload."""
     from oracle import tis_oracle as O
@@ -70,9 +142,16 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="gqa_32k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--traffic", default=None,
-                    help="JSON file with measured HBM bytes per build launch")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one 256 MiB device-to-device copy first (the reference "
+                         "dispatch for scaling HBM byte counters)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter files (FETCH_SIZE, WRITE_SIZE) of "
+                         "a --calibrate-copy run into profiles/traffic_<workload>.json and exit")
     args = ap.parse_args(argv)
+    if args.traffic_from:
+        print(json.dumps(traffic_from_counters(args.workload, *args.traffic_from)))
+        return 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); every tree is "
               "independent per (batch, KV head), so N GPUs would each run their own share "
@@ -97,8 +176,19 @@ def main(argv=None):
     K = tis.from_storage(x["K"], w.dtype, dev)
     V = tis.from_storage(x["V"], w.dtype, dev)
     plan = tis.DecodePlan(Q, K, V, w.branching, w.leaf_block, w.levels, w.beam)
+    if args.calibrate_copy:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step():
+        plan.build()
+        plan.decode()  # route + attend of every query in one launch
+
+    def step_separate():
         plan.build()
         plan.route()
         plan.attend()
@@ -122,6 +212,14 @@ def main(argv=None):
     h2 = time.perf_counter()
     total_ms = start.elapsed_time(end)
     ms_step = total_ms / K_
+    # the same steps with route and attend as separate calls (reference)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(K_):
+        step_separate()
+    end.record()
+    torch.cuda.synchronize()
+    ms_step_separate = start.elapsed_time(end) / K_
     # timed region 2: each kernel K times back to back between one event pair
     # (its average launch duration; event overhead is spread over K launches)
     def per_launch(fn):
@@ -137,10 +235,11 @@ def main(argv=None):
     t_build = np.array([per_launch(plan.build)])
     t_route = np.array([per_launch(plan.route)])
     t_attend = np.array([per_launch(plan.attend)])
+    t_decode = per_launch(plan.decode)
 
     by = algorithmic_bytes(w)
     build_gbs = by["build"] / t_build.mean() / 1e9
-    decode_s = (t_route + t_attend).mean()
+    decode_s = t_decode
     idx = plan.indices.cpu().numpy()
     uniq = 0
     for bb in range(w.batch):
@@ -148,7 +247,8 @@ def main(argv=None):
             uniq += len(np.unique(idx[bb, h * w.group:(h + 1) * w.group]))
     attend_dedup = uniq * w.leaf_block * w.head_dim * w.elem_bytes * 2
     log(f"step {ms_step * 1e3:.1f} us (host enqueue {(h1 - h0) / K_ * 1e6:.1f} us/step, "
-        f"wall {(h2 - h0) / K_ * 1e6:.1f} us/step)")
+        f"wall {(h2 - h0) / K_ * 1e6:.1f} us/step); with separate route + attend calls "
+        f"{ms_step_separate * 1e3:.1f} us")
     log(f"build  {t_build.mean() * 1e6:8.2f} us  {build_gbs:8.1f} GB/s "
         f"({build_gbs / HBM_PEAK_GBS:.1%} of 8 TB/s) on {by['build'] / 1e6:.1f} MB")
     log(f"route  {t_route.mean() * 1e6:8.2f} us  {by['route'] / t_route.mean() / 1e9:8.1f} GB/s "
@@ -157,14 +257,13 @@ def main(argv=None):
         f"GB/s on {by['attend'] / 1e6:.2f} MB per-query sum; "
         f"{attend_dedup / t_attend.mean() / 1e9:.1f} GB/s on {attend_dedup / 1e6:.2f} MB of "
         f"distinct blocks per KV head")
-    log(f"decode (route + attend, back to back) {decode_s * 1e6:.2f} us -> "
-        f"{w.queries / decode_s:.3e} queries/s; in the step (step - build): "
-        f"{ms_step * 1e3 - t_build.mean() * 1e6:.2f} us")
+    dec_bytes = by["route"] + by["attend"]
+    log(f"decode (fused route + attend) {decode_s * 1e6:.2f} us -> "
+        f"{w.queries / decode_s:.3e} queries/s, {dec_bytes / decode_s / 1e9:.1f} GB/s "
+        f"({dec_bytes / decode_s / 1e9 / HBM_PEAK_GBS:.1%}) on {dec_bytes / 1e6:.2f} MB; "
+        f"in the step (step - build): {ms_step * 1e3 - t_build.mean() * 1e6:.2f} us")
 
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        with open(args.traffic) as f:
-            traffic = json.load(f).get("build_bytes_per_launch")
+    traffic = load_traffic(w.name)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -189,13 +288,17 @@ def main(argv=None):
         "config": {"workload": w.name, "batch": w.batch, "q_heads": w.q_heads,
                    "kv_heads": w.kv_heads, "head_dim": w.head_dim, "n_keys": w.n_keys,
                    "branching": w.branching, "leaf_block": w.leaf_block, "levels": w.levels,
-                   "beam": w.beam, "step": "tree_build + tree_route + tree_attend"},
+                   "beam": w.beam,
+                   "step": "tree_build + tree_decode (tree_route and tree_attend in one launch)"},
         "roofline": {"kernel": "tree_build", "bound": "hbm", "achieved": build_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": build_gbs / HBM_PEAK_GBS,
                      "traffic": traffic},
-        "decode": {"regime": "route and attend each timed back to back on the step's data",
+        "decode": {"regime": "fused route + attend launches back to back on the step's data",
                    "us": decode_s * 1e6, "queries_per_s": w.queries / decode_s,
+                   "gbs": dec_bytes / decode_s / 1e9,
+                   "frac": dec_bytes / decode_s / 1e9 / HBM_PEAK_GBS,
                    "in_step_us": ms_step * 1e3 - t_build.mean() * 1e6,
+                   "step_us_separate_calls": ms_step_separate * 1e3,
                    "route_us": t_route.mean() * 1e6, "attend_us": t_attend.mean() * 1e6,
                    "attend_gbs_per_query_bytes": by["attend"] / t_attend.mean() / 1e9,
                    "attend_gbs_distinct_blocks": attend_dedup / t_attend.mean() / 1e9},

@@ -154,6 +154,24 @@ tis_status tis_tree_attend(const void *Q, const void *K, const void *V, tis_dtyp
                            int beam, float scale, float *O, void *workspace,
                            size_t workspace_bytes, void *stream);
 
+/*
+ * tis_tree_decode -- one decode step: tis_tree_route and tis_tree_attend for
+ * every query in a single launch (ZHA abstract: the cost of a query is the
+ * routing plus the final attention over the retrieved keys).
+ *
+ * Q [B][Hq][d] and K, V [B][Hkv][N][d] of type `dtype`, matching the tree
+ * (B, Hkv, N, d, L as built).  The leaves each query keeps are exactly those
+ * tis_tree_route returns; O is the softmax attention over their keys as in
+ * tis_tree_attend (summation order may differ in the last fp32 bits).
+ * indices  optional (NULL to skip): int32 [B][Hq][beam], the kept leaves in
+ *          ascending order.
+ * scale    softmax scale; <= 0 selects 1/sqrt(d); NaN or infinite rejected.
+ * Requires 1 <= beam <= b^lv and beam * b <= TIS_MAX_CANDIDATES.
+ */
+tis_status tis_tree_decode(const void *Q, const void *K, const void *V, tis_dtype dtype,
+                           int q_heads, const tis_tree *tree, int beam, float scale, float *O,
+                           int32_t *indices, void *stream);
+
 /* Message for the last non-OK status returned on the calling thread. */
 const char *tis_last_error(void);
 

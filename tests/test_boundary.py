@@ -27,7 +27,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert {"tis_tree_build", "tis_tree_route", "tis_tree_attend"} <= set(names)
+    assert {"tis_tree_build", "tis_tree_route", "tis_tree_attend", "tis_tree_decode"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES), "binding and header disagree"
@@ -167,4 +167,28 @@ def _attend(lib, **kw):
 ])
 def test_attend_rejects(lib, kw, status):
     assert _attend(lib, **kw) == status
+    assert lib.tis_last_error().decode()
+
+
+def _decode(lib, Q=FAKE, K=FAKE, V=FAKE, dt=_lib.TIS_BF16, Hq=2, tree=None, beam=2, scale=0.0,
+            O=FAKE, idx=None):
+    t = tree if tree is not None else _tree(H=1)
+    return lib.tis_tree_decode(Q, K, V, dt, Hq, ctypes.byref(t), beam, scale, O, idx, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=None), _lib.TIS_E_NULL),
+    (dict(O=None), _lib.TIS_E_NULL),
+    (dict(tree=_tree(summ=None)), _lib.TIS_E_NULL),
+    (dict(dt=9), _lib.TIS_E_DTYPE),
+    (dict(tree=_tree(H=2), Hq=3), _lib.TIS_E_SHAPE),
+    (dict(beam=0), _lib.TIS_E_SHAPE),
+    (dict(beam=9), _lib.TIS_E_SHAPE),
+    (dict(tree=_tree(b=64, lv=2, L=1), beam=5), _lib.TIS_E_UNSUPPORTED),
+    (dict(scale=float("nan")), _lib.TIS_E_SHAPE),
+    (dict(V=FAKE + 4), _lib.TIS_E_ALIGN),
+    (dict(idx=FAKE + 2), _lib.TIS_E_ALIGN),
+])
+def test_decode_rejects(lib, kw, status):
+    assert _decode(lib, **kw) == status
     assert lib.tis_last_error().decode()

@@ -51,9 +51,10 @@ def run_gpu(t, w, x, oracle_idx=None):
     if oracle_idx is not None:
         oi = torch.from_numpy(np.ascontiguousarray(oracle_idx, dtype=np.int32)).to(dev)
         res["out_oracle_idx"] = t.tree_attend(Q, K, V, oi, w.leaf_block)
+    res["fused_out"], res["fused_idx"] = t.tree_decode(Q, K, V, tree, w.beam, return_indices=True)
     torch.cuda.synchronize()
     res["levels"] = [tree.level(l).cpu().numpy() for l in range(1, w.levels + 1)]
-    for k in ("idx", "trace", "out", "out_oracle_idx"):
+    for k in ("idx", "trace", "out", "out_oracle_idx", "fused_out", "fused_idx"):
         if k in res:
             res[k] = res[k].cpu().numpy()
     return res
@@ -78,9 +79,12 @@ def check_case(t, w, x=None, label=""):
     # every query's output is also checked on the leaves the GPU chose
     o_g = O.tree_attend(x["Q"], x["K"], x["V"], w.dtype, g["idx"], w.leaf_block)
     err2 = parity.compare_outputs(g["out"], o_g, w.dtype)
+    # the fused decode keeps the same leaves and attends over them
+    assert np.array_equal(g["fused_idx"], g["idx"]), "fused decode kept other leaves"
+    err3 = parity.compare_outputs(g["fused_out"], o_g, w.dtype)
     _say(f"{label or w.name}: summaries bit-equal {eq}/{tot} (worst {worst} ulp); "
          f"indices exact {exact}/{nq}, tie-exposed mismatches {tie}; "
-         f"attend max-abs {err1:.2e} (oracle idx) {err2:.2e} (gpu idx); "
+         f"attend max-abs {err1:.2e} (oracle idx) {err2:.2e} (gpu idx) {err3:.2e} (fused); "
          f"min cut gap {float(np.min(orr['gap'])):.2e}; {time.time() - t0:.1f}s")
     return x, ob, orr, g
 

@@ -6,6 +6,6 @@ exact softmax attention over the keys of its selected leaf blocks
 ("Subquadratic Attention with a Hierarchical Tree-Structured Indexer",
 Abstract).  The three calls run as hand-written HIP kernels in libtis.so.
 """
-from .ops import (Tree, tree_build, tree_route, tree_attend, decode, version,  # noqa: F401
-                  from_storage, DecodePlan)
+from .ops import (Tree, tree_build, tree_route, tree_attend, tree_decode, decode,  # noqa: F401
+                  version, from_storage, DecodePlan)
 from ._lib import TisError  # noqa: F401

@@ -1,0 +1,161 @@
+// Exact softmax attention of one query over a set of leaf blocks, as a
+// device function shared by the attend kernel and the fused decode kernel
+// ("Subquadratic Attention with a Hierarchical Tree-Structured Indexer",
+// Abstract: the final attention over the retrieved keys; the NSA / InfLLMv2
+// abstract on the Progressive Sparse Attention related-papers page: fine
+// softmax attention on the selected tokens).
+//
+// Gather flash-decode inside one workgroup.  The query's work is cut into
+// units of RB rows of one leaf block; each wave takes units in turn, issues
+// the unit's K and V loads together (16 bytes per lane, whole 256-byte rows
+// per lane group), and keeps an online softmax (m, l, acc) in fp32.  The
+// waves' partials meet in LDS and are merged by log-sum-exp.
+#pragma once
+
+#include "tis_device.hpp"
+#include "tis_internal.hpp"
+
+namespace tis {
+
+template <typename T, int D> struct AttendGeom {
+  using G = RowGeom<T, D>;
+  static constexpr int E = G::kElemsPerLane;
+  static constexpr int LPR = G::kLanesPerRow;
+  static constexpr int R = G::kRowsPerInstr;
+  static constexpr int U = 8;       // K loads (and V loads) per lane per unit
+  static constexpr int RB = U * R;  // rows per unit
+  static constexpr int REP = LPR / U;
+  static_assert(U <= LPR, "a unit's scores must fit one reduction");
+};
+
+template <typename T, int D> struct AttendShared {
+  float p[kAttendMaxWaves][AttendGeom<T, D>::RB];
+  float m[kAttendMaxWaves], l[kAttendMaxWaves];
+  float acc[kAttendMaxWaves][D];
+};
+
+// This lane's part of the query row in the attend layout (E elements).
+template <typename T, int D> __device__ inline uint4 attend_q_raw(const AttendArgs &a, int64_t qi) {
+  constexpr int LPR = AttendGeom<T, D>::LPR, E = AttendGeom<T, D>::E;
+  const int lane = threadIdx.x & 63;
+  return load16(static_cast<const T *>(a.Q) + qi * D + (lane % LPR) * E);
+}
+
+// Attention of query qi over the leaf blocks slots[s] (s < nslots) whose
+// use[s] is nonzero (use == nullptr: all), every wave of the workgroup
+// taking part; writes row qi of O (NaN if `bad`, zero if no slot is used).
+template <typename T, int D>
+__device__ void attend_query(const AttendArgs &a, AttendShared<T, D> &sh, int64_t qi,
+                             uint4 qraw, const int *slots, const int *use, int nslots,
+                             bool bad) {
+  using AG = AttendGeom<T, D>;
+  constexpr int E = AG::E, LPR = AG::LPR, R = AG::R, U = AG::U, RB = AG::RB, REP = AG::REP;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int nw = blockDim.x >> 6;
+  const int L = a.leaf_block;
+  const int64_t bi = qi / a.q_heads;
+  const int hq = static_cast<int>(qi - bi * a.q_heads);
+  const int64_t head = bi * a.kv_heads + hq / a.group;
+  const int col = (lane % LPR) * E;
+  const int rsub = lane / LPR;
+
+  float q[E];
+  Vec16<T>::unpack(qraw, q);
+  const T *kh = static_cast<const T *>(a.K) + head * a.n_keys * D + col;
+  const T *vh = static_cast<const T *>(a.V) + head * a.n_keys * D + col;
+  const int nc = (L + RB - 1) / RB;
+  const int units = nslots * nc;
+
+  float m = -INFINITY, l = 0.f;
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+
+  for (int u = w; u < units; u += nw) {
+    const int s = u / nc;
+    if (use && !use[s]) continue;
+    const int r0 = (u - s * nc) * RB;
+    const int64_t rowb = static_cast<int64_t>(slots[s]) * L + r0;
+    uint4 kv[U], vv[U];
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      const int row = r0 + i * R + rsub;
+      kv[i] = row < L ? load16(kh + (rowb + i * R + rsub) * D) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      const int row = r0 + i * R + rsub;
+      vv[i] = row < L ? load16(vh + (rowb + i * R + rsub) * D) : make_uint4(0u, 0u, 0u, 0u);
+    }
+    float part[U];
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      float k[E];
+      Vec16<T>::unpack(kv[i], k);
+      float dot = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) dot = fmaf(q[e], k[e], dot);
+      part[i] = dot;
+    }
+    // lane holds the score of row r0 + kk * R + rsub
+    const float sc = group_transpose_reduce<U, LPR>(part, lane);
+    const int kk = (lane % LPR) / REP;
+    const bool valid = r0 + kk * R + rsub < L;
+    const float x = valid ? sc * a.scale_log2 : -INFINITY;
+    const float mnew = fmaxf(m, wave_max(x));
+    const float p = valid ? exp2f(x - mnew) : 0.f;
+    const float alpha = exp2f(m - mnew);
+    l = l * alpha + wave_sum((lane % REP) == 0 ? p : 0.f);
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] *= alpha;
+    m = mnew;
+    // hand the probabilities to the lanes holding the matching V rows
+    if ((lane % REP) == 0) sh.p[w][rsub * U + kk] = p;
+    __builtin_amdgcn_wave_barrier();
+    float pr[U];
+#pragma unroll
+    for (int i = 0; i < U; ++i) pr[i] = sh.p[w][rsub * U + i];
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      float v[E];
+      Vec16<T>::unpack(vv[i], v);
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] = fmaf(pr[i], v[e], acc[e]);
+    }
+  }
+  // rows were spread over the R lane groups of the wave
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = group_sum<LPR, 32>(acc[e], lane);
+  if (lane < LPR) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) sh.acc[w][col + e] = acc[e];
+  }
+  if (lane == 0) {
+    sh.m[w] = m;
+    sh.l[w] = l;
+  }
+  __syncthreads();
+
+  // ---- log-sum-exp merge of the waves' partials, one column per thread
+  for (int c = tid; c < D; c += blockDim.x) {
+    float mx = -INFINITY;
+    for (int j = 0; j < nw; ++j) mx = fmaxf(mx, sh.m[j]);
+    float r = 0.f;
+    if (mx != -INFINITY) {
+      float num = 0.f, den = 0.f;
+      for (int j = 0; j < nw; ++j) {
+        const float wj = exp2f(sh.m[j] - mx);  // 0 for waves that saw no key
+        den = fmaf(wj, sh.l[j], den);
+        num = fmaf(wj, sh.acc[j][c], num);
+      }
+      r = num / den;
+    }
+    if (bad) r = NAN;
+    a.O[qi * D + c] = r;
+  }
+}
+
+}  // namespace tis

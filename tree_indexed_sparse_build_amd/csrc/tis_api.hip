@@ -292,6 +292,72 @@ tis_status tis_tree_attend(const void *Q, const void *K, const void *V, tis_dtyp
                     "tis_tree_attend launch");
 }
 
+tis_status tis_tree_decode(const void *Q, const void *K, const void *V, tis_dtype dtype,
+                           int q_heads, const tis_tree *tree, int beam, float scale, float *O,
+                           int32_t *indices, void *stream) {
+  if (!Q || !K || !V || !tree || !tree->summaries || !O)
+    return fail(TIS_E_NULL, "tis_tree_decode: Q, K, V, tree, tree->summaries and O are required");
+  tis_status st = check_dtype(dtype);
+  if (st != TIS_OK) return st;
+  Geometry g;
+  st = check_tree(tree->batch, tree->kv_heads, tree->n_keys, tree->head_dim, tree->branching,
+                  tree->leaf_block, tree->levels, &g);
+  if (st != TIS_OK) return st;
+  if (q_heads < 1 || q_heads % tree->kv_heads != 0)
+    return fail(TIS_E_SHAPE, "tis_tree_decode: q_heads %d is not a positive multiple of kv_heads %d",
+                q_heads, tree->kv_heads);
+  const int64_t leaves = g.n_at[tree->levels];
+  if (beam < 1 || beam > leaves)
+    return fail(TIS_E_SHAPE, "tis_tree_decode: beam %d outside [1, %lld]", beam, (long long)leaves);
+  if (static_cast<int64_t>(beam) * tree->branching > TIS_MAX_CANDIDATES)
+    return fail(TIS_E_UNSUPPORTED, "tis_tree_decode: beam * branching = %lld > %d",
+                (long long)beam * tree->branching, TIS_MAX_CANDIDATES);
+  if (!(scale == scale) || isinf(scale))
+    return fail(TIS_E_SHAPE, "tis_tree_decode: scale must be finite");
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) ||
+      !aligned(tree->summaries, 16) || (indices && !aligned(indices, 4)))
+    return fail(TIS_E_ALIGN, "tis_tree_decode: Q, K, V, O and summaries need 16-byte alignment");
+  const int64_t queries = static_cast<int64_t>(tree->batch) * q_heads;
+  if (queries > 0x7fffffffLL) return fail(TIS_E_UNSUPPORTED, "tis_tree_decode: too many queries");
+
+  tis::RouteArgs ra{};
+  ra.Q = Q;
+  ra.summ = tree->summaries;
+  ra.indices = indices;
+  ra.trace = nullptr;
+  ra.queries = queries;
+  ra.q_heads = q_heads;
+  ra.kv_heads = tree->kv_heads;
+  ra.group = q_heads / tree->kv_heads;
+  ra.branching = tree->branching;
+  ra.levels = tree->levels;
+  ra.beam = beam;
+  for (int l = 0; l <= tis::kMaxLevels; ++l) {
+    ra.n_at[l] = g.n_at[l];
+    ra.summ_off[l] = g.summ_off[l];
+  }
+  const double sc =
+      scale > 0.f ? static_cast<double>(scale) : 1.0 / sqrt(static_cast<double>(tree->head_dim));
+  tis::AttendArgs aa{};
+  aa.Q = Q;
+  aa.K = K;
+  aa.V = V;
+  aa.indices = nullptr;
+  aa.O = O;
+  aa.queries = queries;
+  aa.n_keys = tree->n_keys;
+  aa.q_heads = q_heads;
+  aa.kv_heads = tree->kv_heads;
+  aa.group = q_heads / tree->kv_heads;
+  aa.leaf_block = tree->leaf_block;
+  aa.beam = beam;
+  aa.n_blocks = tree->n_keys / tree->leaf_block;
+  aa.scale_log2 = static_cast<float>(sc * 1.4426950408889634);
+  const tis::Dt dt = dtype == TIS_BF16 ? tis::Dt::BF16 : tis::Dt::F32;
+  return hip_status(tis::launch_decode(dt, tree->head_dim, ra, aa, static_cast<hipStream_t>(stream)),
+                    "tis_tree_decode launch");
+}
+
 const char *tis_last_error(void) { return g_err; }
 
 const char *tis_version(void) { return "tis 0.1.0 gfx950"; }

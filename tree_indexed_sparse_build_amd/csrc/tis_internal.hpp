@@ -91,6 +91,11 @@ struct AttendArgs {
 int attend_waves(int head_dim, Dt dt, int beam, int leaf_block);
 hipError_t launch_attend(Dt dt, int head_dim, const AttendArgs &a, hipStream_t s);
 
+// ---------------------------------------------------------------- decode --
+// Route and attend of each query in one workgroup (one launch).
+hipError_t launch_decode(Dt dt, int head_dim, const RouteArgs &ra, const AttendArgs &aa,
+                         hipStream_t s);
+
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace tis

@@ -17,7 +17,8 @@ from ._lib import TisTree, check, lib
 
 _DTYPES = {torch.float32: _lib.TIS_F32, torch.bfloat16: _lib.TIS_BF16}
 
-__all__ = ["Tree", "DecodePlan", "tree_build", "tree_route", "tree_attend", "decode", "version", "from_storage",
+__all__ = ["Tree", "DecodePlan", "tree_build", "tree_route", "tree_attend", "tree_decode",
+           "decode", "version", "from_storage",
            "summary_offsets"]
 
 
@@ -159,12 +160,36 @@ def tree_attend(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, indices: torc
     return O
 
 
+def tree_decode(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, tree: Tree, beam: int,
+                scale: Optional[float] = None, return_indices: bool = False):
+    """Route and attend every query in one launch.  Returns O (float32
+    [B, Hq, d]), and with return_indices=True also the kept leaves (int32
+    [B, Hq, beam], ascending, the same as tree_route's)."""
+    _need_device(Q, K, V, tree.summaries)
+    if K.dtype != Q.dtype or V.dtype != Q.dtype:
+        raise TypeError("Q, K and V must share one dtype")
+    B, Hq, d = Q.shape
+    if (B, d) != (tree.batch, tree.head_dim) or tuple(K.shape) != (
+            tree.batch, tree.kv_heads, tree.n_keys, tree.head_dim) or V.shape != K.shape:
+        raise ValueError("Q, K, V do not match the tree")
+    O = torch.empty((B, Hq, d), dtype=torch.float32, device=Q.device)
+    idx = (torch.empty((B, Hq, beam), dtype=torch.int32, device=Q.device)
+           if return_indices else None)
+    t = tree.c_struct()
+    check(lib().tis_tree_decode(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q), Hq,
+                                ctypes.byref(t), beam, 0.0 if scale is None else float(scale),
+                                O.data_ptr(), idx.data_ptr() if idx is not None else None,
+                                _stream(Q.device)))
+    return (O, idx) if return_indices else O
+
+
 def decode(Q, K, V, branching: int, leaf_block: int, levels: int, beam: int,
            scale: Optional[float] = None):
-    """Build, route and attend on the current stream (no host sync between)."""
+    """Build, then one fused decode step, on the current stream (no host sync
+    between).  Returns (tree, indices, O)."""
     tree = tree_build(K, branching, leaf_block, levels)
-    idx = tree_route(Q, tree, beam)
-    return tree, idx, tree_attend(Q, K, V, idx, leaf_block, scale)
+    out, idx = tree_decode(Q, K, V, tree, beam, scale, return_indices=True)
+    return tree, idx, out
 
 
 def version() -> str:
@@ -239,6 +264,14 @@ class DecodePlan:
                                         else self.ws_attend.data_ptr(),
                                         0 if self.ws_attend is None
                                         else self.ws_attend.numel(), self.stream))
+
+    def decode(self) -> None:
+        """Route and attend in one launch (indices not written)."""
+        B, H, N, d, b, Lb, lv = self.geom
+        check(self._lib.tis_tree_decode(self.Q.data_ptr(), self.K.data_ptr(), self.V.data_ptr(),
+                                        self.dt, self.q_heads, ctypes.byref(self.tree_c),
+                                        self.beam, self.scale, self.out.data_ptr(), None,
+                                        self.stream))
 
     def tree(self) -> Tree:
         B, H, N, d, b, Lb, lv = self.geom
