@@ -51,7 +51,6 @@ template <> __device__ inline void load_q<bf16_bits, 64>(const bf16_bits *q, int
 // Shared memory of one query's walk, for a workgroup of NW waves.
 template <int NW> struct RouteShared {
   uint64_t keys[kMaxCandidates];
-  int pcnt[NW * 64];               // partial rank counts, one per thread
   int cand[2][kMaxCandidates];     // node id of every candidate, this level / next
   int front[kMaxCandidates];       // kept nodes of the level, in rank order
 };
@@ -143,42 +142,42 @@ __device__ void route_walk(const RouteArgs &a, RouteShared<NW> &sh, int64_t qi) 
           sh.keys[pos] = score_key(s, all ? pos : sh.cand[cur][pos], bits);
       }
       __syncthreads();
-      // rank of candidate i = number of candidates with a larger key.
-      // Threads form `parts` groups of cp (the power of two >= C); group p
-      // compares every candidate with one slice of the keys.
-      const int lcp = 32 - __clz(C - 1);
-      const int lparts = min(LOG_NT - lcp, 3);
-      const int span = (((C + (1 << lparts) - 1) >> lparts) + 7) & ~7;
+      // rank of candidate i = number of candidates with a larger key.  Each
+      // candidate has a group of g adjacent lanes (g <= 8); lane p of the
+      // group counts over keys p, p+g, p+2g, ... (so the g lanes read g
+      // neighbouring keys: no bank conflict, and every group of the wave
+      // reads the same addresses), then the group adds its counts with DPP,
+      // so the ranks need no further trip through LDS.
       {
-        const int i = tid & ((1 << lcp) - 1);
-        const int part = tid >> lcp;
+        const int lcp = 32 - __clz(C - 1);
+        const int lg = min(LOG_NT - lcp, 3);
+        const int g = 1 << lg;
+        const int i = tid >> lg;
+        const int part = tid & (g - 1);
         int cnt = 0;
-        if (i < C && part < (1 << lparts)) {
+        if (i < C) {
           const uint64_t ki = sh.keys[i];
-          int j = part * span;
-          const int j1 = min(C, j + span);
-          for (; j + 8 <= j1; j += 8) {
+          int j = part;
+          for (; j + 7 * g < C; j += 8 * g) {
             uint64_t kj[8];
 #pragma unroll
-            for (int t = 0; t < 8; ++t) kj[t] = sh.keys[j + t];
+            for (int t = 0; t < 8; ++t) kj[t] = sh.keys[j + t * g];
 #pragma unroll
             for (int t = 0; t < 8; ++t) cnt += kj[t] > ki ? 1 : 0;
           }
-          for (; j < j1; ++j) cnt += sh.keys[j] > ki ? 1 : 0;
+          for (; j < C; j += g) cnt += sh.keys[j] > ki ? 1 : 0;
         }
-        sh.pcnt[tid] = cnt;
-      }
-      __syncthreads();
-      // the W best go to front[] at their rank; their children, in the same
-      // order, are the next level's candidates
-      if (tid < C) {
-        int r = 0;
-        for (int p = 0; p < (1 << lparts); ++p) r += sh.pcnt[(p << lcp) + tid];
-        if (r < W) {
-          const int node = all ? tid : sh.cand[cur][tid];
-          sh.front[r] = node;
+        // g is uniform: every lane of the wave takes the same branches
+        if (g >= 2) cnt = xor_sum<1>(cnt, lane);
+        if (g >= 4) cnt = xor_sum<2>(cnt, lane);
+        if (g >= 8) cnt = xor_sum<4>(cnt, lane);
+        // the W best go to front[] at their rank; their children, in the
+        // same order, are the next level's candidates
+        if (i < C && part == 0 && cnt < W) {
+          const int node = all ? i : sh.cand[cur][i];
+          sh.front[cnt] = node;
           if (l < lv) {
-            for (int c = 0; c < b; ++c) sh.cand[cur ^ 1][r * b + c] = node * b + c;
+            for (int c = 0; c < b; ++c) sh.cand[cur ^ 1][cnt * b + c] = node * b + c;
           }
         }
       }

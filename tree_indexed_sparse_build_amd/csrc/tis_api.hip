@@ -150,6 +150,10 @@ tis_status tis_tree_build(const void *K, tis_dtype dtype, int batch, int kv_head
   a.levels = levels;
   a.root_level = p.root_level;
   a.wave_depth = p.wave_depth;
+  a.stream_loads = static_cast<double>(heads) * n_keys * head_dim * (dtype == TIS_BF16 ? 2 : 4) >
+                   static_cast<double>(tis::kStreamLoadBytes);
+  a.top_rows = 1;
+  for (int l = 2; l < p.root_level; ++l) a.top_rows *= branching;
   a.wave_leaves = 1;
   for (int i = 0; i < p.wave_depth; ++i) a.wave_leaves *= branching;
   a.pow2_levels = 0;

@@ -42,6 +42,13 @@ __device__ inline uint4 load16(const void *p) {
   return *reinterpret_cast<const uint4 *>(p);
 }
 
+// 16-byte load with the non-temporal (streaming) hint.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ inline uint4 load16_stream(const void *p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Row geometry for a wave reading rows of D elements of T, 16 bytes per lane:
 // kLanesPerRow lanes cover one row; one wave-wide load covers kRowsPerInstr
 // consecutive rows.
@@ -80,6 +87,9 @@ template <int M> __device__ inline uint32_t xor_lane(uint32_t v, int lane) {
     const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
     return (lane & 32) ? p[0] : p[1];
   }
+}
+template <int M> __device__ inline int xor_lane(int v, int lane) {
+  return static_cast<int>(xor_lane<M>(static_cast<uint32_t>(v), lane));
 }
 template <int M> __device__ inline float xor_lane(float v, int lane) {
   return __uint_as_float(xor_lane<M>(__float_as_uint(v), lane));

@@ -21,6 +21,8 @@ enum class Dt : int { F32 = 0, BF16 = 1 };
 // levels in LDS.  When r >= 2 the chunk roots leave fp64 sums in the
 // workspace and one small kernel per level computes levels r-1 .. 1.
 constexpr int kMaxWaveDepth = 3;
+constexpr size_t kTopLdsBytes = 64 * 1024;     // LDS budget of the one-launch top levels
+constexpr size_t kStreamLoadBytes = 384u << 20;  // K larger than this: streaming loads
 
 struct BuildArgs {
   const void *K;
@@ -33,6 +35,8 @@ struct BuildArgs {
   int root_level;        // r
   int wave_depth;        // kw
   uint32_t pow2_levels;  // bit l set: M_l = N / n_l is a power of two
+  int stream_loads;      // nonzero: K loads carry the non-temporal hint
+  int64_t top_rows;      // b^(r-2): level r-1 nodes under one level-1 node
   int64_t n_at[kMaxLevels + 1];            // b^l
   int64_t chunks_at_level[kMaxLevels + 1]; // B*Hkv*b^l
   int64_t summ_off[kMaxLevels + 1];        // element offset of level l in summ
