@@ -68,7 +68,7 @@ template <typename T, int D> __global__ void __launch_bounds__(1024) k_build(Bui
   constexpr int LPR = G::kLanesPerRow;
   constexpr int R = G::kRowsPerInstr;
   constexpr int CPL = E / R;  // finished columns per lane (D / 64)
-  constexpr int U = 16;       // 16-byte loads in flight per lane
+  constexpr int U = 8;        // 16-byte loads per lane per batch (two batches in flight)
   static_assert(CPL * 64 == D, "one finished column block per lane");
   extern __shared__ double lds[];
 
@@ -109,28 +109,44 @@ template <typename T, int D> __global__ void __launch_bounds__(1024) k_build(Bui
       nid[k] = n;
     }
   }
-  for (int64_t c = 0; c < a.wave_leaves; ++c) {
-    const int64_t leaf = leaf0 + c;
-    const T *kl = kh + leaf * static_cast<int64_t>(L) * D;
-    double acc[E];
+  // The wave's leaves are streamed as one sequence of batches of U*R rows
+  // (nb batches per leaf).  Loads are double-buffered: the next batch is in
+  // flight while the current one is added up and, at a leaf's end, reduced.
+  const int nb = (L + U * R - 1) / (U * R);
+  int64_t lc = 0;  // leaf / batch of the next load
+  int lb = 0;
+  int64_t cc = 0;  // leaf / batch being added up
+  int cb = 0;
+  auto issue = [&](uint4 (&v)[U]) {
+    const T *kl = kh + (leaf0 + lc) * static_cast<int64_t>(L) * D;
+    const int r0 = lb * U * R;
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = 0.0;
-    for (int r0 = 0; r0 < L; r0 += U * R) {
-      uint4 v[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int row = r0 + u * R + rsub;
-        const T *p = kl + static_cast<int64_t>(row) * D;
-        v[u] = row >= L ? make_uint4(0u, 0u, 0u, 0u) : a.stream_loads ? load16_stream(p) : load16(p);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        float f[E];
-        Vec16<T>::unpack(v[u], f);
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] += static_cast<double>(f[e]);
-      }
+    for (int u = 0; u < U; ++u) {
+      const int row = r0 + u * R + rsub;
+      const T *p = kl + static_cast<int64_t>(row) * D;
+      v[u] = row >= L ? make_uint4(0u, 0u, 0u, 0u) : a.stream_loads ? load16_stream(p) : load16(p);
     }
+    if (++lb == nb) {
+      lb = 0;
+      ++lc;
+    }
+  };
+  double acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.0;
+  auto consume = [&](const uint4 (&v)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float f[E];
+      Vec16<T>::unpack(v[u], f);
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] += static_cast<double>(f[e]);
+    }
+    if (++cb < nb) return;
+    // ---- leaf cc complete
+    cb = 0;
+    const int64_t leaf = leaf0 + cc;
+    ++cc;
     rowgroup_steps<E, LPR, 32, 0>(acc, lane);
     {
       float f[CPL];
@@ -141,6 +157,8 @@ template <typename T, int D> __global__ void __launch_bounds__(1024) k_build(Bui
     double carry[CPL];
 #pragma unroll
     for (int j = 0; j < CPL; ++j) carry[j] = root[j] = acc[j];
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = 0.0;
     // close every level whose node this leaf completes
 #pragma unroll
     for (int k = 0; k < kMaxWaveDepth; ++k) {
@@ -163,6 +181,18 @@ template <typename T, int D> __global__ void __launch_bounds__(1024) k_build(Bui
       ctr[k] = 0;
       ++nid[k];
     }
+  };
+  uint4 va[U], vb[U];
+  issue(va);
+  while (true) {
+    bool more = lc < a.wave_leaves;
+    if (more) issue(vb);
+    consume(va);
+    if (!more) break;
+    more = lc < a.wave_leaves;
+    if (more) issue(va);
+    consume(vb);
+    if (!more) break;
   }
 
   // ---- the workgroup's inner levels, from the waves' fp64 root sums in LDS
