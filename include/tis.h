@@ -37,14 +37,14 @@
  *   status of the calling thread.  No C++ exception crosses this interface.
  *
  * Workspaces
- *   tis_tree_build takes a caller-owned device workspace of at least the size
- *   tis_build_workspace_bytes returns (0 when the tree is shallow enough for
- *   one kernel; then NULL is accepted).  It holds fp64 node sums passed
- *   between the build's two kernels; its contents on entry do not matter.
- *   Calls that share a workspace must be ordered (same stream or
- *   synchronised).  tis_tree_attend keeps workspace arguments for a split
- *   mode; this version needs none (tis_attend_workspace_bytes returns 0) and
- *   ignores them.
+ *   tis_tree_build, tis_tree_attend and tis_tree_decode take a caller-owned
+ *   device workspace (16-byte aligned) of at least the size the matching
+ *   *_workspace_bytes query returns.  A size of 0 means none is needed and
+ *   NULL is accepted.  The build keeps fp64 node sums there when its second
+ *   kernel runs.  Attend and decode keep partial softmax states there when a
+ *   query is split over several workgroups (few queries, long key sets).
+ *   Contents on entry never matter.  Calls that share a workspace must be
+ *   ordered (same stream or synchronised).
  */
 #ifndef TIS_H_
 #define TIS_H_
@@ -125,8 +125,7 @@ tis_status tis_tree_route(const void *Q, tis_dtype dtype, int q_heads,
                           const tis_tree *tree, int beam, int32_t *indices,
                           int32_t *trace, void *stream);
 
-/* Bytes of workspace tis_tree_attend needs for this geometry: 0 in this
- * version, which finishes each query inside one workgroup. */
+/* Bytes of workspace tis_tree_attend needs for this geometry (0: none). */
 size_t tis_attend_workspace_bytes(int batch, int q_heads, int head_dim, int beam,
                                   int leaf_block);
 
@@ -145,7 +144,7 @@ size_t tis_attend_workspace_bytes(int batch, int q_heads, int head_dim, int beam
  *          rejected (TIS_E_SHAPE).
  * O        out: float32 [B][Hq][d], o = sum_t softmax(scale*q.k_t) v_t over
  *          the union of the selected blocks; fp32 accumulation.
- * workspace, workspace_bytes: unused in this version (may be NULL / 0).
+ * workspace, workspace_bytes: see Workspaces (tis_attend_workspace_bytes).
  * Requires N % L == 0 and 1 <= beam <= TIS_MAX_CANDIDATES.
  */
 tis_status tis_tree_attend(const void *Q, const void *K, const void *V, tis_dtype dtype,
@@ -166,11 +165,17 @@ tis_status tis_tree_attend(const void *Q, const void *K, const void *V, tis_dtyp
  * indices  optional (NULL to skip): int32 [B][Hq][beam], the kept leaves in
  *          ascending order.
  * scale    softmax scale; <= 0 selects 1/sqrt(d); NaN or infinite rejected.
+ * workspace, workspace_bytes: see Workspaces (tis_decode_workspace_bytes).
  * Requires 1 <= beam <= b^lv and beam * b <= TIS_MAX_CANDIDATES.
  */
 tis_status tis_tree_decode(const void *Q, const void *K, const void *V, tis_dtype dtype,
                            int q_heads, const tis_tree *tree, int beam, float scale, float *O,
-                           int32_t *indices, void *stream);
+                           int32_t *indices, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/* Bytes of workspace tis_tree_decode needs for this geometry (0: none). */
+size_t tis_decode_workspace_bytes(int batch, int q_heads, int head_dim, int beam,
+                                  int leaf_block);
 
 /* Message for the last non-OK status returned on the calling thread. */
 const char *tis_last_error(void);

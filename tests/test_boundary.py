@@ -58,8 +58,16 @@ def test_workspace_bytes(lib):
     assert lib.tis_build_workspace_bytes(1, 1, 64, 128, 16, 4, 1) == 0
     # invalid geometry -> 0
     assert lib.tis_build_workspace_bytes(4, 8, 1000, 128, 8, 64, 3) == 0
-    # attend finishes each query inside one workgroup: no workspace
+    # attend and decode: 128 queries run one workgroup each, no workspace
     assert lib.tis_attend_workspace_bytes(4, 32, 128, 8, 64) == 0
+    assert lib.tis_decode_workspace_bytes(4, 32, 128, 8, 64) == 0
+    # 32 queries with 512 keys each: still one workgroup per query
+    assert lib.tis_attend_workspace_bytes(1, 32, 128, 16, 32) == 0
+    # 32 queries with 64 x 64 keys each: 8 workgroups per query keep partial states
+    assert lib.tis_attend_workspace_bytes(1, 32, 128, 64, 64) == 32 * 8 * (128 + 4) * 4
+    assert lib.tis_decode_workspace_bytes(1, 32, 128, 64, 64) == 32 * 8 * (128 + 4) * 4
+    # a short key set is never split
+    assert lib.tis_attend_workspace_bytes(1, 4, 64, 2, 16) == 0
 
 
 FAKE = 0x10000  # 16-byte aligned, never dereferenced: each call fails a check first
@@ -164,6 +172,9 @@ def _attend(lib, **kw):
     (dict(K=FAKE + 8), _lib.TIS_E_ALIGN),
     (dict(O=FAKE + 4), _lib.TIS_E_ALIGN),
     (dict(idx=FAKE + 2), _lib.TIS_E_ALIGN),
+    # 4 queries with 64 x 64 keys each: split, so a workspace is needed
+    (dict(B=1, Hq=4, Hkv=2, N=4096, L=64, beam=64, ws=None), _lib.TIS_E_NULL),
+    (dict(B=1, Hq=4, Hkv=2, N=4096, L=64, beam=64, ws=FAKE, wsb=100), _lib.TIS_E_WORKSPACE),
 ])
 def test_attend_rejects(lib, kw, status):
     assert _attend(lib, **kw) == status
@@ -171,9 +182,10 @@ def test_attend_rejects(lib, kw, status):
 
 
 def _decode(lib, Q=FAKE, K=FAKE, V=FAKE, dt=_lib.TIS_BF16, Hq=2, tree=None, beam=2, scale=0.0,
-            O=FAKE, idx=None):
+            O=FAKE, idx=None, ws=None, wsb=0):
     t = tree if tree is not None else _tree(H=1)
-    return lib.tis_tree_decode(Q, K, V, dt, Hq, ctypes.byref(t), beam, scale, O, idx, None)
+    return lib.tis_tree_decode(Q, K, V, dt, Hq, ctypes.byref(t), beam, scale, O, idx, ws, wsb,
+                               None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -188,6 +200,11 @@ def _decode(lib, Q=FAKE, K=FAKE, V=FAKE, dt=_lib.TIS_BF16, Hq=2, tree=None, beam
     (dict(scale=float("nan")), _lib.TIS_E_SHAPE),
     (dict(V=FAKE + 4), _lib.TIS_E_ALIGN),
     (dict(idx=FAKE + 2), _lib.TIS_E_ALIGN),
+    # 2 queries, beam 64 over leaves of 64 keys: split, so a workspace is needed
+    (dict(tree=_tree(b=4, lv=4, L=64, d=128), beam=64, Hq=2), _lib.TIS_E_NULL),
+    (dict(tree=_tree(b=4, lv=4, L=64, d=128), beam=64, Hq=2, ws=FAKE, wsb=16), _lib.TIS_E_WORKSPACE),
+    (dict(tree=_tree(b=4, lv=4, L=64, d=128), beam=64, Hq=2, ws=FAKE + 8, wsb=1 << 20),
+     _lib.TIS_E_ALIGN),
 ])
 def test_decode_rejects(lib, kw, status):
     assert _decode(lib, **kw) == status

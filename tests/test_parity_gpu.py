@@ -130,6 +130,10 @@ EDGE = [
     _custom("deep_binary", "bf16", 2, 4, 9, 6, d=64, Hkv=3, G=1),
     # many heads, GQA group 8, batch 3
     _custom("gqa8_batch3", "bf16", 4, 32, 3, 6, B=3, Hkv=2, G=8),
+    # few queries with long key sets: each query split over several
+    # workgroups (64 x 64 keys, 6 queries -> 32 parts each), merged after
+    _custom("split_long_gather", "bf16", 4, 64, 4, 64, Hkv=2, G=3),
+    _custom("split_long_gather_f32", "f32", 8, 128, 2, 32, d=64, Hkv=1, G=2),
 ]
 
 

@@ -51,7 +51,8 @@ SIGNATURES = {
     "tis_tree_attend": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                  _c_int, _vp, _c_int, _c_float, _vp, _vp, _c_size, _vp]),
     "tis_tree_decode": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, ctypes.POINTER(TisTree), _c_int,
-                                 _c_float, _vp, _vp, _vp]),
+                                 _c_float, _vp, _vp, _vp, _c_size, _vp]),
+    "tis_decode_workspace_bytes": (_c_size, [_c_int] * 5),
     "tis_last_error": (ctypes.c_char_p, []),
     "tis_version": (ctypes.c_char_p, []),
 }

@@ -4,10 +4,12 @@
 // abstract on the Progressive Sparse Attention related-papers page: fine
 // softmax attention on the selected tokens).
 //
-// One workgroup per query: it reads the query's slot list, applies the slot
-// rules (repeats count once, negatives are empty, out-of-range gives NaN)
-// and runs attend_query.  No global workspace, atomics or device-scope
-// fences.
+// One workgroup per query (or, when few queries would leave most CUs idle,
+// `splits` workgroups per query, each on a share of the slots, followed by a
+// small log-sum-exp combine kernel): it reads the query's slot list, applies
+// the slot rules (repeats count once, negatives are empty, out-of-range gives
+// NaN) and runs attend_query.  Parts meet through a kernel boundary, never
+// through atomics or device-scope fences.
 #include "attend_query.hpp"
 
 namespace tis {
@@ -20,15 +22,16 @@ __global__ void __launch_bounds__(kAttendMaxWaves * 64) k_attend(AttendArgs a) {
   __shared__ int s_use[kMaxCandidates];
   __shared__ int s_bad;
   const int tid = threadIdx.x;
-  const int64_t qi = blockIdx.x;
+  // part sp of query qi; the parts of a query are queries apart in the grid,
+  // so with a multiple of 8 queries they land on one XCD and share its L2
+  const int64_t sp = blockIdx.x / a.queries;
+  const int64_t qi = blockIdx.x - sp * a.queries;
   const int W = a.beam;
 
   // the query row and the slot list are loaded before anything waits on them
-  // (the launch gives at least min(W, 16) waves, so tid < W covers W <= 1024)
   const uint4 qraw = attend_q_raw<T, D>(a, qi);
-  const int my_idx = tid < W ? a.indices[qi * W + tid] : -1;
   if (tid == 0) s_bad = 0;
-  if (tid < W) s_idx[tid] = my_idx;
+  for (int s = tid; s < W; s += blockDim.x) s_idx[s] = a.indices[qi * W + s];
   __syncthreads();
   for (int s = tid; s < W; s += blockDim.x) {
     const int idx = s_idx[s];
@@ -39,7 +42,10 @@ __global__ void __launch_bounds__(kAttendMaxWaves * 64) k_attend(AttendArgs a) {
     if (bad) s_bad = 1;
   }
   __syncthreads();
-  attend_query<T, D>(a, sh, qi, qraw, s_idx, s_use, W, s_bad != 0);
+  const int s0 = static_cast<int>(sp * W / a.splits);
+  const int s1 = static_cast<int>((sp + 1) * W / a.splits);
+  float *part = a.splits > 1 ? a.part + (qi * a.splits + sp) * (D + kPartHeader) : nullptr;
+  attend_query<T, D>(a, sh, qi, qraw, s_idx + s0, s_use + s0, s1 - s0, s_bad != 0, part);
 }
 
 }  // namespace
@@ -54,9 +60,34 @@ int attend_waves(int head_dim, Dt dt, int beam, int leaf_block) {
   return static_cast<int>(units < kAttendMaxWaves ? units : kAttendMaxWaves);
 }
 
-hipError_t launch_attend(Dt dt, int head_dim, const AttendArgs &a, hipStream_t s) {
+int attend_splits(int64_t queries, int beam, int leaf_block) {
+  // A split costs one more launch (~4.5 us on MI355X) and pays only when a
+  // query's own gather is long: >= 4096 keys (>= 1 MB of K and V at d = 128
+  // in bf16) and too few queries to give every CU a workgroup.
+  if (queries >= 128 || static_cast<int64_t>(beam) * leaf_block < 4096) return 1;
+  int s = 1;
+  while (s * 2 <= beam && queries * s * 2 <= 256) s *= 2;
+  return s;
+}
+
+size_t attend_workspace(int64_t queries, int head_dim, int splits) {
+  if (splits <= 1) return 0;
+  return static_cast<size_t>(queries) * splits * (head_dim + kPartHeader) * sizeof(float);
+}
+
+hipError_t launch_combine(int head_dim, const AttendArgs &a, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.queries));
-  const dim3 block(static_cast<unsigned>(attend_waves(head_dim, dt, a.beam, a.leaf_block) * 64));
+  if (head_dim == 128)
+    hipLaunchKernelGGL((k_combine<128>), grid, dim3(128), 0, s, a.part, a.O, a.splits);
+  else
+    hipLaunchKernelGGL((k_combine<64>), grid, dim3(64), 0, s, a.part, a.O, a.splits);
+  return hipGetLastError();
+}
+
+hipError_t launch_attend(Dt dt, int head_dim, const AttendArgs &a, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(a.queries * a.splits));
+  const int per = (a.beam + a.splits - 1) / a.splits;
+  const dim3 block(static_cast<unsigned>(attend_waves(head_dim, dt, per, a.leaf_block) * 64));
   if (dt == Dt::BF16 && head_dim == 128)
     hipLaunchKernelGGL((k_attend<bf16_bits, 128>), grid, block, 0, s, a);
   else if (dt == Dt::BF16 && head_dim == 64)
@@ -67,7 +98,9 @@ hipError_t launch_attend(Dt dt, int head_dim, const AttendArgs &a, hipStream_t s
     hipLaunchKernelGGL((k_attend<float, 64>), grid, block, 0, s, a);
   else
     return hipErrorInvalidValue;
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.splits <= 1) return e;
+  return launch_combine(head_dim, a, s);
 }
 
 }  // namespace tis

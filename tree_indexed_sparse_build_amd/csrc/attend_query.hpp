@@ -28,6 +28,8 @@ template <typename T, int D> struct AttendGeom {
   static_assert(U <= LPR, "a unit's scores must fit one reduction");
 };
 
+constexpr int kPartHeader = 4;  // m, l, two pad words: keeps acc 16-byte aligned
+
 template <typename T, int D> struct AttendShared {
   float p[kAttendMaxWaves][AttendGeom<T, D>::RB];
   float m[kAttendMaxWaves], l[kAttendMaxWaves];
@@ -43,11 +45,14 @@ template <typename T, int D> __device__ inline uint4 attend_q_raw(const AttendAr
 
 // Attention of query qi over the leaf blocks slots[s] (s < nslots) whose
 // use[s] is nonzero (use == nullptr: all), every wave of the workgroup
-// taking part; writes row qi of O (NaN if `bad`, zero if no slot is used).
+// taking part.  With part == nullptr it writes row qi of O (NaN if `bad`,
+// zero if no slot is used); otherwise it writes the workgroup's partial
+// softmax state to part: m (log2 units), l (NaN if `bad`), two pad words,
+// acc[D], for a later log-sum-exp merge with the query's other parts.
 template <typename T, int D>
 __device__ void attend_query(const AttendArgs &a, AttendShared<T, D> &sh, int64_t qi,
                              uint4 qraw, const int *slots, const int *use, int nslots,
-                             bool bad) {
+                             bool bad, float *part) {
   using AG = AttendGeom<T, D>;
   constexpr int E = AG::E, LPR = AG::LPR, R = AG::R, U = AG::U, RB = AG::RB, REP = AG::REP;
   const int tid = threadIdx.x;
@@ -143,19 +148,54 @@ __device__ void attend_query(const AttendArgs &a, AttendShared<T, D> &sh, int64_
   for (int c = tid; c < D; c += blockDim.x) {
     float mx = -INFINITY;
     for (int j = 0; j < nw; ++j) mx = fmaxf(mx, sh.m[j]);
-    float r = 0.f;
+    float num = 0.f, den = 0.f;
     if (mx != -INFINITY) {
-      float num = 0.f, den = 0.f;
       for (int j = 0; j < nw; ++j) {
         const float wj = exp2f(sh.m[j] - mx);  // 0 for waves that saw no key
         den = fmaf(wj, sh.l[j], den);
         num = fmaf(wj, sh.acc[j][c], num);
       }
-      r = num / den;
     }
-    if (bad) r = NAN;
-    a.O[qi * D + c] = r;
+    if (part) {
+      part[kPartHeader + c] = num;
+      if (c == 0) {
+        part[0] = mx;
+        part[1] = bad ? NAN : den;
+      }
+    } else {
+      float r = mx == -INFINITY ? 0.f : num / den;
+      if (bad) r = NAN;
+      a.O[qi * D + c] = r;
+    }
   }
+}
+
+// Log-sum-exp merge of each query's `splits` partial states into row qi of
+// O: o = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s, M = max_s m_s;
+// zero if no part saw a key, NaN if any part is NaN.
+template <int D> __global__ void __launch_bounds__(D) k_combine(const float *part, float *O,
+                                                                 int splits) {
+  const int64_t qi = blockIdx.x;
+  const int c = threadIdx.x;
+  const float *pq = part + qi * splits * (D + kPartHeader);
+  float mx = -INFINITY;
+  bool bad = false;
+  for (int s = 0; s < splits; ++s) {
+    mx = fmaxf(mx, pq[s * (D + kPartHeader)]);
+    bad |= isnan(pq[s * (D + kPartHeader) + 1]);
+  }
+  float r = 0.f;
+  if (mx != -INFINITY) {
+    float num = 0.f, den = 0.f;
+    for (int s = 0; s < splits; ++s) {
+      const float *ps = pq + s * (D + kPartHeader);
+      const float ws = exp2f(ps[0] - mx);
+      den = fmaf(ws, ps[1], den);
+      num = fmaf(ws, ps[kPartHeader + c], num);
+    }
+    r = num / den;
+  }
+  O[qi * D + c] = bad ? NAN : r;
 }
 
 }  // namespace tis

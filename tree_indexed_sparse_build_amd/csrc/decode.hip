@@ -6,6 +6,9 @@
 // LDS and attend_query gathers them straight away, so the leaf list never
 // goes through memory and the step pays for one launch instead of two.  The
 // leaves are also written out (ascending) when the caller asks for them.
+// With few queries each query gets `splits` workgroups that all walk the
+// tree and each attend over a share of the kept leaves; a small combine
+// kernel merges their partial softmax states.
 #include "attend_query.hpp"
 #include "route_walk.hpp"
 
@@ -18,18 +21,26 @@ template <typename T, int D>
 __global__ void __launch_bounds__(kDecodeWaves * 64) k_decode(RouteArgs ra, AttendArgs aa) {
   __shared__ RouteShared<kDecodeWaves> rsh;
   __shared__ AttendShared<T, D> ash;
-  const int64_t qi = blockIdx.x;
+  // part sp of query qi (see k_attend: a query's parts share an XCD)
+  const int64_t sp = blockIdx.x / aa.queries;
+  const int64_t qi = blockIdx.x - sp * aa.queries;
   const uint4 qraw = attend_q_raw<T, D>(aa, qi);  // in flight during the walk
+  // every part walks the tree (the repeated summary reads hit the XCD's L2)
   route_walk<T, D, kDecodeWaves>(ra, rsh, qi);
-  if (ra.indices) write_ascending<kDecodeWaves * 64>(rsh.front, ra.beam, ra.indices + qi * ra.beam);
-  attend_query<T, D>(aa, ash, qi, qraw, rsh.front, nullptr, ra.beam, false);
+  if (ra.indices && sp == 0)
+    write_ascending<kDecodeWaves * 64>(rsh.front, ra.beam, ra.indices + qi * ra.beam);
+  const int W = ra.beam;
+  const int s0 = static_cast<int>(sp * W / aa.splits);
+  const int s1 = static_cast<int>((sp + 1) * W / aa.splits);
+  float *part = aa.splits > 1 ? aa.part + (qi * aa.splits + sp) * (D + kPartHeader) : nullptr;
+  attend_query<T, D>(aa, ash, qi, qraw, rsh.front + s0, nullptr, s1 - s0, false, part);
 }
 
 }  // namespace
 
 hipError_t launch_decode(Dt dt, int head_dim, const RouteArgs &ra, const AttendArgs &aa,
                          hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(ra.queries));
+  const dim3 grid(static_cast<unsigned>(ra.queries * aa.splits));
   const dim3 block(kDecodeWaves * 64);
   if (dt == Dt::BF16 && head_dim == 128)
     hipLaunchKernelGGL((k_decode<bf16_bits, 128>), grid, block, 0, s, ra, aa);
@@ -41,7 +52,9 @@ hipError_t launch_decode(Dt dt, int head_dim, const RouteArgs &ra, const AttendA
     hipLaunchKernelGGL((k_decode<float, 64>), grid, block, 0, s, ra, aa);
   else
     return hipErrorInvalidValue;
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || aa.splits <= 1) return e;
+  return launch_combine(head_dim, aa, s);
 }
 
 }  // namespace tis

@@ -238,20 +238,40 @@ tis_status tis_tree_route(const void *Q, tis_dtype dtype, int q_heads, const tis
 }
 
 size_t tis_attend_workspace_bytes(int batch, int q_heads, int head_dim, int beam, int leaf_block) {
-  (void)batch;
-  (void)q_heads;
-  (void)head_dim;
-  (void)beam;
-  (void)leaf_block;
-  return 0;  // each query is finished inside one workgroup
+  if (batch < 1 || q_heads < 1 || (head_dim != 64 && head_dim != 128) || beam < 1 ||
+      leaf_block < 1)
+    return 0;
+  const int64_t queries = static_cast<int64_t>(batch) * q_heads;
+  return tis::attend_workspace(queries, head_dim, tis::attend_splits(queries, beam, leaf_block));
+}
+
+size_t tis_decode_workspace_bytes(int batch, int q_heads, int head_dim, int beam, int leaf_block) {
+  return tis_attend_workspace_bytes(batch, q_heads, head_dim, beam, leaf_block);
+}
+
+// Splits and workspace of an attend or decode call; fails without enqueuing.
+static tis_status plan_split(const char *who, int64_t queries, int head_dim, int beam,
+                             int leaf_block, void *workspace, size_t workspace_bytes,
+                             tis::AttendArgs *a) {
+  a->splits = tis::attend_splits(queries, beam, leaf_block);
+  a->part = nullptr;
+  const size_t need = tis::attend_workspace(queries, head_dim, a->splits);
+  if (need == 0) return TIS_OK;
+  if (!workspace)
+    return fail(TIS_E_NULL, "%s: a workspace of %zu bytes is required", who, need);
+  if (!aligned(workspace, 16))
+    return fail(TIS_E_ALIGN, "%s: workspace must be 16-byte aligned", who);
+  if (workspace_bytes < need)
+    return fail(TIS_E_WORKSPACE, "%s: workspace %zu bytes < %zu required", who, workspace_bytes,
+                need);
+  a->part = static_cast<float *>(workspace);
+  return TIS_OK;
 }
 
 tis_status tis_tree_attend(const void *Q, const void *K, const void *V, tis_dtype dtype, int batch,
                            int q_heads, int kv_heads, int n_keys, int head_dim, int leaf_block,
                            const int32_t *indices, int beam, float scale, float *O,
                            void *workspace, size_t workspace_bytes, void *stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   if (!Q || !K || !V || !indices || !O)
     return fail(TIS_E_NULL, "tis_tree_attend: Q, K, V, indices and O are required");
   tis_status st = check_dtype(dtype);
@@ -291,6 +311,9 @@ tis_status tis_tree_attend(const void *Q, const void *K, const void *V, tis_dtyp
   a.beam = beam;
   a.n_blocks = n_keys / leaf_block;
   a.scale_log2 = static_cast<float>(sc * 1.4426950408889634);
+  st = plan_split("tis_tree_attend", queries, head_dim, beam, leaf_block, workspace,
+                  workspace_bytes, &a);
+  if (st != TIS_OK) return st;
   const tis::Dt dt = dtype == TIS_BF16 ? tis::Dt::BF16 : tis::Dt::F32;
   return hip_status(tis::launch_attend(dt, head_dim, a, static_cast<hipStream_t>(stream)),
                     "tis_tree_attend launch");
@@ -298,7 +321,8 @@ tis_status tis_tree_attend(const void *Q, const void *K, const void *V, tis_dtyp
 
 tis_status tis_tree_decode(const void *Q, const void *K, const void *V, tis_dtype dtype,
                            int q_heads, const tis_tree *tree, int beam, float scale, float *O,
-                           int32_t *indices, void *stream) {
+                           int32_t *indices, void *workspace, size_t workspace_bytes,
+                           void *stream) {
   if (!Q || !K || !V || !tree || !tree->summaries || !O)
     return fail(TIS_E_NULL, "tis_tree_decode: Q, K, V, tree, tree->summaries and O are required");
   tis_status st = check_dtype(dtype);
@@ -357,6 +381,9 @@ tis_status tis_tree_decode(const void *Q, const void *K, const void *V, tis_dtyp
   aa.beam = beam;
   aa.n_blocks = tree->n_keys / tree->leaf_block;
   aa.scale_log2 = static_cast<float>(sc * 1.4426950408889634);
+  st = plan_split("tis_tree_decode", queries, tree->head_dim, beam, tree->leaf_block, workspace,
+                  workspace_bytes, &aa);
+  if (st != TIS_OK) return st;
   const tis::Dt dt = dtype == TIS_BF16 ? tis::Dt::BF16 : tis::Dt::F32;
   return hip_status(tis::launch_decode(dt, tree->head_dim, ra, aa, static_cast<hipStream_t>(stream)),
                     "tis_tree_decode launch");

@@ -84,6 +84,8 @@ struct AttendArgs {
   const void *Q, *K, *V;
   const int32_t *indices;
   float *O;
+  float *part;           // [queries][splits][d + 4] partial states when splits > 1
+  int splits;            // workgroups per query (1: no split, no workspace)
   int64_t queries;       // B * Hq
   int64_t n_keys;
   int q_heads, kv_heads, group;
@@ -93,7 +95,12 @@ struct AttendArgs {
 };
 
 int attend_waves(int head_dim, Dt dt, int beam, int leaf_block);
+// Workgroups per query: more than one only when few queries would leave most
+// CUs idle and each query gathers enough keys to share out.
+int attend_splits(int64_t queries, int beam, int leaf_block);
+size_t attend_workspace(int64_t queries, int head_dim, int splits);
 hipError_t launch_attend(Dt dt, int head_dim, const AttendArgs &a, hipStream_t s);
+hipError_t launch_combine(int head_dim, const AttendArgs &a, hipStream_t s);
 
 // ---------------------------------------------------------------- decode --
 // Route and attend of each query in one workgroup (one launch).

@@ -176,10 +176,14 @@ def tree_decode(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, tree: Tree, b
     idx = (torch.empty((B, Hq, beam), dtype=torch.int32, device=Q.device)
            if return_indices else None)
     t = tree.c_struct()
-    check(lib().tis_tree_decode(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q), Hq,
-                                ctypes.byref(t), beam, 0.0 if scale is None else float(scale),
-                                O.data_ptr(), idx.data_ptr() if idx is not None else None,
-                                _stream(Q.device)))
+    L = lib()
+    wsb = L.tis_decode_workspace_bytes(B, Hq, d, beam, tree.leaf_block)
+    ws = _workspace(Q.device, "decode", wsb) if wsb else None
+    check(L.tis_tree_decode(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q), Hq,
+                            ctypes.byref(t), beam, 0.0 if scale is None else float(scale),
+                            O.data_ptr(), idx.data_ptr() if idx is not None else None,
+                            ws.data_ptr() if ws is not None else None,
+                            ws.numel() if ws is not None else 0, _stream(Q.device)))
     return (O, idx) if return_indices else O
 
 
@@ -234,7 +238,10 @@ class DecodePlan:
         self.ws_build = (torch.empty(wsb, dtype=torch.uint8, device=K.device) if wsb
                          else None)
         wsa = L.tis_attend_workspace_bytes(B, Hq, d, beam, leaf_block)
-        self.ws_attend = (torch.zeros(wsa, dtype=torch.uint8, device=K.device) if wsa
+        self.ws_attend = (torch.empty(wsa, dtype=torch.uint8, device=K.device) if wsa
+                          else None)
+        wsd = L.tis_decode_workspace_bytes(B, Hq, d, beam, leaf_block)
+        self.ws_decode = (torch.empty(wsd, dtype=torch.uint8, device=K.device) if wsd
                           else None)
         self.indices = torch.empty((B, Hq, beam), dtype=torch.int32, device=K.device)
         self.out = torch.empty((B, Hq, d), dtype=torch.float32, device=K.device)
@@ -268,10 +275,12 @@ class DecodePlan:
     def decode(self) -> None:
         """Route and attend in one launch (indices not written)."""
         B, H, N, d, b, Lb, lv = self.geom
+        ws = self.ws_decode
         check(self._lib.tis_tree_decode(self.Q.data_ptr(), self.K.data_ptr(), self.V.data_ptr(),
                                         self.dt, self.q_heads, ctypes.byref(self.tree_c),
                                         self.beam, self.scale, self.out.data_ptr(), None,
-                                        self.stream))
+                                        None if ws is None else ws.data_ptr(),
+                                        0 if ws is None else ws.numel(), self.stream))
 
     def tree(self) -> Tree:
         B, H, N, d, b, Lb, lv = self.geom
