@@ -115,7 +115,7 @@ def traffic_from_counters(workload: str, fetch_csv: str, write_csv: str) -> dict
     return out
 
 
-def cpu_baseline(w, x, min_seconds: float = 10.0, max_reps: int = 20):
+def cpu_baseline(w, x, min_seconds: float = 10.0, max_reps: int = 500):
     """The CPU oracle, as it stands, on whole steps of the same workload."""
     from oracle import tis_oracle as O
     from threadpoolctl import threadpool_limits
