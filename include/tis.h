@@ -2,11 +2,12 @@
  * tis.h -- tree-indexed sparse attention decode on AMD Instinct MI355X (gfx950).
  *
  * The method (ZHA abstract, "Subquadratic Attention with a Hierarchical
- * Tree-Structured Indexer"): build a tree of recursively compressed key
- * summaries over the KV cache; each decode query walks it from the top down
- * to retrieve a sparse subset of keys; final softmax attention runs over that
- * subset only.  The tree is static and routing is hierarchical, as in the ALHR
- * post ("Vdev-Ctrl Releases ALHR", Technical Breakthrough and Core Features).
+ * Tree-Structured Indexer"): an index tree over the KV cache whose nodes hold
+ * compressed summaries of the keys below them; each decode query descends it
+ * level by level to a small set of keys, and softmax attention runs over that
+ * set only.  The tree is static and the keys are routed level by level, as
+ * in the ALHR post ("Vdev-Ctrl Releases ALHR", Technical Breakthrough and
+ * Core Features).
  *
  * Geometry used by every call
  *   B  batch, Hkv KV heads, Hq query heads (Hq % Hkv == 0, G = Hq / Hkv),
@@ -91,9 +92,9 @@ size_t tis_build_workspace_bytes(int batch, int kv_heads, int n_keys, int head_d
                                  int branching, int leaf_block, int levels);
 
 /*
- * tis_tree_build -- node summaries for every level (ZHA abstract: recursively
- * compressed key summaries over the KV cache; the summary of a node is the
- * mean of the keys under it).
+ * tis_tree_build -- node summaries for every level (ZHA abstract: each node
+ * of the index tree summarizes the cached keys below it; here the summary of
+ * a node is the mean of those keys).
  *
  * K        [B][Hkv][N][d] keys, dtype TIS_F32 or TIS_BF16 (read once).
  * tree     in: tree->summaries; out: geometry fields filled in.
@@ -107,8 +108,8 @@ tis_status tis_tree_build(const void *K, tis_dtype dtype, int batch, int kv_head
                           size_t workspace_bytes, void *stream);
 
 /*
- * tis_tree_route -- top-down beam traversal (ZHA abstract: queries traverse
- * the tree from the top down to retrieve a sparse subset of keys).
+ * tis_tree_route -- top-down beam traversal (ZHA abstract: a query descends
+ * the summary tree level by level and ends with a small set of keys).
  *
  * Q        [B][Hq][d], dtype TIS_F32 or TIS_BF16; tree->batch is B.
  * For every query: the candidates of level 1 are the b children of the
@@ -131,9 +132,9 @@ size_t tis_attend_workspace_bytes(int batch, int q_heads, int head_dim, int beam
 
 /*
  * tis_tree_attend -- exact softmax attention over the keys of the selected
- * leaf blocks (ZHA abstract: the final attention after routing; the NSA /
+ * leaf blocks (ZHA abstract: the attention after the descent; the NSA /
  * InfLLMv2 abstract on the Progressive Sparse Attention related-papers page:
- * fine-grained softmax attention on the selected tokens).
+ * exact softmax restricted to the tokens of the chosen blocks).
  *
  * Q [B][Hq][d], K and V [B][Hkv][N][d], all of type `dtype`.
  * indices  int32 [B][Hq][beam] leaf-block numbers, any order.  A negative
@@ -155,8 +156,8 @@ tis_status tis_tree_attend(const void *Q, const void *K, const void *V, tis_dtyp
 
 /*
  * tis_tree_decode -- one decode step: tis_tree_route and tis_tree_attend for
- * every query in a single launch (ZHA abstract: the cost of a query is the
- * routing plus the final attention over the retrieved keys).
+ * every query in a single launch (ZHA abstract: a query costs its descent
+ * through the tree plus the attention over the keys it ends with).
  *
  * Q [B][Hq][d] and K, V [B][Hkv][N][d] of type `dtype`, matching the tree
  * (B, Hkv, N, d, L as built).  The leaves each query keeps are exactly those

@@ -8,10 +8,10 @@ it shares no code with the HIP library or its Python binding.
 What is computed, and where it comes from
 -----------------------------------------
 "Subquadratic Attention with a Hierarchical Tree-Structured Indexer" (ZHA),
-Abstract: a tree of recursively compressed key summaries is built over the KV
-cache; future queries traverse it from the top down to retrieve a sparse
-subset of keys; the cost counted is routing plus the final attention over that
-subset.  "Vdev-Ctrl Releases ALHR", Technical Breakthrough and Core Features:
+Abstract: every node of an index tree over the KV cache holds a compressed
+summary of the keys below it, each level built on the one beneath; a later
+query descends the tree level by level and ends with a small set of keys; a
+query costs its descent plus the attention over that set.  "Vdev-Ctrl Releases ALHR", Technical Breakthrough and Core Features:
 the tree is static and keys/values are routed hierarchically.  Progressive
 Sparse Attention related-papers page (the NSA / InfLLMv2 abstract): blocks are
 chosen by coarse scores and fine softmax attention runs on the selected tokens.
@@ -71,8 +71,8 @@ def _check_geometry(n_keys: int, branching: int, leaf_block: int, levels: int) -
 
 def tree_build(K: np.ndarray, dtype: str, branching: int, leaf_block: int,
                levels: int) -> Dict[str, List[np.ndarray]]:
-    """Summaries of every node at levels 1..levels (ZHA Abstract: recursively
-    compressed key summaries over the KV cache).
+    """Summaries of every node at levels 1..levels (ZHA Abstract: each tree
+    node holds a compressed summary of the cached keys below it).
 
     K: [B, Hkv, N, d] stored keys. Level l has n_l = branching**l nodes; node
     n of level l covers the M_l = N / n_l contiguous keys [n*M_l, (n+1)*M_l).
@@ -106,8 +106,8 @@ def tree_build(K: np.ndarray, dtype: str, branching: int, leaf_block: int,
 def tree_route(Q: np.ndarray, dtype: str, stored: Sequence[np.ndarray],
                branching: int, beam: int) -> Dict[str, np.ndarray]:
     """Top-down traversal that keeps a fixed beam of nodes per level (ZHA
-    Abstract: queries traverse the tree from the top down to retrieve a sparse
-    subset of keys; ALHR post: keys are routed hierarchically).
+    Abstract: a query descends the tree level by level to a small set of
+    keys; ALHR post: the static tree routes keys level by level).
 
     Q: [B, Hq, d] stored queries; stored[l-1]: float32 [B, Hkv, n_l, d].
     Level 1 candidates are the `branching` children of the implicit root; at
@@ -172,9 +172,9 @@ def tree_route(Q: np.ndarray, dtype: str, stored: Sequence[np.ndarray],
 def tree_attend(Q: np.ndarray, K: np.ndarray, V: np.ndarray, dtype: str,
                 indices: np.ndarray, leaf_block: int,
                 scale: Optional[float] = None) -> np.ndarray:
-    """Final attention restricted to the retrieved keys (ZHA Abstract: routing
-    plus final attention; NSA/InfLLMv2 abstract on the Progressive Sparse
-    Attention page: fine-grained softmax attention on the selected tokens).
+    """Final attention restricted to the retrieved keys (ZHA Abstract: the
+    attention after the descent; NSA/InfLLMv2 abstract on the Progressive
+    Sparse Attention page: exact softmax over the tokens of the chosen blocks).
 
     The key set of a query is the union of the leaf blocks named in its row of
     `indices` ([B, Hq, W], any order; negative entries are empty slots;

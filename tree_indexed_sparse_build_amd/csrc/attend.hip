@@ -1,8 +1,8 @@
 // tree_attend: exact softmax attention over the keys of the selected leaf
 // blocks ("Subquadratic Attention with a Hierarchical Tree-Structured
-// Indexer", Abstract: the final attention after routing; the NSA / InfLLMv2
-// abstract on the Progressive Sparse Attention related-papers page: fine
-// softmax attention on the selected tokens).
+// Indexer", Abstract: the attention that follows the descent; the NSA /
+// InfLLMv2 abstract on the Progressive Sparse Attention related-papers page:
+// exact softmax restricted to the tokens of the chosen blocks).
 //
 // One workgroup per query (or, when few queries would leave most CUs idle,
 // `splits` workgroups per query, each on a share of the slots, followed by a

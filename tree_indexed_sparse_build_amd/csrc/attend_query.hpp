@@ -1,9 +1,9 @@
 // Exact softmax attention of one query over a set of leaf blocks, as a
 // device function shared by the attend kernel and the fused decode kernel
 // ("Subquadratic Attention with a Hierarchical Tree-Structured Indexer",
-// Abstract: the final attention over the retrieved keys; the NSA / InfLLMv2
-// abstract on the Progressive Sparse Attention related-papers page: fine
-// softmax attention on the selected tokens).
+// Abstract: the attention over the keys a query ends with; the NSA /
+// InfLLMv2 abstract on the Progressive Sparse Attention related-papers page:
+// exact softmax restricted to the tokens of the chosen blocks).
 //
 // Gather flash-decode inside one workgroup.  The query's work is cut into
 // units of RB rows of one leaf block; each wave takes units in turn, issues

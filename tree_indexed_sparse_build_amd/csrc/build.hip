@@ -1,7 +1,7 @@
 // tree_build: node summaries = mean of the keys under each node, for every
 // level ("Subquadratic Attention with a Hierarchical Tree-Structured
-// Indexer", Abstract: a tree of recursively compressed key summaries over
-// the KV cache).
+// Indexer", Abstract: each node of the index tree holds a compressed summary
+// of the cached keys below it, built one level on top of the next).
 //
 // HBM-bound: K is read exactly once with 16-byte coalesced loads (a wave
 // reads whole 1 KB stretches of a leaf block, 16 KB in flight per wave),

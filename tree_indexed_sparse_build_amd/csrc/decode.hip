@@ -1,6 +1,6 @@
 // tree_decode: route then attend for each query in one launch ("Subquadratic
-// Attention with a Hierarchical Tree-Structured Indexer", Abstract: routing
-// plus final attention is the whole cost of a decode step).
+// Attention with a Hierarchical Tree-Structured Indexer", Abstract: a query
+// costs its descent through the tree plus the attention at the end).
 //
 // One workgroup of 16 waves per query: route_walk leaves the kept leaves in
 // LDS and attend_query gathers them straight away, so the leaf list never

@@ -1,6 +1,6 @@
 // tree_route: top-down beam traversal ("Subquadratic Attention with a
-// Hierarchical Tree-Structured Indexer", Abstract: queries traverse the tree
-// from the top down to retrieve a sparse subset of keys).
+// Hierarchical Tree-Structured Indexer", Abstract: a query descends the
+// summary tree one level at a time and ends with a small set of keys).
 //
 // One workgroup (8 waves) walks one query through every level in a single
 // launch (route_walk); the kept leaves are written in ascending order.

@@ -1,6 +1,6 @@
 // One query's walk down the tree ("Subquadratic Attention with a Hierarchical
-// Tree-Structured Indexer", Abstract: queries traverse the tree of key
-// summaries from the top down to retrieve a sparse subset of keys), as a
+// Tree-Structured Indexer", Abstract: a query descends the summary tree one
+// level at a time and ends with a small set of keys to attend to), as a
 // device function shared by the route kernel and the fused decode kernel.
 //
 // Per scored level: gather the candidate summary rows (half a wave per fp32
