@@ -49,9 +49,13 @@ BUILD_SOURCE = os.path.join(ROOT, "tree_indexed_sparse_build_amd", "csrc", "buil
 
 
 def _source_digest() -> str:
+    """Digest of build.hip's code (comments and blank space ignored)."""
     import hashlib
-    with open(BUILD_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    import re
+    with open(BUILD_SOURCE) as f:
+        code = re.sub(r"//[^\n]*", "", f.read())
+    code = re.sub(r"\s+", " ", code).strip()
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def load_traffic(workload: str):
