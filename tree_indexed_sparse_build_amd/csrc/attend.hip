@@ -24,14 +24,14 @@ __global__ void __launch_bounds__(kAttendMaxWaves * 64) k_attend(AttendArgs a) {
   const int tid = threadIdx.x;
   // part sp of query qi; the parts of a query are queries apart in the grid,
   // so with a multiple of 8 queries they land on one XCD and share its L2
-  const int64_t sp = blockIdx.x / a.queries;
-  const int64_t qi = blockIdx.x - sp * a.queries;
+  const int sp = blockIdx.x / a.queries;
+  const int qi = query_of_slot(blockIdx.x - sp * a.queries, a.queries, a.group);
   const int W = a.beam;
 
   // the query row and the slot list are loaded before anything waits on them
   const uint4 qraw = attend_q_raw<T, D>(a, qi);
   if (tid == 0) s_bad = 0;
-  for (int s = tid; s < W; s += blockDim.x) s_idx[s] = a.indices[qi * W + s];
+  for (int s = tid; s < W; s += blockDim.x) s_idx[s] = a.indices[static_cast<int64_t>(qi) * W + s];
   __syncthreads();
   for (int s = tid; s < W; s += blockDim.x) {
     const int idx = s_idx[s];
@@ -42,9 +42,11 @@ __global__ void __launch_bounds__(kAttendMaxWaves * 64) k_attend(AttendArgs a) {
     if (bad) s_bad = 1;
   }
   __syncthreads();
-  const int s0 = static_cast<int>(sp * W / a.splits);
-  const int s1 = static_cast<int>((sp + 1) * W / a.splits);
-  float *part = a.splits > 1 ? a.part + (qi * a.splits + sp) * (D + kPartHeader) : nullptr;
+  const int s0 = sp * W / a.splits;
+  const int s1 = (sp + 1) * W / a.splits;
+  float *part = a.splits > 1
+                    ? a.part + (static_cast<int64_t>(qi) * a.splits + sp) * (D + kPartHeader)
+                    : nullptr;
   attend_query<T, D>(a, sh, qi, qraw, s_idx + s0, s_use + s0, s1 - s0, s_bad != 0, part);
 }
 
@@ -85,7 +87,7 @@ hipError_t launch_combine(int head_dim, const AttendArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_attend(Dt dt, int head_dim, const AttendArgs &a, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(a.queries * a.splits));
+  const dim3 grid(static_cast<unsigned>(a.queries) * static_cast<unsigned>(a.splits));
   const int per = (a.beam + a.splits - 1) / a.splits;
   const dim3 block(static_cast<unsigned>(attend_waves(head_dim, dt, per, a.leaf_block) * 64));
   if (dt == Dt::BF16 && head_dim == 128)

@@ -37,10 +37,10 @@ template <typename T, int D> struct AttendShared {
 };
 
 // This lane's part of the query row in the attend layout (E elements).
-template <typename T, int D> __device__ inline uint4 attend_q_raw(const AttendArgs &a, int64_t qi) {
+template <typename T, int D> __device__ inline uint4 attend_q_raw(const AttendArgs &a, int qi) {
   constexpr int LPR = AttendGeom<T, D>::LPR, E = AttendGeom<T, D>::E;
   const int lane = threadIdx.x & 63;
-  return load16(static_cast<const T *>(a.Q) + qi * D + (lane % LPR) * E);
+  return load16(static_cast<const T *>(a.Q) + static_cast<int64_t>(qi) * D + (lane % LPR) * E);
 }
 
 // Attention of query qi over the leaf blocks slots[s] (s < nslots) whose
@@ -50,7 +50,7 @@ template <typename T, int D> __device__ inline uint4 attend_q_raw(const AttendAr
 // softmax state to part: m (log2 units), l (NaN if `bad`), two pad words,
 // acc[D], for a later log-sum-exp merge with the query's other parts.
 template <typename T, int D>
-__device__ void attend_query(const AttendArgs &a, AttendShared<T, D> &sh, int64_t qi,
+__device__ void attend_query(const AttendArgs &a, AttendShared<T, D> &sh, int qi,
                              uint4 qraw, const int *slots, const int *use, int nslots,
                              bool bad, float *part) {
   using AG = AttendGeom<T, D>;
@@ -60,9 +60,9 @@ __device__ void attend_query(const AttendArgs &a, AttendShared<T, D> &sh, int64_
   const int w = tid >> 6;
   const int nw = blockDim.x >> 6;
   const int L = a.leaf_block;
-  const int64_t bi = qi / a.q_heads;
-  const int hq = static_cast<int>(qi - bi * a.q_heads);
-  const int64_t head = bi * a.kv_heads + hq / a.group;
+  const int bi = qi / a.q_heads;
+  const int hq = qi - bi * a.q_heads;
+  const int64_t head = static_cast<int64_t>(bi) * a.kv_heads + hq / a.group;
   const int col = (lane % LPR) * E;
   const int rsub = lane / LPR;
 
@@ -110,8 +110,10 @@ __device__ void attend_query(const AttendArgs &a, AttendShared<T, D> &sh, int64_
     const bool valid = r0 + kk * R + rsub < L;
     const float x = valid ? sc * a.scale_log2 : -INFINITY;
     const float mnew = fmaxf(m, wave_max(x));
-    const float p = valid ? exp2f(x - mnew) : 0.f;
-    const float alpha = exp2f(m - mnew);
+    // hardware 2^x: results below 2^-126 flush to zero, which leaves the
+    // weights of everything that contributes at fp32 precision unchanged
+    const float p = valid ? __builtin_amdgcn_exp2f(x - mnew) : 0.f;
+    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
     l = l * alpha + wave_sum((lane % REP) == 0 ? p : 0.f);
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] *= alpha;
@@ -144,16 +146,35 @@ __device__ void attend_query(const AttendArgs &a, AttendShared<T, D> &sh, int64_
   }
   __syncthreads();
 
-  // ---- log-sum-exp merge of the waves' partials, one column per thread
+  // ---- log-sum-exp merge of the waves' partials, one column per thread.
+  // Every read has a compile-time offset and all are issued before the
+  // first is used; slots of waves past nw are never written and are masked
+  // (m = -inf, l = acc = 0).
   for (int c = tid; c < D; c += blockDim.x) {
+    float mj[kAttendMaxWaves], lj[kAttendMaxWaves], aj[kAttendMaxWaves];
+#pragma unroll
+    for (int j = 0; j < kAttendMaxWaves; ++j) {
+      mj[j] = sh.m[j];
+      lj[j] = sh.l[j];
+      aj[j] = sh.acc[j][c];
+    }
     float mx = -INFINITY;
-    for (int j = 0; j < nw; ++j) mx = fmaxf(mx, sh.m[j]);
+#pragma unroll
+    for (int j = 0; j < kAttendMaxWaves; ++j) {
+      if (j >= nw) {
+        mj[j] = -INFINITY;
+        lj[j] = 0.f;
+        aj[j] = 0.f;
+      }
+      mx = fmaxf(mx, mj[j]);
+    }
     float num = 0.f, den = 0.f;
     if (mx != -INFINITY) {
-      for (int j = 0; j < nw; ++j) {
-        const float wj = exp2f(sh.m[j] - mx);  // 0 for waves that saw no key
-        den = fmaf(wj, sh.l[j], den);
-        num = fmaf(wj, sh.acc[j][c], num);
+#pragma unroll
+      for (int j = 0; j < kAttendMaxWaves; ++j) {
+        const float wj = __builtin_amdgcn_exp2f(mj[j] - mx);  // 0 for waves that saw no key
+        den = fmaf(wj, lj[j], den);
+        num = fmaf(wj, aj[j], num);
       }
     }
     if (part) {
@@ -165,7 +186,7 @@ __device__ void attend_query(const AttendArgs &a, AttendShared<T, D> &sh, int64_
     } else {
       float r = mx == -INFINITY ? 0.f : num / den;
       if (bad) r = NAN;
-      a.O[qi * D + c] = r;
+      a.O[static_cast<int64_t>(qi) * D + c] = r;
     }
   }
 }

@@ -22,17 +22,20 @@ __global__ void __launch_bounds__(kDecodeWaves * 64) k_decode(RouteArgs ra, Atte
   __shared__ RouteShared<kDecodeWaves> rsh;
   __shared__ AttendShared<T, D> ash;
   // part sp of query qi (see k_attend: a query's parts share an XCD)
-  const int64_t sp = blockIdx.x / aa.queries;
-  const int64_t qi = blockIdx.x - sp * aa.queries;
+  const int sp = blockIdx.x / aa.queries;
+  const int qi = query_of_slot(blockIdx.x - sp * aa.queries, aa.queries, aa.group);
   const uint4 qraw = attend_q_raw<T, D>(aa, qi);  // in flight during the walk
   // every part walks the tree (the repeated summary reads hit the XCD's L2)
   route_walk<T, D, kDecodeWaves>(ra, rsh, qi);
   if (ra.indices && sp == 0)
-    write_ascending<kDecodeWaves * 64>(rsh.front, ra.beam, ra.indices + qi * ra.beam);
+    write_ascending<kDecodeWaves * 64>(rsh.front, ra.beam,
+                                       ra.indices + static_cast<int64_t>(qi) * ra.beam);
   const int W = ra.beam;
-  const int s0 = static_cast<int>(sp * W / aa.splits);
-  const int s1 = static_cast<int>((sp + 1) * W / aa.splits);
-  float *part = aa.splits > 1 ? aa.part + (qi * aa.splits + sp) * (D + kPartHeader) : nullptr;
+  const int s0 = sp * W / aa.splits;
+  const int s1 = (sp + 1) * W / aa.splits;
+  float *part = aa.splits > 1
+                    ? aa.part + (static_cast<int64_t>(qi) * aa.splits + sp) * (D + kPartHeader)
+                    : nullptr;
   attend_query<T, D>(aa, ash, qi, qraw, rsh.front + s0, nullptr, s1 - s0, false, part);
 }
 
@@ -40,7 +43,7 @@ __global__ void __launch_bounds__(kDecodeWaves * 64) k_decode(RouteArgs ra, Atte
 
 hipError_t launch_decode(Dt dt, int head_dim, const RouteArgs &ra, const AttendArgs &aa,
                          hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(ra.queries * aa.splits));
+  const dim3 grid(static_cast<unsigned>(ra.queries) * static_cast<unsigned>(aa.splits));
   const dim3 block(kDecodeWaves * 64);
   if (dt == Dt::BF16 && head_dim == 128)
     hipLaunchKernelGGL((k_decode<bf16_bits, 128>), grid, block, 0, s, ra, aa);

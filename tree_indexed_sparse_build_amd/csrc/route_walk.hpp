@@ -29,24 +29,40 @@ __device__ inline uint64_t score_key(double s, int node, int bits) {
   return (u & ~mask) | (mask - static_cast<uint64_t>(node));
 }
 
-template <typename T, int D> __device__ inline void load_q(const T *q, int col, double *out);
-template <> __device__ inline void load_q<float, 128>(const float *q, int col, double *out) {
-  const float4 v = *reinterpret_cast<const float4 *>(q + col);
-  out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+// Pins a register value where it stands: the empty asm reads and "writes"
+// it, so the compiler can neither hoist what uses it above this point nor
+// out of a loop.  Used to keep the query's widening (which waits for its
+// load) behind the summary loads that should already be in flight.
+__device__ inline uint32_t pin(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
 }
-template <> __device__ inline void load_q<float, 64>(const float *q, int col, double *out) {
-  load_q<float, 128>(q, col, out);
-}
-template <> __device__ inline void load_q<bf16_bits, 128>(const bf16_bits *q, int col, double *out) {
-  const uint2 v = *reinterpret_cast<const uint2 *>(q + col);
-  out[0] = __uint_as_float(v.x << 16);
-  out[1] = __uint_as_float(v.x & 0xffff0000u);
-  out[2] = __uint_as_float(v.y << 16);
-  out[3] = __uint_as_float(v.y & 0xffff0000u);
-}
-template <> __device__ inline void load_q<bf16_bits, 64>(const bf16_bits *q, int col, double *out) {
-  load_q<bf16_bits, 128>(q, col, out);
-}
+
+// Raw bits of this lane's 4 query elements (columns col .. col + 3).  They
+// stay raw until a level's summary loads are in flight, so the wait for the
+// query row overlaps those loads.
+template <typename T> struct QRaw;
+template <> struct QRaw<float> {
+  uint4 r;
+  __device__ inline void load(const float *q) { r = *reinterpret_cast<const uint4 *>(q); }
+  __device__ inline void widen(double *out) const {
+    out[0] = __uint_as_float(pin(r.x));
+    out[1] = __uint_as_float(pin(r.y));
+    out[2] = __uint_as_float(pin(r.z));
+    out[3] = __uint_as_float(pin(r.w));
+  }
+};
+template <> struct QRaw<bf16_bits> {
+  uint2 r;
+  __device__ inline void load(const bf16_bits *q) { r = *reinterpret_cast<const uint2 *>(q); }
+  __device__ inline void widen(double *out) const {
+    const uint32_t x = pin(r.x), y = pin(r.y);
+    out[0] = __uint_as_float(x << 16);
+    out[1] = __uint_as_float(x & 0xffff0000u);
+    out[2] = __uint_as_float(y << 16);
+    out[3] = __uint_as_float(y & 0xffff0000u);
+  }
+};
 
 // Shared memory of one query's walk, for a workgroup of NW waves.
 template <int NW> struct RouteShared {
@@ -66,81 +82,121 @@ template <int NT> __device__ inline void write_ascending(const int *v, int n, in
   }
 }
 
+// Scores the C candidates of one level: candidate p is node p of the level
+// (all) or node cand[p], and its key goes to keys[p].  The nsw waves of the
+// workgroup cover UU rows per lane per pass, UU just large enough for C, and
+// every load of a pass is issued before any is used: rows past C read
+// candidate 0 again (always a valid address) and their scores are dropped,
+// so no branch splits the loads.
+template <typename T, int D, int UU>
+__device__ inline void score_rows(const float *sl, int C, bool all, const int *cand,
+                                  uint64_t *keys, int bits, const QRaw<T> &qr, int nsw,
+                                  int w, int lane) {
+  constexpr int LPR = D / 4;    // lanes per fp32 summary row
+  constexpr int RPI = 64 / LPR; // rows per wave-wide load
+  constexpr int REP = LPR / UU; // lanes sharing one reduced score
+  static_assert(UU >= 1 && UU <= LPR, "rows per lane");
+  const int rsub = lane / LPR;
+  const int rows = UU * nsw * RPI;
+  for (int base = 0; base < C; base += rows) {
+    int node[UU];
+#pragma unroll
+    for (int u = 0; u < UU; ++u) {
+      const int pos = base + (u * nsw + w) * RPI + rsub;
+      const int pc = pos < C ? pos : 0;
+      node[u] = all ? pc : cand[pc];
+    }
+    float4 v[UU];
+#pragma unroll
+    for (int u = 0; u < UU; ++u)
+      v[u] = *reinterpret_cast<const float4 *>(sl + static_cast<int64_t>(node[u]) * D);
+    double q[4];
+    qr.widen(q);
+    double part[UU];
+#pragma unroll
+    for (int u = 0; u < UU; ++u) {
+      // fp32 x (fp32 or bf16) products are exact in fp64
+      double s = q[0] * static_cast<double>(v[u].x);
+      s = fma(q[1], static_cast<double>(v[u].y), s);
+      s = fma(q[2], static_cast<double>(v[u].z), s);
+      s = fma(q[3], static_cast<double>(v[u].w), s);
+      part[u] = s;
+    }
+    const double s = group_transpose_reduce<UU, LPR>(part, lane);
+    const int k = (lane % LPR) / REP;
+    const int pos = base + (k * nsw + w) * RPI + rsub;
+    if ((lane % REP) == 0 && pos < C) keys[pos] = score_key(s, all ? pos : cand[pos], bits);
+  }
+}
+
 // Walks query qi down the tree (every wave of the NW-wave workgroup takes
 // part).  On return, after a barrier, sh.front[0 .. beam) holds the kept
 // leaves in rank order, best first.  Levels whose candidate set is no larger
 // than the beam keep every node whatever the scores, so the walk starts at
-// the first level l0 that cuts; its candidates are all of its nodes, so its
-// loads need no selection and go out together with the query row.
+// the first level that cuts (a.first_cut); its candidates are all of its
+// nodes, so its loads need no selection and go out together with the query
+// row.
 template <typename T, int D, int NW>
-__device__ void route_walk(const RouteArgs &a, RouteShared<NW> &sh, int64_t qi) {
+__device__ void route_walk(const RouteArgs &a, RouteShared<NW> &sh, int qi) {
   constexpr int NT = NW * 64;
   constexpr int LOG_NT = NW == 16 ? 10 : NW == 8 ? 9 : NW == 4 ? 8 : -1;
   static_assert(LOG_NT > 0, "4, 8 or 16 waves");
   static_assert(kMaxCandidates <= NT / 2, "two or more threads per candidate");
   constexpr int LPR = D / 4;          // lanes per fp32 summary row
   constexpr int RPI = 64 / LPR;       // rows per wave-wide load
-  constexpr int U = 8;                // loads in flight per lane
-  constexpr int REP = LPR / U;        // lanes sharing one reduced score
-  constexpr int ROWS = U * NW * RPI;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
-  const int64_t bi = qi / a.q_heads;
-  const int hq = static_cast<int>(qi - bi * a.q_heads);
-  const int64_t head = bi * a.kv_heads + hq / a.group;
+  const int bi = qi / a.q_heads;
+  const int hq = qi - bi * a.q_heads;
+  const int64_t head = static_cast<int64_t>(bi) * a.kv_heads + hq / a.group;
   const int b = a.branching;
   const int W = a.beam;
   const int lv = a.levels;
+  const int l0 = a.first_cut;
   const int col = (lane % LPR) * 4;
-  const int rsub = lane / LPR;
 
-  int l0 = 1;
-  while (l0 < lv && a.n_at[l0] <= W) ++l0;
+  QRaw<T> qr;
+  qr.load(static_cast<const T *>(a.Q) + static_cast<int64_t>(qi) * D + col);
   if (a.trace) {
+    int n_at_l = 1;
     for (int l = 1; l < l0; ++l) {
-      int32_t *tr = a.trace + (qi * lv + (l - 1)) * W;
-      for (int k = tid; k < W; k += NT) tr[k] = k < a.n_at[l] ? k : -1;
+      n_at_l *= b;  // levels before l0 have at most beam nodes
+      int32_t *tr = a.trace + (static_cast<int64_t>(qi) * lv + (l - 1)) * W;
+      for (int k = tid; k < W; k += NT) tr[k] = k < n_at_l ? k : -1;
     }
   }
 
-  double q[4];
-  load_q<T, D>(static_cast<const T *>(a.Q) + qi * D, col, q);
-
+  // level sizes and offsets follow from b alone (scalar arithmetic, no
+  // loads): n_l = b^l, and level l starts after heads * d * (b + ... + b^(l-1))
+  const int64_t heads = static_cast<int64_t>(a.queries / a.q_heads) * a.kv_heads;
+  int64_t n_l = 1, off = 0;
+  for (int l = 1; l < l0; ++l) {
+    n_l *= b;
+    off += heads * n_l * D;
+  }
   int cur = 0;
-  int nf = static_cast<int>(a.n_at[l0 - 1]);
+  int nf = static_cast<int>(n_l);
   for (int l = l0; l <= lv; ++l) {
+    n_l *= b;
     const int C = nf * b;
     const bool all = l == l0;  // candidates are nodes 0..C-1 of level l
     if (C > W) {
-      const int bits = 32 - __clz(static_cast<int>(a.n_at[l]) - 1);
-      const float *sl = a.summ + a.summ_off[l] + head * a.n_at[l] * D + col;
-      for (int base = 0; base < C; base += ROWS) {
-        float4 v[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int pos = base + (u * NW + w) * RPI + rsub;
-          const int node = all ? pos : sh.cand[cur][pos < C ? pos : 0];
-          v[u] = pos < C ? *reinterpret_cast<const float4 *>(sl + static_cast<int64_t>(node) * D)
-                         : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-        double part[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          // fp32 x (fp32 or bf16) products are exact in fp64
-          double s = q[0] * static_cast<double>(v[u].x);
-          s = fma(q[1], static_cast<double>(v[u].y), s);
-          s = fma(q[2], static_cast<double>(v[u].z), s);
-          s = fma(q[3], static_cast<double>(v[u].w), s);
-          part[u] = s;
-        }
-        const double s = group_transpose_reduce<U, LPR>(part, lane);
-        const int k = (lane % LPR) / REP;
-        const int pos = base + (k * NW + w) * RPI + rsub;
-        if ((lane % REP) == 0 && pos < C)
-          sh.keys[pos] = score_key(s, all ? pos : sh.cand[cur][pos], bits);
-      }
+      const int bits = 32 - __clz(static_cast<int>(n_l) - 1);
+      const float *sl = a.summ + off + head * n_l * D + col;
+      // every wave scores (more waves with fewer rows each measured faster
+      // than fewer waves with more rows), each lane taking `per` rows
+      const int per = (C + NW * RPI - 1) / (NW * RPI);
+      const int *cand = sh.cand[cur];
+      if (per <= 1)
+        score_rows<T, D, 1>(sl, C, all, cand, sh.keys, bits, qr, NW, w, lane);
+      else if (per <= 2)
+        score_rows<T, D, 2>(sl, C, all, cand, sh.keys, bits, qr, NW, w, lane);
+      else if (per <= 4)
+        score_rows<T, D, 4>(sl, C, all, cand, sh.keys, bits, qr, NW, w, lane);
+      else
+        score_rows<T, D, 8>(sl, C, all, cand, sh.keys, bits, qr, NW, w, lane);
       __syncthreads();
       // rank of candidate i = number of candidates with a larger key.  Each
       // candidate has a group of g adjacent lanes (g <= 8); lane p of the
@@ -174,7 +230,7 @@ __device__ void route_walk(const RouteArgs &a, RouteShared<NW> &sh, int64_t qi) 
         // the W best go to front[] at their rank; their children, in the
         // same order, are the next level's candidates
         if (i < C && part == 0 && cnt < W) {
-          const int node = all ? i : sh.cand[cur][i];
+          const int node = all ? i : cand[i];
           sh.front[cnt] = node;
           if (l < lv) {
             for (int c = 0; c < b; ++c) sh.cand[cur ^ 1][cnt * b + c] = node * b + c;
@@ -194,8 +250,9 @@ __device__ void route_walk(const RouteArgs &a, RouteShared<NW> &sh, int64_t qi) 
     __syncthreads();
     cur ^= 1;
     nf = C < W ? C : W;
+    off += heads * n_l * D;
     if (a.trace) {
-      int32_t *tr = a.trace + (qi * lv + (l - 1)) * W;
+      int32_t *tr = a.trace + (static_cast<int64_t>(qi) * lv + (l - 1)) * W;
       write_ascending<NT>(sh.front, nf, tr);
       for (int k = nf + tid; k < W; k += NT) tr[k] = -1;
     }

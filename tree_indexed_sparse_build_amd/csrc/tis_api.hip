@@ -82,6 +82,26 @@ tis_status hip_status(hipError_t e, const char *what) {
   return fail(TIS_E_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Route arguments of a checked tree; queries < 2^31 is checked by the caller.
+tis::RouteArgs route_args(const void *Q, const tis_tree *tree, const Geometry &g, int q_heads,
+                          int beam, int32_t *indices, int32_t *trace, int64_t queries) {
+  tis::RouteArgs a{};
+  a.Q = Q;
+  a.summ = tree->summaries;
+  a.indices = indices;
+  a.trace = trace;
+  a.queries = static_cast<int>(queries);
+  a.q_heads = q_heads;
+  a.kv_heads = tree->kv_heads;
+  a.group = q_heads / tree->kv_heads;
+  a.branching = tree->branching;
+  a.levels = tree->levels;
+  a.beam = beam;
+  a.first_cut = 1;
+  while (a.first_cut < tree->levels && g.n_at[a.first_cut] <= beam) ++a.first_cut;
+  return a;
+}
+
 }  // namespace
 
 extern "C" {
@@ -216,22 +236,7 @@ tis_status tis_tree_route(const void *Q, tis_dtype dtype, int q_heads, const tis
   const int64_t queries = static_cast<int64_t>(tree->batch) * q_heads;
   if (queries > 0x7fffffffLL) return fail(TIS_E_UNSUPPORTED, "tis_tree_route: too many queries");
 
-  tis::RouteArgs a{};
-  a.Q = Q;
-  a.summ = tree->summaries;
-  a.indices = indices;
-  a.trace = trace;
-  a.queries = queries;
-  a.q_heads = q_heads;
-  a.kv_heads = tree->kv_heads;
-  a.group = q_heads / tree->kv_heads;
-  a.branching = tree->branching;
-  a.levels = tree->levels;
-  a.beam = beam;
-  for (int l = 0; l <= tis::kMaxLevels; ++l) {
-    a.n_at[l] = g.n_at[l];
-    a.summ_off[l] = g.summ_off[l];
-  }
+  const tis::RouteArgs a = route_args(Q, tree, g, q_heads, beam, indices, trace, queries);
   const tis::Dt dt = dtype == TIS_BF16 ? tis::Dt::BF16 : tis::Dt::F32;
   return hip_status(tis::launch_route(dt, tree->head_dim, a, static_cast<hipStream_t>(stream)),
                     "tis_tree_route launch");
@@ -302,7 +307,7 @@ tis_status tis_tree_attend(const void *Q, const void *K, const void *V, tis_dtyp
   a.V = V;
   a.indices = indices;
   a.O = O;
-  a.queries = queries;
+  a.queries = static_cast<int>(queries);
   a.n_keys = n_keys;
   a.q_heads = q_heads;
   a.kv_heads = kv_heads;
@@ -348,22 +353,7 @@ tis_status tis_tree_decode(const void *Q, const void *K, const void *V, tis_dtyp
   const int64_t queries = static_cast<int64_t>(tree->batch) * q_heads;
   if (queries > 0x7fffffffLL) return fail(TIS_E_UNSUPPORTED, "tis_tree_decode: too many queries");
 
-  tis::RouteArgs ra{};
-  ra.Q = Q;
-  ra.summ = tree->summaries;
-  ra.indices = indices;
-  ra.trace = nullptr;
-  ra.queries = queries;
-  ra.q_heads = q_heads;
-  ra.kv_heads = tree->kv_heads;
-  ra.group = q_heads / tree->kv_heads;
-  ra.branching = tree->branching;
-  ra.levels = tree->levels;
-  ra.beam = beam;
-  for (int l = 0; l <= tis::kMaxLevels; ++l) {
-    ra.n_at[l] = g.n_at[l];
-    ra.summ_off[l] = g.summ_off[l];
-  }
+  const tis::RouteArgs ra = route_args(Q, tree, g, q_heads, beam, indices, nullptr, queries);
   const double sc =
       scale > 0.f ? static_cast<double>(scale) : 1.0 / sqrt(static_cast<double>(tree->head_dim));
   tis::AttendArgs aa{};
@@ -372,7 +362,7 @@ tis_status tis_tree_decode(const void *Q, const void *K, const void *V, tis_dtyp
   aa.V = V;
   aa.indices = nullptr;
   aa.O = O;
-  aa.queries = queries;
+  aa.queries = static_cast<int>(queries);
   aa.n_keys = tree->n_keys;
   aa.q_heads = q_heads;
   aa.kv_heads = tree->kv_heads;

@@ -49,6 +49,21 @@ __device__ inline uint4 load16_stream(const void *p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Query served by workgroup slot s (0 <= s < queries).  Workgroups are
+// dispatched to the 8 XCDs in turn, so slots s = x (mod 8) share XCD x and
+// its L2.  When queries is a multiple of 8 * group, the group queries that
+// share a KV head get slots on one XCD, and the reads they have in common
+// (the upper tree levels, leaf blocks chosen by several of them) meet in
+// that L2 instead of going to HBM once per query.  Any other shape keeps
+// the identity.  The map is a bijection either way; only locality depends
+// on it.
+__device__ inline int query_of_slot(int s, int queries, int group) {
+  if (group == 1 || queries % (8 * group) != 0) return s;
+  const int x = s & 7;
+  const int t = s >> 3;
+  return ((t / group) * 8 + x) * group + t % group;
+}
+
 // Row geometry for a wave reading rows of D elements of T, 16 bytes per lane:
 // kLanesPerRow lanes cover one row; one wave-wide load covers kRowsPerInstr
 // consecutive rows.

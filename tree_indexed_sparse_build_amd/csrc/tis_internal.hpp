@@ -66,11 +66,10 @@ struct RouteArgs {
   const float *summ;
   int32_t *indices;
   int32_t *trace;        // may be null
-  int64_t queries;       // B * Hq
+  int queries;           // B * Hq (< 2^31, checked by the host)
   int q_heads, kv_heads, group;
   int branching, levels, beam;
-  int64_t n_at[kMaxLevels + 1];
-  int64_t summ_off[kMaxLevels + 1];
+  int first_cut;         // first level with more than beam nodes (levels if none)
 };
 
 hipError_t launch_route(Dt dt, int head_dim, const RouteArgs &a, hipStream_t s);
@@ -86,7 +85,7 @@ struct AttendArgs {
   float *O;
   float *part;           // [queries][splits][d + 4] partial states when splits > 1
   int splits;            // workgroups per query (1: no split, no workspace)
-  int64_t queries;       // B * Hq
+  int queries;           // B * Hq (< 2^31, checked by the host)
   int64_t n_keys;
   int q_heads, kv_heads, group;
   int leaf_block, beam;
