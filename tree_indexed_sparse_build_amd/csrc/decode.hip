@@ -16,6 +16,7 @@ namespace tis {
 namespace {
 
 constexpr int kDecodeWaves = 16;
+constexpr int kDecodeWalkWaves = 8;  // waves that walk the tree (see route_walk)
 
 template <typename T, int D>
 __global__ void __launch_bounds__(kDecodeWaves * 64) k_decode(RouteArgs ra, AttendArgs aa) {
@@ -26,7 +27,7 @@ __global__ void __launch_bounds__(kDecodeWaves * 64) k_decode(RouteArgs ra, Atte
   const int qi = query_of_slot(blockIdx.x - sp * aa.queries, aa.queries, aa.group);
   const uint4 qraw = attend_q_raw<T, D>(aa, qi);  // in flight during the walk
   // every part walks the tree (the repeated summary reads hit the XCD's L2)
-  route_walk<T, D, kDecodeWaves>(ra, rsh, qi);
+  route_walk<T, D, kDecodeWaves, kDecodeWalkWaves>(ra, rsh, qi);
   if (ra.indices && sp == 0)
     write_ascending<kDecodeWaves * 64>(rsh.front, ra.beam,
                                        ra.indices + static_cast<int64_t>(qi) * ra.beam);

@@ -15,7 +15,7 @@ template <typename T, int D>
 __global__ void __launch_bounds__(kRouteWaves * 64) k_route(RouteArgs a) {
   __shared__ RouteShared<kRouteWaves> sh;
   const int qi = query_of_slot(blockIdx.x, a.queries, a.group);
-  route_walk<T, D, kRouteWaves>(a, sh, qi);
+  route_walk<T, D, kRouteWaves, kRouteWaves>(a, sh, qi);
   write_ascending<kRouteWaves * 64>(sh.front, a.beam, a.indices + static_cast<int64_t>(qi) * a.beam);
 }
 

@@ -136,12 +136,18 @@ __device__ inline void score_rows(const float *sl, int C, bool all, const int *c
 // the first level that cuts (a.first_cut); its candidates are all of its
 // nodes, so its loads need no selection and go out together with the query
 // row.
-template <typename T, int D, int NW>
+//
+// Only the first NRW waves work on the walk; all NW waves pass its barriers.
+// A workgroup's waves start one after another (on MI355X the last of 16
+// starts about a microsecond after the first), so leaving the late waves out
+// of the walk keeps them off its critical path: they only have to reach
+// each barrier, and the attention after the walk is where they are needed.
+template <typename T, int D, int NW, int NRW>
 __device__ void route_walk(const RouteArgs &a, RouteShared<NW> &sh, int qi) {
   constexpr int NT = NW * 64;
-  constexpr int LOG_NT = NW == 16 ? 10 : NW == 8 ? 9 : NW == 4 ? 8 : -1;
-  static_assert(LOG_NT > 0, "4, 8 or 16 waves");
-  static_assert(kMaxCandidates <= NT / 2, "two or more threads per candidate");
+  constexpr int LOG_NRT = NRW == 16 ? 10 : NRW == 8 ? 9 : NRW == 4 ? 8 : -1;
+  static_assert(LOG_NRT > 0 && NRW <= NW, "4, 8 or 16 walking waves");
+  static_assert(kMaxCandidates <= NRW * 64 / 2, "two or more threads per candidate");
   constexpr int LPR = D / 4;          // lanes per fp32 summary row
   constexpr int RPI = 64 / LPR;       // rows per wave-wide load
 
@@ -185,18 +191,19 @@ __device__ void route_walk(const RouteArgs &a, RouteShared<NW> &sh, int qi) {
     if (C > W) {
       const int bits = 32 - __clz(static_cast<int>(n_l) - 1);
       const float *sl = a.summ + off + head * n_l * D + col;
-      // every wave scores (more waves with fewer rows each measured faster
-      // than fewer waves with more rows), each lane taking `per` rows
-      const int per = (C + NW * RPI - 1) / (NW * RPI);
+      // the walking waves score, each lane taking `per` rows
+      const int per = (C + NRW * RPI - 1) / (NRW * RPI);
       const int *cand = sh.cand[cur];
-      if (per <= 1)
-        score_rows<T, D, 1>(sl, C, all, cand, sh.keys, bits, qr, NW, w, lane);
-      else if (per <= 2)
-        score_rows<T, D, 2>(sl, C, all, cand, sh.keys, bits, qr, NW, w, lane);
-      else if (per <= 4)
-        score_rows<T, D, 4>(sl, C, all, cand, sh.keys, bits, qr, NW, w, lane);
-      else
-        score_rows<T, D, 8>(sl, C, all, cand, sh.keys, bits, qr, NW, w, lane);
+      if (w < NRW) {
+        if (per <= 1)
+          score_rows<T, D, 1>(sl, C, all, cand, sh.keys, bits, qr, NRW, w, lane);
+        else if (per <= 2)
+          score_rows<T, D, 2>(sl, C, all, cand, sh.keys, bits, qr, NRW, w, lane);
+        else if (per <= 4)
+          score_rows<T, D, 4>(sl, C, all, cand, sh.keys, bits, qr, NRW, w, lane);
+        else
+          score_rows<T, D, 8>(sl, C, all, cand, sh.keys, bits, qr, NRW, w, lane);
+      }
       __syncthreads();
       // rank of candidate i = number of candidates with a larger key.  Each
       // candidate has a group of g adjacent lanes (g <= 8); lane p of the
@@ -204,9 +211,9 @@ __device__ void route_walk(const RouteArgs &a, RouteShared<NW> &sh, int qi) {
       // neighbouring keys: no bank conflict, and every group of the wave
       // reads the same addresses), then the group adds its counts with DPP,
       // so the ranks need no further trip through LDS.
-      {
+      if (w < NRW) {
         const int lcp = 32 - __clz(C - 1);
-        const int lg = min(LOG_NT - lcp, 3);
+        const int lg = min(LOG_NRT - lcp, 3);
         const int g = 1 << lg;
         const int i = tid >> lg;
         const int part = tid & (g - 1);
