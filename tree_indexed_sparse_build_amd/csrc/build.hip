@@ -55,11 +55,22 @@ template <int E, int LPR> __device__ inline int rowgroup_offset(int lane) {
   return off;
 }
 
-template <int CPL> __device__ inline void store_cols(float *dst, const float *f) {
-  if constexpr (CPL == 2)
+// With `through` set (the streaming-load builds of a large K) the summary
+// stores carry the device-coherence bit (a relaxed agent-scope atomic store
+// is a plain store with that bit): written through rather than left dirty
+// in L2.  Measured on MI355X: 1-2% faster on the 0.5-2 GB K builds, 6%
+// slower on a K that partly stays in the Infinity Cache, where plain stores
+// are used.  Streaming (non-temporal) stores are slower in both cases.
+template <int CPL> __device__ inline void store_cols(float *dst, const float *f, bool through) {
+  if (through) {
+#pragma unroll
+    for (int j = 0; j < CPL; ++j)
+      __hip_atomic_store(dst + j, f[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else if constexpr (CPL == 2) {
     *reinterpret_cast<float2 *>(dst) = make_float2(f[0], f[1]);
-  else
+  } else {
     dst[0] = f[0];
+  }
 }
 
 template <typename T, int D> __global__ void __launch_bounds__(1024) k_build(BuildArgs a) {
@@ -152,7 +163,8 @@ template <typename T, int D> __global__ void __launch_bounds__(1024) k_build(Bui
       float f[CPL];
 #pragma unroll
       for (int j = 0; j < CPL; ++j) f[j] = node_mean(a, lv, acc[j]);
-      store_cols<CPL>(a.summ + a.summ_off[lv] + (head * a.n_at[lv] + leaf) * D + colf, f);
+      store_cols<CPL>(a.summ + a.summ_off[lv] + (head * a.n_at[lv] + leaf) * D + colf, f,
+                      a.stream_loads != 0);
     }
     double carry[CPL];
 #pragma unroll
@@ -171,7 +183,8 @@ template <typename T, int D> __global__ void __launch_bounds__(1024) k_build(Bui
         float f[CPL];
 #pragma unroll
         for (int j = 0; j < CPL; ++j) f[j] = node_mean(a, lvl, st[k][j]);
-        store_cols<CPL>(a.summ + a.summ_off[lvl] + (head * a.n_at[lvl] + nid[k]) * D + colf, f);
+        store_cols<CPL>(a.summ + a.summ_off[lvl] + (head * a.n_at[lvl] + nid[k]) * D + colf, f,
+                        a.stream_loads != 0);
       }
 #pragma unroll
       for (int j = 0; j < CPL; ++j) {
