@@ -216,6 +216,30 @@ def main(argv=None):
     h2 = time.perf_counter()
     total_ms = start.elapsed_time(end)
     ms_step = total_ms / K_
+    # the same steps replayed from a HIP graph (one capture of build + decode):
+    # the replays must reproduce the eager outputs bit for bit
+    out_eager = plan.out.clone()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(3):
+        plan.out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(plan.out, out_eager):
+            raise RuntimeError("graph replay does not reproduce the eager step")
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(K_):
+        graph.replay()
+    end.record()
+    torch.cuda.synchronize()
+    ms_step_graph = start.elapsed_time(end) / K_
     # the same steps with route and attend as separate calls (reference)
     torch.cuda.synchronize()
     start.record()
@@ -251,7 +275,8 @@ def main(argv=None):
             uniq += len(np.unique(idx[bb, h * w.group:(h + 1) * w.group]))
     attend_dedup = uniq * w.leaf_block * w.head_dim * w.elem_bytes * 2
     log(f"step {ms_step * 1e3:.1f} us (host enqueue {(h1 - h0) / K_ * 1e6:.1f} us/step, "
-        f"wall {(h2 - h0) / K_ * 1e6:.1f} us/step); with separate route + attend calls "
+        f"wall {(h2 - h0) / K_ * 1e6:.1f} us/step); replayed from a graph "
+        f"{ms_step_graph * 1e3:.1f} us; with separate route + attend calls "
         f"{ms_step_separate * 1e3:.1f} us")
     log(f"build  {t_build.mean() * 1e6:8.2f} us  {build_gbs:8.1f} GB/s "
         f"({build_gbs / HBM_PEAK_GBS:.1%} of 8 TB/s) on {by['build'] / 1e6:.1f} MB")
@@ -303,6 +328,7 @@ def main(argv=None):
                    "frac": dec_bytes / decode_s / 1e9 / HBM_PEAK_GBS,
                    "in_step_us": ms_step * 1e3 - t_build.mean() * 1e6,
                    "step_us_separate_calls": ms_step_separate * 1e3,
+                   "step_us_graph_replay": ms_step_graph * 1e3,
                    "route_us": t_route.mean() * 1e6, "attend_us": t_attend.mean() * 1e6,
                    "attend_gbs_per_query_bytes": by["attend"] / t_attend.mean() / 1e9,
                    "attend_gbs_distinct_blocks": attend_dedup / t_attend.mean() / 1e9},

@@ -126,7 +126,8 @@ EDGE = [
     _custom("full_beam", "f32", 2, 8, 4, 16, d=64),
     # long leaf blocks (several batches of rows per wave)
     _custom("long_leaf", "bf16", 2, 200, 2, 2),
-    # deep binary tree whose chunks climb through the arrival counters
+    # deep binary tree: the levels above the chunk roots take the small
+    # per-level kernels
     _custom("deep_binary", "bf16", 2, 4, 9, 6, d=64, Hkv=3, G=1),
     # many heads, GQA group 8, batch 3
     _custom("gqa8_batch3", "bf16", 4, 32, 3, 6, B=3, Hkv=2, G=8),
@@ -250,3 +251,59 @@ def test_workspace_reuse_across_geometries(tis):
         for ws in tis.ops._workspaces.values():
             ws.fill_(0x7F)  # garbage (large finite doubles) must not matter
         check_case(tis, w)
+
+
+GRAPH_CASES = [
+    _custom("graph_split", "bf16", 4, 64, 4, 64, Hkv=2, G=3, seed=31),   # split + combine
+    _custom("graph_deep", "bf16", 2, 4, 9, 6, d=64, Hkv=3, G=1, seed=32),  # per-level build kernels
+    workloads.small("deep_planted", levels=4, kv_heads=2),                # top-level build kernel
+]
+
+
+@pytest.mark.parametrize("w", GRAPH_CASES, ids=[w.name for w in GRAPH_CASES])
+def test_graph_replay_matches_eager(tis, w):
+    """A step (build, fused decode, route, attend) captured into a HIP graph
+    reproduces the eager results bit for bit on every replay, with other
+    eager work on the same buffers between the replays."""
+    x = workloads.generate(w)
+    dev = "cuda"
+    Q = tis.from_storage(x["Q"], w.dtype, dev)
+    K = tis.from_storage(x["K"], w.dtype, dev)
+    V = tis.from_storage(x["V"], w.dtype, dev)
+    plan = tis.DecodePlan(Q, K, V, w.branching, w.leaf_block, w.levels, w.beam)
+
+    def step():
+        plan.build()
+        plan.decode()
+        fused = plan.out.clone()
+        plan.route()
+        plan.attend()
+        return fused
+
+    fused_eager = step()
+    torch.cuda.synchronize()
+    ref = {"summ": plan.summaries.clone(), "idx": plan.indices.clone(),
+           "out": plan.out.clone(), "fused": fused_eager}
+    _say(f"{w.name}: eager step done")
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    with torch.cuda.graph(graph):
+        fused_g = step()
+    for rep in range(3):
+        # eager work that overwrites every output between the replays
+        plan.summaries.fill_(float("nan"))
+        plan.indices.fill_(-7)
+        plan.out.fill_(float("nan"))
+        fused_g.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(plan.summaries.view(torch.int32), ref["summ"].view(torch.int32)), rep
+        assert torch.equal(plan.indices, ref["idx"]), rep
+        assert torch.equal(plan.out.view(torch.int32), ref["out"].view(torch.int32)), rep
+        assert torch.equal(fused_g.view(torch.int32), ref["fused"].view(torch.int32)), rep
+        _say(f"{w.name}: replay {rep} matches the eager step")

@@ -217,7 +217,8 @@ def from_storage(arr, dtype: str, device="cuda") -> torch.Tensor:
 class DecodePlan:
     """Pre-allocated buffers and C-ABI arguments for repeated build / route /
     attend over fixed device tensors, so a call costs one C-ABI call and no
-    allocation (used by timing loops)."""
+    allocation (used by timing loops).  Each call goes to the current stream,
+    so a step can be captured into a graph and replayed."""
 
     def __init__(self, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, branching: int,
                  leaf_block: int, levels: int, beam: int, scale: Optional[float] = None):
@@ -246,7 +247,7 @@ class DecodePlan:
         self.indices = torch.empty((B, Hq, beam), dtype=torch.int32, device=K.device)
         self.out = torch.empty((B, Hq, d), dtype=torch.float32, device=K.device)
         self.tree_c = TisTree(0, 0, 0, 0, 0, 0, 0, self.summaries.data_ptr())
-        self.stream = _stream(K.device)
+        self.device = K.device
 
     def build(self) -> None:
         B, H, N, d, b, Lb, lv = self.geom
@@ -254,12 +255,12 @@ class DecodePlan:
         check(self._lib.tis_tree_build(self.K.data_ptr(), self.dt, B, H, N, d, b, Lb, lv,
                                        ctypes.byref(self.tree_c),
                                        None if ws is None else ws.data_ptr(),
-                                       0 if ws is None else ws.numel(), self.stream))
+                                       0 if ws is None else ws.numel(), _stream(self.device)))
 
     def route(self) -> None:
         check(self._lib.tis_tree_route(self.Q.data_ptr(), self.dt, self.q_heads,
                                        ctypes.byref(self.tree_c), self.beam,
-                                       self.indices.data_ptr(), None, self.stream))
+                                       self.indices.data_ptr(), None, _stream(self.device)))
 
     def attend(self) -> None:
         B, H, N, d, b, Lb, lv = self.geom
@@ -270,7 +271,7 @@ class DecodePlan:
                                         None if self.ws_attend is None
                                         else self.ws_attend.data_ptr(),
                                         0 if self.ws_attend is None
-                                        else self.ws_attend.numel(), self.stream))
+                                        else self.ws_attend.numel(), _stream(self.device)))
 
     def decode(self) -> None:
         """Route and attend in one launch (indices not written)."""
@@ -280,7 +281,7 @@ class DecodePlan:
                                         self.dt, self.q_heads, ctypes.byref(self.tree_c),
                                         self.beam, self.scale, self.out.data_ptr(), None,
                                         None if ws is None else ws.data_ptr(),
-                                        0 if ws is None else ws.numel(), self.stream))
+                                        0 if ws is None else ws.numel(), _stream(self.device)))
 
     def tree(self) -> Tree:
         B, H, N, d, b, Lb, lv = self.geom
