@@ -184,6 +184,89 @@ const char *tis_last_error(void);
 /* Library version string, e.g. "tis 0.1.0 gfx950". */
 const char *tis_version(void);
 
+/* ------------------------------------------------------------------------
+ * Tree over a growing KV cache
+ *
+ * The ZHA abstract describes the index as living over the KV cache and
+ * growing deeper step by step as the context lengthens; decode appends keys
+ * one step at a time (ALHR post).  These calls keep a tree over the first
+ * n_keys rows of a cache that has room for `capacity` keys per head:
+ *   - depth: the fewest levels lv >= 1 with b^lv * L >= n_keys, so the tree
+ *     gains a level exactly when n_keys first exceeds b^lv * L;
+ *   - node n of level l covers keys [n*M_l, (n+1)*M_l) cut at n_keys, with
+ *     M_l = b^(lv-l) * L, and exists when that range is not empty (leaf j
+ *     holds keys [j*L, min((j+1)*L, n_keys)));
+ *   - summary = the exact mean of the keys the node covers, rounded once to
+ *     float32 (as for the full tree);
+ *   - route: each level scores the existing children of the nodes kept
+ *     above and keeps the best min(beam, their number), (score desc, node
+ *     index asc); attention runs over the keys of the kept leaves.
+ * With n_keys = b^lv * L these are the full-tree definitions exactly.
+ *
+ * Storage (caller-owned device memory, sized by the two queries below):
+ *   K, V       [B][Hkv][capacity][d], element type dtype; rows past n_keys
+ *              are never read
+ *   summaries  float32, height-major so that no level moves when the tree
+ *              deepens: for height h = 0 (leaves) .. H-1 a block
+ *              [B][Hkv][ceil(capacity / (L*b^h))][d], where H is the depth
+ *              of a full cache; level l of a tree of depth lv lives at
+ *              height lv - l, node n at row n of its (batch, head) block
+ *   state      float64 [B][Hkv][H][d]: for every height h, the exact sum of
+ *              the keys of the node that holds key n_keys (the open node;
+ *              zero when n_keys is a multiple of L*b^h).  Appends start from
+ *              it, which keeps every summary an exact mean rounded once.
+ * Summaries are kept for every height up to H-1 whatever the current depth,
+ * so a deeper tree finds its upper levels already in place.
+ * --------------------------------------------------------------------- */
+
+typedef struct tis_cache_tree {
+  int32_t batch, kv_heads, head_dim, branching, leaf_block;
+  int32_t capacity;  /* keys per (batch, KV head) the cache has room for     */
+  int32_t n_keys;    /* keys in the tree: set by reset (0) and append        */
+  int32_t levels;    /* depth over n_keys (0 while empty): set by the library */
+  float *summaries;  /* tis_cache_tree_summary_bytes() bytes                 */
+  double *state;     /* tis_cache_tree_state_bytes() bytes                   */
+} tis_cache_tree;
+
+/* Bytes of the summaries / state buffers of a cache with this geometry
+ * (d 64 or 128, b >= 2, L >= 1, capacity >= 1, the full-cache depth H at
+ * most 16); 0 if invalid or overflowing. */
+size_t tis_cache_tree_summary_bytes(int batch, int kv_heads, int head_dim, int branching,
+                                    int leaf_block, int capacity);
+size_t tis_cache_tree_state_bytes(int batch, int kv_heads, int head_dim, int branching,
+                                  int leaf_block, int capacity);
+
+/* Empties the tree: n_keys = levels = 0 and the state zeroed (by a kernel
+ * on `stream`).  The caller fills in the geometry fields and both pointers
+ * first.  Summaries need no clearing: only existing nodes are ever read. */
+tis_status tis_cache_tree_reset(tis_cache_tree *tree, void *stream);
+
+/* Adds keys [n_keys, n_keys + n_new) of K (already written to the cache) to
+ * the tree, then sets n_keys += n_new and levels to the new depth (host-side
+ * fields, updated when the work is enqueued).  Rewrites the summary of every
+ * node that gains a key, at every height, and the state; O(n_new * d + H * d
+ * * (leaves touched)) work, one workgroup per (batch, KV head).
+ * Requires 0 <= n_new <= capacity - n_keys.  n_new = 0 does nothing. */
+tis_status tis_cache_tree_append(const void *K, tis_dtype dtype, int n_new,
+                                 tis_cache_tree *tree, void *stream);
+
+/* tis_tree_route over the tree of a cache (n_keys >= 1).  indices [B][Hq]
+ * [beam]: the kept leaves ascending, padded with -1 when the tree has fewer
+ * than beam leaves; trace (optional) [B][Hq][levels][beam] as for
+ * tis_tree_route.  Requires beam >= 1 and beam * b <= TIS_MAX_CANDIDATES. */
+tis_status tis_cache_tree_route(const void *Q, tis_dtype dtype, int q_heads,
+                                const tis_cache_tree *tree, int beam, int32_t *indices,
+                                int32_t *trace, void *stream);
+
+/* tis_tree_decode over the tree of a cache: route and attend in one launch,
+ * O [B][Hq][d] float32, indices optional as for tis_cache_tree_route.
+ * workspace: tis_decode_workspace_bytes(batch, q_heads, head_dim, beam,
+ * leaf_block) bytes, as for tis_tree_decode. */
+tis_status tis_cache_tree_decode(const void *Q, const void *K, const void *V, tis_dtype dtype,
+                                 int q_heads, const tis_cache_tree *tree, int beam, float scale,
+                                 float *O, int32_t *indices, void *workspace,
+                                 size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -209,3 +209,112 @@ def _decode(lib, Q=FAKE, K=FAKE, V=FAKE, dt=_lib.TIS_BF16, Hq=2, tree=None, beam
 def test_decode_rejects(lib, kw, status):
     assert _decode(lib, **kw) == status
     assert lib.tis_last_error().decode()
+
+
+# ------------------------------------------------------- growing cache --
+
+def test_cache_tree_bytes(lib):
+    # capacity 40000, b 8, L 64: heights 0..3 (8^4 * 64 >= 40000), rows
+    # ceil(40000 / 64) = 625, 79, 10, 2 per head
+    heads, d = 4 * 8, 128
+    assert lib.tis_cache_tree_summary_bytes(4, 8, d, 8, 64, 40000) == 4 * d * heads * (625 + 79 + 10 + 2)
+    assert lib.tis_cache_tree_state_bytes(4, 8, d, 8, 64, 40000) == 8 * d * heads * 4
+    # a cache of one leaf: one height with one row
+    assert lib.tis_cache_tree_summary_bytes(1, 1, 64, 2, 16, 10) == 4 * 64
+    assert lib.tis_cache_tree_state_bytes(1, 1, 64, 2, 16, 10) == 8 * 64
+    # invalid geometry -> 0
+    assert lib.tis_cache_tree_summary_bytes(1, 1, 64, 1, 16, 100) == 0
+    assert lib.tis_cache_tree_summary_bytes(1, 1, 96, 2, 16, 100) == 0
+    assert lib.tis_cache_tree_state_bytes(1, 1, 64, 2, 16, 0) == 0
+    # a full cache deeper than 16 levels
+    assert lib.tis_cache_tree_state_bytes(1, 1, 64, 2, 1, 1 << 20) == 0
+
+
+def _ctree(summ=FAKE, state=FAKE, B=1, H=1, d=64, b=2, L=16, C=1000, n=0, lv=0):
+    return _lib.TisCacheTree(B, H, d, b, L, C, n, lv, summ, state)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(summ=None), _lib.TIS_E_NULL),
+    (dict(state=None), _lib.TIS_E_NULL),
+    (dict(b=1), _lib.TIS_E_SHAPE),
+    (dict(d=32), _lib.TIS_E_UNSUPPORTED),
+    (dict(C=0), _lib.TIS_E_SHAPE),
+    (dict(state=FAKE + 8), _lib.TIS_E_ALIGN),
+])
+def test_cache_reset_rejects(lib, kw, status):
+    t = _ctree(**kw)
+    assert lib.tis_cache_tree_reset(ctypes.byref(t), None) == status
+    assert lib.tis_last_error().decode()
+
+
+@pytest.mark.parametrize("tree_kw,call_kw,status", [
+    (dict(), dict(K=None), _lib.TIS_E_NULL),
+    (dict(summ=None), dict(), _lib.TIS_E_NULL),
+    (dict(), dict(dt=5), _lib.TIS_E_DTYPE),
+    (dict(), dict(n_new=-1), _lib.TIS_E_SHAPE),
+    (dict(), dict(n_new=1001), _lib.TIS_E_SHAPE),
+    (dict(n=990, lv=6), dict(n_new=11), _lib.TIS_E_SHAPE),   # past the capacity
+    (dict(n=100, lv=2), dict(n_new=1), _lib.TIS_E_SHAPE),    # 100 keys need 3 levels
+    (dict(n=-1), dict(n_new=1), _lib.TIS_E_SHAPE),
+    (dict(), dict(K=FAKE + 4, n_new=1), _lib.TIS_E_ALIGN),
+])
+def test_cache_append_rejects(lib, tree_kw, call_kw, status):
+    t = _ctree(**tree_kw)
+    a = dict(K=FAKE, dt=_lib.TIS_BF16, n_new=1)
+    a.update(call_kw)
+    assert lib.tis_cache_tree_append(a["K"], a["dt"], a["n_new"], ctypes.byref(t), None) == status
+    assert lib.tis_last_error().decode()
+    assert t.n_keys == tree_kw.get("n", 0)  # a rejected append changes nothing
+
+
+def test_cache_append_of_nothing_is_a_no_op(lib):
+    t = _ctree(n=100, lv=3)
+    assert lib.tis_cache_tree_append(FAKE, _lib.TIS_BF16, 0, ctypes.byref(t), None) == _lib.TIS_OK
+    assert (t.n_keys, t.levels) == (100, 3)
+
+
+@pytest.mark.parametrize("tree_kw,call_kw,status", [
+    (dict(), dict(), _lib.TIS_E_SHAPE),                      # empty tree
+    (dict(n=100, lv=3), dict(Q=None), _lib.TIS_E_NULL),
+    (dict(n=100, lv=3), dict(idx=None), _lib.TIS_E_NULL),
+    (dict(n=100, lv=3, state=None), dict(), _lib.TIS_E_NULL),
+    (dict(n=100, lv=3), dict(dt=2), _lib.TIS_E_DTYPE),
+    (dict(n=100, lv=4), dict(), _lib.TIS_E_SHAPE),           # levels do not match n_keys
+    (dict(n=100, lv=3), dict(Hq=0), _lib.TIS_E_SHAPE),
+    (dict(n=100, lv=3, H=2), dict(Hq=3), _lib.TIS_E_SHAPE),
+    (dict(n=100, lv=3), dict(beam=0), _lib.TIS_E_SHAPE),
+    (dict(n=100, lv=3), dict(beam=129), _lib.TIS_E_UNSUPPORTED),
+    (dict(n=100, lv=3), dict(Q=FAKE + 2), _lib.TIS_E_ALIGN),
+    (dict(n=100, lv=3), dict(idx=FAKE + 2), _lib.TIS_E_ALIGN),
+])
+def test_cache_route_rejects(lib, tree_kw, call_kw, status):
+    t = _ctree(**tree_kw)
+    a = dict(Q=FAKE, dt=_lib.TIS_BF16, Hq=2, beam=4, idx=FAKE, trace=None)
+    a.update(call_kw)
+    assert lib.tis_cache_tree_route(a["Q"], a["dt"], a["Hq"], ctypes.byref(t), a["beam"], a["idx"],
+                                    a["trace"], None) == status
+    assert lib.tis_last_error().decode()
+
+
+@pytest.mark.parametrize("tree_kw,call_kw,status", [
+    (dict(), dict(), _lib.TIS_E_SHAPE),                      # empty tree
+    (dict(n=100, lv=3), dict(V=None), _lib.TIS_E_NULL),
+    (dict(n=100, lv=3), dict(O=None), _lib.TIS_E_NULL),
+    (dict(n=100, lv=3), dict(scale=float("nan")), _lib.TIS_E_SHAPE),
+    (dict(n=100, lv=3), dict(K=FAKE + 8), _lib.TIS_E_ALIGN),
+    (dict(n=100, lv=3), dict(beam=200), _lib.TIS_E_UNSUPPORTED),
+    # 2 queries, beam 64 over leaves of 128 keys: split, so a workspace is needed
+    (dict(n=30000, lv=4, d=128, b=4, L=128, C=30000), dict(beam=64, Hq=2), _lib.TIS_E_NULL),
+    (dict(n=30000, lv=4, d=128, b=4, L=128, C=30000), dict(beam=64, Hq=2, ws=FAKE, wsb=8),
+     _lib.TIS_E_WORKSPACE),
+])
+def test_cache_decode_rejects(lib, tree_kw, call_kw, status):
+    t = _ctree(**tree_kw)
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, dt=_lib.TIS_BF16, Hq=2, beam=4, scale=0.0, O=FAKE, idx=None,
+             ws=None, wsb=0)
+    a.update(call_kw)
+    assert lib.tis_cache_tree_decode(a["Q"], a["K"], a["V"], a["dt"], a["Hq"], ctypes.byref(t),
+                                     a["beam"], a["scale"], a["O"], a["idx"], a["ws"], a["wsb"],
+                                     None) == status
+    assert lib.tis_last_error().decode()

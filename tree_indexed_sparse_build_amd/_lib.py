@@ -31,6 +31,14 @@ class TisTree(ctypes.Structure):
                 ("levels", ctypes.c_int32), ("summaries", ctypes.c_void_p)]
 
 
+class TisCacheTree(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("branching", ctypes.c_int32),
+                ("leaf_block", ctypes.c_int32), ("capacity", ctypes.c_int32),
+                ("n_keys", ctypes.c_int32), ("levels", ctypes.c_int32),
+                ("summaries", ctypes.c_void_p), ("state", ctypes.c_void_p)]
+
+
 class TisError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
@@ -53,6 +61,15 @@ SIGNATURES = {
     "tis_tree_decode": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, ctypes.POINTER(TisTree), _c_int,
                                  _c_float, _vp, _vp, _vp, _c_size, _vp]),
     "tis_decode_workspace_bytes": (_c_size, [_c_int] * 5),
+    "tis_cache_tree_summary_bytes": (_c_size, [_c_int] * 6),
+    "tis_cache_tree_state_bytes": (_c_size, [_c_int] * 6),
+    "tis_cache_tree_reset": (_c_int, [ctypes.POINTER(TisCacheTree), _vp]),
+    "tis_cache_tree_append": (_c_int, [_vp, _c_int, _c_int, ctypes.POINTER(TisCacheTree), _vp]),
+    "tis_cache_tree_route": (_c_int, [_vp, _c_int, _c_int, ctypes.POINTER(TisCacheTree), _c_int,
+                                      _vp, _vp, _vp]),
+    "tis_cache_tree_decode": (_c_int, [_vp, _vp, _vp, _c_int, _c_int,
+                                       ctypes.POINTER(TisCacheTree), _c_int, _c_float, _vp, _vp,
+                                       _vp, _c_size, _vp]),
     "tis_last_error": (ctypes.c_char_p, []),
     "tis_version": (ctypes.c_char_p, []),
 }

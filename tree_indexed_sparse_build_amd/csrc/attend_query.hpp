@@ -45,11 +45,12 @@ template <typename T, int D> __device__ inline uint4 attend_q_raw(const AttendAr
 
 // Attention of query qi over the leaf blocks slots[s] (s < nslots) whose
 // use[s] is nonzero (use == nullptr: all), every wave of the workgroup
-// taking part.  With part == nullptr it writes row qi of O (NaN if `bad`,
+// taking part (RAGGED: the last block of a growing cache may hold fewer
+// than L keys).  With part == nullptr it writes row qi of O (NaN if `bad`,
 // zero if no slot is used); otherwise it writes the workgroup's partial
 // softmax state to part: m (log2 units), l (NaN if `bad`), two pad words,
 // acc[D], for a later log-sum-exp merge with the query's other parts.
-template <typename T, int D>
+template <typename T, int D, bool RAGGED = false>
 __device__ void attend_query(const AttendArgs &a, AttendShared<T, D> &sh, int qi,
                              uint4 qraw, const int *slots, const int *use, int nslots,
                              bool bad, float *part) {
@@ -68,8 +69,8 @@ __device__ void attend_query(const AttendArgs &a, AttendShared<T, D> &sh, int qi
 
   float q[E];
   Vec16<T>::unpack(qraw, q);
-  const T *kh = static_cast<const T *>(a.K) + head * a.n_keys * D + col;
-  const T *vh = static_cast<const T *>(a.V) + head * a.n_keys * D + col;
+  const T *kh = static_cast<const T *>(a.K) + head * a.key_stride * D + col;
+  const T *vh = static_cast<const T *>(a.V) + head * a.key_stride * D + col;
   const int nc = (L + RB - 1) / RB;
   const int units = nslots * nc;
 
@@ -82,17 +83,21 @@ __device__ void attend_query(const AttendArgs &a, AttendShared<T, D> &sh, int qi
     const int s = u / nc;
     if (use && !use[s]) continue;
     const int r0 = (u - s * nc) * RB;
-    const int64_t rowb = static_cast<int64_t>(slots[s]) * L + r0;
+    const int64_t blk0 = static_cast<int64_t>(slots[s]) * L;
+    const int64_t rowb = blk0 + r0;
+    // keys of the block in use: L, or fewer in the last block of a cache
+    const int len = RAGGED ? static_cast<int>(min(static_cast<int64_t>(L), a.n_keys - blk0)) : L;
+    if (RAGGED && r0 >= len) continue;
     uint4 kv[U], vv[U];
 #pragma unroll
     for (int i = 0; i < U; ++i) {
       const int row = r0 + i * R + rsub;
-      kv[i] = row < L ? load16(kh + (rowb + i * R + rsub) * D) : make_uint4(0u, 0u, 0u, 0u);
+      kv[i] = row < len ? load16(kh + (rowb + i * R + rsub) * D) : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
     for (int i = 0; i < U; ++i) {
       const int row = r0 + i * R + rsub;
-      vv[i] = row < L ? load16(vh + (rowb + i * R + rsub) * D) : make_uint4(0u, 0u, 0u, 0u);
+      vv[i] = row < len ? load16(vh + (rowb + i * R + rsub) * D) : make_uint4(0u, 0u, 0u, 0u);
     }
     float part[U];
 #pragma unroll
@@ -107,7 +112,7 @@ __device__ void attend_query(const AttendArgs &a, AttendShared<T, D> &sh, int qi
     // lane holds the score of row r0 + kk * R + rsub
     const float sc = group_transpose_reduce<U, LPR>(part, lane);
     const int kk = (lane % LPR) / REP;
-    const bool valid = r0 + kk * R + rsub < L;
+    const bool valid = r0 + kk * R + rsub < len;
     const float x = valid ? sc * a.scale_log2 : -INFINITY;
     const float mnew = fmaxf(m, wave_max(x));
     // hardware 2^x: results below 2^-126 flush to zero, which leaves the

@@ -18,7 +18,7 @@ namespace {
 constexpr int kDecodeWaves = 16;
 constexpr int kDecodeWalkWaves = 8;  // waves that walk the tree (see route_walk)
 
-template <typename T, int D>
+template <typename T, int D, bool CACHE>
 __global__ void __launch_bounds__(kDecodeWaves * 64) k_decode(RouteArgs ra, AttendArgs aa) {
   __shared__ RouteShared<kDecodeWaves> rsh;
   __shared__ AttendShared<T, D> ash;
@@ -27,36 +27,45 @@ __global__ void __launch_bounds__(kDecodeWaves * 64) k_decode(RouteArgs ra, Atte
   const int qi = query_of_slot(blockIdx.x - sp * aa.queries, aa.queries, aa.group);
   const uint4 qraw = attend_q_raw<T, D>(aa, qi);  // in flight during the walk
   // every part walks the tree (the repeated summary reads hit the XCD's L2)
-  route_walk<T, D, kDecodeWaves, kDecodeWalkWaves>(ra, rsh, qi);
-  if (ra.indices && sp == 0)
-    write_ascending<kDecodeWaves * 64>(rsh.front, ra.beam,
-                                       ra.indices + static_cast<int64_t>(qi) * ra.beam);
-  const int W = ra.beam;
-  const int s0 = sp * W / aa.splits;
-  const int s1 = (sp + 1) * W / aa.splits;
+  const int kept = route_walk<T, D, kDecodeWaves, kDecodeWalkWaves, CACHE>(ra, rsh, qi);
+  if (ra.indices && sp == 0) {
+    int32_t *out = ra.indices + static_cast<int64_t>(qi) * ra.beam;
+    write_ascending<kDecodeWaves * 64>(rsh.front, kept, out);
+    for (int k = kept + static_cast<int>(threadIdx.x); k < ra.beam; k += kDecodeWaves * 64)
+      out[k] = -1;
+  }
+  const int s0 = sp * kept / aa.splits;
+  const int s1 = (sp + 1) * kept / aa.splits;
   float *part = aa.splits > 1
                     ? aa.part + (static_cast<int64_t>(qi) * aa.splits + sp) * (D + kPartHeader)
                     : nullptr;
-  attend_query<T, D>(aa, ash, qi, qraw, rsh.front + s0, nullptr, s1 - s0, false, part);
+  attend_query<T, D, CACHE>(aa, ash, qi, qraw, rsh.front + s0, nullptr, s1 - s0, false, part);
+}
+
+template <bool CACHE>
+hipError_t launch_decode_layout(Dt dt, int head_dim, const RouteArgs &ra, const AttendArgs &aa,
+                                hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(ra.queries) * static_cast<unsigned>(aa.splits));
+  const dim3 block(kDecodeWaves * 64);
+  if (dt == Dt::BF16 && head_dim == 128)
+    hipLaunchKernelGGL((k_decode<bf16_bits, 128, CACHE>), grid, block, 0, s, ra, aa);
+  else if (dt == Dt::BF16 && head_dim == 64)
+    hipLaunchKernelGGL((k_decode<bf16_bits, 64, CACHE>), grid, block, 0, s, ra, aa);
+  else if (dt == Dt::F32 && head_dim == 128)
+    hipLaunchKernelGGL((k_decode<float, 128, CACHE>), grid, block, 0, s, ra, aa);
+  else if (dt == Dt::F32 && head_dim == 64)
+    hipLaunchKernelGGL((k_decode<float, 64, CACHE>), grid, block, 0, s, ra, aa);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_decode(Dt dt, int head_dim, const RouteArgs &ra, const AttendArgs &aa,
                          hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(ra.queries) * static_cast<unsigned>(aa.splits));
-  const dim3 block(kDecodeWaves * 64);
-  if (dt == Dt::BF16 && head_dim == 128)
-    hipLaunchKernelGGL((k_decode<bf16_bits, 128>), grid, block, 0, s, ra, aa);
-  else if (dt == Dt::BF16 && head_dim == 64)
-    hipLaunchKernelGGL((k_decode<bf16_bits, 64>), grid, block, 0, s, ra, aa);
-  else if (dt == Dt::F32 && head_dim == 128)
-    hipLaunchKernelGGL((k_decode<float, 128>), grid, block, 0, s, ra, aa);
-  else if (dt == Dt::F32 && head_dim == 64)
-    hipLaunchKernelGGL((k_decode<float, 64>), grid, block, 0, s, ra, aa);
-  else
-    return hipErrorInvalidValue;
-  hipError_t e = hipGetLastError();
+  hipError_t e = ra.cache ? launch_decode_layout<true>(dt, head_dim, ra, aa, s)
+                          : launch_decode_layout<false>(dt, head_dim, ra, aa, s);
   if (e != hipSuccess || aa.splits <= 1) return e;
   return launch_combine(head_dim, aa, s);
 }

@@ -67,8 +67,69 @@ template <> struct QRaw<bf16_bits> {
 // Shared memory of one query's walk, for a workgroup of NW waves.
 template <int NW> struct RouteShared {
   uint64_t keys[kMaxCandidates];
-  int cand[2][kMaxCandidates];     // node id of every candidate, this level / next
+  int cand[2][kMaxCandidates];     // node id of every candidate (-1: hole), this level / next
   int front[kMaxCandidates];       // kept nodes of the level, in rank order
+  int holes[3];                    // holes among a level's candidates, slot l mod 3
+};
+
+// Sizes and summary rows of the levels of one (batch, KV head), walked from
+// level l0 downwards; CACHE selects the growing-cache layout.  Scalar
+// arithmetic only (no argument-table loads).
+template <bool CACHE> struct LevelCursor {
+  int64_t exist;   // nodes of the current level that exist
+  int64_t rows;    // summary rows per head in the current level's block
+  int64_t off;     // element offset of the current level's block
+  int64_t span;    // keys under one node of the current level (growing cache)
+  int64_t heads;
+  int64_t n_keys, capacity;
+  int b;
+
+  __device__ void init(const RouteArgs &ra, int l0, int d) {
+    b = ra.branching;
+    heads = static_cast<int64_t>(ra.queries / ra.q_heads) * ra.kv_heads;
+    n_keys = ra.n_keys;
+    capacity = ra.capacity;
+    if constexpr (!CACHE) {
+      // full tree: level l has b^l nodes, levels 1 .. l-1 come first
+      int64_t n = 1;
+      off = 0;
+      for (int l = 1; l < l0; ++l) {
+        n *= b;
+        off += heads * n * d;
+      }
+      exist = rows = n * b;
+      span = 0;
+    } else {
+      // growing cache: level l is height h = levels - l, heights 0 .. h-1 first
+      const int h0 = ra.levels - l0;
+      span = ra.leaf_block;
+      off = 0;
+      for (int h = 0; h < h0; ++h) {
+        off += heads * ((capacity + span - 1) / span) * d;
+        span *= b;
+      }
+      rows = (capacity + span - 1) / span;
+      exist = (n_keys + span - 1) / span;
+    }
+  }
+  // nodes of the next level down that exist
+  __device__ int64_t exist_below() const {
+    if constexpr (!CACHE) return exist * b;
+    const int64_t s = span / b;
+    return (n_keys + s - 1) / s;
+  }
+  __device__ void down(int d) {
+    if constexpr (!CACHE) {
+      off += heads * rows * d;
+      rows *= b;
+      exist = rows;
+    } else {
+      exist = exist_below();
+      span /= b;
+      rows = (capacity + span - 1) / span;
+      off -= heads * rows * d;
+    }
+  }
 };
 
 // Writes the n distinct values v[0..n) to out[0..n) in ascending order (each
@@ -83,12 +144,12 @@ template <int NT> __device__ inline void write_ascending(const int *v, int n, in
 }
 
 // Scores the C candidates of one level: candidate p is node p of the level
-// (all) or node cand[p], and its key goes to keys[p].  The nsw waves of the
+// (all) or node cand[p] (-1: a hole), and its key goes to keys[p].  The nsw waves of the
 // workgroup cover UU rows per lane per pass, UU just large enough for C, and
 // every load of a pass is issued before any is used: rows past C read
 // candidate 0 again (always a valid address) and their scores are dropped,
 // so no branch splits the loads.
-template <typename T, int D, int UU>
+template <typename T, int D, int UU, bool HOLES>
 __device__ inline void score_rows(const float *sl, int C, bool all, const int *cand,
                                   uint64_t *keys, int bits, const QRaw<T> &qr, int nsw,
                                   int w, int lane) {
@@ -108,8 +169,10 @@ __device__ inline void score_rows(const float *sl, int C, bool all, const int *c
     }
     float4 v[UU];
 #pragma unroll
-    for (int u = 0; u < UU; ++u)
-      v[u] = *reinterpret_cast<const float4 *>(sl + static_cast<int64_t>(node[u]) * D);
+    for (int u = 0; u < UU; ++u) {
+      const int nd = HOLES && node[u] < 0 ? 0 : node[u];  // a hole reads node 0
+      v[u] = *reinterpret_cast<const float4 *>(sl + static_cast<int64_t>(nd) * D);
+    }
     double q[4];
     qr.widen(q);
     double part[UU];
@@ -125,25 +188,33 @@ __device__ inline void score_rows(const float *sl, int C, bool all, const int *c
     const double s = group_transpose_reduce<UU, LPR>(part, lane);
     const int k = (lane % LPR) / REP;
     const int pos = base + (k * nsw + w) * RPI + rsub;
-    if ((lane % REP) == 0 && pos < C) keys[pos] = score_key(s, all ? pos : cand[pos], bits);
+    if ((lane % REP) == 0 && pos < C) {
+      const int nd = all ? pos : cand[pos];
+      // a hole (a child past the end of a growing cache) gets key 0, below
+      // every real key, so it is never ranked among the kept
+      keys[pos] = HOLES && nd < 0 ? 0ull : score_key(s, nd, bits);
+    }
   }
 }
 
 // Walks query qi down the tree (every wave of the NW-wave workgroup takes
-// part).  On return, after a barrier, sh.front[0 .. beam) holds the kept
-// leaves in rank order, best first.  Levels whose candidate set is no larger
-// than the beam keep every node whatever the scores, so the walk starts at
-// the first level that cuts (a.first_cut); its candidates are all of its
-// nodes, so its loads need no selection and go out together with the query
-// row.
+// part) and returns how many leaves it keeps (beam, or fewer when a growing
+// cache has fewer leaves).  On return, after a barrier, sh.front[0 .. that)
+// holds the kept leaves in rank order, best first.  Levels whose existing
+// nodes number no more than the beam keep them all whatever the scores, so
+// the walk starts at the first level l0 that cuts (a.first_cut); its
+// candidates are all of its nodes, so its loads need no selection and go out
+// together with the query row.  Below l0 the candidates are the children of
+// the kept nodes; in a growing cache the last existing node may have fewer
+// children, and the missing ones are holes that score below every node.
 //
 // Only the first NRW waves work on the walk; all NW waves pass its barriers.
 // A workgroup's waves start one after another (on MI355X the last of 16
 // starts about a microsecond after the first), so leaving the late waves out
 // of the walk keeps them off its critical path: they only have to reach
 // each barrier, and the attention after the walk is where they are needed.
-template <typename T, int D, int NW, int NRW>
-__device__ void route_walk(const RouteArgs &a, RouteShared<NW> &sh, int qi) {
+template <typename T, int D, int NW, int NRW, bool CACHE>
+__device__ int route_walk(const RouteArgs &a, RouteShared<NW> &sh, int qi) {
   constexpr int NT = NW * 64;
   constexpr int LOG_NRT = NRW == 16 ? 10 : NRW == 8 ? 9 : NRW == 4 ? 8 : -1;
   static_assert(LOG_NRT > 0 && NRW <= NW, "4, 8 or 16 walking waves");
@@ -165,44 +236,65 @@ __device__ void route_walk(const RouteArgs &a, RouteShared<NW> &sh, int qi) {
 
   QRaw<T> qr;
   qr.load(static_cast<const T *>(a.Q) + static_cast<int64_t>(qi) * D + col);
+
+  LevelCursor<CACHE> lc;
+  lc.init(a, l0, D);
   if (a.trace) {
-    int n_at_l = 1;
+    // levels above l0 keep every node that exists
     for (int l = 1; l < l0; ++l) {
-      n_at_l *= b;  // levels before l0 have at most beam nodes
+      int64_t span = a.leaf_block;
+      for (int h = 0; h < lv - l; ++h) span *= b;
+      int64_t n = 1;
+      for (int k = 0; k < l; ++k) n *= b;
+      const int64_t e = CACHE ? (a.n_keys + span - 1) / span : n;
       int32_t *tr = a.trace + (static_cast<int64_t>(qi) * lv + (l - 1)) * W;
-      for (int k = tid; k < W; k += NT) tr[k] = k < n_at_l ? k : -1;
+      for (int k = tid; k < W; k += NT) tr[k] = k < e ? k : -1;
     }
   }
+  // slot l mod 3 holds the holes among level l's candidates: level l reads
+  // its slot, writes the next one and clears the one after, which no level
+  // touches between two barriers of this one
+  if (CACHE && tid == 0) sh.holes[0] = sh.holes[1] = sh.holes[2] = 0;
 
-  // level sizes and offsets follow from b alone (scalar arithmetic, no
-  // loads): n_l = b^l, and level l starts after heads * d * (b + ... + b^(l-1))
-  const int64_t heads = static_cast<int64_t>(a.queries / a.q_heads) * a.kv_heads;
-  int64_t n_l = 1, off = 0;
-  for (int l = 1; l < l0; ++l) {
-    n_l *= b;
-    off += heads * n_l * D;
-  }
   int cur = 0;
-  int nf = static_cast<int>(n_l);
+  // kept nodes of the level above l0: all that exist (the root when l0 = 1)
+  int nf;
+  {
+    int64_t n_above = 1;
+    if (l0 > 1) {
+      if constexpr (!CACHE) {
+        for (int l = 1; l < l0; ++l) n_above *= b;
+      } else {
+        n_above = (a.n_keys + lc.span * b - 1) / (lc.span * b);
+      }
+    }
+    nf = static_cast<int>(n_above);
+  }
   for (int l = l0; l <= lv; ++l) {
-    n_l *= b;
-    const int C = nf * b;
     const bool all = l == l0;  // candidates are nodes 0..C-1 of level l
-    if (C > W) {
-      const int bits = 32 - __clz(static_cast<int>(n_l) - 1);
-      const float *sl = a.summ + off + head * n_l * D + col;
+    // candidate slots, and how many of them are real nodes
+    const int C = all ? static_cast<int>(lc.exist) : nf * b;
+    // a full tree has no holes: every child exists
+    const int live = (all || !CACHE) ? C : C - sh.holes[l % 3];
+    const int keep = live < W ? live : W;
+    const int64_t e_below = CACHE && l < lv ? lc.exist_below() : 0;
+    int *holes_next = &sh.holes[(l + 1) % 3];
+    if (CACHE && tid == 0) sh.holes[(l + 2) % 3] = 0;
+    if (live > W) {
+      const int bits = 32 - __clz(static_cast<int>(lc.exist) - 1);
+      const float *sl = a.summ + lc.off + head * lc.rows * D + col;
       // the walking waves score, each lane taking `per` rows
       const int per = (C + NRW * RPI - 1) / (NRW * RPI);
       const int *cand = sh.cand[cur];
       if (w < NRW) {
         if (per <= 1)
-          score_rows<T, D, 1>(sl, C, all, cand, sh.keys, bits, qr, NRW, w, lane);
+          score_rows<T, D, 1, CACHE>(sl, C, all, cand, sh.keys, bits, qr, NRW, w, lane);
         else if (per <= 2)
-          score_rows<T, D, 2>(sl, C, all, cand, sh.keys, bits, qr, NRW, w, lane);
+          score_rows<T, D, 2, CACHE>(sl, C, all, cand, sh.keys, bits, qr, NRW, w, lane);
         else if (per <= 4)
-          score_rows<T, D, 4>(sl, C, all, cand, sh.keys, bits, qr, NRW, w, lane);
+          score_rows<T, D, 4, CACHE>(sl, C, all, cand, sh.keys, bits, qr, NRW, w, lane);
         else
-          score_rows<T, D, 8>(sl, C, all, cand, sh.keys, bits, qr, NRW, w, lane);
+          score_rows<T, D, 8, CACHE>(sl, C, all, cand, sh.keys, bits, qr, NRW, w, lane);
       }
       __syncthreads();
       // rank of candidate i = number of candidates with a larger key.  Each
@@ -210,7 +302,8 @@ __device__ void route_walk(const RouteArgs &a, RouteShared<NW> &sh, int qi) {
       // group counts over keys p, p+g, p+2g, ... (so the g lanes read g
       // neighbouring keys: no bank conflict, and every group of the wave
       // reads the same addresses), then the group adds its counts with DPP,
-      // so the ranks need no further trip through LDS.
+      // so the ranks need no further trip through LDS.  Holes have key 0 and
+      // rank at least `live`, so they are never kept.
       if (w < NRW) {
         const int lcp = 32 - __clz(C - 1);
         const int lg = min(LOG_NRT - lcp, 3);
@@ -236,34 +329,56 @@ __device__ void route_walk(const RouteArgs &a, RouteShared<NW> &sh, int qi) {
         if (g >= 8) cnt = xor_sum<4>(cnt, lane);
         // the W best go to front[] at their rank; their children, in the
         // same order, are the next level's candidates
-        if (i < C && part == 0 && cnt < W) {
+        if (i < C && part == 0 && cnt < keep) {
           const int node = all ? i : cand[i];
           sh.front[cnt] = node;
           if (l < lv) {
-            for (int c = 0; c < b; ++c) sh.cand[cur ^ 1][cnt * b + c] = node * b + c;
+            int missing = 0;
+            for (int c = 0; c < b; ++c) {
+              const int child = node * b + c;
+              const bool exists = !CACHE || child < e_below;
+              sh.cand[cur ^ 1][cnt * b + c] = exists ? child : -1;
+              missing += exists ? 0 : 1;
+            }
+            if (CACHE && missing) *holes_next = missing;  // only the last node has holes
           }
         }
       }
     } else {
-      // no cut: every candidate is kept
+      // no cut: every real candidate is kept, in slot order
       if (tid < C) {
         const int node = all ? tid : sh.cand[cur][tid];
-        sh.front[tid] = node;
-        if (l < lv) {
-          for (int c = 0; c < b; ++c) sh.cand[cur ^ 1][tid * b + c] = node * b + c;
+        if (node >= 0) {
+          // slots past the holes move down by their number
+          int r = tid;
+          if (CACHE && !all && sh.holes[l % 3] && tid > 0) {
+            for (int j = 0; j < tid; ++j) r -= sh.cand[cur][j] < 0 ? 1 : 0;
+          }
+          sh.front[r] = node;
+          if (l < lv) {
+            int missing = 0;
+            for (int c = 0; c < b; ++c) {
+              const int child = node * b + c;
+              const bool exists = !CACHE || child < e_below;
+              sh.cand[cur ^ 1][r * b + c] = exists ? child : -1;
+              missing += exists ? 0 : 1;
+            }
+            if (CACHE && missing) *holes_next = missing;
+          }
         }
       }
     }
     __syncthreads();
     cur ^= 1;
-    nf = C < W ? C : W;
-    off += heads * n_l * D;
+    nf = keep;
+    if (l < lv) lc.down(D);
     if (a.trace) {
       int32_t *tr = a.trace + (static_cast<int64_t>(qi) * lv + (l - 1)) * W;
       write_ascending<NT>(sh.front, nf, tr);
       for (int k = nf + tid; k < W; k += NT) tr[k] = -1;
     }
   }
+  return nf;
 }
 
 }  // namespace tis

@@ -309,6 +309,7 @@ tis_status tis_tree_attend(const void *Q, const void *K, const void *V, tis_dtyp
   a.O = O;
   a.queries = static_cast<int>(queries);
   a.n_keys = n_keys;
+  a.key_stride = n_keys;
   a.q_heads = q_heads;
   a.kv_heads = kv_heads;
   a.group = q_heads / kv_heads;
@@ -364,6 +365,7 @@ tis_status tis_tree_decode(const void *Q, const void *K, const void *V, tis_dtyp
   aa.O = O;
   aa.queries = static_cast<int>(queries);
   aa.n_keys = tree->n_keys;
+  aa.key_stride = tree->n_keys;
   aa.q_heads = q_heads;
   aa.kv_heads = tree->kv_heads;
   aa.group = q_heads / tree->kv_heads;
@@ -377,6 +379,259 @@ tis_status tis_tree_decode(const void *Q, const void *K, const void *V, tis_dtyp
   const tis::Dt dt = dtype == TIS_BF16 ? tis::Dt::BF16 : tis::Dt::F32;
   return hip_status(tis::launch_decode(dt, tree->head_dim, ra, aa, static_cast<hipStream_t>(stream)),
                     "tis_tree_decode launch");
+}
+
+// ------------------------------------------------------- growing cache --
+
+namespace {
+
+// Fewest levels lv >= 1 with b^lv * L >= n (n >= 1); 0 past kMaxLevels.
+int cache_depth(int64_t n, int branching, int leaf_block) {
+  int64_t cap = static_cast<int64_t>(branching) * leaf_block;
+  for (int lv = 1; lv <= tis::kMaxLevels; ++lv) {
+    if (cap >= n) return lv;
+    if (cap > (int64_t{1} << 40)) return 0;
+    cap *= branching;
+  }
+  return 0;
+}
+
+struct CacheGeometry {
+  int heights;          // H
+  int64_t heads;
+  int64_t summ_elems;   // floats
+  int64_t state_elems;  // doubles
+};
+
+tis_status check_cache(const char *who, int batch, int kv_heads, int head_dim, int branching,
+                       int leaf_block, int capacity, CacheGeometry *g) {
+  if (batch < 1 || kv_heads < 1)
+    return fail(TIS_E_SHAPE, "%s: batch and kv_heads must be >= 1", who);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(head_dim < 1 ? TIS_E_SHAPE : TIS_E_UNSUPPORTED,
+                "%s: head_dim %d: only 64 and 128 are compiled", who, head_dim);
+  if (branching < 2) return fail(TIS_E_SHAPE, "%s: branching %d < 2", who, branching);
+  if (branching > tis::kMaxBranching)
+    return fail(TIS_E_UNSUPPORTED, "%s: branching %d > %d", who, branching, tis::kMaxBranching);
+  if (leaf_block < 1) return fail(TIS_E_SHAPE, "%s: leaf_block %d < 1", who, leaf_block);
+  if (capacity < 1) return fail(TIS_E_SHAPE, "%s: capacity %d < 1", who, capacity);
+  const int H = cache_depth(capacity, branching, leaf_block);
+  if (H < 1)
+    return fail(TIS_E_UNSUPPORTED, "%s: a full cache would need more than %d levels", who,
+                tis::kMaxLevels);
+  g->heights = H;
+  g->heads = static_cast<int64_t>(batch) * kv_heads;
+  int64_t span = leaf_block, elems = 0;
+  for (int h = 0; h < H; ++h) {
+    elems += g->heads * ((capacity + span - 1) / span) * head_dim;
+    span *= branching;
+  }
+  g->summ_elems = elems;
+  g->state_elems = g->heads * H * head_dim;
+  return TIS_OK;
+}
+
+tis_status check_cache_tree(const char *who, const tis_cache_tree *t, CacheGeometry *g) {
+  if (!t || !t->summaries || !t->state)
+    return fail(TIS_E_NULL, "%s: tree, tree->summaries and tree->state are required", who);
+  tis_status st = check_cache(who, t->batch, t->kv_heads, t->head_dim, t->branching,
+                              t->leaf_block, t->capacity, g);
+  if (st != TIS_OK) return st;
+  if (!aligned(t->summaries, 16) || !aligned(t->state, 16))
+    return fail(TIS_E_ALIGN, "%s: summaries and state need 16-byte alignment", who);
+  if (t->n_keys < 0 || t->n_keys > t->capacity)
+    return fail(TIS_E_SHAPE, "%s: n_keys %d outside [0, capacity %d]", who, t->n_keys,
+                t->capacity);
+  const int want = t->n_keys ? cache_depth(t->n_keys, t->branching, t->leaf_block) : 0;
+  if (t->levels != want)
+    return fail(TIS_E_SHAPE, "%s: levels %d does not match n_keys %d (depth %d)", who, t->levels,
+                t->n_keys, want);
+  return TIS_OK;
+}
+
+// Route arguments over the tree of a cache (n_keys >= 1, checked).
+tis::RouteArgs cache_route_args(const void *Q, const tis_cache_tree *t, int q_heads, int beam,
+                                int32_t *indices, int32_t *trace, int64_t queries) {
+  tis::RouteArgs a{};
+  a.Q = Q;
+  a.summ = t->summaries;
+  a.indices = indices;
+  a.trace = trace;
+  a.queries = static_cast<int>(queries);
+  a.q_heads = q_heads;
+  a.kv_heads = t->kv_heads;
+  a.group = q_heads / t->kv_heads;
+  a.branching = t->branching;
+  a.levels = t->levels;
+  a.beam = beam;
+  a.cache = 1;
+  a.n_keys = t->n_keys;
+  a.leaf_block = t->leaf_block;
+  a.capacity = t->capacity;
+  // first level whose existing nodes outnumber the beam
+  a.first_cut = 1;
+  for (;;) {
+    int64_t span = t->leaf_block;
+    for (int h = 0; h < t->levels - a.first_cut; ++h) span *= t->branching;
+    const int64_t exist = (t->n_keys + span - 1) / span;
+    if (a.first_cut >= t->levels || exist > beam) break;
+    ++a.first_cut;
+  }
+  return a;
+}
+
+tis_status check_cache_query(const char *who, const void *Q, tis_dtype dtype, int q_heads,
+                             const tis_cache_tree *t, int beam, CacheGeometry *g,
+                             int64_t *queries) {
+  tis_status st = check_dtype(dtype);
+  if (st != TIS_OK) return st;
+  st = check_cache_tree(who, t, g);
+  if (st != TIS_OK) return st;
+  if (t->n_keys < 1) return fail(TIS_E_SHAPE, "%s: the tree is empty", who);
+  if (q_heads < 1 || q_heads % t->kv_heads != 0)
+    return fail(TIS_E_SHAPE, "%s: q_heads %d is not a positive multiple of kv_heads %d", who,
+                q_heads, t->kv_heads);
+  if (beam < 1) return fail(TIS_E_SHAPE, "%s: beam %d < 1", who, beam);
+  if (static_cast<int64_t>(beam) * t->branching > TIS_MAX_CANDIDATES)
+    return fail(TIS_E_UNSUPPORTED, "%s: beam * branching = %lld > %d", who,
+                (long long)beam * t->branching, TIS_MAX_CANDIDATES);
+  if (!aligned(Q, 16)) return fail(TIS_E_ALIGN, "%s: Q needs 16-byte alignment", who);
+  *queries = static_cast<int64_t>(t->batch) * q_heads;
+  if (*queries > 0x7fffffffLL) return fail(TIS_E_UNSUPPORTED, "%s: too many queries", who);
+  return TIS_OK;
+}
+
+}  // namespace
+
+size_t tis_cache_tree_summary_bytes(int batch, int kv_heads, int head_dim, int branching,
+                                    int leaf_block, int capacity) {
+  CacheGeometry g;
+  if (check_cache("tis_cache_tree_summary_bytes", batch, kv_heads, head_dim, branching,
+                  leaf_block, capacity, &g) != TIS_OK)
+    return 0;
+  return static_cast<size_t>(g.summ_elems) * sizeof(float);
+}
+
+size_t tis_cache_tree_state_bytes(int batch, int kv_heads, int head_dim, int branching,
+                                  int leaf_block, int capacity) {
+  CacheGeometry g;
+  if (check_cache("tis_cache_tree_state_bytes", batch, kv_heads, head_dim, branching,
+                  leaf_block, capacity, &g) != TIS_OK)
+    return 0;
+  return static_cast<size_t>(g.state_elems) * sizeof(double);
+}
+
+tis_status tis_cache_tree_reset(tis_cache_tree *tree, void *stream) {
+  if (!tree || !tree->summaries || !tree->state)
+    return fail(TIS_E_NULL, "tis_cache_tree_reset: tree, tree->summaries and tree->state are required");
+  CacheGeometry g;
+  tis_status st = check_cache("tis_cache_tree_reset", tree->batch, tree->kv_heads,
+                              tree->head_dim, tree->branching, tree->leaf_block, tree->capacity,
+                              &g);
+  if (st != TIS_OK) return st;
+  if (!aligned(tree->summaries, 16) || !aligned(tree->state, 16))
+    return fail(TIS_E_ALIGN, "tis_cache_tree_reset: summaries and state need 16-byte alignment");
+  st = hip_status(tis::launch_cache_reset(tree->state, g.state_elems,
+                                          static_cast<hipStream_t>(stream)),
+                  "tis_cache_tree_reset launch");
+  if (st != TIS_OK) return st;
+  tree->n_keys = 0;
+  tree->levels = 0;
+  return TIS_OK;
+}
+
+tis_status tis_cache_tree_append(const void *K, tis_dtype dtype, int n_new, tis_cache_tree *tree,
+                                 void *stream) {
+  if (!K) return fail(TIS_E_NULL, "tis_cache_tree_append: K is required");
+  tis_status st = check_dtype(dtype);
+  if (st != TIS_OK) return st;
+  CacheGeometry g;
+  st = check_cache_tree("tis_cache_tree_append", tree, &g);
+  if (st != TIS_OK) return st;
+  if (!aligned(K, 16)) return fail(TIS_E_ALIGN, "tis_cache_tree_append: K needs 16-byte alignment");
+  if (n_new < 0 || n_new > tree->capacity - tree->n_keys)
+    return fail(TIS_E_SHAPE, "tis_cache_tree_append: n_new %d outside [0, %d] (capacity %d, n_keys %d)",
+                n_new, tree->capacity - tree->n_keys, tree->capacity, tree->n_keys);
+  if (n_new == 0) return TIS_OK;
+  if (g.heads > 0x7fffffffLL)
+    return fail(TIS_E_UNSUPPORTED, "tis_cache_tree_append: too many heads");
+  tis::AppendArgs a{};
+  a.K = K;
+  a.summ = tree->summaries;
+  a.state = tree->state;
+  a.heads = g.heads;
+  a.capacity = tree->capacity;
+  a.n0 = tree->n_keys;
+  a.n1 = static_cast<int64_t>(tree->n_keys) + n_new;
+  a.leaf_block = tree->leaf_block;
+  a.branching = tree->branching;
+  a.heights = g.heights;
+  const tis::Dt dt = dtype == TIS_BF16 ? tis::Dt::BF16 : tis::Dt::F32;
+  st = hip_status(tis::launch_cache_append(dt, tree->head_dim, a, static_cast<hipStream_t>(stream)),
+                  "tis_cache_tree_append launch");
+  if (st != TIS_OK) return st;
+  tree->n_keys += n_new;
+  tree->levels = cache_depth(tree->n_keys, tree->branching, tree->leaf_block);
+  return TIS_OK;
+}
+
+tis_status tis_cache_tree_route(const void *Q, tis_dtype dtype, int q_heads,
+                                const tis_cache_tree *tree, int beam, int32_t *indices,
+                                int32_t *trace, void *stream) {
+  if (!Q || !indices) return fail(TIS_E_NULL, "tis_cache_tree_route: Q and indices are required");
+  CacheGeometry g;
+  int64_t queries = 0;
+  tis_status st = check_cache_query("tis_cache_tree_route", Q, dtype, q_heads, tree, beam, &g,
+                                    &queries);
+  if (st != TIS_OK) return st;
+  if (!aligned(indices, 4) || (trace && !aligned(trace, 4)))
+    return fail(TIS_E_ALIGN, "tis_cache_tree_route: indices and trace need 4-byte alignment");
+  const tis::RouteArgs a = cache_route_args(Q, tree, q_heads, beam, indices, trace, queries);
+  const tis::Dt dt = dtype == TIS_BF16 ? tis::Dt::BF16 : tis::Dt::F32;
+  return hip_status(tis::launch_route(dt, tree->head_dim, a, static_cast<hipStream_t>(stream)),
+                    "tis_cache_tree_route launch");
+}
+
+tis_status tis_cache_tree_decode(const void *Q, const void *K, const void *V, tis_dtype dtype,
+                                 int q_heads, const tis_cache_tree *tree, int beam, float scale,
+                                 float *O, int32_t *indices, void *workspace,
+                                 size_t workspace_bytes, void *stream) {
+  if (!Q || !K || !V || !O)
+    return fail(TIS_E_NULL, "tis_cache_tree_decode: Q, K, V and O are required");
+  CacheGeometry g;
+  int64_t queries = 0;
+  tis_status st = check_cache_query("tis_cache_tree_decode", Q, dtype, q_heads, tree, beam, &g,
+                                    &queries);
+  if (st != TIS_OK) return st;
+  if (!(scale == scale) || isinf(scale))
+    return fail(TIS_E_SHAPE, "tis_cache_tree_decode: scale must be finite");
+  if (!aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || (indices && !aligned(indices, 4)))
+    return fail(TIS_E_ALIGN, "tis_cache_tree_decode: K, V and O need 16-byte alignment");
+  const tis::RouteArgs ra = cache_route_args(Q, tree, q_heads, beam, indices, nullptr, queries);
+  const double sc =
+      scale > 0.f ? static_cast<double>(scale) : 1.0 / sqrt(static_cast<double>(tree->head_dim));
+  tis::AttendArgs aa{};
+  aa.Q = Q;
+  aa.K = K;
+  aa.V = V;
+  aa.indices = nullptr;
+  aa.O = O;
+  aa.queries = static_cast<int>(queries);
+  aa.n_keys = tree->n_keys;
+  aa.key_stride = tree->capacity;
+  aa.q_heads = q_heads;
+  aa.kv_heads = tree->kv_heads;
+  aa.group = q_heads / tree->kv_heads;
+  aa.leaf_block = tree->leaf_block;
+  aa.beam = beam;
+  aa.n_blocks = (static_cast<int64_t>(tree->n_keys) + tree->leaf_block - 1) / tree->leaf_block;
+  aa.scale_log2 = static_cast<float>(sc * 1.4426950408889634);
+  st = plan_split("tis_cache_tree_decode", queries, tree->head_dim, beam, tree->leaf_block,
+                  workspace, workspace_bytes, &aa);
+  if (st != TIS_OK) return st;
+  const tis::Dt dt = dtype == TIS_BF16 ? tis::Dt::BF16 : tis::Dt::F32;
+  return hip_status(tis::launch_decode(dt, tree->head_dim, ra, aa, static_cast<hipStream_t>(stream)),
+                    "tis_cache_tree_decode launch");
 }
 
 const char *tis_last_error(void) { return g_err; }

@@ -61,6 +61,13 @@ hipError_t launch_build(Dt dt, int head_dim, int64_t heads, const BuildArgs &a,
                         const BuildPlan &p, hipStream_t s);
 
 // ---------------------------------------------------------------- route --
+// The walk reads one of two summary layouts:
+//  * full tree (cache == 0): N = b^levels * L, level-major, level l a block
+//    [B*Hkv][b^l][d];
+//  * growing cache (cache != 0): the tree over the first n_keys of a cache
+//    of `capacity` keys per head; height-major (height h = levels - l), height
+//    h a block [B*Hkv][ceil(capacity / (L b^h))][d]; node n of level l exists
+//    when n * L * b^(levels-l) < n_keys.
 struct RouteArgs {
   const void *Q;
   const float *summ;
@@ -70,6 +77,8 @@ struct RouteArgs {
   int q_heads, kv_heads, group;
   int branching, levels, beam;
   int first_cut;         // first level with more than beam nodes (levels if none)
+  int cache;             // layout (see above)
+  int n_keys, leaf_block, capacity;  // growing cache only
 };
 
 hipError_t launch_route(Dt dt, int head_dim, const RouteArgs &a, hipStream_t s);
@@ -86,7 +95,8 @@ struct AttendArgs {
   float *part;           // [queries][splits][d + 4] partial states when splits > 1
   int splits;            // workgroups per query (1: no split, no workspace)
   int queries;           // B * Hq (< 2^31, checked by the host)
-  int64_t n_keys;
+  int64_t n_keys;        // keys in use per head (leaf j holds [jL, min((j+1)L, n_keys)))
+  int64_t key_stride;    // rows per head in K and V (n_keys, or a cache's capacity)
   int q_heads, kv_heads, group;
   int leaf_block, beam;
   int64_t n_blocks;      // N / L
@@ -105,6 +115,24 @@ hipError_t launch_combine(int head_dim, const AttendArgs &a, hipStream_t s);
 // Route and attend of each query in one workgroup (one launch).
 hipError_t launch_decode(Dt dt, int head_dim, const RouteArgs &ra, const AttendArgs &aa,
                          hipStream_t s);
+
+// ------------------------------------------------------- growing cache --
+// Append keys [n0, n1) of a cache of `capacity` keys per head to its tree:
+// summaries height-major (height h a block [heads][ceil(capacity / (L
+// b^h))][d]), state fp64 [heads][heights][d] open-node sums.
+struct AppendArgs {
+  const void *K;
+  float *summ;
+  double *state;
+  int64_t heads;         // B * Hkv
+  int64_t capacity;
+  int64_t n0, n1;
+  int leaf_block, branching;
+  int heights;           // H: depth of a full cache, stored heights 0 .. H-1
+};
+
+hipError_t launch_cache_reset(double *state, int64_t elems, hipStream_t s);
+hipError_t launch_cache_append(Dt dt, int head_dim, const AppendArgs &a, hipStream_t s);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

@@ -13,13 +13,12 @@ from typing import Dict, Optional, Tuple
 import torch
 
 from . import _lib
-from ._lib import TisTree, check, lib
+from ._lib import TisCacheTree, TisTree, check, lib
 
 _DTYPES = {torch.float32: _lib.TIS_F32, torch.bfloat16: _lib.TIS_BF16}
 
-__all__ = ["Tree", "DecodePlan", "tree_build", "tree_route", "tree_attend", "tree_decode",
-           "decode", "version", "from_storage",
-           "summary_offsets"]
+__all__ = ["Tree", "DecodePlan", "CacheTree", "tree_build", "tree_route", "tree_attend",
+           "tree_decode", "decode", "version", "from_storage", "summary_offsets"]
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -286,3 +285,107 @@ class DecodePlan:
     def tree(self) -> Tree:
         B, H, N, d, b, Lb, lv = self.geom
         return Tree(self.summaries, B, H, N, d, b, Lb, lv)
+
+
+class CacheTree:
+    """The tree over a growing KV cache (tis_cache_tree_* calls).
+
+    K and V are the cache: [B, Hkv, capacity, d] device tensors whose first
+    n_keys rows are in use.  Write new rows into K (and V) first, then call
+    append(n) to add them to the tree.  Summaries are height-major: height h
+    (0 = leaves) is a [B, Hkv, ceil(capacity / (L b^h)), d] block; level l of
+    the current tree is height levels - l.
+    """
+
+    def __init__(self, K: torch.Tensor, V: torch.Tensor, branching: int, leaf_block: int):
+        _need_device(K, V)
+        if V.shape != K.shape or V.dtype != K.dtype:
+            raise ValueError("K and V must match")
+        B, H, C, d = K.shape
+        L = lib()
+        self.K, self.V = K, V
+        self.dt = _dtype_code(K)
+        sb = L.tis_cache_tree_summary_bytes(B, H, d, branching, leaf_block, C)
+        stb = L.tis_cache_tree_state_bytes(B, H, d, branching, leaf_block, C)
+        if sb == 0 or stb == 0:
+            raise _lib.TisError(_lib.TIS_E_SHAPE, "invalid cache geometry")
+        self.summaries = torch.empty(sb // 4, dtype=torch.float32, device=K.device)
+        self.state = torch.empty(stb // 8, dtype=torch.float64, device=K.device)
+        self.c = TisCacheTree(B, H, d, branching, leaf_block, C, 0, 0,
+                              self.summaries.data_ptr(), self.state.data_ptr())
+        self.reset()
+
+    @property
+    def n_keys(self) -> int:
+        return self.c.n_keys
+
+    @property
+    def levels(self) -> int:
+        return self.c.levels
+
+    def reset(self) -> None:
+        check(lib().tis_cache_tree_reset(ctypes.byref(self.c), _stream(self.K.device)))
+
+    def append(self, n_new: int) -> None:
+        check(lib().tis_cache_tree_append(self.K.data_ptr(), self.dt, int(n_new),
+                                          ctypes.byref(self.c), _stream(self.K.device)))
+
+    def height_block(self, h: int) -> torch.Tensor:
+        """Summaries of height h as [B, Hkv, rows, d] (a view)."""
+        c = self.c
+        heads = c.batch * c.kv_heads
+        off, span = 0, c.leaf_block
+        for _ in range(h):
+            off += heads * -(-c.capacity // span) * c.head_dim
+            span *= c.branching
+        rows = -(-c.capacity // span)
+        return self.summaries[off:off + heads * rows * c.head_dim].view(
+            c.batch, c.kv_heads, rows, c.head_dim)
+
+    def level(self, l: int) -> torch.Tensor:
+        """The existing nodes of level l (1 = below the root) of the current
+        tree, [B, Hkv, e_l, d] (a view)."""
+        c = self.c
+        if not 1 <= l <= c.levels:
+            raise ValueError(f"level {l} outside 1..{c.levels}")
+        span = c.leaf_block * c.branching ** (c.levels - l)
+        return self.height_block(c.levels - l)[:, :, :-(-c.n_keys // span)]
+
+    def route(self, Q: torch.Tensor, beam: int, trace: bool = False):
+        """Kept leaves ([B, Hq, beam] int32, ascending, -1 padded) and, with
+        trace=True, the kept nodes per level ([B, Hq, levels, beam])."""
+        _need_device(Q)
+        if Q.dtype != self.K.dtype:
+            raise TypeError("Q must have the cache's dtype")
+        B, Hq, d = Q.shape
+        idx = torch.empty((B, Hq, beam), dtype=torch.int32, device=Q.device)
+        tr = (torch.empty((B, Hq, max(self.levels, 1), beam), dtype=torch.int32,
+                          device=Q.device) if trace else None)
+        check(lib().tis_cache_tree_route(Q.data_ptr(), self.dt, Hq, ctypes.byref(self.c), beam,
+                                         idx.data_ptr(), tr.data_ptr() if tr is not None else None,
+                                         _stream(Q.device)))
+        return (idx, tr) if trace else idx
+
+    def decode(self, Q: torch.Tensor, beam: int, scale: Optional[float] = None,
+               return_indices: bool = False, out: Optional[torch.Tensor] = None,
+               indices: Optional[torch.Tensor] = None):
+        """Route and attend every query over the cache in one launch."""
+        _need_device(Q)
+        if Q.dtype != self.K.dtype:
+            raise TypeError("Q must have the cache's dtype")
+        B, Hq, d = Q.shape
+        O = out if out is not None else torch.empty((B, Hq, d), dtype=torch.float32,
+                                                     device=Q.device)
+        idx = indices
+        if idx is None and return_indices:
+            idx = torch.empty((B, Hq, beam), dtype=torch.int32, device=Q.device)
+        L = lib()
+        wsb = L.tis_decode_workspace_bytes(B, Hq, d, beam, self.c.leaf_block)
+        ws = _workspace(Q.device, "decode", wsb) if wsb else None
+        check(L.tis_cache_tree_decode(Q.data_ptr(), self.K.data_ptr(), self.V.data_ptr(),
+                                      self.dt, Hq, ctypes.byref(self.c), beam,
+                                      0.0 if scale is None else float(scale), O.data_ptr(),
+                                      idx.data_ptr() if idx is not None else None,
+                                      ws.data_ptr() if ws is not None else None,
+                                      ws.numel() if ws is not None else 0, _stream(Q.device)))
+        return (O, idx) if return_indices else O
