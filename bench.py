@@ -139,6 +139,50 @@ def cpu_baseline(w, x, min_seconds: float = 10.0, max_reps: int = 500):
                       f"numpy fp64, BLAS limited to 1 thread, {el:.1f} s"}
 
 
+def cache_decode_loop(tis, w, K, V, Q, steps, warmup):
+    """The decode loop over a growing cache of the same shape: the tree over
+    the first keys of the cache is filled by one long append, then every
+    step appends one key per head (tis_cache_tree_append) and decodes every
+    query (tis_cache_tree_decode).  Times: the long append, one-key appends
+    back to back, decodes back to back, and whole steps back to back."""
+    import torch
+    need = 3 * (steps + warmup) + 8
+    prefill = w.n_keys - need
+    if prefill < 1:
+        return None
+    ct = tis.CacheTree(K, V, w.branching, w.leaf_block)
+    out = torch.empty((w.batch, w.q_heads, w.head_dim), dtype=torch.float32, device=K.device)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps):
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps  # us
+
+    ct.append(prefill)  # warm the kernel once, then time a fresh prefill
+    ct.reset()
+    prefill_us = timed(lambda: ct.append(prefill), 1)
+    step = lambda: (ct.append(1), ct.decode(Q, w.beam, out=out))
+    for _ in range(warmup):
+        step()
+    step_us = timed(step, steps)
+    append_us = timed(lambda: ct.append(1), steps)
+    decode_us = timed(lambda: ct.decode(Q, w.beam, out=out), steps)
+    kbytes = prefill * w.batch * w.kv_heads * w.head_dim * w.elem_bytes
+    return {"regime": "tree over the first n keys of a cache of the workload's size; "
+                      "one key appended per head per step",
+            "n_keys_at_end": ct.n_keys, "levels": ct.levels,
+            "prefill_keys": prefill, "prefill_us": prefill_us,
+            "prefill_gbs": kbytes / (prefill_us * 1e-6) / 1e9,
+            "append1_us": append_us, "decode_us": decode_us, "step_us": step_us,
+            "queries_per_s": w.queries / (step_us * 1e-6)}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -146,6 +190,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="gqa_32k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cache-loop", action="store_true",
+                    help="skip the growing-cache decode loop measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 256 MiB device-to-device copy first (the reference "
                          "dispatch for scaling HBM byte counters)")
@@ -294,6 +340,14 @@ def main(argv=None):
 
     traffic = load_traffic(w.name)
 
+    cache = None
+    if not args.no_cache_loop:
+        cache = cache_decode_loop(tis, w, K, V, Q, K_, args.warmup)
+        log(f"growing cache: prefill append of {cache['prefill_keys']} keys/head "
+            f"{cache['prefill_us']:.1f} us ({cache['prefill_gbs']:.1f} GB/s); append of 1 key "
+            f"{cache['append1_us']:.2f} us; decode {cache['decode_us']:.2f} us; decode step "
+            f"(append + decode) {cache['step_us']:.2f} us -> {cache['queries_per_s']:.3e} queries/s")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
@@ -333,6 +387,7 @@ def main(argv=None):
                    "attend_gbs_per_query_bytes": by["attend"] / t_attend.mean() / 1e9,
                    "attend_gbs_distinct_blocks": attend_dedup / t_attend.mean() / 1e9},
         "cpu_baseline": cpu,
+        "cache_decode_loop": cache,
     }
     print(json.dumps(line), flush=True)
     return 0

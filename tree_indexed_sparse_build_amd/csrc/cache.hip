@@ -49,38 +49,37 @@ __global__ void __launch_bounds__(kAppendThreads) k_cache_append(AppendArgs a) {
 
   // per height h: first summary row of this head, keys under one node
   int64_t base[kMaxLevels];
-  double span_keys[kMaxLevels];
+  uint32_t span[kMaxLevels];
   double open[kMaxLevels];
-  {
-    int64_t span = L, off = 0;
 #pragma unroll
-    for (int h = 0; h < kMaxLevels; ++h) {
-      base[h] = 0;
-      span_keys[h] = 1.0;
-      open[h] = 0.0;
-      if (h < H) {  // heights past H would overflow the span
-        const int64_t rows = (a.capacity + span - 1) / span;
-        base[h] = off + head * rows * D;
-        span_keys[h] = static_cast<double>(span);
-        if (tid < D) open[h] = st[h * D];
-        off += a.heads * rows * D;
-        span *= b;
-      }
-    }
+  for (int h = 0; h < kMaxLevels; ++h) {
+    base[h] = h < H ? a.block_off[h] + head * a.rows[h] * D : 0;
+    span[h] = h < H ? a.span[h] : 1u;
+    open[h] = (tid < D && h < H) ? st[h * D] : 0.0;
   }
 
-  const int64_t j0 = a.n0 / L;
-  const int64_t j1 = (a.n1 - 1) / L;
-  for (int64_t jb = j0; jb <= j1; jb += kAppendBatch) {
-    const int nb = static_cast<int>(j1 - jb + 1 < kAppendBatch ? j1 - jb + 1 : kAppendBatch);
+  const uint32_t n0 = static_cast<uint32_t>(a.n0), n1 = static_cast<uint32_t>(a.n1);
+  const uint32_t j0 = n0 / static_cast<uint32_t>(L);
+  const uint32_t j1 = (n1 - 1u) / static_cast<uint32_t>(L);
+  for (uint32_t jb = j0; jb <= j1; jb += kAppendBatch) {
+    const int nb = static_cast<int>(j1 - jb + 1u < kAppendBatch ? j1 - jb + 1u : kAppendBatch);
     // new keys of each leaf of the batch, summed per column in fp64
     for (int s = slot; s < nb; s += kPar) {
       const int64_t j = jb + s;
       const int64_t lo = j * L > a.n0 ? j * L : a.n0;
       const int64_t hi = (j + 1) * L < a.n1 ? (j + 1) * L : a.n1;
+      // 8 rows in flight before any is added (a plain loop would wait on
+      // every load), then a tail
       double sum = 0.0;
-#pragma unroll 8
-      for (int64_t t = lo; t < hi; ++t) sum += key_elem<T>(kh + t * D);
+      int64_t t = lo;
+      for (; t + 8 <= hi; t += 8) {
+        double v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = key_elem<T>(kh + (t + u) * D);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) sum += v[u];
+      }
+      for (; t < hi; ++t) sum += key_elem<T>(kh + t * D);
       ls[s][c] = sum;
     }
     __syncthreads();
@@ -89,19 +88,20 @@ __global__ void __launch_bounds__(kAppendThreads) k_cache_append(AppendArgs a) {
     // it: mean written, sum restarted
     if (tid < D) {
       for (int s = 0; s < nb; ++s) {
-        const int64_t j = jb + s;
+        const uint32_t j = jb + s;
         const double v = ls[s][c];
-        bool closing = (j + 1) * L <= a.n1;  // the leaf itself is complete
-        int64_t m = j + 1;                    // nodes of height h up to this leaf
+        bool closing = (static_cast<int64_t>(j) + 1) * L <= a.n1;  // the leaf is complete
+        uint32_t m = j + 1u;  // nodes of height h up to this leaf
 #pragma unroll
         for (int h = 0; h < kMaxLevels; ++h) {
           if (h < H) {
             open[h] += v;
             if (closing) {
-              a.summ[base[h] + (m - 1) * D + c] = static_cast<float>(open[h] / span_keys[h]);
+              a.summ[base[h] + static_cast<int64_t>(m - 1u) * D + c] =
+                  static_cast<float>(open[h] / static_cast<double>(span[h]));
               open[h] = 0.0;
-              closing = m % b == 0;
-              m /= b;
+              closing = m % static_cast<uint32_t>(b) == 0u;
+              m /= static_cast<uint32_t>(b);
             }
           }
         }
@@ -114,12 +114,12 @@ __global__ void __launch_bounds__(kAppendThreads) k_cache_append(AppendArgs a) {
 #pragma unroll
     for (int h = 0; h < kMaxLevels; ++h) {
       if (h < H) {
-        const int64_t span = static_cast<int64_t>(span_keys[h]);
-        const int64_t node = a.n1 / span;
-        const int64_t held = a.n1 - node * span;
-        if (held > 0)
-          a.summ[base[h] + node * D + c] = static_cast<float>(open[h] / static_cast<double>(held));
-        st[h * D] = held > 0 ? open[h] : 0.0;
+        const uint32_t node = n1 / span[h];
+        const uint32_t held = n1 - node * span[h];
+        if (held > 0u)
+          a.summ[base[h] + static_cast<int64_t>(node) * D + c] =
+              static_cast<float>(open[h] / static_cast<double>(held));
+        st[h * D] = held > 0u ? open[h] : 0.0;
       }
     }
   }

@@ -79,16 +79,20 @@ template <bool CACHE> struct LevelCursor {
   int64_t exist;   // nodes of the current level that exist
   int64_t rows;    // summary rows per head in the current level's block
   int64_t off;     // element offset of the current level's block
-  int64_t span;    // keys under one node of the current level (growing cache)
+  uint32_t span;   // keys under one node of the current level (growing cache)
   int64_t heads;
-  int64_t n_keys, capacity;
+  uint32_t n_keys, capacity;
   int b;
+
+  // ceil(x / y) in 32 bits: every span of a stored height is below the
+  // capacity (< 2^31), so the 64-bit division sequence is never needed
+  __device__ static int64_t ceil_div(uint32_t x, uint32_t y) { return (x + y - 1u) / y; }
 
   __device__ void init(const RouteArgs &ra, int l0, int d) {
     b = ra.branching;
     heads = static_cast<int64_t>(ra.queries / ra.q_heads) * ra.kv_heads;
-    n_keys = ra.n_keys;
-    capacity = ra.capacity;
+    n_keys = static_cast<uint32_t>(ra.n_keys);
+    capacity = static_cast<uint32_t>(ra.capacity);
     if constexpr (!CACHE) {
       // full tree: level l has b^l nodes, levels 1 .. l-1 come first
       int64_t n = 1;
@@ -102,21 +106,20 @@ template <bool CACHE> struct LevelCursor {
     } else {
       // growing cache: level l is height h = levels - l, heights 0 .. h-1 first
       const int h0 = ra.levels - l0;
-      span = ra.leaf_block;
+      span = static_cast<uint32_t>(ra.leaf_block);
       off = 0;
       for (int h = 0; h < h0; ++h) {
-        off += heads * ((capacity + span - 1) / span) * d;
-        span *= b;
+        off += heads * ceil_div(capacity, span) * d;
+        span *= static_cast<uint32_t>(b);
       }
-      rows = (capacity + span - 1) / span;
-      exist = (n_keys + span - 1) / span;
+      rows = ceil_div(capacity, span);
+      exist = ceil_div(n_keys, span);
     }
   }
   // nodes of the next level down that exist
   __device__ int64_t exist_below() const {
     if constexpr (!CACHE) return exist * b;
-    const int64_t s = span / b;
-    return (n_keys + s - 1) / s;
+    return ceil_div(n_keys, span / static_cast<uint32_t>(b));
   }
   __device__ void down(int d) {
     if constexpr (!CACHE) {
@@ -124,9 +127,9 @@ template <bool CACHE> struct LevelCursor {
       rows *= b;
       exist = rows;
     } else {
-      exist = exist_below();
-      span /= b;
-      rows = (capacity + span - 1) / span;
+      span /= static_cast<uint32_t>(b);
+      exist = ceil_div(n_keys, span);
+      rows = ceil_div(capacity, span);
       off -= heads * rows * d;
     }
   }
@@ -265,7 +268,9 @@ __device__ int route_walk(const RouteArgs &a, RouteShared<NW> &sh, int qi) {
       if constexpr (!CACHE) {
         for (int l = 1; l < l0; ++l) n_above *= b;
       } else {
-        n_above = (a.n_keys + lc.span * b - 1) / (lc.span * b);
+        // level l0-1 is a stored height too (l0 > 1), so its span fits
+        n_above = LevelCursor<CACHE>::ceil_div(static_cast<uint32_t>(a.n_keys),
+                                               lc.span * static_cast<uint32_t>(b));
       }
     }
     nf = static_cast<int>(n_above);

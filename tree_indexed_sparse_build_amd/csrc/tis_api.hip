@@ -566,6 +566,19 @@ tis_status tis_cache_tree_append(const void *K, tis_dtype dtype, int n_new, tis_
   a.leaf_block = tree->leaf_block;
   a.branching = tree->branching;
   a.heights = g.heights;
+  {
+    int64_t span = tree->leaf_block, off = 0;
+    for (int h = 0; h < g.heights; ++h) {
+      const int64_t rows = (tree->capacity + span - 1) / span;
+      a.block_off[h] = off;
+      a.rows[h] = static_cast<uint32_t>(rows);
+      // L b^h < capacity for h < H - 1 by the choice of H, and L b^(H-1)
+      // < capacity too unless H = 1 (then it is L): 32 bits always hold it
+      a.span[h] = static_cast<uint32_t>(span);
+      off += g.heads * rows * tree->head_dim;
+      span *= tree->branching;
+    }
+  }
   const tis::Dt dt = dtype == TIS_BF16 ? tis::Dt::BF16 : tis::Dt::F32;
   st = hip_status(tis::launch_cache_append(dt, tree->head_dim, a, static_cast<hipStream_t>(stream)),
                   "tis_cache_tree_append launch");

@@ -126,9 +126,14 @@ struct AppendArgs {
   double *state;
   int64_t heads;         // B * Hkv
   int64_t capacity;
-  int64_t n0, n1;
+  int64_t n0, n1;        // n1 <= capacity < 2^31
   int leaf_block, branching;
   int heights;           // H: depth of a full cache, stored heights 0 .. H-1
+  // per stored height h (host-computed, so the kernel divides nothing wider
+  // than 32 bits): element offset of the block, rows per head, keys per node
+  int64_t block_off[kMaxLevels];
+  uint32_t rows[kMaxLevels];
+  uint32_t span[kMaxLevels];   // L b^h: below the capacity (or L itself when H = 1)
 };
 
 hipError_t launch_cache_reset(double *state, int64_t elems, hipStream_t s);
