@@ -167,12 +167,13 @@ def cache_decode_loop(tis, w, K, V, Q, steps, warmup):
     ct.append(prefill)  # warm the kernel once, then time a fresh prefill
     ct.reset()
     prefill_us = timed(lambda: ct.append(prefill), 1)
-    step = lambda: (ct.append(1), ct.decode(Q, w.beam, out=out))
+    decode = ct.bind_decode(Q, w.beam, out)
+    step = lambda: (ct.append(1), decode())
     for _ in range(warmup):
         step()
     step_us = timed(step, steps)
     append_us = timed(lambda: ct.append(1), steps)
-    decode_us = timed(lambda: ct.decode(Q, w.beam, out=out), steps)
+    decode_us = timed(decode, steps)
     kbytes = prefill * w.batch * w.kv_heads * w.head_dim * w.elem_bytes
     return {"regime": "tree over the first n keys of a cache of the workload's size; "
                       "one key appended per head per step",

@@ -318,3 +318,13 @@ def test_cache_decode_rejects(lib, tree_kw, call_kw, status):
                                      a["beam"], a["scale"], a["O"], a["idx"], a["ws"], a["wsb"],
                                      None) == status
     assert lib.tis_last_error().decode()
+
+
+def test_caller_buffers_must_match():
+    """An output buffer handed to the binding is checked before any launch."""
+    torch = pytest.importorskip("torch")
+    from tree_indexed_sparse_build_amd import ops
+    with pytest.raises(ValueError, match="shape"):
+        ops._check_buffer(torch.empty(2, 3, 4), (2, 3, 8), torch.float32, "out")
+    with pytest.raises(ValueError, match="int32"):
+        ops._check_buffer(torch.empty(2, 3, 4), (2, 3, 4), torch.int32, "indices")

@@ -79,58 +79,47 @@ template <bool CACHE> struct LevelCursor {
   int64_t exist;   // nodes of the current level that exist
   int64_t rows;    // summary rows per head in the current level's block
   int64_t off;     // element offset of the current level's block
-  uint32_t span;   // keys under one node of the current level (growing cache)
   int64_t heads;
-  uint32_t n_keys, capacity;
+  int l;           // current level
   int b;
-
-  // ceil(x / y) in 32 bits: every span of a stored height is below the
-  // capacity (< 2^31), so the 64-bit division sequence is never needed
-  __device__ static int64_t ceil_div(uint32_t x, uint32_t y) { return (x + y - 1u) / y; }
+  const RouteArgs *a;
 
   __device__ void init(const RouteArgs &ra, int l0, int d) {
+    a = &ra;
     b = ra.branching;
+    l = l0;
     heads = static_cast<int64_t>(ra.queries / ra.q_heads) * ra.kv_heads;
-    n_keys = static_cast<uint32_t>(ra.n_keys);
-    capacity = static_cast<uint32_t>(ra.capacity);
     if constexpr (!CACHE) {
       // full tree: level l has b^l nodes, levels 1 .. l-1 come first
       int64_t n = 1;
       off = 0;
-      for (int l = 1; l < l0; ++l) {
+      for (int k = 1; k < l0; ++k) {
         n *= b;
         off += heads * n * d;
       }
       exist = rows = n * b;
-      span = 0;
     } else {
-      // growing cache: level l is height h = levels - l, heights 0 .. h-1 first
-      const int h0 = ra.levels - l0;
-      span = static_cast<uint32_t>(ra.leaf_block);
-      off = 0;
-      for (int h = 0; h < h0; ++h) {
-        off += heads * ceil_div(capacity, span) * d;
-        span *= static_cast<uint32_t>(b);
-      }
-      rows = ceil_div(capacity, span);
-      exist = ceil_div(n_keys, span);
+      // growing cache: sizes and offsets come from the host (no division)
+      exist = ra.lvl_exist[l0];
+      rows = ra.lvl_rows[l0];
+      off = ra.lvl_off[l0];
     }
   }
   // nodes of the next level down that exist
   __device__ int64_t exist_below() const {
     if constexpr (!CACHE) return exist * b;
-    return ceil_div(n_keys, span / static_cast<uint32_t>(b));
+    return a->lvl_exist[l + 1];
   }
   __device__ void down(int d) {
+    ++l;
     if constexpr (!CACHE) {
       off += heads * rows * d;
       rows *= b;
       exist = rows;
     } else {
-      span /= static_cast<uint32_t>(b);
-      exist = ceil_div(n_keys, span);
-      rows = ceil_div(capacity, span);
-      off -= heads * rows * d;
+      exist = a->lvl_exist[l];
+      rows = a->lvl_rows[l];
+      off = a->lvl_off[l];
     }
   }
 };
@@ -249,7 +238,7 @@ __device__ int route_walk(const RouteArgs &a, RouteShared<NW> &sh, int qi) {
       for (int h = 0; h < lv - l; ++h) span *= b;
       int64_t n = 1;
       for (int k = 0; k < l; ++k) n *= b;
-      const int64_t e = CACHE ? (a.n_keys + span - 1) / span : n;
+      const int64_t e = CACHE ? a.lvl_exist[l] : n;
       int32_t *tr = a.trace + (static_cast<int64_t>(qi) * lv + (l - 1)) * W;
       for (int k = tid; k < W; k += NT) tr[k] = k < e ? k : -1;
     }
@@ -268,9 +257,7 @@ __device__ int route_walk(const RouteArgs &a, RouteShared<NW> &sh, int qi) {
       if constexpr (!CACHE) {
         for (int l = 1; l < l0; ++l) n_above *= b;
       } else {
-        // level l0-1 is a stored height too (l0 > 1), so its span fits
-        n_above = LevelCursor<CACHE>::ceil_div(static_cast<uint32_t>(a.n_keys),
-                                               lc.span * static_cast<uint32_t>(b));
+        n_above = a.lvl_exist[l0 - 1];
       }
     }
     nf = static_cast<int>(n_above);

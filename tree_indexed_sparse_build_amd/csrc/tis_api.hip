@@ -468,15 +468,30 @@ tis::RouteArgs cache_route_args(const void *Q, const tis_cache_tree *t, int q_he
   a.n_keys = t->n_keys;
   a.leaf_block = t->leaf_block;
   a.capacity = t->capacity;
+  // per level l of the current tree (height levels - l): existing nodes,
+  // rows per head and the block's offset in the height-major layout
+  const int64_t heads = static_cast<int64_t>(t->batch) * t->kv_heads;
+  int64_t span_h[tis::kMaxLevels + 1], hoff[tis::kMaxLevels + 1];
+  {
+    int64_t span = t->leaf_block, off = 0;
+    for (int h = 0; h < t->levels; ++h) {
+      span_h[h] = span;
+      hoff[h] = off;
+      off += heads * ((t->capacity + span - 1) / span) * t->head_dim;
+      span *= t->branching;
+    }
+  }
+  for (int l = 0; l <= tis::kMaxLevels + 1; ++l) a.lvl_exist[l] = 0;
+  a.lvl_exist[0] = 1;  // the root
+  for (int l = 1; l <= t->levels; ++l) {
+    const int h = t->levels - l;
+    a.lvl_exist[l] = (t->n_keys + span_h[h] - 1) / span_h[h];
+    a.lvl_rows[l] = (t->capacity + span_h[h] - 1) / span_h[h];
+    a.lvl_off[l] = hoff[h];
+  }
   // first level whose existing nodes outnumber the beam
   a.first_cut = 1;
-  for (;;) {
-    int64_t span = t->leaf_block;
-    for (int h = 0; h < t->levels - a.first_cut; ++h) span *= t->branching;
-    const int64_t exist = (t->n_keys + span - 1) / span;
-    if (a.first_cut >= t->levels || exist > beam) break;
-    ++a.first_cut;
-  }
+  while (a.first_cut < t->levels && a.lvl_exist[a.first_cut] <= beam) ++a.first_cut;
   return a;
 }
 

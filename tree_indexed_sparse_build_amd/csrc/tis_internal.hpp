@@ -79,6 +79,11 @@ struct RouteArgs {
   int first_cut;         // first level with more than beam nodes (levels if none)
   int cache;             // layout (see above)
   int n_keys, leaf_block, capacity;  // growing cache only
+  // growing cache, per level l (host-computed): nodes that exist, summary
+  // rows per head and element offset of the level's block
+  int64_t lvl_exist[kMaxLevels + 2];
+  int64_t lvl_rows[kMaxLevels + 1];
+  int64_t lvl_off[kMaxLevels + 1];
 };
 
 hipError_t launch_route(Dt dt, int head_dim, const RouteArgs &a, hipStream_t s);

@@ -36,6 +36,13 @@ def _need_device(*ts: torch.Tensor) -> None:
             raise ValueError("tensors must be contiguous")
 
 
+def _check_buffer(t: torch.Tensor, shape, dtype: torch.dtype, name: str) -> None:
+    """A caller-supplied output must be exactly what the kernel writes."""
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} of shape {tuple(shape)}")
+    _need_device(t)
+
+
 def _stream(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
@@ -313,6 +320,9 @@ class CacheTree:
         self.state = torch.empty(stb // 8, dtype=torch.float64, device=K.device)
         self.c = TisCacheTree(B, H, d, branching, leaf_block, C, 0, 0,
                               self.summaries.data_ptr(), self.state.data_ptr())
+        self._cref = ctypes.byref(self.c)
+        self._kptr = K.data_ptr()
+        self._append = L.tis_cache_tree_append
         self.reset()
 
     @property
@@ -327,8 +337,7 @@ class CacheTree:
         check(lib().tis_cache_tree_reset(ctypes.byref(self.c), _stream(self.K.device)))
 
     def append(self, n_new: int) -> None:
-        check(lib().tis_cache_tree_append(self.K.data_ptr(), self.dt, int(n_new),
-                                          ctypes.byref(self.c), _stream(self.K.device)))
+        check(self._append(self._kptr, self.dt, int(n_new), self._cref, _stream(self.K.device)))
 
     def height_block(self, h: int) -> torch.Tensor:
         """Summaries of height h as [B, Hkv, rows, d] (a view)."""
@@ -366,6 +375,32 @@ class CacheTree:
                                          _stream(Q.device)))
         return (idx, tr) if trace else idx
 
+    def bind_decode(self, Q: torch.Tensor, beam: int, out: torch.Tensor,
+                    scale: Optional[float] = None):
+        """A zero-argument callable that decodes Q into `out` on the current
+        stream with every argument prepared once (for decode loops, where the
+        host cost of a call would otherwise exceed the kernel's)."""
+        _need_device(Q)
+        if Q.dtype != self.K.dtype:
+            raise TypeError("Q must have the cache's dtype")
+        B, Hq, d = Q.shape
+        _check_buffer(out, (B, Hq, d), torch.float32, "out")
+        L = lib()
+        wsb = L.tis_decode_workspace_bytes(B, Hq, d, beam, self.c.leaf_block)
+        ws = _workspace(Q.device, "decode", wsb) if wsb else None
+        f = L.tis_cache_tree_decode
+        args = (Q.data_ptr(), self.K.data_ptr(), self.V.data_ptr(), self.dt, Hq,
+                ctypes.byref(self.c), beam, 0.0 if scale is None else float(scale),
+                out.data_ptr(), None, ws.data_ptr() if ws is not None else None,
+                ws.numel() if ws is not None else 0)
+        dev = Q.device
+        keep = (Q, out, ws)  # the buffers must outlive the callable
+
+        def run() -> None:
+            _ = keep
+            check(f(*args, _stream(dev)))
+        return run
+
     def decode(self, Q: torch.Tensor, beam: int, scale: Optional[float] = None,
                return_indices: bool = False, out: Optional[torch.Tensor] = None,
                indices: Optional[torch.Tensor] = None):
@@ -376,9 +411,12 @@ class CacheTree:
         B, Hq, d = Q.shape
         O = out if out is not None else torch.empty((B, Hq, d), dtype=torch.float32,
                                                      device=Q.device)
+        _check_buffer(O, (B, Hq, d), torch.float32, "out")
         idx = indices
         if idx is None and return_indices:
             idx = torch.empty((B, Hq, beam), dtype=torch.int32, device=Q.device)
+        if idx is not None:
+            _check_buffer(idx, (B, Hq, beam), torch.int32, "indices")
         L = lib()
         wsb = L.tis_decode_workspace_bytes(B, Hq, d, beam, self.c.leaf_block)
         ws = _workspace(Q.device, "decode", wsb) if wsb else None
