@@ -44,6 +44,7 @@ def algorithmic_bytes(w):
 
 
 COPY_BYTES = 256 << 20
+FLUSH_BYTES = 1 << 30  # 4x the 256 MB Infinity Cache, 32x the L2s together
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{}.json")
 BUILD_SOURCE = os.path.join(ROOT, "tree_indexed_sparse_build_amd", "csrc", "build.hip")
 
@@ -137,6 +138,48 @@ def cpu_baseline(w, x, min_seconds: float = 10.0, max_reps: int = 500):
             "sample": f"{reps} whole steps (build over all {w.batch * w.kv_heads} KV heads, "
                       f"route + attend of all {w.queries} queries) of the same workload, "
                       f"numpy fp64, BLAS limited to 1 thread, {el:.1f} s"}
+
+
+def cache_states(torch, dev, plan, reps, back_to_back):
+    """Durations in two cache states.  cold: 1 GiB read first, which leaves
+    none of the inputs in the Infinity Cache or an L2 and no dirty lines to
+    write back (a flush by writing would charge its write-backs to the timed
+    kernel); steady: cold, then one read of the summaries, as when the tree
+    stays hot across decode steps.  Each is the median of `reps` lone
+    launches between their own events, compared with lone warm launches
+    timed the same way (nothing in between): the difference is what the
+    cache state costs, and adding it to the back-to-back duration removes
+    the event and dispatch overhead a lone launch carries."""
+    import numpy as np
+    flush = torch.zeros(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+
+    def one(fn, state):
+        if state != "warm":
+            flush.sum()
+        if state == "steady":
+            plan.summaries.sum()
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3
+
+    out = {}
+    for name, fn in (("build", plan.build), ("decode", plan.decode)):
+        lone = {}
+        for state in ("warm", "cold", "steady"):
+            if name == "build" and state == "steady":
+                continue
+            one(fn, state)
+            lone[state] = float(np.median([one(fn, state) for _ in range(reps)]))
+        for state, us in lone.items():
+            out[f"{name}_{state}_lone_us"] = us
+            if state != "warm":
+                out[f"{name}_{state}_us"] = back_to_back[name] + us - lone["warm"]
+    del flush
+    return out
 
 
 def cache_decode_loop(tis, w, K, V, Q, steps, warmup):
@@ -339,6 +382,17 @@ def main(argv=None):
         f"({dec_bytes / decode_s / 1e9 / HBM_PEAK_GBS:.1%}) on {dec_bytes / 1e6:.2f} MB; "
         f"in the step (step - build): {ms_step * 1e3 - t_build.mean() * 1e6:.2f} us")
 
+    states = cache_states(torch, dev, plan, 30,
+                          {"build": t_build.mean() * 1e6, "decode": decode_s * 1e6})
+    log(f"cache states (lone launches, median of 30; cold = 1 GiB read first, steady = cold + "
+        f"summaries read; lone warm build {states['build_warm_lone_us']:.1f} us, decode "
+        f"{states['decode_warm_lone_us']:.2f} us): build cold {states['build_cold_us']:.1f} us "
+        f"({by['build'] / states['build_cold_us'] / 1e3:.0f} GB/s, "
+        f"{by['build'] / states['build_cold_us'] / 1e3 / HBM_PEAK_GBS:.1%}); decode cold "
+        f"{states['decode_cold_us']:.2f} us ({dec_bytes / states['decode_cold_us'] / 1e3:.0f} "
+        f"GB/s, {dec_bytes / states['decode_cold_us'] / 1e3 / HBM_PEAK_GBS:.1%}), steady "
+        f"{states['decode_steady_us']:.2f} us")
+
     traffic = load_traffic(w.name)
 
     cache = None
@@ -386,7 +440,12 @@ def main(argv=None):
                    "step_us_graph_replay": ms_step_graph * 1e3,
                    "route_us": t_route.mean() * 1e6, "attend_us": t_attend.mean() * 1e6,
                    "attend_gbs_per_query_bytes": by["attend"] / t_attend.mean() / 1e9,
-                   "attend_gbs_distinct_blocks": attend_dedup / t_attend.mean() / 1e9},
+                   "attend_gbs_distinct_blocks": attend_dedup / t_attend.mean() / 1e9,
+                   "cache_states": dict(states, regime="cold: 1 GiB read first; steady: cold, "
+                                        "then the summaries read once; *_lone_us: median of "
+                                        "30 lone launches between events; *_cold_us and "
+                                        "*_steady_us: back-to-back duration + (lone in that "
+                                        "state - lone warm)")},
         "cpu_baseline": cpu,
         "cache_decode_loop": cache,
     }

@@ -20,7 +20,8 @@ reading that keeps every other definition of tis_oracle unchanged:
   * node n of level l covers keys [n * M_l, (n + 1) * M_l) cut at N, with
     M_l = branching**(lv - l) * leaf_block; a node exists when it covers at
     least one key (n * M_l < N);
-  * summary = exact mean of the keys the node covers, rounded once to float32;
+  * summary = exact mean of the keys the node covers, rounded once to float32
+    (or bfloat16, as tis_oracle.round_summary does);
   * route: as in tis_oracle, but the candidates of a level are only the
     children that exist; the beam is min(beam, number of candidates);
   * attend: as in tis_oracle, with leaf block j holding keys
@@ -38,7 +39,7 @@ from typing import Dict, List, Optional, Sequence
 
 import numpy as np
 
-from oracle.tis_oracle import widen
+from oracle.tis_oracle import round_summary, widen
 
 __all__ = ["depth_for", "grow_build", "grow_route", "grow_attend"]
 
@@ -60,14 +61,15 @@ def _existing(n_keys: int, branching: int, leaf_block: int, lv: int, level: int)
 
 
 def grow_build(K: np.ndarray, dtype: str, n_keys: int, branching: int,
-               leaf_block: int) -> Dict[str, object]:
+               leaf_block: int, summary_dtype: str = "f32") -> Dict[str, object]:
     """Summaries of every existing node of the tree over the first n_keys keys.
 
     K: [B, Hkv, C, d] stored keys of a cache with room for C >= n_keys keys
     (rows past n_keys are ignored).  Returns
       levels : lv = depth_for(n_keys, ...)
       mean   : [fp64 [B, Hkv, e_l, d] for l = 1..lv], e_l existing nodes
-      stored : the same rounded once to float32
+      stored : the same rounded once to summary_dtype ("f32" or "bf16",
+               tis_oracle.round_summary), as float32 arrays
     """
     B, H, C, d = K.shape
     if not 1 <= n_keys <= C:
@@ -87,7 +89,7 @@ def grow_build(K: np.ndarray, dtype: str, n_keys: int, branching: int,
                     lo, hi = n * M, min((n + 1) * M, n_keys)
                     means[l - 1][bi, h, n] = k64[lo:hi].sum(axis=0) / (hi - lo)
             del k64
-    stored = [m.astype(np.float32) for m in means]
+    stored = [round_summary(m, summary_dtype) for m in means]
     return {"levels": lv, "mean": means, "stored": stored}
 
 

@@ -19,7 +19,9 @@ chosen by coarse scores and fine softmax attention runs on the selected tokens.
 Readings taken where the pages are silent (each is listed with its reason in
 the design notes of the repository):
   * summary of a node = arithmetic mean of the keys under it, computed exactly
-    and rounded once to float32 (the stored summary);
+    and rounded once to float32 (the stored summary), or, for reduced-precision
+    summaries, rounded once, straight from the exact mean, to bfloat16 (round
+    to nearest, ties to even; never through float32, which would round twice);
   * levels = branchings below the root; leaves = branching**levels contiguous
     blocks of leaf_block keys; the root is implicit and never scored;
   * node score = plain dot product q . summary (fp64, no scale);
@@ -38,7 +40,7 @@ from typing import Dict, List, Optional, Sequence
 
 import numpy as np
 
-__all__ = ["widen", "tree_build", "tree_route", "tree_attend", "decode"]
+__all__ = ["widen", "round_summary", "tree_build", "tree_route", "tree_attend", "decode"]
 
 
 # ---------------------------------------------------------------------------
@@ -58,6 +60,39 @@ def widen(x: np.ndarray, dtype: str) -> np.ndarray:
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
+# ---------------------------------------------------------------------------
+# rounding of the exact means to the stored summary type
+# ---------------------------------------------------------------------------
+
+_BF16_SIG_BITS = 8            # significant bits of a bfloat16 (7 stored + 1)
+_BF16_MIN_QUANTUM_EXP = -133  # spacing of bfloat16 subnormals: 2^-133
+_BF16_OVERFLOW = 2.0 ** 128   # the first power of two past the largest bfloat16
+
+
+def round_summary(x: np.ndarray, summary_dtype: str) -> np.ndarray:
+    """Exact float64 values rounded once to the stored summary type, returned
+    as float32 (every bfloat16 value is a float32 value).
+
+    "f32": IEEE round to nearest even.  "bf16": round to nearest even on the
+    bfloat16 grid (8 significant bits; below 2^-126 the fixed subnormal spacing
+    2^-133), taken directly from the float64 value: x = m * 2^e with
+    0.5 <= |m| < 1 lies on a grid of spacing 2^(e-8), so x / spacing is rounded
+    to an integer (numpy's rint rounds halves to even) and scaled back; both
+    scalings are by powers of two and exact.  Results of magnitude 2^128 or more
+    overflow to infinity, as round to nearest gives."""
+    x = np.asarray(x, dtype=np.float64)
+    if summary_dtype == "f32":
+        return x.astype(np.float32)
+    if summary_dtype != "bf16":
+        raise ValueError(f"unknown summary dtype {summary_dtype!r}")
+    ax = np.abs(x)
+    _, e = np.frexp(ax)
+    q = np.maximum(e - _BF16_SIG_BITS, _BF16_MIN_QUANTUM_EXP)
+    y = np.ldexp(np.rint(np.ldexp(ax, -q)), q)
+    y = np.where(y >= _BF16_OVERFLOW, np.inf, y)
+    return np.copysign(y, x).astype(np.float32)
+
+
 def _check_geometry(n_keys: int, branching: int, leaf_block: int, levels: int) -> None:
     if branching < 2 or leaf_block < 1 or levels < 1:
         raise ValueError("need branching >= 2, leaf_block >= 1, levels >= 1")
@@ -70,7 +105,7 @@ def _check_geometry(n_keys: int, branching: int, leaf_block: int, levels: int) -
 # ---------------------------------------------------------------------------
 
 def tree_build(K: np.ndarray, dtype: str, branching: int, leaf_block: int,
-               levels: int) -> Dict[str, List[np.ndarray]]:
+               levels: int, summary_dtype: str = "f32") -> Dict[str, List[np.ndarray]]:
     """Summaries of every node at levels 1..levels (ZHA Abstract: each tree
     node holds a compressed summary of the cached keys below it).
 
@@ -80,7 +115,8 @@ def tree_build(K: np.ndarray, dtype: str, branching: int, leaf_block: int,
     equal-sized, this equals the recursive mean of child means.
 
     Returns {"mean": [fp64 [B,Hkv,n_l,d] for l=1..levels],
-             "stored": [the same rounded once to float32]}.
+             "stored": [the same rounded once to summary_dtype ("f32" or
+                        "bf16"), as float32 arrays]}.
     """
     B, H, N, d = K.shape
     _check_geometry(N, branching, leaf_block, levels)
@@ -95,7 +131,7 @@ def tree_build(K: np.ndarray, dtype: str, branching: int, leaf_block: int,
                 node_sums = k64.reshape(n_l, M_l, d).sum(axis=1)
                 means[l - 1][bi, h] = node_sums / M_l
             del k64
-    stored = [m.astype(np.float32) for m in means]
+    stored = [round_summary(m, summary_dtype) for m in means]
     return {"mean": means, "stored": stored}
 
 
