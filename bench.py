@@ -29,15 +29,16 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(w):
-    """Bytes the method must move (see the byte model in the design notes)."""
+def algorithmic_bytes(w, summary_bytes: int = 4):
+    """Bytes the method must move (see the byte model in the design notes);
+    summary_bytes: 4 for float32 summaries, 2 for bfloat16."""
     s = w.elem_bytes
     d, b, W, L = w.head_dim, w.branching, w.beam, w.leaf_block
     heads = w.batch * w.kv_heads
     nodes = sum(b ** l for l in range(1, w.levels + 1))
-    build = heads * (w.n_keys * d * s + nodes * d * 4)
+    build = heads * (w.n_keys * d * s + nodes * d * summary_bytes)
     cand = b + sum(min(W, b ** (l - 1)) * b for l in range(2, w.levels + 1))
-    route_q = cand * d * 4 + d * s + 4 * W
+    route_q = cand * d * summary_bytes + d * s + 4 * W
     attend_q = W * L * d * s * 2 + d * s + 4 * W + 4 * d
     return {"build": build, "route": w.queries * route_q, "attend": w.queries * attend_q,
             "candidates_per_query": cand}
@@ -140,6 +141,46 @@ def cpu_baseline(w, x, min_seconds: float = 10.0, max_reps: int = 500):
                       f"numpy fp64, BLAS limited to 1 thread, {el:.1f} s"}
 
 
+def per_launch(torch, fn, reps):
+    """Average duration (s) of fn's launch: reps launches back to back
+    between one event pair (event overhead spread over reps launches)."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / reps
+
+
+def bf16_summaries(tis, torch, w, Q, K, V, reps, warmup):
+    """The step with summaries stored as bfloat16 (the same means rounded
+    once to bfloat16): build and fused decode durations, and the decode's
+    rate on its own algorithmic bytes (each routing level reads half)."""
+    plan = tis.DecodePlan(Q, K, V, w.branching, w.leaf_block, w.levels, w.beam,
+                          summary_dtype="bf16")
+    for _ in range(warmup):
+        plan.build()
+        plan.decode()
+
+    def step():
+        plan.build()
+        plan.decode()
+    step_s = per_launch(torch, step, reps)
+    build_s = per_launch(torch, plan.build, reps)
+    decode_s = per_launch(torch, plan.decode, reps)
+    by = algorithmic_bytes(w, summary_bytes=2)
+    dec = by["route"] + by["attend"]
+    return {"regime": "as the headline step, summaries stored as bfloat16",
+            "step_us": step_s * 1e6, "queries_per_s_step": w.queries / step_s,
+            "build_us": build_s * 1e6, "build_gbs": by["build"] / build_s / 1e9,
+            "decode_us": decode_s * 1e6, "decode_queries_per_s": w.queries / decode_s,
+            "decode_gbs": dec / decode_s / 1e9, "decode_frac": dec / decode_s / 1e9 / HBM_PEAK_GBS,
+            "decode_bytes": dec}
+
+
 def cache_states(torch, dev, plan, reps, back_to_back):
     """Durations in two cache states.  cold: 1 GiB read first, which leaves
     none of the inputs in the Infinity Cache or an L2 and no dirty lines to
@@ -236,6 +277,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cache-loop", action="store_true",
                     help="skip the growing-cache decode loop measurement")
+    ap.add_argument("--no-bf16-summaries", action="store_true",
+                    help="skip the measurement of the step with bfloat16 summaries")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 256 MiB device-to-device copy first (the reference "
                          "dispatch for scaling HBM byte counters)")
@@ -340,20 +383,10 @@ def main(argv=None):
     ms_step_separate = start.elapsed_time(end) / K_
     # timed region 2: each kernel K times back to back between one event pair
     # (its average launch duration; event overhead is spread over K launches)
-    def per_launch(fn):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(K_):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e-3 / K_
-    t_build = np.array([per_launch(plan.build)])
-    t_route = np.array([per_launch(plan.route)])
-    t_attend = np.array([per_launch(plan.attend)])
-    t_decode = per_launch(plan.decode)
+    t_build = np.array([per_launch(torch, plan.build, K_)])
+    t_route = np.array([per_launch(torch, plan.route, K_)])
+    t_attend = np.array([per_launch(torch, plan.attend, K_)])
+    t_decode = per_launch(torch, plan.decode, K_)
 
     by = algorithmic_bytes(w)
     build_gbs = by["build"] / t_build.mean() / 1e9
@@ -392,6 +425,15 @@ def main(argv=None):
         f"{states['decode_cold_us']:.2f} us ({dec_bytes / states['decode_cold_us'] / 1e3:.0f} "
         f"GB/s, {dec_bytes / states['decode_cold_us'] / 1e3 / HBM_PEAK_GBS:.1%}), steady "
         f"{states['decode_steady_us']:.2f} us")
+
+    bf = None
+    if not args.no_bf16_summaries:
+        bf = bf16_summaries(tis, torch, w, Q, K, V, K_, args.warmup)
+        log(f"bf16 summaries: step {bf['step_us']:.1f} us ({bf['queries_per_s_step']:.3e} "
+            f"queries/s); build {bf['build_us']:.2f} us ({bf['build_gbs']:.0f} GB/s); decode "
+            f"{bf['decode_us']:.2f} us -> {bf['decode_queries_per_s']:.3e} queries/s, "
+            f"{bf['decode_gbs']:.0f} GB/s ({bf['decode_frac']:.1%}) on "
+            f"{bf['decode_bytes'] / 1e6:.2f} MB")
 
     traffic = load_traffic(w.name)
 
@@ -448,6 +490,7 @@ def main(argv=None):
                                         "state - lone warm)")},
         "cpu_baseline": cpu,
         "cache_decode_loop": cache,
+        "bf16_summaries": bf,
     }
     print(json.dumps(line), flush=True)
     return 0

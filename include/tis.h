@@ -25,8 +25,9 @@
  *   Layouts are dense row-major:
  *     K, V       [B][Hkv][N][d]   element type `dtype`
  *     Q          [B][Hq][d]       element type `dtype`
- *     summaries  float32, level-major: for l = 1..lv a block [B][Hkv][n_l][d],
- *                block l starting at element offset d*B*Hkv*(n_1+...+n_{l-1})
+ *     summaries  float32 or bfloat16 (the tree's summary_dtype), level-major:
+ *                for l = 1..lv a block [B][Hkv][n_l][d], block l starting at
+ *                element offset d*B*Hkv*(n_1+...+n_{l-1})
  *     indices    int32 [B][Hq][W]
  *     O          float32 [B][Hq][d]
  *
@@ -74,17 +75,31 @@ typedef enum tis_dtype { TIS_F32 = 0, TIS_BF16 = 1 } tis_dtype;
 #define TIS_MAX_CANDIDATES 256
 
 /* A built tree: plain descriptor (no hidden state).  The caller sets
- * `summaries` (device, tis_tree_summary_bytes() bytes) before
- * tis_tree_build; the build fills in the geometry fields. */
+ * `summaries` (device, tis_tree_summary_bytes_as() bytes) and
+ * `summary_dtype` before tis_tree_build; the build fills in the geometry
+ * fields.  Route and decode read summary_dtype from the descriptor.
+ *
+ * summary_dtype: the type the summaries are stored in.  TIS_F32 (0, also
+ *   what a zero-initialised descriptor holds): each node mean rounded once
+ *   to float32.  TIS_BF16: rounded once, straight from the fp64 mean, to
+ *   bfloat16 (round to nearest, ties to even; not through float32), which
+ *   halves the bytes every routing level reads.  The pages fix no precision
+ *   for the summaries; both are the same mean, stored at two widths.  Any
+ *   other value: TIS_E_DTYPE. */
 typedef struct tis_tree {
   int32_t batch, kv_heads, n_keys, head_dim, branching, leaf_block, levels;
-  float *summaries;
+  int32_t summary_dtype;  /* tis_dtype of the stored summaries */
+  void *summaries;
 } tis_tree;
 
-/* Bytes of the summaries buffer: 4 * d * B * Hkv * (n_1 + ... + n_lv).
+/* Bytes of a float32 summaries buffer: 4 * d * B * Hkv * (n_1 + ... + n_lv).
  * Returns 0 if the geometry is invalid or the size overflows. */
 size_t tis_tree_summary_bytes(int batch, int kv_heads, int head_dim, int branching,
                               int levels);
+/* The same for summaries stored as summary_dtype (2 bytes an element for
+ * TIS_BF16); 0 also for an unknown summary_dtype. */
+size_t tis_tree_summary_bytes_as(int batch, int kv_heads, int head_dim, int branching,
+                                 int levels, tis_dtype summary_dtype);
 
 /* Bytes of workspace tis_tree_build needs for this geometry; 0 if none or if
  * the geometry is invalid. */
@@ -99,7 +114,8 @@ size_t tis_build_workspace_bytes(int batch, int kv_heads, int n_keys, int head_d
  * K        [B][Hkv][N][d] keys, dtype TIS_F32 or TIS_BF16 (read once).
  * tree     in: tree->summaries; out: geometry fields filled in.
  * Each summary is the exact mean of the node's keys (sums accumulated in
- * fp64, in a fixed order), rounded once to float32.  Deterministic.
+ * fp64, in a fixed order), rounded once to tree->summary_dtype.
+ * Deterministic.
  * Requires N == b^lv * L, lv >= 1, b >= 2, d in {64,128}.
  */
 tis_status tis_tree_build(const void *K, tis_dtype dtype, int batch, int kv_heads,
@@ -114,8 +130,8 @@ tis_status tis_tree_build(const void *K, tis_dtype dtype, int batch, int kv_head
  * Q        [B][Hq][d], dtype TIS_F32 or TIS_BF16; tree->batch is B.
  * For every query: the candidates of level 1 are the b children of the
  * root; those of level l are all children of the nodes kept at level l-1.
- * A candidate's score is q . summary, computed in fp64 from the stored fp32
- * summary.  The kept set is the first min(beam, #candidates) candidates in
+ * A candidate's score is q . summary, computed in fp64 from the stored
+ * (float32 or bfloat16) summary.  The kept set is the first min(beam, #candidates) candidates in
  * (score descending, node index ascending) order.
  * indices  out: int32 [B][Hq][beam], the kept leaves in ascending order.
  * trace    optional (NULL to skip): int32 [B][Hq][lv][beam], the kept nodes
@@ -206,7 +222,8 @@ const char *tis_version(void);
  * Storage (caller-owned device memory, sized by the two queries below):
  *   K, V       [B][Hkv][capacity][d], element type dtype; rows past n_keys
  *              are never read
- *   summaries  float32, height-major so that no level moves when the tree
+ *   summaries  summary_dtype (float32 or bfloat16, as for tis_tree),
+ *              height-major so that no level moves when the tree
  *              deepens: for height h = 0 (leaves) .. H-1 a block
  *              [B][Hkv][ceil(capacity / (L*b^h))][d], where H is the depth
  *              of a full cache; level l of a tree of depth lv lives at
@@ -224,7 +241,8 @@ typedef struct tis_cache_tree {
   int32_t capacity;  /* keys per (batch, KV head) the cache has room for     */
   int32_t n_keys;    /* keys in the tree: set by reset (0) and append        */
   int32_t levels;    /* depth over n_keys (0 while empty): set by the library */
-  float *summaries;  /* tis_cache_tree_summary_bytes() bytes                 */
+  int32_t summary_dtype; /* tis_dtype of the stored summaries (as tis_tree)  */
+  void *summaries;   /* tis_cache_tree_summary_bytes_as() bytes              */
   double *state;     /* tis_cache_tree_state_bytes() bytes                   */
 } tis_cache_tree;
 
@@ -233,6 +251,9 @@ typedef struct tis_cache_tree {
  * most 16); 0 if invalid or overflowing. */
 size_t tis_cache_tree_summary_bytes(int batch, int kv_heads, int head_dim, int branching,
                                     int leaf_block, int capacity);
+/* Summary bytes for summaries stored as summary_dtype (0 if unknown). */
+size_t tis_cache_tree_summary_bytes_as(int batch, int kv_heads, int head_dim, int branching,
+                                       int leaf_block, int capacity, tis_dtype summary_dtype);
 size_t tis_cache_tree_state_bytes(int batch, int kv_heads, int head_dim, int branching,
                                   int leaf_block, int capacity);
 

@@ -1,8 +1,9 @@
 """Comparison rules between the HIP path and the CPU oracle.
 
-* summaries: float32 values, equal or at most `max_ulp` units in the last
-  place apart (the oracle rounds the exact mean once; the kernel sums in fp64
-  in another order, so a different rounding needs a near-tie of the mean);
+* summaries: equal or at most `max_ulp` units in the last place of the stored
+  type (float32 or bfloat16) apart (the oracle rounds the exact mean once; the
+  kernel sums in fp64 in another order, so a different rounding needs a
+  near-tie of the mean);
 * leaf indices: bit-exact, except on queries whose oracle cut gap at some
   level is below 1e-5 relative, which are counted and reported instead;
 * attention outputs: max-abs error within the tolerance for the input type
@@ -24,13 +25,21 @@ def ulp_distance(a: np.ndarray, b: np.ndarray) -> np.ndarray:
     return np.abs(key(a) - key(b))
 
 
-def compare_summaries(gpu_levels, oracle_stored, max_ulp: int = 1):
-    """Returns (bit_equal, total, worst_ulp); raises AssertionError past max_ulp."""
+# float32 units in the last place per unit of the stored summary type (a
+# bfloat16 drops the low 16 bits of a float32)
+ULP_SCALE = {"f32": 1, "bf16": 1 << 16}
+
+
+def compare_summaries(gpu_levels, oracle_stored, max_ulp: int = 1, summary_dtype: str = "f32"):
+    """Returns (bit_equal, total, worst_ulp), ulps of the stored type; raises
+    AssertionError past max_ulp.  gpu_levels hold float32 values (a bfloat16
+    summary widened exactly)."""
+    scale = ULP_SCALE[summary_dtype]
     equal = total = worst = 0
     for l, (g, o) in enumerate(zip(gpu_levels, oracle_stored), start=1):
         g = np.asarray(g, dtype=np.float32)
         assert g.shape == o.shape, (l, g.shape, o.shape)
-        d = ulp_distance(g, o)
+        d = -(-ulp_distance(g, o) // scale)   # whole units of the stored type, rounded up
         equal += int(np.count_nonzero(d == 0))
         total += d.size
         worst = max(worst, int(d.max()))

@@ -37,6 +37,15 @@ def test_version(lib):
     assert lib.tis_version().decode().startswith("tis ")
 
 
+def test_summary_bytes_by_type(lib):
+    assert lib.tis_tree_summary_bytes_as(4, 8, 128, 8, 3, _lib.TIS_F32) == 4 * 128 * 32 * 584
+    assert lib.tis_tree_summary_bytes_as(4, 8, 128, 8, 3, _lib.TIS_BF16) == 2 * 128 * 32 * 584
+    assert lib.tis_tree_summary_bytes_as(4, 8, 128, 8, 3, 2) == 0
+    assert lib.tis_cache_tree_summary_bytes_as(4, 8, 128, 8, 64, 40000, _lib.TIS_BF16) == (
+        2 * 128 * 32 * (625 + 79 + 10 + 2))
+    assert lib.tis_cache_tree_summary_bytes_as(4, 8, 128, 8, 64, 40000, 9) == 0
+
+
 def test_summary_bytes(lib):
     # 4 * d * B * Hkv * (8 + 64 + 512) for the 32K-key GQA workload
     assert lib.tis_tree_summary_bytes(4, 8, 128, 8, 3) == 4 * 128 * 32 * 584
@@ -82,14 +91,14 @@ def _no_device_visible():
         pytest.skip("host-check tests run where no GPU is visible")
 
 
-def _tree(summ=FAKE, b=2, L=16, lv=3, d=64, B=1, H=1):
-    return _lib.TisTree(B, H, b ** lv * L, d, b, L, lv, summ)
+def _tree(summ=FAKE, b=2, L=16, lv=3, d=64, B=1, H=1, sd=_lib.TIS_F32):
+    return _lib.TisTree(B, H, b ** lv * L, d, b, L, lv, sd, summ)
 
 
 def _build(lib, **kw):
     # b=2, lv=6: the build needs a workspace (two kernels), so ws / wsb are checked
     a = dict(K=FAKE, dt=_lib.TIS_BF16, B=1, H=1, N=1024, d=64, b=2, L=16, lv=6,
-             tree=_lib.TisTree(0, 0, 0, 0, 0, 0, 0, FAKE), ws=FAKE, wsb=0)
+             tree=_lib.TisTree(0, 0, 0, 0, 0, 0, 0, 0, FAKE), ws=FAKE, wsb=0)
     a.update(kw)
     return lib.tis_tree_build(a["K"], a["dt"], a["B"], a["H"], a["N"], a["d"], a["b"], a["L"],
                               a["lv"], ctypes.byref(a["tree"]), a["ws"], a["wsb"], None)
@@ -98,8 +107,9 @@ def _build(lib, **kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(K=None), _lib.TIS_E_NULL),
     (dict(ws=None), _lib.TIS_E_NULL),
-    (dict(tree=_lib.TisTree(0, 0, 0, 0, 0, 0, 0, None)), _lib.TIS_E_NULL),
+    (dict(tree=_lib.TisTree(0, 0, 0, 0, 0, 0, 0, 0, None)), _lib.TIS_E_NULL),
     (dict(dt=7), _lib.TIS_E_DTYPE),
+    (dict(tree=_lib.TisTree(0, 0, 0, 0, 0, 0, 0, 2, FAKE)), _lib.TIS_E_DTYPE),
     (dict(N=96), _lib.TIS_E_SHAPE),
     (dict(b=1), _lib.TIS_E_SHAPE),
     (dict(b=65, N=65 ** 3 * 16, lv=3), _lib.TIS_E_UNSUPPORTED),
@@ -138,7 +148,8 @@ def _route(lib, Q=FAKE, dt=_lib.TIS_F32, Hq=2, tree=None, beam=2, idx=FAKE, trac
     (dict(beam=0), _lib.TIS_E_SHAPE),
     (dict(beam=9), _lib.TIS_E_SHAPE),
     (dict(tree=_tree(b=64, lv=2, L=1), beam=5), _lib.TIS_E_UNSUPPORTED),
-    (dict(tree=_lib.TisTree(1, 1, 100, 64, 2, 16, 3, FAKE)), _lib.TIS_E_SHAPE),
+    (dict(tree=_lib.TisTree(1, 1, 100, 64, 2, 16, 3, 0, FAKE)), _lib.TIS_E_SHAPE),
+    (dict(tree=_tree(sd=-1)), _lib.TIS_E_DTYPE),
     (dict(Q=FAKE + 4), _lib.TIS_E_ALIGN),
     (dict(idx=FAKE + 2), _lib.TIS_E_ALIGN),
     (dict(trace=FAKE + 1), _lib.TIS_E_ALIGN),
@@ -198,6 +209,7 @@ def _decode(lib, Q=FAKE, K=FAKE, V=FAKE, dt=_lib.TIS_BF16, Hq=2, tree=None, beam
     (dict(beam=9), _lib.TIS_E_SHAPE),
     (dict(tree=_tree(b=64, lv=2, L=1), beam=5), _lib.TIS_E_UNSUPPORTED),
     (dict(scale=float("nan")), _lib.TIS_E_SHAPE),
+    (dict(tree=_tree(sd=5)), _lib.TIS_E_DTYPE),
     (dict(V=FAKE + 4), _lib.TIS_E_ALIGN),
     (dict(idx=FAKE + 2), _lib.TIS_E_ALIGN),
     # 2 queries, beam 64 over leaves of 64 keys: split, so a workspace is needed
@@ -230,8 +242,9 @@ def test_cache_tree_bytes(lib):
     assert lib.tis_cache_tree_state_bytes(1, 1, 64, 2, 1, 1 << 20) == 0
 
 
-def _ctree(summ=FAKE, state=FAKE, B=1, H=1, d=64, b=2, L=16, C=1000, n=0, lv=0):
-    return _lib.TisCacheTree(B, H, d, b, L, C, n, lv, summ, state)
+def _ctree(summ=FAKE, state=FAKE, B=1, H=1, d=64, b=2, L=16, C=1000, n=0, lv=0,
+           sd=_lib.TIS_F32):
+    return _lib.TisCacheTree(B, H, d, b, L, C, n, lv, sd, summ, state)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -241,6 +254,7 @@ def _ctree(summ=FAKE, state=FAKE, B=1, H=1, d=64, b=2, L=16, C=1000, n=0, lv=0):
     (dict(d=32), _lib.TIS_E_UNSUPPORTED),
     (dict(C=0), _lib.TIS_E_SHAPE),
     (dict(state=FAKE + 8), _lib.TIS_E_ALIGN),
+    (dict(sd=3), _lib.TIS_E_DTYPE),
 ])
 def test_cache_reset_rejects(lib, kw, status):
     t = _ctree(**kw)

@@ -53,11 +53,12 @@ def _inputs(dtype, b, L, d, Hkv, G, capacity, gen="normal", seed=7, name="cache"
 
 
 def _check(tis, ct, x, Qd, dtype, n, b, L, beam, label):
-    ob = GO.grow_build(x["K"], dtype, n, b, L)
+    sd = ct.summary_dtype
+    ob = GO.grow_build(x["K"], dtype, n, b, L, summary_dtype=sd)
     lv = ob["levels"]
     assert ct.levels == lv and ct.n_keys == n
-    g_levels = [ct.level(l).cpu().numpy() for l in range(1, lv + 1)]
-    eq, tot, worst = parity.compare_summaries(g_levels, ob["stored"])
+    g_levels = [ct.level(l).float().cpu().numpy() for l in range(1, lv + 1)]
+    eq, tot, worst = parity.compare_summaries(g_levels, ob["stored"], summary_dtype=sd)
     orr = GO.grow_route(x["Q"], dtype, ob["stored"], n, b, L, beam)
     idx, tr = ct.route(Qd, beam, trace=True)
     out, didx = ct.decode(Qd, beam, return_indices=True)
@@ -78,24 +79,30 @@ def _check(tis, ct, x, Qd, dtype, n, b, L, beam, label):
 
 
 SEQUENCES = [
-    # (label, dtype, b, L, d, Hkv, G, capacity, beam, first appends)
+    # (label, dtype, b, L, d, Hkv, G, capacity, beam, first appends[, summary type])
     ("tiny_f32", "f32", 3, 5, 64, 2, 2, 405, 4, [1, 1, 3, 1, 4, 5, 9, 1, 20, 1, 44, 1, 90]),
     ("bf16_d128", "bf16", 4, 16, 128, 2, 3, 1000, 6, [1, 15, 1, 47, 1, 191, 1, 100, 300]),
     ("beam_wide", "bf16", 2, 8, 64, 1, 4, 300, 16, [1, 2, 5, 8, 16, 1, 31, 64, 1, 127]),
     ("leaf_1", "f32", 2, 1, 64, 1, 2, 100, 3, [1, 1, 1, 1, 4, 8, 16, 1, 31, 1]),
     ("branch_8_f32", "f32", 8, 4, 128, 2, 2, 600, 5, [7, 1, 24, 1, 224, 1, 255, 2]),
+    # bfloat16 summaries, both head dims
+    ("bf16s_d128", "bf16", 4, 16, 128, 2, 3, 1000, 6, [1, 15, 1, 47, 1, 191, 1, 100, 300],
+     "bf16"),
+    ("bf16s_f32_d64", "f32", 3, 5, 64, 2, 2, 405, 4, [1, 1, 3, 1, 4, 5, 9, 1, 20, 1, 44, 1, 90],
+     "bf16"),
 ]
 
 
 @pytest.mark.parametrize("case", SEQUENCES, ids=[c[0] for c in SEQUENCES])
 def test_append_sequence_matches_oracle(tis, case):
-    label, dtype, b, L, d, Hkv, G, cap, beam, chunks = case
+    label, dtype, b, L, d, Hkv, G, cap, beam, chunks = case[:10]
+    sd = case[10] if len(case) > 10 else "f32"
     t0 = time.time()
     x = _inputs(dtype, b, L, d, Hkv, G, cap, seed=len(label))
     Kd = tis.from_storage(x["K"], dtype, "cuda")
     Vd = tis.from_storage(x["V"], dtype, "cuda")
     Qd = tis.from_storage(x["Q"], dtype, "cuda")
-    ct = tis.CacheTree(Kd, Vd, b, L)
+    ct = tis.CacheTree(Kd, Vd, b, L, summary_dtype=sd)
     n = 0
     rest = cap - sum(chunks)
     assert rest >= 0
@@ -125,7 +132,8 @@ def test_reset_then_refill_matches(tis):
     _check(tis, ct, x, Qd, dtype, 100, b, L, beam, "refill")
 
 
-def test_full_cache_equals_full_tree_calls(tis):
+@pytest.mark.parametrize("sd", ["f32", "bf16"])
+def test_full_cache_equals_full_tree_calls(tis, sd):
     """With n = b^lv * L the cache tree is the full tree: the same summaries
     and the same decode output, bit for bit, as tree_build + tree_decode."""
     w = workloads.small("gqa_32k", levels=2, kv_heads=2)
@@ -134,17 +142,17 @@ def test_full_cache_equals_full_tree_calls(tis):
     Kd = tis.from_storage(x["K"], dtype, "cuda")
     Vd = tis.from_storage(x["V"], dtype, "cuda")
     Qd = tis.from_storage(x["Q"], dtype, "cuda")
-    ct = tis.CacheTree(Kd, Vd, b, L)
+    ct = tis.CacheTree(Kd, Vd, b, L, summary_dtype=sd)
     ct.append(w.n_keys - 129)
     for _ in range(129):
         ct.append(1)
-    tree = tis.tree_build(Kd, b, L, w.levels)
+    tree = tis.tree_build(Kd, b, L, w.levels, summary_dtype=sd)
     out_c, idx_c = ct.decode(Qd, w.beam, return_indices=True)
     out_f, idx_f = tis.tree_decode(Qd, Kd, Vd, tree, w.beam, return_indices=True)
     torch.cuda.synchronize()
     for l in range(1, w.levels + 1):
-        a = ct.level(l).cpu().numpy()
-        f = tree.level(l).cpu().numpy()
+        a = ct.level(l).float().cpu().numpy()
+        f = tree.level(l).float().cpu().numpy()
         assert np.array_equal(a.view(np.uint32), f.view(np.uint32)), l
     assert torch.equal(idx_c, idx_f)
     assert torch.equal(out_c.view(torch.int32), out_f.view(torch.int32))

@@ -39,12 +39,12 @@ def tis():
     return t
 
 
-def run_gpu(t, w, x, oracle_idx=None):
+def run_gpu(t, w, x, oracle_idx=None, summary_dtype="f32"):
     dev = "cuda"
     K = t.from_storage(x["K"], w.dtype, dev)
     V = t.from_storage(x["V"], w.dtype, dev)
     Q = t.from_storage(x["Q"], w.dtype, dev)
-    tree = t.tree_build(K, w.branching, w.leaf_block, w.levels)
+    tree = t.tree_build(K, w.branching, w.leaf_block, w.levels, summary_dtype=summary_dtype)
     idx, tr = t.tree_route(Q, tree, w.beam, trace=True)
     out = t.tree_attend(Q, K, V, idx, w.leaf_block)
     res = {"tree": tree, "idx": idx, "trace": tr, "out": out}
@@ -53,25 +53,28 @@ def run_gpu(t, w, x, oracle_idx=None):
         res["out_oracle_idx"] = t.tree_attend(Q, K, V, oi, w.leaf_block)
     res["fused_out"], res["fused_idx"] = t.tree_decode(Q, K, V, tree, w.beam, return_indices=True)
     torch.cuda.synchronize()
-    res["levels"] = [tree.level(l).cpu().numpy() for l in range(1, w.levels + 1)]
+    res["levels"] = [tree.level(l).float().cpu().numpy() for l in range(1, w.levels + 1)]
     for k in ("idx", "trace", "out", "out_oracle_idx", "fused_out", "fused_idx"):
         if k in res:
             res[k] = res[k].cpu().numpy()
     return res
 
 
-def check_case(t, w, x=None, label=""):
+def check_case(t, w, x=None, label="", summary_dtype="f32"):
     t0 = time.time()
     if x is None:
         x = workloads.generate(w)
     _say(f"{label or w.name}: generated in {time.time() - t0:.1f}s "
          f"(B={w.batch} Hq={w.q_heads} Hkv={w.kv_heads} d={w.head_dim} N={w.n_keys} "
-         f"b={w.branching} L={w.leaf_block} lv={w.levels} W={w.beam} {w.dtype})")
-    ob = O.tree_build(x["K"], w.dtype, w.branching, w.leaf_block, w.levels)
+         f"b={w.branching} L={w.leaf_block} lv={w.levels} W={w.beam} {w.dtype}; "
+         f"{summary_dtype} summaries)")
+    ob = O.tree_build(x["K"], w.dtype, w.branching, w.leaf_block, w.levels,
+                      summary_dtype=summary_dtype)
     orr = O.tree_route(x["Q"], w.dtype, ob["stored"], w.branching, w.beam)
     _say(f"{label or w.name}: oracle build+route done at {time.time() - t0:.1f}s")
-    g = run_gpu(t, w, x, oracle_idx=orr["indices"])
-    eq, tot, worst = parity.compare_summaries(g["levels"], ob["stored"])
+    g = run_gpu(t, w, x, oracle_idx=orr["indices"], summary_dtype=summary_dtype)
+    eq, tot, worst = parity.compare_summaries(g["levels"], ob["stored"],
+                                              summary_dtype=summary_dtype)
     exact, tie, nq = parity.compare_indices(g["idx"], orr)
     parity.compare_trace(g["trace"], orr)
     o_or = O.tree_attend(x["Q"], x["K"], x["V"], w.dtype, orr["indices"], w.leaf_block)
@@ -222,6 +225,32 @@ def test_errors_through_binding(tis):
 
 
 # -------------------------------------------------------------- full size --
+# bfloat16 summaries: the build rounds every mean straight from fp64 and the
+# walk reads 8 summary elements per 16-byte load (both head dims, the
+# single-launch, top-level and per-level builds, splits)
+BF16_SUMMARY_CASES = [
+    workloads.small("gqa_32k", levels=2, kv_heads=2),
+    workloads.small("deep_planted", levels=4, kv_heads=2),
+    workloads.small("long_1m", levels=3, kv_heads=1),
+    _custom("bf16s_ragged_f32_d64", "f32", 3, 5, 3, 4, d=64),
+    _custom("bf16s_single_level", "bf16", 16, 8, 1, 5),
+    _custom("bf16s_cand_256", "bf16", 16, 4, 2, 16),
+    _custom("bf16s_deep_binary", "bf16", 2, 4, 9, 6, d=64, Hkv=3, G=1),
+    _custom("bf16s_split", "bf16", 4, 64, 4, 64, Hkv=2, G=3),
+]
+
+
+@pytest.mark.parametrize("w", BF16_SUMMARY_CASES, ids=[w.name for w in BF16_SUMMARY_CASES])
+def test_bf16_summaries(tis, w):
+    check_case(tis, w, label=f"{w.name} (bf16 summaries)", summary_dtype="bf16")
+
+
+@pytest.mark.timeout(900)
+def test_bf16_summaries_full_gqa_32k(tis):
+    w = workloads.get("gqa_32k")
+    check_case(tis, w, label="gqa_32k (full size, bf16 summaries)", summary_dtype="bf16")
+
+
 FULL = ["alhr_1k", "gqa_32k", "gqa_256k", "deep_planted", "long_1m"]
 
 

@@ -27,28 +27,51 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libtis)")
 
 
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    # packed fp32 instructions stay off (their use is left to no one)
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-command-line-argument",
+    "-I", INCLUDE, "-I", CSRC,
+]
+
+
 def command(out: str = LIB) -> list:
-    return [
-        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-        # packed fp32 instructions stay off (their use is left to no one)
-        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-Wall", "-Wno-unused-command-line-argument",
-        "-I", INCLUDE, "-I", CSRC,
-        "-o", out,
-    ] + [os.path.join(CSRC, s) for s in SOURCES]
+    """The whole build as one hipcc command (what build_library runs, split
+    into one compile per source plus a link so the sources build in parallel)."""
+    return [hipcc()] + FLAGS + ["-shared", "-o", out] + [os.path.join(CSRC, s) for s in SOURCES]
+
+
+def _run(cmd: list) -> subprocess.CompletedProcess:
+    return subprocess.run(cmd, capture_output=True, text=True)
 
 
 def build_library(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = command(tmp)
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError(f"hipcc failed with status {r.returncode}")
-    if verbose and r.stderr.strip():
-        sys.stderr.write(r.stderr)
+    """Compiles every source to an object (in parallel), links libtis.so."""
+    import tempfile
+    from concurrent.futures import ThreadPoolExecutor
+
+    cc = hipcc()
+    with tempfile.TemporaryDirectory(prefix="libtis_") as tmpdir:
+        objs = [os.path.join(tmpdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+        cmds = [[cc] + FLAGS + ["-c", "-o", o, os.path.join(CSRC, s)]
+                for s, o in zip(SOURCES, objs)]
+        tmp = LIB + ".tmp"
+        cmds_link = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+        workers = max(1, min(len(cmds), os.cpu_count() or 1, 8))
+        with ThreadPoolExecutor(workers) as ex:
+            results = list(ex.map(_run, cmds))
+        results.append(_run(cmds_link) if all(r.returncode == 0 for r in results) else None)
+        for cmd, r in zip(cmds + [cmds_link], results):
+            if r is None:
+                continue
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            if r.returncode != 0:
+                sys.stderr.write(r.stdout + r.stderr)
+                raise RuntimeError(f"hipcc failed with status {r.returncode}")
+            if verbose and r.stderr.strip():
+                sys.stderr.write(r.stderr)
     os.replace(tmp, LIB)
     return LIB
 

@@ -28,7 +28,8 @@ class TisTree(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("kv_heads", ctypes.c_int32),
                 ("n_keys", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("branching", ctypes.c_int32), ("leaf_block", ctypes.c_int32),
-                ("levels", ctypes.c_int32), ("summaries", ctypes.c_void_p)]
+                ("levels", ctypes.c_int32), ("summary_dtype", ctypes.c_int32),
+                ("summaries", ctypes.c_void_p)]
 
 
 class TisCacheTree(ctypes.Structure):
@@ -36,6 +37,7 @@ class TisCacheTree(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("branching", ctypes.c_int32),
                 ("leaf_block", ctypes.c_int32), ("capacity", ctypes.c_int32),
                 ("n_keys", ctypes.c_int32), ("levels", ctypes.c_int32),
+                ("summary_dtype", ctypes.c_int32),
                 ("summaries", ctypes.c_void_p), ("state", ctypes.c_void_p)]
 
 
@@ -50,6 +52,7 @@ _c_int, _c_size, _vp, _c_float = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p,
 
 SIGNATURES = {
     "tis_tree_summary_bytes": (_c_size, [_c_int] * 5),
+    "tis_tree_summary_bytes_as": (_c_size, [_c_int] * 6),
     "tis_build_workspace_bytes": (_c_size, [_c_int] * 7),
     "tis_tree_build": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                 _c_int, ctypes.POINTER(TisTree), _vp, _c_size, _vp]),
@@ -62,6 +65,7 @@ SIGNATURES = {
                                  _c_float, _vp, _vp, _vp, _c_size, _vp]),
     "tis_decode_workspace_bytes": (_c_size, [_c_int] * 5),
     "tis_cache_tree_summary_bytes": (_c_size, [_c_int] * 6),
+    "tis_cache_tree_summary_bytes_as": (_c_size, [_c_int] * 7),
     "tis_cache_tree_state_bytes": (_c_size, [_c_int] * 6),
     "tis_cache_tree_reset": (_c_int, [ctypes.POINTER(TisCacheTree), _vp]),
     "tis_cache_tree_append": (_c_int, [_vp, _c_int, _c_int, ctypes.POINTER(TisCacheTree), _vp]),

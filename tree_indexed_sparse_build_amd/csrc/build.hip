@@ -6,9 +6,9 @@
 // HBM-bound: K is read exactly once with 16-byte coalesced loads (a wave
 // reads whole 1 KB stretches of a leaf block, 16 KB in flight per wave),
 // each summary row is written once.  Sums are carried in fp64 in a fixed
-// order and rounded once to fp32.  A wave reduces a subtree of b^kw leaves
-// (a stack of open node sums in registers); a workgroup of b^kg waves
-// finishes its chunk's inner levels in LDS.  When the chunk roots sit below
+// order and rounded once to the summary type (float32 or bfloat16).  A wave
+// reduces a subtree of b^kw leaves (a stack of open node sums in registers);
+// a workgroup of b^kg waves finishes its chunk's inner levels in LDS.  When the chunk roots sit below
 // level 1, a second small kernel climbs from their fp64 sums (one launch
 // while a level-1 subtree fits in LDS, else one launch per level): kernel
 // boundaries instead of device-scope fences between workgroups.  When K is
@@ -21,11 +21,11 @@
 namespace tis {
 namespace {
 
-// Mean of a node from its fp64 sum over M keys, rounded once to fp32.  When M
-// is a power of two the product with 1/M is exact, the same value as s / M.
-__device__ inline float node_mean(const BuildArgs &a, int level, double s) {
-  return static_cast<float>(((a.pow2_levels >> level) & 1) ? s * a.mean_inv[level]
-                                                          : s / a.mean_div[level]);
+// Mean of a node from its fp64 sum over M keys (rounded once when stored).
+// When M is a power of two the product with 1/M is exact, the same value as
+// s / M.
+__device__ inline double node_mean(const BuildArgs &a, int level, double s) {
+  return ((a.pow2_levels >> level) & 1) ? s * a.mean_inv[level] : s / a.mean_div[level];
 }
 
 // Transposed reduction of a lane's E column sums over the R = 64 / LPR row
@@ -61,7 +61,10 @@ template <int E, int LPR> __device__ inline int rowgroup_offset(int lane) {
 // in L2.  Measured on MI355X: 1-2% faster on the 0.5-2 GB K builds, 6%
 // slower on a K that partly stays in the Infinity Cache, where plain stores
 // are used.  Streaming (non-temporal) stores are slower in both cases.
-template <int CPL> __device__ inline void store_cols(float *dst, const float *f, bool through) {
+template <int CPL> __device__ inline void store_cols(float *dst, const double *m, bool through) {
+  float f[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) f[j] = static_cast<float>(m[j]);
   if (through) {
 #pragma unroll
     for (int j = 0; j < CPL; ++j)
@@ -72,8 +75,25 @@ template <int CPL> __device__ inline void store_cols(float *dst, const float *f,
     dst[0] = f[0];
   }
 }
+// bfloat16 summaries: CPL adjacent columns in one 4- or 2-byte store (the
+// write-through form only where it is a whole dword)
+template <int CPL>
+__device__ inline void store_cols(bf16_bits *dst, const double *m, bool through) {
+  if constexpr (CPL == 2) {
+    const uint32_t v = static_cast<uint32_t>(bf16_from_double(m[0])) |
+                       (static_cast<uint32_t>(bf16_from_double(m[1])) << 16);
+    uint32_t *p = reinterpret_cast<uint32_t *>(dst);
+    if (through)
+      __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      *p = v;
+  } else {
+    dst[0].v = bf16_from_double(m[0]);
+  }
+}
 
-template <typename T, int D> __global__ void __launch_bounds__(1024) k_build(BuildArgs a) {
+template <typename T, typename S, int D>
+__global__ void __launch_bounds__(1024) k_build(BuildArgs a) {
   using G = RowGeom<T, D>;
   constexpr int E = G::kElemsPerLane;
   constexpr int LPR = G::kLanesPerRow;
@@ -82,6 +102,7 @@ template <typename T, int D> __global__ void __launch_bounds__(1024) k_build(Bui
   constexpr int U = 8;        // 16-byte loads per lane per batch (two batches in flight)
   static_assert(CPL * 64 == D, "one finished column block per lane");
   extern __shared__ double lds[];
+  S *const summ = static_cast<S *>(a.summ);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -160,10 +181,10 @@ template <typename T, int D> __global__ void __launch_bounds__(1024) k_build(Bui
     ++cc;
     rowgroup_steps<E, LPR, 32, 0>(acc, lane);
     {
-      float f[CPL];
+      double m[CPL];
 #pragma unroll
-      for (int j = 0; j < CPL; ++j) f[j] = node_mean(a, lv, acc[j]);
-      store_cols<CPL>(a.summ + a.summ_off[lv] + (head * a.n_at[lv] + leaf) * D + colf, f,
+      for (int j = 0; j < CPL; ++j) m[j] = node_mean(a, lv, acc[j]);
+      store_cols<CPL>(summ + a.summ_off[lv] + (head * a.n_at[lv] + leaf) * D + colf, m,
                       a.stream_loads != 0);
     }
     double carry[CPL];
@@ -180,10 +201,10 @@ template <typename T, int D> __global__ void __launch_bounds__(1024) k_build(Bui
       if (++ctr[k] < b) break;
       const int lvl = lv - k - 1;
       if (lvl >= 1) {
-        float f[CPL];
+        double m[CPL];
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) f[j] = node_mean(a, lvl, st[k][j]);
-        store_cols<CPL>(a.summ + a.summ_off[lvl] + (head * a.n_at[lvl] + nid[k]) * D + colf, f,
+        for (int j = 0; j < CPL; ++j) m[j] = node_mean(a, lvl, st[k][j]);
+        store_cols<CPL>(summ + a.summ_off[lvl] + (head * a.n_at[lvl] + nid[k]) * D + colf, m,
                         a.stream_loads != 0);
       }
 #pragma unroll
@@ -227,7 +248,8 @@ template <typename T, int D> __global__ void __launch_bounds__(1024) k_build(Bui
       for (int c = 0; c < b; ++c) s += cur[(n * b + c) * D + dd];
       nxt[n * D + dd] = s;
       if (lvl >= 1)
-        a.summ[a.summ_off[lvl] + (head * a.n_at[lvl] + base + n) * D + dd] = node_mean(a, lvl, s);
+        SummaryType<S>::put(summ + a.summ_off[lvl] + (head * a.n_at[lvl] + base + n) * D + dd,
+                            node_mean(a, lvl, s));
     }
     __syncthreads();
     double *t = cur;
@@ -246,7 +268,8 @@ template <typename T, int D> __global__ void __launch_bounds__(1024) k_build(Bui
 // sums (level l+1), one thread per (node, column), every load independent.
 // Launched once per level, from r-1 down to 1; the kernel boundary between
 // levels orders the writes of one level before the reads of the next.
-template <int D> __global__ void __launch_bounds__(256) k_build_level(BuildArgs a, int l) {
+template <typename S, int D>
+__global__ void __launch_bounds__(256) k_build_level(BuildArgs a, int l) {
   const int64_t item = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t nodes = a.chunks_at_level[l];  // B*Hkv*n_l
   if (item >= nodes * D) return;
@@ -256,7 +279,7 @@ template <int D> __global__ void __launch_bounds__(256) k_build_level(BuildArgs 
   const double *child = a.ws_sum + a.ws_off[l + 1] + node * b * D + t;
   double s = 0.0;
   for (int c = 0; c < b; ++c) s += child[static_cast<int64_t>(c) * D];
-  a.summ[a.summ_off[l] + node * D + t] = node_mean(a, l, s);
+  SummaryType<S>::put(static_cast<S *>(a.summ) + a.summ_off[l] + node * D + t, node_mean(a, l, s));
   if (l >= 2) a.ws_sum[a.ws_off[l] + node * D + t] = s;
 }
 
@@ -264,8 +287,9 @@ template <int D> __global__ void __launch_bounds__(256) k_build_level(BuildArgs 
 // b^(r-2) nodes of level r-1 in its subtree sum their children's fp64 sums
 // from the workspace (all loads independent), the levels above are summed in
 // LDS.  Used when the subtree's level r-1 fits in LDS.
-template <int D> __global__ void __launch_bounds__(256) k_build_top(BuildArgs a) {
+template <typename S, int D> __global__ void __launch_bounds__(256) k_build_top(BuildArgs a) {
   extern __shared__ double lds[];
+  S *const summ = static_cast<S *>(a.summ);
   const int tid = threadIdx.x;
   const int b = a.branching;
   const int r = a.root_level;
@@ -284,7 +308,7 @@ template <int D> __global__ void __launch_bounds__(256) k_build_top(BuildArgs a)
     double s = 0.0;
     for (int c = 0; c < b; ++c) s += child[static_cast<int64_t>(c) * D];
     cur[i] = s;
-    a.summ[a.summ_off[l] + node * D + t] = node_mean(a, l, s);
+    SummaryType<S>::put(summ + a.summ_off[l] + node * D + t, node_mean(a, l, s));
   }
   __syncthreads();
   for (--l; l >= 1; --l) {
@@ -296,7 +320,8 @@ template <int D> __global__ void __launch_bounds__(256) k_build_top(BuildArgs a)
       double s = 0.0;
       for (int c = 0; c < b; ++c) s += cur[(n * b + c) * D + t];
       nxt[i] = s;
-      a.summ[a.summ_off[l] + (head * a.n_at[l] + first + n) * D + t] = node_mean(a, l, s);
+      SummaryType<S>::put(summ + a.summ_off[l] + (head * a.n_at[l] + first + n) * D + t,
+                          node_mean(a, l, s));
     }
     __syncthreads();
     double *tmp = cur;
@@ -366,41 +391,48 @@ bool plan_build(int64_t heads, int head_dim, int branching, int leaf_block, int 
   return true;
 }
 
-hipError_t launch_build(Dt dt, int head_dim, int64_t heads, const BuildArgs &a,
-                        const BuildPlan &p, hipStream_t s) {
+namespace {
+
+// Launches of one (input type, summary type, head dim).
+template <typename T, typename S, int D>
+hipError_t launch_build_t(int64_t heads, const BuildArgs &a, const BuildPlan &p, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(heads * p.chunks));
   const dim3 block(static_cast<unsigned>(p.waves * 64));
-  if (dt == Dt::BF16 && head_dim == 128)
-    hipLaunchKernelGGL((k_build<bf16_bits, 128>), grid, block, p.lds_bytes, s, a);
-  else if (dt == Dt::BF16 && head_dim == 64)
-    hipLaunchKernelGGL((k_build<bf16_bits, 64>), grid, block, p.lds_bytes, s, a);
-  else if (dt == Dt::F32 && head_dim == 128)
-    hipLaunchKernelGGL((k_build<float, 128>), grid, block, p.lds_bytes, s, a);
-  else if (dt == Dt::F32 && head_dim == 64)
-    hipLaunchKernelGGL((k_build<float, 64>), grid, block, p.lds_bytes, s, a);
-  else
-    return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_build<T, S, D>), grid, block, p.lds_bytes, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.root_level < 2) return e;
-  if (a.top_rows * head_dim * sizeof(double) * 2 <= kTopLdsBytes) {
+  if (a.top_rows * D * sizeof(double) * 2 <= kTopLdsBytes) {
     const dim3 g(static_cast<unsigned>(heads * a.branching));
-    const size_t lds = static_cast<size_t>(a.top_rows) * head_dim * sizeof(double) * 2;
-    if (head_dim == 128)
-      hipLaunchKernelGGL((k_build_top<128>), g, dim3(256), lds, s, a);
-    else
-      hipLaunchKernelGGL((k_build_top<64>), g, dim3(256), lds, s, a);
+    const size_t lds = static_cast<size_t>(a.top_rows) * D * sizeof(double) * 2;
+    hipLaunchKernelGGL((k_build_top<S, D>), g, dim3(256), lds, s, a);
     return hipGetLastError();
   }
   for (int l = p.root_level - 1; e == hipSuccess && l >= 1; --l) {
-    const int64_t items = a.chunks_at_level[l] * head_dim;
+    const int64_t items = a.chunks_at_level[l] * D;
     const dim3 g(static_cast<unsigned>((items + 255) / 256));
-    if (head_dim == 128)
-      hipLaunchKernelGGL((k_build_level<128>), g, dim3(256), 0, s, a, l);
-    else
-      hipLaunchKernelGGL((k_build_level<64>), g, dim3(256), 0, s, a, l);
+    hipLaunchKernelGGL((k_build_level<S, D>), g, dim3(256), 0, s, a, l);
     e = hipGetLastError();
   }
   return e;
+}
+
+template <typename T, typename S>
+hipError_t launch_build_ts(int head_dim, int64_t heads, const BuildArgs &a, const BuildPlan &p,
+                           hipStream_t s) {
+  if (head_dim == 128) return launch_build_t<T, S, 128>(heads, a, p, s);
+  if (head_dim == 64) return launch_build_t<T, S, 64>(heads, a, p, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_build(Dt dt, Dt sdt, int head_dim, int64_t heads, const BuildArgs &a,
+                        const BuildPlan &p, hipStream_t s) {
+  if (dt == Dt::BF16)
+    return sdt == Dt::BF16 ? launch_build_ts<bf16_bits, bf16_bits>(head_dim, heads, a, p, s)
+                           : launch_build_ts<bf16_bits, float>(head_dim, heads, a, p, s);
+  return sdt == Dt::BF16 ? launch_build_ts<float, bf16_bits>(head_dim, heads, a, p, s)
+                         : launch_build_ts<float, float>(head_dim, heads, a, p, s);
 }
 
 }  // namespace tis

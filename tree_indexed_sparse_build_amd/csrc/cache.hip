@@ -33,7 +33,7 @@ template <> __device__ inline double key_elem<bf16_bits>(const bf16_bits *p) {
   return __uint_as_float(static_cast<uint32_t>(p->v) << 16);
 }
 
-template <typename T, int D>
+template <typename T, typename S, int D>
 __global__ void __launch_bounds__(kAppendThreads) k_cache_append(AppendArgs a) {
   __shared__ double ls[kAppendBatch][D];
   const int64_t head = blockIdx.x;
@@ -45,6 +45,7 @@ __global__ void __launch_bounds__(kAppendThreads) k_cache_append(AppendArgs a) {
   const int b = a.branching;
   const int H = a.heights;
   const T *kh = static_cast<const T *>(a.K) + head * a.capacity * D + c;
+  S *const summ = static_cast<S *>(a.summ);
   double *st = a.state + head * H * D + c;
 
   // per height h: first summary row of this head, keys under one node
@@ -97,8 +98,8 @@ __global__ void __launch_bounds__(kAppendThreads) k_cache_append(AppendArgs a) {
           if (h < H) {
             open[h] += v;
             if (closing) {
-              a.summ[base[h] + static_cast<int64_t>(m - 1u) * D + c] =
-                  static_cast<float>(open[h] / static_cast<double>(span[h]));
+              SummaryType<S>::put(summ + base[h] + static_cast<int64_t>(m - 1u) * D + c,
+                                  open[h] / static_cast<double>(span[h]));
               open[h] = 0.0;
               closing = m % static_cast<uint32_t>(b) == 0u;
               m /= static_cast<uint32_t>(b);
@@ -117,8 +118,8 @@ __global__ void __launch_bounds__(kAppendThreads) k_cache_append(AppendArgs a) {
         const uint32_t node = n1 / span[h];
         const uint32_t held = n1 - node * span[h];
         if (held > 0u)
-          a.summ[base[h] + static_cast<int64_t>(node) * D + c] =
-              static_cast<float>(open[h] / static_cast<double>(held));
+          SummaryType<S>::put(summ + base[h] + static_cast<int64_t>(node) * D + c,
+                              open[h] / static_cast<double>(held));
         st[h * D] = held > 0u ? open[h] : 0.0;
       }
     }
@@ -139,20 +140,29 @@ hipError_t launch_cache_reset(double *state, int64_t elems, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_cache_append(Dt dt, int head_dim, const AppendArgs &a, hipStream_t s) {
+namespace {
+
+template <typename T, typename S>
+hipError_t launch_cache_append_ts(int head_dim, const AppendArgs &a, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.heads));
   const dim3 block(kAppendThreads);
-  if (dt == Dt::BF16 && head_dim == 128)
-    hipLaunchKernelGGL((k_cache_append<bf16_bits, 128>), grid, block, 0, s, a);
-  else if (dt == Dt::BF16 && head_dim == 64)
-    hipLaunchKernelGGL((k_cache_append<bf16_bits, 64>), grid, block, 0, s, a);
-  else if (dt == Dt::F32 && head_dim == 128)
-    hipLaunchKernelGGL((k_cache_append<float, 128>), grid, block, 0, s, a);
-  else if (dt == Dt::F32 && head_dim == 64)
-    hipLaunchKernelGGL((k_cache_append<float, 64>), grid, block, 0, s, a);
+  if (head_dim == 128)
+    hipLaunchKernelGGL((k_cache_append<T, S, 128>), grid, block, 0, s, a);
+  else if (head_dim == 64)
+    hipLaunchKernelGGL((k_cache_append<T, S, 64>), grid, block, 0, s, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_cache_append(Dt dt, Dt sdt, int head_dim, const AppendArgs &a, hipStream_t s) {
+  if (dt == Dt::BF16)
+    return sdt == Dt::BF16 ? launch_cache_append_ts<bf16_bits, bf16_bits>(head_dim, a, s)
+                           : launch_cache_append_ts<bf16_bits, float>(head_dim, a, s);
+  return sdt == Dt::BF16 ? launch_cache_append_ts<float, bf16_bits>(head_dim, a, s)
+                         : launch_cache_append_ts<float, float>(head_dim, a, s);
 }
 
 }  // namespace tis

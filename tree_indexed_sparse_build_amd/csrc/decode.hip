@@ -18,7 +18,7 @@ namespace {
 constexpr int kDecodeWaves = 16;
 constexpr int kDecodeWalkWaves = 8;  // waves that walk the tree (see route_walk)
 
-template <typename T, int D, bool CACHE>
+template <typename T, typename S, int D, bool CACHE>
 __global__ void __launch_bounds__(kDecodeWaves * 64) k_decode(RouteArgs ra, AttendArgs aa) {
   __shared__ RouteShared<kDecodeWaves> rsh;
   __shared__ AttendShared<T, D> ash;
@@ -27,7 +27,7 @@ __global__ void __launch_bounds__(kDecodeWaves * 64) k_decode(RouteArgs ra, Atte
   const int qi = query_of_slot(blockIdx.x - sp * aa.queries, aa.queries, aa.group);
   const uint4 qraw = attend_q_raw<T, D>(aa, qi);  // in flight during the walk
   // every part walks the tree (the repeated summary reads hit the XCD's L2)
-  const int kept = route_walk<T, D, kDecodeWaves, kDecodeWalkWaves, CACHE>(ra, rsh, qi);
+  const int kept = route_walk<T, S, D, kDecodeWaves, kDecodeWalkWaves, CACHE>(ra, rsh, qi);
   if (ra.indices && sp == 0) {
     int32_t *out = ra.indices + static_cast<int64_t>(qi) * ra.beam;
     write_ascending<kDecodeWaves * 64>(rsh.front, kept, out);
@@ -42,30 +42,38 @@ __global__ void __launch_bounds__(kDecodeWaves * 64) k_decode(RouteArgs ra, Atte
   attend_query<T, D, CACHE>(aa, ash, qi, qraw, rsh.front + s0, nullptr, s1 - s0, false, part);
 }
 
-template <bool CACHE>
-hipError_t launch_decode_layout(Dt dt, int head_dim, const RouteArgs &ra, const AttendArgs &aa,
-                                hipStream_t s) {
+template <typename T, typename S, bool CACHE>
+hipError_t launch_decode_t(int head_dim, const RouteArgs &ra, const AttendArgs &aa,
+                           hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(ra.queries) * static_cast<unsigned>(aa.splits));
   const dim3 block(kDecodeWaves * 64);
-  if (dt == Dt::BF16 && head_dim == 128)
-    hipLaunchKernelGGL((k_decode<bf16_bits, 128, CACHE>), grid, block, 0, s, ra, aa);
-  else if (dt == Dt::BF16 && head_dim == 64)
-    hipLaunchKernelGGL((k_decode<bf16_bits, 64, CACHE>), grid, block, 0, s, ra, aa);
-  else if (dt == Dt::F32 && head_dim == 128)
-    hipLaunchKernelGGL((k_decode<float, 128, CACHE>), grid, block, 0, s, ra, aa);
-  else if (dt == Dt::F32 && head_dim == 64)
-    hipLaunchKernelGGL((k_decode<float, 64, CACHE>), grid, block, 0, s, ra, aa);
+  if (head_dim == 128)
+    hipLaunchKernelGGL((k_decode<T, S, 128, CACHE>), grid, block, 0, s, ra, aa);
+  else if (head_dim == 64)
+    hipLaunchKernelGGL((k_decode<T, S, 64, CACHE>), grid, block, 0, s, ra, aa);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
+template <typename T, typename S>
+hipError_t launch_decode_ts(int head_dim, const RouteArgs &ra, const AttendArgs &aa,
+                            hipStream_t s) {
+  return ra.cache ? launch_decode_t<T, S, true>(head_dim, ra, aa, s)
+                  : launch_decode_t<T, S, false>(head_dim, ra, aa, s);
+}
+
 }  // namespace
 
-hipError_t launch_decode(Dt dt, int head_dim, const RouteArgs &ra, const AttendArgs &aa,
-                         hipStream_t s) {
-  hipError_t e = ra.cache ? launch_decode_layout<true>(dt, head_dim, ra, aa, s)
-                          : launch_decode_layout<false>(dt, head_dim, ra, aa, s);
+hipError_t launch_decode(Dt dt, Dt sdt, int head_dim, const RouteArgs &ra,
+                         const AttendArgs &aa, hipStream_t s) {
+  hipError_t e;
+  if (dt == Dt::BF16)
+    e = sdt == Dt::BF16 ? launch_decode_ts<bf16_bits, bf16_bits>(head_dim, ra, aa, s)
+                        : launch_decode_ts<bf16_bits, float>(head_dim, ra, aa, s);
+  else
+    e = sdt == Dt::BF16 ? launch_decode_ts<float, bf16_bits>(head_dim, ra, aa, s)
+                        : launch_decode_ts<float, float>(head_dim, ra, aa, s);
   if (e != hipSuccess || aa.splits <= 1) return e;
   return launch_combine(head_dim, aa, s);
 }

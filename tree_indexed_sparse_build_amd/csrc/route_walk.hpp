@@ -38,11 +38,12 @@ __device__ inline uint32_t pin(uint32_t x) {
   return x;
 }
 
-// Raw bits of this lane's 4 query elements (columns col .. col + 3).  They
-// stay raw until a level's summary loads are in flight, so the wait for the
-// query row overlaps those loads.
-template <typename T> struct QRaw;
-template <> struct QRaw<float> {
+// Raw bits of this lane's E query elements (columns col .. col + E - 1, E
+// the summary elements one 16-byte load holds: 4 float32 or 8 bfloat16).
+// They stay raw until a level's summary loads are in flight, so the wait for
+// the query row overlaps those loads.
+template <typename T, int E> struct QRaw;
+template <> struct QRaw<float, 4> {
   uint4 r;
   __device__ inline void load(const float *q) { r = *reinterpret_cast<const uint4 *>(q); }
   __device__ inline void widen(double *out) const {
@@ -52,7 +53,18 @@ template <> struct QRaw<float> {
     out[3] = __uint_as_float(pin(r.w));
   }
 };
-template <> struct QRaw<bf16_bits> {
+template <> struct QRaw<float, 8> {
+  QRaw<float, 4> lo, hi;
+  __device__ inline void load(const float *q) {
+    lo.load(q);
+    hi.load(q + 4);
+  }
+  __device__ inline void widen(double *out) const {
+    lo.widen(out);
+    hi.widen(out + 4);
+  }
+};
+template <> struct QRaw<bf16_bits, 4> {
   uint2 r;
   __device__ inline void load(const bf16_bits *q) { r = *reinterpret_cast<const uint2 *>(q); }
   __device__ inline void widen(double *out) const {
@@ -61,6 +73,17 @@ template <> struct QRaw<bf16_bits> {
     out[1] = __uint_as_float(x & 0xffff0000u);
     out[2] = __uint_as_float(y << 16);
     out[3] = __uint_as_float(y & 0xffff0000u);
+  }
+};
+template <> struct QRaw<bf16_bits, 8> {
+  uint4 r;
+  __device__ inline void load(const bf16_bits *q) { r = *reinterpret_cast<const uint4 *>(q); }
+  __device__ inline void widen(double *out) const {
+    const uint4 p = make_uint4(pin(r.x), pin(r.y), pin(r.z), pin(r.w));
+    float f[8];
+    Vec16<bf16_bits>::unpack(p, f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = f[e];
   }
 };
 
@@ -140,12 +163,15 @@ template <int NT> __device__ inline void write_ascending(const int *v, int n, in
 // workgroup cover UU rows per lane per pass, UU just large enough for C, and
 // every load of a pass is issued before any is used: rows past C read
 // candidate 0 again (always a valid address) and their scores are dropped,
-// so no branch splits the loads.
-template <typename T, int D, int UU, bool HOLES>
-__device__ inline void score_rows(const float *sl, int C, bool all, const int *cand,
-                                  uint64_t *keys, int bits, const QRaw<T> &qr, int nsw,
-                                  int w, int lane) {
-  constexpr int LPR = D / 4;    // lanes per fp32 summary row
+// so no branch splits the loads.  A lane loads 16 bytes of a row: 4 float32
+// or 8 bfloat16 summary elements.
+template <typename T, typename S, int D, int UU, bool HOLES>
+__device__ inline void score_rows(const S *sl, int C, bool all, const int *cand,
+                                  uint64_t *keys, int bits,
+                                  const QRaw<T, Vec16<S>::kElems> &qr, int nsw, int w,
+                                  int lane) {
+  constexpr int E = Vec16<S>::kElems;
+  constexpr int LPR = D / E;    // lanes per summary row
   constexpr int RPI = 64 / LPR; // rows per wave-wide load
   constexpr int REP = LPR / UU; // lanes sharing one reduced score
   static_assert(UU >= 1 && UU <= LPR, "rows per lane");
@@ -159,22 +185,23 @@ __device__ inline void score_rows(const float *sl, int C, bool all, const int *c
       const int pc = pos < C ? pos : 0;
       node[u] = all ? pc : cand[pc];
     }
-    float4 v[UU];
+    uint4 v[UU];
 #pragma unroll
     for (int u = 0; u < UU; ++u) {
       const int nd = HOLES && node[u] < 0 ? 0 : node[u];  // a hole reads node 0
-      v[u] = *reinterpret_cast<const float4 *>(sl + static_cast<int64_t>(nd) * D);
+      v[u] = load16(sl + static_cast<int64_t>(nd) * D);
     }
-    double q[4];
+    double q[E];
     qr.widen(q);
     double part[UU];
 #pragma unroll
     for (int u = 0; u < UU; ++u) {
       // fp32 x (fp32 or bf16) products are exact in fp64
-      double s = q[0] * static_cast<double>(v[u].x);
-      s = fma(q[1], static_cast<double>(v[u].y), s);
-      s = fma(q[2], static_cast<double>(v[u].z), s);
-      s = fma(q[3], static_cast<double>(v[u].w), s);
+      float f[E];
+      Vec16<S>::unpack(v[u], f);
+      double s = q[0] * static_cast<double>(f[0]);
+#pragma unroll
+      for (int e = 1; e < E; ++e) s = fma(q[e], static_cast<double>(f[e]), s);
       part[u] = s;
     }
     const double s = group_transpose_reduce<UU, LPR>(part, lane);
@@ -205,14 +232,15 @@ __device__ inline void score_rows(const float *sl, int C, bool all, const int *c
 // starts about a microsecond after the first), so leaving the late waves out
 // of the walk keeps them off its critical path: they only have to reach
 // each barrier, and the attention after the walk is where they are needed.
-template <typename T, int D, int NW, int NRW, bool CACHE>
+template <typename T, typename S, int D, int NW, int NRW, bool CACHE>
 __device__ int route_walk(const RouteArgs &a, RouteShared<NW> &sh, int qi) {
   constexpr int NT = NW * 64;
   constexpr int LOG_NRT = NRW == 16 ? 10 : NRW == 8 ? 9 : NRW == 4 ? 8 : -1;
   static_assert(LOG_NRT > 0 && NRW <= NW, "4, 8 or 16 walking waves");
   static_assert(kMaxCandidates <= NRW * 64 / 2, "two or more threads per candidate");
-  constexpr int LPR = D / 4;          // lanes per fp32 summary row
-  constexpr int RPI = 64 / LPR;       // rows per wave-wide load
+  constexpr int E = Vec16<S>::kElems;  // summary elements per lane (16 bytes)
+  constexpr int LPR = D / E;           // lanes per summary row
+  constexpr int RPI = 64 / LPR;        // rows per wave-wide load
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -224,9 +252,9 @@ __device__ int route_walk(const RouteArgs &a, RouteShared<NW> &sh, int qi) {
   const int W = a.beam;
   const int lv = a.levels;
   const int l0 = a.first_cut;
-  const int col = (lane % LPR) * 4;
+  const int col = (lane % LPR) * E;
 
-  QRaw<T> qr;
+  QRaw<T, E> qr;
   qr.load(static_cast<const T *>(a.Q) + static_cast<int64_t>(qi) * D + col);
 
   LevelCursor<CACHE> lc;
@@ -274,19 +302,19 @@ __device__ int route_walk(const RouteArgs &a, RouteShared<NW> &sh, int qi) {
     if (CACHE && tid == 0) sh.holes[(l + 2) % 3] = 0;
     if (live > W) {
       const int bits = 32 - __clz(static_cast<int>(lc.exist) - 1);
-      const float *sl = a.summ + lc.off + head * lc.rows * D + col;
+      const S *sl = static_cast<const S *>(a.summ) + lc.off + head * lc.rows * D + col;
       // the walking waves score, each lane taking `per` rows
       const int per = (C + NRW * RPI - 1) / (NRW * RPI);
       const int *cand = sh.cand[cur];
       if (w < NRW) {
         if (per <= 1)
-          score_rows<T, D, 1, CACHE>(sl, C, all, cand, sh.keys, bits, qr, NRW, w, lane);
+          score_rows<T, S, D, 1, CACHE>(sl, C, all, cand, sh.keys, bits, qr, NRW, w, lane);
         else if (per <= 2)
-          score_rows<T, D, 2, CACHE>(sl, C, all, cand, sh.keys, bits, qr, NRW, w, lane);
+          score_rows<T, S, D, 2, CACHE>(sl, C, all, cand, sh.keys, bits, qr, NRW, w, lane);
         else if (per <= 4)
-          score_rows<T, D, 4, CACHE>(sl, C, all, cand, sh.keys, bits, qr, NRW, w, lane);
+          score_rows<T, S, D, 4, CACHE>(sl, C, all, cand, sh.keys, bits, qr, NRW, w, lane);
         else
-          score_rows<T, D, 8, CACHE>(sl, C, all, cand, sh.keys, bits, qr, NRW, w, lane);
+          score_rows<T, S, D, 8, CACHE>(sl, C, all, cand, sh.keys, bits, qr, NRW, w, lane);
       }
       __syncthreads();
       // rank of candidate i = number of candidates with a larger key.  Each

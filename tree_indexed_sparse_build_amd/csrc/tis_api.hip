@@ -77,6 +77,17 @@ tis_status check_dtype(tis_dtype dt) {
   return TIS_OK;
 }
 
+// The stored type of a tree's summaries (a field the caller sets).
+tis_status check_summary_dtype(const char *who, int32_t sd) {
+  if (sd != TIS_F32 && sd != TIS_BF16)
+    return fail(TIS_E_DTYPE, "%s: unknown summary_dtype %d", who, (int)sd);
+  return TIS_OK;
+}
+
+tis::Dt to_dt(int32_t d) { return d == TIS_BF16 ? tis::Dt::BF16 : tis::Dt::F32; }
+
+size_t summary_elem_bytes(int32_t sd) { return sd == TIS_BF16 ? 2 : 4; }
+
 tis_status hip_status(hipError_t e, const char *what) {
   if (e == hipSuccess) return TIS_OK;
   return fail(TIS_E_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -107,9 +118,15 @@ tis::RouteArgs route_args(const void *Q, const tis_tree *tree, const Geometry &g
 extern "C" {
 
 size_t tis_tree_summary_bytes(int batch, int kv_heads, int head_dim, int branching, int levels) {
+  return tis_tree_summary_bytes_as(batch, kv_heads, head_dim, branching, levels, TIS_F32);
+}
+
+size_t tis_tree_summary_bytes_as(int batch, int kv_heads, int head_dim, int branching, int levels,
+                                 tis_dtype summary_dtype) {
   if (batch < 1 || kv_heads < 1 || head_dim < 1 || branching < 2 || levels < 1 ||
-      levels > tis::kMaxLevels)
+      levels > tis::kMaxLevels || (summary_dtype != TIS_F32 && summary_dtype != TIS_BF16))
     return 0;
+  const size_t es = summary_elem_bytes(summary_dtype);
   int64_t n = 1, total = 0;
   for (int l = 1; l <= levels; ++l) {
     n *= branching;
@@ -118,8 +135,7 @@ size_t tis_tree_summary_bytes(int batch, int kv_heads, int head_dim, int branchi
   }
   const double bytes = 4.0 * head_dim * (double)batch * kv_heads * (double)total;
   if (bytes > 9.0e18) return 0;
-  return static_cast<size_t>(4) * head_dim * static_cast<size_t>(batch) * kv_heads *
-         static_cast<size_t>(total);
+  return es * head_dim * static_cast<size_t>(batch) * kv_heads * static_cast<size_t>(total);
 }
 
 size_t tis_build_workspace_bytes(int batch, int kv_heads, int n_keys, int head_dim,
@@ -144,6 +160,8 @@ tis_status tis_tree_build(const void *K, tis_dtype dtype, int batch, int kv_head
   if (!K || !tree || !tree->summaries)
     return fail(TIS_E_NULL, "tis_tree_build: K, tree and tree->summaries are required");
   tis_status st = check_dtype(dtype);
+  if (st != TIS_OK) return st;
+  st = check_summary_dtype("tis_tree_build", tree->summary_dtype);
   if (st != TIS_OK) return st;
   Geometry g;
   st = check_tree(batch, kv_heads, n_keys, head_dim, branching, leaf_block, levels, &g);
@@ -198,7 +216,8 @@ tis_status tis_tree_build(const void *K, tis_dtype dtype, int batch, int kv_head
     sum_off += heads * g.n_at[l] * head_dim;
   }
   const tis::Dt dt = dtype == TIS_BF16 ? tis::Dt::BF16 : tis::Dt::F32;
-  st = hip_status(tis::launch_build(dt, head_dim, heads, a, p, static_cast<hipStream_t>(stream)),
+  st = hip_status(tis::launch_build(dt, to_dt(tree->summary_dtype), head_dim, heads, a, p,
+                                    static_cast<hipStream_t>(stream)),
                   "tis_tree_build launch");
   if (st != TIS_OK) return st;
   tree->batch = batch;
@@ -216,6 +235,8 @@ tis_status tis_tree_route(const void *Q, tis_dtype dtype, int q_heads, const tis
   if (!Q || !tree || !tree->summaries || !indices)
     return fail(TIS_E_NULL, "tis_tree_route: Q, tree, tree->summaries and indices are required");
   tis_status st = check_dtype(dtype);
+  if (st != TIS_OK) return st;
+  st = check_summary_dtype("tis_tree_route", tree->summary_dtype);
   if (st != TIS_OK) return st;
   Geometry g;
   st = check_tree(tree->batch, tree->kv_heads, tree->n_keys, tree->head_dim, tree->branching,
@@ -238,7 +259,8 @@ tis_status tis_tree_route(const void *Q, tis_dtype dtype, int q_heads, const tis
 
   const tis::RouteArgs a = route_args(Q, tree, g, q_heads, beam, indices, trace, queries);
   const tis::Dt dt = dtype == TIS_BF16 ? tis::Dt::BF16 : tis::Dt::F32;
-  return hip_status(tis::launch_route(dt, tree->head_dim, a, static_cast<hipStream_t>(stream)),
+  return hip_status(tis::launch_route(dt, to_dt(tree->summary_dtype), tree->head_dim, a,
+                                     static_cast<hipStream_t>(stream)),
                     "tis_tree_route launch");
 }
 
@@ -333,6 +355,8 @@ tis_status tis_tree_decode(const void *Q, const void *K, const void *V, tis_dtyp
     return fail(TIS_E_NULL, "tis_tree_decode: Q, K, V, tree, tree->summaries and O are required");
   tis_status st = check_dtype(dtype);
   if (st != TIS_OK) return st;
+  st = check_summary_dtype("tis_tree_decode", tree->summary_dtype);
+  if (st != TIS_OK) return st;
   Geometry g;
   st = check_tree(tree->batch, tree->kv_heads, tree->n_keys, tree->head_dim, tree->branching,
                   tree->leaf_block, tree->levels, &g);
@@ -377,7 +401,8 @@ tis_status tis_tree_decode(const void *Q, const void *K, const void *V, tis_dtyp
                   workspace_bytes, &aa);
   if (st != TIS_OK) return st;
   const tis::Dt dt = dtype == TIS_BF16 ? tis::Dt::BF16 : tis::Dt::F32;
-  return hip_status(tis::launch_decode(dt, tree->head_dim, ra, aa, static_cast<hipStream_t>(stream)),
+  return hip_status(tis::launch_decode(dt, to_dt(tree->summary_dtype), tree->head_dim, ra, aa,
+                                      static_cast<hipStream_t>(stream)),
                     "tis_tree_decode launch");
 }
 
@@ -399,7 +424,7 @@ int cache_depth(int64_t n, int branching, int leaf_block) {
 struct CacheGeometry {
   int heights;          // H
   int64_t heads;
-  int64_t summ_elems;   // floats
+  int64_t summ_elems;   // summary elements
   int64_t state_elems;  // doubles
 };
 
@@ -436,6 +461,8 @@ tis_status check_cache_tree(const char *who, const tis_cache_tree *t, CacheGeome
     return fail(TIS_E_NULL, "%s: tree, tree->summaries and tree->state are required", who);
   tis_status st = check_cache(who, t->batch, t->kv_heads, t->head_dim, t->branching,
                               t->leaf_block, t->capacity, g);
+  if (st != TIS_OK) return st;
+  st = check_summary_dtype(who, t->summary_dtype);
   if (st != TIS_OK) return st;
   if (!aligned(t->summaries, 16) || !aligned(t->state, 16))
     return fail(TIS_E_ALIGN, "%s: summaries and state need 16-byte alignment", who);
@@ -520,11 +547,18 @@ tis_status check_cache_query(const char *who, const void *Q, tis_dtype dtype, in
 
 size_t tis_cache_tree_summary_bytes(int batch, int kv_heads, int head_dim, int branching,
                                     int leaf_block, int capacity) {
+  return tis_cache_tree_summary_bytes_as(batch, kv_heads, head_dim, branching, leaf_block,
+                                         capacity, TIS_F32);
+}
+
+size_t tis_cache_tree_summary_bytes_as(int batch, int kv_heads, int head_dim, int branching,
+                                       int leaf_block, int capacity, tis_dtype summary_dtype) {
   CacheGeometry g;
+  if (summary_dtype != TIS_F32 && summary_dtype != TIS_BF16) return 0;
   if (check_cache("tis_cache_tree_summary_bytes", batch, kv_heads, head_dim, branching,
                   leaf_block, capacity, &g) != TIS_OK)
     return 0;
-  return static_cast<size_t>(g.summ_elems) * sizeof(float);
+  return static_cast<size_t>(g.summ_elems) * summary_elem_bytes(summary_dtype);
 }
 
 size_t tis_cache_tree_state_bytes(int batch, int kv_heads, int head_dim, int branching,
@@ -543,6 +577,8 @@ tis_status tis_cache_tree_reset(tis_cache_tree *tree, void *stream) {
   tis_status st = check_cache("tis_cache_tree_reset", tree->batch, tree->kv_heads,
                               tree->head_dim, tree->branching, tree->leaf_block, tree->capacity,
                               &g);
+  if (st != TIS_OK) return st;
+  st = check_summary_dtype("tis_cache_tree_reset", tree->summary_dtype);
   if (st != TIS_OK) return st;
   if (!aligned(tree->summaries, 16) || !aligned(tree->state, 16))
     return fail(TIS_E_ALIGN, "tis_cache_tree_reset: summaries and state need 16-byte alignment");
@@ -595,7 +631,8 @@ tis_status tis_cache_tree_append(const void *K, tis_dtype dtype, int n_new, tis_
     }
   }
   const tis::Dt dt = dtype == TIS_BF16 ? tis::Dt::BF16 : tis::Dt::F32;
-  st = hip_status(tis::launch_cache_append(dt, tree->head_dim, a, static_cast<hipStream_t>(stream)),
+  st = hip_status(tis::launch_cache_append(dt, to_dt(tree->summary_dtype), tree->head_dim, a,
+                                           static_cast<hipStream_t>(stream)),
                   "tis_cache_tree_append launch");
   if (st != TIS_OK) return st;
   tree->n_keys += n_new;
@@ -616,7 +653,8 @@ tis_status tis_cache_tree_route(const void *Q, tis_dtype dtype, int q_heads,
     return fail(TIS_E_ALIGN, "tis_cache_tree_route: indices and trace need 4-byte alignment");
   const tis::RouteArgs a = cache_route_args(Q, tree, q_heads, beam, indices, trace, queries);
   const tis::Dt dt = dtype == TIS_BF16 ? tis::Dt::BF16 : tis::Dt::F32;
-  return hip_status(tis::launch_route(dt, tree->head_dim, a, static_cast<hipStream_t>(stream)),
+  return hip_status(tis::launch_route(dt, to_dt(tree->summary_dtype), tree->head_dim, a,
+                                     static_cast<hipStream_t>(stream)),
                     "tis_cache_tree_route launch");
 }
 
@@ -658,7 +696,8 @@ tis_status tis_cache_tree_decode(const void *Q, const void *K, const void *V, ti
                   workspace, workspace_bytes, &aa);
   if (st != TIS_OK) return st;
   const tis::Dt dt = dtype == TIS_BF16 ? tis::Dt::BF16 : tis::Dt::F32;
-  return hip_status(tis::launch_decode(dt, tree->head_dim, ra, aa, static_cast<hipStream_t>(stream)),
+  return hip_status(tis::launch_decode(dt, to_dt(tree->summary_dtype), tree->head_dim, ra, aa,
+                                      static_cast<hipStream_t>(stream)),
                     "tis_cache_tree_decode launch");
 }
 

@@ -38,6 +38,44 @@ template <> struct Vec16<bf16_bits> {
   }
 };
 
+// ---- stored summaries --------------------------------------------------
+// A summary is the fp64 mean of a node's keys rounded once to its storage
+// type: float32 (hardware conversion, round to nearest even) or bfloat16.
+// The bfloat16 rounding works on the fp64 bits so that it is one rounding
+// (through float32 it would be two, which can differ at a float32 value that
+// sits exactly halfway between two bfloat16 values).  In the normal bfloat16
+// range, rounding the 52-bit fraction to 7 bits to nearest even is adding
+// 2^44 - 1 plus the lowest kept bit and dropping 45 bits; a carry out of the
+// fraction steps the exponent, which is the right result, including the step
+// past the largest bfloat16 to infinity.  Below 2^-126 the bfloat16 grid is
+// the fixed spacing 2^-133: the value is scaled onto it (exactly, a power of
+// two) and rounded by rint, which rounds halves to even.
+__device__ inline uint16_t bf16_from_double(double x) {
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(x));
+  const uint32_t sign = static_cast<uint32_t>(u >> 48) & 0x8000u;
+  const uint64_t a = u & 0x7fffffffffffffffull;
+  const uint32_t e = static_cast<uint32_t>(a >> 52);  // biased fp64 exponent
+  if (e >= 1023u - 126u) {
+    const uint64_t r = (a + 0x00000fffffffffffull + ((a >> 45) & 1ull)) >> 45;  // exp | 7 bits
+    const uint32_t be = static_cast<uint32_t>(r >> 7);                         // fp64-biased
+    if (be >= 1023u + 128u) return static_cast<uint16_t>(sign | 0x7f80u);     // overflow
+    return static_cast<uint16_t>(sign | ((be - (1023u - 127u)) << 7) |
+                                 static_cast<uint32_t>(r & 0x7fu));
+  }
+  const double m = __builtin_rint(__longlong_as_double(static_cast<long long>(a)) * 0x1p133);
+  return static_cast<uint16_t>(sign | static_cast<uint32_t>(m));  // m <= 128 (128: 2^-126)
+}
+
+template <typename S> struct SummaryType;
+template <> struct SummaryType<float> {
+  __device__ static inline float from_mean(double m) { return static_cast<float>(m); }
+  __device__ static inline void put(float *p, double m) { *p = static_cast<float>(m); }
+};
+template <> struct SummaryType<bf16_bits> {
+  __device__ static inline bf16_bits from_mean(double m) { return bf16_bits{bf16_from_double(m)}; }
+  __device__ static inline void put(bf16_bits *p, double m) { p->v = bf16_from_double(m); }
+};
+
 __device__ inline uint4 load16(const void *p) {
   return *reinterpret_cast<const uint4 *>(p);
 }

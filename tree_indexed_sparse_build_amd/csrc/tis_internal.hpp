@@ -26,7 +26,7 @@ constexpr size_t kStreamLoadBytes = 384u << 20;  // K larger than this: streamin
 
 struct BuildArgs {
   const void *K;
-  float *summ;
+  void *summ;            // float or bf16 bits (the summary type)
   double *ws_sum;        // fp64 node sums of levels 2..r
   int64_t n_keys;        // N
   int64_t chunks;        // b^r chunks per head
@@ -57,7 +57,8 @@ struct BuildPlan {
 
 bool plan_build(int64_t heads, int head_dim, int branching, int leaf_block, int levels,
                 BuildPlan *plan);
-hipError_t launch_build(Dt dt, int head_dim, int64_t heads, const BuildArgs &a,
+// dt: type of K; sdt: type the summaries are stored in
+hipError_t launch_build(Dt dt, Dt sdt, int head_dim, int64_t heads, const BuildArgs &a,
                         const BuildPlan &p, hipStream_t s);
 
 // ---------------------------------------------------------------- route --
@@ -70,7 +71,7 @@ hipError_t launch_build(Dt dt, int head_dim, int64_t heads, const BuildArgs &a,
 //    when n * L * b^(levels-l) < n_keys.
 struct RouteArgs {
   const void *Q;
-  const float *summ;
+  const void *summ;      // float or bf16 bits (the summary type)
   int32_t *indices;
   int32_t *trace;        // may be null
   int queries;           // B * Hq (< 2^31, checked by the host)
@@ -86,7 +87,7 @@ struct RouteArgs {
   int64_t lvl_off[kMaxLevels + 1];
 };
 
-hipError_t launch_route(Dt dt, int head_dim, const RouteArgs &a, hipStream_t s);
+hipError_t launch_route(Dt dt, Dt sdt, int head_dim, const RouteArgs &a, hipStream_t s);
 
 // --------------------------------------------------------------- attend --
 // One workgroup per query: its waves split the selected leaf blocks into
@@ -118,8 +119,8 @@ hipError_t launch_combine(int head_dim, const AttendArgs &a, hipStream_t s);
 
 // ---------------------------------------------------------------- decode --
 // Route and attend of each query in one workgroup (one launch).
-hipError_t launch_decode(Dt dt, int head_dim, const RouteArgs &ra, const AttendArgs &aa,
-                         hipStream_t s);
+hipError_t launch_decode(Dt dt, Dt sdt, int head_dim, const RouteArgs &ra,
+                         const AttendArgs &aa, hipStream_t s);
 
 // ------------------------------------------------------- growing cache --
 // Append keys [n0, n1) of a cache of `capacity` keys per head to its tree:
@@ -127,7 +128,7 @@ hipError_t launch_decode(Dt dt, int head_dim, const RouteArgs &ra, const AttendA
 // b^h))][d]), state fp64 [heads][heights][d] open-node sums.
 struct AppendArgs {
   const void *K;
-  float *summ;
+  void *summ;            // float or bf16 bits (the summary type)
   double *state;
   int64_t heads;         // B * Hkv
   int64_t capacity;
@@ -142,7 +143,7 @@ struct AppendArgs {
 };
 
 hipError_t launch_cache_reset(double *state, int64_t elems, hipStream_t s);
-hipError_t launch_cache_append(Dt dt, int head_dim, const AppendArgs &a, hipStream_t s);
+hipError_t launch_cache_append(Dt dt, Dt sdt, int head_dim, const AppendArgs &a, hipStream_t s);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

@@ -36,6 +36,17 @@ def _need_device(*ts: torch.Tensor) -> None:
             raise ValueError("tensors must be contiguous")
 
 
+# stored summary types: name -> (tis_dtype code, torch dtype)
+SUMMARY_DTYPES = {"f32": (0, torch.float32), "bf16": (1, torch.bfloat16)}
+
+
+def _summary_dtype(name: str):
+    try:
+        return SUMMARY_DTYPES[name]
+    except KeyError:
+        raise ValueError(f"summary_dtype must be one of {sorted(SUMMARY_DTYPES)}") from None
+
+
 def _check_buffer(t: torch.Tensor, shape, dtype: torch.dtype, name: str) -> None:
     """A caller-supplied output must be exactly what the kernel writes."""
     if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
@@ -63,8 +74,9 @@ def _workspace(device: torch.device, kind: str, nbytes: int) -> torch.Tensor:
 
 @dataclasses.dataclass
 class Tree:
-    """A built tree: fp32 summaries, level-major ([B, Hkv, n_l, d] blocks for
-    l = 1..levels, concatenated), plus its geometry."""
+    """A built tree: summaries (float32, or bfloat16 with summary_dtype
+    "bf16"), level-major ([B, Hkv, n_l, d] blocks for l = 1..levels,
+    concatenated), plus its geometry."""
     summaries: torch.Tensor
     batch: int
     kv_heads: int
@@ -73,10 +85,12 @@ class Tree:
     branching: int
     leaf_block: int
     levels: int
+    summary_dtype: str = "f32"
 
     def c_struct(self) -> TisTree:
         return TisTree(self.batch, self.kv_heads, self.n_keys, self.head_dim, self.branching,
-                       self.leaf_block, self.levels, self.summaries.data_ptr())
+                       self.leaf_block, self.levels, _summary_dtype(self.summary_dtype)[0],
+                       self.summaries.data_ptr())
 
     def level(self, l: int) -> torch.Tensor:
         """Summaries of level l (1..levels) as a [B, Hkv, b**l, d] view."""
@@ -96,25 +110,28 @@ def summary_offsets(batch, kv_heads, head_dim, branching, levels):
     return out
 
 
-def tree_build(K: torch.Tensor, branching: int, leaf_block: int, levels: int) -> Tree:
-    """Summaries of every node: K [B, Hkv, N, d] with N = branching**levels * leaf_block."""
+def tree_build(K: torch.Tensor, branching: int, leaf_block: int, levels: int,
+               summary_dtype: str = "f32") -> Tree:
+    """Summaries of every node: K [B, Hkv, N, d] with N = branching**levels * leaf_block;
+    summary_dtype "f32" or "bf16" (each mean rounded once to that type)."""
     _need_device(K)
     if K.dim() != 4:
         raise ValueError("K must be [B, Hkv, N, d]")
     B, H, N, d = K.shape
+    code, tdt = _summary_dtype(summary_dtype)
     L = lib()
-    nbytes = L.tis_tree_summary_bytes(B, H, d, branching, levels)
+    nbytes = L.tis_tree_summary_bytes_as(B, H, d, branching, levels, code)
     if nbytes == 0:
         raise _lib.TisError(_lib.TIS_E_SHAPE, "invalid tree geometry")
-    summ = torch.empty(nbytes // 4, dtype=torch.float32, device=K.device)
+    summ = torch.empty(nbytes // tdt.itemsize, dtype=tdt, device=K.device)
     wsb = L.tis_build_workspace_bytes(B, H, N, d, branching, leaf_block, levels)
     ws = _workspace(K.device, "build", wsb) if wsb else None
-    t = TisTree(0, 0, 0, 0, 0, 0, 0, summ.data_ptr())
+    t = TisTree(0, 0, 0, 0, 0, 0, 0, code, summ.data_ptr())
     check(L.tis_tree_build(K.data_ptr(), _dtype_code(K), B, H, N, d, branching, leaf_block,
                            levels, ctypes.byref(t), ws.data_ptr() if ws is not None else None,
                            ws.numel() if ws is not None else 0, _stream(K.device)))
     return Tree(summ, t.batch, t.kv_heads, t.n_keys, t.head_dim, t.branching, t.leaf_block,
-                t.levels)
+                t.levels, summary_dtype)
 
 
 def tree_route(Q: torch.Tensor, tree: Tree, beam: int, trace: bool = False):
@@ -227,7 +244,8 @@ class DecodePlan:
     so a step can be captured into a graph and replayed."""
 
     def __init__(self, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, branching: int,
-                 leaf_block: int, levels: int, beam: int, scale: Optional[float] = None):
+                 leaf_block: int, levels: int, beam: int, scale: Optional[float] = None,
+                 summary_dtype: str = "f32"):
         _need_device(Q, K, V)
         L = lib()
         self._lib = L
@@ -237,10 +255,12 @@ class DecodePlan:
         self.dt = _dtype_code(K)
         self.geom = (B, H, N, d, branching, leaf_block, levels)
         self.q_heads, self.beam, self.scale = Hq, beam, 0.0 if scale is None else float(scale)
-        nbytes = L.tis_tree_summary_bytes(B, H, d, branching, levels)
+        code, tdt = _summary_dtype(summary_dtype)
+        self.summary_dtype = summary_dtype
+        nbytes = L.tis_tree_summary_bytes_as(B, H, d, branching, levels, code)
         if nbytes == 0:
             raise _lib.TisError(_lib.TIS_E_SHAPE, "invalid tree geometry")
-        self.summaries = torch.empty(nbytes // 4, dtype=torch.float32, device=K.device)
+        self.summaries = torch.empty(nbytes // tdt.itemsize, dtype=tdt, device=K.device)
         wsb = L.tis_build_workspace_bytes(*self.geom)
         self.ws_build = (torch.empty(wsb, dtype=torch.uint8, device=K.device) if wsb
                          else None)
@@ -252,7 +272,7 @@ class DecodePlan:
                           else None)
         self.indices = torch.empty((B, Hq, beam), dtype=torch.int32, device=K.device)
         self.out = torch.empty((B, Hq, d), dtype=torch.float32, device=K.device)
-        self.tree_c = TisTree(0, 0, 0, 0, 0, 0, 0, self.summaries.data_ptr())
+        self.tree_c = TisTree(0, 0, 0, 0, 0, 0, 0, code, self.summaries.data_ptr())
         self.device = K.device
 
     def build(self) -> None:
@@ -304,7 +324,8 @@ class CacheTree:
     the current tree is height levels - l.
     """
 
-    def __init__(self, K: torch.Tensor, V: torch.Tensor, branching: int, leaf_block: int):
+    def __init__(self, K: torch.Tensor, V: torch.Tensor, branching: int, leaf_block: int,
+                 summary_dtype: str = "f32"):
         _need_device(K, V)
         if V.shape != K.shape or V.dtype != K.dtype:
             raise ValueError("K and V must match")
@@ -312,13 +333,15 @@ class CacheTree:
         L = lib()
         self.K, self.V = K, V
         self.dt = _dtype_code(K)
-        sb = L.tis_cache_tree_summary_bytes(B, H, d, branching, leaf_block, C)
+        code, tdt = _summary_dtype(summary_dtype)
+        self.summary_dtype = summary_dtype
+        sb = L.tis_cache_tree_summary_bytes_as(B, H, d, branching, leaf_block, C, code)
         stb = L.tis_cache_tree_state_bytes(B, H, d, branching, leaf_block, C)
         if sb == 0 or stb == 0:
             raise _lib.TisError(_lib.TIS_E_SHAPE, "invalid cache geometry")
-        self.summaries = torch.empty(sb // 4, dtype=torch.float32, device=K.device)
+        self.summaries = torch.empty(sb // tdt.itemsize, dtype=tdt, device=K.device)
         self.state = torch.empty(stb // 8, dtype=torch.float64, device=K.device)
-        self.c = TisCacheTree(B, H, d, branching, leaf_block, C, 0, 0,
+        self.c = TisCacheTree(B, H, d, branching, leaf_block, C, 0, 0, code,
                               self.summaries.data_ptr(), self.state.data_ptr())
         self._cref = ctypes.byref(self.c)
         self._kptr = K.data_ptr()
