@@ -194,6 +194,77 @@ tis_status tis_tree_decode(const void *Q, const void *K, const void *V, tis_dtyp
 size_t tis_decode_workspace_bytes(int batch, int q_heads, int head_dim, int beam,
                                   int leaf_block);
 
+/* ------------------------------------------------------------------------
+ * Threshold retrieval with bounding spheres
+ *
+ * The Louver explainer ("Sparse Attention as a Range Searching Problem",
+ * Methodologie) retrieves every key whose score q.k reaches a threshold tau,
+ * pruning clusters whose bounding sphere cannot reach tau, which never loses
+ * such a key.  Here the clusters are the nodes of a built tree:
+ *   - centre of a node: its stored summary; radius: the smallest float32 r
+ *     with r * r >= the largest squared distance (evaluated in fp64) from
+ *     the centre to a key under the node, so every key lies in the sphere;
+ *   - a node survives when q.c + |q| r >= tau (fp64; |q| from the fp64 sum of
+ *     squares), the largest score any point of its sphere can have;
+ *   - level 1 scores the root's children, level l the children of the
+ *     level-(l-1) survivors; a level may keep at most max_nodes survivors,
+ *     more is an overflow;
+ *   - attention: exact softmax over the keys of the surviving leaves whose
+ *     fp64 score q.k is >= tau.  As no such key is pruned, this is softmax
+ *     over every key of the cache with q.k >= tau.
+ * Radii are float32, level-major with one element per node: for l = 1..lv
+ * a block [B][Hkv][n_l] starting at node offset B*Hkv*(n_1+...+n_{l-1}).
+ * --------------------------------------------------------------------- */
+
+/* Survivors one level may keep (max_nodes). */
+#define TIS_MAX_SURVIVORS 2048
+
+/* Bytes of the radii of a tree: 4 * B * Hkv * (n_1 + ... + n_lv) (0 if
+ * invalid), and of the workspace tis_tree_radii needs (8 bytes a node). */
+size_t tis_tree_radius_bytes(int batch, int kv_heads, int branching, int levels);
+size_t tis_radius_workspace_bytes(int batch, int kv_heads, int branching, int levels);
+
+/*
+ * tis_tree_radii -- radius of every node of a built tree about its stored
+ * summary (either summary type).  K as given to tis_tree_build (read once).
+ * radii out: float32, layout above.  workspace: tis_radius_workspace_bytes()
+ * bytes, 16-byte aligned (fp64 maxima; contents on entry never matter).
+ */
+tis_status tis_tree_radii(const void *K, tis_dtype dtype, const tis_tree *tree, float *radii,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * tis_tree_route_threshold -- the surviving leaves of every query.
+ * Q [B][Hq][d] of type dtype; radii from tis_tree_radii for this tree;
+ * tau float32 [B][Hq] (any value, infinities included).
+ * indices out: int32 [B][Hq][max_nodes], the surviving leaves ascending,
+ *          padded with -1 (all -1 after an overflow).
+ * counts   optional: int32 [B][Hq], the number of surviving leaves, or -1
+ *          when some level had more than max_nodes survivors.
+ * Requires 1 <= max_nodes <= TIS_MAX_SURVIVORS.
+ */
+tis_status tis_tree_route_threshold(const void *Q, tis_dtype dtype, int q_heads,
+                                    const tis_tree *tree, const float *radii, const float *tau,
+                                    int max_nodes, int32_t *indices, int32_t *counts,
+                                    void *stream);
+
+/* Bytes of workspace tis_tree_decode_threshold needs (0: none). */
+size_t tis_decode_threshold_workspace_bytes(int batch, int q_heads, int head_dim, int max_nodes,
+                                            int leaf_block);
+
+/*
+ * tis_tree_decode_threshold -- the route above and the attention over the
+ * surviving leaves in one launch.  O out: float32 [B][Hq][d], softmax over
+ * the keys with fp64 q.k >= tau (a zero row when there is none, NaN after an
+ * overflow); scale as for tis_tree_decode.  indices and counts optional, as
+ * for tis_tree_route_threshold.
+ */
+tis_status tis_tree_decode_threshold(const void *Q, const void *K, const void *V, tis_dtype dtype,
+                                     int q_heads, const tis_tree *tree, const float *radii,
+                                     const float *tau, int max_nodes, float scale, float *O,
+                                     int32_t *indices, int32_t *counts, void *workspace,
+                                     size_t workspace_bytes, void *stream);
+
 /* Message for the last non-OK status returned on the calling thread. */
 const char *tis_last_error(void);
 

@@ -342,3 +342,84 @@ def test_caller_buffers_must_match():
         ops._check_buffer(torch.empty(2, 3, 4), (2, 3, 8), torch.float32, "out")
     with pytest.raises(ValueError, match="int32"):
         ops._check_buffer(torch.empty(2, 3, 4), (2, 3, 4), torch.int32, "indices")
+
+
+# ----------------------------------------------------- bounding spheres --
+
+def test_radius_bytes(lib):
+    # 4 x 8 heads, b 8, 3 levels: 8 + 64 + 512 nodes each
+    assert lib.tis_tree_radius_bytes(4, 8, 8, 3) == 4 * 32 * 584
+    assert lib.tis_radius_workspace_bytes(4, 8, 8, 3) == 8 * 32 * 584
+    assert lib.tis_tree_radius_bytes(1, 1, 1, 3) == 0
+    assert lib.tis_radius_workspace_bytes(1, 1, 2, 17) == 0
+    assert lib.tis_decode_threshold_workspace_bytes(4, 32, 128, 8, 64) == 0
+
+
+def _radii(lib, **kw):
+    a = dict(K=FAKE, dt=_lib.TIS_BF16, tree=_tree(), radii=FAKE, ws=FAKE, wsb=1 << 20)
+    a.update(kw)
+    return lib.tis_tree_radii(a["K"], a["dt"], ctypes.byref(a["tree"]), a["radii"], a["ws"],
+                              a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=None), _lib.TIS_E_NULL),
+    (dict(radii=None), _lib.TIS_E_NULL),
+    (dict(ws=None), _lib.TIS_E_NULL),
+    (dict(tree=_tree(summ=None)), _lib.TIS_E_NULL),
+    (dict(dt=4), _lib.TIS_E_DTYPE),
+    (dict(tree=_tree(sd=7)), _lib.TIS_E_DTYPE),
+    (dict(tree=_lib.TisTree(1, 1, 100, 64, 2, 16, 3, 0, FAKE)), _lib.TIS_E_SHAPE),
+    (dict(wsb=8 * 14 - 1), _lib.TIS_E_WORKSPACE),      # 2 + 4 + 8 nodes need 112 bytes
+    (dict(radii=FAKE + 2), _lib.TIS_E_ALIGN),
+    (dict(ws=FAKE + 8), _lib.TIS_E_ALIGN),
+])
+def test_radii_rejects(lib, kw, status):
+    assert _radii(lib, **kw) == status
+    assert lib.tis_last_error().decode()
+
+
+def _threshold(lib, fused, **kw):
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, dt=_lib.TIS_BF16, Hq=2, tree=_tree(H=1), radii=FAKE,
+             tau=FAKE, nodes=8, idx=FAKE, cnt=FAKE, O=FAKE, scale=0.0, ws=None, wsb=0)
+    a.update(kw)
+    if not fused:
+        return lib.tis_tree_route_threshold(a["Q"], a["dt"], a["Hq"], ctypes.byref(a["tree"]),
+                                            a["radii"], a["tau"], a["nodes"], a["idx"], a["cnt"],
+                                            None)
+    return lib.tis_tree_decode_threshold(a["Q"], a["K"], a["V"], a["dt"], a["Hq"],
+                                         ctypes.byref(a["tree"]), a["radii"], a["tau"],
+                                         a["nodes"], a["scale"], a["O"], a["idx"], a["cnt"],
+                                         a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("kw,status", [
+    (dict(Q=None), _lib.TIS_E_NULL),
+    (dict(radii=None), _lib.TIS_E_NULL),
+    (dict(tau=None), _lib.TIS_E_NULL),
+    (dict(tree=_tree(summ=None)), _lib.TIS_E_NULL),
+    (dict(dt=3), _lib.TIS_E_DTYPE),
+    (dict(tree=_tree(sd=9)), _lib.TIS_E_DTYPE),
+    (dict(Hq=0), _lib.TIS_E_SHAPE),
+    (dict(tree=_tree(H=2), Hq=3), _lib.TIS_E_SHAPE),
+    (dict(nodes=0), _lib.TIS_E_SHAPE),
+    (dict(nodes=_lib.TIS_MAX_SURVIVORS + 1), _lib.TIS_E_UNSUPPORTED),
+    (dict(tau=FAKE + 2), _lib.TIS_E_ALIGN),
+    (dict(radii=FAKE + 1), _lib.TIS_E_ALIGN),
+    (dict(Q=FAKE + 8), _lib.TIS_E_ALIGN),
+    (dict(cnt=FAKE + 2), _lib.TIS_E_ALIGN),
+])
+def test_threshold_rejects(lib, fused, kw, status):
+    assert _threshold(lib, fused, **kw) == status
+    assert lib.tis_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=None), _lib.TIS_E_NULL),
+    (dict(O=None), _lib.TIS_E_NULL),
+    (dict(scale=float("inf")), _lib.TIS_E_SHAPE),
+    (dict(V=FAKE + 4), _lib.TIS_E_ALIGN),
+])
+def test_decode_threshold_rejects(lib, kw, status):
+    assert _threshold(lib, True, **kw) == status

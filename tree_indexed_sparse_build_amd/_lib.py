@@ -23,6 +23,8 @@ STATUS_NAMES = {
     TIS_E_HIP: "TIS_E_HIP",
 }
 
+TIS_MAX_SURVIVORS = 2048
+
 
 class TisTree(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("kv_heads", ctypes.c_int32),
@@ -74,6 +76,15 @@ SIGNATURES = {
     "tis_cache_tree_decode": (_c_int, [_vp, _vp, _vp, _c_int, _c_int,
                                        ctypes.POINTER(TisCacheTree), _c_int, _c_float, _vp, _vp,
                                        _vp, _c_size, _vp]),
+    "tis_tree_radius_bytes": (_c_size, [_c_int] * 4),
+    "tis_radius_workspace_bytes": (_c_size, [_c_int] * 4),
+    "tis_tree_radii": (_c_int, [_vp, _c_int, ctypes.POINTER(TisTree), _vp, _vp, _c_size, _vp]),
+    "tis_tree_route_threshold": (_c_int, [_vp, _c_int, _c_int, ctypes.POINTER(TisTree), _vp, _vp,
+                                          _c_int, _vp, _vp, _vp]),
+    "tis_decode_threshold_workspace_bytes": (_c_size, [_c_int] * 5),
+    "tis_tree_decode_threshold": (_c_int, [_vp, _vp, _vp, _c_int, _c_int,
+                                           ctypes.POINTER(TisTree), _vp, _vp, _c_int, _c_float,
+                                           _vp, _vp, _vp, _vp, _c_size, _vp]),
     "tis_last_error": (ctypes.c_char_p, []),
     "tis_version": (ctypes.c_char_p, []),
 }

@@ -46,14 +46,16 @@ template <typename T, int D> __device__ inline uint4 attend_q_raw(const AttendAr
 // Attention of query qi over the leaf blocks slots[s] (s < nslots) whose
 // use[s] is nonzero (use == nullptr: all), every wave of the workgroup
 // taking part (RAGGED: the last block of a growing cache may hold fewer
-// than L keys).  With part == nullptr it writes row qi of O (NaN if `bad`,
+// than L keys; THRESH: only keys whose score q.k, computed in fp64, is at
+// least tau take part, and that fp64 score is also the one the softmax
+// uses).  With part == nullptr it writes row qi of O (NaN if `bad`,
 // zero if no slot is used); otherwise it writes the workgroup's partial
 // softmax state to part: m (log2 units), l (NaN if `bad`), two pad words,
 // acc[D], for a later log-sum-exp merge with the query's other parts.
-template <typename T, int D, bool RAGGED = false>
+template <typename T, int D, bool RAGGED = false, bool THRESH = false>
 __device__ void attend_query(const AttendArgs &a, AttendShared<T, D> &sh, int qi,
                              uint4 qraw, const int *slots, const int *use, int nslots,
-                             bool bad, float *part) {
+                             bool bad, float *part, double tau = 0.0) {
   using AG = AttendGeom<T, D>;
   constexpr int E = AG::E, LPR = AG::LPR, R = AG::R, U = AG::U, RB = AG::RB, REP = AG::REP;
   const int tid = threadIdx.x;
@@ -99,26 +101,48 @@ __device__ void attend_query(const AttendArgs &a, AttendShared<T, D> &sh, int qi
       const int row = r0 + i * R + rsub;
       vv[i] = row < len ? load16(vh + (rowb + i * R + rsub) * D) : make_uint4(0u, 0u, 0u, 0u);
     }
-    float part[U];
+    float sc;
+    bool pass = true;
+    if constexpr (THRESH) {
+      // fp32 x fp32 (or bf16) products are exact in fp64
+      double part[U];
 #pragma unroll
-    for (int i = 0; i < U; ++i) {
-      float k[E];
-      Vec16<T>::unpack(kv[i], k);
-      float dot = 0.f;
+      for (int i = 0; i < U; ++i) {
+        float k[E];
+        Vec16<T>::unpack(kv[i], k);
+        double dot = 0.0;
 #pragma unroll
-      for (int e = 0; e < E; ++e) dot = fmaf(q[e], k[e], dot);
-      part[i] = dot;
+        for (int e = 0; e < E; ++e)
+          dot = fma(static_cast<double>(q[e]), static_cast<double>(k[e]), dot);
+        part[i] = dot;
+      }
+      const double s64 = group_transpose_reduce<U, LPR>(part, lane);
+      pass = s64 >= tau;
+      sc = static_cast<float>(s64);
+    } else {
+      float part[U];
+#pragma unroll
+      for (int i = 0; i < U; ++i) {
+        float k[E];
+        Vec16<T>::unpack(kv[i], k);
+        float dot = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) dot = fmaf(q[e], k[e], dot);
+        part[i] = dot;
+      }
+      sc = group_transpose_reduce<U, LPR>(part, lane);
     }
     // lane holds the score of row r0 + kk * R + rsub
-    const float sc = group_transpose_reduce<U, LPR>(part, lane);
     const int kk = (lane % LPR) / REP;
-    const bool valid = r0 + kk * R + rsub < len;
+    const bool valid = r0 + kk * R + rsub < len && pass;
     const float x = valid ? sc * a.scale_log2 : -INFINITY;
     const float mnew = fmaxf(m, wave_max(x));
     // hardware 2^x: results below 2^-126 flush to zero, which leaves the
     // weights of everything that contributes at fp32 precision unchanged
     const float p = valid ? __builtin_amdgcn_exp2f(x - mnew) : 0.f;
-    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+    // (a threshold can mask every row seen so far: m = mnew = -inf, no rescale)
+    const float alpha =
+        THRESH && mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - mnew);
     l = l * alpha + wave_sum((lane % REP) == 0 ? p : 0.f);
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] *= alpha;

@@ -133,10 +133,10 @@ __global__ void __launch_bounds__(256) k_fill_zero(double *p, int64_t n) {
 
 }  // namespace
 
-hipError_t launch_cache_reset(double *state, int64_t elems, hipStream_t s) {
+hipError_t launch_fill_zero(double *p, int64_t elems, hipStream_t s) {
   if (elems <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>((elems + 255) / 256));
-  hipLaunchKernelGGL(k_fill_zero, grid, dim3(256), 0, s, state, elems);
+  hipLaunchKernelGGL(k_fill_zero, grid, dim3(256), 0, s, p, elems);
   return hipGetLastError();
 }
 

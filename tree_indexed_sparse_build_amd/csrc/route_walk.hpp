@@ -158,16 +158,16 @@ template <int NT> __device__ inline void write_ascending(const int *v, int n, in
   }
 }
 
-// Scores the C candidates of one level: candidate p is node p of the level
-// (all) or node cand[p] (-1: a hole), and its key goes to keys[p].  The nsw waves of the
-// workgroup cover UU rows per lane per pass, UU just large enough for C, and
-// every load of a pass is issued before any is used: rows past C read
+// Scores the C candidates of one level: candidate p is node node_of(p) of
+// the level (negative: a hole, which reads node 0), and emit(p, node, score)
+// receives its fp64 dot with the query (once per candidate).  The nsw waves
+// of the workgroup cover UU rows per lane per pass, UU just large enough for
+// C, and every load of a pass is issued before any is used: rows past C read
 // candidate 0 again (always a valid address) and their scores are dropped,
 // so no branch splits the loads.  A lane loads 16 bytes of a row: 4 float32
 // or 8 bfloat16 summary elements.
-template <typename T, typename S, int D, int UU, bool HOLES>
-__device__ inline void score_rows(const S *sl, int C, bool all, const int *cand,
-                                  uint64_t *keys, int bits,
+template <typename T, typename S, int D, int UU, bool HOLES, typename NodeOf, typename Emit>
+__device__ inline void score_rows(const S *sl, int C, NodeOf node_of, Emit emit,
                                   const QRaw<T, Vec16<S>::kElems> &qr, int nsw, int w,
                                   int lane) {
   constexpr int E = Vec16<S>::kElems;
@@ -182,8 +182,7 @@ __device__ inline void score_rows(const S *sl, int C, bool all, const int *cand,
 #pragma unroll
     for (int u = 0; u < UU; ++u) {
       const int pos = base + (u * nsw + w) * RPI + rsub;
-      const int pc = pos < C ? pos : 0;
-      node[u] = all ? pc : cand[pc];
+      node[u] = node_of(pos < C ? pos : 0);
     }
     uint4 v[UU];
 #pragma unroll
@@ -207,12 +206,7 @@ __device__ inline void score_rows(const S *sl, int C, bool all, const int *cand,
     const double s = group_transpose_reduce<UU, LPR>(part, lane);
     const int k = (lane % LPR) / REP;
     const int pos = base + (k * nsw + w) * RPI + rsub;
-    if ((lane % REP) == 0 && pos < C) {
-      const int nd = all ? pos : cand[pos];
-      // a hole (a child past the end of a growing cache) gets key 0, below
-      // every real key, so it is never ranked among the kept
-      keys[pos] = HOLES && nd < 0 ? 0ull : score_key(s, nd, bits);
-    }
+    if ((lane % REP) == 0 && pos < C) emit(pos, node_of(pos), s);
   }
 }
 
@@ -306,15 +300,22 @@ __device__ int route_walk(const RouteArgs &a, RouteShared<NW> &sh, int qi) {
       // the walking waves score, each lane taking `per` rows
       const int per = (C + NRW * RPI - 1) / (NRW * RPI);
       const int *cand = sh.cand[cur];
+      const auto node_of = [&](int p) { return all ? p : cand[p]; };
+      uint64_t *keys = sh.keys;
+      const auto emit = [&](int pos, int nd, double s) {
+        // a hole (a child past the end of a growing cache) gets key 0, below
+        // every real key, so it is never ranked among the kept
+        keys[pos] = CACHE && nd < 0 ? 0ull : score_key(s, nd, bits);
+      };
       if (w < NRW) {
         if (per <= 1)
-          score_rows<T, S, D, 1, CACHE>(sl, C, all, cand, sh.keys, bits, qr, NRW, w, lane);
+          score_rows<T, S, D, 1, CACHE>(sl, C, node_of, emit, qr, NRW, w, lane);
         else if (per <= 2)
-          score_rows<T, S, D, 2, CACHE>(sl, C, all, cand, sh.keys, bits, qr, NRW, w, lane);
+          score_rows<T, S, D, 2, CACHE>(sl, C, node_of, emit, qr, NRW, w, lane);
         else if (per <= 4)
-          score_rows<T, S, D, 4, CACHE>(sl, C, all, cand, sh.keys, bits, qr, NRW, w, lane);
+          score_rows<T, S, D, 4, CACHE>(sl, C, node_of, emit, qr, NRW, w, lane);
         else
-          score_rows<T, S, D, 8, CACHE>(sl, C, all, cand, sh.keys, bits, qr, NRW, w, lane);
+          score_rows<T, S, D, 8, CACHE>(sl, C, node_of, emit, qr, NRW, w, lane);
       }
       __syncthreads();
       // rank of candidate i = number of candidates with a larger key.  Each

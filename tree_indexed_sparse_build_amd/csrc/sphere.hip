@@ -1,0 +1,396 @@
+// Threshold retrieval over the summary tree with bounding spheres ("Sparse
+// Attention as a Range Searching Problem", Methodologie: every key whose
+// score reaches a threshold is retrieved; clusters enclosed by bounding
+// spheres are pruned when the sphere cannot reach the threshold, so no such
+// key is ever lost; survivors are checked exactly).  The clusters are the
+// nodes of the summary tree ("Subquadratic Attention with a Hierarchical
+// Tree-Structured Indexer", Abstract), so pruning runs level by level.
+//
+//  * k_radius: for every key, its squared distance (fp64) to the stored
+//    summary of each of its lv ancestors; the largest per node is reduced
+//    with 64-bit atomic max on the ordered fp64 bits.  A wave owns a run of
+//    consecutive leaves of one head and keeps, per level, the running
+//    maximum of the node its leaves are under (one lane per level), so it
+//    issues one atomic per node it touches.  K is streamed once, 8 rows per
+//    lane in flight; the ancestors' summaries go through LDS.
+//  * k_radius_finish: radius = smallest float32 r with r * r >= the maximum
+//    (r * r is exact in fp64, so the test is exact).
+//  * threshold walk: one workgroup per query; level by level, the children
+//    of the survivors are scored (the beam walk's fp64 row dots) and
+//    survive when q.c + |q| r >= tau (fp64); survivors are compacted in
+//    ascending order by wave ballots.  A level with more than max_nodes
+//    survivors ends the walk as an overflow.
+//  * the fused decode attends over the surviving leaves, keeping only keys
+//    whose fp64 score reaches tau.
+#include "attend_query.hpp"
+#include "route_walk.hpp"
+
+namespace tis {
+namespace {
+
+constexpr int kRadiusWaves = 4;
+
+__device__ inline double wave_max_d(double v) {
+  const int lane = __lane_id();
+  v = fmax(v, xor_lane<1>(v, lane));
+  v = fmax(v, xor_lane<2>(v, lane));
+  v = fmax(v, xor_lane<4>(v, lane));
+  v = fmax(v, xor_lane<8>(v, lane));
+  v = fmax(v, xor_lane<16>(v, lane));
+  return fmax(v, xor_lane<32>(v, lane));
+}
+
+template <typename T, typename S, int D>
+__global__ void __launch_bounds__(kRadiusWaves * 64) k_radius(RadiusArgs a) {
+  using AG = AttendGeom<T, D>;  // row geometry of 16-byte K loads
+  constexpr int E = AG::E, LPR = AG::LPR, R = AG::R, U = AG::U, RB = AG::RB, REP = AG::REP;
+  __shared__ float ctr[kRadiusWaves][kMaxLevels + 1][D];  // this leaf's ancestors' centres
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int64_t gw = static_cast<int64_t>(blockIdx.x) * kRadiusWaves + w;
+  const int64_t head = gw / a.waves_per_head;
+  if (head >= a.heads) return;  // whole wave: no barrier below spans waves
+  const int64_t n_leaves = a.n_at[a.levels];
+  const int64_t leaf0 = (gw - head * a.waves_per_head) * a.leaves_per_wave;
+  const int64_t leaf1 = min(leaf0 + a.leaves_per_wave, n_leaves);
+  const int lv = a.levels;
+  const int L = a.leaf_block;
+  const int col = (lane % LPR) * E;
+  const int rsub = lane / LPR;
+  const int kk = (lane % LPR) / REP;
+  const T *kh = static_cast<const T *>(a.K) + head * a.n_keys * D + col;
+  const S *summ = static_cast<const S *>(a.summ);
+  float (*cw)[D] = ctr[w];
+
+  // lane l - 1 keeps level l's node and the running maximum under it
+  const int my_level = lane + 1;
+  const bool owner = my_level <= lv;
+  const int64_t my_span = owner ? a.span[my_level] : 1;
+  int64_t my_node = -1;
+  double my_max = 0.0;
+  auto flush = [&]() {
+    if (owner && my_node >= 0)
+      atomicMax(a.d2 + a.node_off[my_level] + head * a.n_at[my_level] + my_node,
+                static_cast<unsigned long long>(__double_as_longlong(my_max)));
+  };
+
+  for (int64_t leaf = leaf0; leaf < leaf1; ++leaf) {
+    // ancestors: a level whose node changes flushes the old one's maximum
+    const int64_t node = owner ? leaf / my_span : -1;
+    if (owner && node != my_node) {
+      flush();
+      my_node = node;
+      my_max = 0.0;
+    }
+    // centres of every ancestor of this leaf into LDS (every level: the
+    // upper rows are L2-resident and a leaf's keys cost far more)
+    for (int l = 1; l <= lv; ++l) {
+      const int64_t anc = leaf / a.span[l];
+      const S *row = summ + a.summ_off[l] + (head * a.n_at[l] + anc) * D;
+      for (int c = lane; c < D; c += 64) {
+        float f;
+        if constexpr (sizeof(S) == 4) {
+          f = reinterpret_cast<const float *>(row)[c];
+        } else {
+          f = __uint_as_float(static_cast<uint32_t>(reinterpret_cast<const bf16_bits *>(row)[c].v)
+                              << 16);
+        }
+        cw[l][c] = f;
+      }
+    }
+    // LDS accesses of one wave are performed in order: the rows written
+    // above are what the lanes read below
+    __builtin_amdgcn_wave_barrier();
+    const T *kl = kh + leaf * L * D;
+    for (int r0 = 0; r0 < L; r0 += RB) {
+      uint4 kv[U];
+#pragma unroll
+      for (int i = 0; i < U; ++i) {
+        const int row = r0 + i * R + rsub;
+        kv[i] = row < L ? load16(kl + static_cast<int64_t>(row) * D) : make_uint4(0u, 0u, 0u, 0u);
+      }
+      float k[U][E];
+#pragma unroll
+      for (int i = 0; i < U; ++i) Vec16<T>::unpack(kv[i], k[i]);
+      const bool valid = r0 + kk * R + rsub < L;
+      for (int l = 1; l <= lv; ++l) {
+        float c[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) c[e] = cw[l][col + e];
+        double part[U];
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+          double s = 0.0;
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            const double diff = static_cast<double>(k[i][e]) - static_cast<double>(c[e]);
+            s = fma(diff, diff, s);
+          }
+          part[i] = s;
+        }
+        // lane holds the squared distance of row r0 + kk * R + rsub
+        const double d2 = group_transpose_reduce<U, LPR>(part, lane);
+        const double m = wave_max_d(valid ? d2 : 0.0);
+        if (lane == l - 1) my_max = fmax(my_max, m);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  flush();
+}
+
+// Smallest float32 r >= 0 with r * r >= D, from the reduced maxima.
+__global__ void __launch_bounds__(256) k_radius_finish(const unsigned long long *d2,
+                                                       float *radii, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const double D = __longlong_as_double(static_cast<long long>(d2[i]));
+  float r = static_cast<float>(sqrt(D));
+  for (int k = 0; k < 4; ++k)
+    if (static_cast<double>(r) * static_cast<double>(r) < D) r = __uint_as_float(__float_as_uint(r) + 1u);
+  for (int k = 0; k < 4; ++k) {
+    if (r > 0.f) {
+      const float dn = __uint_as_float(__float_as_uint(r) - 1u);
+      if (static_cast<double>(dn) * static_cast<double>(dn) >= D) r = dn;
+    }
+  }
+  radii[i] = r;
+}
+
+// ------------------------------------------------------------------ walk --
+template <int NW> struct ThreshShared {
+  double sc[NW * 64];            // scores of one chunk of candidates
+  int front[2][kMaxSurvivors];   // survivors of the level above / this level
+  int wcnt[NW];                  // survivors per wave of a chunk
+};
+
+// Walks query qi down the tree with the sphere bound (every wave of the
+// NW-wave workgroup takes part; the first NRW score).  Returns the number
+// of surviving leaves, or -1 when a level keeps more than max_nodes; the
+// survivors are in sh.front[*buf][0 ..), ascending.
+template <typename T, typename S, int D, int NW, int NRW>
+__device__ int threshold_walk(const RouteArgs &a, const SphereArgs &sa, ThreshShared<NW> &sh,
+                              int qi, int *buf) {
+  constexpr int NT = NW * 64;
+  constexpr int E = Vec16<S>::kElems;
+  constexpr int LPR = D / E;
+  constexpr int RPI = 64 / LPR;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int bi = qi / a.q_heads;
+  const int hq = qi - bi * a.q_heads;
+  const int64_t head = static_cast<int64_t>(bi) * a.kv_heads + hq / a.group;
+  const int b = a.branching;
+  const int lv = a.levels;
+  const int col = (lane % LPR) * E;
+
+  QRaw<T, E> qr;
+  qr.load(static_cast<const T *>(a.Q) + static_cast<int64_t>(qi) * D + col);
+  double qq;
+  {
+    double qv[E];
+    qr.widen(qv);
+    qq = 0.0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) qq = fma(qv[e], qv[e], qq);
+    qq = group_sum<1, LPR / 2>(qq, lane);
+  }
+  const double qn = sqrt(qq);
+  const double tau = static_cast<double>(sa.tau[qi]);
+
+  LevelCursor<false> lc;
+  lc.init(a, 1, D);
+  if (tid == 0) sh.front[0][0] = 0;  // the root: its children are nodes 0 .. b-1
+  __syncthreads();
+  int cur = 0, nf = 1;
+  for (int l = 1; l <= lv; ++l) {
+    const int C = nf * b;
+    const S *sl = static_cast<const S *>(a.summ) + lc.off + head * lc.rows * D + col;
+    const float *rl = sa.radii + sa.node_off[l] + head * lc.rows;
+    const int *fr = sh.front[cur];
+    int *nx = sh.front[cur ^ 1];
+    double *sc = sh.sc;
+    int kept = 0;
+    for (int c0 = 0; c0 < C; c0 += NT) {
+      const int Cc = min(NT, C - c0);
+      const auto node_of = [&](int p) {
+        const int g = c0 + p;
+        return fr[g / b] * b + g % b;
+      };
+      int nd = 0;
+      float r = 0.f;
+      if (tid < Cc) {
+        nd = node_of(tid);
+        r = rl[nd];
+      }
+      const auto emit = [&](int pos, int, double s) { sc[pos] = s; };
+      const int per = (Cc + NRW * RPI - 1) / (NRW * RPI);
+      if (w < NRW) {
+        if (per <= 1)
+          score_rows<T, S, D, 1, false>(sl, Cc, node_of, emit, qr, NRW, w, lane);
+        else if (per <= 2)
+          score_rows<T, S, D, 2, false>(sl, Cc, node_of, emit, qr, NRW, w, lane);
+        else if (per <= 4)
+          score_rows<T, S, D, 4, false>(sl, Cc, node_of, emit, qr, NRW, w, lane);
+        else
+          score_rows<T, S, D, 8, false>(sl, Cc, node_of, emit, qr, NRW, w, lane);
+      }
+      __syncthreads();
+      const bool pass = tid < Cc && sc[tid] + qn * static_cast<double>(r) >= tau;
+      const uint64_t m = __ballot(pass);
+      if (lane == 0) sh.wcnt[w] = __popcll(m);
+      __syncthreads();
+      int off = 0, total = 0;
+#pragma unroll
+      for (int j = 0; j < NW; ++j) {
+        const int cj = sh.wcnt[j];
+        off += j < w ? cj : 0;
+        total += cj;
+      }
+      if (pass) {
+        const int pos = kept + off + __popcll(m & ((1ull << lane) - 1ull));
+        if (pos < sa.max_nodes) nx[pos] = nd;
+      }
+      kept += total;
+      __syncthreads();
+    }
+    if (kept > sa.max_nodes) return -1;  // the same on every thread
+    nf = kept;
+    cur ^= 1;
+    if (l < lv) lc.down(D);
+  }
+  *buf = cur;
+  return nf;
+}
+
+constexpr int kThreshRouteWaves = 8;
+
+template <typename T, typename S, int D>
+__global__ void __launch_bounds__(kThreshRouteWaves * 64)
+    k_route_threshold(RouteArgs a, SphereArgs sa) {
+  __shared__ ThreshShared<kThreshRouteWaves> sh;
+  const int qi = query_of_slot(blockIdx.x, a.queries, a.group);
+  int buf = 0;
+  const int kept = threshold_walk<T, S, D, kThreshRouteWaves, kThreshRouteWaves>(a, sa, sh, qi,
+                                                                                 &buf);
+  int32_t *out = a.indices + static_cast<int64_t>(qi) * sa.max_nodes;
+  for (int k = threadIdx.x; k < sa.max_nodes; k += kThreshRouteWaves * 64)
+    out[k] = k < kept ? sh.front[buf][k] : -1;
+  if (threadIdx.x == 0 && sa.counts) sa.counts[qi] = kept;
+}
+
+constexpr int kThreshDecodeWaves = 16;
+constexpr int kThreshDecodeWalkWaves = 8;
+
+template <typename T, typename S, int D>
+__global__ void __launch_bounds__(kThreshDecodeWaves * 64)
+    k_decode_threshold(RouteArgs ra, SphereArgs sa, AttendArgs aa) {
+  __shared__ ThreshShared<kThreshDecodeWaves> sh;
+  __shared__ AttendShared<T, D> ash;
+  const int sp = blockIdx.x / aa.queries;
+  const int qi = query_of_slot(blockIdx.x - sp * aa.queries, aa.queries, aa.group);
+  const uint4 qraw = attend_q_raw<T, D>(aa, qi);
+  int buf = 0;
+  const int kept = threshold_walk<T, S, D, kThreshDecodeWaves, kThreshDecodeWalkWaves>(
+      ra, sa, sh, qi, &buf);
+  if (sp == 0) {
+    if (ra.indices) {
+      int32_t *out = ra.indices + static_cast<int64_t>(qi) * sa.max_nodes;
+      for (int k = threadIdx.x; k < sa.max_nodes; k += kThreshDecodeWaves * 64)
+        out[k] = k < kept ? sh.front[buf][k] : -1;
+    }
+    if (threadIdx.x == 0 && sa.counts) sa.counts[qi] = kept;
+  }
+  const int n = kept < 0 ? 0 : kept;
+  const int s0 = sp * n / aa.splits;
+  const int s1 = (sp + 1) * n / aa.splits;
+  float *part = aa.splits > 1
+                    ? aa.part + (static_cast<int64_t>(qi) * aa.splits + sp) * (D + kPartHeader)
+                    : nullptr;
+  attend_query<T, D, false, true>(aa, ash, qi, qraw, sh.front[buf] + s0, nullptr, s1 - s0,
+                                  kept < 0, part, static_cast<double>(sa.tau[qi]));
+}
+
+// ------------------------------------------------------------- launches --
+template <typename T, typename S>
+hipError_t launch_radii_ts(int head_dim, const RadiusArgs &a, int64_t waves, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((waves + kRadiusWaves - 1) / kRadiusWaves));
+  const dim3 block(kRadiusWaves * 64);
+  if (head_dim == 128)
+    hipLaunchKernelGGL((k_radius<T, S, 128>), grid, block, 0, s, a);
+  else if (head_dim == 64)
+    hipLaunchKernelGGL((k_radius<T, S, 64>), grid, block, 0, s, a);
+  else
+    return hipErrorInvalidValue;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 g2(static_cast<unsigned>((a.total_nodes + 255) / 256));
+  hipLaunchKernelGGL(k_radius_finish, g2, dim3(256), 0, s, a.d2, a.radii, a.total_nodes);
+  return hipGetLastError();
+}
+
+template <typename T, typename S>
+hipError_t launch_route_threshold_ts(int head_dim, const RouteArgs &ra, const SphereArgs &sa,
+                                     hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(ra.queries));
+  const dim3 block(kThreshRouteWaves * 64);
+  if (head_dim == 128)
+    hipLaunchKernelGGL((k_route_threshold<T, S, 128>), grid, block, 0, s, ra, sa);
+  else if (head_dim == 64)
+    hipLaunchKernelGGL((k_route_threshold<T, S, 64>), grid, block, 0, s, ra, sa);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+template <typename T, typename S>
+hipError_t launch_decode_threshold_ts(int head_dim, const RouteArgs &ra, const SphereArgs &sa,
+                                      const AttendArgs &aa, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(ra.queries) * static_cast<unsigned>(aa.splits));
+  const dim3 block(kThreshDecodeWaves * 64);
+  if (head_dim == 128)
+    hipLaunchKernelGGL((k_decode_threshold<T, S, 128>), grid, block, 0, s, ra, sa, aa);
+  else if (head_dim == 64)
+    hipLaunchKernelGGL((k_decode_threshold<T, S, 64>), grid, block, 0, s, ra, sa, aa);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_radii(Dt dt, Dt sdt, int head_dim, const RadiusArgs &a, int64_t waves,
+                        hipStream_t s) {
+  hipError_t e = launch_fill_zero(reinterpret_cast<double *>(a.d2), a.total_nodes, s);
+  if (e != hipSuccess) return e;
+  if (dt == Dt::BF16)
+    return sdt == Dt::BF16 ? launch_radii_ts<bf16_bits, bf16_bits>(head_dim, a, waves, s)
+                           : launch_radii_ts<bf16_bits, float>(head_dim, a, waves, s);
+  return sdt == Dt::BF16 ? launch_radii_ts<float, bf16_bits>(head_dim, a, waves, s)
+                         : launch_radii_ts<float, float>(head_dim, a, waves, s);
+}
+
+hipError_t launch_route_threshold(Dt dt, Dt sdt, int head_dim, const RouteArgs &ra,
+                                  const SphereArgs &sa, hipStream_t s) {
+  if (dt == Dt::BF16)
+    return sdt == Dt::BF16 ? launch_route_threshold_ts<bf16_bits, bf16_bits>(head_dim, ra, sa, s)
+                           : launch_route_threshold_ts<bf16_bits, float>(head_dim, ra, sa, s);
+  return sdt == Dt::BF16 ? launch_route_threshold_ts<float, bf16_bits>(head_dim, ra, sa, s)
+                         : launch_route_threshold_ts<float, float>(head_dim, ra, sa, s);
+}
+
+hipError_t launch_decode_threshold(Dt dt, Dt sdt, int head_dim, const RouteArgs &ra,
+                                   const SphereArgs &sa, const AttendArgs &aa, hipStream_t s) {
+  hipError_t e;
+  if (dt == Dt::BF16)
+    e = sdt == Dt::BF16 ? launch_decode_threshold_ts<bf16_bits, bf16_bits>(head_dim, ra, sa, aa, s)
+                        : launch_decode_threshold_ts<bf16_bits, float>(head_dim, ra, sa, aa, s);
+  else
+    e = sdt == Dt::BF16 ? launch_decode_threshold_ts<float, bf16_bits>(head_dim, ra, sa, aa, s)
+                        : launch_decode_threshold_ts<float, float>(head_dim, ra, sa, aa, s);
+  if (e != hipSuccess || aa.splits <= 1) return e;
+  return launch_combine(head_dim, aa, s);
+}
+
+}  // namespace tis

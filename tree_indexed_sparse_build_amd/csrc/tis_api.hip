@@ -582,7 +582,7 @@ tis_status tis_cache_tree_reset(tis_cache_tree *tree, void *stream) {
   if (st != TIS_OK) return st;
   if (!aligned(tree->summaries, 16) || !aligned(tree->state, 16))
     return fail(TIS_E_ALIGN, "tis_cache_tree_reset: summaries and state need 16-byte alignment");
-  st = hip_status(tis::launch_cache_reset(tree->state, g.state_elems,
+  st = hip_status(tis::launch_fill_zero(tree->state, g.state_elems,
                                           static_cast<hipStream_t>(stream)),
                   "tis_cache_tree_reset launch");
   if (st != TIS_OK) return st;
@@ -699,6 +699,214 @@ tis_status tis_cache_tree_decode(const void *Q, const void *K, const void *V, ti
   return hip_status(tis::launch_decode(dt, to_dt(tree->summary_dtype), tree->head_dim, ra, aa,
                                       static_cast<hipStream_t>(stream)),
                     "tis_cache_tree_decode launch");
+}
+
+// ------------------------------------------------------ bounding spheres --
+
+namespace {
+
+int64_t tree_nodes(int batch, int kv_heads, int branching, int levels) {
+  if (batch < 1 || kv_heads < 1 || branching < 2 || levels < 1 || levels > tis::kMaxLevels)
+    return 0;
+  int64_t n = 1, total = 0;
+  for (int l = 1; l <= levels; ++l) {
+    n *= branching;
+    if (n > 0x7fffffffLL) return 0;
+    total += n;
+  }
+  const double nodes = static_cast<double>(batch) * kv_heads * static_cast<double>(total);
+  if (nodes > 1.0e17) return 0;
+  return static_cast<int64_t>(batch) * kv_heads * total;
+}
+
+// Checks shared by the threshold route and decode.
+tis_status check_threshold(const char *who, const void *Q, tis_dtype dtype, int q_heads,
+                           const tis_tree *tree, const float *radii, const float *tau,
+                           int max_nodes, Geometry *g, int64_t *queries) {
+  tis_status st = check_dtype(dtype);
+  if (st != TIS_OK) return st;
+  st = check_summary_dtype(who, tree->summary_dtype);
+  if (st != TIS_OK) return st;
+  st = check_tree(tree->batch, tree->kv_heads, tree->n_keys, tree->head_dim, tree->branching,
+                  tree->leaf_block, tree->levels, g);
+  if (st != TIS_OK) return st;
+  if (q_heads < 1 || q_heads % tree->kv_heads != 0)
+    return fail(TIS_E_SHAPE, "%s: q_heads %d is not a positive multiple of kv_heads %d", who,
+                q_heads, tree->kv_heads);
+  if (max_nodes < 1) return fail(TIS_E_SHAPE, "%s: max_nodes %d < 1", who, max_nodes);
+  if (max_nodes > TIS_MAX_SURVIVORS)
+    return fail(TIS_E_UNSUPPORTED, "%s: max_nodes %d > %d", who, max_nodes, TIS_MAX_SURVIVORS);
+  if (!aligned(Q, 16) || !aligned(tree->summaries, 16) || !aligned(radii, 4) ||
+      !aligned(tau, 4))
+    return fail(TIS_E_ALIGN, "%s: Q and summaries need 16-byte, radii and tau 4-byte alignment",
+                who);
+  *queries = static_cast<int64_t>(tree->batch) * q_heads;
+  if (*queries > 0x7fffffffLL) return fail(TIS_E_UNSUPPORTED, "%s: too many queries", who);
+  return TIS_OK;
+}
+
+tis::SphereArgs sphere_args(const tis_tree *tree, const float *radii, const float *tau,
+                            int max_nodes, int32_t *counts) {
+  tis::SphereArgs sa{};
+  sa.radii = radii;
+  sa.tau = tau;
+  sa.counts = counts;
+  sa.max_nodes = max_nodes;
+  const int64_t heads = static_cast<int64_t>(tree->batch) * tree->kv_heads;
+  int64_t n = 1, off = 0;
+  for (int l = 1; l <= tis::kMaxLevels; ++l) {
+    if (l <= tree->levels) {
+      n *= tree->branching;
+      sa.node_off[l] = off;
+      off += heads * n;
+    } else {
+      sa.node_off[l] = off;
+    }
+  }
+  return sa;
+}
+
+}  // namespace
+
+size_t tis_tree_radius_bytes(int batch, int kv_heads, int branching, int levels) {
+  return static_cast<size_t>(tree_nodes(batch, kv_heads, branching, levels)) * sizeof(float);
+}
+
+size_t tis_radius_workspace_bytes(int batch, int kv_heads, int branching, int levels) {
+  return static_cast<size_t>(tree_nodes(batch, kv_heads, branching, levels)) * sizeof(double);
+}
+
+tis_status tis_tree_radii(const void *K, tis_dtype dtype, const tis_tree *tree, float *radii,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+  if (!K || !tree || !tree->summaries || !radii || !workspace)
+    return fail(TIS_E_NULL, "tis_tree_radii: K, tree, tree->summaries, radii and workspace are "
+                            "required");
+  tis_status st = check_dtype(dtype);
+  if (st != TIS_OK) return st;
+  st = check_summary_dtype("tis_tree_radii", tree->summary_dtype);
+  if (st != TIS_OK) return st;
+  Geometry g;
+  st = check_tree(tree->batch, tree->kv_heads, tree->n_keys, tree->head_dim, tree->branching,
+                  tree->leaf_block, tree->levels, &g);
+  if (st != TIS_OK) return st;
+  const int64_t nodes = tree_nodes(tree->batch, tree->kv_heads, tree->branching, tree->levels);
+  if (workspace_bytes < static_cast<size_t>(nodes) * sizeof(double))
+    return fail(TIS_E_WORKSPACE, "tis_tree_radii: workspace of %zu bytes required, %zu given",
+                static_cast<size_t>(nodes) * sizeof(double), workspace_bytes);
+  if (!aligned(K, 16) || !aligned(tree->summaries, 16) || !aligned(radii, 4) ||
+      !aligned(workspace, 16))
+    return fail(TIS_E_ALIGN, "tis_tree_radii: K, summaries and workspace need 16-byte, radii "
+                             "4-byte alignment");
+  const int64_t heads = static_cast<int64_t>(tree->batch) * tree->kv_heads;
+  const int64_t leaves = g.n_at[tree->levels];
+  tis::RadiusArgs a{};
+  a.K = K;
+  a.summ = tree->summaries;
+  a.d2 = static_cast<unsigned long long *>(workspace);
+  a.radii = radii;
+  a.n_keys = tree->n_keys;
+  a.heads = heads;
+  // about 4096 waves over the whole tree, each a run of consecutive leaves
+  int64_t lpw = heads * leaves / 4096;
+  lpw = lpw < 1 ? 1 : lpw > leaves ? leaves : lpw;
+  a.leaves_per_wave = lpw;
+  a.waves_per_head = (leaves + lpw - 1) / lpw;
+  a.total_nodes = nodes;
+  a.branching = tree->branching;
+  a.leaf_block = tree->leaf_block;
+  a.levels = tree->levels;
+  int64_t off = 0;
+  for (int l = 0; l <= tis::kMaxLevels; ++l) {
+    a.n_at[l] = g.n_at[l];
+    a.summ_off[l] = g.summ_off[l];
+    a.node_off[l] = off;  // level l's block: after the nodes of levels 1 .. l-1
+    a.span[l] = 1;
+    if (l >= 1 && l <= tree->levels) {
+      for (int k = l; k < tree->levels; ++k) a.span[l] *= tree->branching;
+      off += heads * g.n_at[l];
+    }
+  }
+  const int64_t waves = heads * a.waves_per_head;
+  if (waves / 4 + 1 > 0x7fffffffLL)
+    return fail(TIS_E_UNSUPPORTED, "tis_tree_radii: grid too large");
+  return hip_status(tis::launch_radii(to_dt(dtype), to_dt(tree->summary_dtype), tree->head_dim,
+                                      a, waves, static_cast<hipStream_t>(stream)),
+                    "tis_tree_radii launch");
+}
+
+tis_status tis_tree_route_threshold(const void *Q, tis_dtype dtype, int q_heads,
+                                    const tis_tree *tree, const float *radii, const float *tau,
+                                    int max_nodes, int32_t *indices, int32_t *counts,
+                                    void *stream) {
+  if (!Q || !tree || !tree->summaries || !radii || !tau || !indices)
+    return fail(TIS_E_NULL, "tis_tree_route_threshold: Q, tree, tree->summaries, radii, tau and "
+                            "indices are required");
+  Geometry g;
+  int64_t queries = 0;
+  tis_status st = check_threshold("tis_tree_route_threshold", Q, dtype, q_heads, tree, radii,
+                                  tau, max_nodes, &g, &queries);
+  if (st != TIS_OK) return st;
+  if (!aligned(indices, 4) || (counts && !aligned(counts, 4)))
+    return fail(TIS_E_ALIGN, "tis_tree_route_threshold: indices and counts need 4-byte alignment");
+  const tis::RouteArgs ra = route_args(Q, tree, g, q_heads, 1, indices, nullptr, queries);
+  const tis::SphereArgs sa = sphere_args(tree, radii, tau, max_nodes, counts);
+  return hip_status(tis::launch_route_threshold(to_dt(dtype), to_dt(tree->summary_dtype),
+                                                tree->head_dim, ra, sa,
+                                                static_cast<hipStream_t>(stream)),
+                    "tis_tree_route_threshold launch");
+}
+
+size_t tis_decode_threshold_workspace_bytes(int batch, int q_heads, int head_dim, int max_nodes,
+                                            int leaf_block) {
+  return tis_attend_workspace_bytes(batch, q_heads, head_dim, max_nodes, leaf_block);
+}
+
+tis_status tis_tree_decode_threshold(const void *Q, const void *K, const void *V, tis_dtype dtype,
+                                     int q_heads, const tis_tree *tree, const float *radii,
+                                     const float *tau, int max_nodes, float scale, float *O,
+                                     int32_t *indices, int32_t *counts, void *workspace,
+                                     size_t workspace_bytes, void *stream) {
+  if (!Q || !K || !V || !tree || !tree->summaries || !radii || !tau || !O)
+    return fail(TIS_E_NULL, "tis_tree_decode_threshold: Q, K, V, tree, tree->summaries, radii, "
+                            "tau and O are required");
+  Geometry g;
+  int64_t queries = 0;
+  tis_status st = check_threshold("tis_tree_decode_threshold", Q, dtype, q_heads, tree, radii,
+                                  tau, max_nodes, &g, &queries);
+  if (st != TIS_OK) return st;
+  if (!(scale == scale) || isinf(scale))
+    return fail(TIS_E_SHAPE, "tis_tree_decode_threshold: scale must be finite");
+  if (!aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || (indices && !aligned(indices, 4)) ||
+      (counts && !aligned(counts, 4)))
+    return fail(TIS_E_ALIGN, "tis_tree_decode_threshold: K, V and O need 16-byte, indices and "
+                             "counts 4-byte alignment");
+  const tis::RouteArgs ra = route_args(Q, tree, g, q_heads, 1, indices, nullptr, queries);
+  const tis::SphereArgs sa = sphere_args(tree, radii, tau, max_nodes, counts);
+  const double sc =
+      scale > 0.f ? static_cast<double>(scale) : 1.0 / sqrt(static_cast<double>(tree->head_dim));
+  tis::AttendArgs aa{};
+  aa.Q = Q;
+  aa.K = K;
+  aa.V = V;
+  aa.indices = nullptr;
+  aa.O = O;
+  aa.queries = static_cast<int>(queries);
+  aa.n_keys = tree->n_keys;
+  aa.key_stride = tree->n_keys;
+  aa.q_heads = q_heads;
+  aa.kv_heads = tree->kv_heads;
+  aa.group = q_heads / tree->kv_heads;
+  aa.leaf_block = tree->leaf_block;
+  aa.beam = max_nodes;
+  aa.n_blocks = tree->n_keys / tree->leaf_block;
+  aa.scale_log2 = static_cast<float>(sc * 1.4426950408889634);
+  st = plan_split("tis_tree_decode_threshold", queries, tree->head_dim, max_nodes,
+                  tree->leaf_block, workspace, workspace_bytes, &aa);
+  if (st != TIS_OK) return st;
+  return hip_status(tis::launch_decode_threshold(to_dt(dtype), to_dt(tree->summary_dtype),
+                                                 tree->head_dim, ra, sa, aa,
+                                                 static_cast<hipStream_t>(stream)),
+                    "tis_tree_decode_threshold launch");
 }
 
 const char *tis_last_error(void) { return g_err; }

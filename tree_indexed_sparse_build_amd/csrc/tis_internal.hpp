@@ -142,8 +142,49 @@ struct AppendArgs {
   uint32_t span[kMaxLevels];   // L b^h: below the capacity (or L itself when H = 1)
 };
 
-hipError_t launch_cache_reset(double *state, int64_t elems, hipStream_t s);
+// zero `elems` doubles with a kernel (no memset node, so it can sit in a graph)
+hipError_t launch_fill_zero(double *p, int64_t elems, hipStream_t s);
 hipError_t launch_cache_append(Dt dt, Dt sdt, int head_dim, const AppendArgs &a, hipStream_t s);
+
+// ------------------------------------------------------ bounding spheres --
+// Radius of every node of a full tree about its stored summary: the largest
+// squared key distance, max-reduced in fp64 (as ordered bits, atomically)
+// into d2, then rounded up to float32 into radii.  Both are level-major with
+// one element per node: level l's block [B*Hkv][b^l] at node_off[l].
+struct RadiusArgs {
+  const void *K;
+  const void *summ;            // float or bf16 bits (the summary type)
+  unsigned long long *d2;      // fp64 bits, zeroed before the launch
+  float *radii;
+  int64_t n_keys;              // N
+  int64_t heads;               // B * Hkv
+  int64_t leaves_per_wave;
+  int64_t waves_per_head;
+  int64_t total_nodes;         // B * Hkv * (n_1 + ... + n_lv)
+  int branching, leaf_block, levels;
+  int64_t n_at[kMaxLevels + 1];      // b^l
+  int64_t span[kMaxLevels + 1];      // leaves under a level-l node: b^(lv - l)
+  int64_t summ_off[kMaxLevels + 1];  // element offset of level l in summ
+  int64_t node_off[kMaxLevels + 1];  // node offset of level l in d2 / radii
+};
+
+hipError_t launch_radii(Dt dt, Dt sdt, int head_dim, const RadiusArgs &a, int64_t waves,
+                        hipStream_t s);
+
+// Threshold walk and decode: survivors of the sphere bound q.c + |q| r >= tau.
+constexpr int kMaxSurvivors = 2048;  // survivors one level may keep
+struct SphereArgs {
+  const float *radii;          // level-major, as RadiusArgs
+  const float *tau;            // [B * Hq]
+  int32_t *counts;             // [B * Hq] survivors (-1: overflow), may be null
+  int max_nodes;               // survivors a level may keep (<= kMaxSurvivors)
+  int64_t node_off[kMaxLevels + 1];
+};
+
+hipError_t launch_route_threshold(Dt dt, Dt sdt, int head_dim, const RouteArgs &ra,
+                                  const SphereArgs &sa, hipStream_t s);
+hipError_t launch_decode_threshold(Dt dt, Dt sdt, int head_dim, const RouteArgs &ra,
+                                   const SphereArgs &sa, const AttendArgs &aa, hipStream_t s);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

@@ -210,6 +210,87 @@ def tree_decode(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, tree: Tree, b
     return (O, idx) if return_indices else O
 
 
+def tree_radii(K: torch.Tensor, tree: Tree) -> torch.Tensor:
+    """Radius of every node about its stored summary (the smallest float32
+    whose square covers the largest squared key distance): float32, level-
+    major, one element per node (level l a [B, Hkv, b**l] block)."""
+    _need_device(K, tree.summaries)
+    L = lib()
+    nb = L.tis_tree_radius_bytes(tree.batch, tree.kv_heads, tree.branching, tree.levels)
+    wsb = L.tis_radius_workspace_bytes(tree.batch, tree.kv_heads, tree.branching, tree.levels)
+    if nb == 0:
+        raise _lib.TisError(_lib.TIS_E_SHAPE, "invalid tree geometry")
+    radii = torch.empty(nb // 4, dtype=torch.float32, device=K.device)
+    ws = _workspace(K.device, "radii", wsb)
+    t = tree.c_struct()
+    check(L.tis_tree_radii(K.data_ptr(), _dtype_code(K), ctypes.byref(t), radii.data_ptr(),
+                           ws.data_ptr(), ws.numel(), _stream(K.device)))
+    return radii
+
+
+def radii_level(tree: Tree, radii: torch.Tensor, l: int) -> torch.Tensor:
+    """Radii of level l as a [B, Hkv, b**l] view."""
+    heads = tree.batch * tree.kv_heads
+    off = heads * sum(tree.branching ** k for k in range(1, l))
+    n = tree.branching ** l
+    return radii[off:off + heads * n].view(tree.batch, tree.kv_heads, n)
+
+
+def _check_tau(tau: torch.Tensor, B: int, Hq: int) -> None:
+    _check_buffer(tau, (B, Hq), torch.float32, "tau")
+
+
+def tree_route_threshold(Q: torch.Tensor, tree: Tree, radii: torch.Tensor, tau: torch.Tensor,
+                         max_nodes: int):
+    """Leaves whose every ancestor's sphere bound q.c + |q| r reaches tau:
+    (indices int32 [B, Hq, max_nodes] ascending, -1 padded; counts int32
+    [B, Hq], -1 where a level had more than max_nodes survivors)."""
+    _need_device(Q, tree.summaries, radii)
+    B, Hq, d = Q.shape
+    _check_tau(tau, B, Hq)
+    idx = torch.empty((B, Hq, max_nodes), dtype=torch.int32, device=Q.device)
+    cnt = torch.empty((B, Hq), dtype=torch.int32, device=Q.device)
+    t = tree.c_struct()
+    check(lib().tis_tree_route_threshold(Q.data_ptr(), _dtype_code(Q), Hq, ctypes.byref(t),
+                                         radii.data_ptr(), tau.data_ptr(), int(max_nodes),
+                                         idx.data_ptr(), cnt.data_ptr(), _stream(Q.device)))
+    return idx, cnt
+
+
+def tree_decode_threshold(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, tree: Tree,
+                          radii: torch.Tensor, tau: torch.Tensor, max_nodes: int,
+                          scale: Optional[float] = None, return_indices: bool = False,
+                          out: Optional[torch.Tensor] = None):
+    """Softmax over the keys with q.k >= tau, found through the sphere bound,
+    in one launch.  Returns O (float32 [B, Hq, d]; zero rows where no key
+    reaches tau, NaN after an overflow) and, with return_indices=True, also
+    (indices, counts) as tree_route_threshold gives them."""
+    _need_device(Q, K, V, tree.summaries, radii)
+    if K.dtype != Q.dtype or V.dtype != Q.dtype:
+        raise TypeError("Q, K and V must share one dtype")
+    B, Hq, d = Q.shape
+    _check_tau(tau, B, Hq)
+    O = out if out is not None else torch.empty((B, Hq, d), dtype=torch.float32,
+                                                 device=Q.device)
+    _check_buffer(O, (B, Hq, d), torch.float32, "out")
+    idx = cnt = None
+    if return_indices:
+        idx = torch.empty((B, Hq, max_nodes), dtype=torch.int32, device=Q.device)
+        cnt = torch.empty((B, Hq), dtype=torch.int32, device=Q.device)
+    L = lib()
+    wsb = L.tis_decode_threshold_workspace_bytes(B, Hq, d, max_nodes, tree.leaf_block)
+    ws = _workspace(Q.device, "decode", wsb) if wsb else None
+    t = tree.c_struct()
+    check(L.tis_tree_decode_threshold(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q),
+                                      Hq, ctypes.byref(t), radii.data_ptr(), tau.data_ptr(),
+                                      int(max_nodes), 0.0 if scale is None else float(scale),
+                                      O.data_ptr(), idx.data_ptr() if idx is not None else None,
+                                      cnt.data_ptr() if cnt is not None else None,
+                                      ws.data_ptr() if ws is not None else None,
+                                      ws.numel() if ws is not None else 0, _stream(Q.device)))
+    return (O, idx, cnt) if return_indices else O
+
+
 def decode(Q, K, V, branching: int, leaf_block: int, levels: int, beam: int,
            scale: Optional[float] = None):
     """Build, then one fused decode step, on the current stream (no host sync
