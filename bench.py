@@ -181,6 +181,46 @@ def bf16_summaries(tis, torch, w, Q, K, V, reps, warmup):
             "decode_bytes": dec}
 
 
+def threshold_retrieval(tis, torch, w, Q, K, V, reps, warmup, k_ranks=(64, 512)):
+    """Bounding-sphere threshold retrieval on the step's data: the radii pass
+    over K, then the fused threshold decode at thresholds halfway between
+    each query's k-th and (k+1)-th best key score (set up with a dense torch
+    matmul, not timed)."""
+    tree = tis.tree_build(K, w.branching, w.leaf_block, w.levels)
+    radii = tis.tree_radii(K, tree)
+    for _ in range(warmup):
+        tis.tree_radii(K, tree)
+    radii_s = per_launch(torch, lambda: tis.tree_radii(K, tree), reps)
+    nodes = sum(w.branching ** l for l in range(1, w.levels + 1))
+    radii_bytes = w.batch * w.kv_heads * (w.n_keys * w.head_dim * w.elem_bytes
+                                          + nodes * w.head_dim * 4 + nodes * 4)
+    max_nodes = min(w.n_leaves, tis.TIS_MAX_SURVIVORS)
+    out = {"radii_us": radii_s * 1e6, "radii_gbs": radii_bytes / radii_s / 1e9,
+           "radii_bytes": radii_bytes, "max_nodes": max_nodes, "thresholds": []}
+    G = w.group
+    for k in k_ranks:
+        tau = torch.empty((w.batch, w.q_heads), dtype=torch.float32, device=Q.device)
+        for bi in range(w.batch):
+            for h in range(w.kv_heads):
+                s = Q[bi, h * G:(h + 1) * G].float() @ K[bi, h].float().t()
+                top = torch.topk(s, k + 1, dim=1).values
+                tau[bi, h * G:(h + 1) * G] = (top[:, k - 1] + top[:, k]) / 2
+        o = torch.empty((w.batch, w.q_heads, w.head_dim), dtype=torch.float32, device=Q.device)
+        _, _, cnt = tis.tree_decode_threshold(Q, K, V, tree, radii, tau, max_nodes,
+                                              return_indices=True)
+        for _ in range(warmup):
+            tis.tree_decode_threshold(Q, K, V, tree, radii, tau, max_nodes, out=o)
+        dec_s = per_launch(torch, lambda: tis.tree_decode_threshold(
+            Q, K, V, tree, radii, tau, max_nodes, out=o), reps)
+        c = cnt.float()
+        kept_bytes = float(c.clamp(min=0).sum()) * w.leaf_block * w.head_dim * w.elem_bytes * 2
+        out["thresholds"].append({
+            "k": k, "decode_us": dec_s * 1e6, "queries_per_s": w.queries / dec_s,
+            "leaves_kept_mean": float(c.mean()), "leaves_kept_max": int(c.max()),
+            "overflow": int((cnt < 0).sum()), "gathered_gbs": kept_bytes / dec_s / 1e9})
+    return out
+
+
 def cache_states(torch, dev, plan, reps, back_to_back):
     """Durations in two cache states.  cold: 1 GiB read first, which leaves
     none of the inputs in the Infinity Cache or an L2 and no dirty lines to
@@ -279,6 +319,8 @@ def main(argv=None):
                     help="skip the growing-cache decode loop measurement")
     ap.add_argument("--no-bf16-summaries", action="store_true",
                     help="skip the measurement of the step with bfloat16 summaries")
+    ap.add_argument("--no-threshold", action="store_true",
+                    help="skip the bounding-sphere threshold retrieval measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 256 MiB device-to-device copy first (the reference "
                          "dispatch for scaling HBM byte counters)")
@@ -426,6 +468,17 @@ def main(argv=None):
         f"GB/s, {dec_bytes / states['decode_cold_us'] / 1e3 / HBM_PEAK_GBS:.1%}), steady "
         f"{states['decode_steady_us']:.2f} us")
 
+    thr = None
+    if not args.no_threshold:
+        thr = threshold_retrieval(tis, torch, w, Q, K, V, K_, args.warmup)
+        log(f"bounding spheres: radii {thr['radii_us']:.1f} us ({thr['radii_gbs']:.0f} GB/s on "
+            f"{thr['radii_bytes'] / 1e6:.1f} MB); " + "; ".join(
+                f"threshold at the {t['k']}-th best score: decode {t['decode_us']:.2f} us -> "
+                f"{t['queries_per_s']:.3e} queries/s, leaves kept mean "
+                f"{t['leaves_kept_mean']:.1f} max {t['leaves_kept_max']} of {w.n_leaves}, "
+                f"overflow {t['overflow']}"
+                for t in thr["thresholds"]))
+
     bf = None
     if not args.no_bf16_summaries:
         bf = bf16_summaries(tis, torch, w, Q, K, V, K_, args.warmup)
@@ -491,6 +544,7 @@ def main(argv=None):
         "cpu_baseline": cpu,
         "cache_decode_loop": cache,
         "bf16_summaries": bf,
+        "threshold_retrieval": thr,
     }
     print(json.dumps(line), flush=True)
     return 0

@@ -9,4 +9,4 @@ Abstract).  The three calls run as hand-written HIP kernels in libtis.so.
 from .ops import (Tree, tree_build, tree_route, tree_attend, tree_decode, decode,  # noqa: F401
                   version, from_storage, DecodePlan, CacheTree, tree_radii, radii_level,
                   tree_route_threshold, tree_decode_threshold)
-from ._lib import TisError  # noqa: F401
+from ._lib import TisError, TIS_MAX_SURVIVORS  # noqa: F401
