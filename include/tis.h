@@ -359,6 +359,44 @@ tis_status tis_cache_tree_decode(const void *Q, const void *K, const void *V, ti
                                  float *O, int32_t *indices, void *workspace,
                                  size_t workspace_bytes, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Causal prefill routing
+ *
+ * The ALHR post (Summary) counts the keys a query reads averaged over the
+ * positions of a 1,024-token input: every position is a query over the
+ * keys up to it.  Here the query at position t routes over the tree of the
+ * first t + 1 keys -- the growing-cache tree at n_keys = t + 1, with its
+ * depth, nodes cut at t + 1 and means over the keys they hold -- and attends
+ * over the keys of its kept leaf blocks up to t.  The nodes left of key t are
+ * the ones a tree over all n_keys keys stores; the node holding key t at
+ * each height (partial for t) gets its mean from a table the call computes
+ * first.
+ * --------------------------------------------------------------------- */
+
+/* Bytes of the workspace tis_causal_prefill needs: the partial means,
+ * B * Hkv * n_keys * depth(n_keys) * d elements of the summary type
+ * (0 if invalid). */
+size_t tis_causal_prefill_workspace_bytes(int batch, int kv_heads, int head_dim, int branching,
+                                          int leaf_block, int n_keys, tis_dtype summary_dtype);
+
+/*
+ * tis_causal_prefill -- every position of the first tree->n_keys keys of a
+ * cache as a query over its own prefix.
+ * tree     a growing-cache tree holding those keys (tis_cache_tree_append),
+ *          n_keys >= 1; K, V the cache it was built over.
+ * Q        [B][Hq][n_keys][d] of type dtype: the query of every position.
+ * O        out: float32 [B][Hq][n_keys][d].
+ * indices  optional: int32 [B][Hq][n_keys][beam], each position's kept
+ *          leaves ascending, -1 padded where its tree has fewer leaves.
+ * workspace: tis_causal_prefill_workspace_bytes() bytes, 16-byte aligned.
+ * Requires beam >= 1, beam * b <= TIS_MAX_CANDIDATES and
+ * B * Hq * n_keys < 2^31.
+ */
+tis_status tis_causal_prefill(const void *Q, const void *K, const void *V, tis_dtype dtype,
+                              int q_heads, const tis_cache_tree *tree, int beam, float scale,
+                              float *O, int32_t *indices, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -423,3 +423,47 @@ def test_threshold_rejects(lib, fused, kw, status):
 ])
 def test_decode_threshold_rejects(lib, kw, status):
     assert _threshold(lib, True, **kw) == status
+
+
+# -------------------------------------------------------- causal prefill --
+
+def test_prefill_workspace_bytes(lib):
+    # 1,024 keys, b 2, L 16: depth 6; one fp32 row per (head, position, height)
+    assert lib.tis_causal_prefill_workspace_bytes(1, 1, 64, 2, 16, 1024, _lib.TIS_F32) == (
+        1024 * 6 * 64 * 4)
+    assert lib.tis_causal_prefill_workspace_bytes(2, 3, 128, 4, 16, 100, _lib.TIS_BF16) == (
+        6 * 100 * 2 * 128 * 2)   # 100 keys: 4^2 * 16 = 256 >= 100, depth 2
+    assert lib.tis_causal_prefill_workspace_bytes(1, 1, 64, 2, 16, 0, _lib.TIS_F32) == 0
+    assert lib.tis_causal_prefill_workspace_bytes(1, 1, 96, 2, 16, 10, _lib.TIS_F32) == 0
+    assert lib.tis_causal_prefill_workspace_bytes(1, 1, 64, 2, 16, 10, 5) == 0
+
+
+def _prefill(lib, tree_kw=None, **kw):
+    t = _ctree(**(tree_kw or dict(n=100, lv=3)))
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, dt=_lib.TIS_BF16, Hq=2, beam=2, scale=0.0, O=FAKE,
+             idx=FAKE, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return lib.tis_causal_prefill(a["Q"], a["K"], a["V"], a["dt"], a["Hq"], ctypes.byref(t),
+                                  a["beam"], a["scale"], a["O"], a["idx"], a["ws"], a["wsb"],
+                                  None)
+
+
+@pytest.mark.parametrize("tree_kw,kw,status", [
+    (None, dict(Q=None), _lib.TIS_E_NULL),
+    (None, dict(ws=None), _lib.TIS_E_NULL),
+    (None, dict(O=None), _lib.TIS_E_NULL),
+    (dict(n=0, lv=0), dict(), _lib.TIS_E_SHAPE),            # empty tree
+    (dict(n=100, lv=2), dict(), _lib.TIS_E_SHAPE),          # wrong depth
+    (None, dict(dt=6), _lib.TIS_E_DTYPE),
+    (dict(n=100, lv=3, sd=4), dict(), _lib.TIS_E_DTYPE),
+    (None, dict(beam=0), _lib.TIS_E_SHAPE),
+    (dict(n=100, lv=3, H=2), dict(Hq=3), _lib.TIS_E_SHAPE),
+    (None, dict(scale=float("nan")), _lib.TIS_E_SHAPE),
+    (None, dict(wsb=100 * 3 * 64 * 4 - 1), _lib.TIS_E_WORKSPACE),
+    (None, dict(ws=FAKE + 4), _lib.TIS_E_ALIGN),
+    (None, dict(O=FAKE + 4), _lib.TIS_E_ALIGN),
+    (None, dict(Hq=1 << 25), _lib.TIS_E_UNSUPPORTED),       # 2^25 heads x 100 positions
+])
+def test_prefill_rejects(lib, tree_kw, kw, status):
+    assert _prefill(lib, tree_kw, **kw) == status
+    assert lib.tis_last_error().decode()

@@ -1,0 +1,110 @@
+"""Parity of causal prefill routing (tis_causal_prefill through the C-ABI)
+with the CPU oracle in oracle/tis_causal_oracle.py: every position's kept
+leaves exactly (positions whose oracle cut gap is below 1e-5 are counted
+instead), every position's output within the input type's tolerance of the
+oracle's attention over the GPU's leaves.
+"""
+from __future__ import annotations
+
+import sys
+import time
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import tis_causal_oracle as C
+from oracle import tis_grow_oracle as GO
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _say(*a):
+    print("[prefill]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def tis():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import tree_indexed_sparse_build_amd as t
+    t.version()
+    return t
+
+
+def _inputs(dtype, B, Hkv, G, N, d, gen, seed, b=2, L=16):
+    lv = GO.depth_for(N, b, L)
+    clusters = b ** lv * L // 64 if gen == "mixture" else 0
+    w = workloads.Workload("prefill", dtype, B, Hkv * G, Hkv, d, b, L, lv, 1, gen,
+                           clusters=clusters, seed=seed)
+    x = workloads.generate(w)
+    rng = np.random.default_rng(seed + 1000)
+    K = np.ascontiguousarray(x["K"][:, :, :N])
+    V = np.ascontiguousarray(x["V"][:, :, :N])
+    # one query per position: the workload's queries plus per-position noise
+    q = workloads.generate(workloads.Workload("prefill_q", dtype, B, Hkv * G, Hkv, d, b, L, lv,
+                                              1, "normal", seed=seed + 7))
+    qf = O_widen(q["Q"], dtype)[:, :, None, :] + rng.standard_normal((B, Hkv * G, N, d))
+    Q = to_storage(qf, dtype)
+    return Q, K, V
+
+
+def O_widen(x, dtype):
+    return workloads.bf16_bits_to_f32(x).astype(np.float64) if dtype == "bf16" else \
+        np.asarray(x, dtype=np.float64)
+
+
+def to_storage(x, dtype):
+    x32 = np.ascontiguousarray(x, dtype=np.float32)
+    return x32 if dtype == "f32" else workloads.f32_to_bf16_bits(x32)
+
+
+CASES = [
+    # (label, dtype, summary type, B, Hkv, G, N, d, b, L, beam, generator)
+    ("alhr_shape", "f32", "f32", 1, 1, 8, 1024, 64, 2, 16, 2, "normal"),
+    ("ragged_bf16_d128", "bf16", "f32", 1, 2, 2, 301, 128, 3, 5, 4, "normal"),
+    ("clustered_bf16", "bf16", "f32", 2, 1, 4, 640, 128, 4, 16, 3, "mixture"),
+    ("bf16_summaries", "bf16", "bf16", 1, 2, 2, 200, 64, 2, 8, 3, "normal"),
+    ("wide_beam", "f32", "f32", 1, 1, 2, 129, 64, 2, 4, 40, "normal"),
+    ("leaf_1", "f32", "f32", 1, 1, 2, 50, 64, 2, 1, 3, "normal"),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_causal_prefill_matches_oracle(tis, case):
+    label, dtype, sd, B, Hkv, G, N, d, b, L, beam, gen = case
+    t0 = time.time()
+    Q, K, V = _inputs(dtype, B, Hkv, G, N, d, gen, seed=N, b=b, L=L)
+    cap = N + 37  # the cache has room past the prefilled keys
+    Kc = np.zeros((B, Hkv, cap, d), dtype=K.dtype)
+    Vc = np.zeros_like(Kc)
+    Kc[:, :, :N], Vc[:, :, :N] = K, V
+    Kd = tis.from_storage(Kc, dtype, "cuda")
+    Vd = tis.from_storage(Vc, dtype, "cuda")
+    Qd = tis.from_storage(Q, dtype, "cuda")
+    ct = tis.CacheTree(Kd, Vd, b, L, summary_dtype=sd)
+    ct.append(N)
+    out, idx = ct.causal_prefill(Qd, beam, return_indices=True)
+    torch.cuda.synchronize()
+    out, idx = out.cpu().numpy(), idx.cpu().numpy()
+    orc = C.causal_prefill(Q, K, V, dtype, b, L, beam, summary_dtype=sd)
+    _say(f"{label}: oracle done in {time.time() - t0:.1f}s")
+    tie = orc["gap"] < parity.TIE_GAP
+    same = np.all(idx == orc["indices"], axis=-1)
+    assert np.all(same | tie), f"{np.count_nonzero(~same & ~tie)} positions keep other leaves"
+    # outputs: the oracle's attention over the GPU's leaves, position by position
+    err = 0.0
+    Bq, Hq = Q.shape[:2]
+    for t in range(N):
+        o_g = GO.grow_attend(np.ascontiguousarray(Q[:, :, t]), K, V, dtype, idx[:, :, t], t + 1, L)
+        err = max(err, parity.compare_outputs(out[:, :, t], o_g, dtype))
+    reads = np.array([[[C.keys_read(idx[bi, h, t], t + 1, L) for t in range(N)]
+                       for h in range(Hq)] for bi in range(Bq)])
+    _say(f"{label}: positions exact {int(same.sum())}/{same.size} (tie-exposed mismatches "
+         f"{int((~same & tie).sum())}); keys read per query {reads.mean():.2f} on average over "
+         f"{N} positions (dense causal: {(N + 1) / 2:.1f}); max-abs {err:.2e}; "
+         f"{time.time() - t0:.1f}s")

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libtis.so")
 SOURCES = ["tis_api.hip", "build.hip", "route.hip", "attend.hip", "decode.hip", "cache.hip",
-           "sphere.hip"]
+           "sphere.hip", "prefill.hip"]
 ARCH = "gfx950"
 
 

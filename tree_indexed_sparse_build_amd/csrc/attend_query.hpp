@@ -48,14 +48,17 @@ template <typename T, int D> __device__ inline uint4 attend_q_raw(const AttendAr
 // taking part (RAGGED: the last block of a growing cache may hold fewer
 // than L keys; THRESH: only keys whose score q.k, computed in fp64, is at
 // least tau take part, and that fp64 score is also the one the softmax
-// uses).  With part == nullptr it writes row qi of O (NaN if `bad`,
+// uses; PREFILL: the query is position t of a causal prefill, its (batch,
+// head) row is hrow and its keys end at nk = t + 1).  With part == nullptr
+// it writes row qi of O (NaN if `bad`,
 // zero if no slot is used); otherwise it writes the workgroup's partial
 // softmax state to part: m (log2 units), l (NaN if `bad`), two pad words,
 // acc[D], for a later log-sum-exp merge with the query's other parts.
-template <typename T, int D, bool RAGGED = false, bool THRESH = false>
+template <typename T, int D, bool RAGGED = false, bool THRESH = false, bool PREFILL = false>
 __device__ void attend_query(const AttendArgs &a, AttendShared<T, D> &sh, int qi,
                              uint4 qraw, const int *slots, const int *use, int nslots,
-                             bool bad, float *part, double tau = 0.0) {
+                             bool bad, float *part, double tau = 0.0, int hrow = 0,
+                             int64_t nk = 0) {
   using AG = AttendGeom<T, D>;
   constexpr int E = AG::E, LPR = AG::LPR, R = AG::R, U = AG::U, RB = AG::RB, REP = AG::REP;
   const int tid = threadIdx.x;
@@ -63,11 +66,13 @@ __device__ void attend_query(const AttendArgs &a, AttendShared<T, D> &sh, int qi
   const int w = tid >> 6;
   const int nw = blockDim.x >> 6;
   const int L = a.leaf_block;
-  const int bi = qi / a.q_heads;
-  const int hq = qi - bi * a.q_heads;
+  const int hr = PREFILL ? hrow : qi;
+  const int bi = hr / a.q_heads;
+  const int hq = hr - bi * a.q_heads;
   const int64_t head = static_cast<int64_t>(bi) * a.kv_heads + hq / a.group;
   const int col = (lane % LPR) * E;
   const int rsub = lane / LPR;
+  const int64_t n_keys = PREFILL ? nk : a.n_keys;
 
   float q[E];
   Vec16<T>::unpack(qraw, q);
@@ -88,7 +93,7 @@ __device__ void attend_query(const AttendArgs &a, AttendShared<T, D> &sh, int qi
     const int64_t blk0 = static_cast<int64_t>(slots[s]) * L;
     const int64_t rowb = blk0 + r0;
     // keys of the block in use: L, or fewer in the last block of a cache
-    const int len = RAGGED ? static_cast<int>(min(static_cast<int64_t>(L), a.n_keys - blk0)) : L;
+    const int len = RAGGED ? static_cast<int>(min(static_cast<int64_t>(L), n_keys - blk0)) : L;
     if (RAGGED && r0 >= len) continue;
     uint4 kv[U], vv[U];
 #pragma unroll

@@ -1,0 +1,163 @@
+// Causal prefill routing: the query at position t routes over the tree of
+// the first t + 1 keys and attends over the keys of its kept leaves up to t
+// ("Vdev-Ctrl Releases ALHR", Summary: keys read per query averaged over the
+// positions of a 1,024-token input; "Subquadratic Attention with a
+// Hierarchical Tree-Structured Indexer", Abstract: the tree over the KV cache
+// deepens as the context grows).  Position t sees the growing-cache tree at
+// n = t + 1: every node to the left of key t is complete and its summary is
+// the one a tree over all n keys stores; only the node holding key t at each
+// height (the open node) covers fewer keys, and its mean differs per t.
+//
+//  * k_prefix_means: for every height h of the tree and every position t,
+//    the mean of the keys from the start of t's height-h node up to t (the
+//    open node's summary as position t sees it), summed in fp64 in key order
+//    and rounded once to the summary type.  One workgroup per (head, height,
+//    block of 64 positions), a thread per column: it first sums the keys of
+//    the node that lie before the block, then walks the block.
+//  * k_prefill: one workgroup per (batch, query head, position).  Thread 0
+//    builds the position's level table (depth, existing nodes, first cut, the
+//    open rows' offsets) in LDS; the walk reads complete nodes from the
+//    cache tree and the open node of each level from the table of partial
+//    means; the attention stops at key t.
+#include "attend_query.hpp"
+#include "route_walk.hpp"
+
+namespace tis {
+namespace {
+
+constexpr int kPrefixRows = 64;   // positions per workgroup of k_prefix_means
+constexpr int kPrefillWaves = 16;
+constexpr int kPrefillWalkWaves = 8;
+
+template <typename T> __device__ inline double elem64(const T *p);
+template <> __device__ inline double elem64<float>(const float *p) { return *p; }
+template <> __device__ inline double elem64<bf16_bits>(const bf16_bits *p) {
+  return __uint_as_float(static_cast<uint32_t>(p->v) << 16);
+}
+
+template <typename T, typename S, int D>
+__global__ void __launch_bounds__(D) k_prefix_means(PrefillArgs a) {
+  const int64_t nblk = (a.positions + kPrefixRows - 1) / kPrefixRows;
+  const int64_t per_head = a.levels * nblk;
+  const int64_t head = blockIdx.x / per_head;
+  const int64_t rem = blockIdx.x - head * per_head;
+  const int h = static_cast<int>(rem / nblk);
+  const int64_t p0 = (rem - h * nblk) * kPrefixRows;
+  const int64_t p1 = min(p0 + static_cast<int64_t>(kPrefixRows), static_cast<int64_t>(a.positions));
+  const int c = threadIdx.x;
+  const uint32_t span = static_cast<uint32_t>(a.h_span[h]);
+  const T *kh = static_cast<const T *>(a.K) + head * a.capacity * D + c;
+  S *pm = static_cast<S *>(a.open_summ);
+
+  // keys of t's node that come before the block
+  const int64_t s0 = (p0 / span) * span;
+  double acc = 0.0;
+  int64_t k = s0;
+  for (; k + 8 <= p0; k += 8) {
+    double v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = elem64<T>(kh + (k + u) * D);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += v[u];
+  }
+  for (; k < p0; ++k) acc += elem64<T>(kh + k * D);
+  uint32_t held = static_cast<uint32_t>(p0 - s0);  // keys of the node summed so far
+  for (int64_t t0 = p0; t0 < p1; t0 += 8) {
+    double v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = t0 + u < p1 ? elem64<T>(kh + (t0 + u) * D) : 0.0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t t = t0 + u;
+      if (t < p1) {
+        if (held == span) {  // t starts a new node
+          acc = 0.0;
+          held = 0;
+        }
+        acc += v[u];
+        ++held;
+        SummaryType<S>::put(pm + ((head * a.positions + t) * a.levels + h) * D + c,
+                            acc / static_cast<double>(held));
+      }
+    }
+  }
+}
+
+template <typename T, typename S, int D>
+__global__ void __launch_bounds__(kPrefillWaves * 64)
+    k_prefill(RouteArgs ra, AttendArgs aa, PrefillArgs pa) {
+  __shared__ RouteShared<kPrefillWaves> rsh;
+  __shared__ AttendShared<T, D> ash;
+  __shared__ CausalLevels cl;
+  const int qi = blockIdx.x;
+  const int hrow = qi / pa.positions;          // (batch, query head)
+  const int t = qi - hrow * pa.positions;      // position
+  const uint4 qraw = attend_q_raw<T, D>(aa, qi);
+  if (threadIdx.x == 0) {
+    const int bi = hrow / ra.q_heads;
+    const int hq = hrow - bi * ra.q_heads;
+    const int64_t head = static_cast<int64_t>(bi) * ra.kv_heads + hq / ra.group;
+    const int64_t n = static_cast<int64_t>(t) + 1;
+    int lv = 1;
+    while (lv < pa.levels && pa.h_span[lv] < n) ++lv;  // fewest levels covering n keys
+    cl.levels = lv;
+    cl.exist[0] = 1;
+    for (int l = 1; l <= lv; ++l) {
+      const int h = lv - l;
+      cl.exist[l] = (n + pa.h_span[h] - 1) / pa.h_span[h];
+      cl.rows[l] = pa.h_rows[h];
+      cl.off[l] = pa.h_off[h];
+      cl.open_off[l] = ((head * pa.positions + t) * pa.levels + h) * D;
+    }
+    cl.exist[lv + 1] = 0;
+    int fc = 1;
+    while (fc < lv && cl.exist[fc] <= ra.beam) ++fc;
+    cl.first_cut = fc;
+  }
+  __syncthreads();
+  const int kept = route_walk<T, S, D, kPrefillWaves, kPrefillWalkWaves, 2>(ra, rsh, qi, &cl,
+                                                                            pa.open_summ, hrow);
+  if (ra.indices) {
+    int32_t *out = ra.indices + static_cast<int64_t>(qi) * ra.beam;
+    write_ascending<kPrefillWaves * 64>(rsh.front, kept, out);
+    for (int k = kept + static_cast<int>(threadIdx.x); k < ra.beam; k += kPrefillWaves * 64)
+      out[k] = -1;
+  }
+  attend_query<T, D, true, false, true>(aa, ash, qi, qraw, rsh.front, nullptr, kept, false,
+                                        nullptr, 0.0, hrow, static_cast<int64_t>(t) + 1);
+}
+
+template <typename T, typename S>
+hipError_t launch_prefill_ts(int head_dim, const RouteArgs &ra, const AttendArgs &aa,
+                             const PrefillArgs &pa, hipStream_t s) {
+  const int64_t nblk = (pa.positions + kPrefixRows - 1) / kPrefixRows;
+  const dim3 g1(static_cast<unsigned>(pa.heads * pa.levels * nblk));
+  const dim3 g2(static_cast<unsigned>(ra.queries));
+  if (head_dim == 128) {
+    hipLaunchKernelGGL((k_prefix_means<T, S, 128>), g1, dim3(128), 0, s, pa);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_prefill<T, S, 128>), g2, dim3(kPrefillWaves * 64), 0, s, ra, aa, pa);
+  } else if (head_dim == 64) {
+    hipLaunchKernelGGL((k_prefix_means<T, S, 64>), g1, dim3(64), 0, s, pa);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_prefill<T, S, 64>), g2, dim3(kPrefillWaves * 64), 0, s, ra, aa, pa);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill(Dt dt, Dt sdt, int head_dim, const RouteArgs &ra, const AttendArgs &aa,
+                          const PrefillArgs &pa, hipStream_t s) {
+  if (dt == Dt::BF16)
+    return sdt == Dt::BF16 ? launch_prefill_ts<bf16_bits, bf16_bits>(head_dim, ra, aa, pa, s)
+                           : launch_prefill_ts<bf16_bits, float>(head_dim, ra, aa, pa, s);
+  return sdt == Dt::BF16 ? launch_prefill_ts<float, bf16_bits>(head_dim, ra, aa, pa, s)
+                         : launch_prefill_ts<float, float>(head_dim, ra, aa, pa, s);
+}
+
+}  // namespace tis

@@ -95,10 +95,24 @@ template <int NW> struct RouteShared {
   int holes[3];                    // holes among a level's candidates, slot l mod 3
 };
 
+// Level table of one causal-prefill query (position t routes over the tree
+// of the first n = t + 1 keys): its depth, first cut level, and per level l
+// the nodes that exist, the summary rows per head and block offset of its
+// height, and the element offset of its open node's row (the node holding
+// key t, whose mean covers keys up to t only) in the table of partial means.
+struct CausalLevels {
+  int levels, first_cut;
+  int64_t exist[kMaxLevels + 2];
+  int64_t rows[kMaxLevels + 1];
+  int64_t off[kMaxLevels + 1];
+  int64_t open_off[kMaxLevels + 1];
+};
+
 // Sizes and summary rows of the levels of one (batch, KV head), walked from
-// level l0 downwards; CACHE selects the growing-cache layout.  Scalar
-// arithmetic only (no argument-table loads).
-template <bool CACHE> struct LevelCursor {
+// level l0 downwards.  LAYOUT 0: full tree (sizes by scalar arithmetic);
+// 1: growing cache (a host table in the arguments); 2: causal prefill (the
+// query's own table, in LDS).
+template <int LAYOUT> struct LevelCursor {
   int64_t exist;   // nodes of the current level that exist
   int64_t rows;    // summary rows per head in the current level's block
   int64_t off;     // element offset of the current level's block
@@ -106,13 +120,15 @@ template <bool CACHE> struct LevelCursor {
   int l;           // current level
   int b;
   const RouteArgs *a;
+  const CausalLevels *cl;
 
-  __device__ void init(const RouteArgs &ra, int l0, int d) {
+  __device__ void init(const RouteArgs &ra, const CausalLevels *c, int l0, int d) {
     a = &ra;
+    cl = c;
     b = ra.branching;
     l = l0;
     heads = static_cast<int64_t>(ra.queries / ra.q_heads) * ra.kv_heads;
-    if constexpr (!CACHE) {
+    if constexpr (LAYOUT == 0) {
       // full tree: level l has b^l nodes, levels 1 .. l-1 come first
       int64_t n = 1;
       off = 0;
@@ -121,28 +137,37 @@ template <bool CACHE> struct LevelCursor {
         off += heads * n * d;
       }
       exist = rows = n * b;
-    } else {
+    } else if constexpr (LAYOUT == 1) {
       // growing cache: sizes and offsets come from the host (no division)
       exist = ra.lvl_exist[l0];
       rows = ra.lvl_rows[l0];
       off = ra.lvl_off[l0];
+    } else {
+      exist = cl->exist[l0];
+      rows = cl->rows[l0];
+      off = cl->off[l0];
     }
   }
   // nodes of the next level down that exist
   __device__ int64_t exist_below() const {
-    if constexpr (!CACHE) return exist * b;
-    return a->lvl_exist[l + 1];
+    if constexpr (LAYOUT == 0) return exist * b;
+    if constexpr (LAYOUT == 1) return a->lvl_exist[l + 1];
+    return cl->exist[l + 1];
   }
   __device__ void down(int d) {
     ++l;
-    if constexpr (!CACHE) {
+    if constexpr (LAYOUT == 0) {
       off += heads * rows * d;
       rows *= b;
       exist = rows;
-    } else {
+    } else if constexpr (LAYOUT == 1) {
       exist = a->lvl_exist[l];
       rows = a->lvl_rows[l];
       off = a->lvl_off[l];
+    } else {
+      exist = cl->exist[l];
+      rows = cl->rows[l];
+      off = cl->off[l];
     }
   }
 };
@@ -159,15 +184,17 @@ template <int NT> __device__ inline void write_ascending(const int *v, int n, in
 }
 
 // Scores the C candidates of one level: candidate p is node node_of(p) of
-// the level (negative: a hole, which reads node 0), and emit(p, node, score)
+// the level (negative: a hole, which reads node 0), whose summary elements
+// for this lane's columns start at row_of(node), and emit(p, node, score)
 // receives its fp64 dot with the query (once per candidate).  The nsw waves
 // of the workgroup cover UU rows per lane per pass, UU just large enough for
 // C, and every load of a pass is issued before any is used: rows past C read
 // candidate 0 again (always a valid address) and their scores are dropped,
 // so no branch splits the loads.  A lane loads 16 bytes of a row: 4 float32
 // or 8 bfloat16 summary elements.
-template <typename T, typename S, int D, int UU, bool HOLES, typename NodeOf, typename Emit>
-__device__ inline void score_rows(const S *sl, int C, NodeOf node_of, Emit emit,
+template <typename T, typename S, int D, int UU, bool HOLES, typename NodeOf, typename RowOf,
+          typename Emit>
+__device__ inline void score_rows(RowOf row_of, int C, NodeOf node_of, Emit emit,
                                   const QRaw<T, Vec16<S>::kElems> &qr, int nsw, int w,
                                   int lane) {
   constexpr int E = Vec16<S>::kElems;
@@ -188,7 +215,7 @@ __device__ inline void score_rows(const S *sl, int C, NodeOf node_of, Emit emit,
 #pragma unroll
     for (int u = 0; u < UU; ++u) {
       const int nd = HOLES && node[u] < 0 ? 0 : node[u];  // a hole reads node 0
-      v[u] = load16(sl + static_cast<int64_t>(nd) * D);
+      v[u] = load16(row_of(nd));
     }
     double q[E];
     qr.widen(q);
@@ -226,8 +253,11 @@ __device__ inline void score_rows(const S *sl, int C, NodeOf node_of, Emit emit,
 // starts about a microsecond after the first), so leaving the late waves out
 // of the walk keeps them off its critical path: they only have to reach
 // each barrier, and the attention after the walk is where they are needed.
-template <typename T, typename S, int D, int NW, int NRW, bool CACHE>
-__device__ int route_walk(const RouteArgs &a, RouteShared<NW> &sh, int qi) {
+template <typename T, typename S, int D, int NW, int NRW, int LAYOUT>
+__device__ int route_walk(const RouteArgs &a, RouteShared<NW> &sh, int qi,
+                          const CausalLevels *cl = nullptr, const void *open_summ = nullptr,
+                          int hrow = -1) {
+  constexpr bool CACHE = LAYOUT != 0;  // nodes past the last key may be missing
   constexpr int NT = NW * 64;
   constexpr int LOG_NRT = NRW == 16 ? 10 : NRW == 8 ? 9 : NRW == 4 ? 8 : -1;
   static_assert(LOG_NRT > 0 && NRW <= NW, "4, 8 or 16 walking waves");
@@ -239,20 +269,22 @@ __device__ int route_walk(const RouteArgs &a, RouteShared<NW> &sh, int qi) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
-  const int bi = qi / a.q_heads;
-  const int hq = qi - bi * a.q_heads;
+  // (batch, query head) row of the query: qi itself, or given (prefill)
+  const int hr = LAYOUT == 2 ? hrow : qi;
+  const int bi = hr / a.q_heads;
+  const int hq = hr - bi * a.q_heads;
   const int64_t head = static_cast<int64_t>(bi) * a.kv_heads + hq / a.group;
   const int b = a.branching;
   const int W = a.beam;
-  const int lv = a.levels;
-  const int l0 = a.first_cut;
+  const int lv = LAYOUT == 2 ? cl->levels : a.levels;
+  const int l0 = LAYOUT == 2 ? cl->first_cut : a.first_cut;
   const int col = (lane % LPR) * E;
 
   QRaw<T, E> qr;
   qr.load(static_cast<const T *>(a.Q) + static_cast<int64_t>(qi) * D + col);
 
-  LevelCursor<CACHE> lc;
-  lc.init(a, l0, D);
+  LevelCursor<LAYOUT> lc;
+  lc.init(a, cl, l0, D);
   if (a.trace) {
     // levels above l0 keep every node that exists
     for (int l = 1; l < l0; ++l) {
@@ -260,7 +292,7 @@ __device__ int route_walk(const RouteArgs &a, RouteShared<NW> &sh, int qi) {
       for (int h = 0; h < lv - l; ++h) span *= b;
       int64_t n = 1;
       for (int k = 0; k < l; ++k) n *= b;
-      const int64_t e = CACHE ? a.lvl_exist[l] : n;
+      const int64_t e = LAYOUT == 2 ? cl->exist[l] : CACHE ? a.lvl_exist[l] : n;
       int32_t *tr = a.trace + (static_cast<int64_t>(qi) * lv + (l - 1)) * W;
       for (int k = tid; k < W; k += NT) tr[k] = k < e ? k : -1;
     }
@@ -276,10 +308,12 @@ __device__ int route_walk(const RouteArgs &a, RouteShared<NW> &sh, int qi) {
   {
     int64_t n_above = 1;
     if (l0 > 1) {
-      if constexpr (!CACHE) {
+      if constexpr (LAYOUT == 0) {
         for (int l = 1; l < l0; ++l) n_above *= b;
-      } else {
+      } else if constexpr (LAYOUT == 1) {
         n_above = a.lvl_exist[l0 - 1];
+      } else {
+        n_above = cl->exist[l0 - 1];
       }
     }
     nf = static_cast<int>(n_above);
@@ -297,6 +331,14 @@ __device__ int route_walk(const RouteArgs &a, RouteShared<NW> &sh, int qi) {
     if (live > W) {
       const int bits = 32 - __clz(static_cast<int>(lc.exist) - 1);
       const S *sl = static_cast<const S *>(a.summ) + lc.off + head * lc.rows * D + col;
+      // prefill: the open node (the last that exists) covers keys up to the
+      // query's position only; its mean comes from the table of partial means
+      const S *open_row = LAYOUT == 2 ? static_cast<const S *>(open_summ) + cl->open_off[l] + col
+                                      : sl;
+      const int64_t last = lc.exist - 1;
+      const auto row_of = [&](int nd) {
+        return LAYOUT == 2 && nd == last ? open_row : sl + static_cast<int64_t>(nd) * D;
+      };
       // the walking waves score, each lane taking `per` rows
       const int per = (C + NRW * RPI - 1) / (NRW * RPI);
       const int *cand = sh.cand[cur];
@@ -309,13 +351,13 @@ __device__ int route_walk(const RouteArgs &a, RouteShared<NW> &sh, int qi) {
       };
       if (w < NRW) {
         if (per <= 1)
-          score_rows<T, S, D, 1, CACHE>(sl, C, node_of, emit, qr, NRW, w, lane);
+          score_rows<T, S, D, 1, CACHE>(row_of, C, node_of, emit, qr, NRW, w, lane);
         else if (per <= 2)
-          score_rows<T, S, D, 2, CACHE>(sl, C, node_of, emit, qr, NRW, w, lane);
+          score_rows<T, S, D, 2, CACHE>(row_of, C, node_of, emit, qr, NRW, w, lane);
         else if (per <= 4)
-          score_rows<T, S, D, 4, CACHE>(sl, C, node_of, emit, qr, NRW, w, lane);
+          score_rows<T, S, D, 4, CACHE>(row_of, C, node_of, emit, qr, NRW, w, lane);
         else
-          score_rows<T, S, D, 8, CACHE>(sl, C, node_of, emit, qr, NRW, w, lane);
+          score_rows<T, S, D, 8, CACHE>(row_of, C, node_of, emit, qr, NRW, w, lane);
       }
       __syncthreads();
       // rank of candidate i = number of candidates with a larger key.  Each

@@ -199,8 +199,8 @@ __device__ int threshold_walk(const RouteArgs &a, const SphereArgs &sa, ThreshSh
   const double qn = sqrt(qq);
   const double tau = static_cast<double>(sa.tau[qi]);
 
-  LevelCursor<false> lc;
-  lc.init(a, 1, D);
+  LevelCursor<0> lc;
+  lc.init(a, nullptr, 1, D);
   if (tid == 0) sh.front[0][0] = 0;  // the root: its children are nodes 0 .. b-1
   __syncthreads();
   int cur = 0, nf = 1;
@@ -225,16 +225,17 @@ __device__ int threshold_walk(const RouteArgs &a, const SphereArgs &sa, ThreshSh
         r = rl[nd];
       }
       const auto emit = [&](int pos, int, double s) { sc[pos] = s; };
+      const auto row_of = [&](int n) { return sl + static_cast<int64_t>(n) * D; };
       const int per = (Cc + NRW * RPI - 1) / (NRW * RPI);
       if (w < NRW) {
         if (per <= 1)
-          score_rows<T, S, D, 1, false>(sl, Cc, node_of, emit, qr, NRW, w, lane);
+          score_rows<T, S, D, 1, false>(row_of, Cc, node_of, emit, qr, NRW, w, lane);
         else if (per <= 2)
-          score_rows<T, S, D, 2, false>(sl, Cc, node_of, emit, qr, NRW, w, lane);
+          score_rows<T, S, D, 2, false>(row_of, Cc, node_of, emit, qr, NRW, w, lane);
         else if (per <= 4)
-          score_rows<T, S, D, 4, false>(sl, Cc, node_of, emit, qr, NRW, w, lane);
+          score_rows<T, S, D, 4, false>(row_of, Cc, node_of, emit, qr, NRW, w, lane);
         else
-          score_rows<T, S, D, 8, false>(sl, Cc, node_of, emit, qr, NRW, w, lane);
+          score_rows<T, S, D, 8, false>(row_of, Cc, node_of, emit, qr, NRW, w, lane);
       }
       __syncthreads();
       const bool pass = tid < Cc && sc[tid] + qn * static_cast<double>(r) >= tau;

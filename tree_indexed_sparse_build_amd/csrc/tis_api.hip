@@ -701,6 +701,95 @@ tis_status tis_cache_tree_decode(const void *Q, const void *K, const void *V, ti
                     "tis_cache_tree_decode launch");
 }
 
+// -------------------------------------------------------- causal prefill --
+
+size_t tis_causal_prefill_workspace_bytes(int batch, int kv_heads, int head_dim, int branching,
+                                          int leaf_block, int n_keys, tis_dtype summary_dtype) {
+  if (batch < 1 || kv_heads < 1 || (head_dim != 64 && head_dim != 128) || branching < 2 ||
+      branching > tis::kMaxBranching || leaf_block < 1 || n_keys < 1 ||
+      (summary_dtype != TIS_F32 && summary_dtype != TIS_BF16))
+    return 0;
+  const int lv = cache_depth(n_keys, branching, leaf_block);
+  if (lv < 1) return 0;
+  const double bytes = static_cast<double>(batch) * kv_heads * n_keys * lv * head_dim *
+                       summary_elem_bytes(summary_dtype);
+  if (bytes > 9.0e18) return 0;
+  return static_cast<size_t>(batch) * kv_heads * static_cast<size_t>(n_keys) * lv * head_dim *
+         summary_elem_bytes(summary_dtype);
+}
+
+tis_status tis_causal_prefill(const void *Q, const void *K, const void *V, tis_dtype dtype,
+                              int q_heads, const tis_cache_tree *tree, int beam, float scale,
+                              float *O, int32_t *indices, void *workspace, size_t workspace_bytes,
+                              void *stream) {
+  if (!Q || !K || !V || !O || !workspace)
+    return fail(TIS_E_NULL, "tis_causal_prefill: Q, K, V, O and workspace are required");
+  CacheGeometry g;
+  int64_t queries = 0;
+  tis_status st = check_cache_query("tis_causal_prefill", Q, dtype, q_heads, tree, beam, &g,
+                                    &queries);
+  if (st != TIS_OK) return st;
+  if (!(scale == scale) || isinf(scale))
+    return fail(TIS_E_SHAPE, "tis_causal_prefill: scale must be finite");
+  const int64_t positions = tree->n_keys;
+  const int64_t pq = queries * positions;  // one query per (batch, head, position)
+  if (pq > 0x7fffffffLL)
+    return fail(TIS_E_UNSUPPORTED, "tis_causal_prefill: %lld queries (batch * q_heads * n_keys) "
+                "exceed 2^31 - 1", (long long)pq);
+  const size_t need = tis_causal_prefill_workspace_bytes(
+      tree->batch, tree->kv_heads, tree->head_dim, tree->branching, tree->leaf_block,
+      tree->n_keys, static_cast<tis_dtype>(tree->summary_dtype));
+  if (workspace_bytes < need)
+    return fail(TIS_E_WORKSPACE, "tis_causal_prefill: workspace of %zu bytes required, %zu given",
+                need, workspace_bytes);
+  if (!aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(workspace, 16) ||
+      (indices && !aligned(indices, 4)))
+    return fail(TIS_E_ALIGN, "tis_causal_prefill: K, V, O and workspace need 16-byte, indices "
+                             "4-byte alignment");
+  tis::RouteArgs ra = cache_route_args(Q, tree, q_heads, beam, indices, nullptr, queries);
+  ra.queries = static_cast<int>(pq);
+  tis::PrefillArgs pa{};
+  pa.K = K;
+  pa.open_summ = workspace;
+  pa.heads = g.heads;
+  pa.capacity = tree->capacity;
+  pa.positions = tree->n_keys;
+  pa.levels = tree->levels;
+  {
+    int64_t span = tree->leaf_block, off = 0;
+    for (int h = 0; h <= tis::kMaxLevels; ++h) {
+      pa.h_span[h] = span;
+      pa.h_rows[h] = h < g.heights ? (tree->capacity + span - 1) / span : 0;
+      pa.h_off[h] = off;
+      if (h < g.heights) off += g.heads * pa.h_rows[h] * tree->head_dim;
+      if (span <= (int64_t{1} << 40)) span *= tree->branching;
+    }
+  }
+  const double sc =
+      scale > 0.f ? static_cast<double>(scale) : 1.0 / sqrt(static_cast<double>(tree->head_dim));
+  tis::AttendArgs aa{};
+  aa.Q = Q;
+  aa.K = K;
+  aa.V = V;
+  aa.indices = nullptr;
+  aa.O = O;
+  aa.splits = 1;
+  aa.part = nullptr;
+  aa.queries = static_cast<int>(pq);
+  aa.n_keys = tree->n_keys;
+  aa.key_stride = tree->capacity;
+  aa.q_heads = q_heads;
+  aa.kv_heads = tree->kv_heads;
+  aa.group = q_heads / tree->kv_heads;
+  aa.leaf_block = tree->leaf_block;
+  aa.beam = beam;
+  aa.n_blocks = (static_cast<int64_t>(tree->n_keys) + tree->leaf_block - 1) / tree->leaf_block;
+  aa.scale_log2 = static_cast<float>(sc * 1.4426950408889634);
+  return hip_status(tis::launch_prefill(to_dt(dtype), to_dt(tree->summary_dtype), tree->head_dim,
+                                        ra, aa, pa, static_cast<hipStream_t>(stream)),
+                    "tis_causal_prefill launch");
+}
+
 // ------------------------------------------------------ bounding spheres --
 
 namespace {

@@ -186,6 +186,26 @@ hipError_t launch_route_threshold(Dt dt, Dt sdt, int head_dim, const RouteArgs &
 hipError_t launch_decode_threshold(Dt dt, Dt sdt, int head_dim, const RouteArgs &ra,
                                    const SphereArgs &sa, const AttendArgs &aa, hipStream_t s);
 
+// -------------------------------------------------------- causal prefill --
+// Every position t of a growing cache's first `positions` keys is a query
+// over the tree of the first t + 1 keys.  open_summ holds, for every
+// (head, position, height < levels), the mean of the keys of t's node up to
+// t; complete nodes come from the cache tree's height-major summaries.
+struct PrefillArgs {
+  const void *K;             // the cache's keys [heads][capacity][d]
+  void *open_summ;           // [heads][positions][levels][d], the summary type
+  int64_t heads;             // B * Hkv
+  int64_t capacity;
+  int positions;             // keys in the tree = queries per (batch, head)
+  int levels;                // depth of the tree over all positions
+  int64_t h_span[kMaxLevels + 1];  // keys under a node of height h: L b^h
+  int64_t h_rows[kMaxLevels + 1];  // summary rows per head of height h
+  int64_t h_off[kMaxLevels + 1];   // element offset of height h's block
+};
+
+hipError_t launch_prefill(Dt dt, Dt sdt, int head_dim, const RouteArgs &ra, const AttendArgs &aa,
+                          const PrefillArgs &pa, hipStream_t s);
+
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace tis

@@ -479,6 +479,36 @@ class CacheTree:
                                          _stream(Q.device)))
         return (idx, tr) if trace else idx
 
+    def causal_prefill(self, Q: torch.Tensor, beam: int, scale: Optional[float] = None,
+                       return_indices: bool = False, out: Optional[torch.Tensor] = None):
+        """Every position t < n_keys as a query over the tree of the first
+        t + 1 keys, attending causally.  Q: [B, Hq, n_keys, d], the query of
+        each position.  Returns O (float32 [B, Hq, n_keys, d]) and, with
+        return_indices=True, the kept leaves (int32 [B, Hq, n_keys, beam],
+        ascending, -1 padded)."""
+        _need_device(Q)
+        if Q.dtype != self.K.dtype:
+            raise TypeError("Q must have the cache's dtype")
+        if Q.dim() != 4 or Q.shape[2] != self.n_keys:
+            raise ValueError("Q must be [B, Hq, n_keys, d]")
+        B, Hq, n, d = Q.shape
+        O = out if out is not None else torch.empty((B, Hq, n, d), dtype=torch.float32,
+                                                     device=Q.device)
+        _check_buffer(O, (B, Hq, n, d), torch.float32, "out")
+        idx = (torch.empty((B, Hq, n, beam), dtype=torch.int32, device=Q.device)
+               if return_indices else None)
+        c = self.c
+        L = lib()
+        wsb = L.tis_causal_prefill_workspace_bytes(c.batch, c.kv_heads, c.head_dim, c.branching,
+                                                   c.leaf_block, c.n_keys, c.summary_dtype)
+        ws = _workspace(Q.device, "prefill", wsb)
+        check(L.tis_causal_prefill(Q.data_ptr(), self.K.data_ptr(), self.V.data_ptr(), self.dt,
+                                   Hq, ctypes.byref(c), beam,
+                                   0.0 if scale is None else float(scale), O.data_ptr(),
+                                   idx.data_ptr() if idx is not None else None, ws.data_ptr(),
+                                   ws.numel(), _stream(Q.device)))
+        return (O, idx) if return_indices else O
+
     def bind_decode(self, Q: torch.Tensor, beam: int, out: torch.Tensor,
                     scale: Optional[float] = None):
         """A zero-argument callable that decodes Q into `out` on the current
