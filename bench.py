@@ -221,6 +221,34 @@ def threshold_retrieval(tis, torch, w, Q, K, V, reps, warmup, k_ranks=(64, 512))
     return out
 
 
+def causal_prefill_bench(tis, torch, w, Q, K, V, reps, warmup, max_positions=4096):
+    """Causal prefill of the first P = min(N, max_positions) keys: every
+    position a query over the tree of its prefix (queries: the workload's,
+    one per head, plus seeded per-position noise).  Times the whole call
+    (partial means + routing + causal attention) and counts the keys each
+    query reads."""
+    P = min(w.n_keys, max_positions)
+    g = torch.Generator(device=Q.device).manual_seed(1234)
+    qf = Q.float()[:, :, None, :] + torch.randn((w.batch, w.q_heads, P, w.head_dim),
+                                                generator=g, device=Q.device)
+    Qp = qf.to(Q.dtype).contiguous()
+    ct = tis.CacheTree(K, V, w.branching, w.leaf_block)
+    ct.append(P)
+    out = torch.empty((w.batch, w.q_heads, P, w.head_dim), dtype=torch.float32, device=Q.device)
+    _, idx = ct.causal_prefill(Qp, w.beam, return_indices=True)
+    for _ in range(warmup):
+        ct.causal_prefill(Qp, w.beam, out=out)
+    reps = max(3, min(reps, 20))
+    t = per_launch(torch, lambda: ct.causal_prefill(Qp, w.beam, out=out), reps)
+    pos = torch.arange(P, device=Q.device).view(1, 1, P, 1)
+    blk = idx.long()
+    size = torch.clamp(pos + 1 - blk * w.leaf_block, max=w.leaf_block)
+    reads = torch.where(blk >= 0, size, torch.zeros_like(size)).sum(-1).double()
+    queries = w.batch * w.q_heads * P
+    return {"positions": P, "queries": queries, "us": t * 1e6, "queries_per_s": queries / t,
+            "keys_read_mean": float(reads.mean()), "dense_causal_keys_mean": (P + 1) / 2}
+
+
 def cache_states(torch, dev, plan, reps, back_to_back):
     """Durations in two cache states.  cold: 1 GiB read first, which leaves
     none of the inputs in the Infinity Cache or an L2 and no dirty lines to
@@ -321,6 +349,8 @@ def main(argv=None):
                     help="skip the measurement of the step with bfloat16 summaries")
     ap.add_argument("--no-threshold", action="store_true",
                     help="skip the bounding-sphere threshold retrieval measurement")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the causal prefill measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 256 MiB device-to-device copy first (the reference "
                          "dispatch for scaling HBM byte counters)")
@@ -468,6 +498,14 @@ def main(argv=None):
         f"GB/s, {dec_bytes / states['decode_cold_us'] / 1e3 / HBM_PEAK_GBS:.1%}), steady "
         f"{states['decode_steady_us']:.2f} us")
 
+    pre = None
+    if not args.no_prefill:
+        pre = causal_prefill_bench(tis, torch, w, Q, K, V, K_, args.warmup)
+        log(f"causal prefill of the first {pre['positions']} keys ({pre['queries']} queries): "
+            f"{pre['us']:.1f} us -> {pre['queries_per_s']:.3e} queries/s; keys read per query "
+            f"{pre['keys_read_mean']:.2f} on average (dense causal "
+            f"{pre['dense_causal_keys_mean']:.1f})")
+
     thr = None
     if not args.no_threshold:
         thr = threshold_retrieval(tis, torch, w, Q, K, V, K_, args.warmup)
@@ -545,6 +583,7 @@ def main(argv=None):
         "cache_decode_loop": cache,
         "bf16_summaries": bf,
         "threshold_retrieval": thr,
+        "causal_prefill": pre,
     }
     print(json.dumps(line), flush=True)
     return 0
