@@ -71,6 +71,8 @@ CASES = [
     ("bf16_summaries", "bf16", "bf16", 1, 2, 2, 200, 64, 2, 8, 3, "normal"),
     ("wide_beam", "f32", "f32", 1, 1, 2, 129, 64, 2, 4, 40, "normal"),
     ("leaf_1", "f32", "f32", 1, 1, 2, 50, 64, 2, 1, 3, "normal"),
+    # more than 128 candidates a level (8-wave workgroups)
+    ("cand_160", "bf16", "f32", 1, 2, 2, 700, 128, 8, 4, 20, "normal"),
 ]
 
 

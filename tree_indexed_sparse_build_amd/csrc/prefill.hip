@@ -14,7 +14,10 @@
 //    and rounded once to the summary type.  One workgroup per (head, height,
 //    block of 64 positions), a thread per column: it first sums the keys of
 //    the node that lie before the block, then walks the block.
-//  * k_prefill: one workgroup per (batch, query head, position).  Thread 0
+//  * k_prefill: one workgroup per (batch, query head, position), of 4 waves
+//    when a level has at most 128 candidates (beam * b), else 8: a prefill
+//    query reads few keys, so small workgroups keep more positions in
+//    flight on each CU (measured: 8 waves 1.5-1.8x the rate of 16).  Thread 0
 //    builds the position's level table (depth, existing nodes, first cut, the
 //    open rows' offsets) in LDS; the walk reads complete nodes from the
 //    cache tree and the open node of each level from the table of partial
@@ -26,8 +29,6 @@ namespace tis {
 namespace {
 
 constexpr int kPrefixRows = 64;   // positions per workgroup of k_prefix_means
-constexpr int kPrefillWaves = 16;
-constexpr int kPrefillWalkWaves = 8;
 
 template <typename T> __device__ inline double elem64(const T *p);
 template <> __device__ inline double elem64<float>(const float *p) { return *p; }
@@ -83,10 +84,9 @@ __global__ void __launch_bounds__(D) k_prefix_means(PrefillArgs a) {
   }
 }
 
-template <typename T, typename S, int D>
-__global__ void __launch_bounds__(kPrefillWaves * 64)
-    k_prefill(RouteArgs ra, AttendArgs aa, PrefillArgs pa) {
-  __shared__ RouteShared<kPrefillWaves> rsh;
+template <typename T, typename S, int D, int NW>
+__global__ void __launch_bounds__(NW * 64) k_prefill(RouteArgs ra, AttendArgs aa, PrefillArgs pa) {
+  __shared__ RouteShared<NW> rsh;
   __shared__ AttendShared<T, D> ash;
   __shared__ CausalLevels cl;
   const int qi = blockIdx.x;
@@ -115,38 +115,38 @@ __global__ void __launch_bounds__(kPrefillWaves * 64)
     cl.first_cut = fc;
   }
   __syncthreads();
-  const int kept = route_walk<T, S, D, kPrefillWaves, kPrefillWalkWaves, 2>(ra, rsh, qi, &cl,
-                                                                            pa.open_summ, hrow);
+  const int kept = route_walk<T, S, D, NW, NW, 2, NW * 32>(ra, rsh, qi, &cl, pa.open_summ, hrow);
   if (ra.indices) {
     int32_t *out = ra.indices + static_cast<int64_t>(qi) * ra.beam;
-    write_ascending<kPrefillWaves * 64>(rsh.front, kept, out);
-    for (int k = kept + static_cast<int>(threadIdx.x); k < ra.beam; k += kPrefillWaves * 64)
-      out[k] = -1;
+    write_ascending<NW * 64>(rsh.front, kept, out);
+    for (int k = kept + static_cast<int>(threadIdx.x); k < ra.beam; k += NW * 64) out[k] = -1;
   }
   attend_query<T, D, true, false, true>(aa, ash, qi, qraw, rsh.front, nullptr, kept, false,
                                         nullptr, 0.0, hrow, static_cast<int64_t>(t) + 1);
 }
 
-template <typename T, typename S>
-hipError_t launch_prefill_ts(int head_dim, const RouteArgs &ra, const AttendArgs &aa,
-                             const PrefillArgs &pa, hipStream_t s) {
+template <typename T, typename S, int D>
+hipError_t launch_prefill_d(const RouteArgs &ra, const AttendArgs &aa, const PrefillArgs &pa,
+                            hipStream_t s) {
   const int64_t nblk = (pa.positions + kPrefixRows - 1) / kPrefixRows;
   const dim3 g1(static_cast<unsigned>(pa.heads * pa.levels * nblk));
   const dim3 g2(static_cast<unsigned>(ra.queries));
-  if (head_dim == 128) {
-    hipLaunchKernelGGL((k_prefix_means<T, S, 128>), g1, dim3(128), 0, s, pa);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_prefill<T, S, 128>), g2, dim3(kPrefillWaves * 64), 0, s, ra, aa, pa);
-  } else if (head_dim == 64) {
-    hipLaunchKernelGGL((k_prefix_means<T, S, 64>), g1, dim3(64), 0, s, pa);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_prefill<T, S, 64>), g2, dim3(kPrefillWaves * 64), 0, s, ra, aa, pa);
-  } else {
-    return hipErrorInvalidValue;
-  }
+  hipLaunchKernelGGL((k_prefix_means<T, S, D>), g1, dim3(D), 0, s, pa);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (ra.beam * ra.branching <= 4 * 32)
+    hipLaunchKernelGGL((k_prefill<T, S, D, 4>), g2, dim3(4 * 64), 0, s, ra, aa, pa);
+  else
+    hipLaunchKernelGGL((k_prefill<T, S, D, 8>), g2, dim3(8 * 64), 0, s, ra, aa, pa);
   return hipGetLastError();
+}
+
+template <typename T, typename S>
+hipError_t launch_prefill_ts(int head_dim, const RouteArgs &ra, const AttendArgs &aa,
+                             const PrefillArgs &pa, hipStream_t s) {
+  if (head_dim == 128) return launch_prefill_d<T, S, 128>(ra, aa, pa, s);
+  if (head_dim == 64) return launch_prefill_d<T, S, 64>(ra, aa, pa, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace

@@ -253,7 +253,8 @@ __device__ inline void score_rows(RowOf row_of, int C, NodeOf node_of, Emit emit
 // starts about a microsecond after the first), so leaving the late waves out
 // of the walk keeps them off its critical path: they only have to reach
 // each barrier, and the attention after the walk is where they are needed.
-template <typename T, typename S, int D, int NW, int NRW, int LAYOUT>
+template <typename T, typename S, int D, int NW, int NRW, int LAYOUT,
+          int MAXC = kMaxCandidates>
 __device__ int route_walk(const RouteArgs &a, RouteShared<NW> &sh, int qi,
                           const CausalLevels *cl = nullptr, const void *open_summ = nullptr,
                           int hrow = -1) {
@@ -261,7 +262,10 @@ __device__ int route_walk(const RouteArgs &a, RouteShared<NW> &sh, int qi,
   constexpr int NT = NW * 64;
   constexpr int LOG_NRT = NRW == 16 ? 10 : NRW == 8 ? 9 : NRW == 4 ? 8 : -1;
   static_assert(LOG_NRT > 0 && NRW <= NW, "4, 8 or 16 walking waves");
-  static_assert(kMaxCandidates <= NRW * 64 / 2, "two or more threads per candidate");
+  // MAXC: the most candidates a level of this launch may have (beam * b,
+  // checked by the host); the ranking needs two or more threads for each
+  static_assert(MAXC <= kMaxCandidates && MAXC <= NRW * 64 / 2,
+                "two or more threads per candidate");
   constexpr int E = Vec16<S>::kElems;  // summary elements per lane (16 bytes)
   constexpr int LPR = D / E;           // lanes per summary row
   constexpr int RPI = 64 / LPR;        // rows per wave-wide load
