@@ -21,7 +21,8 @@ the design notes of the repository):
   * summary of a node = arithmetic mean of the keys under it, computed exactly
     and rounded once to float32 (the stored summary), or, for reduced-precision
     summaries, rounded once, straight from the exact mean, to bfloat16 (round
-    to nearest, ties to even; never through float32, which would round twice);
+    to nearest, ties to even; never through float32, which would round twice),
+    or to fp8 e4m3 with a power-of-two scale per node (round_summary);
   * levels = branchings below the root; leaves = branching**levels contiguous
     blocks of leaf_block keys; the root is implicit and never scored;
   * node score = plain dot product q . summary (fp64, no scale);
@@ -40,7 +41,8 @@ from typing import Dict, List, Optional, Sequence
 
 import numpy as np
 
-__all__ = ["widen", "round_summary", "tree_build", "tree_route", "tree_attend", "decode"]
+__all__ = ["widen", "round_summary", "round_e4m3", "fp8_scale_exponent", "tree_build",
+           "tree_route", "tree_attend", "decode"]
 
 
 # ---------------------------------------------------------------------------
@@ -64,16 +66,48 @@ def widen(x: np.ndarray, dtype: str) -> np.ndarray:
 # rounding of the exact means to the stored summary type
 # ---------------------------------------------------------------------------
 
+_E4M3_SIG_BITS = 4            # significant bits of an fp8 e4m3 value (3 stored + 1)
+_E4M3_MIN_QUANTUM_EXP = -9    # spacing of e4m3 subnormals: 2^-9
+_E4M3_MAX = 448.0             # largest finite e4m3 value (1.75 * 2^8)
+_FP8_SCALE_EXP_RANGE = (-126, 127)   # the scale 2^e is a normal float32
 _BF16_SIG_BITS = 8            # significant bits of a bfloat16 (7 stored + 1)
 _BF16_MIN_QUANTUM_EXP = -133  # spacing of bfloat16 subnormals: 2^-133
 _BF16_OVERFLOW = 2.0 ** 128   # the first power of two past the largest bfloat16
+
+
+def fp8_scale_exponent(amax: np.ndarray) -> np.ndarray:
+    """Per row, the smallest integer e with amax * 2^-e <= 448 (the largest
+    e4m3 value), so the row's largest magnitude lands in (224, 448]; 0 for an
+    all-zero row; clamped to [-126, 127] so that 2^e is a normal float32.
+    With amax = f * 2^k, 0.5 <= f < 1, and 448 = 0.875 * 2^9: e = k - 9 when
+    f <= 0.875, else k - 8."""
+    amax = np.asarray(amax, dtype=np.float64)
+    f, k = np.frexp(amax)
+    e = np.where(f <= 0.875, k - 9, k - 8)
+    e = np.where(amax == 0, 0, e)
+    return np.clip(e, *_FP8_SCALE_EXP_RANGE).astype(np.int64)
+
+
+def round_e4m3(x: np.ndarray) -> np.ndarray:
+    """Round to nearest even on the fp8 e4m3 grid (4 significant bits; below
+    2^-6 the fixed subnormal spacing 2^-9), for |x| <= 448, from float64."""
+    x = np.asarray(x, dtype=np.float64)
+    if np.any(np.abs(x) > _E4M3_MAX):
+        raise ValueError("e4m3 rounding needs |x| <= 448")
+    ax = np.abs(x)
+    _, e = np.frexp(ax)
+    q = np.maximum(e - _E4M3_SIG_BITS, _E4M3_MIN_QUANTUM_EXP)
+    return np.copysign(np.ldexp(np.rint(np.ldexp(ax, -q)), q), x)
 
 
 def round_summary(x: np.ndarray, summary_dtype: str) -> np.ndarray:
     """Exact float64 values rounded once to the stored summary type, returned
     as float32 (every bfloat16 value is a float32 value).
 
-    "f32": IEEE round to nearest even.  "bf16": round to nearest even on the
+    "f32": IEEE round to nearest even.  "fp8": each row (the last axis, one
+    node's summary) is scaled by 2^-e, e = fp8_scale_exponent(its largest
+    magnitude), rounded once to e4m3 (round_e4m3) and scaled back: the stored
+    value code * 2^e, exact in float32.  "bf16": round to nearest even on the
     bfloat16 grid (8 significant bits; below 2^-126 the fixed subnormal spacing
     2^-133), taken directly from the float64 value: x = m * 2^e with
     0.5 <= |m| < 1 lies on a grid of spacing 2^(e-8), so x / spacing is rounded
@@ -83,6 +117,9 @@ def round_summary(x: np.ndarray, summary_dtype: str) -> np.ndarray:
     x = np.asarray(x, dtype=np.float64)
     if summary_dtype == "f32":
         return x.astype(np.float32)
+    if summary_dtype == "fp8":
+        e = fp8_scale_exponent(np.abs(x).max(axis=-1))[..., None]
+        return np.ldexp(round_e4m3(np.ldexp(x, -e)), e).astype(np.float32)
     if summary_dtype != "bf16":
         raise ValueError(f"unknown summary dtype {summary_dtype!r}")
     ax = np.abs(x)

@@ -1,8 +1,9 @@
-"""Pins of the oracle's reduced-precision summaries (bfloat16 storage of the
-exact node means, rounded once).
+"""Pins of the oracle's reduced-precision summaries (bfloat16, and fp8 e4m3
+with a power-of-two scale per node, of the exact node means, rounded once).
 
-The rounding is pinned against torch's float32 -> bfloat16 conversion (round
-to nearest even, a library routine independent of the oracle) on values that
+The rounding is pinned against torch's float32 -> bfloat16 and float32 ->
+float8_e4m3fn conversions (round to nearest even, library routines
+independent of the oracle) on values that
 are float32 numbers, where one rounding from float64 and one from float32 are
 the same operation; against hand-built ties and a double-rounding witness for
 values that are not; and against closed-form node means for the build.
@@ -97,7 +98,7 @@ def test_f32_summaries_are_plain_float32_rounding():
     x = np.random.default_rng(2).standard_normal(1000)
     assert np.array_equal(O.round_summary(x, "f32"), x.astype(np.float32))
     with pytest.raises(ValueError):
-        O.round_summary(x, "fp8")
+        O.round_summary(x, "fp16")
 
 
 @pytest.mark.parametrize("b,L,lv", [(2, 16, 6), (8, 64, 2), (3, 5, 3)])
@@ -147,3 +148,89 @@ def test_grow_build_bf16_partial_nodes():
             hi = np.minimum(lo + M, n)
             closed = ((lo + hi - 1) / 2)[:, None] + np.arange(d)[None, :]
             assert np.array_equal(g["stored"][l - 1][0, 0], _torch_bf16(closed.astype(np.float32)))
+
+
+# ------------------------------------------------------------ fp8 e4m3 --
+
+def _torch_e4m3(x32: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32)).to(
+        torch.float8_e4m3fn).to(torch.float32).numpy()
+
+
+def test_e4m3_equals_torch_on_float32_values():
+    rng = np.random.default_rng(21)
+    x = np.concatenate([
+        rng.uniform(-448, 448, 20000),
+        rng.standard_normal(20000) * 2.0 ** rng.integers(-12, 8, 20000),
+        # ties on the e4m3 grid of [1, 2): k/8 + 1/16
+        1 + (np.arange(8) * 2 + 1) / 16.0,
+        # subnormal range and the smallest values
+        rng.uniform(-2.0 ** -6, 2.0 ** -6, 2000), [2.0 ** -10, 3 * 2.0 ** -11, 448.0, -448.0, 0.0],
+    ]).astype(np.float32)
+    x = x[np.abs(x) <= 448]
+    got = O.round_e4m3(x.astype(np.float64)).astype(np.float32)
+    assert np.array_equal(got, _torch_e4m3(x))
+    with pytest.raises(ValueError):
+        O.round_e4m3(np.array([449.0]))
+
+
+def test_e4m3_rounds_once_from_float64():
+    """1 + 2^-4 + 2^-30 lies just above the midpoint of 1 and 1.125: it rounds
+    up; through float32 it would become the midpoint and round to even, 1."""
+    x = np.array([1 + 2.0 ** -4 + 2.0 ** -30])
+    assert O.round_e4m3(x)[0] == 1.125
+    assert _torch_e4m3(x.astype(np.float32))[0] == 1.0
+    # and as a node summary (a row whose scale is 2^0 because of the 448)
+    row = np.array([[1 + 2.0 ** -4 + 2.0 ** -30, 448.0]])
+    assert np.array_equal(O.round_summary(row, "fp8"), np.array([[1.125, 448.0]], dtype=np.float32))
+
+
+def test_fp8_scale_is_the_smallest_that_fits():
+    rng = np.random.default_rng(22)
+    amax = np.concatenate([rng.uniform(0, 1, 5000) * 2.0 ** rng.integers(-60, 60, 5000),
+                           448.0 * 2.0 ** np.arange(-5, 6), [448.0 * (1 + 2.0 ** -40)]])
+    e = O.fp8_scale_exponent(amax)
+    assert np.all(np.ldexp(amax, -e) <= 448)
+    assert np.all(np.ldexp(amax, -(e - 1)) > 448)
+    assert O.fp8_scale_exponent(np.array([0.0]))[0] == 0
+    assert O.fp8_scale_exponent(np.array([1e-300]))[0] == -126   # clamped: 2^e stays normal
+
+
+def test_fp8_summaries_are_per_row_and_scale_equivariant():
+    rng = np.random.default_rng(23)
+    m = rng.standard_normal((6, 32)) * 0.1
+    s = O.round_summary(m, "fp8")
+    # each row: code * 2^e with the row's own e, codes on the e4m3 grid
+    e = O.fp8_scale_exponent(np.abs(m).max(axis=1))
+    codes = np.ldexp(s.astype(np.float64), -e[:, None])
+    assert np.array_equal(O.round_e4m3(codes), codes)
+    assert np.all(np.abs(codes).max(axis=1) > 224)   # the largest lands in (224, 448]
+    # scaling one row by a power of two scales its stored values exactly
+    m2 = m.copy()
+    m2[2] *= 2.0 ** 13
+    s2 = O.round_summary(m2, "fp8")
+    assert np.array_equal(s2[2].astype(np.float64), s[2].astype(np.float64) * 2.0 ** 13)
+    assert np.array_equal(np.delete(s2, 2, axis=0), np.delete(s, 2, axis=0))
+    # half-spacing error bound: 2^(k-5) for |x| = f 2^k, at least 2^-10 before scaling back
+    _, k = np.frexp(np.abs(np.ldexp(m, -e[:, None])))
+    bound = np.ldexp(1.0, np.maximum(k - 5, -10) + e[:, None])
+    assert np.all(np.abs(s - m) <= bound)
+    assert np.array_equal(O.round_summary(np.zeros((2, 8)), "fp8"), np.zeros((2, 8)))
+
+
+@pytest.mark.parametrize("b,L,lv", [(2, 16, 4), (8, 64, 2)])
+def test_build_fp8_summaries_position_keys(b, L, lv):
+    """Position keys: node means are the closed form (lo + hi - 1) / 2 + i,
+    float32 numbers; each node's fp8 summary is torch's e4m3 rounding of the
+    row scaled by its power of two."""
+    N, d = b ** lv * L, 8
+    t = np.arange(N, dtype=np.float64)[:, None] + np.arange(d)[None, :]
+    K = t.astype(np.float32)[None, None]
+    tree = O.tree_build(K, "f32", b, L, lv, summary_dtype="fp8")
+    for l in range(1, lv + 1):
+        M = N // b ** l
+        lo = np.arange(b ** l) * M
+        closed = ((2 * lo + M - 1) / 2)[:, None] + np.arange(d)[None, :]
+        e = O.fp8_scale_exponent(np.abs(closed).max(axis=1))[:, None]
+        want = np.ldexp(_torch_e4m3(np.ldexp(closed, -e).astype(np.float32)).astype(np.float64), e)
+        assert np.array_equal(tree["stored"][l - 1][0, 0], want.astype(np.float32))
