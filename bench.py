@@ -29,16 +29,21 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(w, summary_bytes: int = 4):
+SUMMARY_ROW_BYTES = {"f32": lambda d: 4 * d, "bf16": lambda d: 2 * d,
+                     "fp8": lambda d: d + 4}   # fp8: the codes and the row's scale
+
+
+def algorithmic_bytes(w, summary_dtype: str = "f32"):
     """Bytes the method must move (see the byte model in the design notes);
-    summary_bytes: 4 for float32 summaries, 2 for bfloat16."""
+    a summary row is 4d bytes as float32, 2d as bfloat16, d + 4 as fp8."""
     s = w.elem_bytes
     d, b, W, L = w.head_dim, w.branching, w.beam, w.leaf_block
     heads = w.batch * w.kv_heads
     nodes = sum(b ** l for l in range(1, w.levels + 1))
-    build = heads * (w.n_keys * d * s + nodes * d * summary_bytes)
+    row = SUMMARY_ROW_BYTES[summary_dtype](d)
+    build = heads * (w.n_keys * d * s + nodes * row)
     cand = b + sum(min(W, b ** (l - 1)) * b for l in range(2, w.levels + 1))
-    route_q = cand * d * summary_bytes + d * s + 4 * W
+    route_q = cand * row + d * s + 4 * W
     attend_q = W * L * d * s * 2 + d * s + 4 * W + 4 * d
     return {"build": build, "route": w.queries * route_q, "attend": w.queries * attend_q,
             "candidates_per_query": cand}
@@ -155,12 +160,13 @@ def per_launch(torch, fn, reps):
     return e0.elapsed_time(e1) * 1e-3 / reps
 
 
-def bf16_summaries(tis, torch, w, Q, K, V, reps, warmup):
-    """The step with summaries stored as bfloat16 (the same means rounded
-    once to bfloat16): build and fused decode durations, and the decode's
-    rate on its own algorithmic bytes (each routing level reads half)."""
+def reduced_summaries(tis, torch, w, Q, K, V, reps, warmup, summary_dtype):
+    """The step with summaries stored as bfloat16 or fp8 (the same means
+    rounded once to the narrower type): build and fused decode durations, and
+    the decode's rate on its own algorithmic bytes (each routing level reads
+    a half or about a quarter of the float32 bytes)."""
     plan = tis.DecodePlan(Q, K, V, w.branching, w.leaf_block, w.levels, w.beam,
-                          summary_dtype="bf16")
+                          summary_dtype=summary_dtype)
     for _ in range(warmup):
         plan.build()
         plan.decode()
@@ -171,9 +177,9 @@ def bf16_summaries(tis, torch, w, Q, K, V, reps, warmup):
     step_s = per_launch(torch, step, reps)
     build_s = per_launch(torch, plan.build, reps)
     decode_s = per_launch(torch, plan.decode, reps)
-    by = algorithmic_bytes(w, summary_bytes=2)
+    by = algorithmic_bytes(w, summary_dtype)
     dec = by["route"] + by["attend"]
-    return {"regime": "as the headline step, summaries stored as bfloat16",
+    return {"regime": f"as the headline step, summaries stored as {summary_dtype}",
             "step_us": step_s * 1e6, "queries_per_s_step": w.queries / step_s,
             "build_us": build_s * 1e6, "build_gbs": by["build"] / build_s / 1e9,
             "decode_us": decode_s * 1e6, "decode_queries_per_s": w.queries / decode_s,
@@ -346,7 +352,7 @@ def main(argv=None):
     ap.add_argument("--no-cache-loop", action="store_true",
                     help="skip the growing-cache decode loop measurement")
     ap.add_argument("--no-bf16-summaries", action="store_true",
-                    help="skip the measurement of the step with bfloat16 summaries")
+                    help="skip the measurement of the step with bfloat16 and fp8 summaries")
     ap.add_argument("--no-threshold", action="store_true",
                     help="skip the bounding-sphere threshold retrieval measurement")
     ap.add_argument("--no-prefill", action="store_true",
@@ -519,12 +525,15 @@ def main(argv=None):
 
     bf = None
     if not args.no_bf16_summaries:
-        bf = bf16_summaries(tis, torch, w, Q, K, V, K_, args.warmup)
-        log(f"bf16 summaries: step {bf['step_us']:.1f} us ({bf['queries_per_s_step']:.3e} "
-            f"queries/s); build {bf['build_us']:.2f} us ({bf['build_gbs']:.0f} GB/s); decode "
-            f"{bf['decode_us']:.2f} us -> {bf['decode_queries_per_s']:.3e} queries/s, "
-            f"{bf['decode_gbs']:.0f} GB/s ({bf['decode_frac']:.1%}) on "
-            f"{bf['decode_bytes'] / 1e6:.2f} MB")
+        bf = {}
+        for sd in ("bf16", "fp8"):
+            r = reduced_summaries(tis, torch, w, Q, K, V, K_, args.warmup, sd)
+            bf[sd] = r
+            log(f"{sd} summaries: step {r['step_us']:.1f} us ({r['queries_per_s_step']:.3e} "
+                f"queries/s); build {r['build_us']:.2f} us ({r['build_gbs']:.0f} GB/s); decode "
+                f"{r['decode_us']:.2f} us -> {r['decode_queries_per_s']:.3e} queries/s, "
+                f"{r['decode_gbs']:.0f} GB/s ({r['decode_frac']:.1%}) on "
+                f"{r['decode_bytes'] / 1e6:.2f} MB")
 
     traffic = load_traffic(w.name)
 
@@ -581,7 +590,7 @@ def main(argv=None):
                                         "state - lone warm)")},
         "cpu_baseline": cpu,
         "cache_decode_loop": cache,
-        "bf16_summaries": bf,
+        "reduced_summaries": bf,
         "threshold_retrieval": thr,
         "causal_prefill": pre,
     }

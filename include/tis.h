@@ -69,7 +69,9 @@ typedef enum tis_status {
   TIS_E_HIP = 7          /* the HIP runtime reported an error                 */
 } tis_status;
 
-typedef enum tis_dtype { TIS_F32 = 0, TIS_BF16 = 1 } tis_dtype;
+/* Element types.  TIS_FP8_E4M3 is a summary type only (summary_dtype of a
+ * tis_tree); inputs are TIS_F32 or TIS_BF16. */
+typedef enum tis_dtype { TIS_F32 = 0, TIS_BF16 = 1, TIS_FP8_E4M3 = 2 } tis_dtype;
 
 /* Largest candidate set one level may score: beam * branching <= 256. */
 #define TIS_MAX_CANDIDATES 256
@@ -83,9 +85,17 @@ typedef enum tis_dtype { TIS_F32 = 0, TIS_BF16 = 1 } tis_dtype;
  *   what a zero-initialised descriptor holds): each node mean rounded once
  *   to float32.  TIS_BF16: rounded once, straight from the fp64 mean, to
  *   bfloat16 (round to nearest, ties to even; not through float32), which
- *   halves the bytes every routing level reads.  The pages fix no precision
- *   for the summaries; both are the same mean, stored at two widths.  Any
- *   other value: TIS_E_DTYPE. */
+ *   halves the bytes every routing level reads.  TIS_FP8_E4M3: per node, the
+ *   smallest power of two 2^e with max_i |mean_i| * 2^-e <= 448 (0 for an
+ *   all-zero row; e clamped to [-126, 127]), and each mean * 2^-e rounded
+ *   once to OCP e4m3 (round to nearest even, from the fp64 value); a quarter
+ *   of the float32 bytes.  Layout: the codes, one byte an element with the
+ *   float32 element layout, then (16-byte aligned) one float32 scale 2^e per
+ *   node, level-major like the rows.  fp8 summaries serve tis_tree_build,
+ *   tis_tree_route and tis_tree_decode; the other calls reject them with
+ *   TIS_E_UNSUPPORTED.  The pages fix no precision for the summaries; all
+ *   three are the same mean, stored at different widths.  Any other value:
+ *   TIS_E_DTYPE. */
 typedef struct tis_tree {
   int32_t batch, kv_heads, n_keys, head_dim, branching, leaf_block, levels;
   int32_t summary_dtype;  /* tis_dtype of the stored summaries */
@@ -97,7 +107,8 @@ typedef struct tis_tree {
 size_t tis_tree_summary_bytes(int batch, int kv_heads, int head_dim, int branching,
                               int levels);
 /* The same for summaries stored as summary_dtype (2 bytes an element for
- * TIS_BF16); 0 also for an unknown summary_dtype. */
+ * TIS_BF16; for TIS_FP8_E4M3 one byte an element rounded up to 16 bytes plus
+ * 4 bytes a node); 0 also for an unknown summary_dtype. */
 size_t tis_tree_summary_bytes_as(int batch, int kv_heads, int head_dim, int branching,
                                  int levels, tis_dtype summary_dtype);
 

@@ -26,8 +26,9 @@ def ulp_distance(a: np.ndarray, b: np.ndarray) -> np.ndarray:
 
 
 # float32 units in the last place per unit of the stored summary type (a
-# bfloat16 drops the low 16 bits of a float32)
-ULP_SCALE = {"f32": 1, "bf16": 1 << 16}
+# bfloat16 drops the low 16 bits of a float32, an e4m3 code keeps 3 fraction
+# bits of its 23: a step of a normal code is 2^20 float32 units)
+ULP_SCALE = {"f32": 1, "bf16": 1 << 16, "fp8": 1 << 20}
 
 
 def compare_summaries(gpu_levels, oracle_stored, max_ulp: int = 1, summary_dtype: str = "f32"):

@@ -40,7 +40,13 @@ def test_version(lib):
 def test_summary_bytes_by_type(lib):
     assert lib.tis_tree_summary_bytes_as(4, 8, 128, 8, 3, _lib.TIS_F32) == 4 * 128 * 32 * 584
     assert lib.tis_tree_summary_bytes_as(4, 8, 128, 8, 3, _lib.TIS_BF16) == 2 * 128 * 32 * 584
-    assert lib.tis_tree_summary_bytes_as(4, 8, 128, 8, 3, 2) == 0
+    # fp8: a byte an element (16-byte aligned), then a float32 scale a node
+    nodes = 32 * 584
+    assert lib.tis_tree_summary_bytes_as(4, 8, 128, 8, 3, _lib.TIS_FP8_E4M3) == (
+        -(-nodes * 128 // 16) * 16 + 4 * nodes)
+    assert lib.tis_tree_summary_bytes_as(4, 8, 128, 8, 3, 3) == 0
+    # growing caches take float32 or bfloat16 summaries only
+    assert lib.tis_cache_tree_summary_bytes_as(4, 8, 128, 8, 64, 40000, _lib.TIS_FP8_E4M3) == 0
     assert lib.tis_cache_tree_summary_bytes_as(4, 8, 128, 8, 64, 40000, _lib.TIS_BF16) == (
         2 * 128 * 32 * (625 + 79 + 10 + 2))
     assert lib.tis_cache_tree_summary_bytes_as(4, 8, 128, 8, 64, 40000, 9) == 0
@@ -109,7 +115,7 @@ def _build(lib, **kw):
     (dict(ws=None), _lib.TIS_E_NULL),
     (dict(tree=_lib.TisTree(0, 0, 0, 0, 0, 0, 0, 0, None)), _lib.TIS_E_NULL),
     (dict(dt=7), _lib.TIS_E_DTYPE),
-    (dict(tree=_lib.TisTree(0, 0, 0, 0, 0, 0, 0, 2, FAKE)), _lib.TIS_E_DTYPE),
+    (dict(tree=_lib.TisTree(0, 0, 0, 0, 0, 0, 0, 3, FAKE)), _lib.TIS_E_DTYPE),
     (dict(N=96), _lib.TIS_E_SHAPE),
     (dict(b=1), _lib.TIS_E_SHAPE),
     (dict(b=65, N=65 ** 3 * 16, lv=3), _lib.TIS_E_UNSUPPORTED),
@@ -255,6 +261,7 @@ def _ctree(summ=FAKE, state=FAKE, B=1, H=1, d=64, b=2, L=16, C=1000, n=0, lv=0,
     (dict(C=0), _lib.TIS_E_SHAPE),
     (dict(state=FAKE + 8), _lib.TIS_E_ALIGN),
     (dict(sd=3), _lib.TIS_E_DTYPE),
+    (dict(sd=_lib.TIS_FP8_E4M3), _lib.TIS_E_UNSUPPORTED),
 ])
 def test_cache_reset_rejects(lib, kw, status):
     t = _ctree(**kw)
@@ -369,6 +376,7 @@ def _radii(lib, **kw):
     (dict(tree=_tree(summ=None)), _lib.TIS_E_NULL),
     (dict(dt=4), _lib.TIS_E_DTYPE),
     (dict(tree=_tree(sd=7)), _lib.TIS_E_DTYPE),
+    (dict(tree=_tree(sd=_lib.TIS_FP8_E4M3)), _lib.TIS_E_UNSUPPORTED),
     (dict(tree=_lib.TisTree(1, 1, 100, 64, 2, 16, 3, 0, FAKE)), _lib.TIS_E_SHAPE),
     (dict(wsb=8 * 14 - 1), _lib.TIS_E_WORKSPACE),      # 2 + 4 + 8 nodes need 112 bytes
     (dict(radii=FAKE + 2), _lib.TIS_E_ALIGN),
@@ -401,6 +409,7 @@ def _threshold(lib, fused, **kw):
     (dict(tree=_tree(summ=None)), _lib.TIS_E_NULL),
     (dict(dt=3), _lib.TIS_E_DTYPE),
     (dict(tree=_tree(sd=9)), _lib.TIS_E_DTYPE),
+    (dict(tree=_tree(sd=_lib.TIS_FP8_E4M3)), _lib.TIS_E_UNSUPPORTED),
     (dict(Hq=0), _lib.TIS_E_SHAPE),
     (dict(tree=_tree(H=2), Hq=3), _lib.TIS_E_SHAPE),
     (dict(nodes=0), _lib.TIS_E_SHAPE),
@@ -456,6 +465,7 @@ def _prefill(lib, tree_kw=None, **kw):
     (dict(n=100, lv=2), dict(), _lib.TIS_E_SHAPE),          # wrong depth
     (None, dict(dt=6), _lib.TIS_E_DTYPE),
     (dict(n=100, lv=3, sd=4), dict(), _lib.TIS_E_DTYPE),
+    (dict(n=100, lv=3, sd=_lib.TIS_FP8_E4M3), dict(), _lib.TIS_E_UNSUPPORTED),
     (None, dict(beam=0), _lib.TIS_E_SHAPE),
     (dict(n=100, lv=3, H=2), dict(Hq=3), _lib.TIS_E_SHAPE),
     (None, dict(scale=float("nan")), _lib.TIS_E_SHAPE),

@@ -245,6 +245,32 @@ def test_bf16_summaries(tis, w):
     check_case(tis, w, label=f"{w.name} (bf16 summaries)", summary_dtype="bf16")
 
 
+# fp8 summaries (full tree): per-row scales from a wave-wide max in the
+# build's leaf and node stores, the LDS levels, the top-level and per-level
+# kernels; the walk reads 8 codes a lane and scales each row's partial dot
+FP8_SUMMARY_CASES = [
+    workloads.small("gqa_32k", levels=2, kv_heads=2),
+    workloads.small("deep_planted", levels=4, kv_heads=2),
+    workloads.small("long_1m", levels=3, kv_heads=1),
+    _custom("fp8s_ragged_f32_d64", "f32", 3, 5, 3, 4, d=64),
+    _custom("fp8s_single_level", "bf16", 16, 8, 1, 5),
+    _custom("fp8s_cand_256", "bf16", 16, 4, 2, 16),
+    _custom("fp8s_deep_binary", "bf16", 2, 4, 9, 6, d=64, Hkv=3, G=1),
+    _custom("fp8s_split", "bf16", 4, 64, 4, 64, Hkv=2, G=3),
+]
+
+
+@pytest.mark.parametrize("w", FP8_SUMMARY_CASES, ids=[w.name for w in FP8_SUMMARY_CASES])
+def test_fp8_summaries(tis, w):
+    check_case(tis, w, label=f"{w.name} (fp8 summaries)", summary_dtype="fp8")
+
+
+@pytest.mark.timeout(900)
+def test_fp8_summaries_full_gqa_32k(tis):
+    w = workloads.get("gqa_32k")
+    check_case(tis, w, label="gqa_32k (full size, fp8 summaries)", summary_dtype="fp8")
+
+
 @pytest.mark.timeout(900)
 def test_bf16_summaries_full_gqa_32k(tis):
     w = workloads.get("gqa_32k")

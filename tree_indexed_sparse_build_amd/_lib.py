@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtis.so")
 
 TIS_OK, TIS_E_NULL, TIS_E_SHAPE, TIS_E_DTYPE, TIS_E_ALIGN, TIS_E_UNSUPPORTED, \
     TIS_E_WORKSPACE, TIS_E_HIP = range(8)
-TIS_F32, TIS_BF16 = 0, 1
+TIS_F32, TIS_BF16, TIS_FP8_E4M3 = 0, 1, 2
 TIS_MAX_CANDIDATES = 256
 
 STATUS_NAMES = {

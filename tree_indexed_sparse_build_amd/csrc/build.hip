@@ -184,8 +184,16 @@ __global__ void __launch_bounds__(1024) k_build(BuildArgs a) {
       double m[CPL];
 #pragma unroll
       for (int j = 0; j < CPL; ++j) m[j] = node_mean(a, lv, acc[j]);
-      store_cols<CPL>(summ + a.summ_off[lv] + (head * a.n_at[lv] + leaf) * D + colf, m,
-                      a.stream_loads != 0);
+      const int64_t node = head * a.n_at[lv] + leaf;
+      if constexpr (kIsFp8<S>) {
+        int cols[CPL];
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) cols[j] = colf + j;
+        store_row_fp8<CPL>(summ + a.summ_off[lv] + node * D, a.scales + a.summ_off[lv] / D + node,
+                           m, cols, lane);
+      } else {
+        store_cols<CPL>(summ + a.summ_off[lv] + node * D + colf, m, a.stream_loads != 0);
+      }
     }
     double carry[CPL];
 #pragma unroll
@@ -204,8 +212,16 @@ __global__ void __launch_bounds__(1024) k_build(BuildArgs a) {
         double m[CPL];
 #pragma unroll
         for (int j = 0; j < CPL; ++j) m[j] = node_mean(a, lvl, st[k][j]);
-        store_cols<CPL>(summ + a.summ_off[lvl] + (head * a.n_at[lvl] + nid[k]) * D + colf, m,
-                        a.stream_loads != 0);
+        const int64_t node = head * a.n_at[lvl] + nid[k];
+        if constexpr (kIsFp8<S>) {
+          int cols[CPL];
+#pragma unroll
+          for (int j = 0; j < CPL; ++j) cols[j] = colf + j;
+          store_row_fp8<CPL>(summ + a.summ_off[lvl] + node * D,
+                             a.scales + a.summ_off[lvl] / D + node, m, cols, lane);
+        } else {
+          store_cols<CPL>(summ + a.summ_off[lvl] + node * D + colf, m, a.stream_loads != 0);
+        }
       }
 #pragma unroll
       for (int j = 0; j < CPL; ++j) {
@@ -247,11 +263,30 @@ __global__ void __launch_bounds__(1024) k_build(BuildArgs a) {
       double s = 0.0;
       for (int c = 0; c < b; ++c) s += cur[(n * b + c) * D + dd];
       nxt[n * D + dd] = s;
-      if (lvl >= 1)
-        SummaryType<S>::put(summ + a.summ_off[lvl] + (head * a.n_at[lvl] + base + n) * D + dd,
-                            node_mean(a, lvl, s));
+      if constexpr (!kIsFp8<S>) {
+        if (lvl >= 1)
+          SummaryType<S>::put(summ + a.summ_off[lvl] + (head * a.n_at[lvl] + base + n) * D + dd,
+                              node_mean(a, lvl, s));
+      }
     }
     __syncthreads();
+    if constexpr (kIsFp8<S>) {
+      // fp8 rows need their whole row's largest magnitude: one wave a row
+      if (lvl >= 1) {
+        for (int r = w; r < nn; r += nw) {
+          double m[CPL];
+          int cols[CPL];
+#pragma unroll
+          for (int j = 0; j < CPL; ++j) {
+            cols[j] = lane + 64 * j;
+            m[j] = node_mean(a, lvl, nxt[r * D + cols[j]]);
+          }
+          const int64_t node = head * a.n_at[lvl] + base + r;
+          store_row_fp8<CPL>(summ + a.summ_off[lvl] + node * D,
+                             a.scales + a.summ_off[lvl] / D + node, m, cols, lane);
+        }
+      }
+    }
     double *t = cur;
     cur = nxt;
     nxt = t;
@@ -283,6 +318,51 @@ __global__ void __launch_bounds__(256) k_build_level(BuildArgs a, int l) {
   if (l >= 2) a.ws_sum[a.ws_off[l] + node * D + t] = s;
 }
 
+// k_build_level for fp8 summaries: one wave per node row (the row's scale
+// needs its largest magnitude), 4 rows per workgroup.
+template <int D> __global__ void __launch_bounds__(256) k_build_level_fp8(BuildArgs a, int l) {
+  constexpr int C = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t node = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (node >= a.chunks_at_level[l]) return;  // whole wave
+  const int b = a.branching;
+  double m[C];
+  int cols[C];
+#pragma unroll
+  for (int j = 0; j < C; ++j) {
+    const int t = lane + 64 * j;
+    const double *child = a.ws_sum + a.ws_off[l + 1] + node * b * D + t;
+    double s = 0.0;
+    for (int c = 0; c < b; ++c) s += child[static_cast<int64_t>(c) * D];
+    if (l >= 2) a.ws_sum[a.ws_off[l] + node * D + t] = s;
+    cols[j] = t;
+    m[j] = node_mean(a, l, s);
+  }
+  store_row_fp8<C>(static_cast<fp8_bits *>(a.summ) + a.summ_off[l] + node * D,
+                   a.scales + a.summ_off[l] / D + node, m, cols, lane);
+}
+
+// fp8 rows of nn nodes of level l whose fp64 sums sit in LDS (rows of D),
+// the first being node `node0` of the level (head included): one wave a row.
+template <int D>
+__device__ inline void top_rows_fp8(const BuildArgs &a, fp8_bits *summ, const double *sums,
+                                    int nn, int64_t node0, int l) {
+  constexpr int C = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int nw = blockDim.x >> 6;
+  for (int r = threadIdx.x >> 6; r < nn; r += nw) {
+    double m[C];
+    int cols[C];
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      cols[j] = lane + 64 * j;
+      m[j] = node_mean(a, l, sums[r * D + cols[j]]);
+    }
+    store_row_fp8<C>(summ + a.summ_off[l] + (node0 + r) * D, a.scales + a.summ_off[l] / D + node0 + r,
+                     m, cols, lane);
+  }
+}
+
 // Levels r-1 .. 1 in one launch, one workgroup per (head, level-1 node): the
 // b^(r-2) nodes of level r-1 in its subtree sum their children's fp64 sums
 // from the workspace (all loads independent), the levels above are summed in
@@ -308,9 +388,10 @@ template <typename S, int D> __global__ void __launch_bounds__(256) k_build_top(
     double s = 0.0;
     for (int c = 0; c < b; ++c) s += child[static_cast<int64_t>(c) * D];
     cur[i] = s;
-    SummaryType<S>::put(summ + a.summ_off[l] + node * D + t, node_mean(a, l, s));
+    if constexpr (!kIsFp8<S>) SummaryType<S>::put(summ + a.summ_off[l] + node * D + t, node_mean(a, l, s));
   }
   __syncthreads();
+  if constexpr (kIsFp8<S>) top_rows_fp8<D>(a, summ, cur, nn, head * a.n_at[l] + first, l);
   for (--l; l >= 1; --l) {
     nn /= b;
     first /= b;
@@ -320,10 +401,12 @@ template <typename S, int D> __global__ void __launch_bounds__(256) k_build_top(
       double s = 0.0;
       for (int c = 0; c < b; ++c) s += cur[(n * b + c) * D + t];
       nxt[i] = s;
-      SummaryType<S>::put(summ + a.summ_off[l] + (head * a.n_at[l] + first + n) * D + t,
-                          node_mean(a, l, s));
+      if constexpr (!kIsFp8<S>)
+        SummaryType<S>::put(summ + a.summ_off[l] + (head * a.n_at[l] + first + n) * D + t,
+                            node_mean(a, l, s));
     }
     __syncthreads();
+    if constexpr (kIsFp8<S>) top_rows_fp8<D>(a, summ, nxt, nn, head * a.n_at[l] + first, l);
     double *tmp = cur;
     cur = nxt;
     nxt = tmp;
@@ -408,9 +491,14 @@ hipError_t launch_build_t(int64_t heads, const BuildArgs &a, const BuildPlan &p,
     return hipGetLastError();
   }
   for (int l = p.root_level - 1; e == hipSuccess && l >= 1; --l) {
-    const int64_t items = a.chunks_at_level[l] * D;
-    const dim3 g(static_cast<unsigned>((items + 255) / 256));
-    hipLaunchKernelGGL((k_build_level<S, D>), g, dim3(256), 0, s, a, l);
+    if constexpr (kIsFp8<S>) {
+      const dim3 g(static_cast<unsigned>((a.chunks_at_level[l] + 3) / 4));
+      hipLaunchKernelGGL((k_build_level_fp8<D>), g, dim3(256), 0, s, a, l);
+    } else {
+      const int64_t items = a.chunks_at_level[l] * D;
+      const dim3 g(static_cast<unsigned>((items + 255) / 256));
+      hipLaunchKernelGGL((k_build_level<S, D>), g, dim3(256), 0, s, a, l);
+    }
     e = hipGetLastError();
   }
   return e;
@@ -428,9 +516,12 @@ hipError_t launch_build_ts(int head_dim, int64_t heads, const BuildArgs &a, cons
 
 hipError_t launch_build(Dt dt, Dt sdt, int head_dim, int64_t heads, const BuildArgs &a,
                         const BuildPlan &p, hipStream_t s) {
-  if (dt == Dt::BF16)
+  if (dt == Dt::BF16) {
+    if (sdt == Dt::FP8) return launch_build_ts<bf16_bits, fp8_bits>(head_dim, heads, a, p, s);
     return sdt == Dt::BF16 ? launch_build_ts<bf16_bits, bf16_bits>(head_dim, heads, a, p, s)
                            : launch_build_ts<bf16_bits, float>(head_dim, heads, a, p, s);
+  }
+  if (sdt == Dt::FP8) return launch_build_ts<float, fp8_bits>(head_dim, heads, a, p, s);
   return sdt == Dt::BF16 ? launch_build_ts<float, bf16_bits>(head_dim, heads, a, p, s)
                          : launch_build_ts<float, float>(head_dim, heads, a, p, s);
 }

@@ -68,12 +68,17 @@ hipError_t launch_decode_ts(int head_dim, const RouteArgs &ra, const AttendArgs 
 hipError_t launch_decode(Dt dt, Dt sdt, int head_dim, const RouteArgs &ra,
                          const AttendArgs &aa, hipStream_t s) {
   hipError_t e;
-  if (dt == Dt::BF16)
+  if (sdt == Dt::FP8) {  // full tree only
+    if (ra.cache) return hipErrorInvalidValue;
+    e = dt == Dt::BF16 ? launch_decode_t<bf16_bits, fp8_bits, false>(head_dim, ra, aa, s)
+                       : launch_decode_t<float, fp8_bits, false>(head_dim, ra, aa, s);
+  } else if (dt == Dt::BF16) {
     e = sdt == Dt::BF16 ? launch_decode_ts<bf16_bits, bf16_bits>(head_dim, ra, aa, s)
                         : launch_decode_ts<bf16_bits, float>(head_dim, ra, aa, s);
-  else
+  } else {
     e = sdt == Dt::BF16 ? launch_decode_ts<float, bf16_bits>(head_dim, ra, aa, s)
                         : launch_decode_ts<float, float>(head_dim, ra, aa, s);
+  }
   if (e != hipSuccess || aa.splits <= 1) return e;
   return launch_combine(head_dim, aa, s);
 }

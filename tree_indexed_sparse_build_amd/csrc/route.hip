@@ -43,6 +43,11 @@ hipError_t launch_route_ts(int head_dim, const RouteArgs &a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_route(Dt dt, Dt sdt, int head_dim, const RouteArgs &a, hipStream_t s) {
+  if (sdt == Dt::FP8) {  // full tree only
+    if (a.cache) return hipErrorInvalidValue;
+    return dt == Dt::BF16 ? launch_route_t<bf16_bits, fp8_bits, false>(head_dim, a, s)
+                          : launch_route_t<float, fp8_bits, false>(head_dim, a, s);
+  }
   if (dt == Dt::BF16)
     return sdt == Dt::BF16 ? launch_route_ts<bf16_bits, bf16_bits>(head_dim, a, s)
                            : launch_route_ts<bf16_bits, float>(head_dim, a, s);

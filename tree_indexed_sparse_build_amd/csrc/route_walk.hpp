@@ -192,12 +192,16 @@ template <int NT> __device__ inline void write_ascending(const int *v, int n, in
 // candidate 0 again (always a valid address) and their scores are dropped,
 // so no branch splits the loads.  A lane loads 16 bytes of a row: 4 float32
 // or 8 bfloat16 summary elements.
+struct NoScale {
+  __device__ float operator()(int) const { return 1.f; }
+};
+
 template <typename T, typename S, int D, int UU, bool HOLES, typename NodeOf, typename RowOf,
-          typename Emit>
+          typename Emit, typename ScaleOf = NoScale>
 __device__ inline void score_rows(RowOf row_of, int C, NodeOf node_of, Emit emit,
-                                  const QRaw<T, Vec16<S>::kElems> &qr, int nsw, int w,
-                                  int lane) {
-  constexpr int E = Vec16<S>::kElems;
+                                  const QRaw<T, RowLoad<S>::E> &qr, int nsw, int w, int lane,
+                                  ScaleOf scale_of = ScaleOf()) {
+  constexpr int E = RowLoad<S>::E;
   constexpr int LPR = D / E;    // lanes per summary row
   constexpr int RPI = 64 / LPR; // rows per wave-wide load
   constexpr int REP = LPR / UU; // lanes sharing one reduced score
@@ -211,23 +215,27 @@ __device__ inline void score_rows(RowOf row_of, int C, NodeOf node_of, Emit emit
       const int pos = base + (u * nsw + w) * RPI + rsub;
       node[u] = node_of(pos < C ? pos : 0);
     }
-    uint4 v[UU];
+    typename RowLoad<S>::Raw v[UU];
+    float scl[UU];  // fp8 rows: the row's power-of-two scale
 #pragma unroll
     for (int u = 0; u < UU; ++u) {
       const int nd = HOLES && node[u] < 0 ? 0 : node[u];  // a hole reads node 0
-      v[u] = load16(row_of(nd));
+      v[u] = RowLoad<S>::load(row_of(nd));
+      if constexpr (kIsFp8<S>) scl[u] = scale_of(nd);
     }
     double q[E];
     qr.widen(q);
     double part[UU];
 #pragma unroll
     for (int u = 0; u < UU; ++u) {
-      // fp32 x (fp32 or bf16) products are exact in fp64
+      // fp32 x (fp32, bf16 or e4m3) products are exact in fp64, and so is
+      // the scaling of an fp8 row's partial dot by its power of two
       float f[E];
-      Vec16<S>::unpack(v[u], f);
+      RowLoad<S>::unpack(v[u], f);
       double s = q[0] * static_cast<double>(f[0]);
 #pragma unroll
       for (int e = 1; e < E; ++e) s = fma(q[e], static_cast<double>(f[e]), s);
+      if constexpr (kIsFp8<S>) s *= static_cast<double>(scl[u]);
       part[u] = s;
     }
     const double s = group_transpose_reduce<UU, LPR>(part, lane);
@@ -259,6 +267,7 @@ __device__ int route_walk(const RouteArgs &a, RouteShared<NW> &sh, int qi,
                           const CausalLevels *cl = nullptr, const void *open_summ = nullptr,
                           int hrow = -1) {
   constexpr bool CACHE = LAYOUT != 0;  // nodes past the last key may be missing
+  static_assert(!kIsFp8<S> || LAYOUT == 0, "fp8 summaries: full tree only");
   constexpr int NT = NW * 64;
   constexpr int LOG_NRT = NRW == 16 ? 10 : NRW == 8 ? 9 : NRW == 4 ? 8 : -1;
   static_assert(LOG_NRT > 0 && NRW <= NW, "4, 8 or 16 walking waves");
@@ -266,7 +275,7 @@ __device__ int route_walk(const RouteArgs &a, RouteShared<NW> &sh, int qi,
   // checked by the host); the ranking needs two or more threads for each
   static_assert(MAXC <= kMaxCandidates && MAXC <= NRW * 64 / 2,
                 "two or more threads per candidate");
-  constexpr int E = Vec16<S>::kElems;  // summary elements per lane (16 bytes)
+  constexpr int E = RowLoad<S>::E;     // summary elements per lane (one load)
   constexpr int LPR = D / E;           // lanes per summary row
   constexpr int RPI = 64 / LPR;        // rows per wave-wide load
 
@@ -343,6 +352,8 @@ __device__ int route_walk(const RouteArgs &a, RouteShared<NW> &sh, int qi,
       const auto row_of = [&](int nd) {
         return LAYOUT == 2 && nd == last ? open_row : sl + static_cast<int64_t>(nd) * D;
       };
+      const float *scl = kIsFp8<S> ? a.scales + lc.off / D + head * lc.rows : nullptr;
+      const auto scale_of = [&](int nd) { return scl[nd]; };
       // the walking waves score, each lane taking `per` rows
       const int per = (C + NRW * RPI - 1) / (NRW * RPI);
       const int *cand = sh.cand[cur];
@@ -355,13 +366,13 @@ __device__ int route_walk(const RouteArgs &a, RouteShared<NW> &sh, int qi,
       };
       if (w < NRW) {
         if (per <= 1)
-          score_rows<T, S, D, 1, CACHE>(row_of, C, node_of, emit, qr, NRW, w, lane);
+          score_rows<T, S, D, 1, CACHE>(row_of, C, node_of, emit, qr, NRW, w, lane, scale_of);
         else if (per <= 2)
-          score_rows<T, S, D, 2, CACHE>(row_of, C, node_of, emit, qr, NRW, w, lane);
-        else if (per <= 4)
-          score_rows<T, S, D, 4, CACHE>(row_of, C, node_of, emit, qr, NRW, w, lane);
+          score_rows<T, S, D, 2, CACHE>(row_of, C, node_of, emit, qr, NRW, w, lane, scale_of);
+        else if (per <= 4 || kIsFp8<S>)  // fp8: at most 4 rows a lane (registers), then passes
+          score_rows<T, S, D, 4, CACHE>(row_of, C, node_of, emit, qr, NRW, w, lane, scale_of);
         else
-          score_rows<T, S, D, 8, CACHE>(row_of, C, node_of, emit, qr, NRW, w, lane);
+          score_rows<T, S, D, 8, CACHE>(row_of, C, node_of, emit, qr, NRW, w, lane, scale_of);
       }
       __syncthreads();
       // rank of candidate i = number of candidates with a larger key.  Each

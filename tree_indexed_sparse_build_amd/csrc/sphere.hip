@@ -30,16 +30,6 @@ namespace {
 
 constexpr int kRadiusWaves = 4;
 
-__device__ inline double wave_max_d(double v) {
-  const int lane = __lane_id();
-  v = fmax(v, xor_lane<1>(v, lane));
-  v = fmax(v, xor_lane<2>(v, lane));
-  v = fmax(v, xor_lane<4>(v, lane));
-  v = fmax(v, xor_lane<8>(v, lane));
-  v = fmax(v, xor_lane<16>(v, lane));
-  return fmax(v, xor_lane<32>(v, lane));
-}
-
 template <typename T, typename S, int D>
 __global__ void __launch_bounds__(kRadiusWaves * 64) k_radius(RadiusArgs a) {
   using AG = AttendGeom<T, D>;  // row geometry of 16-byte K loads

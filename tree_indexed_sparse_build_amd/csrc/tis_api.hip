@@ -79,14 +79,32 @@ tis_status check_dtype(tis_dtype dt) {
 
 // The stored type of a tree's summaries (a field the caller sets).
 tis_status check_summary_dtype(const char *who, int32_t sd) {
-  if (sd != TIS_F32 && sd != TIS_BF16)
+  if (sd != TIS_F32 && sd != TIS_BF16 && sd != TIS_FP8_E4M3)
     return fail(TIS_E_DTYPE, "%s: unknown summary_dtype %d", who, (int)sd);
   return TIS_OK;
 }
 
-tis::Dt to_dt(int32_t d) { return d == TIS_BF16 ? tis::Dt::BF16 : tis::Dt::F32; }
+// Calls built for float32 and bfloat16 summaries only (fp8 summaries serve
+// the full tree's build, route and decode).
+tis_status check_summary_dtype_no_fp8(const char *who, int32_t sd) {
+  tis_status st = check_summary_dtype(who, sd);
+  if (st == TIS_OK && sd == TIS_FP8_E4M3)
+    return fail(TIS_E_UNSUPPORTED, "%s: fp8 summaries serve tis_tree_build / route / decode only",
+                who);
+  return st;
+}
 
-size_t summary_elem_bytes(int32_t sd) { return sd == TIS_BF16 ? 2 : 4; }
+tis::Dt to_dt(int32_t d) {
+  return d == TIS_BF16 ? tis::Dt::BF16 : d == TIS_FP8_E4M3 ? tis::Dt::FP8 : tis::Dt::F32;
+}
+
+size_t summary_elem_bytes(int32_t sd) { return sd == TIS_BF16 ? 2 : sd == TIS_FP8_E4M3 ? 1 : 4; }
+
+// fp8 summaries: the codes (level-major, one byte an element) come first,
+// then, 16-byte aligned, one float32 power-of-two scale per node.
+size_t fp8_scales_offset(int64_t nodes, int head_dim) {
+  return tis::align_up(static_cast<size_t>(nodes) * head_dim, 16);
+}
 
 tis_status hip_status(hipError_t e, const char *what) {
   if (e == hipSuccess) return TIS_OK;
@@ -110,6 +128,10 @@ tis::RouteArgs route_args(const void *Q, const tis_tree *tree, const Geometry &g
   a.beam = beam;
   a.first_cut = 1;
   while (a.first_cut < tree->levels && g.n_at[a.first_cut] <= beam) ++a.first_cut;
+  if (tree->summary_dtype == TIS_FP8_E4M3)
+    a.scales = reinterpret_cast<const float *>(
+        static_cast<const char *>(tree->summaries) +
+        fp8_scales_offset(g.summ_elems / tree->head_dim, tree->head_dim));
   return a;
 }
 
@@ -124,7 +146,8 @@ size_t tis_tree_summary_bytes(int batch, int kv_heads, int head_dim, int branchi
 size_t tis_tree_summary_bytes_as(int batch, int kv_heads, int head_dim, int branching, int levels,
                                  tis_dtype summary_dtype) {
   if (batch < 1 || kv_heads < 1 || head_dim < 1 || branching < 2 || levels < 1 ||
-      levels > tis::kMaxLevels || (summary_dtype != TIS_F32 && summary_dtype != TIS_BF16))
+      levels > tis::kMaxLevels ||
+      (summary_dtype != TIS_F32 && summary_dtype != TIS_BF16 && summary_dtype != TIS_FP8_E4M3))
     return 0;
   const size_t es = summary_elem_bytes(summary_dtype);
   int64_t n = 1, total = 0;
@@ -135,7 +158,10 @@ size_t tis_tree_summary_bytes_as(int batch, int kv_heads, int head_dim, int bran
   }
   const double bytes = 4.0 * head_dim * (double)batch * kv_heads * (double)total;
   if (bytes > 9.0e18) return 0;
-  return es * head_dim * static_cast<size_t>(batch) * kv_heads * static_cast<size_t>(total);
+  const int64_t nodes = static_cast<int64_t>(batch) * kv_heads * total;
+  if (summary_dtype == TIS_FP8_E4M3)
+    return fp8_scales_offset(nodes, head_dim) + static_cast<size_t>(nodes) * sizeof(float);
+  return es * head_dim * static_cast<size_t>(nodes);
 }
 
 size_t tis_build_workspace_bytes(int batch, int kv_heads, int n_keys, int head_dim,
@@ -180,6 +206,9 @@ tis_status tis_tree_build(const void *K, tis_dtype dtype, int batch, int kv_head
   tis::BuildArgs a{};
   a.K = K;
   a.summ = tree->summaries;
+  if (tree->summary_dtype == TIS_FP8_E4M3)
+    a.scales = reinterpret_cast<float *>(static_cast<char *>(tree->summaries) +
+                                         fp8_scales_offset(g.summ_elems / head_dim, head_dim));
   a.ws_sum = static_cast<double *>(workspace);
   a.n_keys = n_keys;
   a.chunks = p.chunks;
@@ -462,7 +491,7 @@ tis_status check_cache_tree(const char *who, const tis_cache_tree *t, CacheGeome
   tis_status st = check_cache(who, t->batch, t->kv_heads, t->head_dim, t->branching,
                               t->leaf_block, t->capacity, g);
   if (st != TIS_OK) return st;
-  st = check_summary_dtype(who, t->summary_dtype);
+  st = check_summary_dtype_no_fp8(who, t->summary_dtype);
   if (st != TIS_OK) return st;
   if (!aligned(t->summaries, 16) || !aligned(t->state, 16))
     return fail(TIS_E_ALIGN, "%s: summaries and state need 16-byte alignment", who);
@@ -554,7 +583,7 @@ size_t tis_cache_tree_summary_bytes(int batch, int kv_heads, int head_dim, int b
 size_t tis_cache_tree_summary_bytes_as(int batch, int kv_heads, int head_dim, int branching,
                                        int leaf_block, int capacity, tis_dtype summary_dtype) {
   CacheGeometry g;
-  if (summary_dtype != TIS_F32 && summary_dtype != TIS_BF16) return 0;
+  if (summary_dtype != TIS_F32 && summary_dtype != TIS_BF16) return 0;  // no fp8 cache trees
   if (check_cache("tis_cache_tree_summary_bytes", batch, kv_heads, head_dim, branching,
                   leaf_block, capacity, &g) != TIS_OK)
     return 0;
@@ -578,7 +607,7 @@ tis_status tis_cache_tree_reset(tis_cache_tree *tree, void *stream) {
                               tree->head_dim, tree->branching, tree->leaf_block, tree->capacity,
                               &g);
   if (st != TIS_OK) return st;
-  st = check_summary_dtype("tis_cache_tree_reset", tree->summary_dtype);
+  st = check_summary_dtype_no_fp8("tis_cache_tree_reset", tree->summary_dtype);
   if (st != TIS_OK) return st;
   if (!aligned(tree->summaries, 16) || !aligned(tree->state, 16))
     return fail(TIS_E_ALIGN, "tis_cache_tree_reset: summaries and state need 16-byte alignment");
@@ -814,7 +843,7 @@ tis_status check_threshold(const char *who, const void *Q, tis_dtype dtype, int 
                            int max_nodes, Geometry *g, int64_t *queries) {
   tis_status st = check_dtype(dtype);
   if (st != TIS_OK) return st;
-  st = check_summary_dtype(who, tree->summary_dtype);
+  st = check_summary_dtype_no_fp8(who, tree->summary_dtype);
   if (st != TIS_OK) return st;
   st = check_tree(tree->batch, tree->kv_heads, tree->n_keys, tree->head_dim, tree->branching,
                   tree->leaf_block, tree->levels, g);
@@ -872,7 +901,7 @@ tis_status tis_tree_radii(const void *K, tis_dtype dtype, const tis_tree *tree, 
                             "required");
   tis_status st = check_dtype(dtype);
   if (st != TIS_OK) return st;
-  st = check_summary_dtype("tis_tree_radii", tree->summary_dtype);
+  st = check_summary_dtype_no_fp8("tis_tree_radii", tree->summary_dtype);
   if (st != TIS_OK) return st;
   Geometry g;
   st = check_tree(tree->batch, tree->kv_heads, tree->n_keys, tree->head_dim, tree->branching,

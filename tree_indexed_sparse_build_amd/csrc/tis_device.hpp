@@ -12,6 +12,13 @@ struct bf16_bits {
   uint16_t v;
 };
 
+// Storage element of fp8 summaries: an OCP e4m3 code (1 sign, 4 exponent
+// bits with bias 7, 3 fraction bits; largest finite value 448).  A node's
+// codes are scaled by a power of two kept beside them (see fp8_scale_exp).
+struct fp8_bits {
+  uint8_t v;
+};
+
 template <typename T> struct Vec16;
 template <> struct Vec16<float> {
   static constexpr int kElems = 4;
@@ -64,6 +71,50 @@ __device__ inline uint16_t bf16_from_double(double x) {
   }
   const double m = __builtin_rint(__longlong_as_double(static_cast<long long>(a)) * 0x1p133);
   return static_cast<uint16_t>(sign | static_cast<uint32_t>(m));  // m <= 128 (128: 2^-126)
+}
+
+// e4m3 code -> float (exact): 0 exponent field = subnormal (m * 2^-9).
+__device__ inline float e4m3_to_float(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20))
+                      : static_cast<float>(m) * 0x1p-9f;
+  return (c & 0x80u) ? -mag : mag;
+}
+
+// fp64 -> e4m3, round to nearest even, for |x| <= 448 (the caller's scale
+// guarantees it).  From 2^-6 up (normal codes) the 52-bit fraction is
+// rounded to 3 bits as for bf16 (add 2^48 - 1 plus the lowest kept bit, drop
+// 49 bits; a carry steps the exponent); below, the grid is the fixed spacing
+// 2^-9, reached by an exact scaling and rint (halves to even).
+__device__ inline uint32_t e4m3_from_double(double x) {
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(x));
+  const uint32_t sign = static_cast<uint32_t>(u >> 56) & 0x80u;
+  const uint64_t a = u & 0x7fffffffffffffffull;
+  if ((a >> 52) >= 1023u - 6u) {
+    const uint64_t r = (a + 0x0000ffffffffffffull + ((a >> 49) & 1ull)) >> 49;
+    return sign | ((static_cast<uint32_t>(r >> 3) - (1023u - 7u)) << 3) |
+           static_cast<uint32_t>(r & 7u);
+  }
+  const double m = __builtin_rint(__longlong_as_double(static_cast<long long>(a)) * 0x1p9);
+  return sign | static_cast<uint32_t>(m);  // m <= 8 (8: 2^-6, the smallest normal)
+}
+
+// Scale exponent of an fp8 summary row: the smallest e with amax * 2^-e <=
+// 448; 0 for amax = 0; clamped to [-126, 127] (2^e a normal float32).
+// With amax = f * 2^k, 0.5 <= f < 1: e = k - 9 if f <= 0.875 (448 = 0.875 *
+// 2^9), else k - 8.  f <= 0.875 is the fp64 fraction field <= 0.75 * 2^52.
+__device__ inline int fp8_scale_exp(double amax) {
+  if (!(amax > 0.0)) return 0;
+  const uint64_t a = static_cast<uint64_t>(__double_as_longlong(amax));
+  const int k = static_cast<int>(a >> 52) - 1022;
+  const bool low = (a & 0x000fffffffffffffull) <= 0x000c000000000000ull;
+  int e = low ? k - 9 : k - 8;
+  if ((a >> 52) == 0) e = -126;  // a subnormal double: far below any clamp
+  return e < -126 ? -126 : e > 127 ? 127 : e;
+}
+
+__device__ inline double pow2_double(int e) {
+  return __longlong_as_double(static_cast<long long>(static_cast<uint64_t>(e + 1023) << 52));
 }
 
 template <typename S> struct SummaryType;
@@ -170,6 +221,16 @@ __device__ inline float wave_max(float v) {
   return fmaxf(v, xor_lane<32>(v, lane));
 }
 
+__device__ inline double wave_max_d(double v) {
+  const int lane = __lane_id();
+  v = fmax(v, xor_lane<1>(v, lane));
+  v = fmax(v, xor_lane<2>(v, lane));
+  v = fmax(v, xor_lane<4>(v, lane));
+  v = fmax(v, xor_lane<8>(v, lane));
+  v = fmax(v, xor_lane<16>(v, lane));
+  return fmax(v, xor_lane<32>(v, lane));
+}
+
 __device__ inline float wave_sum(float v) {
   const int lane = __lane_id();
   v = xor_sum<1>(v, lane);
@@ -217,6 +278,64 @@ template <int U, int LPR, typename F> __device__ inline F group_transpose_reduce
   static_assert(U >= 1 && U <= LPR, "need U <= LPR");
   transpose_steps<U, LPR, 0>(v, lane);
   return group_sum<1, LPR / U / 2>(v[0], lane);
+}
+
+}  // namespace tis
+
+namespace tis {
+
+// A lane's share of a summary row when a walk scores it: E consecutive
+// elements from one load (16 bytes of float32 or bf16, 8 bytes of fp8 codes,
+// so that fp8 rows keep the bf16 lane layout).
+template <typename S> struct RowLoad {
+  static constexpr int E = Vec16<S>::kElems;
+  using Raw = uint4;
+  __device__ static inline Raw load(const S *p) { return load16(p); }
+  __device__ static inline void unpack(const Raw &r, float *f) { Vec16<S>::unpack(r, f); }
+};
+template <> struct RowLoad<fp8_bits> {
+  static constexpr int E = 8;
+  using Raw = uint2;
+  __device__ static inline Raw load(const fp8_bits *p) {
+    return *reinterpret_cast<const uint2 *>(p);
+  }
+  // gfx950's packed conversion decodes OCP e4m3, two codes an instruction
+  // (checked against e4m3_to_float for every finite code)
+  __device__ static inline void unpack(const Raw &r, float *f) {
+    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(r.x), false);
+    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(r.x), true);
+    const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(r.y), false);
+    const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(r.y), true);
+    f[0] = a[0];
+    f[1] = a[1];
+    f[2] = b[0];
+    f[3] = b[1];
+    f[4] = c[0];
+    f[5] = c[1];
+    f[6] = d[0];
+    f[7] = d[1];
+  }
+};
+
+template <typename S> inline constexpr bool kIsFp8 = false;
+template <> inline constexpr bool kIsFp8<fp8_bits> = true;
+
+// Stores one node's fp8 summary row, held by the 64 lanes of a wave (lane
+// value j is column cols[j]): the row's power-of-two scale 2^e from its
+// largest magnitude, each mean rounded once to e4m3 after an exact scaling by
+// 2^-e; lane 0 stores the scale.
+template <int C>
+__device__ inline void store_row_fp8(fp8_bits *row, float *scale, const double (&m)[C],
+                                     const int (&cols)[C], int lane) {
+  double amax = 0.0;
+#pragma unroll
+  for (int j = 0; j < C; ++j) amax = fmax(amax, fabs(m[j]));
+  amax = wave_max_d(amax);
+  const int e = fp8_scale_exp(amax);
+  const double inv = pow2_double(-e);
+#pragma unroll
+  for (int j = 0; j < C; ++j) row[cols[j]].v = static_cast<uint8_t>(e4m3_from_double(m[j] * inv));
+  if (lane == 0) *scale = static_cast<float>(pow2_double(e));
 }
 
 }  // namespace tis

@@ -12,7 +12,7 @@ constexpr int kMaxLevels = 16;
 constexpr int kMaxCandidates = 256;   // beam * branching scored per level
 constexpr int kMaxBranching = 64;
 
-enum class Dt : int { F32 = 0, BF16 = 1 };
+enum class Dt : int { F32 = 0, BF16 = 1, FP8 = 2 };  // FP8: summaries only
 
 // ---------------------------------------------------------------- build --
 // Work split.  A wave reduces the b^kw leaves under one node of level lv-kw
@@ -26,7 +26,8 @@ constexpr size_t kStreamLoadBytes = 384u << 20;  // K larger than this: streamin
 
 struct BuildArgs {
   const void *K;
-  void *summ;            // float or bf16 bits (the summary type)
+  void *summ;            // float, bf16 bits or fp8 codes (the summary type)
+  float *scales;         // fp8 only: a power-of-two scale per node, level-major
   double *ws_sum;        // fp64 node sums of levels 2..r
   int64_t n_keys;        // N
   int64_t chunks;        // b^r chunks per head
@@ -71,7 +72,8 @@ hipError_t launch_build(Dt dt, Dt sdt, int head_dim, int64_t heads, const BuildA
 //    when n * L * b^(levels-l) < n_keys.
 struct RouteArgs {
   const void *Q;
-  const void *summ;      // float or bf16 bits (the summary type)
+  const void *summ;      // float, bf16 bits or fp8 codes (the summary type)
+  const float *scales;   // fp8 (full tree only): a scale per node, level-major
   int32_t *indices;
   int32_t *trace;        // may be null
   int queries;           // B * Hq (< 2^31, checked by the host)

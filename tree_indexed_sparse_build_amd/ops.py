@@ -36,8 +36,10 @@ def _need_device(*ts: torch.Tensor) -> None:
             raise ValueError("tensors must be contiguous")
 
 
-# stored summary types: name -> (tis_dtype code, torch dtype)
-SUMMARY_DTYPES = {"f32": (0, torch.float32), "bf16": (1, torch.bfloat16)}
+# stored summary types: name -> (tis_dtype code, torch dtype of the buffer);
+# "fp8" (full tree only): e4m3 codes, then a float32 power-of-two scale per node
+SUMMARY_DTYPES = {"f32": (0, torch.float32), "bf16": (1, torch.bfloat16),
+                  "fp8": (2, torch.uint8)}
 
 
 def _summary_dtype(name: str):
@@ -93,12 +95,29 @@ class Tree:
                        self.summaries.data_ptr())
 
     def level(self, l: int) -> torch.Tensor:
-        """Summaries of level l (1..levels) as a [B, Hkv, b**l, d] view."""
+        """Summaries of level l (1..levels) as a [B, Hkv, b**l, d] view; for
+        fp8 summaries a float32 copy of the values they stand for (each code
+        times its node's scale)."""
         off = summary_offsets(self.batch, self.kv_heads, self.head_dim, self.branching,
                               self.levels)
         n = self.branching ** l
-        return self.summaries[off[l - 1]:off[l - 1] + self.batch * self.kv_heads * n *
+        rows = self.summaries[off[l - 1]:off[l - 1] + self.batch * self.kv_heads * n *
                               self.head_dim].view(self.batch, self.kv_heads, n, self.head_dim)
+        if self.summary_dtype != "fp8":
+            return rows
+        total = off[-1]
+        sc_off = -(-total // 16) * 16
+        scales = self.summaries[sc_off:sc_off + 4 * (total // self.head_dim)].view(torch.float32)
+        first = off[l - 1] // self.head_dim
+        sc = scales[first:first + self.batch * self.kv_heads * n].view(
+            self.batch, self.kv_heads, n, 1)
+        return _e4m3_values(rows) * sc
+
+
+def _e4m3_values(codes: torch.Tensor) -> torch.Tensor:
+    """float32 values of e4m3 codes (torch's own float8_e4m3fn decoding)."""
+    table = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).float()
+    return table.to(codes.device)[codes.long()]
 
 
 def summary_offsets(batch, kv_heads, head_dim, branching, levels):
