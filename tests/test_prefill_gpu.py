@@ -110,3 +110,43 @@ def test_causal_prefill_matches_oracle(tis, case):
          f"{int((~same & tie).sum())}); keys read per query {reads.mean():.2f} on average over "
          f"{N} positions (dense causal: {(N + 1) / 2:.1f}); max-abs {err:.2e}; "
          f"{time.time() - t0:.1f}s")
+
+
+@pytest.mark.timeout(900)
+def test_prefill_gqa_4096_positions_sampled(tis):
+    """The benchmark's prefill launch (the GQA workload's first 4,096 keys,
+    all 128 query heads, one query per position), checked at sampled
+    positions: the first, leaf and node boundaries, depth changes, the last."""
+    w = workloads.get("gqa_32k")
+    x = workloads.generate(w)
+    P = 4096
+    rng = np.random.default_rng(99)
+    q = O_widen(x["Q"], w.dtype)[:, :, None, :] + rng.standard_normal(
+        (w.batch, w.q_heads, P, w.head_dim))
+    Q = to_storage(q, w.dtype)
+    Kd = tis.from_storage(x["K"], w.dtype, "cuda")
+    Vd = tis.from_storage(x["V"], w.dtype, "cuda")
+    Qd = tis.from_storage(Q, w.dtype, "cuda")
+    ct = tis.CacheTree(Kd, Vd, w.branching, w.leaf_block)
+    ct.append(P)
+    out, idx = ct.causal_prefill(Qd, w.beam, return_indices=True)
+    torch.cuda.synchronize()
+    out, idx = out.cpu().numpy(), idx.cpu().numpy()
+    L = w.leaf_block
+    pos = np.unique(np.array([0, 1, L - 1, L, 8 * L - 1, 8 * L, 8 * L + 1, 64 * L - 1, 64 * L,
+                              1000, 2047, 2048, P - 2, P - 1]))
+    pos = pos[pos < P]
+    K = np.ascontiguousarray(x["K"][:, :, :P])
+    V = np.ascontiguousarray(x["V"][:, :, :P])
+    orc = C.causal_prefill(Q, K, V, w.dtype, w.branching, L, w.beam, positions=pos)
+    tie = orc["gap"] < parity.TIE_GAP
+    same = np.all(idx[:, :, pos] == orc["indices"], axis=-1)
+    assert np.all(same | tie), f"{np.count_nonzero(~same & ~tie)} sampled positions differ"
+    err = 0.0
+    for i, t in enumerate(pos):
+        o_g = GO.grow_attend(np.ascontiguousarray(Q[:, :, t]), K, V, w.dtype, idx[:, :, t],
+                             int(t) + 1, L)
+        err = max(err, parity.compare_outputs(out[:, :, t], o_g, w.dtype))
+    _say(f"gqa_32k prefill of {P} positions: {len(pos)} sampled positions x "
+         f"{w.batch * w.q_heads} queries exact {int(same.sum())}/{same.size} (tie-exposed "
+         f"{int((~same & tie).sum())}); max-abs {err:.2e}")
