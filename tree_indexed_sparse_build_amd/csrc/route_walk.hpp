@@ -301,8 +301,6 @@ __device__ int route_walk(const RouteArgs &a, RouteShared<NW> &sh, int qi,
   if (a.trace) {
     // levels above l0 keep every node that exists
     for (int l = 1; l < l0; ++l) {
-      int64_t span = a.leaf_block;
-      for (int h = 0; h < lv - l; ++h) span *= b;
       int64_t n = 1;
       for (int k = 0; k < l; ++k) n *= b;
       const int64_t e = LAYOUT == 2 ? cl->exist[l] : CACHE ? a.lvl_exist[l] : n;
