@@ -132,6 +132,9 @@ EDGE = [
     # deep binary tree: the levels above the chunk roots take the small
     # per-level kernels
     _custom("deep_binary", "bf16", 2, 4, 9, 6, d=64, Hkv=3, G=1),
+    # the deepest tree the library takes: 16 levels (binary, leaf blocks of
+    # one key, 65,536 keys)
+    _custom("max_levels_16", "f32", 2, 1, 16, 3, d=64, Hkv=1, G=2),
     # many heads, GQA group 8, batch 3
     _custom("gqa8_batch3", "bf16", 4, 32, 3, 6, B=3, Hkv=2, G=8),
     # few queries with long key sets: each query split over several
