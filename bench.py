@@ -302,9 +302,10 @@ def cache_decode_loop(tis, w, K, V, Q, steps, warmup):
     the first keys of the cache is filled by one long append, then every
     step appends one key per head (tis_cache_tree_append) and decodes every
     query (tis_cache_tree_decode).  Times: the long append, one-key appends
-    back to back, decodes back to back, and whole steps back to back."""
+    back to back, decodes back to back, whole steps back to back, and the
+    same step as one fused call (tis_cache_tree_append_decode)."""
     import torch
-    need = 3 * (steps + warmup) + 8
+    need = 4 * (steps + warmup) + 8
     prefill = w.n_keys - need
     if prefill < 1:
         return None
@@ -332,6 +333,10 @@ def cache_decode_loop(tis, w, K, V, Q, steps, warmup):
     step_us = timed(step, steps)
     append_us = timed(lambda: ct.append(1), steps)
     decode_us = timed(decode, steps)
+    fused = ct.bind_decode(Q, w.beam, out, append=True)
+    for _ in range(warmup):
+        fused()
+    fused_us = timed(fused, steps)
     kbytes = prefill * w.batch * w.kv_heads * w.head_dim * w.elem_bytes
     return {"regime": "tree over the first n keys of a cache of the workload's size; "
                       "one key appended per head per step",
@@ -339,7 +344,8 @@ def cache_decode_loop(tis, w, K, V, Q, steps, warmup):
             "prefill_keys": prefill, "prefill_us": prefill_us,
             "prefill_gbs": kbytes / (prefill_us * 1e-6) / 1e9,
             "append1_us": append_us, "decode_us": decode_us, "step_us": step_us,
-            "queries_per_s": w.queries / (step_us * 1e-6)}
+            "queries_per_s": w.queries / (step_us * 1e-6),
+            "fused_step_us": fused_us, "fused_queries_per_s": w.queries / (fused_us * 1e-6)}
 
 
 def main(argv=None):
@@ -543,7 +549,9 @@ def main(argv=None):
         log(f"growing cache: prefill append of {cache['prefill_keys']} keys/head "
             f"{cache['prefill_us']:.1f} us ({cache['prefill_gbs']:.1f} GB/s); append of 1 key "
             f"{cache['append1_us']:.2f} us; decode {cache['decode_us']:.2f} us; decode step "
-            f"(append + decode) {cache['step_us']:.2f} us -> {cache['queries_per_s']:.3e} queries/s")
+            f"(append + decode) {cache['step_us']:.2f} us -> {cache['queries_per_s']:.3e} queries/s; "
+            f"fused step {cache['fused_step_us']:.2f} us -> "
+            f"{cache['fused_queries_per_s']:.3e} queries/s")
 
     cpu = None
     if not args.no_cpu_baseline:

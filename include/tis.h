@@ -310,10 +310,15 @@ const char *tis_version(void);
  *              [B][Hkv][ceil(capacity / (L*b^h))][d], where H is the depth
  *              of a full cache; level l of a tree of depth lv lives at
  *              height lv - l, node n at row n of its (batch, head) block
- *   state      float64 [B][Hkv][H][d]: for every height h, the exact sum of
+ *   state      float64 [2][B][Hkv][H][d], two halves of which state_half
+ *              names the one in use: for every height h, the exact sum of
  *              the keys of the node that holds key n_keys (the open node;
  *              zero when n_keys is a multiple of L*b^h).  Appends start from
  *              it, which keeps every summary an exact mean rounded once.
+ *              tis_cache_tree_append updates the half in use in place;
+ *              tis_cache_tree_append_decode writes the other half and
+ *              switches to it (its workgroups read the old sums while one
+ *              of them writes the new ones).
  * Summaries are kept for every height up to H-1 whatever the current depth,
  * so a deeper tree finds its upper levels already in place.
  * --------------------------------------------------------------------- */
@@ -324,6 +329,7 @@ typedef struct tis_cache_tree {
   int32_t n_keys;    /* keys in the tree: set by reset (0) and append        */
   int32_t levels;    /* depth over n_keys (0 while empty): set by the library */
   int32_t summary_dtype; /* tis_dtype of the stored summaries (as tis_tree)  */
+  int32_t state_half; /* half of `state` in use (0 or 1): set by the library */
   void *summaries;   /* tis_cache_tree_summary_bytes_as() bytes              */
   double *state;     /* tis_cache_tree_state_bytes() bytes                   */
 } tis_cache_tree;
@@ -339,8 +345,8 @@ size_t tis_cache_tree_summary_bytes_as(int batch, int kv_heads, int head_dim, in
 size_t tis_cache_tree_state_bytes(int batch, int kv_heads, int head_dim, int branching,
                                   int leaf_block, int capacity);
 
-/* Empties the tree: n_keys = levels = 0 and the state zeroed (by a kernel
- * on `stream`).  The caller fills in the geometry fields and both pointers
+/* Empties the tree: n_keys = levels = state_half = 0 and both state
+ * halves zeroed (by a kernel on `stream`).  The caller fills in the geometry fields and both pointers
  * first.  Summaries need no clearing: only existing nodes are ever read. */
 tis_status tis_cache_tree_reset(tis_cache_tree *tree, void *stream);
 
@@ -369,6 +375,24 @@ tis_status tis_cache_tree_decode(const void *Q, const void *K, const void *V, ti
                                  int q_heads, const tis_cache_tree *tree, int beam, float scale,
                                  float *O, int32_t *indices, void *workspace,
                                  size_t workspace_bytes, void *stream);
+
+/* One decode step of a growing cache (ZHA Abstract: the tree grows with the
+ * context; ALHR Summary: one key arrives per decoded token): adds key n_keys
+ * (row n_keys of K and V, already written by the caller, for every batch
+ * and KV head) to the tree and decodes Q over the tree of n_keys + 1 keys,
+ * in one launch (two when the decode splits its queries).  Results, the
+ * summaries and the state left behind are those of
+ * tis_cache_tree_append(K, dtype, 1, tree) followed by
+ * tis_cache_tree_decode(...), bit for bit; n_keys, levels and state_half are
+ * updated when the work is enqueued.  Arguments as for tis_cache_tree_decode;
+ * requires n_keys < capacity (TIS_E_SHAPE otherwise, nothing launched).
+ * Only the node that holds the new key changes at each height, so every
+ * workgroup computes that node's new mean from the state and the key and
+ * reads every other node as stored. */
+tis_status tis_cache_tree_append_decode(const void *Q, const void *K, const void *V,
+                                        tis_dtype dtype, int q_heads, tis_cache_tree *tree,
+                                        int beam, float scale, float *O, int32_t *indices,
+                                        void *workspace, size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * Causal prefill routing

@@ -236,10 +236,11 @@ def test_cache_tree_bytes(lib):
     # ceil(40000 / 64) = 625, 79, 10, 2 per head
     heads, d = 4 * 8, 128
     assert lib.tis_cache_tree_summary_bytes(4, 8, d, 8, 64, 40000) == 4 * d * heads * (625 + 79 + 10 + 2)
-    assert lib.tis_cache_tree_state_bytes(4, 8, d, 8, 64, 40000) == 8 * d * heads * 4
+    # two halves of fp64 open-node sums, one row per height
+    assert lib.tis_cache_tree_state_bytes(4, 8, d, 8, 64, 40000) == 2 * 8 * d * heads * 4
     # a cache of one leaf: one height with one row
     assert lib.tis_cache_tree_summary_bytes(1, 1, 64, 2, 16, 10) == 4 * 64
-    assert lib.tis_cache_tree_state_bytes(1, 1, 64, 2, 16, 10) == 8 * 64
+    assert lib.tis_cache_tree_state_bytes(1, 1, 64, 2, 16, 10) == 2 * 8 * 64
     # invalid geometry -> 0
     assert lib.tis_cache_tree_summary_bytes(1, 1, 64, 1, 16, 100) == 0
     assert lib.tis_cache_tree_summary_bytes(1, 1, 96, 2, 16, 100) == 0
@@ -249,8 +250,10 @@ def test_cache_tree_bytes(lib):
 
 
 def _ctree(summ=FAKE, state=FAKE, B=1, H=1, d=64, b=2, L=16, C=1000, n=0, lv=0,
-           sd=_lib.TIS_F32):
-    return _lib.TisCacheTree(B, H, d, b, L, C, n, lv, sd, summ, state)
+           sd=_lib.TIS_F32, half=0):
+    return _lib.TisCacheTree(batch=B, kv_heads=H, head_dim=d, branching=b, leaf_block=L,
+                             capacity=C, n_keys=n, levels=lv, summary_dtype=sd, state_half=half,
+                             summaries=summ, state=state)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -339,6 +342,36 @@ def test_cache_decode_rejects(lib, tree_kw, call_kw, status):
                                      a["beam"], a["scale"], a["O"], a["idx"], a["ws"], a["wsb"],
                                      None) == status
     assert lib.tis_last_error().decode()
+
+
+@pytest.mark.parametrize("tree_kw,call_kw,status", [
+    (dict(n=100, lv=3), dict(Q=None), _lib.TIS_E_NULL),
+    (dict(n=100, lv=3), dict(K=None), _lib.TIS_E_NULL),
+    (dict(n=100, lv=3, state=None), dict(), _lib.TIS_E_NULL),
+    (dict(n=1000, lv=6), dict(), _lib.TIS_E_SHAPE),            # the cache is full
+    (dict(n=100, lv=4), dict(), _lib.TIS_E_SHAPE),             # levels do not match n_keys
+    (dict(n=100, lv=3, half=2), dict(), _lib.TIS_E_SHAPE),     # no such state half
+    (dict(n=100, lv=3, sd=_lib.TIS_FP8_E4M3), dict(), _lib.TIS_E_UNSUPPORTED),
+    (dict(n=100, lv=3), dict(dt=2), _lib.TIS_E_DTYPE),
+    (dict(n=100, lv=3, H=2), dict(Hq=3), _lib.TIS_E_SHAPE),
+    (dict(n=100, lv=3), dict(beam=0), _lib.TIS_E_SHAPE),
+    (dict(n=100, lv=3), dict(beam=200), _lib.TIS_E_UNSUPPORTED),
+    (dict(n=100, lv=3), dict(scale=float("inf")), _lib.TIS_E_SHAPE),
+    (dict(n=100, lv=3), dict(V=FAKE + 8), _lib.TIS_E_ALIGN),
+    (dict(n=30000, lv=4, d=128, b=4, L=128, C=30001), dict(beam=64, Hq=2), _lib.TIS_E_NULL),
+])
+def test_cache_append_decode_rejects(lib, tree_kw, call_kw, status):
+    """A rejected step launches nothing and leaves the tree as it was."""
+    t = _ctree(**tree_kw)
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, dt=_lib.TIS_BF16, Hq=2, beam=4, scale=0.0, O=FAKE, idx=None,
+             ws=None, wsb=0)
+    a.update(call_kw)
+    assert lib.tis_cache_tree_append_decode(a["Q"], a["K"], a["V"], a["dt"], a["Hq"],
+                                            ctypes.byref(t), a["beam"], a["scale"], a["O"],
+                                            a["idx"], a["ws"], a["wsb"], None) == status
+    assert lib.tis_last_error().decode()
+    assert (t.n_keys, t.levels, t.state_half) == (tree_kw.get("n", 0), tree_kw.get("lv", 0),
+                                                  tree_kw.get("half", 0))
 
 
 def test_caller_buffers_must_match():

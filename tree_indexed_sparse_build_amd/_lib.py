@@ -39,7 +39,7 @@ class TisCacheTree(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("branching", ctypes.c_int32),
                 ("leaf_block", ctypes.c_int32), ("capacity", ctypes.c_int32),
                 ("n_keys", ctypes.c_int32), ("levels", ctypes.c_int32),
-                ("summary_dtype", ctypes.c_int32),
+                ("summary_dtype", ctypes.c_int32), ("state_half", ctypes.c_int32),
                 ("summaries", ctypes.c_void_p), ("state", ctypes.c_void_p)]
 
 
@@ -76,6 +76,9 @@ SIGNATURES = {
     "tis_cache_tree_decode": (_c_int, [_vp, _vp, _vp, _c_int, _c_int,
                                        ctypes.POINTER(TisCacheTree), _c_int, _c_float, _vp, _vp,
                                        _vp, _c_size, _vp]),
+    "tis_cache_tree_append_decode": (_c_int, [_vp, _vp, _vp, _c_int, _c_int,
+                                              ctypes.POINTER(TisCacheTree), _c_int, _c_float, _vp,
+                                              _vp, _vp, _c_size, _vp]),
     "tis_tree_radius_bytes": (_c_size, [_c_int] * 4),
     "tis_radius_workspace_bytes": (_c_size, [_c_int] * 4),
     "tis_tree_radii": (_c_int, [_vp, _c_int, ctypes.POINTER(TisTree), _vp, _vp, _c_size, _vp]),

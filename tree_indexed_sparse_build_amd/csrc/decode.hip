@@ -9,6 +9,21 @@
 // With few queries each query gets `splits` workgroups that all walk the
 // tree and each attend over a share of the kept leaves; a small combine
 // kernel merges their partial softmax states.
+//
+// Fused one-key append + decode over a growing cache (k_decode_append).
+// Adding key t = n0 to the tree changes one node per height: the node that
+// holds t, whose new sum is the old open sum (zero when t starts the node)
+// plus the key; every other node keeps its summary.  So every workgroup can
+// decode over the tree of t + 1 keys without waiting for any summary to be
+// rewritten: it reads the stored rows of the unchanged nodes, and for the
+// node holding t (the last existing node of each level) it computes the new
+// mean from the state and the key itself, scored in fp64 by its idle waves
+// while the walking waves score the first cut level.  One workgroup per
+// (batch, KV head) (part 0 of the group's first query head) also stores the
+// new means and sums; the sums go to the other of two state buffers, so no
+// workgroup that still reads the old sums sees the new ones.  The summaries
+// and state it leaves are the ones a separate one-key append writes, bit for
+// bit, and the step costs one launch instead of two.
 #include "attend_query.hpp"
 #include "route_walk.hpp"
 
@@ -18,16 +33,12 @@ namespace {
 constexpr int kDecodeWaves = 16;
 constexpr int kDecodeWalkWaves = 8;  // waves that walk the tree (see route_walk)
 
-template <typename T, typename S, int D, bool CACHE>
-__global__ void __launch_bounds__(kDecodeWaves * 64) k_decode(RouteArgs ra, AttendArgs aa) {
-  __shared__ RouteShared<kDecodeWaves> rsh;
-  __shared__ AttendShared<T, D> ash;
-  // part sp of query qi (see k_attend: a query's parts share an XCD)
-  const int sp = blockIdx.x / aa.queries;
-  const int qi = query_of_slot(blockIdx.x - sp * aa.queries, aa.queries, aa.group);
-  const uint4 qraw = attend_q_raw<T, D>(aa, qi);  // in flight during the walk
-  // every part walks the tree (the repeated summary reads hit the XCD's L2)
-  const int kept = route_walk<T, S, D, kDecodeWaves, kDecodeWalkWaves, CACHE>(ra, rsh, qi);
+// After the walk: the kept leaves out (part 0, when asked for), then part
+// sp's share of them attended.
+template <typename T, int D, bool CACHE>
+__device__ inline void decode_attend(const RouteArgs &ra, const AttendArgs &aa,
+                                     RouteShared<kDecodeWaves> &rsh, AttendShared<T, D> &ash,
+                                     int qi, int sp, uint4 qraw, int kept) {
   if (ra.indices && sp == 0) {
     int32_t *out = ra.indices + static_cast<int64_t>(qi) * ra.beam;
     write_ascending<kDecodeWaves * 64>(rsh.front, kept, out);
@@ -40,6 +51,112 @@ __global__ void __launch_bounds__(kDecodeWaves * 64) k_decode(RouteArgs ra, Atte
                     ? aa.part + (static_cast<int64_t>(qi) * aa.splits + sp) * (D + kPartHeader)
                     : nullptr;
   attend_query<T, D, CACHE>(aa, ash, qi, qraw, rsh.front + s0, nullptr, s1 - s0, false, part);
+}
+
+template <typename T, typename S, int D, bool CACHE>
+__global__ void __launch_bounds__(kDecodeWaves * 64) k_decode(RouteArgs ra, AttendArgs aa) {
+  __shared__ RouteShared<kDecodeWaves> rsh;
+  __shared__ AttendShared<T, D> ash;
+  // part sp of query qi (see k_attend: a query's parts share an XCD)
+  const int sp = blockIdx.x / aa.queries;
+  const int qi = query_of_slot(blockIdx.x - sp * aa.queries, aa.queries, aa.group);
+  const uint4 qraw = attend_q_raw<T, D>(aa, qi);  // in flight during the walk
+  // every part walks the tree (the repeated summary reads hit the XCD's L2)
+  const int kept = route_walk<T, S, D, kDecodeWaves, kDecodeWalkWaves, CACHE>(ra, rsh, qi);
+  decode_attend<T, D, CACHE>(ra, aa, rsh, ash, qi, sp, qraw, kept);
+}
+
+template <typename T> __device__ inline float widen1(const T *p);
+template <> __device__ inline float widen1<float>(const float *p) { return *p; }
+template <> __device__ inline float widen1<bf16_bits>(const bf16_bits *p) {
+  return __uint_as_float(static_cast<uint32_t>(p->v) << 16);
+}
+
+// The node holding the new key t at every height: new sum (old open sum +
+// key, in fp64, as a one-key append adds it), new mean rounded once to the
+// summary type and, for the levels of the tree, its fp64 score with query
+// qi (the walk's lane layout and arithmetic) into open_score[level]; at the
+// first cut level also its ranking key.  The writer also stores the means
+// (every height of the cache, as an append does) and the new sums.  Run by
+// the waves that do not walk, before the walk's first barrier.
+template <typename T, typename S, int D>
+__device__ void open_nodes(const RouteArgs &ra, const AppendArgs &ap, int qi, bool writer,
+                           uint64_t *keys, double *open_score) {
+  constexpr int NP = kDecodeWaves - kDecodeWalkWaves;  // waves taking part
+  constexpr int E = RowLoad<S>::E;
+  constexpr int LPR = D / E;   // lanes per row
+  constexpr int RPI = 64 / LPR;  // rows (heights) per wave
+  const int lane = threadIdx.x & 63;
+  const int pw = (static_cast<int>(threadIdx.x) >> 6) - kDecodeWalkWaves;
+  const int bi = qi / ra.q_heads;
+  const int hq = qi - bi * ra.q_heads;
+  const int64_t head = static_cast<int64_t>(bi) * ra.kv_heads + hq / ra.group;
+  const int col = (lane % LPR) * E;
+  const int lv = ra.levels;
+  const int nh = writer ? ap.heights : lv;
+  const uint32_t t = static_cast<uint32_t>(ap.n0);
+  const T *key = static_cast<const T *>(ap.K) + (head * ap.capacity + t) * D + col;
+  const T *qp = static_cast<const T *>(ra.Q) + static_cast<int64_t>(qi) * D + col;
+  float kf[E], qf[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    kf[e] = widen1<T>(key + e);
+    qf[e] = widen1<T>(qp + e);
+  }
+  S *const summ = static_cast<S *>(ap.summ);
+  // the loop bound is uniform over the wave (whole row groups drop out
+  // through `act`), so the cross-lane sums always have their partners
+  for (int h0 = pw * RPI; h0 < nh; h0 += NP * RPI) {
+    const int h = h0 + lane / LPR;
+    const bool act = h < nh;
+    const int hh = act ? h : 0;
+    const uint32_t span = ap.span[hh];
+    const uint32_t held = t % span + 1u;  // keys of t's node up to t
+    const double *st = ap.state + (head * ap.heights + hh) * D + col;
+    S *row = summ + ap.block_off[hh] + (head * ap.rows[hh] + t / span) * D + col;
+    double *nx = ap.state_next + (head * ap.heights + hh) * D + col;
+    const bool store = writer && act;
+    const bool closed = held == span;  // t completes its node: the next starts empty
+    double v[1];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const double sum = st[e] + static_cast<double>(kf[e]);
+      const double mean = sum / static_cast<double>(held);
+      if (store) {
+        SummaryType<S>::put(row + e, mean);
+        nx[e] = closed ? 0.0 : sum;
+      }
+      // the walk's dot: fp64 products of exact float32 values, fma chain
+      const double f = SummaryType<S>::value(mean);
+      v[0] = e == 0 ? static_cast<double>(qf[0]) * f : fma(static_cast<double>(qf[e]), f, v[0]);
+    }
+    const double s = group_transpose_reduce<1, LPR>(v, lane);
+    if (act && h < lv && lane % LPR == 0) {
+      const int l = lv - h;
+      open_score[l] = s;
+      if (l == ra.first_cut) {
+        const int last = static_cast<int>(ra.lvl_exist[l]) - 1;
+        keys[last] = score_key(s, last, 32 - __clz(last));
+      }
+    }
+  }
+}
+
+template <typename T, typename S, int D>
+__global__ void __launch_bounds__(kDecodeWaves * 64)
+    k_decode_append(RouteArgs ra, AttendArgs aa, AppendArgs ap) {
+  __shared__ RouteShared<kDecodeWaves> rsh;
+  __shared__ AttendShared<T, D> ash;
+  __shared__ double open_score[kMaxLevels + 1];
+  const int sp = blockIdx.x / aa.queries;
+  const int qi = query_of_slot(blockIdx.x - sp * aa.queries, aa.queries, aa.group);
+  const uint4 qraw = attend_q_raw<T, D>(aa, qi);
+  const bool writer = sp == 0 && (qi % ra.q_heads) % ra.group == 0;
+  const auto prep = [&]() { open_nodes<T, S, D>(ra, ap, qi, writer, rsh.keys, open_score); };
+  const int kept =
+      route_walk<T, S, D, kDecodeWaves, kDecodeWalkWaves, 1, kMaxCandidates, decltype(prep)>(
+          ra, rsh, qi, nullptr, nullptr, -1, prep, open_score);
+  decode_attend<T, D, true>(ra, aa, rsh, ash, qi, sp, qraw, kept);
 }
 
 template <typename T, typename S, bool CACHE>
@@ -63,7 +180,35 @@ hipError_t launch_decode_ts(int head_dim, const RouteArgs &ra, const AttendArgs 
                   : launch_decode_t<T, S, false>(head_dim, ra, aa, s);
 }
 
+template <typename T, typename S>
+hipError_t launch_decode_append_ts(int head_dim, const RouteArgs &ra, const AttendArgs &aa,
+                                   const AppendArgs &ap, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(ra.queries) * static_cast<unsigned>(aa.splits));
+  const dim3 block(kDecodeWaves * 64);
+  if (head_dim == 128)
+    hipLaunchKernelGGL((k_decode_append<T, S, 128>), grid, block, 0, s, ra, aa, ap);
+  else if (head_dim == 64)
+    hipLaunchKernelGGL((k_decode_append<T, S, 64>), grid, block, 0, s, ra, aa, ap);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_decode_append(Dt dt, Dt sdt, int head_dim, const RouteArgs &ra,
+                                const AttendArgs &aa, const AppendArgs &ap, hipStream_t s) {
+  hipError_t e;
+  if (sdt == Dt::FP8 || !ra.cache) return hipErrorInvalidValue;
+  if (dt == Dt::BF16)
+    e = sdt == Dt::BF16 ? launch_decode_append_ts<bf16_bits, bf16_bits>(head_dim, ra, aa, ap, s)
+                        : launch_decode_append_ts<bf16_bits, float>(head_dim, ra, aa, ap, s);
+  else
+    e = sdt == Dt::BF16 ? launch_decode_append_ts<float, bf16_bits>(head_dim, ra, aa, ap, s)
+                        : launch_decode_append_ts<float, float>(head_dim, ra, aa, ap, s);
+  if (e != hipSuccess || aa.splits <= 1) return e;
+  return launch_combine(head_dim, aa, s);
+}
 
 hipError_t launch_decode(Dt dt, Dt sdt, int head_dim, const RouteArgs &ra,
                          const AttendArgs &aa, hipStream_t s) {

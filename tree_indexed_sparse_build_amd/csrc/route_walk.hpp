@@ -196,6 +196,12 @@ struct NoScale {
   __device__ float operator()(int) const { return 1.f; }
 };
 
+// The walk's optional side job for the waves that do not walk (see
+// route_walk): the default does nothing.
+struct NoPrep {
+  __device__ void operator()() const {}
+};
+
 template <typename T, typename S, int D, int UU, bool HOLES, typename NodeOf, typename RowOf,
           typename Emit, typename ScaleOf = NoScale>
 __device__ inline void score_rows(RowOf row_of, int C, NodeOf node_of, Emit emit,
@@ -261,13 +267,23 @@ __device__ inline void score_rows(RowOf row_of, int C, NodeOf node_of, Emit emit
 // starts about a microsecond after the first), so leaving the late waves out
 // of the walk keeps them off its critical path: they only have to reach
 // each barrier, and the attention after the walk is where they are needed.
+//
+// With a Prep other than NoPrep (growing cache only), the waves that do not
+// walk run prep() while the walking waves score level l0, and the score of
+// the last existing node of each level (the open node, whose stored row is
+// not current) comes from open_score[l] instead of its row: prep() must fill
+// open_score[l] for l0 < l <= levels and write level l0's key of that node
+// into sh.keys, all before the walk's first barrier.
 template <typename T, typename S, int D, int NW, int NRW, int LAYOUT,
-          int MAXC = kMaxCandidates>
+          int MAXC = kMaxCandidates, typename Prep = NoPrep>
 __device__ int route_walk(const RouteArgs &a, RouteShared<NW> &sh, int qi,
                           const CausalLevels *cl = nullptr, const void *open_summ = nullptr,
-                          int hrow = -1) {
+                          int hrow = -1, const Prep &prep = Prep(),
+                          const double *open_score = nullptr) {
   constexpr bool CACHE = LAYOUT != 0;  // nodes past the last key may be missing
+  constexpr bool OPEN = !__is_same(Prep, NoPrep);
   static_assert(!kIsFp8<S> || LAYOUT == 0, "fp8 summaries: full tree only");
+  static_assert(!OPEN || (LAYOUT == 1 && NRW < NW), "open-node scores: growing cache, idle waves");
   constexpr int NT = NW * 64;
   constexpr int LOG_NRT = NRW == 16 ? 10 : NRW == 8 ? 9 : NRW == 4 ? 8 : -1;
   static_assert(LOG_NRT > 0 && NRW <= NW, "4, 8 or 16 walking waves");
@@ -295,6 +311,10 @@ __device__ int route_walk(const RouteArgs &a, RouteShared<NW> &sh, int qi,
 
   QRaw<T, E> qr;
   qr.load(static_cast<const T *>(a.Q) + static_cast<int64_t>(qi) * D + col);
+
+  if constexpr (OPEN) {
+    if (w >= NRW) prep();
+  }
 
   LevelCursor<LAYOUT> lc;
   lc.init(a, cl, l0, D);
@@ -358,6 +378,13 @@ __device__ int route_walk(const RouteArgs &a, RouteShared<NW> &sh, int qi,
       const auto node_of = [&](int p) { return all ? p : cand[p]; };
       uint64_t *keys = sh.keys;
       const auto emit = [&](int pos, int nd, double s) {
+        if constexpr (OPEN) {
+          // the open node: prep() wrote its key at l0 and its score below
+          if (nd == last) {
+            if (l != l0) keys[pos] = score_key(open_score[l], nd, bits);
+            return;
+          }
+        }
         // a hole (a child past the end of a growing cache) gets key 0, below
         // every real key, so it is never ranked among the kept
         keys[pos] = CACHE && nd < 0 ? 0ull : score_key(s, nd, bits);

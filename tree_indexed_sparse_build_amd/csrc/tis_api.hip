@@ -481,7 +481,7 @@ tis_status check_cache(const char *who, int batch, int kv_heads, int head_dim, i
     span *= branching;
   }
   g->summ_elems = elems;
-  g->state_elems = g->heads * H * head_dim;
+  g->state_elems = g->heads * H * head_dim;  // one of the two halves
   return TIS_OK;
 }
 
@@ -495,6 +495,8 @@ tis_status check_cache_tree(const char *who, const tis_cache_tree *t, CacheGeome
   if (st != TIS_OK) return st;
   if (!aligned(t->summaries, 16) || !aligned(t->state, 16))
     return fail(TIS_E_ALIGN, "%s: summaries and state need 16-byte alignment", who);
+  if (t->state_half != 0 && t->state_half != 1)
+    return fail(TIS_E_SHAPE, "%s: state_half %d is neither 0 nor 1", who, t->state_half);
   if (t->n_keys < 0 || t->n_keys > t->capacity)
     return fail(TIS_E_SHAPE, "%s: n_keys %d outside [0, capacity %d]", who, t->n_keys,
                 t->capacity);
@@ -572,6 +574,61 @@ tis_status check_cache_query(const char *who, const void *Q, tis_dtype dtype, in
   return TIS_OK;
 }
 
+// Append arguments of keys [n_keys, n_keys + n_new) of a checked tree: the
+// state in use and the other half, per-height offsets, rows and spans.
+tis::AppendArgs cache_append_args(const void *K, const tis_cache_tree *t, const CacheGeometry &g,
+                                  int n_new) {
+  tis::AppendArgs a{};
+  a.K = K;
+  a.summ = t->summaries;
+  a.state = t->state + (t->state_half ? g.state_elems : 0);
+  a.state_next = t->state + (t->state_half ? 0 : g.state_elems);
+  a.heads = g.heads;
+  a.capacity = t->capacity;
+  a.n0 = t->n_keys;
+  a.n1 = static_cast<int64_t>(t->n_keys) + n_new;
+  a.leaf_block = t->leaf_block;
+  a.branching = t->branching;
+  a.heights = g.heights;
+  int64_t span = t->leaf_block, off = 0;
+  for (int h = 0; h < g.heights; ++h) {
+    const int64_t rows = (t->capacity + span - 1) / span;
+    a.block_off[h] = off;
+    a.rows[h] = static_cast<uint32_t>(rows);
+    // L b^h < capacity for h < H - 1 by the choice of H, and L b^(H-1)
+    // < capacity too unless H = 1 (then it is L): 32 bits always hold it
+    a.span[h] = static_cast<uint32_t>(span);
+    off += g.heads * rows * t->head_dim;
+    span *= t->branching;
+  }
+  return a;
+}
+
+// Attend arguments of a decode over the first n_keys keys of a cache.
+tis::AttendArgs cache_attend_args(const void *Q, const void *K, const void *V, float *O,
+                                  const tis_cache_tree *t, int q_heads, int beam, float scale,
+                                  int64_t queries, int64_t n_keys) {
+  const double sc =
+      scale > 0.f ? static_cast<double>(scale) : 1.0 / sqrt(static_cast<double>(t->head_dim));
+  tis::AttendArgs aa{};
+  aa.Q = Q;
+  aa.K = K;
+  aa.V = V;
+  aa.indices = nullptr;
+  aa.O = O;
+  aa.queries = static_cast<int>(queries);
+  aa.n_keys = n_keys;
+  aa.key_stride = t->capacity;
+  aa.q_heads = q_heads;
+  aa.kv_heads = t->kv_heads;
+  aa.group = q_heads / t->kv_heads;
+  aa.leaf_block = t->leaf_block;
+  aa.beam = beam;
+  aa.n_blocks = (n_keys + t->leaf_block - 1) / t->leaf_block;
+  aa.scale_log2 = static_cast<float>(sc * 1.4426950408889634);
+  return aa;
+}
+
 }  // namespace
 
 size_t tis_cache_tree_summary_bytes(int batch, int kv_heads, int head_dim, int branching,
@@ -596,7 +653,7 @@ size_t tis_cache_tree_state_bytes(int batch, int kv_heads, int head_dim, int bra
   if (check_cache("tis_cache_tree_state_bytes", batch, kv_heads, head_dim, branching,
                   leaf_block, capacity, &g) != TIS_OK)
     return 0;
-  return static_cast<size_t>(g.state_elems) * sizeof(double);
+  return 2 * static_cast<size_t>(g.state_elems) * sizeof(double);
 }
 
 tis_status tis_cache_tree_reset(tis_cache_tree *tree, void *stream) {
@@ -611,12 +668,13 @@ tis_status tis_cache_tree_reset(tis_cache_tree *tree, void *stream) {
   if (st != TIS_OK) return st;
   if (!aligned(tree->summaries, 16) || !aligned(tree->state, 16))
     return fail(TIS_E_ALIGN, "tis_cache_tree_reset: summaries and state need 16-byte alignment");
-  st = hip_status(tis::launch_fill_zero(tree->state, g.state_elems,
+  st = hip_status(tis::launch_fill_zero(tree->state, 2 * g.state_elems,
                                           static_cast<hipStream_t>(stream)),
                   "tis_cache_tree_reset launch");
   if (st != TIS_OK) return st;
   tree->n_keys = 0;
   tree->levels = 0;
+  tree->state_half = 0;
   return TIS_OK;
 }
 
@@ -635,30 +693,7 @@ tis_status tis_cache_tree_append(const void *K, tis_dtype dtype, int n_new, tis_
   if (n_new == 0) return TIS_OK;
   if (g.heads > 0x7fffffffLL)
     return fail(TIS_E_UNSUPPORTED, "tis_cache_tree_append: too many heads");
-  tis::AppendArgs a{};
-  a.K = K;
-  a.summ = tree->summaries;
-  a.state = tree->state;
-  a.heads = g.heads;
-  a.capacity = tree->capacity;
-  a.n0 = tree->n_keys;
-  a.n1 = static_cast<int64_t>(tree->n_keys) + n_new;
-  a.leaf_block = tree->leaf_block;
-  a.branching = tree->branching;
-  a.heights = g.heights;
-  {
-    int64_t span = tree->leaf_block, off = 0;
-    for (int h = 0; h < g.heights; ++h) {
-      const int64_t rows = (tree->capacity + span - 1) / span;
-      a.block_off[h] = off;
-      a.rows[h] = static_cast<uint32_t>(rows);
-      // L b^h < capacity for h < H - 1 by the choice of H, and L b^(H-1)
-      // < capacity too unless H = 1 (then it is L): 32 bits always hold it
-      a.span[h] = static_cast<uint32_t>(span);
-      off += g.heads * rows * tree->head_dim;
-      span *= tree->branching;
-    }
-  }
+  const tis::AppendArgs a = cache_append_args(K, tree, g, n_new);  // state updated in place
   const tis::Dt dt = dtype == TIS_BF16 ? tis::Dt::BF16 : tis::Dt::F32;
   st = hip_status(tis::launch_cache_append(dt, to_dt(tree->summary_dtype), tree->head_dim, a,
                                            static_cast<hipStream_t>(stream)),
@@ -703,24 +738,8 @@ tis_status tis_cache_tree_decode(const void *Q, const void *K, const void *V, ti
   if (!aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || (indices && !aligned(indices, 4)))
     return fail(TIS_E_ALIGN, "tis_cache_tree_decode: K, V and O need 16-byte alignment");
   const tis::RouteArgs ra = cache_route_args(Q, tree, q_heads, beam, indices, nullptr, queries);
-  const double sc =
-      scale > 0.f ? static_cast<double>(scale) : 1.0 / sqrt(static_cast<double>(tree->head_dim));
-  tis::AttendArgs aa{};
-  aa.Q = Q;
-  aa.K = K;
-  aa.V = V;
-  aa.indices = nullptr;
-  aa.O = O;
-  aa.queries = static_cast<int>(queries);
-  aa.n_keys = tree->n_keys;
-  aa.key_stride = tree->capacity;
-  aa.q_heads = q_heads;
-  aa.kv_heads = tree->kv_heads;
-  aa.group = q_heads / tree->kv_heads;
-  aa.leaf_block = tree->leaf_block;
-  aa.beam = beam;
-  aa.n_blocks = (static_cast<int64_t>(tree->n_keys) + tree->leaf_block - 1) / tree->leaf_block;
-  aa.scale_log2 = static_cast<float>(sc * 1.4426950408889634);
+  tis::AttendArgs aa =
+      cache_attend_args(Q, K, V, O, tree, q_heads, beam, scale, queries, tree->n_keys);
   st = plan_split("tis_cache_tree_decode", queries, tree->head_dim, beam, tree->leaf_block,
                   workspace, workspace_bytes, &aa);
   if (st != TIS_OK) return st;
@@ -728,6 +747,46 @@ tis_status tis_cache_tree_decode(const void *Q, const void *K, const void *V, ti
   return hip_status(tis::launch_decode(dt, to_dt(tree->summary_dtype), tree->head_dim, ra, aa,
                                       static_cast<hipStream_t>(stream)),
                     "tis_cache_tree_decode launch");
+}
+
+tis_status tis_cache_tree_append_decode(const void *Q, const void *K, const void *V,
+                                        tis_dtype dtype, int q_heads, tis_cache_tree *tree,
+                                        int beam, float scale, float *O, int32_t *indices,
+                                        void *workspace, size_t workspace_bytes, void *stream) {
+  const char *who = "tis_cache_tree_append_decode";
+  if (!Q || !K || !V || !O) return fail(TIS_E_NULL, "%s: Q, K, V and O are required", who);
+  CacheGeometry g;
+  tis_status st = check_cache_tree(who, tree, &g);
+  if (st != TIS_OK) return st;
+  if (tree->n_keys >= tree->capacity)
+    return fail(TIS_E_SHAPE, "%s: the cache is full (capacity %d)", who, tree->capacity);
+  // the decode is over the tree with the new key in it
+  tis_cache_tree next = *tree;
+  next.n_keys = tree->n_keys + 1;
+  next.levels = cache_depth(next.n_keys, tree->branching, tree->leaf_block);
+  int64_t queries = 0;
+  st = check_cache_query(who, Q, dtype, q_heads, &next, beam, &g, &queries);
+  if (st != TIS_OK) return st;
+  if (!(scale == scale) || isinf(scale)) return fail(TIS_E_SHAPE, "%s: scale must be finite", who);
+  if (!aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || (indices && !aligned(indices, 4)))
+    return fail(TIS_E_ALIGN, "%s: K, V and O need 16-byte alignment", who);
+  if (g.heads > 0x7fffffffLL) return fail(TIS_E_UNSUPPORTED, "%s: too many heads", who);
+  const tis::RouteArgs ra = cache_route_args(Q, &next, q_heads, beam, indices, nullptr, queries);
+  tis::AttendArgs aa =
+      cache_attend_args(Q, K, V, O, &next, q_heads, beam, scale, queries, next.n_keys);
+  st = plan_split(who, queries, tree->head_dim, beam, tree->leaf_block, workspace,
+                  workspace_bytes, &aa);
+  if (st != TIS_OK) return st;
+  const tis::AppendArgs ap = cache_append_args(K, tree, g, 1);
+  const tis::Dt dt = dtype == TIS_BF16 ? tis::Dt::BF16 : tis::Dt::F32;
+  st = hip_status(tis::launch_decode_append(dt, to_dt(tree->summary_dtype), tree->head_dim, ra,
+                                            aa, ap, static_cast<hipStream_t>(stream)),
+                  "tis_cache_tree_append_decode launch");
+  if (st != TIS_OK) return st;
+  tree->n_keys = next.n_keys;
+  tree->levels = next.levels;
+  tree->state_half ^= 1;
+  return TIS_OK;
 }
 
 // -------------------------------------------------------- causal prefill --

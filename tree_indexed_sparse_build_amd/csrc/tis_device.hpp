@@ -121,10 +121,15 @@ template <typename S> struct SummaryType;
 template <> struct SummaryType<float> {
   __device__ static inline float from_mean(double m) { return static_cast<float>(m); }
   __device__ static inline void put(float *p, double m) { *p = static_cast<float>(m); }
+  // the stored value, as float32
+  __device__ static inline float value(double m) { return static_cast<float>(m); }
 };
 template <> struct SummaryType<bf16_bits> {
   __device__ static inline bf16_bits from_mean(double m) { return bf16_bits{bf16_from_double(m)}; }
   __device__ static inline void put(bf16_bits *p, double m) { p->v = bf16_from_double(m); }
+  __device__ static inline float value(double m) {
+    return __uint_as_float(static_cast<uint32_t>(bf16_from_double(m)) << 16);
+  }
 };
 
 __device__ inline uint4 load16(const void *p) {

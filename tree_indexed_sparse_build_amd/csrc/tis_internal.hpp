@@ -131,7 +131,8 @@ hipError_t launch_decode(Dt dt, Dt sdt, int head_dim, const RouteArgs &ra,
 struct AppendArgs {
   const void *K;
   void *summ;            // float or bf16 bits (the summary type)
-  double *state;
+  double *state;         // the open-node sums before the append
+  double *state_next;    // fused append + decode: where the sums after it go
   int64_t heads;         // B * Hkv
   int64_t capacity;
   int64_t n0, n1;        // n1 <= capacity < 2^31
@@ -143,6 +144,13 @@ struct AppendArgs {
   uint32_t rows[kMaxLevels];
   uint32_t span[kMaxLevels];   // L b^h: below the capacity (or L itself when H = 1)
 };
+
+// Append of one key (n1 = n0 + 1) fused with a decode over the tree of n1
+// keys: ra and aa describe the decode at n1, ap the append, with the state
+// read from ap.state and written to ap.state_next (two buffers, so that the
+// workgroups that read the old sums never see the new ones).
+hipError_t launch_decode_append(Dt dt, Dt sdt, int head_dim, const RouteArgs &ra,
+                                const AttendArgs &aa, const AppendArgs &ap, hipStream_t s);
 
 // zero `elems` doubles with a kernel (no memset node, so it can sit in a graph)
 hipError_t launch_fill_zero(double *p, int64_t elems, hipStream_t s);

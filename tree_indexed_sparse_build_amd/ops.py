@@ -441,7 +441,7 @@ class CacheTree:
             raise _lib.TisError(_lib.TIS_E_SHAPE, "invalid cache geometry")
         self.summaries = torch.empty(sb // tdt.itemsize, dtype=tdt, device=K.device)
         self.state = torch.empty(stb // 8, dtype=torch.float64, device=K.device)
-        self.c = TisCacheTree(B, H, d, branching, leaf_block, C, 0, 0, code,
+        self.c = TisCacheTree(B, H, d, branching, leaf_block, C, 0, 0, code, 0,
                               self.summaries.data_ptr(), self.state.data_ptr())
         self._cref = ctypes.byref(self.c)
         self._kptr = K.data_ptr()
@@ -529,10 +529,12 @@ class CacheTree:
         return (O, idx) if return_indices else O
 
     def bind_decode(self, Q: torch.Tensor, beam: int, out: torch.Tensor,
-                    scale: Optional[float] = None):
+                    scale: Optional[float] = None, append: bool = False):
         """A zero-argument callable that decodes Q into `out` on the current
         stream with every argument prepared once (for decode loops, where the
-        host cost of a call would otherwise exceed the kernel's)."""
+        host cost of a call would otherwise exceed the kernel's).  With
+        append=True each call is append_decode: it first adds key n_keys
+        (already written into K and V) to the tree."""
         _need_device(Q)
         if Q.dtype != self.K.dtype:
             raise TypeError("Q must have the cache's dtype")
@@ -541,7 +543,7 @@ class CacheTree:
         L = lib()
         wsb = L.tis_decode_workspace_bytes(B, Hq, d, beam, self.c.leaf_block)
         ws = _workspace(Q.device, "decode", wsb) if wsb else None
-        f = L.tis_cache_tree_decode
+        f = L.tis_cache_tree_append_decode if append else L.tis_cache_tree_decode
         args = (Q.data_ptr(), self.K.data_ptr(), self.V.data_ptr(), self.dt, Hq,
                 ctypes.byref(self.c), beam, 0.0 if scale is None else float(scale),
                 out.data_ptr(), None, ws.data_ptr() if ws is not None else None,
@@ -554,9 +556,17 @@ class CacheTree:
             check(f(*args, _stream(dev)))
         return run
 
+    def append_decode(self, Q: torch.Tensor, beam: int, scale: Optional[float] = None,
+                      return_indices: bool = False, out: Optional[torch.Tensor] = None,
+                      indices: Optional[torch.Tensor] = None):
+        """One decode step: add key n_keys (already written into K and V) to
+        the tree and decode Q over the tree with it, in one launch.  Same
+        results and tree as append(1) followed by decode(...)."""
+        return self.decode(Q, beam, scale, return_indices, out, indices, _append=True)
+
     def decode(self, Q: torch.Tensor, beam: int, scale: Optional[float] = None,
                return_indices: bool = False, out: Optional[torch.Tensor] = None,
-               indices: Optional[torch.Tensor] = None):
+               indices: Optional[torch.Tensor] = None, _append: bool = False):
         """Route and attend every query over the cache in one launch."""
         _need_device(Q)
         if Q.dtype != self.K.dtype:
@@ -573,10 +583,10 @@ class CacheTree:
         L = lib()
         wsb = L.tis_decode_workspace_bytes(B, Hq, d, beam, self.c.leaf_block)
         ws = _workspace(Q.device, "decode", wsb) if wsb else None
-        check(L.tis_cache_tree_decode(Q.data_ptr(), self.K.data_ptr(), self.V.data_ptr(),
-                                      self.dt, Hq, ctypes.byref(self.c), beam,
-                                      0.0 if scale is None else float(scale), O.data_ptr(),
-                                      idx.data_ptr() if idx is not None else None,
-                                      ws.data_ptr() if ws is not None else None,
-                                      ws.numel() if ws is not None else 0, _stream(Q.device)))
+        f = L.tis_cache_tree_append_decode if _append else L.tis_cache_tree_decode
+        check(f(Q.data_ptr(), self.K.data_ptr(), self.V.data_ptr(), self.dt, Hq,
+                ctypes.byref(self.c), beam, 0.0 if scale is None else float(scale), O.data_ptr(),
+                idx.data_ptr() if idx is not None else None,
+                ws.data_ptr() if ws is not None else None,
+                ws.numel() if ws is not None else 0, _stream(Q.device)))
         return (O, idx) if return_indices else O
