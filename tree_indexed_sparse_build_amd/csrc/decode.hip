@@ -17,13 +17,13 @@
 // decode over the tree of t + 1 keys without waiting for any summary to be
 // rewritten: it reads the stored rows of the unchanged nodes, and for the
 // node holding t (the last existing node of each level) it computes the new
-// mean from the state and the key itself, scored in fp64 by its idle waves
-// while the walking waves score the first cut level.  One workgroup per
-// (batch, KV head) (part 0 of the group's first query head) also stores the
-// new means and sums; the sums go to the other of two state buffers, so no
-// workgroup that still reads the old sums sees the new ones.  The summaries
-// and state it leaves are the ones a separate one-key append writes, bit for
-// bit, and the step costs one launch instead of two.
+// mean from the state and the key itself, scored in fp64 while the walk
+// scores the first cut level (see OpenNodes).  B * Hkv more workgroups of
+// the same launch store the new means and sums; the sums go to the other of
+// two state buffers, so no workgroup that still reads the old sums sees the
+// new ones.
+// The summaries and state it leaves are the ones a separate one-key append
+// writes, bit for bit, and the step costs one launch instead of two.
 #include "attend_query.hpp"
 #include "route_walk.hpp"
 
@@ -72,90 +72,117 @@ template <> __device__ inline float widen1<bf16_bits>(const bf16_bits *p) {
   return __uint_as_float(static_cast<uint32_t>(p->v) << 16);
 }
 
-// The node holding the new key t at every height: new sum (old open sum +
-// key, in fp64, as a one-key append adds it), new mean rounded once to the
-// summary type and, for the levels of the tree, its fp64 score with query
-// qi (the walk's lane layout and arithmetic) into open_score[level]; at the
-// first cut level also its ranking key.  The writer also stores the means
-// (every height of the cache, as an append does) and the new sums.  Run by
-// the waves that do not walk, before the walk's first barrier.
-template <typename T, typename S, int D>
-__device__ void open_nodes(const RouteArgs &ra, const AppendArgs &ap, int qi, bool writer,
-                           uint64_t *keys, double *open_score) {
-  constexpr int NP = kDecodeWaves - kDecodeWalkWaves;  // waves taking part
-  constexpr int E = RowLoad<S>::E;
-  constexpr int LPR = D / E;   // lanes per row
-  constexpr int RPI = 64 / LPR;  // rows (heights) per wave
-  const int lane = threadIdx.x & 63;
-  const int pw = (static_cast<int>(threadIdx.x) >> 6) - kDecodeWalkWaves;
-  const int bi = qi / ra.q_heads;
-  const int hq = qi - bi * ra.q_heads;
-  const int64_t head = static_cast<int64_t>(bi) * ra.kv_heads + hq / ra.group;
-  const int col = (lane % LPR) * E;
-  const int lv = ra.levels;
-  const int nh = writer ? ap.heights : lv;
-  const uint32_t t = static_cast<uint32_t>(ap.n0);
-  const T *key = static_cast<const T *>(ap.K) + (head * ap.capacity + t) * D + col;
-  const T *qp = static_cast<const T *>(ra.Q) + static_cast<int64_t>(qi) * D + col;
-  float kf[E], qf[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    kf[e] = widen1<T>(key + e);
-    qf[e] = widen1<T>(qp + e);
+// The node holding the new key t at every height of the tree: new sum (old
+// open sum + key, in fp64, as a one-key append adds it), new mean rounded
+// once to the summary type, and its fp64 score with query qi (as the walk
+// scores) into open_score[level]; at the first cut level also its ranking
+// key.  Run by the waves that do not walk (one height per row group of
+// lanes, 4 columns a lane) while the walking waves score the first cut
+// level.
+template <typename T, typename S, int D> struct OpenNodes {
+  static constexpr int NP = kDecodeWaves - kDecodeWalkWaves;  // waves taking part
+  static constexpr int E = 4;
+  static constexpr int LPR = D / E;     // lanes per row
+  static constexpr int RPI = 64 / LPR;  // rows (heights) per wave
+  const RouteArgs &ra;
+  const AppendArgs &ap;
+  uint64_t *keys;
+  double *open_score;
+  int64_t head;
+  int qi;
+
+  __device__ OpenNodes(const RouteArgs &r, const AppendArgs &a, int q, uint64_t *k, double *os)
+      : ra(r), ap(a), keys(k), open_score(os), qi(q) {
+    const int bi = q / ra.q_heads;
+    const int hq = q - bi * ra.q_heads;
+    head = static_cast<int64_t>(bi) * ra.kv_heads + hq / ra.group;
   }
-  S *const summ = static_cast<S *>(ap.summ);
-  // the loop bound is uniform over the wave (whole row groups drop out
-  // through `act`), so the cross-lane sums always have their partners
-  for (int h0 = pw * RPI; h0 < nh; h0 += NP * RPI) {
-    const int h = h0 + lane / LPR;
-    const bool act = h < nh;
-    const int hh = act ? h : 0;
-    const uint32_t span = ap.span[hh];
-    const uint32_t held = t % span + 1u;  // keys of t's node up to t
-    const double *st = ap.state + (head * ap.heights + hh) * D + col;
-    S *row = summ + ap.block_off[hh] + (head * ap.rows[hh] + t / span) * D + col;
-    double *nx = ap.state_next + (head * ap.heights + hh) * D + col;
-    const bool store = writer && act;
-    const bool closed = held == span;  // t completes its node: the next starts empty
-    double v[1];
+
+  // pw: this wave among the NP; every lane of the wave calls it (the
+  // cross-lane sums need their partners, so the loop bound is uniform and
+  // whole row groups drop out through `act`)
+  __device__ void run(int pw, int lane) const {
+    const int col = (lane % LPR) * E;
+    const int nh = ra.levels;
+    const uint32_t t = static_cast<uint32_t>(ap.n0);
+    const T *key = static_cast<const T *>(ap.K) + (head * ap.capacity + t) * D + col;
+    const T *qp = static_cast<const T *>(ra.Q) + static_cast<int64_t>(qi) * D + col;
+    float kf[E], qf[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      const double sum = st[e] + static_cast<double>(kf[e]);
-      const double mean = sum / static_cast<double>(held);
-      if (store) {
-        SummaryType<S>::put(row + e, mean);
-        nx[e] = closed ? 0.0 : sum;
-      }
-      // the walk's dot: fp64 products of exact float32 values, fma chain
-      const double f = SummaryType<S>::value(mean);
-      v[0] = e == 0 ? static_cast<double>(qf[0]) * f : fma(static_cast<double>(qf[e]), f, v[0]);
+      kf[e] = widen1<T>(key + e);
+      qf[e] = widen1<T>(qp + e);
     }
-    const double s = group_transpose_reduce<1, LPR>(v, lane);
-    if (act && h < lv && lane % LPR == 0) {
-      const int l = lv - h;
-      open_score[l] = s;
-      if (l == ra.first_cut) {
-        const int last = static_cast<int>(ra.lvl_exist[l]) - 1;
-        keys[last] = score_key(s, last, 32 - __clz(last));
+    for (int h0 = pw * RPI; h0 < nh; h0 += NP * RPI) {
+      const int h = h0 + lane / LPR;
+      const bool act = h < nh;
+      const int hh = act ? h : 0;
+      const uint32_t held = t % ap.span[hh] + 1u;  // keys of t's node up to t
+      const double *st = ap.state + (head * ap.heights + hh) * D + col;
+      double v[1];
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const double sum = st[e] + static_cast<double>(kf[e]);
+        // as the walk scores: fp64 products of exact float32 values, summed in fp64
+        const double f = SummaryType<S>::value(sum / static_cast<double>(held));
+        v[0] = e == 0 ? static_cast<double>(qf[0]) * f : fma(static_cast<double>(qf[e]), f, v[0]);
+      }
+      const double s = group_transpose_reduce<1, LPR>(v, lane);
+      if (act && lane % LPR == 0) {
+        const int l = nh - h;
+        open_score[l] = s;
+        if (l == ra.first_cut) {
+          const int last = static_cast<int>(ra.lvl_exist[l]) - 1;
+          keys[last] = score_key(s, last, 32 - __clz(last));
+        }
       }
     }
+  }
+};
+
+// The append itself, for (batch, KV head) `head`: at every stored height the
+// node holding key t gets the new sum's mean (the summary type), and the new
+// sums go to the other state buffer (zero where t completes its node, as the
+// next node starts empty).  The same arithmetic as a one-key append.
+template <typename T, typename S, int D>
+__device__ void append_one(const AppendArgs &ap, int64_t head) {
+  const uint32_t t = static_cast<uint32_t>(ap.n0);
+  const T *key = static_cast<const T *>(ap.K) + (head * ap.capacity + t) * D;
+  S *const summ = static_cast<S *>(ap.summ);
+  for (int i = threadIdx.x; i < ap.heights * D; i += kDecodeWaves * 64) {
+    const int h = i / D;
+    const int c = i - h * D;
+    const uint32_t span = ap.span[h];
+    const uint32_t held = t % span + 1u;
+    const int64_t r = (head * ap.heights + h) * D + c;
+    const double sum = ap.state[r] + static_cast<double>(widen1<T>(key + c));
+    SummaryType<S>::put(summ + ap.block_off[h] + (head * ap.rows[h] + t / span) * D + c,
+                        sum / static_cast<double>(held));
+    ap.state_next[r] = held == span ? 0.0 : sum;
   }
 }
 
+// Workgroups 0 .. queries * splits - 1 decode (as k_decode); the B * Hkv
+// after them append, one (batch, KV head) each.  The appending workgroups
+// are short and run on CUs the decode leaves free, and no decode barrier
+// waits for their stores.
 template <typename T, typename S, int D>
 __global__ void __launch_bounds__(kDecodeWaves * 64)
     k_decode_append(RouteArgs ra, AttendArgs aa, AppendArgs ap) {
   __shared__ RouteShared<kDecodeWaves> rsh;
   __shared__ AttendShared<T, D> ash;
   __shared__ double open_score[kMaxLevels + 1];
+  const int nq = aa.queries * aa.splits;
+  if (static_cast<int>(blockIdx.x) >= nq) {
+    append_one<T, S, D>(ap, static_cast<int64_t>(blockIdx.x) - nq);
+    return;
+  }
   const int sp = blockIdx.x / aa.queries;
   const int qi = query_of_slot(blockIdx.x - sp * aa.queries, aa.queries, aa.group);
   const uint4 qraw = attend_q_raw<T, D>(aa, qi);
-  const bool writer = sp == 0 && (qi % ra.q_heads) % ra.group == 0;
-  const auto prep = [&]() { open_nodes<T, S, D>(ra, ap, qi, writer, rsh.keys, open_score); };
-  const int kept =
-      route_walk<T, S, D, kDecodeWaves, kDecodeWalkWaves, 1, kMaxCandidates, decltype(prep)>(
-          ra, rsh, qi, nullptr, nullptr, -1, prep, open_score);
+  const OpenNodes<T, S, D> open(ra, ap, qi, rsh.keys, open_score);
+  const int kept = route_walk<T, S, D, kDecodeWaves, kDecodeWalkWaves, 1>(
+      ra, rsh, qi, nullptr, nullptr, -1, &open, open_score);
   decode_attend<T, D, true>(ra, aa, rsh, ash, qi, sp, qraw, kept);
 }
 
@@ -183,7 +210,8 @@ hipError_t launch_decode_ts(int head_dim, const RouteArgs &ra, const AttendArgs 
 template <typename T, typename S>
 hipError_t launch_decode_append_ts(int head_dim, const RouteArgs &ra, const AttendArgs &aa,
                                    const AppendArgs &ap, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(ra.queries) * static_cast<unsigned>(aa.splits));
+  const dim3 grid(static_cast<unsigned>(ra.queries) * static_cast<unsigned>(aa.splits) +
+                  static_cast<unsigned>(ap.heads));
   const dim3 block(kDecodeWaves * 64);
   if (head_dim == 128)
     hipLaunchKernelGGL((k_decode_append<T, S, 128>), grid, block, 0, s, ra, aa, ap);

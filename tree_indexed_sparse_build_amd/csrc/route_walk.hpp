@@ -196,11 +196,8 @@ struct NoScale {
   __device__ float operator()(int) const { return 1.f; }
 };
 
-// The walk's optional side job for the waves that do not walk (see
-// route_walk): the default does nothing.
-struct NoPrep {
-  __device__ void operator()() const {}
-};
+// The walk's optional side job (see route_walk): none.
+struct NoPrep {};
 
 template <typename T, typename S, int D, int UU, bool HOLES, typename NodeOf, typename RowOf,
           typename Emit, typename ScaleOf = NoScale>
@@ -268,17 +265,18 @@ __device__ inline void score_rows(RowOf row_of, int C, NodeOf node_of, Emit emit
 // of the walk keeps them off its critical path: they only have to reach
 // each barrier, and the attention after the walk is where they are needed.
 //
-// With a Prep other than NoPrep (growing cache only), the waves that do not
-// walk run prep() while the walking waves score level l0, and the score of
-// the last existing node of each level (the open node, whose stored row is
-// not current) comes from open_score[l] instead of its row: prep() must fill
+// With a Prep other than NoPrep (growing cache only), the score of the last
+// existing node of each level (the open node, whose stored row is not
+// current) comes from open_score[l] instead of its row.  The waves that do
+// not walk call prep->run(w - NRW, lane) as they start: it must fill
 // open_score[l] for l0 < l <= levels and write level l0's key of that node
-// into sh.keys, all before the walk's first barrier.
+// into sh.keys before they reach the walk's first barrier (the walking
+// waves score the other nodes of level l0 meanwhile).
 template <typename T, typename S, int D, int NW, int NRW, int LAYOUT,
           int MAXC = kMaxCandidates, typename Prep = NoPrep>
 __device__ int route_walk(const RouteArgs &a, RouteShared<NW> &sh, int qi,
                           const CausalLevels *cl = nullptr, const void *open_summ = nullptr,
-                          int hrow = -1, const Prep &prep = Prep(),
+                          int hrow = -1, const Prep *prep = nullptr,
                           const double *open_score = nullptr) {
   constexpr bool CACHE = LAYOUT != 0;  // nodes past the last key may be missing
   constexpr bool OPEN = !__is_same(Prep, NoPrep);
@@ -312,8 +310,9 @@ __device__ int route_walk(const RouteArgs &a, RouteShared<NW> &sh, int qi,
   QRaw<T, E> qr;
   qr.load(static_cast<const T *>(a.Q) + static_cast<int64_t>(qi) * D + col);
 
+
   if constexpr (OPEN) {
-    if (w >= NRW) prep();
+    if (w >= NRW) prep->run(w - NRW, lane);
   }
 
   LevelCursor<LAYOUT> lc;
@@ -379,7 +378,7 @@ __device__ int route_walk(const RouteArgs &a, RouteShared<NW> &sh, int qi,
       uint64_t *keys = sh.keys;
       const auto emit = [&](int pos, int nd, double s) {
         if constexpr (OPEN) {
-          // the open node: prep() wrote its key at l0 and its score below
+          // the open node: prep wrote its key at l0 and its score below
           if (nd == last) {
             if (l != l0) keys[pos] = score_key(open_score[l], nd, bits);
             return;

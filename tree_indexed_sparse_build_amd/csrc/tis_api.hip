@@ -777,6 +777,9 @@ tis_status tis_cache_tree_append_decode(const void *Q, const void *K, const void
   st = plan_split(who, queries, tree->head_dim, beam, tree->leaf_block, workspace,
                   workspace_bytes, &aa);
   if (st != TIS_OK) return st;
+  // one workgroup per query part, then one per (batch, KV head) for the append
+  if (queries * aa.splits + g.heads > 0x7fffffffLL)
+    return fail(TIS_E_UNSUPPORTED, "%s: too many workgroups", who);
   const tis::AppendArgs ap = cache_append_args(K, tree, g, 1);
   const tis::Dt dt = dtype == TIS_BF16 ? tis::Dt::BF16 : tis::Dt::F32;
   st = hip_status(tis::launch_decode_append(dt, to_dt(tree->summary_dtype), tree->head_dim, ra,
