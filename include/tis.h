@@ -315,10 +315,12 @@ const char *tis_version(void);
  *              the keys of the node that holds key n_keys (the open node;
  *              zero when n_keys is a multiple of L*b^h).  Appends start from
  *              it, which keeps every summary an exact mean rounded once.
- *              tis_cache_tree_append updates the half in use in place;
- *              tis_cache_tree_append_decode writes the other half and
- *              switches to it (its workgroups read the old sums while one
- *              of them writes the new ones).
+ *              A short tis_cache_tree_append updates the half in use in
+ *              place; a long one and tis_cache_tree_append_decode write the
+ *              other half and switch to it (their workgroups read the old
+ *              sums while others write the new ones).  After the two halves
+ *              comes the library's scratch for long appends (a float64 row
+ *              of d per (batch, KV head, chunk of the cache)).
  * Summaries are kept for every height up to H-1 whatever the current depth,
  * so a deeper tree finds its upper levels already in place.
  * --------------------------------------------------------------------- */
@@ -354,7 +356,10 @@ tis_status tis_cache_tree_reset(tis_cache_tree *tree, void *stream);
  * the tree, then sets n_keys += n_new and levels to the new depth (host-side
  * fields, updated when the work is enqueued).  Rewrites the summary of every
  * node that gains a key, at every height, and the state; O(n_new * d + H * d
- * * (leaves touched)) work, one workgroup per (batch, KV head).
+ * * (leaves touched)) work.  Short appends run one workgroup per (batch, KV
+ * head); an append of at least one chunk (the nodes of the smallest height
+ * with 512 or more keys, at most 64 leaves) runs a workgroup per (head,
+ * chunk), then one per head for the heights above the chunks.
  * Requires 0 <= n_new <= capacity - n_keys.  n_new = 0 does nothing. */
 tis_status tis_cache_tree_append(const void *K, tis_dtype dtype, int n_new,
                                  tis_cache_tree *tree, void *stream);

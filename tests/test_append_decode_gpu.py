@@ -72,8 +72,9 @@ def _same_tree(ct, ref):
                                                                else torch.int32)
         r = ref.height_block(h)[:, :, :rows].contiguous().view(a.dtype)
         assert torch.equal(a, r), f"height {h} summaries differ"
-    half = ct.state.numel() // 2
-    s_f = ct.state[ct.c.state_half * half:][:half]
+    c = ct.c
+    half = c.batch * c.kv_heads * len(_heights(ct)) * c.head_dim  # doubles in one state half
+    s_f = ct.state[c.state_half * half:][:half]
     s_r = ref.state[ref.c.state_half * half:][:half]
     assert torch.equal(s_f.view(torch.int64), s_r.view(torch.int64)), "open-node sums differ"
 
@@ -124,13 +125,14 @@ def test_append_decode_steps(tis, case):
         ct.append(n0)
         ref.append(n0)
     tot = dict(exact=0, tie=0, nq=0, err=0.0, same=0)
+    half0 = ct.c.state_half  # a long prefix append may have switched halves already
     for s in range(steps):
         n = ct.n_keys + 1
         out_f, idx_f = ct.append_decode(Qd, beam, return_indices=True)
         ref.append(1)
         out_r, idx_r = ref.decode(Qd, beam, return_indices=True)
         torch.cuda.synchronize()
-        assert ct.n_keys == n and ct.c.state_half == (s + 1) % 2
+        assert ct.n_keys == n and ct.c.state_half == (half0 + s + 1) % 2
         idx_f, idx_r = idx_f.cpu().numpy(), idx_r.cpu().numpy()
         out_f, out_r = out_f.cpu().numpy(), out_r.cpu().numpy()
         exact, tie, nq, err = _step_check(x, dtype, n, b, L, beam, idx_f, out_f, sd)

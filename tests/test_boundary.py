@@ -236,11 +236,12 @@ def test_cache_tree_bytes(lib):
     # ceil(40000 / 64) = 625, 79, 10, 2 per head
     heads, d = 4 * 8, 128
     assert lib.tis_cache_tree_summary_bytes(4, 8, d, 8, 64, 40000) == 4 * d * heads * (625 + 79 + 10 + 2)
-    # two halves of fp64 open-node sums, one row per height
-    assert lib.tis_cache_tree_state_bytes(4, 8, d, 8, 64, 40000) == 2 * 8 * d * heads * 4
+    # two halves of fp64 open-node sums, one row per height, then a row per
+    # chunk for long appends (chunks of 512 keys: ceil(40000 / 512) = 79)
+    assert lib.tis_cache_tree_state_bytes(4, 8, d, 8, 64, 40000) == 8 * d * heads * (2 * 4 + 79)
     # a cache of one leaf: one height with one row
     assert lib.tis_cache_tree_summary_bytes(1, 1, 64, 2, 16, 10) == 4 * 64
-    assert lib.tis_cache_tree_state_bytes(1, 1, 64, 2, 16, 10) == 2 * 8 * 64
+    assert lib.tis_cache_tree_state_bytes(1, 1, 64, 2, 16, 10) == (2 + 1) * 8 * 64
     # invalid geometry -> 0
     assert lib.tis_cache_tree_summary_bytes(1, 1, 64, 1, 16, 100) == 0
     assert lib.tis_cache_tree_summary_bytes(1, 1, 96, 2, 16, 100) == 0

@@ -114,6 +114,46 @@ def test_append_sequence_matches_oracle(tis, case):
     _say(f"{label}: {len(chunks) + (1 if rest else 0)} appends checked in {time.time() - t0:.1f}s")
 
 
+LONG = [
+    # (label, dtype, summary type, b, L, d, Hkv, G, capacity, beam, appends)
+    # long appends run in chunks (the nodes of the smallest height with 512
+    # or more keys, at most 64 leaves), then heights above them per head;
+    # appends start mid-leaf and mid-node, and short ones come in between
+    ("b4_bf16", "bf16", "f32", 4, 16, 128, 2, 2, 16000, 6, [5, 3000, 1, 1500, 7, 11000]),
+    ("b8_f32_d64", "f32", "f32", 8, 32, 64, 2, 2, 20000, 5, [100, 5000, 3, 9000]),
+    ("b2_bf16s", "bf16", "bf16", 2, 16, 128, 1, 3, 5000, 4, [1, 700, 2049, 1]),
+    ("leaf_1", "f32", "f32", 2, 1, 64, 1, 2, 3000, 3, [10, 1000, 1, 1500]),
+    # chunks are the top height: no heights above them
+    ("top_chunks", "bf16", "f32", 3, 5, 64, 2, 2, 405, 4, [7, 200, 1]),
+]
+
+
+@pytest.mark.parametrize("case", LONG, ids=[c[0] for c in LONG])
+def test_long_appends_match_oracle(tis, case):
+    label, dtype, sd, b, L, d, Hkv, G, cap, beam, chunks = case
+    t0 = time.time()
+    x = _inputs(dtype, b, L, d, Hkv, G, cap, seed=len(label) + 11)
+    Kd = tis.from_storage(x["K"], dtype, "cuda")
+    Vd = tis.from_storage(x["V"], dtype, "cuda")
+    Qd = tis.from_storage(x["Q"], dtype, "cuda")
+    ct = tis.CacheTree(Kd, Vd, b, L, summary_dtype=sd)
+    n = 0
+    halves = set()
+    for c in chunks + [cap - sum(chunks)]:
+        ct.append(c)
+        n += c
+        halves.add(ct.c.state_half)
+        _check(tis, ct, x, Qd, dtype, n, b, L, beam, label)
+    # the tree goes on growing from the state the long appends left
+    ct.reset()
+    ct.append(cap - 3)
+    for _ in range(3):
+        ct.append_decode(Qd, beam)
+    _check(tis, ct, x, Qd, dtype, cap, b, L, beam, label + " refill")
+    _say(f"{label}: long appends checked (state halves used {sorted(halves)}) in "
+         f"{time.time() - t0:.1f}s")
+
+
 def test_reset_then_refill_matches(tis):
     """A reset empties the tree whatever it held; refilling gives the same tree."""
     dtype, b, L, d, cap, beam = "bf16", 3, 4, 64, 200, 3

@@ -454,7 +454,10 @@ struct CacheGeometry {
   int heights;          // H
   int64_t heads;
   int64_t summ_elems;   // summary elements
-  int64_t state_elems;  // doubles
+  int64_t state_elems;  // doubles in one state half
+  int chunk_height;     // long appends: chunks are the nodes of this height
+  int64_t chunk_keys;   // L b^chunk_height
+  int64_t scratch_elems;  // doubles after the two halves: a sum per (head, chunk, column)
 };
 
 tis_status check_cache(const char *who, int batch, int kv_heads, int head_dim, int branching,
@@ -482,6 +485,10 @@ tis_status check_cache(const char *who, int batch, int kv_heads, int head_dim, i
   }
   g->summ_elems = elems;
   g->state_elems = g->heads * H * head_dim;  // one of the two halves
+  g->chunk_height = tis::append_chunk_height(branching, leaf_block, H);
+  g->chunk_keys = leaf_block;
+  for (int h = 0; h < g->chunk_height; ++h) g->chunk_keys *= branching;
+  g->scratch_elems = g->heads * ((capacity + g->chunk_keys - 1) / g->chunk_keys) * head_dim;
   return TIS_OK;
 }
 
@@ -653,7 +660,7 @@ size_t tis_cache_tree_state_bytes(int batch, int kv_heads, int head_dim, int bra
   if (check_cache("tis_cache_tree_state_bytes", batch, kv_heads, head_dim, branching,
                   leaf_block, capacity, &g) != TIS_OK)
     return 0;
-  return 2 * static_cast<size_t>(g.state_elems) * sizeof(double);
+  return static_cast<size_t>(2 * g.state_elems + g.scratch_elems) * sizeof(double);
 }
 
 tis_status tis_cache_tree_reset(tis_cache_tree *tree, void *stream) {
@@ -693,12 +700,31 @@ tis_status tis_cache_tree_append(const void *K, tis_dtype dtype, int n_new, tis_
   if (n_new == 0) return TIS_OK;
   if (g.heads > 0x7fffffffLL)
     return fail(TIS_E_UNSUPPORTED, "tis_cache_tree_append: too many heads");
-  const tis::AppendArgs a = cache_append_args(K, tree, g, n_new);  // state updated in place
+  tis::AppendArgs a = cache_append_args(K, tree, g, n_new);
   const tis::Dt dt = dtype == TIS_BF16 ? tis::Dt::BF16 : tis::Dt::F32;
-  st = hip_status(tis::launch_cache_append(dt, to_dt(tree->summary_dtype), tree->head_dim, a,
-                                           static_cast<hipStream_t>(stream)),
-                  "tis_cache_tree_append launch");
+  // an append of a chunk's worth of keys or more: chunks in parallel, the
+  // new open sums in the other state half; shorter: one workgroup per head,
+  // the state updated in place
+  const bool chunked = n_new >= g.chunk_keys;
+  if (chunked) {
+    a.chunk_height = g.chunk_height;
+    a.chunk_keys = static_cast<uint32_t>(g.chunk_keys);
+    a.chunk0 = a.n0 / g.chunk_keys;
+    a.nchunks = (a.n1 - 1) / g.chunk_keys - a.chunk0 + 1;
+    a.scratch = tree->state + 2 * g.state_elems;
+    if (g.heads * a.nchunks > 0x7fffffffLL)
+      return fail(TIS_E_UNSUPPORTED, "tis_cache_tree_append: too many chunks");
+    st = hip_status(tis::launch_cache_append_chunked(dt, to_dt(tree->summary_dtype),
+                                                     tree->head_dim, a,
+                                                     static_cast<hipStream_t>(stream)),
+                    "tis_cache_tree_append launch");
+  } else {
+    st = hip_status(tis::launch_cache_append(dt, to_dt(tree->summary_dtype), tree->head_dim, a,
+                                             static_cast<hipStream_t>(stream)),
+                    "tis_cache_tree_append launch");
+  }
   if (st != TIS_OK) return st;
+  if (chunked) tree->state_half ^= 1;
   tree->n_keys += n_new;
   tree->levels = cache_depth(tree->n_keys, tree->branching, tree->leaf_block);
   return TIS_OK;

@@ -143,7 +143,29 @@ struct AppendArgs {
   int64_t block_off[kMaxLevels];
   uint32_t rows[kMaxLevels];
   uint32_t span[kMaxLevels];   // L b^h: below the capacity (or L itself when H = 1)
+  // long appends, split into chunks: the nodes of height chunk_height
+  // (chunk_keys = L b^chunk_height keys each) that hold new keys, chunk0 ..
+  // chunk0 + nchunks - 1; scratch holds fp64 [heads][nchunks][d], the sum of
+  // each chunk's new keys, for the heights above the chunks
+  int chunk_height;
+  uint32_t chunk_keys;
+  int64_t chunk0, nchunks;
+  double *scratch;
 };
+
+// Chunk height of a cache geometry: the smallest h with L b^h >= 512 keys,
+// kept below the cache's depth H and to b^h <= kMaxChunkLeaves leaves.
+constexpr int kMaxChunkLeaves = 64;
+inline int append_chunk_height(int branching, int leaf_block, int heights) {
+  int hc = 0;
+  int64_t leaves = 1;
+  while (hc + 1 < heights && leaves * branching <= kMaxChunkLeaves &&
+         static_cast<int64_t>(leaf_block) * leaves < 512) {
+    leaves *= branching;
+    ++hc;
+  }
+  return hc;
+}
 
 // Append of one key (n1 = n0 + 1) fused with a decode over the tree of n1
 // keys: ra and aa describe the decode at n1, ap the append, with the state
@@ -155,6 +177,10 @@ hipError_t launch_decode_append(Dt dt, Dt sdt, int head_dim, const RouteArgs &ra
 // zero `elems` doubles with a kernel (no memset node, so it can sit in a graph)
 hipError_t launch_fill_zero(double *p, int64_t elems, hipStream_t s);
 hipError_t launch_cache_append(Dt dt, Dt sdt, int head_dim, const AppendArgs &a, hipStream_t s);
+// The chunked append: reads the open sums from a.state, writes the new ones
+// to a.state_next (two launches when heights remain above the chunks).
+hipError_t launch_cache_append_chunked(Dt dt, Dt sdt, int head_dim, const AppendArgs &a,
+                                       hipStream_t s);
 
 // ------------------------------------------------------ bounding spheres --
 // Radius of every node of a full tree about its stored summary: the largest
