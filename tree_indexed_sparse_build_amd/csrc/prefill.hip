@@ -17,9 +17,10 @@
 //  * k_prefill: one workgroup per (batch, query head, position), of 4 waves
 //    when a level has at most 128 candidates (beam * b), else 8: a prefill
 //    query reads few keys, so small workgroups keep more positions in
-//    flight on each CU (measured: 8 waves 1.5-1.8x the rate of 16).  Thread 0
+//    flight on each CU (measured: 8 waves 1.5-1.8x the rate of 16).  Wave 0
 //    builds the position's level table (depth, existing nodes, first cut, the
-//    open rows' offsets) in LDS; the walk reads complete nodes from the
+//    open rows' offsets) in LDS, a lane per level; the walk reads complete
+//    nodes from the
 //    cache tree and the open node of each level from the table of partial
 //    means; the attention stops at key t.
 #include "attend_query.hpp"
@@ -93,26 +94,43 @@ __global__ void __launch_bounds__(NW * 64) k_prefill(RouteArgs ra, AttendArgs aa
   const int hrow = qi / pa.positions;          // (batch, query head)
   const int t = qi - hrow * pa.positions;      // position
   const uint4 qraw = attend_q_raw<T, D>(aa, qi);
-  if (threadIdx.x == 0) {
+  if (threadIdx.x < 64) {
+    // wave 0 builds the level table, lane j for height j and for level j:
+    // every table load at once, then lane exchanges (no serial chain)
+    const int lane = threadIdx.x;
     const int bi = hrow / ra.q_heads;
     const int hq = hrow - bi * ra.q_heads;
     const int64_t head = static_cast<int64_t>(bi) * ra.kv_heads + hq / ra.group;
-    const int64_t n = static_cast<int64_t>(t) + 1;
-    int lv = 1;
-    while (lv < pa.levels && pa.h_span[lv] < n) ++lv;  // fewest levels covering n keys
-    cl.levels = lv;
-    cl.exist[0] = 1;
-    for (int l = 1; l <= lv; ++l) {
-      const int h = lv - l;
-      cl.exist[l] = (n + pa.h_span[h] - 1) / pa.h_span[h];
-      cl.rows[l] = pa.h_rows[h];
-      cl.off[l] = pa.h_off[h];
-      cl.open_off[l] = ((head * pa.positions + t) * pa.levels + h) * D;
+    const uint32_t n = static_cast<uint32_t>(t) + 1u;
+    const int levels = pa.levels;
+    // a stored height's node span is below 2^31 (it is below the positions)
+    const bool hv = lane < levels;
+    const uint32_t span = hv ? static_cast<uint32_t>(pa.h_span[lane]) : 0xffffffffu;
+    const long long rows = hv ? pa.h_rows[lane] : 0;
+    const long long off = hv ? pa.h_off[lane] : 0;
+    // depth: the fewest lv >= 1 whose height-lv span covers n (spans grow with h)
+    const int lv = 1 + static_cast<int>(__popcll(__ballot(lane >= 1 && hv && span < n)));
+    // level l = lane sits at height lv - l
+    const bool lev = lane >= 1 && lane <= lv;
+    const int h = lev ? lv - lane : 0;
+    const uint32_t sp = __shfl(span, h);
+    const long long rows_h = __shfl(rows, h);
+    const long long off_h = __shfl(off, h);
+    const uint32_t ex = lev ? (n + sp - 1u) / sp : 0u;
+    // first level below lv with more nodes than the beam, else lv
+    const uint64_t cut = __ballot(lev && lane < lv && ex > static_cast<uint32_t>(ra.beam));
+    if (lev) {
+      cl.exist[lane] = ex;
+      cl.rows[lane] = rows_h;
+      cl.off[lane] = off_h;
+      cl.open_off[lane] = ((head * pa.positions + t) * levels + h) * D;
     }
-    cl.exist[lv + 1] = 0;
-    int fc = 1;
-    while (fc < lv && cl.exist[fc] <= ra.beam) ++fc;
-    cl.first_cut = fc;
+    if (lane == 0) {
+      cl.levels = lv;
+      cl.exist[0] = 1;
+      cl.exist[lv + 1] = 0;
+      cl.first_cut = cut ? __ffsll(static_cast<unsigned long long>(cut)) - 1 : lv;
+    }
   }
   __syncthreads();
   const int kept = route_walk<T, S, D, NW, NW, 2, NW * 32>(ra, rsh, qi, &cl, pa.open_summ, hrow);
