@@ -71,6 +71,10 @@ CASES = [
     ("bf16_summaries", "bf16", "bf16", 1, 2, 2, 200, 64, 2, 8, 3, "normal"),
     ("wide_beam", "f32", "f32", 1, 1, 2, 129, 64, 2, 4, 40, "normal"),
     ("leaf_1", "f32", "f32", 1, 1, 2, 50, 64, 2, 1, 3, "normal"),
+    # workgroup sizes by candidates a level (beam * b): one wave up to 32
+    # (most cases above), two waves up to 64, four up to 128, else eight
+    ("cand_48", "bf16", "f32", 1, 2, 2, 500, 128, 4, 8, 12, "normal"),
+    ("cand_48_f32_d64", "f32", "f32", 1, 1, 3, 333, 64, 6, 5, 8, "normal"),
     # more than 128 candidates a level (8-wave workgroups)
     ("cand_160", "bf16", "f32", 1, 2, 2, 700, 128, 8, 4, 20, "normal"),
 ]

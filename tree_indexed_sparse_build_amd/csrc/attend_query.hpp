@@ -30,10 +30,11 @@ template <typename T, int D> struct AttendGeom {
 
 constexpr int kPartHeader = 4;  // m, l, two pad words: keeps acc 16-byte aligned
 
-template <typename T, int D> struct AttendShared {
-  float p[kAttendMaxWaves][AttendGeom<T, D>::RB];
-  float m[kAttendMaxWaves], l[kAttendMaxWaves];
-  float acc[kAttendMaxWaves][D];
+// MW: the most waves of the workgroups that use it
+template <typename T, int D, int MW = kAttendMaxWaves> struct AttendShared {
+  float p[MW][AttendGeom<T, D>::RB];
+  float m[MW], l[MW];
+  float acc[MW][D];
 };
 
 // This lane's part of the query row in the attend layout (E elements).
@@ -54,8 +55,9 @@ template <typename T, int D> __device__ inline uint4 attend_q_raw(const AttendAr
 // zero if no slot is used); otherwise it writes the workgroup's partial
 // softmax state to part: m (log2 units), l (NaN if `bad`), two pad words,
 // acc[D], for a later log-sum-exp merge with the query's other parts.
-template <typename T, int D, bool RAGGED = false, bool THRESH = false, bool PREFILL = false>
-__device__ void attend_query(const AttendArgs &a, AttendShared<T, D> &sh, int qi,
+template <typename T, int D, bool RAGGED = false, bool THRESH = false, bool PREFILL = false,
+          int MW = kAttendMaxWaves>
+__device__ void attend_query(const AttendArgs &a, AttendShared<T, D, MW> &sh, int qi,
                              uint4 qraw, const int *slots, const int *use, int nslots,
                              bool bad, float *part, double tau = 0.0, int hrow = 0,
                              int64_t nk = 0) {
@@ -185,16 +187,16 @@ __device__ void attend_query(const AttendArgs &a, AttendShared<T, D> &sh, int qi
   // first is used; slots of waves past nw are never written and are masked
   // (m = -inf, l = acc = 0).
   for (int c = tid; c < D; c += blockDim.x) {
-    float mj[kAttendMaxWaves], lj[kAttendMaxWaves], aj[kAttendMaxWaves];
+    float mj[MW], lj[MW], aj[MW];
 #pragma unroll
-    for (int j = 0; j < kAttendMaxWaves; ++j) {
+    for (int j = 0; j < MW; ++j) {
       mj[j] = sh.m[j];
       lj[j] = sh.l[j];
       aj[j] = sh.acc[j][c];
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < kAttendMaxWaves; ++j) {
+    for (int j = 0; j < MW; ++j) {
       if (j >= nw) {
         mj[j] = -INFINITY;
         lj[j] = 0.f;
@@ -205,7 +207,7 @@ __device__ void attend_query(const AttendArgs &a, AttendShared<T, D> &sh, int qi
     float num = 0.f, den = 0.f;
     if (mx != -INFINITY) {
 #pragma unroll
-      for (int j = 0; j < kAttendMaxWaves; ++j) {
+      for (int j = 0; j < MW; ++j) {
         const float wj = __builtin_amdgcn_exp2f(mj[j] - mx);  // 0 for waves that saw no key
         den = fmaf(wj, lj[j], den);
         num = fmaf(wj, aj[j], num);

@@ -14,10 +14,11 @@
 //    and rounded once to the summary type.  One workgroup per (head, height,
 //    block of 64 positions), a thread per column: it first sums the keys of
 //    the node that lie before the block, then walks the block.
-//  * k_prefill: one workgroup per (batch, query head, position), of 4 waves
-//    when a level has at most 128 candidates (beam * b), else 8: a prefill
-//    query reads few keys, so small workgroups keep more positions in
-//    flight on each CU (measured: 8 waves 1.5-1.8x the rate of 16).  Wave 0
+//  * k_prefill: one workgroup per (batch, query head, position), of one
+//    wave when a level has at most 32 candidates (beam * b), 2 waves up to
+//    64, 4 up to 128, else 8: a prefill query reads few keys, so small workgroups (LDS
+//    sized to them) keep more positions in flight on each CU (measured: 8
+//    waves 1.5-1.8x the rate of 16).  Wave 0
 //    builds the position's level table (depth, existing nodes, first cut, the
 //    open rows' offsets) in LDS, a lane per level; the walk reads complete
 //    nodes from the
@@ -87,8 +88,8 @@ __global__ void __launch_bounds__(D) k_prefix_means(PrefillArgs a) {
 
 template <typename T, typename S, int D, int NW>
 __global__ void __launch_bounds__(NW * 64) k_prefill(RouteArgs ra, AttendArgs aa, PrefillArgs pa) {
-  __shared__ RouteShared<NW> rsh;
-  __shared__ AttendShared<T, D> ash;
+  __shared__ RouteShared<NW, NW * 32> rsh;
+  __shared__ AttendShared<T, D, NW> ash;
   __shared__ CausalLevels cl;
   const int qi = blockIdx.x;
   const int hrow = qi / pa.positions;          // (batch, query head)
@@ -152,7 +153,11 @@ hipError_t launch_prefill_d(const RouteArgs &ra, const AttendArgs &aa, const Pre
   hipLaunchKernelGGL((k_prefix_means<T, S, D>), g1, dim3(D), 0, s, pa);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (ra.beam * ra.branching <= 4 * 32)
+  if (ra.beam * ra.branching <= 32)
+    hipLaunchKernelGGL((k_prefill<T, S, D, 1>), g2, dim3(64), 0, s, ra, aa, pa);
+  else if (ra.beam * ra.branching <= 2 * 32)
+    hipLaunchKernelGGL((k_prefill<T, S, D, 2>), g2, dim3(2 * 64), 0, s, ra, aa, pa);
+  else if (ra.beam * ra.branching <= 4 * 32)
     hipLaunchKernelGGL((k_prefill<T, S, D, 4>), g2, dim3(4 * 64), 0, s, ra, aa, pa);
   else
     hipLaunchKernelGGL((k_prefill<T, S, D, 8>), g2, dim3(8 * 64), 0, s, ra, aa, pa);

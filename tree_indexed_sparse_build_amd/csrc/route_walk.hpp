@@ -87,12 +87,13 @@ template <> struct QRaw<bf16_bits, 8> {
   }
 };
 
-// Shared memory of one query's walk, for a workgroup of NW waves.
-template <int NW> struct RouteShared {
-  uint64_t keys[kMaxCandidates];
-  int cand[2][kMaxCandidates];     // node id of every candidate (-1: hole), this level / next
-  int front[kMaxCandidates];       // kept nodes of the level, in rank order
-  int holes[3];                    // holes among a level's candidates, slot l mod 3
+// Shared memory of one query's walk, for a workgroup of NW waves whose
+// levels have at most MAXC candidates.
+template <int NW, int MAXC = kMaxCandidates> struct RouteShared {
+  uint64_t keys[MAXC];
+  int cand[2][MAXC];     // node id of every candidate (-1: hole), this level / next
+  int front[MAXC];       // kept nodes of the level, in rank order
+  int holes[3];          // holes among a level's candidates, slot l mod 3
 };
 
 // Level table of one causal-prefill query (position t routes over the tree
@@ -273,8 +274,8 @@ __device__ inline void score_rows(RowOf row_of, int C, NodeOf node_of, Emit emit
 // into sh.keys before they reach the walk's first barrier (the walking
 // waves score the other nodes of level l0 meanwhile).
 template <typename T, typename S, int D, int NW, int NRW, int LAYOUT,
-          int MAXC = kMaxCandidates, typename Prep = NoPrep>
-__device__ int route_walk(const RouteArgs &a, RouteShared<NW> &sh, int qi,
+          int MAXC = kMaxCandidates, typename Prep = NoPrep, int SMAXC = kMaxCandidates>
+__device__ int route_walk(const RouteArgs &a, RouteShared<NW, SMAXC> &sh, int qi,
                           const CausalLevels *cl = nullptr, const void *open_summ = nullptr,
                           int hrow = -1, const Prep *prep = nullptr,
                           const double *open_score = nullptr) {
@@ -283,12 +284,12 @@ __device__ int route_walk(const RouteArgs &a, RouteShared<NW> &sh, int qi,
   static_assert(!kIsFp8<S> || LAYOUT == 0, "fp8 summaries: full tree only");
   static_assert(!OPEN || (LAYOUT == 1 && NRW < NW), "open-node scores: growing cache, idle waves");
   constexpr int NT = NW * 64;
-  constexpr int LOG_NRT = NRW == 16 ? 10 : NRW == 8 ? 9 : NRW == 4 ? 8 : -1;
-  static_assert(LOG_NRT > 0 && NRW <= NW, "4, 8 or 16 walking waves");
+  constexpr int LOG_NRT =
+      NRW == 16 ? 10 : NRW == 8 ? 9 : NRW == 4 ? 8 : NRW == 2 ? 7 : NRW == 1 ? 6 : -1;
+  static_assert(LOG_NRT > 0 && NRW <= NW, "1, 2, 4, 8 or 16 walking waves");
   // MAXC: the most candidates a level of this launch may have (beam * b,
   // checked by the host); the ranking needs two or more threads for each
-  static_assert(MAXC <= kMaxCandidates && MAXC <= NRW * 64 / 2,
-                "two or more threads per candidate");
+  static_assert(MAXC <= SMAXC && MAXC <= NRW * 64 / 2, "two or more threads per candidate");
   constexpr int E = RowLoad<S>::E;     // summary elements per lane (one load)
   constexpr int LPR = D / E;           // lanes per summary row
   constexpr int RPI = 64 / LPR;        // rows per wave-wide load
