@@ -11,8 +11,13 @@
 //    with 64-bit atomic max on the ordered fp64 bits.  A wave owns a run of
 //    consecutive leaves of one head and keeps, per level, the running
 //    maximum of the node its leaves are under (one lane per level), so it
-//    issues one atomic per node it touches.  K is streamed once, 8 rows per
-//    lane in flight; the ancestors' summaries go through LDS.
+//    issues one atomic per node it touches.  K is streamed once in batches
+//    of 4 row loads a lane, the next batch in flight while the current one
+//    is worked on; a batch's keys are widened to fp64 once and reused for
+//    every level, since the pass is bound by its fp64 arithmetic (a
+//    subtraction and an FMA per key element and level).  The ancestors'
+//    summaries go through LDS; only the nodes that change are reloaded, and
+//    the next leaf's own centre is fetched ahead of its rows.
 //  * k_radius_finish: radius = smallest float32 r with r * r >= the maximum
 //    (r * r is exact in fp64, so the test is exact).
 //  * threshold walk: one workgroup per query; level by level, the children
@@ -33,7 +38,12 @@ constexpr int kRadiusWaves = 4;
 template <typename T, typename S, int D>
 __global__ void __launch_bounds__(kRadiusWaves * 64) k_radius(RadiusArgs a) {
   using AG = AttendGeom<T, D>;  // row geometry of 16-byte K loads
-  constexpr int E = AG::E, LPR = AG::LPR, R = AG::R, U = AG::U, RB = AG::RB, REP = AG::REP;
+  constexpr int E = AG::E, LPR = AG::LPR, R = AG::R;
+  // U row loads a lane per batch, small enough that the batch's keys stay
+  // widened to fp64 across the levels (each element is converted once, then
+  // costs a subtraction and an FMA per level: the pass is fp64-bound)
+  constexpr int U = 4, RB = U * R, REP = LPR / U;
+  static_assert(U <= LPR, "a batch's distances must fit one reduction");
   __shared__ float ctr[kRadiusWaves][kMaxLevels + 1][D];  // this leaf's ancestors' centres
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -64,67 +74,108 @@ __global__ void __launch_bounds__(kRadiusWaves * 64) k_radius(RadiusArgs a) {
                 static_cast<unsigned long long>(__double_as_longlong(my_max)));
   };
 
-  for (int64_t leaf = leaf0; leaf < leaf1; ++leaf) {
-    // ancestors: a level whose node changes flushes the old one's maximum
+  // centre row of node `anc` of level l, this lane's columns c = lane, lane + 64
+  constexpr int CPL = D / 64;  // centre elements per lane
+  const auto centre = [&](int l, int64_t anc, float (&f)[CPL]) {
+    const S *row = summ + a.summ_off[l] + (head * a.n_at[l] + anc) * D;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int c = lane + 64 * j;
+      if constexpr (sizeof(S) == 4) {
+        f[j] = reinterpret_cast<const float *>(row)[c];
+      } else {
+        f[j] = __uint_as_float(static_cast<uint32_t>(reinterpret_cast<const bf16_bits *>(row)[c].v)
+                               << 16);
+      }
+    }
+  };
+  // the levels whose node changes at `leaf` flush their maximum and get
+  // their new centre (the leaf level's comes from `pre` when given)
+  const auto enter = [&](int64_t leaf, const float *pre) {
     const int64_t node = owner ? leaf / my_span : -1;
     if (owner && node != my_node) {
       flush();
       my_node = node;
       my_max = 0.0;
     }
-    // centres of every ancestor of this leaf into LDS (every level: the
-    // upper rows are L2-resident and a leaf's keys cost far more)
     for (int l = 1; l <= lv; ++l) {
       const int64_t anc = leaf / a.span[l];
-      const S *row = summ + a.summ_off[l] + (head * a.n_at[l] + anc) * D;
-      for (int c = lane; c < D; c += 64) {
-        float f;
-        if constexpr (sizeof(S) == 4) {
-          f = reinterpret_cast<const float *>(row)[c];
-        } else {
-          f = __uint_as_float(static_cast<uint32_t>(reinterpret_cast<const bf16_bits *>(row)[c].v)
-                              << 16);
-        }
-        cw[l][c] = f;
+      if (l < lv && leaf != leaf0 && anc == (leaf - 1) / a.span[l]) continue;  // same node
+      float f[CPL];
+      if (l == lv && pre) {
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) f[j] = pre[j];
+      } else {
+        centre(l, anc, f);
       }
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) cw[l][lane + 64 * j] = f[j];
     }
     // LDS accesses of one wave are performed in order: the rows written
     // above are what the lanes read below
     __builtin_amdgcn_wave_barrier();
+  };
+  // the wave's rows as one stream of batches of RB rows (nb per leaf): the
+  // next batch's loads are issued before the current one is worked on, so
+  // they are in flight during its fp64 arithmetic
+  const int nb = (L + RB - 1) / RB;
+  const int64_t total = (leaf1 - leaf0) * nb;
+  const auto load_batch = [&](int64_t q, uint4 (&kv)[U]) {
+    const int64_t leaf = leaf0 + q / nb;
+    const int r0 = static_cast<int>(q % nb) * RB;
     const T *kl = kh + leaf * L * D;
-    for (int r0 = 0; r0 < L; r0 += RB) {
-      uint4 kv[U];
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      const int row = r0 + i * R + rsub;
+      kv[i] = row < L ? load16(kl + static_cast<int64_t>(row) * D) : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  uint4 cur[U], nxt[U];
+  if (total > 0) {
+    enter(leaf0, nullptr);
+    load_batch(0, cur);
+  }
+  for (int64_t q = 0; q < total; ++q) {
+    const int r0 = static_cast<int>(q % nb) * RB;
+    const bool next_leaf = q + 1 < total && (q + 1) % nb == 0;
+    float pre[CPL];  // the next leaf's own centre, fetched ahead of its rows
+    if (next_leaf) centre(lv, leaf0 + (q + 1) / nb, pre);
+    if (q + 1 < total) load_batch(q + 1, nxt);
+    const bool valid = r0 + kk * R + rsub < L;
+    double kd[U][E];  // the batch's keys, widened once
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      float k[E];
+      Vec16<T>::unpack(cur[i], k);
+#pragma unroll
+      for (int e = 0; e < E; ++e) kd[i][e] = static_cast<double>(k[e]);
+    }
+    for (int l = 1; l <= lv; ++l) {
+      double c[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) c[e] = static_cast<double>(cw[l][col + e]);
+      double part[U];
 #pragma unroll
       for (int i = 0; i < U; ++i) {
-        const int row = r0 + i * R + rsub;
-        kv[i] = row < L ? load16(kl + static_cast<int64_t>(row) * D) : make_uint4(0u, 0u, 0u, 0u);
-      }
-      float k[U][E];
+        double sq = 0.0;
 #pragma unroll
-      for (int i = 0; i < U; ++i) Vec16<T>::unpack(kv[i], k[i]);
-      const bool valid = r0 + kk * R + rsub < L;
-      for (int l = 1; l <= lv; ++l) {
-        float c[E];
-#pragma unroll
-        for (int e = 0; e < E; ++e) c[e] = cw[l][col + e];
-        double part[U];
-#pragma unroll
-        for (int i = 0; i < U; ++i) {
-          double s = 0.0;
-#pragma unroll
-          for (int e = 0; e < E; ++e) {
-            const double diff = static_cast<double>(k[i][e]) - static_cast<double>(c[e]);
-            s = fma(diff, diff, s);
-          }
-          part[i] = s;
+        for (int e = 0; e < E; ++e) {
+          const double diff = kd[i][e] - c[e];  // exact: both are float32 values
+          sq = fma(diff, diff, sq);
         }
-        // lane holds the squared distance of row r0 + kk * R + rsub
-        const double d2 = group_transpose_reduce<U, LPR>(part, lane);
-        const double m = wave_max_d(valid ? d2 : 0.0);
-        if (lane == l - 1) my_max = fmax(my_max, m);
+        part[i] = sq;
       }
+      // lane holds the squared distance of row r0 + kk * R + rsub
+      const double d2 = group_transpose_reduce<U, LPR>(part, lane);
+      const double m = wave_max_d(valid ? d2 : 0.0);
+      if (lane == l - 1) my_max = fmax(my_max, m);
     }
-    __builtin_amdgcn_wave_barrier();
+    if (next_leaf) {
+      __builtin_amdgcn_wave_barrier();  // this leaf's centre reads come first
+      enter(leaf0 + (q + 1) / nb, pre);
+    }
+#pragma unroll
+    for (int i = 0; i < U; ++i) cur[i] = nxt[i];
   }
   flush();
 }
