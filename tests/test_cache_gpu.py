@@ -125,6 +125,9 @@ LONG = [
     ("leaf_1", "f32", "f32", 2, 1, 64, 1, 2, 3000, 3, [10, 1000, 1, 1500]),
     # chunks are the top height: no heights above them
     ("top_chunks", "bf16", "f32", 3, 5, 64, 2, 2, 405, 4, [7, 200, 1]),
+    # appends that start and end on chunk boundaries (512 keys here), the
+    # last one up to a full cache
+    ("aligned", "bf16", "f32", 8, 64, 128, 1, 4, 8 ** 3 * 64, 8, [512, 1024, 1536]),
 ]
 
 
