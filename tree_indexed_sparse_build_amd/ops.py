@@ -562,12 +562,17 @@ class CacheTree:
         """One decode step: add key n_keys (already written into K and V) to
         the tree and decode Q over the tree with it, in one launch.  Same
         results and tree as append(1) followed by decode(...)."""
-        return self.decode(Q, beam, scale, return_indices, out, indices, _append=True)
+        return self._decode(lib().tis_cache_tree_append_decode, Q, beam, scale, return_indices,
+                            out, indices)
 
     def decode(self, Q: torch.Tensor, beam: int, scale: Optional[float] = None,
                return_indices: bool = False, out: Optional[torch.Tensor] = None,
-               indices: Optional[torch.Tensor] = None, _append: bool = False):
+               indices: Optional[torch.Tensor] = None):
         """Route and attend every query over the cache in one launch."""
+        return self._decode(lib().tis_cache_tree_decode, Q, beam, scale, return_indices, out,
+                            indices)
+
+    def _decode(self, f, Q, beam, scale, return_indices, out, indices):
         _need_device(Q)
         if Q.dtype != self.K.dtype:
             raise TypeError("Q must have the cache's dtype")
@@ -583,7 +588,6 @@ class CacheTree:
         L = lib()
         wsb = L.tis_decode_workspace_bytes(B, Hq, d, beam, self.c.leaf_block)
         ws = _workspace(Q.device, "decode", wsb) if wsb else None
-        f = L.tis_cache_tree_append_decode if _append else L.tis_cache_tree_decode
         check(f(Q.data_ptr(), self.K.data_ptr(), self.V.data_ptr(), self.dt, Hq,
                 ctypes.byref(self.c), beam, 0.0 if scale is None else float(scale), O.data_ptr(),
                 idx.data_ptr() if idx is not None else None,
