@@ -511,3 +511,35 @@ def _prefill(lib, tree_kw=None, **kw):
 def test_prefill_rejects(lib, tree_kw, kw, status):
     assert _prefill(lib, tree_kw, **kw) == status
     assert lib.tis_last_error().decode()
+
+
+def test_struct_layout_matches_the_header(tmp_path):
+    """The binding's ctypes structs have the C header's layout: every field's
+    offset and each struct's size, from a C program compiled against
+    include/tis.h."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    structs = {"tis_tree": _lib.TisTree, "tis_cache_tree": _lib.TisCacheTree}
+    lines = ['#include <stddef.h>', '#include <stdio.h>', '#include "tis.h"', "int main(void) {"]
+    for cname, py in structs.items():
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f, _ in py._fields_:
+            lines.append(f'  printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    subprocess.run([cc, "-std=c99", "-I", inc, "-o", str(exe), str(src)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout
+    got = {}
+    for line in out.splitlines():
+        cname, field, value = line.split()
+        got[(cname, field)] = int(value)
+    for cname, py in structs.items():
+        assert got[(cname, "size")] == ctypes.sizeof(py), cname
+        for f, _ in py._fields_:
+            assert got[(cname, f)] == getattr(py, f).offset, (cname, f)
