@@ -297,6 +297,33 @@ def cache_states(torch, dev, plan, reps, back_to_back):
     return out
 
 
+def distinct_route_bytes(tis, w, Q, K):
+    """Summary bytes the route must read when each distinct row is counted
+    once per KV head (its G query heads run on one XCD and share its L2):
+    the rows of every scored level's candidates, from the route's trace.
+    Levels whose nodes all fit in the beam are kept without scoring; the
+    first level that cuts scores all of its nodes, later ones the children
+    of the nodes each query kept."""
+    import numpy as np
+    tree = tis.tree_build(K, w.branching, w.leaf_block, w.levels)
+    _, tr = tis.tree_route(Q, tree, w.beam, trace=True)
+    tr = tr.cpu().numpy()
+    b, lv, W, G = w.branching, w.levels, w.beam, w.group
+    rows = 0
+    for bb in range(w.batch):
+        for h in range(w.kv_heads):
+            grp = tr[bb, h * G:(h + 1) * G]  # [G, levels, W]
+            for l in range(1, lv + 1):
+                if b ** l <= W:
+                    continue  # kept whole, not scored
+                if b ** (l - 1) <= W:
+                    rows += b ** l  # the first level that cuts: all of its nodes
+                    continue
+                kept = np.unique(grp[:, l - 2][grp[:, l - 2] >= 0])
+                rows += len(kept) * b  # distinct parents kept by the group, b children each
+    return rows * w.head_dim * 4
+
+
 def cache_decode_loop(tis, w, K, V, Q, steps, warmup):
     """The decode loop over a growing cache of the same shape: the tree over
     the first keys of the cache is filled by one long append, then every
@@ -481,6 +508,10 @@ def main(argv=None):
         for h in range(w.kv_heads):
             uniq += len(np.unique(idx[bb, h * w.group:(h + 1) * w.group]))
     attend_dedup = uniq * w.leaf_block * w.head_dim * w.elem_bytes * 2
+    route_dedup = distinct_route_bytes(tis, w, Q, K)
+    # the query rows read and the kept leaves written, once per query
+    qio = w.queries * (w.head_dim * w.elem_bytes + 4 * w.beam)
+    dec_dedup = route_dedup + attend_dedup + qio
     log(f"step {ms_step * 1e3:.1f} us (host enqueue {(h1 - h0) / K_ * 1e6:.1f} us/step, "
         f"wall {(h2 - h0) / K_ * 1e6:.1f} us/step); replayed from a graph "
         f"{ms_step_graph * 1e3:.1f} us; with separate route + attend calls "
@@ -496,7 +527,10 @@ def main(argv=None):
     dec_bytes = by["route"] + by["attend"]
     log(f"decode (fused route + attend) {decode_s * 1e6:.2f} us -> "
         f"{w.queries / decode_s:.3e} queries/s, {dec_bytes / decode_s / 1e9:.1f} GB/s "
-        f"({dec_bytes / decode_s / 1e9 / HBM_PEAK_GBS:.1%}) on {dec_bytes / 1e6:.2f} MB; "
+        f"({dec_bytes / decode_s / 1e9 / HBM_PEAK_GBS:.1%}) on {dec_bytes / 1e6:.2f} MB "
+        f"per-query sum, {dec_dedup / decode_s / 1e9:.1f} GB/s "
+        f"({dec_dedup / decode_s / 1e9 / HBM_PEAK_GBS:.1%}) on {dec_dedup / 1e6:.2f} MB "
+        f"distinct per KV head; "
         f"in the step (step - build): {ms_step * 1e3 - t_build.mean() * 1e6:.2f} us")
 
     states = cache_states(torch, dev, plan, 30,
@@ -591,6 +625,9 @@ def main(argv=None):
                    "route_us": t_route.mean() * 1e6, "attend_us": t_attend.mean() * 1e6,
                    "attend_gbs_per_query_bytes": by["attend"] / t_attend.mean() / 1e9,
                    "attend_gbs_distinct_blocks": attend_dedup / t_attend.mean() / 1e9,
+                   "bytes_per_query_sum": dec_bytes, "bytes_distinct": dec_dedup,
+                   "gbs_distinct": dec_dedup / decode_s / 1e9,
+                   "frac_distinct": dec_dedup / decode_s / 1e9 / HBM_PEAK_GBS,
                    "cache_states": dict(states, regime="cold: 1 GiB read first; steady: cold, "
                                         "then the summaries read once; *_lone_us: median of "
                                         "30 lone launches between events; *_cold_us and "
