@@ -328,7 +328,7 @@ const char *tis_version(void);
 typedef struct tis_cache_tree {
   int32_t batch, kv_heads, head_dim, branching, leaf_block;
   int32_t capacity;  /* keys per (batch, KV head) the cache has room for     */
-  int32_t n_keys;    /* keys in the tree: set by reset (0) and append        */
+  int32_t n_keys;    /* keys in the tree: set by reset (0) and the appends   */
   int32_t levels;    /* depth over n_keys (0 while empty): set by the library */
   int32_t summary_dtype; /* tis_dtype of the stored summaries (as tis_tree)  */
   int32_t state_half; /* half of `state` in use (0 or 1): set by the library */
