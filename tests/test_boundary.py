@@ -471,11 +471,18 @@ def test_decode_threshold_rejects(lib, kw, status):
 # -------------------------------------------------------- causal prefill --
 
 def test_prefill_workspace_bytes(lib):
-    # 1,024 keys, b 2, L 16: depth 6; one fp32 row per (head, position, height)
+    # 1,024 keys, b 2, L 16: depth 6; one fp32 row per (head, position, height),
+    # then an fp64 row per (head, run of 64 keys)
     assert lib.tis_causal_prefill_workspace_bytes(1, 1, 64, 2, 16, 1024, _lib.TIS_F32) == (
-        1024 * 6 * 64 * 4)
+        1024 * 6 * 64 * 4 + 16 * 64 * 8)
     assert lib.tis_causal_prefill_workspace_bytes(2, 3, 128, 4, 16, 100, _lib.TIS_BF16) == (
-        6 * 100 * 2 * 128 * 2)   # 100 keys: 4^2 * 16 = 256 >= 100, depth 2
+        6 * 100 * 2 * 128 * 2 + 6 * 2 * 128 * 8)   # 100 keys: 4^2 * 16 = 256 >= 100, depth 2
+    # past 64^2 keys the sums get a second level (runs of 4,096 keys), past
+    # 64^3 a third: 300,000 keys, b 4, L 16: 4^8 * 16 >= 300,000, depth 8
+    n = 300_000
+    runs = -(-n // 64) + -(-n // 64 ** 2) + -(-n // 64 ** 3)
+    assert lib.tis_causal_prefill_workspace_bytes(1, 2, 64, 4, 16, n, _lib.TIS_F32) == (
+        2 * n * 8 * 64 * 4 + 2 * runs * 64 * 8)
     assert lib.tis_causal_prefill_workspace_bytes(1, 1, 64, 2, 16, 0, _lib.TIS_F32) == 0
     assert lib.tis_causal_prefill_workspace_bytes(1, 1, 96, 2, 16, 10, _lib.TIS_F32) == 0
     assert lib.tis_causal_prefill_workspace_bytes(1, 1, 64, 2, 16, 10, 5) == 0

@@ -154,3 +154,53 @@ def test_prefill_gqa_4096_positions_sampled(tis):
     _say(f"gqa_32k prefill of {P} positions: {len(pos)} sampled positions x "
          f"{w.batch * w.q_heads} queries exact {int(same.sum())}/{same.size} (tie-exposed "
          f"{int((~same & tie).sum())}); max-abs {err:.2e}")
+
+
+LONG = [
+    # (label, dtype, b, L, d, G, positions, beam, sampled positions)
+    # spans of 5 * 3^h, not multiples of 64: node starts fall inside the
+    # 64-key runs; 9,000 keys take the runs of 4,096 as well as those of 64
+    ("span_ragged_9000", "f32", 3, 5, 64, 2, 9000, 4,
+     [0, 63, 64, 3644, 3645, 3646, 3708, 3709, 4095, 4096, 4097, 7289, 7290, 7291, 8191, 8192,
+      8959, 8960, 8999]),
+    # past 64^3 keys: runs of 262,144 keys too
+    ("runs_262144", "bf16", 4, 16, 64, 2, 270_000, 4,
+     [0, 4095, 4096, 65535, 65536, 131071, 200_000, 262_143, 262_144, 262_207, 262_208, 269_999]),
+]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("case", LONG, ids=[c[0] for c in LONG])
+def test_prefill_long_sampled(tis, case):
+    """Long prefills, where a position's open node starts tens of thousands
+    of keys back: the partial means come from fp64 sums over runs of 64,
+    4,096, 262,144 keys.  Checked at sampled positions (node and run
+    boundaries on both sides) against the oracle."""
+    label, dtype, b, L, d, G, P, beam, pos = case
+    t0 = time.time()
+    rng = np.random.default_rng(P)
+    K = to_storage(rng.standard_normal((1, 1, P, d)), dtype)
+    V = to_storage(rng.standard_normal((1, 1, P, d)), dtype)
+    Q = to_storage(rng.standard_normal((1, G, P, d)), dtype)
+    Kd = tis.from_storage(K, dtype, "cuda")
+    Vd = tis.from_storage(V, dtype, "cuda")
+    Qd = tis.from_storage(Q, dtype, "cuda")
+    ct = tis.CacheTree(Kd, Vd, b, L)
+    ct.append(P)
+    out, idx = ct.causal_prefill(Qd, beam, return_indices=True)
+    torch.cuda.synchronize()
+    pos = np.array(pos)
+    out, idx = out[:, :, pos].cpu().numpy(), idx[:, :, pos].cpu().numpy()
+    _say(f"{label}: GPU prefill of {P} positions done, {time.time() - t0:.1f}s")
+    orc = C.causal_prefill(Q, K, V, dtype, b, L, beam, positions=pos)
+    tie = orc["gap"] < parity.TIE_GAP
+    same = np.all(idx == orc["indices"], axis=-1)
+    assert np.all(same | tie), f"{np.count_nonzero(~same & ~tie)} sampled positions differ"
+    err = 0.0
+    for i, t in enumerate(pos):
+        o_g = GO.grow_attend(np.ascontiguousarray(Q[:, :, t]), K, V, dtype, idx[:, :, i],
+                             int(t) + 1, L)
+        err = max(err, parity.compare_outputs(out[:, :, i], o_g, dtype))
+    _say(f"{label}: {len(pos)} sampled positions x {G} queries exact {int(same.sum())}/"
+         f"{same.size} (tie-exposed {int((~same & tie).sum())}); max-abs {err:.2e}; "
+         f"{time.time() - t0:.1f}s")

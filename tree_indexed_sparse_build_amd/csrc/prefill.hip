@@ -8,12 +8,15 @@
 // the one a tree over all n keys stores; only the node holding key t at each
 // height (the open node) covers fewer keys, and its mean differs per t.
 //
+//  * k_block_sums + k_sum_up: fp64 key sums in a hierarchy of factor 64
+//    (runs of 64, 4096, ... positions), each key read once.
 //  * k_prefix_means: for every height h of the tree and every position t,
 //    the mean of the keys from the start of t's height-h node up to t (the
-//    open node's summary as position t sees it), summed in fp64 in key order
-//    and rounded once to the summary type.  One workgroup per (head, height,
-//    block of 64 positions), a thread per column: it first sums the keys of
-//    the node that lie before the block, then walks the block.
+//    open node's summary as position t sees it), summed in fp64 and rounded
+//    once to the summary type.  One workgroup per (head, height, block of 64
+//    positions), a thread per column: it adds up the node's keys that lie
+//    before the block from the hierarchy (at most 63 keys, then at most 2 *
+//    63 sums a level), then walks the block in key order.
 //  * k_prefill: one workgroup per (batch, query head, position), of one
 //    wave when a level has at most 32 candidates (beam * b), 2 waves up to
 //    64, 4 up to 128, else 8: a prefill query reads few keys, so small workgroups (LDS
@@ -30,12 +33,79 @@
 namespace tis {
 namespace {
 
-constexpr int kPrefixRows = 64;   // positions per workgroup of k_prefix_means
-
 template <typename T> __device__ inline double elem64(const T *p);
 template <> __device__ inline double elem64<float>(const float *p) { return *p; }
 template <> __device__ inline double elem64<bf16_bits>(const bf16_bits *p) {
   return __uint_as_float(static_cast<uint32_t>(p->v) << 16);
+}
+
+// Level 0 of the hierarchy: the sum of each run of 64 keys, in key order.
+template <typename T, int D>
+__global__ void __launch_bounds__(D) k_block_sums(PrefillArgs a) {
+  const int64_t n0 = a.sum_n[0];
+  const int64_t head = blockIdx.x / n0;
+  const int64_t i = blockIdx.x - head * n0;
+  const int c = threadIdx.x;
+  const T *kh = static_cast<const T *>(a.K) + head * a.capacity * D + c;
+  const int64_t p0 = i * kPrefixRows;
+  const int64_t p1 = min(p0 + kPrefixRows, static_cast<int64_t>(a.positions));
+  double acc = 0.0;
+  for (int64_t t0 = p0; t0 < p1; t0 += 8) {
+    double v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = t0 + u < p1 ? elem64<T>(kh + (t0 + u) * D) : 0.0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += v[u];
+  }
+  a.sums[a.sum_off[0] + (head * n0 + i) * D + c] = acc;
+}
+
+// Level k >= 1: the sum of each run of 64 entries of level k - 1, in order.
+template <int D>
+__global__ void __launch_bounds__(D) k_sum_up(PrefillArgs a, int k) {
+  const int64_t n = a.sum_n[k], nb = a.sum_n[k - 1];
+  const int64_t head = blockIdx.x / n;
+  const int64_t i = blockIdx.x - head * n;
+  const int c = threadIdx.x;
+  const double *src = a.sums + a.sum_off[k - 1] + head * nb * D + c;
+  const int64_t j0 = i * kPrefixRows;
+  const int64_t j1 = min(j0 + kPrefixRows, nb);
+  double acc = 0.0;
+  for (int64_t j = j0; j < j1; j += 8) {
+    double v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = j + u < j1 ? src[(j + u) * D] : 0.0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += v[u];
+  }
+  a.sums[a.sum_off[k] + (head * n + i) * D + c] = acc;
+}
+
+template <typename T, int D>
+__device__ inline double sum_keys(const T *kh, int64_t x, int64_t y) {
+  double acc = 0.0;
+  for (int64_t t0 = x; t0 < y; t0 += 8) {
+    double v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = t0 + u < y ? elem64<T>(kh + (t0 + u) * D) : 0.0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += v[u];
+  }
+  return acc;
+}
+
+// Entries [x, y) of one level's column (stride D), in order.
+template <int D>
+__device__ inline double sum_entries(const double *lvl, int64_t x, int64_t y) {
+  double acc = 0.0;
+  for (int64_t j0 = x; j0 < y; j0 += 8) {
+    double v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = j0 + u < y ? lvl[(j0 + u) * D] : 0.0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += v[u];
+  }
+  return acc;
 }
 
 template <typename T, typename S, int D>
@@ -52,18 +122,28 @@ __global__ void __launch_bounds__(D) k_prefix_means(PrefillArgs a) {
   const T *kh = static_cast<const T *>(a.K) + head * a.capacity * D + c;
   S *pm = static_cast<S *>(a.open_summ);
 
-  // keys of t's node that come before the block
+  // keys of t's node that come before the block: [s0, p0) = up to 63 keys
+  // to the first run boundary, then level by level the runs on both ends of
+  // what is left, then the middle at the level where it fits
   const int64_t s0 = (p0 / span) * span;
   double acc = 0.0;
-  int64_t k = s0;
-  for (; k + 8 <= p0; k += 8) {
-    double v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = elem64<T>(kh + (k + u) * D);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) acc += v[u];
+  if (s0 < p0) {
+    const int64_t a0 = min((s0 + kPrefixRows - 1) / kPrefixRows * kPrefixRows, p0);
+    acc += sum_keys<T, D>(kh, s0, a0);
+    int64_t x = a0 / kPrefixRows, y = p0 / kPrefixRows;  // level-0 entries [x, y)
+    int k = 0;
+    for (; k + 1 < a.sum_levels; ++k) {
+      const int64_t xu = (x + kPrefixRows - 1) / kPrefixRows * kPrefixRows;
+      const int64_t yd = y / kPrefixRows * kPrefixRows;
+      if (xu >= yd) break;  // no whole run of the level above in between
+      const double *lvl = a.sums + a.sum_off[k] + head * a.sum_n[k] * D + c;
+      acc += sum_entries<D>(lvl, x, xu);
+      acc += sum_entries<D>(lvl, yd, y);
+      x = xu / kPrefixRows;
+      y = yd / kPrefixRows;
+    }
+    acc += sum_entries<D>(a.sums + a.sum_off[k] + head * a.sum_n[k] * D + c, x, y);
   }
-  for (; k < p0; ++k) acc += elem64<T>(kh + k * D);
   uint32_t held = static_cast<uint32_t>(p0 - s0);  // keys of the node summed so far
   for (int64_t t0 = p0; t0 < p1; t0 += 8) {
     double v[8];
@@ -150,8 +230,17 @@ hipError_t launch_prefill_d(const RouteArgs &ra, const AttendArgs &aa, const Pre
   const int64_t nblk = (pa.positions + kPrefixRows - 1) / kPrefixRows;
   const dim3 g1(static_cast<unsigned>(pa.heads * pa.levels * nblk));
   const dim3 g2(static_cast<unsigned>(ra.queries));
-  hipLaunchKernelGGL((k_prefix_means<T, S, D>), g1, dim3(D), 0, s, pa);
+  hipLaunchKernelGGL((k_block_sums<T, D>), dim3(static_cast<unsigned>(pa.heads * pa.sum_n[0])),
+                     dim3(D), 0, s, pa);
   hipError_t e = hipGetLastError();
+  for (int k = 1; e == hipSuccess && k < pa.sum_levels; ++k) {
+    hipLaunchKernelGGL((k_sum_up<D>), dim3(static_cast<unsigned>(pa.heads * pa.sum_n[k])),
+                       dim3(D), 0, s, pa, k);
+    e = hipGetLastError();
+  }
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_prefix_means<T, S, D>), g1, dim3(D), 0, s, pa);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (ra.beam * ra.branching <= 32)
     hipLaunchKernelGGL((k_prefill<T, S, D, 1>), g2, dim3(64), 0, s, ra, aa, pa);

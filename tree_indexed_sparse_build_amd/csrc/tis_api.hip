@@ -831,8 +831,15 @@ size_t tis_causal_prefill_workspace_bytes(int batch, int kv_heads, int head_dim,
   const double bytes = static_cast<double>(batch) * kv_heads * n_keys * lv * head_dim *
                        summary_elem_bytes(summary_dtype);
   if (bytes > 9.0e18) return 0;
+  // the partial-means table, then the fp64 key sums over runs of 64, 64^2, ...
+  size_t sums = 0;
+  const int kl = tis::prefix_sum_levels(n_keys);
+  int64_t run = tis::kPrefixRows;
+  for (int k = 0; k < kl; ++k, run *= tis::kPrefixRows)
+    sums += static_cast<size_t>((n_keys + run - 1) / run);
   return static_cast<size_t>(batch) * kv_heads * static_cast<size_t>(n_keys) * lv * head_dim *
-         summary_elem_bytes(summary_dtype);
+             summary_elem_bytes(summary_dtype) +
+         static_cast<size_t>(batch) * kv_heads * sums * head_dim * sizeof(double);
 }
 
 tis_status tis_causal_prefill(const void *Q, const void *K, const void *V, tis_dtype dtype,
@@ -872,6 +879,19 @@ tis_status tis_causal_prefill(const void *Q, const void *K, const void *V, tis_d
   pa.capacity = tree->capacity;
   pa.positions = tree->n_keys;
   pa.levels = tree->levels;
+  {
+    const size_t table = static_cast<size_t>(g.heads) * tree->n_keys * tree->levels *
+                         tree->head_dim * summary_elem_bytes(
+                             static_cast<tis_dtype>(tree->summary_dtype));
+    pa.sums = reinterpret_cast<double *>(static_cast<char *>(workspace) + table);
+    pa.sum_levels = tis::prefix_sum_levels(tree->n_keys);
+    int64_t run = tis::kPrefixRows, off = 0;
+    for (int k = 0; k < pa.sum_levels; ++k, run *= tis::kPrefixRows) {
+      pa.sum_n[k] = (tree->n_keys + run - 1) / run;
+      pa.sum_off[k] = off;
+      off += g.heads * pa.sum_n[k] * tree->head_dim;
+    }
+  }
   {
     int64_t span = tree->leaf_block, off = 0;
     for (int h = 0; h <= tis::kMaxLevels; ++h) {

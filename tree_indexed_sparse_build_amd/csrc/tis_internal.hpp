@@ -223,6 +223,19 @@ hipError_t launch_decode_threshold(Dt dt, Dt sdt, int head_dim, const RouteArgs 
                                    const SphereArgs &sa, const AttendArgs &aa, hipStream_t s);
 
 // -------------------------------------------------------- causal prefill --
+constexpr int kPrefixRows = 64;    // positions a block (and the sums' factor)
+constexpr int kMaxSumLevels = 6;   // 64^6 > 2^31 positions
+// levels of the prefix-sum hierarchy over n positions (entries of 64^(k+1)
+// positions, for every k with 64^(k+1) < n; at least one)
+inline int prefix_sum_levels(int64_t n) {
+  int k = 1;
+  int64_t c = int64_t{kPrefixRows} * kPrefixRows;
+  while (k < kMaxSumLevels && c < n) {
+    ++k;
+    c *= kPrefixRows;
+  }
+  return k;
+}
 // Every position t of a growing cache's first `positions` keys is a query
 // over the tree of the first t + 1 keys.  open_summ holds, for every
 // (head, position, height < levels), the mean of the keys of t's node up to
@@ -237,6 +250,14 @@ struct PrefillArgs {
   int64_t h_span[kMaxLevels + 1];  // keys under a node of height h: L b^h
   int64_t h_rows[kMaxLevels + 1];  // summary rows per head of height h
   int64_t h_off[kMaxLevels + 1];   // element offset of height h's block
+  // fp64 key sums in a hierarchy of factor 64: level k holds, per head, the
+  // sums of consecutive runs of 64^(k+1) positions ([heads][sum_n[k]][d] at
+  // element sum_off[k] of `sums`), so the keys of any range of positions
+  // add up from at most 2 * 63 entries a level
+  double *sums;
+  int sum_levels;
+  int64_t sum_n[kMaxSumLevels];
+  int64_t sum_off[kMaxSumLevels];
 };
 
 hipError_t launch_prefill(Dt dt, Dt sdt, int head_dim, const RouteArgs &ra, const AttendArgs &aa,
