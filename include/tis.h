@@ -413,9 +413,12 @@ tis_status tis_cache_tree_append_decode(const void *Q, const void *K, const void
  * first.
  * --------------------------------------------------------------------- */
 
-/* Bytes of the workspace tis_causal_prefill needs: the partial means,
- * B * Hkv * n_keys * depth(n_keys) * d elements of the summary type
- * (0 if invalid). */
+/* Bytes of the workspace tis_causal_prefill needs (0 if invalid): the
+ * partial means, B * Hkv * n_keys * depth(n_keys) * d elements of the
+ * summary type, then fp64 key sums, B * Hkv * d doubles for every run of
+ * 64 keys, every run of 64^2 keys (past 64^2 keys), of 64^3 (past 64^3),
+ * and so on: runs of 64^(k+1) are kept while 64^(k+1) < n_keys, and the
+ * runs of 64 always. */
 size_t tis_causal_prefill_workspace_bytes(int batch, int kv_heads, int head_dim, int branching,
                                           int leaf_block, int n_keys, tis_dtype summary_dtype);
 
