@@ -413,14 +413,21 @@ tis_status tis_cache_tree_append_decode(const void *Q, const void *K, const void
  * first.
  * --------------------------------------------------------------------- */
 
-/* Bytes of the workspace tis_causal_prefill needs (0 if invalid): the
- * partial means, B * Hkv * n_keys * depth(n_keys) * d elements of the
- * summary type, then fp64 key sums, B * Hkv * d doubles for every run of
- * 64 keys, every run of 64^2 keys (past 64^2 keys), of 64^3 (past 64^3),
- * and so on: runs of 64^(k+1) are kept while 64^(k+1) < n_keys, and the
- * runs of 64 always. */
-size_t tis_causal_prefill_workspace_bytes(int batch, int kv_heads, int head_dim, int branching,
-                                          int leaf_block, int n_keys, tis_dtype summary_dtype);
+/* Bytes of the workspace tis_causal_prefill needs (0 if invalid), for a
+ * tree of n_keys keys, q_heads query heads, the beam and the key type:
+ *  - the partial means, B * Hkv * n_keys * depth(n_keys) * d elements of
+ *    the summary type;
+ *  - fp64 key sums, B * Hkv * d doubles for every run of 64 keys, every run
+ *    of 64^2 keys (past 64^2 keys), of 64^3 (past 64^3), and so on: runs of
+ *    64^(k+1) are kept while 64^(k+1) < n_keys, and the runs of 64 always;
+ *  - when leaf_block is a multiple of 16 and at least 32 (the attention
+ *    then takes 16 positions at a time on the matrix cores, if its LDS fits
+ *    the beam: beam <= 87 always does), at 256-byte offsets: the
+ *    kept leaves, int32 [B][Hq][n_keys][beam], and V transposed per 16 keys,
+ *    B * Hkv * ceil(n_keys / 16) * 16 * d elements of the key type. */
+size_t tis_causal_prefill_workspace_bytes(int batch, int kv_heads, int q_heads, int head_dim,
+                                          int branching, int leaf_block, int n_keys, int beam,
+                                          tis_dtype dtype, tis_dtype summary_dtype);
 
 /*
  * tis_causal_prefill -- every position of the first tree->n_keys keys of a

@@ -471,21 +471,44 @@ def test_decode_threshold_rejects(lib, kw, status):
 # -------------------------------------------------------- causal prefill --
 
 def test_prefill_workspace_bytes(lib):
-    # 1,024 keys, b 2, L 16: depth 6; one fp32 row per (head, position, height),
-    # then an fp64 row per (head, run of 64 keys)
-    assert lib.tis_causal_prefill_workspace_bytes(1, 1, 64, 2, 16, 1024, _lib.TIS_F32) == (
-        1024 * 6 * 64 * 4 + 16 * 64 * 8)
-    assert lib.tis_causal_prefill_workspace_bytes(2, 3, 128, 4, 16, 100, _lib.TIS_BF16) == (
-        6 * 100 * 2 * 128 * 2 + 6 * 2 * 128 * 8)   # 100 keys: 4^2 * 16 = 256 >= 100, depth 2
+    f = lib.tis_causal_prefill_workspace_bytes
+    F32, BF16 = _lib.TIS_F32, _lib.TIS_BF16
+
+    def up(x):
+        return -(-x // 256) * 256
+
+    # 1,024 keys, b 2, L 32: depth 5; one fp32 row per (head, position,
+    # height), an fp64 row per (head, run of 64 keys); L a multiple of 16 and
+    # 32 or more, so also the kept leaves (2 query heads, beam 3) and V per 16
+    # keys (fp32)
+    means, sums = 1024 * 5 * 64 * 4, 16 * 64 * 8
+    idx = up(means + sums)
+    vt = up(idx + 2 * 1024 * 3 * 4)
+    assert f(1, 1, 2, 64, 2, 32, 1024, 3, F32, F32) == vt + 64 * 16 * 64 * 4
+    # bf16 keys: V's copy is half as large
+    assert f(1, 1, 2, 64, 2, 32, 1024, 3, BF16, F32) == vt + 64 * 16 * 64 * 2
+    # L 16 and L 5: no 16-position attention, so no leaves or V copy
+    assert f(1, 1, 2, 64, 2, 16, 1024, 3, F32, F32) == 1024 * 6 * 64 * 4 + sums
+    assert f(2, 3, 6, 128, 4, 5, 100, 2, BF16, BF16) == (
+        6 * 100 * 3 * 128 * 2 + 6 * 2 * 128 * 8)   # 100 keys: 4^3 * 5 = 320 >= 100, depth 3
     # past 64^2 keys the sums get a second level (runs of 4,096 keys), past
-    # 64^3 a third: 300,000 keys, b 4, L 16: 4^8 * 16 >= 300,000, depth 8
+    # 64^3 a third: 300,000 keys, b 4, L 32: 4^7 * 32 >= 300,000, depth 7
     n = 300_000
     runs = -(-n // 64) + -(-n // 64 ** 2) + -(-n // 64 ** 3)
-    assert lib.tis_causal_prefill_workspace_bytes(1, 2, 64, 4, 16, n, _lib.TIS_F32) == (
-        2 * n * 8 * 64 * 4 + 2 * runs * 64 * 8)
-    assert lib.tis_causal_prefill_workspace_bytes(1, 1, 64, 2, 16, 0, _lib.TIS_F32) == 0
-    assert lib.tis_causal_prefill_workspace_bytes(1, 1, 96, 2, 16, 10, _lib.TIS_F32) == 0
-    assert lib.tis_causal_prefill_workspace_bytes(1, 1, 64, 2, 16, 10, 5) == 0
+    idx = up(2 * n * 7 * 64 * 4 + 2 * runs * 64 * 8)
+    vt = up(idx + 2 * n * 1 * 4)
+    assert f(1, 2, 2, 64, 4, 32, n, 1, F32, F32) == vt + 2 * (-(-n // 16)) * 16 * 64 * 4
+    # a beam whose union table fits no workgroup (f32, d 128, beam 88, even
+    # one head a workgroup): the fused kernel, no leaves or V copy
+    assert f(1, 1, 1, 128, 2, 32, 1024, 88, F32, F32) == 1024 * 5 * 128 * 4 + 16 * 128 * 8
+    # invalid: no keys, head_dim 96, summary type 5, fp8 keys, q_heads not a
+    # multiple of kv_heads, beam 0
+    assert f(1, 1, 1, 64, 2, 16, 0, 1, F32, F32) == 0
+    assert f(1, 1, 1, 96, 2, 16, 10, 1, F32, F32) == 0
+    assert f(1, 1, 1, 64, 2, 16, 10, 1, F32, 5) == 0
+    assert f(1, 1, 1, 64, 2, 16, 10, 1, _lib.TIS_FP8_E4M3, F32) == 0
+    assert f(1, 2, 3, 64, 2, 16, 10, 1, F32, F32) == 0
+    assert f(1, 1, 1, 64, 2, 16, 10, 0, F32, F32) == 0
 
 
 def _prefill(lib, tree_kw=None, **kw):

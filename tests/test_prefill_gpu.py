@@ -77,6 +77,18 @@ CASES = [
     ("cand_48_f32_d64", "f32", "f32", 1, 1, 3, 333, 64, 6, 5, 8, "normal"),
     # more than 128 candidates a level (8-wave workgroups)
     ("cand_160", "bf16", "f32", 1, 2, 2, 700, 128, 8, 4, 20, "normal"),
+    # leaf blocks of a multiple of 16 keys, 32 or more: attention 16
+    # positions at a time on the matrix cores, a wave per query head, 4, 2
+    # or 1 heads of a KV group a workgroup (group 3: one); positions not a
+    # multiple of 16, leaves of 2, 3 and 4 key tiles
+    ("tiles_L32_ragged_g3", "bf16", "f32", 1, 2, 3, 333, 128, 3, 32, 5, "normal"),
+    ("tiles_L48_f32_bf16s_g2", "f32", "bf16", 2, 1, 2, 250, 64, 2, 48, 3, "normal"),
+    # a wide beam: up to 64 * 12 leaves in a workgroup's union
+    ("tiles_L32_beam_12_g4", "f32", "f32", 1, 1, 4, 400, 128, 2, 32, 12, "mixture"),
+    ("tiles_L64_bf16_d64_g8", "bf16", "f32", 1, 2, 8, 300, 64, 4, 64, 2, "normal"),
+    ("tiles_L32_bf16_g1", "bf16", "bf16", 2, 3, 1, 129, 64, 4, 32, 3, "normal"),
+    # a beam whose union table does not fit 4 heads' LDS: 2 heads a workgroup
+    ("tiles_L32_beam_48_g4", "bf16", "f32", 1, 1, 4, 200, 64, 2, 32, 48, "normal"),
 ]
 
 

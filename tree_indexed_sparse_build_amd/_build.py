@@ -32,6 +32,10 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 instructions stay off (their use is left to no one)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators in ordinary VGPRs: the prefill's output tile
+    # is rescaled by vector code between products, which in AGPRs would cost
+    # a copy out and back every step
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-command-line-argument",
     "-I", INCLUDE, "-I", CSRC,
 ]

@@ -88,7 +88,7 @@ SIGNATURES = {
     "tis_tree_decode_threshold": (_c_int, [_vp, _vp, _vp, _c_int, _c_int,
                                            ctypes.POINTER(TisTree), _vp, _vp, _c_int, _c_float,
                                            _vp, _vp, _vp, _vp, _c_size, _vp]),
-    "tis_causal_prefill_workspace_bytes": (_c_size, [_c_int] * 7),
+    "tis_causal_prefill_workspace_bytes": (_c_size, [_c_int] * 10),
     "tis_causal_prefill": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, ctypes.POINTER(TisCacheTree),
                                     _c_int, _c_float, _vp, _vp, _vp, _c_size, _vp]),
     "tis_last_error": (ctypes.c_char_p, []),

@@ -166,10 +166,9 @@ __global__ void __launch_bounds__(D) k_prefix_means(PrefillArgs a) {
   }
 }
 
-template <typename T, typename S, int D, int NW>
+template <typename T, typename S, int D, int NW, bool ATTEND>
 __global__ void __launch_bounds__(NW * 64) k_prefill(RouteArgs ra, AttendArgs aa, PrefillArgs pa) {
   __shared__ RouteShared<NW, NW * 32> rsh;
-  __shared__ AttendShared<T, D, NW> ash;
   __shared__ CausalLevels cl;
   const int qi = blockIdx.x;
   const int hrow = qi / pa.positions;          // (batch, query head)
@@ -220,8 +219,408 @@ __global__ void __launch_bounds__(NW * 64) k_prefill(RouteArgs ra, AttendArgs aa
     write_ascending<NW * 64>(rsh.front, kept, out);
     for (int k = kept + static_cast<int>(threadIdx.x); k < ra.beam; k += NW * 64) out[k] = -1;
   }
-  attend_query<T, D, true, false, true>(aa, ash, qi, qraw, rsh.front, nullptr, kept, false,
-                                        nullptr, 0.0, hrow, static_cast<int64_t>(t) + 1);
+  if constexpr (ATTEND) {
+    __shared__ AttendShared<T, D, NW> ash;
+    attend_query<T, D, true, false, true>(aa, ash, qi, qraw, rsh.front, nullptr, kept, false,
+                                          nullptr, 0.0, hrow, static_cast<int64_t>(t) + 1);
+  }
+}
+
+// ---- block-sparse causal attention on the matrix cores ------------------
+// Used when the leaf block is a multiple of 16 keys, after a routing-only
+// pass has written every position's kept leaves.  A workgroup takes 16
+// consecutive positions of HW query heads that share a KV head (HW = 4, 2
+// or 1, dividing the group), a wave per head.  Wave 0 merges the HW * 16
+// rows' kept leaves (each list ascending) into one ascending union, each
+// leaf with the rows that kept it.  The workgroup then walks the union's
+// keys 16 at a time: each key tile of K and of V is loaded once, with
+// contiguous 16-byte loads shared by all waves, into LDS (two buffers: the
+// next tile loads while this one computes), and every wave reads its
+// operands from there:
+//   * scores come out transposed, S^T = K Q^T (16 keys x 16 rows, fp32
+//     accumulation), so lane l holds row l % 16 and keys 4 (l / 16) + i,
+//     i = 0..3, of the key tile: each lane keeps one row's running maximum
+//     and a partial sum of that row's weights;
+//   * a key counts for a row when the row kept the leaf and the key is not
+//     past the row's position;
+//   * weights are taken against a reference maximum that moves only when a
+//     score passes it by more than 2^8, so the output accumulators are
+//     rescaled only then;
+//   * the same registers are the A operand of P V (rows x keys), and V is
+//     read from a transposed copy, [head][key / 16][d][16], whose 4
+//     consecutive keys per lane match the lane's keys.
+// bf16 inputs: scores with the 16x16x32 bf16 product, weights rounded to
+// bf16 for the 16x16x16 bf16 product with V; fp32 inputs: the 16x16x4 fp32
+// product for both.
+typedef short mf_bf16x8 __attribute__((ext_vector_type(8)));
+typedef short mf_bf16x4 __attribute__((ext_vector_type(4)));
+typedef float mf_f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline short bf16_rne(float f) {  // finite f
+  const uint32_t u = __float_as_uint(f);
+  return static_cast<short>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+template <typename T, int D> struct TileMath;
+
+template <int D> struct TileMath<bf16_bits, D> {
+  // the query rows as the B operand of K Q^T: row r, dims 32 s + 8 g .. + 7
+  mf_bf16x8 q[D / 32];
+  struct KReg { uint4 v[D / 32]; };
+  struct VReg { uint2 v[D / 16]; };
+  static constexpr int VS = 24;  // elements per V row in LDS: 16 keys, padded by 16 bytes
+  __device__ void load_q(const bf16_bits *qrow, bool valid, int g) {
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+      uint4 u = valid ? *reinterpret_cast<const uint4 *>(qrow + 32 * s + 8 * g) : make_uint4(0, 0, 0, 0);
+      q[s] = __builtin_bit_cast(mf_bf16x8, u);
+    }
+  }
+  __device__ static void load_k(KReg &k, const bf16_bits *krow, int g) {
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) k.v[s] = *reinterpret_cast<const uint4 *>(krow + 32 * s + 8 * g);
+  }
+  // vt points at a key tile's [d][16] block in LDS (rows VS apart): lane
+  // column r, key group g
+  __device__ static void load_v(VReg &v, const bf16_bits *vt, int r, int g) {
+#pragma unroll
+    for (int nt = 0; nt < D / 16; ++nt)
+      v.v[nt] = *reinterpret_cast<const uint2 *>(vt + (16 * nt + r) * VS + 4 * g);
+  }
+  __device__ mf_f32x4 scores(const KReg &k) const {
+    mf_f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s)
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mf_bf16x8, k.v[s]), q[s], c,
+                                                   0, 0, 0);
+    return c;
+  }
+  // o[nt] += P (rows x 16 keys) V (16 keys x dims 16 nt .. + 15)
+  __device__ static void pv(mf_f32x4 *o, const float *p, const VReg &v) {
+    mf_bf16x4 a;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = bf16_rne(p[i]);
+#pragma unroll
+    for (int nt = 0; nt < D / 16; ++nt)
+      o[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, __builtin_bit_cast(mf_bf16x4, v.v[nt]),
+                                                        o[nt], 0, 0, 0);
+  }
+};
+
+template <int D> struct TileMath<float, D> {
+  // the query rows: row r, dims 16 s + 4 g .. + 3; product (s, i) pairs
+  // lane group g with dim 16 s + 4 g + i in both operands
+  float4 q[D / 16];
+  struct KReg { float4 v[D / 16]; };
+  struct VReg { float4 v[D / 16]; };
+  static constexpr int VS = 20;  // elements per V row in LDS: 16 keys, padded by 16 bytes
+  __device__ void load_q(const float *qrow, bool valid, int g) {
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+      q[s] = valid ? *reinterpret_cast<const float4 *>(qrow + 16 * s + 4 * g)
+                   : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  __device__ static void load_k(KReg &k, const float *krow, int g) {
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) k.v[s] = *reinterpret_cast<const float4 *>(krow + 16 * s + 4 * g);
+  }
+  __device__ static void load_v(VReg &v, const float *vt, int r, int g) {
+#pragma unroll
+    for (int nt = 0; nt < D / 16; ++nt)
+      v.v[nt] = *reinterpret_cast<const float4 *>(vt + (16 * nt + r) * VS + 4 * g);
+  }
+  __device__ mf_f32x4 scores(const KReg &k) const {
+    mf_f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      c = __builtin_amdgcn_mfma_f32_16x16x4f32(k.v[s].x, q[s].x, c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x4f32(k.v[s].y, q[s].y, c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x4f32(k.v[s].z, q[s].z, c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x4f32(k.v[s].w, q[s].w, c, 0, 0, 0);
+    }
+    return c;
+  }
+  // product i pairs lane group g with key 4 g + i of the tile
+  __device__ static void pv(mf_f32x4 *o, const float *p, const VReg &v) {
+#pragma unroll
+    for (int nt = 0; nt < D / 16; ++nt) {
+      o[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[0], v.v[nt].x, o[nt], 0, 0, 0);
+      o[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[1], v.v[nt].y, o[nt], 0, 0, 0);
+      o[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[2], v.v[nt].z, o[nt], 0, 0, 0);
+      o[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[3], v.v[nt].w, o[nt], 0, 0, 0);
+    }
+  }
+};
+
+// V transposed per tile of 16 keys: vt[head][tile][d][16], zero past the
+// positions.  One workgroup of D threads per (head, tile).
+template <typename T, int D>
+__global__ void __launch_bounds__(D) k_v_tiles(PrefillArgs a) {
+  __shared__ T tile[16][D + 1];
+  const int64_t tiles = (a.positions + 15) / 16;
+  const int64_t head = blockIdx.x / tiles;
+  const int64_t tt = blockIdx.x - head * tiles;
+  const int c = threadIdx.x;
+  const T *vh = static_cast<const T *>(a.V) + head * a.capacity * D;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int64_t key = tt * 16 + k;
+    T v{};
+    if (key < a.positions) v = vh[key * D + c];
+    tile[k][c] = v;
+  }
+  __syncthreads();
+  T *dst = static_cast<T *>(a.vt) + (head * tiles + tt) * D * 16;
+  // thread c writes elements c, c + D, ... of the [d][16] block
+#pragma unroll
+  for (int e = c; e < 16 * D; e += D) dst[e] = tile[e & 15][e >> 4];
+}
+
+// Dynamic LDS of k_prefill_tiles, in bytes: the union's length, the rows'
+// kept lists (HW * 16 * beam ints), the union (up to HW * 16 * beam leaves,
+// each with a 64-bit row mask), then two K tiles (16 rows) and two V tiles
+// ([d][16]), every row padded by 16 bytes against bank conflicts.
+struct TilesLds {
+  size_t lists, uni, k, v, total;
+  int k_stride;  // bytes per K row in LDS
+};
+__host__ __device__ inline TilesLds tiles_lds(int hw, int beam, int head_dim, int elem) {
+  TilesLds t;
+  const size_t rows = static_cast<size_t>(hw) * 16;
+  t.lists = 16;
+  t.uni = (t.lists + rows * beam * 4 + 15) / 16 * 16;
+  t.k = t.uni + rows * beam * 16;
+  t.k_stride = head_dim * elem + 16;
+  t.v = t.k + 2 * 16 * static_cast<size_t>(t.k_stride);
+  t.total = t.v + 2 * static_cast<size_t>(head_dim) * (16 * elem + 16);
+  return t;
+}
+constexpr size_t kTilesMaxLds = 64 * 1024;
+
+struct UnionLeaf {
+  int leaf, pad;
+  unsigned long long rows;  // bit w * 16 + r: wave w's row r kept the leaf
+};
+
+template <typename T, int D, int HW>
+__global__ void __launch_bounds__(HW * 64) k_prefill_tiles(AttendArgs aa, PrefillArgs pa) {
+  extern __shared__ __align__(16) unsigned char ls_tiles[];
+  constexpr int NT = HW * 64;
+  constexpr int ES = static_cast<int>(sizeof(T));
+  constexpr int CPR = D * ES / 16;  // 16-byte chunks per K row
+  constexpr int VS = TileMath<T, D>::VS;
+  const TilesLds lay = tiles_lds(HW, aa.beam, D, ES);
+  int *n_union = reinterpret_cast<int *>(ls_tiles);
+  int *lists = reinterpret_cast<int *>(ls_tiles + lay.lists);
+  UnionLeaf *uni = reinterpret_cast<UnionLeaf *>(ls_tiles + lay.uni);
+  unsigned char *ks = ls_tiles + lay.k;
+  T *vs = reinterpret_cast<T *>(ls_tiles + lay.v);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int r = lane & 15;
+  const int g = lane >> 4;
+  const int P = pa.positions;
+  const int64_t tiles = (P + 15) / 16;
+  // workgroups go to the 8 dies in turn: give each die a contiguous run of
+  // them, so that the tiles of a KV head meet in one die's L2
+  const unsigned bid = (gridDim.x & 7u) == 0u
+                           ? (blockIdx.x & 7u) * (gridDim.x >> 3) + (blockIdx.x >> 3)
+                           : blockIdx.x;
+  const int64_t hgrp = bid / tiles;  // (batch, group of HW query heads)
+  const int t0 = static_cast<int>(bid - hgrp * tiles) * 16;
+  const int per_b = aa.q_heads / HW;
+  const int bi = static_cast<int>(hgrp / per_b);
+  const int hq0 = static_cast<int>(hgrp - static_cast<int64_t>(bi) * per_b) * HW;
+  const int64_t head = static_cast<int64_t>(bi) * aa.kv_heads + hq0 / aa.group;
+  const int L = aa.leaf_block;
+  const int W = aa.beam;
+  const int rows = min(16, P - t0);  // rows of this tile that are positions
+  const int tmax = t0 + rows - 1;
+  // query index of row 0 of wave x: ((bi * Hq + hq0 + x) * P + t0)
+  const int64_t qrow0 = (static_cast<int64_t>(bi) * aa.q_heads + hq0) * P + t0;
+  const T *kh = static_cast<const T *>(aa.K) + head * aa.key_stride * D;
+  const T *vth = static_cast<const T *>(pa.vt) + head * tiles * 16 * D;
+
+  // the rows' kept lists: per head one contiguous block of rows * W
+  for (int x = 0; x < HW; ++x) {
+    const int32_t *src = aa.indices + (qrow0 + static_cast<int64_t>(x) * P) * W;
+    for (int e = tid; e < rows * W; e += NT) lists[x * 16 * W + e] = src[e];
+  }
+  __syncthreads();
+  // wave 0 merges: lane l stands for row l % 16 of wave l / 16
+  if (w == 0) {
+    const int lr = lane & 15, lw = lane >> 4;
+    const bool live = lw < HW && lr < rows;
+    const int *mine = lists + (lw * 16 + lr) * W;
+    int ptr = 0;
+    int nxt = INT_MAX;
+    if (live) nxt = mine[0] >= 0 ? mine[0] : INT_MAX;
+    int U = 0;
+    for (;;) {
+      int j = nxt;
+      j = min(j, __shfl_xor(j, 1));
+      j = min(j, __shfl_xor(j, 2));
+      j = min(j, __shfl_xor(j, 4));
+      j = min(j, __shfl_xor(j, 8));
+      j = min(j, __shfl_xor(j, 16));
+      j = min(j, __shfl_xor(j, 32));
+      if (j == INT_MAX) break;
+      const bool act = nxt == j;
+      const unsigned long long m = __ballot(act);
+      if (lane == 0) {
+        uni[U].leaf = j;
+        uni[U].rows = m;
+      }
+      ++U;
+      if (act) {
+        ++ptr;
+        const int v = ptr < W ? mine[ptr] : -1;
+        nxt = v >= 0 ? v : INT_MAX;
+      }
+    }
+    if (lane == 0) *n_union = U;
+  }
+  __syncthreads();
+  const int U = *n_union;
+
+  TileMath<T, D> tm;
+  const int tr = t0 + r;  // this lane's row position
+  tm.load_q(static_cast<const T *>(aa.Q) + (qrow0 + static_cast<int64_t>(w) * P + r) * D,
+            r < rows, g);
+  float m = -INFINITY, lsum = 0.f;
+  mf_f32x4 o[D / 16];
+#pragma unroll
+  for (int nt = 0; nt < D / 16; ++nt) o[nt] = mf_f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // staging of one key tile: K rows kt .. kt + 15 (clamped to the positions)
+  // and V's [d][16] block; each thread takes chunks tid, tid + NT, ...
+  constexpr int KCH = 16 * CPR;        // 16-byte chunks of a K tile
+  constexpr int VCH = 16 * D * ES / 16;  // and of a V tile
+  constexpr int KPT = (KCH + NT - 1) / NT;
+  constexpr int VPT = (VCH + NT - 1) / NT;
+  uint4 kst[KPT], vst[VPT];
+  const auto fetch = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int c = tid + i * NT;
+      if (c < KCH) {
+        const int row = c / CPR;
+        const int64_t key = min(kt + row, P - 1);
+        kst[i] = *(reinterpret_cast<const uint4 *>(kh + key * D) + (c - row * CPR));
+      }
+    }
+    const uint4 *vsrc = reinterpret_cast<const uint4 *>(vth + static_cast<int64_t>(kt / 16) * 16 * D);
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int c = tid + i * NT;
+      if (c < VCH) vst[i] = vsrc[c];
+    }
+  };
+  const auto stash = [&](int buf) {
+    unsigned char *kb = ks + buf * 16 * lay.k_stride;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int c = tid + i * NT;
+      if (c < KCH) {
+        const int row = c / CPR;
+        *reinterpret_cast<uint4 *>(kb + row * lay.k_stride + (c - row * CPR) * 16) = kst[i];
+      }
+    }
+    // a V row (one dim, 16 keys) is ES chunks
+    T *vb = vs + buf * D * VS;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int c = tid + i * NT;
+      if (c < VCH)
+        *reinterpret_cast<uint4 *>(vb + (c / ES) * VS + (c % ES) * (16 / ES)) = vst[i];
+    }
+  };
+
+  // key tiles in order: leaf uni[u].leaf, tiles 0, 16, ... of it up to the
+  // last row's position
+  int u = 0, kt = 0, buf = 0;
+  if (U > 0) {
+    kt = uni[0].leaf * L;
+    fetch(kt);
+    stash(0);
+  }
+  __syncthreads();
+  while (u < U) {
+    int un = u, ktn = kt + 16;
+    if (ktn - uni[u].leaf * L >= L || ktn > tmax) {
+      un = u + 1;
+      if (un < U) ktn = uni[un].leaf * L;
+    }
+    if (un < U) fetch(ktn);
+    const unsigned wrows = static_cast<unsigned>(uni[u].rows >> (16 * w)) & 0xffffu;
+    if (wrows) {
+      typename TileMath<T, D>::KReg kr;
+      typename TileMath<T, D>::VReg vr;
+      TileMath<T, D>::load_k(kr, reinterpret_cast<const T *>(ks + (buf * 16 + r) * lay.k_stride), g);
+      TileMath<T, D>::load_v(vr, vs + buf * D * VS, r, g);
+      // lane holds S^T[key kt + 4 g + i][row r]
+      const mf_f32x4 sc = tm.scores(kr);
+      const bool act = (wrows >> r) & 1u;
+      const int ahead = tr - kt - 4 * g;  // keys 4 g + i with i <= ahead are not past the row
+      float x[4], mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[i] = act && i <= ahead ? sc[i] * aa.scale_log2 : -INFINITY;
+        mx = fmaxf(mx, x[i]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      // the weights are 2^(x - m) for a reference m that moves only when a
+      // score passes it by more than 8, so they stay at most 2^8 and the
+      // accumulators are rescaled rarely (the normalisation at the end
+      // removes m whatever it is)
+      const bool move = mx > m + 8.f;
+      if (__ballot(move)) {
+        const float mnew = move ? mx : m;
+        const float alpha = move ? __builtin_amdgcn_exp2f(m - mnew) : 1.f;  // 0 from -inf
+        lsum *= alpha;
+        m = mnew;
+        // output rows 4 g + i take the factor of lane 4 g + i (row 4 g + i)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float ai = __shfl(alpha, 4 * g + i);
+#pragma unroll
+          for (int nt = 0; nt < D / 16; ++nt) o[nt][i] *= ai;
+        }
+      }
+      // a row with no key yet has m = -inf and only -inf scores
+      const float mref = m == -INFINITY ? 0.f : m;
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = __builtin_amdgcn_exp2f(x[i] - mref);
+        lsum += p[i];
+      }
+      TileMath<T, D>::pv(o, p, vr);
+    }
+    // every wave is done with the other buffer (the barrier before this
+    // tile), so the next tile goes there
+    if (un < U) stash(buf ^ 1);
+    __syncthreads();
+    u = un;
+    kt = ktn;
+    buf ^= 1;
+  }
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 4 * g + i;
+    const float sc = __shfl(inv, row);
+    if (row < rows) {
+      float *dst = aa.O + (qrow0 + static_cast<int64_t>(w) * P + row) * D + r;
+#pragma unroll
+      for (int nt = 0; nt < D / 16; ++nt) dst[16 * nt] = o[nt][i] * sc;
+    }
+  }
 }
 
 template <typename T, typename S, int D>
@@ -242,14 +641,42 @@ hipError_t launch_prefill_d(const RouteArgs &ra, const AttendArgs &aa, const Pre
   hipLaunchKernelGGL((k_prefix_means<T, S, D>), g1, dim3(D), 0, s, pa);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (pa.tiles) {
+    // routing only, then the attention of 16 positions at a time
+    const int64_t vtiles = (pa.positions + 15) / 16;
+    hipLaunchKernelGGL((k_v_tiles<T, D>), dim3(static_cast<unsigned>(pa.heads * vtiles)), dim3(D),
+                       0, s, pa);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (ra.beam * ra.branching <= 32)
+      hipLaunchKernelGGL((k_prefill<T, S, D, 1, false>), g2, dim3(64), 0, s, ra, aa, pa);
+    else if (ra.beam * ra.branching <= 2 * 32)
+      hipLaunchKernelGGL((k_prefill<T, S, D, 2, false>), g2, dim3(2 * 64), 0, s, ra, aa, pa);
+    else if (ra.beam * ra.branching <= 4 * 32)
+      hipLaunchKernelGGL((k_prefill<T, S, D, 4, false>), g2, dim3(4 * 64), 0, s, ra, aa, pa);
+    else
+      hipLaunchKernelGGL((k_prefill<T, S, D, 8, false>), g2, dim3(8 * 64), 0, s, ra, aa, pa);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t hrows = static_cast<int64_t>(ra.queries) / pa.positions;
+    const unsigned grid = static_cast<unsigned>(hrows / pa.tiles * vtiles);
+    const size_t lds = tiles_lds(pa.tiles, aa.beam, D, sizeof(T)).total;
+    if (pa.tiles == 4)
+      hipLaunchKernelGGL((k_prefill_tiles<T, D, 4>), dim3(grid), dim3(4 * 64), lds, s, aa, pa);
+    else if (pa.tiles == 2)
+      hipLaunchKernelGGL((k_prefill_tiles<T, D, 2>), dim3(grid), dim3(2 * 64), lds, s, aa, pa);
+    else
+      hipLaunchKernelGGL((k_prefill_tiles<T, D, 1>), dim3(grid), dim3(64), lds, s, aa, pa);
+    return hipGetLastError();
+  }
   if (ra.beam * ra.branching <= 32)
-    hipLaunchKernelGGL((k_prefill<T, S, D, 1>), g2, dim3(64), 0, s, ra, aa, pa);
+    hipLaunchKernelGGL((k_prefill<T, S, D, 1, true>), g2, dim3(64), 0, s, ra, aa, pa);
   else if (ra.beam * ra.branching <= 2 * 32)
-    hipLaunchKernelGGL((k_prefill<T, S, D, 2>), g2, dim3(2 * 64), 0, s, ra, aa, pa);
+    hipLaunchKernelGGL((k_prefill<T, S, D, 2, true>), g2, dim3(2 * 64), 0, s, ra, aa, pa);
   else if (ra.beam * ra.branching <= 4 * 32)
-    hipLaunchKernelGGL((k_prefill<T, S, D, 4>), g2, dim3(4 * 64), 0, s, ra, aa, pa);
+    hipLaunchKernelGGL((k_prefill<T, S, D, 4, true>), g2, dim3(4 * 64), 0, s, ra, aa, pa);
   else
-    hipLaunchKernelGGL((k_prefill<T, S, D, 8>), g2, dim3(8 * 64), 0, s, ra, aa, pa);
+    hipLaunchKernelGGL((k_prefill<T, S, D, 8, true>), g2, dim3(8 * 64), 0, s, ra, aa, pa);
   return hipGetLastError();
 }
 
@@ -262,6 +689,13 @@ hipError_t launch_prefill_ts(int head_dim, const RouteArgs &ra, const AttendArgs
 }
 
 }  // namespace
+
+int prefill_tile_heads(int group, int beam, int head_dim, int elem_bytes) {
+  for (int hw = 4; hw >= 1; hw /= 2)
+    if (group % hw == 0 && tiles_lds(hw, beam, head_dim, elem_bytes).total <= kTilesMaxLds)
+      return hw;
+  return 0;
+}
 
 hipError_t launch_prefill(Dt dt, Dt sdt, int head_dim, const RouteArgs &ra, const AttendArgs &aa,
                           const PrefillArgs &pa, hipStream_t s) {

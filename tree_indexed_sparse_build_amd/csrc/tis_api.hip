@@ -820,26 +820,64 @@ tis_status tis_cache_tree_append_decode(const void *Q, const void *K, const void
 
 // -------------------------------------------------------- causal prefill --
 
-size_t tis_causal_prefill_workspace_bytes(int batch, int kv_heads, int head_dim, int branching,
-                                          int leaf_block, int n_keys, tis_dtype summary_dtype) {
-  if (batch < 1 || kv_heads < 1 || (head_dim != 64 && head_dim != 128) || branching < 2 ||
-      branching > tis::kMaxBranching || leaf_block < 1 || n_keys < 1 ||
+namespace {
+// Parts of the causal prefill workspace, byte offsets: the partial means,
+// the fp64 run sums, then (leaf blocks of a multiple of 16 keys) the kept
+// leaves of every position and V transposed per 16 keys.
+struct PrefillLayout {
+  size_t sums, indices, vt, total;
+  bool tiles;
+};
+
+bool prefill_layout(int batch, int kv_heads, int q_heads, int head_dim, int branching,
+                    int leaf_block, int n_keys, int beam, tis_dtype dtype,
+                    tis_dtype summary_dtype, PrefillLayout *out) {
+  if (batch < 1 || kv_heads < 1 || q_heads < 1 || q_heads % kv_heads != 0 ||
+      (head_dim != 64 && head_dim != 128) || branching < 2 || branching > tis::kMaxBranching ||
+      leaf_block < 1 || n_keys < 1 || beam < 1 || (dtype != TIS_F32 && dtype != TIS_BF16) ||
       (summary_dtype != TIS_F32 && summary_dtype != TIS_BF16))
-    return 0;
+    return false;
   const int lv = cache_depth(n_keys, branching, leaf_block);
-  if (lv < 1) return 0;
-  const double bytes = static_cast<double>(batch) * kv_heads * n_keys * lv * head_dim *
-                       summary_elem_bytes(summary_dtype);
-  if (bytes > 9.0e18) return 0;
-  // the partial-means table, then the fp64 key sums over runs of 64, 64^2, ...
-  size_t sums = 0;
+  if (lv < 1) return false;
+  const double heads = static_cast<double>(batch) * kv_heads;
+  const double rough = heads * n_keys * (lv * head_dim * 4.0 + 2.0 * head_dim * 8.0) +
+                       static_cast<double>(batch) * q_heads * n_keys * beam * 4.0 +
+                       heads * (n_keys + 16.0) * head_dim * 4.0;
+  if (rough > 9.0e18) return false;
+  const size_t h = static_cast<size_t>(batch) * kv_heads;
+  size_t runs = 0;
   const int kl = tis::prefix_sum_levels(n_keys);
   int64_t run = tis::kPrefixRows;
   for (int k = 0; k < kl; ++k, run *= tis::kPrefixRows)
-    sums += static_cast<size_t>((n_keys + run - 1) / run);
-  return static_cast<size_t>(batch) * kv_heads * static_cast<size_t>(n_keys) * lv * head_dim *
-             summary_elem_bytes(summary_dtype) +
-         static_cast<size_t>(batch) * kv_heads * sums * head_dim * sizeof(double);
+    runs += static_cast<size_t>((n_keys + run - 1) / run);
+  PrefillLayout p{};
+  p.sums = h * static_cast<size_t>(n_keys) * lv * head_dim * summary_elem_bytes(summary_dtype);
+  p.total = p.sums + h * runs * head_dim * sizeof(double);
+  // (16-key leaves: a workgroup would take one key tile per union entry,
+  // and the fused kernel is faster there)
+  p.tiles = leaf_block % 16 == 0 && leaf_block >= 32 &&
+            tis::prefill_tile_heads(q_heads / kv_heads, beam, head_dim,
+                                    dtype == TIS_BF16 ? 2 : 4) > 0;
+  if (p.tiles) {
+    p.indices = tis::align_up(p.total, 256);
+    p.vt = tis::align_up(p.indices + static_cast<size_t>(batch) * q_heads * n_keys * beam *
+                                         sizeof(int32_t), 256);
+    p.total = p.vt + h * static_cast<size_t>((n_keys + 15) / 16) * 16 * head_dim *
+                         (dtype == TIS_BF16 ? 2 : 4);
+  }
+  *out = p;
+  return true;
+}
+}  // namespace
+
+size_t tis_causal_prefill_workspace_bytes(int batch, int kv_heads, int q_heads, int head_dim,
+                                          int branching, int leaf_block, int n_keys, int beam,
+                                          tis_dtype dtype, tis_dtype summary_dtype) {
+  PrefillLayout p;
+  if (!prefill_layout(batch, kv_heads, q_heads, head_dim, branching, leaf_block, n_keys, beam,
+                      dtype, summary_dtype, &p))
+    return 0;
+  return p.total;
 }
 
 tis_status tis_causal_prefill(const void *Q, const void *K, const void *V, tis_dtype dtype,
@@ -860,9 +898,12 @@ tis_status tis_causal_prefill(const void *Q, const void *K, const void *V, tis_d
   if (pq > 0x7fffffffLL)
     return fail(TIS_E_UNSUPPORTED, "tis_causal_prefill: %lld queries (batch * q_heads * n_keys) "
                 "exceed 2^31 - 1", (long long)pq);
-  const size_t need = tis_causal_prefill_workspace_bytes(
-      tree->batch, tree->kv_heads, tree->head_dim, tree->branching, tree->leaf_block,
-      tree->n_keys, static_cast<tis_dtype>(tree->summary_dtype));
+  PrefillLayout lay;
+  if (!prefill_layout(tree->batch, tree->kv_heads, q_heads, tree->head_dim, tree->branching,
+                      tree->leaf_block, tree->n_keys, beam, dtype,
+                      static_cast<tis_dtype>(tree->summary_dtype), &lay))
+    return fail(TIS_E_SHAPE, "tis_causal_prefill: invalid geometry");
+  const size_t need = lay.total;
   if (workspace_bytes < need)
     return fail(TIS_E_WORKSPACE, "tis_causal_prefill: workspace of %zu bytes required, %zu given",
                 need, workspace_bytes);
@@ -880,10 +921,7 @@ tis_status tis_causal_prefill(const void *Q, const void *K, const void *V, tis_d
   pa.positions = tree->n_keys;
   pa.levels = tree->levels;
   {
-    const size_t table = static_cast<size_t>(g.heads) * tree->n_keys * tree->levels *
-                         tree->head_dim * summary_elem_bytes(
-                             static_cast<tis_dtype>(tree->summary_dtype));
-    pa.sums = reinterpret_cast<double *>(static_cast<char *>(workspace) + table);
+    pa.sums = reinterpret_cast<double *>(static_cast<char *>(workspace) + lay.sums);
     pa.sum_levels = tis::prefix_sum_levels(tree->n_keys);
     int64_t run = tis::kPrefixRows, off = 0;
     for (int k = 0; k < pa.sum_levels; ++k, run *= tis::kPrefixRows) {
@@ -922,6 +960,19 @@ tis_status tis_causal_prefill(const void *Q, const void *K, const void *V, tis_d
   aa.beam = beam;
   aa.n_blocks = (static_cast<int64_t>(tree->n_keys) + tree->leaf_block - 1) / tree->leaf_block;
   aa.scale_log2 = static_cast<float>(sc * 1.4426950408889634);
+  if (lay.tiles) {
+    // routing writes the kept leaves (to the caller's indices, else the
+    // workspace); the attention reads them back 16 positions at a time
+    int32_t *kept = indices ? indices
+                            : reinterpret_cast<int32_t *>(static_cast<char *>(workspace) +
+                                                          lay.indices);
+    ra.indices = kept;
+    aa.indices = kept;
+    pa.tiles = tis::prefill_tile_heads(q_heads / tree->kv_heads, beam, tree->head_dim,
+                                       dtype == TIS_BF16 ? 2 : 4);
+    pa.V = V;
+    pa.vt = static_cast<char *>(workspace) + lay.vt;
+  }
   return hip_status(tis::launch_prefill(to_dt(dtype), to_dt(tree->summary_dtype), tree->head_dim,
                                         ra, aa, pa, static_cast<hipStream_t>(stream)),
                     "tis_causal_prefill launch");

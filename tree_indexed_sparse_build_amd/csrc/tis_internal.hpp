@@ -258,10 +258,21 @@ struct PrefillArgs {
   int sum_levels;
   int64_t sum_n[kMaxSumLevels];
   int64_t sum_off[kMaxSumLevels];
+  // attention 16 positions at a time (leaf blocks of a multiple of 16 keys),
+  // `tiles` query heads a workgroup (0: one fused kernel per position): the
+  // routing pass writes every position's kept leaves to the attention's
+  // indices, V is copied transposed per 16 keys to vt ([heads][ceil(positions
+  // / 16)][d][16], the key type)
+  int tiles;
+  const void *V;
+  void *vt;
 };
 
 hipError_t launch_prefill(Dt dt, Dt sdt, int head_dim, const RouteArgs &ra, const AttendArgs &aa,
                           const PrefillArgs &pa, hipStream_t s);
+// Query heads per workgroup of the 16-position attention (4, 2 or 1,
+// dividing the group, within the LDS it may take), 0 if none fits.
+int prefill_tile_heads(int group, int beam, int head_dim, int elem_bytes);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

@@ -518,8 +518,9 @@ class CacheTree:
                if return_indices else None)
         c = self.c
         L = lib()
-        wsb = L.tis_causal_prefill_workspace_bytes(c.batch, c.kv_heads, c.head_dim, c.branching,
-                                                   c.leaf_block, c.n_keys, c.summary_dtype)
+        wsb = L.tis_causal_prefill_workspace_bytes(c.batch, c.kv_heads, Hq, c.head_dim,
+                                                   c.branching, c.leaf_block, c.n_keys, beam,
+                                                   self.dt, c.summary_dtype)
         ws = _workspace(Q.device, "prefill", wsb)
         check(L.tis_causal_prefill(Q.data_ptr(), self.K.data_ptr(), self.V.data_ptr(), self.dt,
                                    Hq, ctypes.byref(c), beam,
