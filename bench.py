@@ -388,6 +388,8 @@ def main(argv=None):
                     help="skip the measurement of the step with bfloat16 and fp8 summaries")
     ap.add_argument("--no-threshold", action="store_true",
                     help="skip the bounding-sphere threshold retrieval measurement")
+    ap.add_argument("--prefill-positions", type=int, default=4096,
+                    help="positions of the causal prefill measurement (at most the workload's keys)")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the causal prefill measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -546,7 +548,8 @@ def main(argv=None):
 
     pre = None
     if not args.no_prefill:
-        pre = causal_prefill_bench(tis, torch, w, Q, K, V, K_, args.warmup)
+        pre = causal_prefill_bench(tis, torch, w, Q, K, V, K_, args.warmup,
+                                   max_positions=args.prefill_positions)
         log(f"causal prefill of the first {pre['positions']} keys ({pre['queries']} queries): "
             f"{pre['us']:.1f} us -> {pre['queries_per_s']:.3e} queries/s; keys read per query "
             f"{pre['keys_read_mean']:.2f} on average (dense causal "
