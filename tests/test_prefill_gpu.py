@@ -89,6 +89,9 @@ CASES = [
     ("tiles_L32_bf16_g1", "bf16", "bf16", 2, 3, 1, 129, 64, 4, 32, 3, "normal"),
     # a beam whose union table does not fit 4 heads' LDS: 2 heads a workgroup
     ("tiles_L32_beam_48_g4", "bf16", "f32", 1, 1, 4, 200, 64, 2, 32, 48, "normal"),
+    # fewer positions than a tile: one workgroup row block, 7 rows
+    ("tiles_7_positions", "f32", "f32", 1, 2, 4, 7, 128, 2, 32, 2, "normal"),
+    ("tiles_1_position", "bf16", "f32", 1, 1, 2, 1, 64, 2, 32, 1, "normal"),
 ]
 
 
@@ -178,6 +181,12 @@ LONG = [
     # past 64^3 keys: runs of 262,144 keys too
     ("runs_262144", "bf16", 4, 16, 64, 2, 270_000, 4,
      [0, 4095, 4096, 65535, 65536, 131071, 200_000, 262_143, 262_144, 262_207, 262_208, 269_999]),
+    # the 16-position attention over a long prefill (leaves of 32 keys, 4
+    # heads a workgroup): unions of many leaves per tile, the last tile
+    # partial
+    ("tiles_20000", "bf16", 4, 32, 64, 4, 20_000, 6,
+     [0, 15, 16, 31, 32, 1000, 4095, 4096, 8191, 8192, 12_345, 16_383, 16_384, 19_983, 19_984,
+      19_999]),
 ]
 
 
