@@ -19,14 +19,17 @@
 //    63 sums a level), then walks the block in key order.
 //  * k_prefill: one workgroup per (batch, query head, position), of one
 //    wave when a level has at most 32 candidates (beam * b), 2 waves up to
-//    64, 4 up to 128, else 8: a prefill query reads few keys, so small workgroups (LDS
-//    sized to them) keep more positions in flight on each CU (measured: 8
-//    waves 1.5-1.8x the rate of 16).  Wave 0
-//    builds the position's level table (depth, existing nodes, first cut, the
-//    open rows' offsets) in LDS, a lane per level; the walk reads complete
-//    nodes from the
-//    cache tree and the open node of each level from the table of partial
-//    means; the attention stops at key t.
+//    64, 4 up to 128, else 8: a prefill query reads few keys, so small
+//    workgroups (LDS sized to them) keep more positions in flight on each CU
+//    (measured: 8 waves 1.5-1.8x the rate of 16).  Wave 0 builds the
+//    position's level table (depth, existing nodes, first cut, the open
+//    rows' offsets) in LDS, a lane per level; the walk reads complete nodes
+//    from the cache tree and the open node of each level from the table of
+//    partial means.  With leaf blocks of 16 keys or a size that is not a
+//    multiple of 16, the same workgroup then attends, stopping at key t;
+//    otherwise it only writes the kept leaves, and
+//  * k_v_tiles + k_prefill_tiles attend 16 positions of up to 4 query heads
+//    at a time on the matrix cores (described below).
 #include "attend_query.hpp"
 #include "route_walk.hpp"
 
