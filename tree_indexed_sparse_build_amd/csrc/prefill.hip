@@ -271,7 +271,9 @@ template <int D> struct TileMath<bf16_bits, D> {
   mf_bf16x8 q[D / 32];
   struct KReg { uint4 v[D / 32]; };
   struct VReg { uint2 v[D / 16]; };
-  static constexpr int VS = 24;  // elements per V row in LDS: 16 keys, padded by 16 bytes
+  // elements per V row in LDS: 16 keys and 4 more, so that 16 lanes reading
+  // 8 bytes each at rows r = 0..15 start on distinct bank pairs
+  static constexpr int VS = 20;
   __device__ void load_q(const bf16_bits *qrow, bool valid, int g) {
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
@@ -316,7 +318,9 @@ template <int D> struct TileMath<float, D> {
   float4 q[D / 16];
   struct KReg { float4 v[D / 16]; };
   struct VReg { float4 v[D / 16]; };
-  static constexpr int VS = 20;  // elements per V row in LDS: 16 keys, padded by 16 bytes
+  // elements per V row in LDS: 16 keys and 4 more, so that 8 lanes reading
+  // 16 bytes each at rows r = 0..7 start on distinct groups of 4 banks
+  static constexpr int VS = 20;
   __device__ void load_q(const float *qrow, bool valid, int g) {
 #pragma unroll
     for (int s = 0; s < D / 16; ++s)
@@ -382,7 +386,8 @@ __global__ void __launch_bounds__(D) k_v_tiles(PrefillArgs a) {
 // Dynamic LDS of k_prefill_tiles, in bytes: the union's length, the rows'
 // kept lists (HW * 16 * beam ints), the union (up to HW * 16 * beam leaves,
 // each with a 64-bit row mask), then two K tiles (16 rows) and two V tiles
-// ([d][16]), every row padded by 16 bytes against bank conflicts.
+// ([d][16]), rows padded against bank conflicts (K by 16 bytes, V by 4
+// elements).
 struct TilesLds {
   size_t lists, uni, k, v, total;
   int k_stride;  // bytes per K row in LDS
@@ -395,7 +400,7 @@ __host__ __device__ inline TilesLds tiles_lds(int hw, int beam, int head_dim, in
   t.k = t.uni + rows * beam * 16;
   t.k_stride = head_dim * elem + 16;
   t.v = t.k + 2 * 16 * static_cast<size_t>(t.k_stride);
-  t.total = t.v + 2 * static_cast<size_t>(head_dim) * (16 * elem + 16);
+  t.total = t.v + 2 * static_cast<size_t>(head_dim) * 20 * elem;
   return t;
 }
 constexpr size_t kTilesMaxLds = 64 * 1024;
@@ -498,7 +503,10 @@ __global__ void __launch_bounds__(HW * 64) k_prefill_tiles(AttendArgs aa, Prefil
   for (int nt = 0; nt < D / 16; ++nt) o[nt] = mf_f32x4{0.f, 0.f, 0.f, 0.f};
 
   // staging of one key tile: K rows kt .. kt + 15 (clamped to the positions)
-  // and V's [d][16] block; each thread takes chunks tid, tid + NT, ...
+  // and V's [d][16] block; each thread takes chunks tid, tid + NT, ...  The
+  // next tile is in flight in registers while this one computes.  (Tiles
+  // further ahead were slower: the compiler then waits for every load in
+  // flight before the staging stores into LDS.)
   constexpr int KCH = 16 * CPR;        // 16-byte chunks of a K tile
   constexpr int VCH = 16 * D * ES / 16;  // and of a V tile
   constexpr int KPT = (KCH + NT - 1) / NT;
@@ -531,13 +539,21 @@ __global__ void __launch_bounds__(HW * 64) k_prefill_tiles(AttendArgs aa, Prefil
         *reinterpret_cast<uint4 *>(kb + row * lay.k_stride + (c - row * CPR) * 16) = kst[i];
       }
     }
-    // a V row (one dim, 16 keys) is ES chunks
+    // a V row (one dim, 16 keys) is ES chunks; bf16 rows are 40 bytes
+    // apart, so their chunks go as two 8-byte halves
     T *vb = vs + buf * D * VS;
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       const int c = tid + i * NT;
-      if (c < VCH)
-        *reinterpret_cast<uint4 *>(vb + (c / ES) * VS + (c % ES) * (16 / ES)) = vst[i];
+      if (c < VCH) {
+        T *dst = vb + (c / ES) * VS + (c % ES) * (16 / ES);
+        if constexpr ((VS * ES) % 16 == 0) {
+          *reinterpret_cast<uint4 *>(dst) = vst[i];
+        } else {
+          reinterpret_cast<uint2 *>(dst)[0] = make_uint2(vst[i].x, vst[i].y);
+          reinterpret_cast<uint2 *>(dst)[1] = make_uint2(vst[i].z, vst[i].w);
+        }
+      }
     }
   };
 
