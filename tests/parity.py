@@ -5,7 +5,8 @@
   kernel sums in fp64 in another order, so a different rounding needs a
   near-tie of the mean);
 * leaf indices: bit-exact, except on queries whose oracle cut gap at some
-  level is below 1e-5 relative, which are counted and reported instead;
+  level is below 1e-5 relative, which are counted and reported instead; their
+  number is bounded (excused_bound: 0 on full-size cases, 0.1% elsewhere);
 * attention outputs: max-abs error within the tolerance for the input type
   (1e-4 for fp32 inputs, 2e-2 for bf16 inputs with fp32 accumulation).
 """
@@ -51,9 +52,24 @@ def compare_summaries(gpu_levels, oracle_stored, max_ulp: int = 1, summary_dtype
     return equal, total, worst
 
 
-def compare_indices(gpu_idx: np.ndarray, oracle_route: dict):
+def excused_bound(n: int) -> int:
+    """Most tie-exposed mismatches a parity case over n queries (or
+    positions) may excuse: 0.1% of them, so 0 below 1,000.  The kernels
+    score in fp64 like the oracle, so a mismatch needs two scores within
+    about 1e-15 of each other; the full-size cases pass 0 explicitly."""
+    return n // 1000
+
+
+def check_excused(excused: int, n: int, max_excused=None, what: str = "queries") -> None:
+    bound = excused_bound(n) if max_excused is None else max_excused
+    assert excused <= bound, (f"{excused} tie-exposed mismatches among {n} {what}, more than "
+                              f"the {bound} a case may excuse")
+
+
+def compare_indices(gpu_idx: np.ndarray, oracle_route: dict, max_excused=None):
     """Returns (exact, tie_exposed_mismatch, n_queries).  Fails on any mismatch
-    of a query whose every cut gap is >= TIE_GAP."""
+    of a query whose every cut gap is >= TIE_GAP, and when the tie-exposed
+    mismatches exceed max_excused (default: excused_bound(n_queries))."""
     want = oracle_route["indices"]
     assert gpu_idx.shape == want.shape, (gpu_idx.shape, want.shape)
     mismatch = np.any(gpu_idx != want, axis=-1)
@@ -66,7 +82,9 @@ def compare_indices(gpu_idx: np.ndarray, oracle_route: dict):
                              f"with no near-tie, e.g. {where}: gpu {gpu_idx[q].tolist()} "
                              f"oracle {want[q].tolist()} gaps {oracle_route['gap'][q].tolist()}")
     n = int(np.prod(mismatch.shape))
-    return n - int(mismatch.sum()), int((mismatch & tie).sum()), n
+    excused = int((mismatch & tie).sum())
+    check_excused(excused, n, max_excused)
+    return n - int(mismatch.sum()), excused, n
 
 
 def compare_trace(gpu_trace: np.ndarray, oracle_route: dict) -> None:

@@ -60,7 +60,7 @@ def run_gpu(t, w, x, oracle_idx=None, summary_dtype="f32"):
     return res
 
 
-def check_case(t, w, x=None, label="", summary_dtype="f32"):
+def check_case(t, w, x=None, label="", summary_dtype="f32", max_excused=None):
     t0 = time.time()
     if x is None:
         x = workloads.generate(w)
@@ -75,7 +75,7 @@ def check_case(t, w, x=None, label="", summary_dtype="f32"):
     g = run_gpu(t, w, x, oracle_idx=orr["indices"], summary_dtype=summary_dtype)
     eq, tot, worst = parity.compare_summaries(g["levels"], ob["stored"],
                                               summary_dtype=summary_dtype)
-    exact, tie, nq = parity.compare_indices(g["idx"], orr)
+    exact, tie, nq = parity.compare_indices(g["idx"], orr, max_excused=max_excused)
     parity.compare_trace(g["trace"], orr)
     o_or = O.tree_attend(x["Q"], x["K"], x["V"], w.dtype, orr["indices"], w.leaf_block)
     err1 = parity.compare_outputs(g["out_oracle_idx"], o_or, w.dtype)
@@ -287,7 +287,8 @@ FULL = ["alhr_1k", "gqa_32k", "gqa_256k", "deep_planted", "long_1m"]
 @pytest.mark.parametrize("name", FULL)
 def test_full_size_workload(tis, name):
     w = workloads.get(name)
-    x, ob, orr, g = check_case(tis, w, label=f"{name} (full size)")
+    # full size: no mismatch may be excused
+    x, ob, orr, g = check_case(tis, w, label=f"{name} (full size)", max_excused=0)
     if w.generator == "planted":
         hit = np.array([[x["planted"][bb, h] in g["idx"][bb, h] for h in range(w.q_heads)]
                         for bb in range(w.batch)])

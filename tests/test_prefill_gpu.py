@@ -117,6 +117,7 @@ def test_causal_prefill_matches_oracle(tis, case):
     tie = orc["gap"] < parity.TIE_GAP
     same = np.all(idx == orc["indices"], axis=-1)
     assert np.all(same | tie), f"{np.count_nonzero(~same & ~tie)} positions keep other leaves"
+    parity.check_excused(int((~same & tie).sum()), same.size, what="positions")
     # outputs: the oracle's attention over the GPU's leaves, position by position
     err = 0.0
     Bq, Hq = Q.shape[:2]
@@ -161,6 +162,7 @@ def test_prefill_gqa_4096_positions_sampled(tis):
     tie = orc["gap"] < parity.TIE_GAP
     same = np.all(idx[:, :, pos] == orc["indices"], axis=-1)
     assert np.all(same | tie), f"{np.count_nonzero(~same & ~tie)} sampled positions differ"
+    parity.check_excused(int((~same & tie).sum()), same.size, what="positions")
     err = 0.0
     for i, t in enumerate(pos):
         o_g = GO.grow_attend(np.ascontiguousarray(Q[:, :, t]), K, V, w.dtype, idx[:, :, t],
@@ -217,6 +219,7 @@ def test_prefill_long_sampled(tis, case):
     tie = orc["gap"] < parity.TIE_GAP
     same = np.all(idx == orc["indices"], axis=-1)
     assert np.all(same | tie), f"{np.count_nonzero(~same & ~tie)} sampled positions differ"
+    parity.check_excused(int((~same & tie).sum()), same.size, what="positions")
     err = 0.0
     for i, t in enumerate(pos):
         o_g = GO.grow_attend(np.ascontiguousarray(Q[:, :, t]), K, V, dtype, idx[:, :, i],

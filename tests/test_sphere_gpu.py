@@ -94,8 +94,11 @@ def check_case(tis, w, k_ranks, sd="f32", max_nodes=None, label=None):
         safe = orr["margin"] > MARGIN
         same = np.all(idx == orr["indices"], axis=-1) & (cnt == orr["counts"])
         assert np.all(same[safe]), f"{np.count_nonzero(~same & safe)} queries differ"
+        parity.check_excused(int((~same & ~safe).sum()), same.size)
         oa = S.threshold_attend(x["Q"], x["K"], x["V"], w.dtype, idx, cnt, w.leaf_block, tau)
         ok = safe & (oa["margin"] > MARGIN)
+        # queries left out of the output check: near-tie routes or key scores
+        parity.check_excused(int((~ok & (cnt >= 0)).sum()), ok.size)
         err = parity.compare_outputs(out[ok], oa["out"][ok], w.dtype) if ok.any() else 0.0
         over = cnt < 0
         assert np.all(np.isnan(out[over]))
