@@ -205,6 +205,32 @@ tis_status tis_tree_decode(const void *Q, const void *K, const void *V, tis_dtyp
 size_t tis_decode_workspace_bytes(int batch, int q_heads, int head_dim, int beam,
                                   int leaf_block);
 
+/* Size of the scratch that tis_tree_decode_noalloc keeps on each GPU. */
+#define TIS_NOALLOC_SCRATCH_BYTES (1u << 20)
+
+/*
+ * tis_tree_decode_noalloc -- tis_tree_decode for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, checks, kernels and
+ * results as tis_tree_decode (bit for bit), without the workspace: the split
+ * partial states go to a scratch array of TIS_NOALLOC_SCRATCH_BYTES that the
+ * library holds on every GPU it runs on, from its first call there until the
+ * process ends.  The call allocates and frees nothing.  The caller still
+ * supplies Q, K, V, the tree, O and (optionally) indices.
+ *
+ * A geometry whose workspace (tis_decode_workspace_bytes) exceeds
+ * TIS_NOALLOC_SCRATCH_BYTES is rejected with TIS_E_WORKSPACE before anything
+ * is enqueued.  All calls on one GPU share its scratch, whatever their
+ * stream: calls that may overlap on one GPU race and give undefined
+ * results, so order them (one stream, or synchronise between them).  The
+ * scratch holds what the last call left; no call depends on its contents.
+ * The first call on a device looks up the scratch's address there (no
+ * allocation); a failure of that lookup returns TIS_E_HIP.
+ */
+tis_status tis_tree_decode_noalloc(const void *Q, const void *K, const void *V, tis_dtype dtype,
+                                   int q_heads, const tis_tree *tree, int beam, float scale,
+                                   float *O, int32_t *indices, void *stream);
+
 /* ------------------------------------------------------------------------
  * Threshold retrieval with bounding spheres
  *

@@ -229,6 +229,46 @@ def test_decode_rejects(lib, kw, status):
     assert lib.tis_last_error().decode()
 
 
+def _decode_noalloc(lib, Q=FAKE, K=FAKE, V=FAKE, dt=_lib.TIS_BF16, Hq=2, tree=None, beam=2,
+                    scale=0.0, O=FAKE, idx=None):
+    t = tree if tree is not None else _tree(H=1)
+    return lib.tis_tree_decode_noalloc(Q, K, V, dt, Hq, ctypes.byref(t), beam, scale, O, idx,
+                                       None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=None), _lib.TIS_E_NULL),
+    (dict(O=None), _lib.TIS_E_NULL),
+    (dict(tree=_tree(summ=None)), _lib.TIS_E_NULL),
+    (dict(dt=9), _lib.TIS_E_DTYPE),
+    (dict(tree=_tree(H=2), Hq=3), _lib.TIS_E_SHAPE),
+    (dict(beam=0), _lib.TIS_E_SHAPE),
+    (dict(beam=9), _lib.TIS_E_SHAPE),
+    (dict(tree=_tree(b=64, lv=2, L=1), beam=5), _lib.TIS_E_UNSUPPORTED),
+    (dict(scale=float("inf")), _lib.TIS_E_SHAPE),
+    (dict(tree=_tree(sd=5)), _lib.TIS_E_DTYPE),
+    (dict(Q=FAKE + 4), _lib.TIS_E_ALIGN),
+    (dict(idx=FAKE + 2), _lib.TIS_E_ALIGN),
+])
+def test_decode_noalloc_rejects(lib, kw, status):
+    """The same host checks as tis_tree_decode, before anything is looked up
+    or enqueued."""
+    assert _decode_noalloc(lib, **kw) == status
+    assert lib.tis_last_error().decode()
+
+
+def test_noalloc_scratch_covers_every_split_geometry(lib):
+    """The split rule gives a query at most 256 / queries parts and splits
+    only below 128 queries, so the largest workspace any geometry asks for
+    fits the library's scratch (no valid decode is turned away)."""
+    worst = 0
+    for queries in range(1, 129):
+        for beam in (16, 64, 256):
+            for d in (64, 128):
+                worst = max(worst, lib.tis_decode_workspace_bytes(1, queries, d, beam, 4096))
+    assert 0 < worst <= _lib.TIS_NOALLOC_SCRATCH_BYTES
+
+
 # ------------------------------------------------------- growing cache --
 
 def test_cache_tree_bytes(lib):

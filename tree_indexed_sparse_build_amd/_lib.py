@@ -24,6 +24,7 @@ STATUS_NAMES = {
 }
 
 TIS_MAX_SURVIVORS = 2048
+TIS_NOALLOC_SCRATCH_BYTES = 1 << 20
 
 
 class TisTree(ctypes.Structure):
@@ -66,6 +67,8 @@ SIGNATURES = {
     "tis_tree_decode": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, ctypes.POINTER(TisTree), _c_int,
                                  _c_float, _vp, _vp, _vp, _c_size, _vp]),
     "tis_decode_workspace_bytes": (_c_size, [_c_int] * 5),
+    "tis_tree_decode_noalloc": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, ctypes.POINTER(TisTree),
+                                         _c_int, _c_float, _vp, _vp, _vp]),
     "tis_cache_tree_summary_bytes": (_c_size, [_c_int] * 6),
     "tis_cache_tree_summary_bytes_as": (_c_size, [_c_int] * 7),
     "tis_cache_tree_state_bytes": (_c_size, [_c_int] * 6),

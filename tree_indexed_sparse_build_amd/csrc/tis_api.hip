@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "tis.h"
 #include "tis_internal.hpp"
 
@@ -376,36 +378,75 @@ tis_status tis_tree_attend(const void *Q, const void *K, const void *V, tis_dtyp
                     "tis_tree_attend launch");
 }
 
-tis_status tis_tree_decode(const void *Q, const void *K, const void *V, tis_dtype dtype,
-                           int q_heads, const tis_tree *tree, int beam, float scale, float *O,
-                           int32_t *indices, void *workspace, size_t workspace_bytes,
-                           void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Scratch of tis_tree_decode_noalloc: the split queries' partial softmax
+// states, which tis_tree_decode keeps in the caller's workspace.  Every GPU
+// the library runs on holds its own copy (part of the code object loaded
+// there) until the process ends.  Host code never passes the array's name to
+// a kernel: on the host it only stands for the symbol, and the device
+// address comes from hipGetSymbolAddress, looked up once per device.
+static __device__ __align__(256) unsigned char scratch[TIS_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 256;
+std::mutex g_scratch_mu;
+void *g_scratch_addr[kMaxScratchDevices];
+
+// Device address of `scratch` on the current device.
+tis_status scratch_address(const char *who, void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, who);
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(TIS_E_UNSUPPORTED, "%s: device %d is past the %d the library serves", who, dev,
+                kMaxScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, who);
+    if (!p || !aligned(p, 256))
+      return fail(TIS_E_HIP, "%s: no usable address for the library's scratch", who);
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return TIS_OK;
+}
+
+// tis_tree_decode, with the split partial states in the caller's workspace
+// or (noalloc) in the library's per-device scratch.
+tis_status decode_full_tree(const char *who, const void *Q, const void *K, const void *V,
+                            tis_dtype dtype, int q_heads, const tis_tree *tree, int beam,
+                            float scale, float *O, int32_t *indices, void *workspace,
+                            size_t workspace_bytes, bool noalloc, void *stream) {
   if (!Q || !K || !V || !tree || !tree->summaries || !O)
-    return fail(TIS_E_NULL, "tis_tree_decode: Q, K, V, tree, tree->summaries and O are required");
+    return fail(TIS_E_NULL, "%s: Q, K, V, tree, tree->summaries and O are required", who);
   tis_status st = check_dtype(dtype);
   if (st != TIS_OK) return st;
-  st = check_summary_dtype("tis_tree_decode", tree->summary_dtype);
+  st = check_summary_dtype(who, tree->summary_dtype);
   if (st != TIS_OK) return st;
   Geometry g;
   st = check_tree(tree->batch, tree->kv_heads, tree->n_keys, tree->head_dim, tree->branching,
                   tree->leaf_block, tree->levels, &g);
   if (st != TIS_OK) return st;
   if (q_heads < 1 || q_heads % tree->kv_heads != 0)
-    return fail(TIS_E_SHAPE, "tis_tree_decode: q_heads %d is not a positive multiple of kv_heads %d",
-                q_heads, tree->kv_heads);
+    return fail(TIS_E_SHAPE, "%s: q_heads %d is not a positive multiple of kv_heads %d",
+                who, q_heads, tree->kv_heads);
   const int64_t leaves = g.n_at[tree->levels];
   if (beam < 1 || beam > leaves)
-    return fail(TIS_E_SHAPE, "tis_tree_decode: beam %d outside [1, %lld]", beam, (long long)leaves);
+    return fail(TIS_E_SHAPE, "%s: beam %d outside [1, %lld]", who, beam, (long long)leaves);
   if (static_cast<int64_t>(beam) * tree->branching > TIS_MAX_CANDIDATES)
-    return fail(TIS_E_UNSUPPORTED, "tis_tree_decode: beam * branching = %lld > %d",
+    return fail(TIS_E_UNSUPPORTED, "%s: beam * branching = %lld > %d", who,
                 (long long)beam * tree->branching, TIS_MAX_CANDIDATES);
   if (!(scale == scale) || isinf(scale))
-    return fail(TIS_E_SHAPE, "tis_tree_decode: scale must be finite");
+    return fail(TIS_E_SHAPE, "%s: scale must be finite", who);
   if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) ||
       !aligned(tree->summaries, 16) || (indices && !aligned(indices, 4)))
-    return fail(TIS_E_ALIGN, "tis_tree_decode: Q, K, V, O and summaries need 16-byte alignment");
+    return fail(TIS_E_ALIGN, "%s: Q, K, V, O and summaries need 16-byte alignment", who);
   const int64_t queries = static_cast<int64_t>(tree->batch) * q_heads;
-  if (queries > 0x7fffffffLL) return fail(TIS_E_UNSUPPORTED, "tis_tree_decode: too many queries");
+  if (queries > 0x7fffffffLL) return fail(TIS_E_UNSUPPORTED, "%s: too many queries", who);
 
   const tis::RouteArgs ra = route_args(Q, tree, g, q_heads, beam, indices, nullptr, queries);
   const double sc =
@@ -426,13 +467,48 @@ tis_status tis_tree_decode(const void *Q, const void *K, const void *V, tis_dtyp
   aa.beam = beam;
   aa.n_blocks = tree->n_keys / tree->leaf_block;
   aa.scale_log2 = static_cast<float>(sc * 1.4426950408889634);
-  st = plan_split("tis_tree_decode", queries, tree->head_dim, beam, tree->leaf_block, workspace,
+  if (noalloc) {
+    const size_t need = tis::attend_workspace(
+        queries, tree->head_dim, tis::attend_splits(queries, beam, tree->leaf_block));
+    if (need > TIS_NOALLOC_SCRATCH_BYTES)
+      return fail(TIS_E_WORKSPACE,
+                  "%s: this geometry needs %zu bytes of scratch, more than the %zu the library "
+                  "holds; use tis_tree_decode with a workspace",
+                  who, need, static_cast<size_t>(TIS_NOALLOC_SCRATCH_BYTES));
+    workspace = nullptr;
+    workspace_bytes = 0;
+    if (need > 0) {
+      st = scratch_address(who, &workspace);
+      if (st != TIS_OK) return st;
+      workspace_bytes = TIS_NOALLOC_SCRATCH_BYTES;
+    }
+  }
+  st = plan_split(who, queries, tree->head_dim, beam, tree->leaf_block, workspace,
                   workspace_bytes, &aa);
   if (st != TIS_OK) return st;
   const tis::Dt dt = dtype == TIS_BF16 ? tis::Dt::BF16 : tis::Dt::F32;
   return hip_status(tis::launch_decode(dt, to_dt(tree->summary_dtype), tree->head_dim, ra, aa,
                                       static_cast<hipStream_t>(stream)),
-                    "tis_tree_decode launch");
+                    who);
+}
+
+}  // namespace
+
+extern "C" {
+
+tis_status tis_tree_decode(const void *Q, const void *K, const void *V, tis_dtype dtype,
+                           int q_heads, const tis_tree *tree, int beam, float scale, float *O,
+                           int32_t *indices, void *workspace, size_t workspace_bytes,
+                           void *stream) {
+  return decode_full_tree("tis_tree_decode", Q, K, V, dtype, q_heads, tree, beam, scale, O,
+                          indices, workspace, workspace_bytes, false, stream);
+}
+
+tis_status tis_tree_decode_noalloc(const void *Q, const void *K, const void *V, tis_dtype dtype,
+                                   int q_heads, const tis_tree *tree, int beam, float scale,
+                                   float *O, int32_t *indices, void *stream) {
+  return decode_full_tree("tis_tree_decode_noalloc", Q, K, V, dtype, q_heads, tree, beam, scale,
+                          O, indices, nullptr, 0, true, stream);
 }
 
 // ------------------------------------------------------- growing cache --

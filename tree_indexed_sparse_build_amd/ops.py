@@ -18,7 +18,8 @@ from ._lib import TisCacheTree, TisTree, check, lib
 _DTYPES = {torch.float32: _lib.TIS_F32, torch.bfloat16: _lib.TIS_BF16}
 
 __all__ = ["Tree", "DecodePlan", "CacheTree", "tree_build", "tree_route", "tree_attend",
-           "tree_decode", "decode", "version", "from_storage", "summary_offsets"]
+           "tree_decode", "tree_decode_noalloc", "decode", "version", "from_storage",
+           "summary_offsets"]
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -227,6 +228,36 @@ def tree_decode(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, tree: Tree, b
                             ws.data_ptr() if ws is not None else None,
                             ws.numel() if ws is not None else 0, _stream(Q.device)))
     return (O, idx) if return_indices else O
+
+
+def tree_decode_noalloc(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, tree: Tree,
+                        beam: int, scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                        indices: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """tree_decode through tis_tree_decode_noalloc: no workspace, the library
+    keeps the split partial states in its own per-GPU scratch.  With `out`
+    (float32 [B, Hq, d]) and, optionally, `indices` (int32 [B, Hq, beam])
+    given, nothing is allocated on this path either.  Calls that may overlap
+    on one GPU race (they share the scratch).  Returns O."""
+    _need_device(Q, K, V, tree.summaries)
+    if K.dtype != Q.dtype or V.dtype != Q.dtype:
+        raise TypeError("Q, K and V must share one dtype")
+    B, Hq, d = Q.shape
+    if (B, d) != (tree.batch, tree.head_dim) or tuple(K.shape) != (
+            tree.batch, tree.kv_heads, tree.n_keys, tree.head_dim) or V.shape != K.shape:
+        raise ValueError("Q, K, V do not match the tree")
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=Q.device)
+    else:
+        _check_buffer(out, (B, Hq, d), torch.float32, "out")
+    if indices is not None:
+        _check_buffer(indices, (B, Hq, beam), torch.int32, "indices")
+    t = tree.c_struct()
+    check(lib().tis_tree_decode_noalloc(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q),
+                                        Hq, ctypes.byref(t), beam,
+                                        0.0 if scale is None else float(scale), out.data_ptr(),
+                                        indices.data_ptr() if indices is not None else None,
+                                        _stream(Q.device)))
+    return out
 
 
 def tree_radii(K: torch.Tensor, tree: Tree) -> torch.Tensor:
