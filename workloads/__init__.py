@@ -26,6 +26,7 @@ bf16 bit patterns produced by round-to-nearest-even from float32.
 from __future__ import annotations
 
 import dataclasses
+import os
 from typing import Dict, Optional
 
 import numpy as np
@@ -139,7 +140,54 @@ def _store(x: np.ndarray, dtype: str) -> np.ndarray:
     return x.astype(np.float32) if dtype == "f32" else f32_to_bf16_bits(x)
 
 
-def generate(w: Workload) -> Dict[str, np.ndarray]:
+def _head(w: Workload, b: int, h: int):
+    """Keys, values (storage dtype), queries (float32) and planted blocks of
+    the G query heads of (batch b, KV head h): one head's own random streams,
+    so heads can be drawn in any order or in parallel with the same result."""
+    N, d, G = w.n_keys, w.head_dim, w.group
+    planted = np.full(G, -1, dtype=np.int64)
+    rk = _rng(w, 1, b * w.kv_heads + h)
+    rv = _rng(w, 2, b * w.kv_heads + h)
+    rq = _rng(w, 3, b * w.kv_heads + h)
+    if w.generator == "normal":
+        k = rk.standard_normal((N, d), dtype=np.float32)
+        q = rq.standard_normal((G, d), dtype=np.float32)
+    elif w.generator == "mixture":
+        C = w.clusters
+        assert N % C == 0, "mixture needs equal contiguous segments"
+        seg = N // C
+        mu = rk.standard_normal((C, d), dtype=np.float32)
+        k = rk.standard_normal((N, d), dtype=np.float32)
+        k *= np.float32(0.3)
+        k += np.repeat(mu, seg, axis=0)
+        cq = rq.integers(0, C, size=G)
+        q = mu[cq] + np.float32(0.3) * rq.standard_normal((G, d), dtype=np.float32)
+    elif w.generator == "planted":
+        k = rk.standard_normal((N, d), dtype=np.float32)
+        q = rq.standard_normal((G, d), dtype=np.float32)
+        rp = _rng(w, 4, b * w.kv_heads + h)
+        L = w.leaf_block
+        blocks = rp.choice(N // L, size=G, replace=False)
+        for g in range(G):
+            qh = q[g].astype(np.float64)
+            qh /= np.linalg.norm(qh)
+            c = rp.uniform(0.9, 1.0, size=L)
+            u = rp.standard_normal((L, d))
+            u -= np.outer(u @ qh, qh)
+            u /= np.linalg.norm(u, axis=1, keepdims=True)
+            kk = np.sqrt(d) * (c[:, None] * qh[None, :]
+                               + np.sqrt(1.0 - c * c)[:, None] * u)
+            k[blocks[g] * L:(blocks[g] + 1) * L] = kk.astype(np.float32)
+            planted[g] = blocks[g]
+    else:
+        raise ValueError(w.generator)
+    ks = _store(k, w.dtype)
+    del k
+    vs = _store(rv.standard_normal((N, d), dtype=np.float32), w.dtype)
+    return ks, vs, q, planted
+
+
+def generate(w: Workload, workers: Optional[int] = None) -> Dict[str, np.ndarray]:
     """Return {"K","V": [B,Hkv,N,d], "Q": [B,Hq,d]} in the storage dtype, plus
     "planted": int64 [B,Hq] planted leaf block per query (-1 if none).
 
@@ -153,6 +201,10 @@ def generate(w: Workload) -> Dict[str, np.ndarray]:
                 KV head is overwritten with keys sqrt(d)*(c*qhat + sqrt(1-c^2)*u),
                 c ~ U[0.9, 1], u a random unit vector orthogonal to qhat, so
                 every planted key has cosine >= 0.9 with its query.
+
+    Every (batch, KV head) draws from its own seeded streams, so the heads
+    are generated by `workers` threads (default: up to 8) with the same
+    result as one at a time.
     """
     B, Hq, Hkv, d, N = w.batch, w.q_heads, w.kv_heads, w.head_dim, w.n_keys
     G = w.group
@@ -160,46 +212,24 @@ def generate(w: Workload) -> Dict[str, np.ndarray]:
     V = np.empty_like(K)
     Qf = np.empty((B, Hq, d), dtype=np.float32)
     planted = np.full((B, Hq), -1, dtype=np.int64)
-    for b in range(B):
-        for h in range(Hkv):
-            rk = _rng(w, 1, b * Hkv + h)
-            rv = _rng(w, 2, b * Hkv + h)
-            rq = _rng(w, 3, b * Hkv + h)
-            if w.generator == "normal":
-                k = rk.standard_normal((N, d), dtype=np.float32)
-                q = rq.standard_normal((G, d), dtype=np.float32)
-            elif w.generator == "mixture":
-                C = w.clusters
-                assert N % C == 0, "mixture needs equal contiguous segments"
-                seg = N // C
-                mu = rk.standard_normal((C, d), dtype=np.float32)
-                k = rk.standard_normal((N, d), dtype=np.float32)
-                k *= np.float32(0.3)
-                k += np.repeat(mu, seg, axis=0)
-                cq = rq.integers(0, C, size=G)
-                q = mu[cq] + np.float32(0.3) * rq.standard_normal((G, d), dtype=np.float32)
-            elif w.generator == "planted":
-                k = rk.standard_normal((N, d), dtype=np.float32)
-                q = rq.standard_normal((G, d), dtype=np.float32)
-                rp = _rng(w, 4, b * Hkv + h)
-                L = w.leaf_block
-                blocks = rp.choice(N // L, size=G, replace=False)
-                for g in range(G):
-                    qh = q[g].astype(np.float64)
-                    qh /= np.linalg.norm(qh)
-                    c = rp.uniform(0.9, 1.0, size=L)
-                    u = rp.standard_normal((L, d))
-                    u -= np.outer(u @ qh, qh)
-                    u /= np.linalg.norm(u, axis=1, keepdims=True)
-                    kk = np.sqrt(d) * (c[:, None] * qh[None, :]
-                                       + np.sqrt(1.0 - c * c)[:, None] * u)
-                    k[blocks[g] * L:(blocks[g] + 1) * L] = kk.astype(np.float32)
-                    planted[b, h * G + g] = blocks[g]
-            else:
-                raise ValueError(w.generator)
-            K[b, h] = _store(k, w.dtype)
-            del k
-            V[b, h] = _store(rv.standard_normal((N, d), dtype=np.float32), w.dtype)
-            Qf[b, h * G:(h + 1) * G] = q
+
+    def one(bh):
+        b, h = bh
+        ks, vs, q, pl = _head(w, b, h)
+        K[b, h] = ks
+        V[b, h] = vs
+        Qf[b, h * G:(h + 1) * G] = q
+        planted[b, h * G:(h + 1) * G] = pl
+
+    heads = [(b, h) for b in range(B) for h in range(Hkv)]
+    if workers is None:
+        workers = min(8, os.cpu_count() or 1)
+    if workers <= 1 or len(heads) == 1:
+        for bh in heads:
+            one(bh)
+    else:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(min(workers, len(heads))) as ex:
+            list(ex.map(one, heads))
     Q = _store(Qf, w.dtype)
     return {"K": K, "V": V, "Q": Q, "planted": planted}
