@@ -97,9 +97,32 @@ CASES = [
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_causal_prefill_matches_oracle(tis, case):
-    label, dtype, sd, B, Hkv, G, N, d, b, L, beam, gen = case
+    _check_case(tis, *case)
+
+
+# Values far from zero: an output is then a weighted mean of values near the
+# offset, so any mismatch between the weights the numerator uses and those
+# the denominator sums shows at the offset's scale.  The tile path keeps the
+# weights at fp32 precision (bf16 high and low parts), so its error stays at
+# the fp32 accumulation level, far inside the bf16 bar.
+V_OFFSET_CASES = [
+    ("tiles_L32_v_offset_64", "bf16", "f32", 1, 2, 3, 333, 128, 3, 32, 5, "normal"),
+    ("tiles_L64_v_offset_64_g4", "bf16", "f32", 1, 1, 4, 700, 128, 4, 64, 6, "mixture"),
+    ("fused_L16_v_offset_64", "bf16", "f32", 1, 1, 2, 300, 64, 2, 16, 3, "normal"),
+]
+
+
+@pytest.mark.parametrize("case", V_OFFSET_CASES, ids=[c[0] for c in V_OFFSET_CASES])
+def test_causal_prefill_values_with_offset(tis, case):
+    err = _check_case(tis, *case, v_offset=64.0)
+    assert err <= 2e-3, f"max-abs {err:.3g} with values near 64"
+
+
+def _check_case(tis, label, dtype, sd, B, Hkv, G, N, d, b, L, beam, gen, v_offset=0.0):
     t0 = time.time()
     Q, K, V = _inputs(dtype, B, Hkv, G, N, d, gen, seed=N, b=b, L=L)
+    if v_offset:
+        V = to_storage(O_widen(V, dtype) + v_offset, dtype)
     cap = N + 37  # the cache has room past the prefilled keys
     Kc = np.zeros((B, Hkv, cap, d), dtype=K.dtype)
     Vc = np.zeros_like(Kc)
@@ -130,6 +153,7 @@ def test_causal_prefill_matches_oracle(tis, case):
          f"{int((~same & tie).sum())}); keys read per query {reads.mean():.2f} on average over "
          f"{N} positions (dense causal: {(N + 1) / 2:.1f}); max-abs {err:.2e}; "
          f"{time.time() - t0:.1f}s")
+    return err
 
 
 @pytest.mark.timeout(900)

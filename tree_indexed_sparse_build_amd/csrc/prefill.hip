@@ -267,9 +267,10 @@ k_prefill_route(RouteArgs ra, AttendArgs aa, PrefillArgs pa) {
 //   * the same registers are the A operand of P V (rows x keys), and V is
 //     read from a transposed copy, [head][key / 16][d][16], whose 4
 //     consecutive keys per lane match the lane's keys.
-// bf16 inputs: scores with the 16x16x32 bf16 product, weights rounded to
-// bf16 for the 16x16x16 bf16 product with V; fp32 inputs: the 16x16x4 fp32
-// product for both.
+// bf16 inputs: scores with the 16x16x32 bf16 product, weights split into
+// bf16 high and low parts for two 16x16x16 bf16 products with V (fp32
+// precision for the weights); fp32 inputs: the 16x16x4 fp32 product for
+// both.
 typedef short mf_bf16x8 __attribute__((ext_vector_type(8)));
 typedef short mf_bf16x4 __attribute__((ext_vector_type(4)));
 typedef float mf_f32x4 __attribute__((ext_vector_type(4)));
@@ -315,15 +316,28 @@ template <int D> struct TileMath<bf16_bits, D> {
                                                    0, 0, 0);
     return c;
   }
-  // o[nt] += P (rows x 16 keys) V (16 keys x dims 16 nt .. + 15)
-  __device__ static void pv(mf_f32x4 *o, const float *p, const VReg &v) {
-    mf_bf16x4 a;
+  // o[nt] += P (rows x 16 keys) V (16 keys x dims 16 nt .. + 15).  Each
+  // weight p is split into a bf16 high part h (p with its low 16 bits
+  // cleared) and a bf16 low part (p - h, which is exact in fp32, rounded to
+  // nearest), so h + lo is p to within 2^-16 relative; both products with
+  // the bf16 values are exact in the fp32 accumulators.  p is replaced by
+  // the weights as used (h + lo), for the normaliser.
+  __device__ static void pv(mf_f32x4 *o, float *p, const VReg &v) {
+    mf_bf16x4 hi, lo;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = bf16_rne(p[i]);
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t u = __float_as_uint(p[i]);
+      const float h = __uint_as_float(u & 0xffff0000u);
+      hi[i] = static_cast<short>(u >> 16);
+      lo[i] = bf16_rne(p[i] - h);
+      p[i] = h + __uint_as_float(static_cast<uint32_t>(static_cast<uint16_t>(lo[i])) << 16);
+    }
 #pragma unroll
-    for (int nt = 0; nt < D / 16; ++nt)
-      o[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, __builtin_bit_cast(mf_bf16x4, v.v[nt]),
-                                                        o[nt], 0, 0, 0);
+    for (int nt = 0; nt < D / 16; ++nt) {
+      const mf_bf16x4 vb = __builtin_bit_cast(mf_bf16x4, v.v[nt]);
+      o[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(hi, vb, o[nt], 0, 0, 0);
+      o[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lo, vb, o[nt], 0, 0, 0);
+    }
   }
 };
 
@@ -362,8 +376,9 @@ template <int D> struct TileMath<float, D> {
     }
     return c;
   }
-  // product i pairs lane group g with key 4 g + i of the tile
-  __device__ static void pv(mf_f32x4 *o, const float *p, const VReg &v) {
+  // product i pairs lane group g with key 4 g + i of the tile (the weights
+  // enter in fp32 as they are)
+  __device__ static void pv(mf_f32x4 *o, float *p, const VReg &v) {
 #pragma unroll
     for (int nt = 0; nt < D / 16; ++nt) {
       o[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[0], v.v[nt].x, o[nt], 0, 0, 0);
@@ -628,11 +643,11 @@ __device__ __forceinline__ void prefill_tiles(const AttendArgs &aa, const Prefil
       const float mref = m == -INFINITY ? 0.f : m;
       float p[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[i] = __builtin_amdgcn_exp2f(x[i] - mref);
-        lsum += p[i];
-      }
+      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - mref);
+      // the normaliser sums the weights as the product used them
       TileMath<T, D>::pv(o, p, vr);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lsum += p[i];
     }
     // every wave is done with the other buffer (the barrier before this
     // tile), so the next tile goes there
@@ -659,16 +674,6 @@ __device__ __forceinline__ void prefill_tiles(const AttendArgs &aa, const Prefil
 
 template <typename T, int D, int HW>
 __global__ void __launch_bounds__(HW * 64) k_prefill_tiles(AttendArgs aa, PrefillArgs pa) {
-  prefill_tiles<T, D, HW>(aa, pa);
-}
-
-// The same with registers capped for 5 waves a SIMD instead of 4: taken for
-// bf16 keys, d 128 and 4 heads a workgroup, where it spills 4 registers and
-// runs faster (gqa_32k prefill: 18.2 against 19.3 ms at 16,384 positions,
-// 48.7 against 52.8 ms at 32,768); the other shapes spill far more.
-template <typename T, int D, int HW>
-__global__ void __launch_bounds__(HW * 64) __attribute__((amdgpu_waves_per_eu(5)))
-k_prefill_tiles_w5(AttendArgs aa, PrefillArgs pa) {
   prefill_tiles<T, D, HW>(aa, pa);
 }
 
@@ -710,13 +715,6 @@ hipError_t launch_prefill_d(const RouteArgs &ra, const AttendArgs &aa, const Pre
     const int64_t hrows = static_cast<int64_t>(ra.queries) / pa.positions;
     const unsigned grid = static_cast<unsigned>(hrows / pa.tiles * vtiles);
     const size_t lds = tiles_lds(pa.tiles, aa.beam, D, sizeof(T)).total;
-    if constexpr (D == 128 && sizeof(T) == 2) {
-      if (pa.tiles == 4) {
-        hipLaunchKernelGGL((k_prefill_tiles_w5<T, D, 4>), dim3(grid), dim3(4 * 64), lds, s, aa,
-                           pa);
-        return hipGetLastError();
-      }
-    }
     if (pa.tiles == 4)
       hipLaunchKernelGGL((k_prefill_tiles<T, D, 4>), dim3(grid), dim3(4 * 64), lds, s, aa, pa);
     else if (pa.tiles == 2)
