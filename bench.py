@@ -2,11 +2,22 @@
 """Throughput of tree-indexed sparse attention decode on one MI355X.
 
 A step is one pass of the whole hot path over one batch: tree_build over the
-KV cache, then tree_route and tree_attend for every query head (one decode
-step).  The default workload is GQA decode in bf16 with 32,768 keys per KV
-head (batch 4, 32 query / 8 KV heads, d = 128, branching 8, leaf block 64,
-3 levels, beam 8), inputs drawn from the seeded generator and resident in
-HBM before timing starts.
+KV cache, then tree_route and tree_attend for every query head (one fused
+decode launch).  The headline workload is GQA decode in bf16 with 32,768 keys
+per KV head (batch 4, 32 query / 8 KV heads, d = 128, branching 8, leaf block
+64, 3 levels, beam 8).  Each timed step starts from cold caches: a 1 GiB
+streaming read before it (not counted) leaves none of its inputs in the L2s
+or the Infinity Cache.  Inputs come from the seeded generator and are
+resident in HBM before timing starts.
+
+The same run measures the other large workloads (262,144 keys, 1,048,576
+keys, the six-level planted tree): the cold build, and the decode cold
+(caches emptied), steady (caches emptied, then the summaries read once, as
+in a decode loop that keeps the tree hot) and warm (back-to-back launches
+replayed from a graph), each as queries/s and as GB/s on the bytes the method
+must move, per query and counting each distinct row and block once per KV
+head.  Beside them: the streaming-read ceiling and the dependent-load latency
+measured by the library's probes, and from them a latency floor per decode.
 
 Prints ONE JSON line on stdout; details go to stderr.
 """
@@ -23,6 +34,12 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+HEADLINE = "gqa_32k"
+OTHERS = ("gqa_256k", "long_1m", "deep_planted")
+FLUSH_BYTES = 1 << 30  # 4x the 256 MB Infinity Cache, 32x the L2s together
+COPY_BYTES = 256 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{}.json")
+BUILD_SOURCE = os.path.join(ROOT, "tree_indexed_sparse_build_amd", "csrc", "build.hip")
 
 
 def log(*a):
@@ -33,9 +50,20 @@ SUMMARY_ROW_BYTES = {"f32": lambda d: 4 * d, "bf16": lambda d: 2 * d,
                      "fp8": lambda d: d + 4}   # fp8: the codes and the row's scale
 
 
+def first_cut(w) -> int:
+    """First level with more nodes than the beam (levels above keep all)."""
+    l0 = 1
+    while l0 < w.levels and w.branching ** l0 <= w.beam:
+        l0 += 1
+    return l0
+
+
 def algorithmic_bytes(w, summary_dtype: str = "f32"):
-    """Bytes the method must move (see the byte model in the design notes);
-    a summary row is 4d bytes as float32, 2d as bfloat16, d + 4 as fp8."""
+    """Bytes the method must move: the build reads K once and writes every
+    summary once; a query's route reads the summary row of every candidate
+    it scores (plus its query row and kept leaves), its attention the K and V
+    rows of its kept leaf blocks (plus query, indices and output).  A summary
+    row is 4d bytes as float32, 2d as bfloat16, d + 4 as fp8."""
     s = w.elem_bytes
     d, b, W, L = w.head_dim, w.branching, w.beam, w.leaf_block
     heads = w.batch * w.kv_heads
@@ -49,10 +77,33 @@ def algorithmic_bytes(w, summary_dtype: str = "f32"):
             "candidates_per_query": cand}
 
 
-COPY_BYTES = 256 << 20
-FLUSH_BYTES = 1 << 30  # 4x the 256 MB Infinity Cache, 32x the L2s together
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{}.json")
-BUILD_SOURCE = os.path.join(ROOT, "tree_indexed_sparse_build_amd", "csrc", "build.hip")
+def distinct_bytes(tis, w, Q, K):
+    """Decode bytes when each distinct summary row and leaf block is counted
+    once per (batch, KV head), as its query heads read them through one L2:
+    the rows of every scored level's candidates (from the route's trace; the
+    first level that cuts scores all of its nodes, later ones the children of
+    the nodes the group kept), the K and V rows of the distinct kept leaves,
+    and each query's own row, kept leaves and output."""
+    import numpy as np
+    tree = tis.tree_build(K, w.branching, w.leaf_block, w.levels)
+    idx, tr = tis.tree_route(Q, tree, w.beam, trace=True)
+    tr, idx = tr.cpu().numpy(), idx.cpu().numpy()
+    b, lv, W, G, d = w.branching, w.levels, w.beam, w.group, w.head_dim
+    rows = blocks = 0
+    for bb in range(w.batch):
+        for h in range(w.kv_heads):
+            grp = tr[bb, h * G:(h + 1) * G]
+            for l in range(1, lv + 1):
+                if b ** l <= W:
+                    continue  # kept whole, not scored
+                if b ** (l - 1) <= W:
+                    rows += b ** l
+                    continue
+                kept = np.unique(grp[:, l - 2][grp[:, l - 2] >= 0])
+                rows += len(kept) * b
+            blocks += len(np.unique(idx[bb, h * G:(h + 1) * G]))
+    per_query = d * w.elem_bytes + 4 * W + 4 * d
+    return rows * d * 4 + blocks * w.leaf_block * d * w.elem_bytes * 2 + w.queries * per_query
 
 
 def _source_digest() -> str:
@@ -90,8 +141,7 @@ def traffic_from_counters(workload: str, fetch_csv: str, write_csv: str) -> dict
             for r in csv.DictReader(f):
                 if r.get("Counter_Name") != counter:
                     continue
-                name = r["Kernel_Name"]
-                vals.setdefault(name, []).append(float(r["Counter_Value"]))
+                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
         return vals
 
     fetch = per_kernel(fetch_csv, "FETCH_SIZE")
@@ -104,7 +154,6 @@ def traffic_from_counters(workload: str, fetch_csv: str, write_csv: str) -> dict
         xs = [v for k in ks for v in vals[k]]
         return (max(xs) if how == "max" else sum(xs) / len(xs)), ks
 
-    # the reference copy is the largest copy dispatch (input uploads are smaller)
     f_copy, _ = pick(fetch, "copyBuffer", "max")
     w_copy, _ = pick(write, "copyBuffer", "max")
     f_build, _ = pick(fetch, "k_build<")
@@ -126,10 +175,338 @@ def traffic_from_counters(workload: str, fetch_csv: str, write_csv: str) -> dict
     return out
 
 
+def trace_summary(db_path: str, out_path: str, title: str, command: str,
+                  segments: str = "") -> None:
+    """Writes a kernel-trace summary (markdown) from a rocprofv3 database:
+    per workload segment, kernel and grid size, the launches and their mean /
+    median / min / max duration, grouped by what ran just before on the
+    stream (a 1 GiB probe read = cold; another probe read = the summaries
+    read after one, steady; the same kernel = back to back).  Segments begin
+    at the marker reads of (k + 1) MiB (64 (k + 1) workgroups) the benchmark
+    launches before the k-th workload; `segments` names them, comma-separated."""
+    import sqlite3
+    import statistics
+    names = [n for n in segments.split(",") if n]
+    con = sqlite3.connect(db_path)
+    rows = list(con.execute("select name, start, end, grid_x, workgroup_x, queue_id "
+                            "from kernels order by start"))
+    groups = {}
+    prev = {}
+    seg = "-"
+    for name, s, e, gx, wx, q in rows:
+        short = name.replace("(anonymous namespace)::", "").replace("tis::", "")
+        short = short.replace("void ", "", 1).split("(")[0]
+        wgs = gx // max(wx, 1)
+        if "k_probe_read" in short and wgs < 4096 and wgs % 64 == 0 and wgs // 64 <= len(names) \
+                and (e - s) < 50e3:
+            k = wgs // 64 - 1
+            if names and (prev.get(q) is None or "k_probe_read" not in prev[q][0]):
+                seg = names[k]
+                prev[q] = None
+                continue
+        p = prev.get(q)
+        if p is None:
+            before = "-"
+        elif "k_probe_read" in p[0]:
+            # the 1 GiB flush takes ~150-250 us, a summaries read far less
+            before = "probe read of 1 GiB (cold)" if p[2] > 100.0 else "probe read of the summaries"
+        elif p[0] == short:
+            before = "same kernel"
+        else:
+            before = p[0].split("<")[0]
+        key = (seg, short, wgs, wx, before)
+        groups.setdefault(key, []).append((e - s) / 1e3)
+        prev[q] = (short, wgs, (e - s) / 1e3)
+    lines = [f"# {title}", "", "Command (run from the repository root):", "", "```",
+             command, "```", "",
+             "rocprofv3 kernel trace; durations in microseconds (kernel begin to end). "
+             "`before` is the dispatch that ran just before on the stream.", "",
+             "| workload | kernel | workgroups x threads | before | launches | mean | median | "
+             "min | max |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    order = {n: i for i, n in enumerate(["-"] + names)}
+    for (seg, short, wgs, wx, before), ds in sorted(
+            groups.items(), key=lambda kv: (order.get(kv[0][0], 99), -sum(kv[1]))):
+        if not (short.startswith("k_") or "probe" in short):
+            continue
+        lines.append(f"| {seg} | `{short}` | {wgs} x {wx} | {before} | {len(ds)} | "
+                     f"{statistics.fmean(ds):.2f} | {statistics.median(ds):.2f} | {min(ds):.2f} | "
+                     f"{max(ds):.2f} |")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+# --------------------------------------------------------------- probes --
+
+class Probes:
+    """The library's measurement probes on torch buffers: a 1 GiB streaming
+    read (the read ceiling, and the cache flush before cold timings) and a
+    dependent-load chase (latency of one round trip)."""
+
+    def __init__(self, tis, torch, dev):
+        self.torch = torch
+        self.lib = tis.ops.lib()
+        self.dev = dev
+        self.buf = torch.zeros(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+        self.sink = torch.zeros(4, dtype=torch.int32, device=dev)
+        self._check = tis.ops.check
+        self._stream = tis.ops._stream
+
+    def read(self, t=None, nbytes=None, nontemporal=False):
+        t = self.buf if t is None else t
+        n = t.numel() * t.element_size() if nbytes is None else nbytes
+        n -= n % 16
+        self._check(self.lib.tis_probe_read(t.data_ptr(), n, int(nontemporal),
+                                            self.sink.data_ptr(), self._stream(self.dev)))
+
+    def flush(self):
+        self.read()
+
+    def marker(self, k: int):
+        """A probe read of (k + 1) MiB: a dispatch of 64 (k + 1) workgroups
+        that marks, in a kernel trace, where the measurement of the k-th
+        workload begins."""
+        self.read(nbytes=(k + 1) << 20)
+
+    def read_ceiling(self, reps=4, nbytes=4 << 30):
+        """GB/s of back-to-back reads of a 4 GiB buffer (16 times the
+        Infinity Cache, so each read finds nothing of its data cached)."""
+        torch = self.torch
+        buf = torch.ones(nbytes, dtype=torch.uint8, device=self.dev)
+        out = {}
+        for nt in (False, True):
+            self.read(buf, nontemporal=nt)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(reps):
+                self.read(buf, nontemporal=nt)
+            e1.record()
+            torch.cuda.synchronize()
+            out["nontemporal" if nt else "plain"] = nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        del buf
+        return out
+
+    def chase(self, footprint: int, hops: int, cold: bool, seed: int = 7):
+        """Microseconds per dependent load on a random cycle through
+        footprint / 128 cache-line slots, `hops` links from one start: cold
+        (caches emptied first, so every hop goes to HBM, through TLB misses
+        across the footprint) or warm (the same links walked just before, so
+        the hops find whichever cache holds hops * 128 bytes of lines).
+        Per hop = (time of `hops` hops - time of none) / hops."""
+        import numpy as np
+        torch = self.torch
+        n = footprint // 4
+        slots = n // 32
+        rng = np.random.default_rng(seed)
+        perm = rng.permutation(slots).astype(np.int64)
+        nxt = np.zeros(n, dtype=np.uint32)
+        nxt[perm * 32] = np.roll(perm, -1) * 32
+        dnext = torch.from_numpy(nxt.view(np.int32)).to(self.dev)
+        out = torch.zeros(1, dtype=torch.int32, device=self.dev)
+        start = int(perm[0] * 32)
+
+        def run(h):
+            self._check(self.lib.tis_probe_chase(dnext.data_ptr(), n, start, h, out.data_ptr(),
+                                                 self._stream(self.dev)))
+
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+        def timed(h):
+            if cold:
+                self.flush()
+            else:
+                run(hops)
+            e0.record()
+            run(h)
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3
+
+        timed(hops)
+        t_h = float(np.median([timed(hops) for _ in range(5)]))
+        t_0 = float(np.median([timed(0) for _ in range(5)]))
+        del dnext
+        return (t_h - t_0) / hops
+
+
+# ------------------------------------------------------------- timings --
+
+def _events(torch, n):
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def graph_time(torch, fn, per_graph=20, replays=5):
+    """Microseconds per call of fn, from a graph holding `per_graph` calls
+    back to back, replayed `replays` times between events (median)."""
+    import numpy as np
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(per_graph):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = _events(torch, 2)
+    ts = []
+    for _ in range(replays):
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3 / per_graph)
+    del g
+    return float(np.median(ts))
+
+
+def graph_diff(torch, prep, fn, per_graph=10, replays=5):
+    """Microseconds of fn in the cache state prep() leaves: a graph of
+    `per_graph` times (prep, fn) and a graph of `per_graph` times prep alone
+    are replayed between events, and the difference of their median times
+    is divided by per_graph.  The launches run back to back inside each
+    graph, so no host gap or event sits between prep and fn, and the result
+    is close to fn's kernel durations."""
+    import numpy as np
+
+    def capture(body):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            body()
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(per_graph):
+                body()
+        return g
+
+    def both():
+        prep()
+        fn()
+    ga, gb = capture(both), capture(prep)
+    e0, e1 = _events(torch, 2)
+
+    def timed(g):
+        g.replay()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(replays):
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        return float(np.median(ts))
+    t = (timed(ga) - timed(gb)) / per_graph
+    del ga, gb
+    return t
+
+
+def decode_regimes(torch, probes, plan):
+    """Decode durations (us): cold (caches emptied by a 1 GiB read), steady
+    (emptied, then the summaries read once: a decode loop that keeps the
+    tree hot while keys and values come from HBM) and warm (back to back:
+    repeated decodes of the same queries, whose blocks stay in the L2s)."""
+    def steady_prep():
+        probes.flush()
+        probes.read(plan.summaries)
+    return {"cold_us": graph_diff(torch, probes.flush, plan.decode),
+            "steady_us": graph_diff(torch, steady_prep, plan.decode),
+            "warm_us": graph_time(torch, plan.decode)}
+
+
+def decode_floor(w, ceil_gbs, hop_us, dec_bytes):
+    """Latency floor of one decode: the scored levels and the gather form a
+    chain of dependent round trips (the first level's rows, each later
+    level's rows, then the leaf blocks), and the bytes cannot move faster
+    than the streaming-read ceiling."""
+    hops = w.levels - first_cut(w) + 2
+    return hops * hop_us + dec_bytes / (ceil_gbs * 1e3)
+
+
+def measure_workload(tis, torch, probes, w, ceil_gbs, hop_us, reps, headline=False, K=0, W=0,
+                     index=0):
+    """Cold build, decode regimes and bytes for one workload; with headline
+    set, also the timed region of K cold steps (build + decode)."""
+    import workloads
+    t0 = time.time()
+    probes.marker(index)
+    x = workloads.generate(w, workers=min(16, os.cpu_count() or 1))
+    dev = probes.dev
+    Q, K_, V = (tis.from_storage(x[k], w.dtype, dev) for k in ("Q", "K", "V"))
+    log(f"{w.name}: generated and uploaded in {time.time() - t0:.1f}s")
+    plan = tis.DecodePlan(Q, K_, V, w.branching, w.leaf_block, w.levels, w.beam)
+    by = algorithmic_bytes(w)
+    dec_bytes = by["route"] + by["attend"]
+    res = {"queries": w.queries, "n_keys": w.n_keys,
+           "bytes": {"build": by["build"], "decode_per_query_sum": dec_bytes,
+                     "route_per_query_sum": by["route"], "attend_per_query_sum": by["attend"],
+                     "candidates_per_query": by["candidates_per_query"]}}
+    step = None
+    if headline:
+        # the timed region: K cold steps (a 1 GiB read, then build and
+        # decode), replayed from one graph between events, less the same K
+        # reads alone
+        def step_fn():
+            plan.build()
+            plan.decode()
+        for _ in range(W):
+            probes.flush()
+            step_fn()
+        torch.cuda.synchronize()
+        h0 = time.perf_counter()
+        step_us = graph_diff(torch, probes.flush, step_fn, per_graph=K, replays=3)
+        h1 = time.perf_counter()
+        step = {"steps": K, "step_us_mean": step_us, "region_wall_s": h1 - h0}
+    bc = graph_diff(torch, probes.flush, plan.build, per_graph=max(5, min(K, 20)), replays=3)
+    if not headline:
+        # the build then one decode, back to back (the decode finds the tree
+        # the build just wrote): the literal sequence of the 1M-key workload
+        def bd():
+            plan.build()
+            plan.decode()
+        res["decode_after_build_us"] = graph_diff(torch, probes.flush, bd, per_graph=5,
+                                                  replays=3) - bc
+    res["build"] = {"cold_us": bc, "cold_gbs": by["build"] / (bc * 1e3),
+                    "cold_frac": by["build"] / (bc * 1e3) / HBM_PEAK_GBS,
+                    "warm_us": graph_time(torch, plan.build, per_graph=5, replays=3)}
+    res["build"]["warm_frac"] = by["build"] / (res["build"]["warm_us"] * 1e3) / HBM_PEAK_GBS
+    dr = decode_regimes(torch, probes, plan)
+    dist = distinct_bytes(tis, w, Q, K_)
+    floor = decode_floor(w, ceil_gbs, hop_us, dec_bytes)
+    dec = {"regimes": dr, "bytes_distinct": dist, "floor_us": floor,
+           "floor_model": f"{w.levels - first_cut(w) + 2} dependent HBM round trips + "
+                          "per-query-sum bytes at the read ceiling"}
+    for r in ("cold", "steady", "warm"):
+        t = dr[f"{r}_us"]
+        dec[r] = {"us": t, "queries_per_s": w.queries / (t * 1e-6),
+                  "gbs": dec_bytes / (t * 1e3), "frac": dec_bytes / (t * 1e3) / HBM_PEAK_GBS,
+                  "gbs_distinct": dist / (t * 1e3),
+                  "frac_distinct": dist / (t * 1e3) / HBM_PEAK_GBS,
+                  "floor_ratio": t / floor}
+    res["decode"] = dec
+    if step is not None:
+        res["step"] = step
+    log(f"{w.name}: build cold {bc:.1f} us ({res['build']['cold_frac']:.1%} of 8 TB/s on "
+        f"{by['build'] / 1e6:.1f} MB), warm {res['build']['warm_us']:.1f} us; decode cold "
+        f"{dr['cold_us']:.2f} / steady {dr['steady_us']:.2f} / warm {dr['warm_us']:.2f} us "
+        f"({dec['cold']['frac']:.1%} / {dec['steady']['frac']:.1%} / {dec['warm']['frac']:.1%} "
+        f"on {dec_bytes / 1e6:.2f} MB per-query sum; {dec['cold']['frac_distinct']:.1%} cold on "
+        f"{dist / 1e6:.2f} MB distinct); floor {floor:.2f} us")
+    return res, (x, Q, K_, V, plan)
+
+
+# ----------------------------------------------------- the other legs --
+
 def cpu_baseline(w, x, min_seconds: float = 10.0, max_reps: int = 500):
     """The CPU oracle, as it stands, on whole steps of the same workload."""
     from oracle import tis_oracle as O
-    from threadpoolctl import threadpool_limits
+    from threadpoolctl import threadpool_info, threadpool_limits
+    blas = [i.get("num_threads") for i in threadpool_info() if i.get("user_api") == "blas"]
     reps = 0
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
@@ -140,17 +517,23 @@ def cpu_baseline(w, x, min_seconds: float = 10.0, max_reps: int = 500):
             el = time.perf_counter() - t0
             if el >= min_seconds or reps >= max_reps:
                 break
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = None
     return {"value": reps * w.queries / el, "unit": "queries/s", "cores": 1, "kind": "oracle",
+            "host_cpu_count": os.cpu_count(), "host_affinity_cpus": affinity,
+            "blas_threads_default": blas[0] if blas else None,
             "sample": f"{reps} whole steps (build over all {w.batch * w.kv_heads} KV heads, "
                       f"route + attend of all {w.queries} queries) of the same workload, "
-                      f"numpy fp64, BLAS limited to 1 thread, {el:.1f} s"}
+                      f"numpy fp64 on one thread (BLAS limited to 1; the oracle's other work "
+                      f"is single-threaded numpy), {el:.1f} s"}
 
 
 def per_launch(torch, fn, reps):
     """Average duration (s) of fn's launch: reps launches back to back
-    between one event pair (event overhead spread over reps launches)."""
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    between one event pair."""
+    e0, e1 = _events(torch, 2)
     torch.cuda.synchronize()
     e0.record()
     for _ in range(reps):
@@ -160,42 +543,32 @@ def per_launch(torch, fn, reps):
     return e0.elapsed_time(e1) * 1e-3 / reps
 
 
-def reduced_summaries(tis, torch, w, Q, K, V, reps, warmup, summary_dtype):
+def reduced_summaries(tis, torch, w, Q, K, V, summary_dtype):
     """The step with summaries stored as bfloat16 or fp8 (the same means
-    rounded once to the narrower type): build and fused decode durations, and
-    the decode's rate on its own algorithmic bytes (each routing level reads
-    a half or about a quarter of the float32 bytes)."""
+    rounded once to the narrower type): warm build and decode durations
+    (graph replay) and the decode's rate on its own algorithmic bytes."""
     plan = tis.DecodePlan(Q, K, V, w.branching, w.leaf_block, w.levels, w.beam,
                           summary_dtype=summary_dtype)
-    for _ in range(warmup):
-        plan.build()
-        plan.decode()
-
-    def step():
-        plan.build()
-        plan.decode()
-    step_s = per_launch(torch, step, reps)
-    build_s = per_launch(torch, plan.build, reps)
-    decode_s = per_launch(torch, plan.decode, reps)
+    plan.build()
+    plan.decode()
+    build_us = graph_time(torch, plan.build, per_graph=5, replays=3)
+    decode_us = graph_time(torch, plan.decode)
     by = algorithmic_bytes(w, summary_dtype)
     dec = by["route"] + by["attend"]
-    return {"regime": f"as the headline step, summaries stored as {summary_dtype}",
-            "step_us": step_s * 1e6, "queries_per_s_step": w.queries / step_s,
-            "build_us": build_s * 1e6, "build_gbs": by["build"] / build_s / 1e9,
-            "decode_us": decode_s * 1e6, "decode_queries_per_s": w.queries / decode_s,
-            "decode_gbs": dec / decode_s / 1e9, "decode_frac": dec / decode_s / 1e9 / HBM_PEAK_GBS,
-            "decode_bytes": dec}
+    return {"regime": f"warm (graph replay), summaries stored as {summary_dtype}",
+            "build_us": build_us, "build_gbs": by["build"] / (build_us * 1e3),
+            "decode_us": decode_us, "decode_queries_per_s": w.queries / (decode_us * 1e-6),
+            "decode_gbs": dec / (decode_us * 1e3),
+            "decode_frac": dec / (decode_us * 1e3) / HBM_PEAK_GBS, "decode_bytes": dec}
 
 
-def threshold_retrieval(tis, torch, w, Q, K, V, reps, warmup, k_ranks=(64, 512)):
+def threshold_retrieval(tis, torch, w, Q, K, V, reps, k_ranks=(64, 512)):
     """Bounding-sphere threshold retrieval on the step's data: the radii pass
     over K, then the fused threshold decode at thresholds halfway between
     each query's k-th and (k+1)-th best key score (set up with a dense torch
     matmul, not timed)."""
     tree = tis.tree_build(K, w.branching, w.leaf_block, w.levels)
     radii = tis.tree_radii(K, tree)
-    for _ in range(warmup):
-        tis.tree_radii(K, tree)
     radii_s = per_launch(torch, lambda: tis.tree_radii(K, tree), reps)
     nodes = sum(w.branching ** l for l in range(1, w.levels + 1))
     radii_bytes = w.batch * w.kv_heads * (w.n_keys * w.head_dim * w.elem_bytes
@@ -214,8 +587,6 @@ def threshold_retrieval(tis, torch, w, Q, K, V, reps, warmup, k_ranks=(64, 512))
         o = torch.empty((w.batch, w.q_heads, w.head_dim), dtype=torch.float32, device=Q.device)
         _, _, cnt = tis.tree_decode_threshold(Q, K, V, tree, radii, tau, max_nodes,
                                               return_indices=True)
-        for _ in range(warmup):
-            tis.tree_decode_threshold(Q, K, V, tree, radii, tau, max_nodes, out=o)
         dec_s = per_launch(torch, lambda: tis.tree_decode_threshold(
             Q, K, V, tree, radii, tau, max_nodes, out=o), reps)
         c = cnt.float()
@@ -227,7 +598,7 @@ def threshold_retrieval(tis, torch, w, Q, K, V, reps, warmup, k_ranks=(64, 512))
     return out
 
 
-def causal_prefill_bench(tis, torch, w, Q, K, V, reps, warmup, max_positions=4096):
+def causal_prefill_bench(tis, torch, w, Q, K, V, reps, max_positions=4096):
     """Causal prefill of the first P = min(N, max_positions) keys: every
     position a query over the tree of its prefix (queries: the workload's,
     one per head, plus seeded per-position noise).  Times the whole call
@@ -242,10 +613,8 @@ def causal_prefill_bench(tis, torch, w, Q, K, V, reps, warmup, max_positions=409
     ct.append(P)
     out = torch.empty((w.batch, w.q_heads, P, w.head_dim), dtype=torch.float32, device=Q.device)
     _, idx = ct.causal_prefill(Qp, w.beam, return_indices=True)
-    for _ in range(warmup):
-        ct.causal_prefill(Qp, w.beam, out=out)
-    reps = max(3, min(reps, 20))
-    t = per_launch(torch, lambda: ct.causal_prefill(Qp, w.beam, out=out), reps)
+    ct.causal_prefill(Qp, w.beam, out=out)
+    t = per_launch(torch, lambda: ct.causal_prefill(Qp, w.beam, out=out), max(3, min(reps, 10)))
     pos = torch.arange(P, device=Q.device).view(1, 1, P, 1)
     blk = idx.long()
     size = torch.clamp(pos + 1 - blk * w.leaf_block, max=w.leaf_block)
@@ -255,118 +624,39 @@ def causal_prefill_bench(tis, torch, w, Q, K, V, reps, warmup, max_positions=409
             "keys_read_mean": float(reads.mean()), "dense_causal_keys_mean": (P + 1) / 2}
 
 
-def cache_states(torch, dev, plan, reps, back_to_back):
-    """Durations in two cache states.  cold: 1 GiB read first, which leaves
-    none of the inputs in the Infinity Cache or an L2 and no dirty lines to
-    write back (a flush by writing would charge its write-backs to the timed
-    kernel); steady: cold, then one read of the summaries, as when the tree
-    stays hot across decode steps.  Each is the median of `reps` lone
-    launches between their own events, compared with lone warm launches
-    timed the same way (nothing in between): the difference is what the
-    cache state costs, and adding it to the back-to-back duration removes
-    the event and dispatch overhead a lone launch carries."""
-    import numpy as np
-    flush = torch.zeros(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-
-    def one(fn, state):
-        if state != "warm":
-            flush.sum()
-        if state == "steady":
-            plan.summaries.sum()
-        e0.record()
-        fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3
-
-    out = {}
-    for name, fn in (("build", plan.build), ("decode", plan.decode)):
-        lone = {}
-        for state in ("warm", "cold", "steady"):
-            if name == "build" and state == "steady":
-                continue
-            one(fn, state)
-            lone[state] = float(np.median([one(fn, state) for _ in range(reps)]))
-        for state, us in lone.items():
-            out[f"{name}_{state}_lone_us"] = us
-            if state != "warm":
-                out[f"{name}_{state}_us"] = back_to_back[name] + us - lone["warm"]
-    del flush
-    return out
-
-
-def distinct_route_bytes(tis, w, Q, K):
-    """Summary bytes the route must read when each distinct row is counted
-    once per KV head (its G query heads run on one XCD and share its L2):
-    the rows of every scored level's candidates, from the route's trace.
-    Levels whose nodes all fit in the beam are kept without scoring; the
-    first level that cuts scores all of its nodes, later ones the children
-    of the nodes each query kept."""
-    import numpy as np
-    tree = tis.tree_build(K, w.branching, w.leaf_block, w.levels)
-    _, tr = tis.tree_route(Q, tree, w.beam, trace=True)
-    tr = tr.cpu().numpy()
-    b, lv, W, G = w.branching, w.levels, w.beam, w.group
-    rows = 0
-    for bb in range(w.batch):
-        for h in range(w.kv_heads):
-            grp = tr[bb, h * G:(h + 1) * G]  # [G, levels, W]
-            for l in range(1, lv + 1):
-                if b ** l <= W:
-                    continue  # kept whole, not scored
-                if b ** (l - 1) <= W:
-                    rows += b ** l  # the first level that cuts: all of its nodes
-                    continue
-                kept = np.unique(grp[:, l - 2][grp[:, l - 2] >= 0])
-                rows += len(kept) * b  # distinct parents kept by the group, b children each
-    return rows * w.head_dim * 4
-
-
-def cache_decode_loop(tis, w, K, V, Q, steps, warmup):
+def cache_decode_loop(tis, torch, w, K, V, Q, steps):
     """The decode loop over a growing cache of the same shape: the tree over
     the first keys of the cache is filled by one long append, then every
-    step appends one key per head (tis_cache_tree_append) and decodes every
-    query (tis_cache_tree_decode).  Times: the long append, one-key appends
-    back to back, decodes back to back, whole steps back to back, and the
-    same step as one fused call (tis_cache_tree_append_decode)."""
-    import torch
-    need = 4 * (steps + warmup) + 8
+    step appends one key per head and decodes every query, as two calls and
+    as the fused call (tis_cache_tree_append_decode).  Appends change the
+    tree, so these launches run eagerly, back to back."""
+    need = 4 * (steps + 4) + 8
     prefill = w.n_keys - need
     if prefill < 1:
         return None
     ct = tis.CacheTree(K, V, w.branching, w.leaf_block)
     out = torch.empty((w.batch, w.q_heads, w.head_dim), dtype=torch.float32, device=K.device)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
 
     def timed(fn, reps):
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(reps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / reps  # us
+        return per_launch(torch, fn, reps) * 1e6
 
-    ct.append(prefill)  # warm the kernel once, then time a fresh prefill
+    ct.append(prefill)
     ct.reset()
     prefill_us = timed(lambda: ct.append(prefill), 1)
     decode = ct.bind_decode(Q, w.beam, out)
     step = lambda: (ct.append(1), decode())
-    for _ in range(warmup):
+    for _ in range(2):
         step()
     step_us = timed(step, steps)
     append_us = timed(lambda: ct.append(1), steps)
     decode_us = timed(decode, steps)
     fused = ct.bind_decode(Q, w.beam, out, append=True)
-    for _ in range(warmup):
+    for _ in range(2):
         fused()
     fused_us = timed(fused, steps)
     kbytes = prefill * w.batch * w.kv_heads * w.head_dim * w.elem_bytes
     return {"regime": "tree over the first n keys of a cache of the workload's size; "
-                      "one key appended per head per step",
+                      "one key appended per head per step; eager launches back to back",
             "n_keys_at_end": ct.n_keys, "levels": ct.levels,
             "prefill_keys": prefill, "prefill_us": prefill_us,
             "prefill_gbs": kbytes / (prefill_us * 1e-6) / 1e9,
@@ -375,32 +665,38 @@ def cache_decode_loop(tis, w, K, V, Q, steps, warmup):
             "fused_step_us": fused_us, "fused_queries_per_s": w.queries / (fused_us * 1e-6)}
 
 
+# ----------------------------------------------------------------- main --
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="gqa_32k")
+    ap.add_argument("--steps", type=int, default=20, help="timed cold steps of the headline")
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=HEADLINE, help="the headline workload")
+    ap.add_argument("--others", default=",".join(OTHERS),
+                    help="comma-separated workloads also measured ('none' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-cache-loop", action="store_true",
-                    help="skip the growing-cache decode loop measurement")
-    ap.add_argument("--no-bf16-summaries", action="store_true",
-                    help="skip the measurement of the step with bfloat16 and fp8 summaries")
-    ap.add_argument("--no-threshold", action="store_true",
-                    help="skip the bounding-sphere threshold retrieval measurement")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the growing-cache loop, reduced-precision summaries, bounding "
+                         "spheres and causal prefill legs")
     ap.add_argument("--prefill-positions", type=int, default=4096,
-                    help="positions of the causal prefill measurement (at most the workload's keys)")
-    ap.add_argument("--no-prefill", action="store_true",
-                    help="skip the causal prefill measurement")
+                    help="positions of the causal prefill leg (at most the workload's keys)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 256 MiB device-to-device copy first (the reference "
                          "dispatch for scaling HBM byte counters)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter files (FETCH_SIZE, WRITE_SIZE) of "
                          "a --calibrate-copy run into profiles/traffic_<workload>.json and exit")
+    ap.add_argument("--trace-summary", nargs=5,
+                    metavar=("DB", "OUT_MD", "TITLE", "COMMAND", "SEGMENTS"),
+                    help="write a markdown kernel-trace summary of a rocprofv3 database (its "
+                         "workload segments named by SEGMENTS, comma-separated) and exit")
     args = ap.parse_args(argv)
     if args.traffic_from:
         print(json.dumps(traffic_from_counters(args.workload, *args.traffic_from)))
+        return 0
+    if args.trace_summary:
+        trace_summary(*args.trace_summary)
         return 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); every tree is "
@@ -408,7 +704,6 @@ def main(argv=None):
               "with no exchange", file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
     import workloads
     import tree_indexed_sparse_build_amd as tis
@@ -416,16 +711,8 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
         return 1
-    w = workloads.get(args.workload)
-    t0 = time.time()
-    x = workloads.generate(w)
-    log(f"workload {w.name}: generated in {time.time() - t0:.1f}s; {tis.version()}; "
-        f"device {torch.cuda.get_device_name(0)}")
     dev = torch.device("cuda", 0)
-    Q = tis.from_storage(x["Q"], w.dtype, dev)
-    K = tis.from_storage(x["K"], w.dtype, dev)
-    V = tis.from_storage(x["V"], w.dtype, dev)
-    plan = tis.DecodePlan(Q, K, V, w.branching, w.leaf_block, w.levels, w.beam)
+    log(f"{tis.version()}; device {torch.cuda.get_device_name(0)}")
     if args.calibrate_copy:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -434,214 +721,113 @@ def main(argv=None):
         torch.cuda.synchronize()
         del src, dst
 
-    def step():
-        plan.build()
-        plan.decode()  # route + attend of every query in one launch
+    probes = Probes(tis, torch, dev)
+    ceil = probes.read_ceiling()
+    # cold: 2,000 hops over a 1 GiB footprint after the caches are emptied;
+    # Infinity Cache: 131,072 warm hops (16 MB of lines, more than an XCD's
+    # 4 MB L2, far less than the 256 MB cache); L2: 2,000 warm hops (256 KB)
+    hop = {"hbm_cold": probes.chase(FLUSH_BYTES, 2000, cold=True),
+           "infinity_cache_warm": probes.chase(64 << 20, 131072, cold=False),
+           "l2_warm": probes.chase(1 << 20, 2000, cold=False)}
+    log(f"read ceiling {ceil['plain']:.0f} GB/s plain, {ceil['nontemporal']:.0f} GB/s "
+        f"nontemporal (4 GiB, back to back); dependent load {hop['hbm_cold']:.3f} us cold "
+        f"(1 GiB footprint), {hop['infinity_cache_warm']:.3f} us (Infinity Cache), "
+        f"{hop['l2_warm']:.3f} us (L2)")
+    ceil_gbs = max(ceil.values())
 
-    def step_separate():
-        plan.build()
-        plan.route()
-        plan.attend()
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
+    w = workloads.get(args.workload)
     K_ = args.steps
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    # timed region 1: whole steps back to back (the headline)
-    torch.cuda.synchronize()
-    h0 = time.perf_counter()
-    start.record()
-    for _ in range(K_):
-        step()
-    end.record()
-    h1 = time.perf_counter()
-    torch.cuda.synchronize()
-    h2 = time.perf_counter()
-    total_ms = start.elapsed_time(end)
-    ms_step = total_ms / K_
-    # the same steps replayed from a HIP graph (one capture of build + decode):
-    # the replays must reproduce the eager outputs bit for bit
-    out_eager = plan.out.clone()
-    graph = torch.cuda.CUDAGraph()
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        step()
-    torch.cuda.current_stream().wait_stream(side)
-    with torch.cuda.graph(graph):
-        step()
-    for _ in range(3):
-        plan.out.zero_()
-        graph.replay()
-        torch.cuda.synchronize()
-        if not torch.equal(plan.out, out_eager):
-            raise RuntimeError("graph replay does not reproduce the eager step")
-    torch.cuda.synchronize()
-    start.record()
-    for _ in range(K_):
-        graph.replay()
-    end.record()
-    torch.cuda.synchronize()
-    ms_step_graph = start.elapsed_time(end) / K_
-    # the same steps with route and attend as separate calls (reference)
-    torch.cuda.synchronize()
-    start.record()
-    for _ in range(K_):
-        step_separate()
-    end.record()
-    torch.cuda.synchronize()
-    ms_step_separate = start.elapsed_time(end) / K_
-    # timed region 2: each kernel K times back to back between one event pair
-    # (its average launch duration; event overhead is spread over K launches)
-    t_build = np.array([per_launch(torch, plan.build, K_)])
-    t_route = np.array([per_launch(torch, plan.route, K_)])
-    t_attend = np.array([per_launch(torch, plan.attend, K_)])
-    t_decode = per_launch(torch, plan.decode, K_)
-
+    head, (x, Q, K, V, plan) = measure_workload(tis, torch, probes, w, ceil_gbs, hop["hbm_cold"],
+                                                reps=K_, headline=True, K=K_, W=args.warmup)
+    step = head["step"]
     by = algorithmic_bytes(w)
-    build_gbs = by["build"] / t_build.mean() / 1e9
-    decode_s = t_decode
-    idx = plan.indices.cpu().numpy()
-    uniq = 0
-    for bb in range(w.batch):
-        for h in range(w.kv_heads):
-            uniq += len(np.unique(idx[bb, h * w.group:(h + 1) * w.group]))
-    attend_dedup = uniq * w.leaf_block * w.head_dim * w.elem_bytes * 2
-    route_dedup = distinct_route_bytes(tis, w, Q, K)
-    # the query rows read and the kept leaves written, once per query
-    qio = w.queries * (w.head_dim * w.elem_bytes + 4 * w.beam)
-    dec_dedup = route_dedup + attend_dedup + qio
-    log(f"step {ms_step * 1e3:.1f} us (host enqueue {(h1 - h0) / K_ * 1e6:.1f} us/step, "
-        f"wall {(h2 - h0) / K_ * 1e6:.1f} us/step); replayed from a graph "
-        f"{ms_step_graph * 1e3:.1f} us; with separate route + attend calls "
-        f"{ms_step_separate * 1e3:.1f} us")
-    log(f"build  {t_build.mean() * 1e6:8.2f} us  {build_gbs:8.1f} GB/s "
-        f"({build_gbs / HBM_PEAK_GBS:.1%} of 8 TB/s) on {by['build'] / 1e6:.1f} MB")
-    log(f"route  {t_route.mean() * 1e6:8.2f} us  {by['route'] / t_route.mean() / 1e9:8.1f} GB/s "
-        f"on {by['route'] / 1e6:.2f} MB ({by['candidates_per_query']} candidates/query)")
-    log(f"attend {t_attend.mean() * 1e6:8.2f} us  {by['attend'] / t_attend.mean() / 1e9:8.1f} "
-        f"GB/s on {by['attend'] / 1e6:.2f} MB per-query sum; "
-        f"{attend_dedup / t_attend.mean() / 1e9:.1f} GB/s on {attend_dedup / 1e6:.2f} MB of "
-        f"distinct blocks per KV head")
-    dec_bytes = by["route"] + by["attend"]
-    log(f"decode (fused route + attend) {decode_s * 1e6:.2f} us -> "
-        f"{w.queries / decode_s:.3e} queries/s, {dec_bytes / decode_s / 1e9:.1f} GB/s "
-        f"({dec_bytes / decode_s / 1e9 / HBM_PEAK_GBS:.1%}) on {dec_bytes / 1e6:.2f} MB "
-        f"per-query sum, {dec_dedup / decode_s / 1e9:.1f} GB/s "
-        f"({dec_dedup / decode_s / 1e9 / HBM_PEAK_GBS:.1%}) on {dec_dedup / 1e6:.2f} MB "
-        f"distinct per KV head; "
-        f"in the step (step - build): {ms_step * 1e3 - t_build.mean() * 1e6:.2f} us")
+    build_gbs = head["build"]["cold_gbs"]
 
-    states = cache_states(torch, dev, plan, 30,
-                          {"build": t_build.mean() * 1e6, "decode": decode_s * 1e6})
-    log(f"cache states (lone launches, median of 30; cold = 1 GiB read first, steady = cold + "
-        f"summaries read; lone warm build {states['build_warm_lone_us']:.1f} us, decode "
-        f"{states['decode_warm_lone_us']:.2f} us): build cold {states['build_cold_us']:.1f} us "
-        f"({by['build'] / states['build_cold_us'] / 1e3:.0f} GB/s, "
-        f"{by['build'] / states['build_cold_us'] / 1e3 / HBM_PEAK_GBS:.1%}); decode cold "
-        f"{states['decode_cold_us']:.2f} us ({dec_bytes / states['decode_cold_us'] / 1e3:.0f} "
-        f"GB/s, {dec_bytes / states['decode_cold_us'] / 1e3 / HBM_PEAK_GBS:.1%}), steady "
-        f"{states['decode_steady_us']:.2f} us")
-
-    pre = None
-    if not args.no_prefill:
-        pre = causal_prefill_bench(tis, torch, w, Q, K, V, K_, args.warmup,
-                                   max_positions=args.prefill_positions)
-        log(f"causal prefill of the first {pre['positions']} keys ({pre['queries']} queries): "
-            f"{pre['us']:.1f} us -> {pre['queries_per_s']:.3e} queries/s; keys read per query "
-            f"{pre['keys_read_mean']:.2f} on average (dense causal "
-            f"{pre['dense_causal_keys_mean']:.1f})")
-
-    thr = None
-    if not args.no_threshold:
-        thr = threshold_retrieval(tis, torch, w, Q, K, V, K_, args.warmup)
-        log(f"bounding spheres: radii {thr['radii_us']:.1f} us ({thr['radii_gbs']:.0f} GB/s on "
-            f"{thr['radii_bytes'] / 1e6:.1f} MB); " + "; ".join(
-                f"threshold at the {t['k']}-th best score: decode {t['decode_us']:.2f} us -> "
-                f"{t['queries_per_s']:.3e} queries/s, leaves kept mean "
-                f"{t['leaves_kept_mean']:.1f} max {t['leaves_kept_max']} of {w.n_leaves}, "
-                f"overflow {t['overflow']}"
-                for t in thr["thresholds"]))
-
-    bf = None
-    if not args.no_bf16_summaries:
-        bf = {}
-        for sd in ("bf16", "fp8"):
-            r = reduced_summaries(tis, torch, w, Q, K, V, K_, args.warmup, sd)
-            bf[sd] = r
-            log(f"{sd} summaries: step {r['step_us']:.1f} us ({r['queries_per_s_step']:.3e} "
-                f"queries/s); build {r['build_us']:.2f} us ({r['build_gbs']:.0f} GB/s); decode "
-                f"{r['decode_us']:.2f} us -> {r['decode_queries_per_s']:.3e} queries/s, "
-                f"{r['decode_gbs']:.0f} GB/s ({r['decode_frac']:.1%}) on "
-                f"{r['decode_bytes'] / 1e6:.2f} MB")
-
-    traffic = load_traffic(w.name)
-
-    cache = None
-    if not args.no_cache_loop:
-        cache = cache_decode_loop(tis, w, K, V, Q, K_, args.warmup)
-        log(f"growing cache: prefill append of {cache['prefill_keys']} keys/head "
-            f"{cache['prefill_us']:.1f} us ({cache['prefill_gbs']:.1f} GB/s); append of 1 key "
-            f"{cache['append1_us']:.2f} us; decode {cache['decode_us']:.2f} us; decode step "
-            f"(append + decode) {cache['step_us']:.2f} us -> {cache['queries_per_s']:.3e} queries/s; "
-            f"fused step {cache['fused_step_us']:.2f} us -> "
-            f"{cache['fused_queries_per_s']:.3e} queries/s")
+    extras = {}
+    if not args.no_extras:
+        extras["causal_prefill"] = causal_prefill_bench(tis, torch, w, Q, K, V, K_,
+                                                        max_positions=args.prefill_positions)
+        p = extras["causal_prefill"]
+        log(f"causal prefill of the first {p['positions']} keys ({p['queries']} queries): "
+            f"{p['us']:.1f} us -> {p['queries_per_s']:.3e} queries/s; keys read per query "
+            f"{p['keys_read_mean']:.2f} (dense causal {p['dense_causal_keys_mean']:.1f})")
+        extras["threshold_retrieval"] = threshold_retrieval(tis, torch, w, Q, K, V, K_)
+        t = extras["threshold_retrieval"]
+        log(f"bounding spheres: radii {t['radii_us']:.1f} us; " + "; ".join(
+            f"k={r['k']}: decode {r['decode_us']:.2f} us, leaves kept {r['leaves_kept_mean']:.1f}"
+            f", overflow {r['overflow']}" for r in t["thresholds"]))
+        extras["reduced_summaries"] = {sd: reduced_summaries(tis, torch, w, Q, K, V, sd)
+                                       for sd in ("bf16", "fp8")}
+        for sd, r in extras["reduced_summaries"].items():
+            log(f"{sd} summaries (warm): build {r['build_us']:.1f} us, decode {r['decode_us']:.2f}"
+                f" us ({r['decode_frac']:.1%} on {r['decode_bytes'] / 1e6:.2f} MB)")
+        extras["cache_decode_loop"] = cache_decode_loop(tis, torch, w, K, V, Q, K_)
+        c = extras["cache_decode_loop"]
+        if c:
+            log(f"growing cache: prefill append {c['prefill_us']:.1f} us; append 1 "
+                f"{c['append1_us']:.2f} us; decode {c['decode_us']:.2f} us; fused step "
+                f"{c['fused_step_us']:.2f} us")
 
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
         cpu = cpu_baseline(w, x)
         log(f"cpu oracle {cpu['value']:.2f} queries/s ({cpu['sample']})")
+    del x, Q, K, V, plan
+    torch.cuda.empty_cache()
 
+    others = {}
+    names = [] if args.others in ("", "none") else [n for n in args.others.split(",") if n]
+    for k, name in enumerate(names, start=1):
+        r, bufs = measure_workload(tis, torch, probes, workloads.get(name), ceil_gbs,
+                                   hop["hbm_cold"], reps=10, index=k)
+        others[name] = r
+        del bufs
+        torch.cuda.empty_cache()
+
+    d = head["decode"]
     line = {
-        "metric": "decode queries/sec + achieved HBM GB/s (% roofline) at N=32K\u20131M keys",
-        "value": w.queries / (ms_step * 1e-3),
+        "metric": "decode queries/sec + achieved HBM GB/s (% roofline) at N=32K–1M keys",
+        "value": w.queries / (step["step_us_mean"] * 1e-6),
         "unit": "queries/s",
         "n_gpus": 1,
         "steps": K_,
         "warmup": args.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": step["step_us_mean"] * 1e-3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 inputs; fp64 build sums and route scores; fp32 attention"
-        if w.dtype == "bf16" else "f32 inputs; fp64 build sums and route scores; fp32 attention",
-        "data": "synthetic (seeded clustered-Gaussian keys, see workloads.py)",
+        "dtype": "bf16 inputs; fp64 build sums and route scores; fp32 attention",
+        "data": "synthetic (seeded clustered-Gaussian keys, see workloads/__init__.py)",
         "config": {"workload": w.name, "batch": w.batch, "q_heads": w.q_heads,
                    "kv_heads": w.kv_heads, "head_dim": w.head_dim, "n_keys": w.n_keys,
                    "branching": w.branching, "leaf_block": w.leaf_block, "levels": w.levels,
                    "beam": w.beam,
-                   "step": "tree_build + tree_decode (tree_route and tree_attend in one launch)"},
-        "roofline": {"kernel": "tree_build", "bound": "hbm", "achieved": build_gbs,
+                   "step": "tree_build + tree_decode (tree_route and tree_attend in one launch)",
+                   "cache_state": "cold: a 1 GiB streaming read before each timed step, not "
+                                  "counted (the K steps, each after its read, are replayed "
+                                  "from one graph between events; the same K reads alone are "
+                                  "timed the same way and subtracted)"},
+        "roofline": {"kernel": "k_build (tree_build)", "bound": "hbm", "achieved": build_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": build_gbs / HBM_PEAK_GBS,
-                     "traffic": traffic},
-        "decode": {"regime": "fused route + attend launches back to back on the step's data",
-                   "us": decode_s * 1e6, "queries_per_s": w.queries / decode_s,
-                   "gbs": dec_bytes / decode_s / 1e9,
-                   "frac": dec_bytes / decode_s / 1e9 / HBM_PEAK_GBS,
-                   "in_step_us": ms_step * 1e3 - t_build.mean() * 1e6,
-                   "step_us_separate_calls": ms_step_separate * 1e3,
-                   "step_us_graph_replay": ms_step_graph * 1e3,
-                   "route_us": t_route.mean() * 1e6, "attend_us": t_attend.mean() * 1e6,
-                   "attend_gbs_per_query_bytes": by["attend"] / t_attend.mean() / 1e9,
-                   "attend_gbs_distinct_blocks": attend_dedup / t_attend.mean() / 1e9,
-                   "bytes_per_query_sum": dec_bytes, "bytes_distinct": dec_dedup,
-                   "gbs_distinct": dec_dedup / decode_s / 1e9,
-                   "frac_distinct": dec_dedup / decode_s / 1e9 / HBM_PEAK_GBS,
-                   "cache_states": dict(states, regime="cold: 1 GiB read first; steady: cold, "
-                                        "then the summaries read once; *_lone_us: median of "
-                                        "30 lone launches between events; *_cold_us and "
-                                        "*_steady_us: back-to-back duration + (lone in that "
-                                        "state - lone warm)")},
+                     "traffic": load_traffic(w.name), "regime": "cold (caches emptied first)",
+                     "launch_us_mean": head["build"]["cold_us"],
+                     "warm_frac": head["build"]["warm_frac"],
+                     "read_ceiling_frac": build_gbs / ceil_gbs},
+        "decode": {"queries_per_s_cold": d["cold"]["queries_per_s"],
+                   "queries_per_s_steady": d["steady"]["queries_per_s"],
+                   "queries_per_s_warm": d["warm"]["queries_per_s"],
+                   "frac_cold": d["cold"]["frac"], "frac_steady": d["steady"]["frac"],
+                   "frac_warm": d["warm"]["frac"],
+                   "frac_distinct_cold": d["cold"]["frac_distinct"],
+                   "regime_note": "cold: caches emptied; steady: emptied, then the summaries "
+                                  "read once (a decode loop keeping the tree hot); warm: "
+                                  "back-to-back launches replayed from a graph"},
+        "ceilings": {"read_gbs": ceil, "dependent_load_us": hop},
+        "workloads": dict({w.name: head}, **others),
         "cpu_baseline": cpu,
-        "cache_decode_loop": cache,
-        "reduced_summaries": bf,
-        "threshold_retrieval": thr,
-        "causal_prefill": pre,
     }
+    line.update(extras)
     print(json.dumps(line), flush=True)
     return 0
 

@@ -302,6 +302,36 @@ tis_status tis_tree_decode_threshold(const void *Q, const void *K, const void *V
                                      int32_t *indices, int32_t *counts, void *workspace,
                                      size_t workspace_bytes, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Measurement probes (no part of the method)
+ *
+ * The benchmark reports each kernel's roofline fraction beside what the
+ * memory system gives the same access pattern on the machine at hand; these
+ * two calls measure it.  The caller times them (events around the call).
+ * --------------------------------------------------------------------- */
+
+/* Reads every 16-byte chunk of buf[0, bytes) once: 16-byte loads, eight in
+ * flight a lane, over up to 16,384 workgroups of 256 threads (the streaming
+ * pattern of the build and the gather).  nontemporal != 0 marks the loads as
+ * streaming.  Nothing is written except, when the XOR of all the data
+ * equals 0x9e3779b9, that value to sink[0] (which keeps the loads live).
+ * Reading a buffer larger than the caches also empties them of everything
+ * else without leaving dirty lines, which is how the benchmark prepares its
+ * cold-cache timings.  buf: device, 16-byte aligned, bytes a positive
+ * multiple of 16; sink: device, 4 bytes.  TIS_E_NULL / TIS_E_ALIGN /
+ * TIS_E_SHAPE otherwise. */
+tis_status tis_probe_read(const void *buf, size_t bytes, int nontemporal, uint32_t *sink,
+                          void *stream);
+
+/* One lane follows the chain i = next[i] for `hops` steps from `start` (an
+ * index at or past n_elems restarts the chain at 0, so every load stays in
+ * the buffer) and writes the last index to out[0].  Timed against hops = 0,
+ * it gives the latency of one dependent load to wherever the chain's
+ * footprint lives.  next: device uint32 [n_elems], n_elems >= 1; out: device,
+ * 4 bytes; 0 <= hops.  TIS_E_NULL / TIS_E_SHAPE otherwise. */
+tis_status tis_probe_chase(const uint32_t *next, size_t n_elems, uint32_t start, int hops,
+                           uint32_t *out, void *stream);
+
 /* Message for the last non-OK status returned on the calling thread. */
 const char *tis_last_error(void);
 

@@ -67,8 +67,9 @@ def test_workspace_bytes(lib):
     assert lib.tis_build_workspace_bytes(4, 8, 32768, 128, 8, 64, 3) == 0
     # 256K keys, 2 x 8 heads: chunks at level 2
     assert lib.tis_build_workspace_bytes(2, 8, 262144, 128, 8, 64, 4) == 16 * 64 * 128 * 8
-    # 1M keys, 8 heads: chunks at level 2 (64 leaves per wave, 8 waves per workgroup)
-    assert lib.tis_build_workspace_bytes(1, 8, 1 << 20, 128, 8, 32, 5) == 8 * 64 * 128 * 8
+    # 1M keys, 8 heads: chunks at level 3 (8 leaves per wave, 8 waves per workgroup:
+    # the deepest plan whose wave-level rows fit the LDS staging), sums of levels 2, 3
+    assert lib.tis_build_workspace_bytes(1, 8, 1 << 20, 128, 8, 32, 5) == 8 * (64 + 512) * 128 * 8
     # a single-level tree needs none
     assert lib.tis_build_workspace_bytes(1, 1, 64, 128, 16, 4, 1) == 0
     # invalid geometry -> 0
@@ -613,3 +614,33 @@ def test_struct_layout_matches_the_header(tmp_path):
         assert got[(cname, "size")] == ctypes.sizeof(py), cname
         for f, _ in py._fields_:
             assert got[(cname, f)] == getattr(py, f).offset, (cname, f)
+
+
+# ------------------------------------------------- measurement probes --
+@pytest.mark.parametrize("kw,status", [
+    (dict(buf=None), _lib.TIS_E_NULL),
+    (dict(sink=None), _lib.TIS_E_NULL),
+    (dict(buf=FAKE + 8), _lib.TIS_E_ALIGN),
+    (dict(nbytes=0), _lib.TIS_E_SHAPE),
+    (dict(nbytes=24), _lib.TIS_E_SHAPE),
+])
+def test_probe_read_rejects(lib, kw, status):
+    a = dict(buf=FAKE, nbytes=1 << 20, nt=0, sink=FAKE)
+    a.update(kw)
+    assert lib.tis_probe_read(a["buf"], a["nbytes"], a["nt"], a["sink"], None) == status
+    assert lib.tis_last_error().decode().startswith("tis_probe_read")
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(nxt=None), _lib.TIS_E_NULL),
+    (dict(out=None), _lib.TIS_E_NULL),
+    (dict(nxt=FAKE + 2), _lib.TIS_E_ALIGN),
+    (dict(n=0), _lib.TIS_E_SHAPE),
+    (dict(n=1 << 32), _lib.TIS_E_SHAPE),
+    (dict(hops=-1), _lib.TIS_E_SHAPE),
+])
+def test_probe_chase_rejects(lib, kw, status):
+    a = dict(nxt=FAKE, n=1024, start=0, hops=10, out=FAKE)
+    a.update(kw)
+    assert lib.tis_probe_chase(a["nxt"], a["n"], a["start"], a["hops"], a["out"], None) == status
+    assert lib.tis_last_error().decode().startswith("tis_probe_chase")

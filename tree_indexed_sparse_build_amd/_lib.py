@@ -94,6 +94,8 @@ SIGNATURES = {
     "tis_causal_prefill_workspace_bytes": (_c_size, [_c_int] * 10),
     "tis_causal_prefill": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, ctypes.POINTER(TisCacheTree),
                                     _c_int, _c_float, _vp, _vp, _vp, _c_size, _vp]),
+    "tis_probe_read": (_c_int, [_vp, _c_size, _c_int, _vp, _vp]),
+    "tis_probe_chase": (_c_int, [_vp, _c_size, ctypes.c_uint32, _c_int, _vp, _vp]),
     "tis_last_error": (ctypes.c_char_p, []),
     "tis_version": (ctypes.c_char_p, []),
 }

@@ -219,8 +219,7 @@ tis_status tis_tree_build(const void *K, tis_dtype dtype, int batch, int kv_head
   a.levels = levels;
   a.root_level = p.root_level;
   a.wave_depth = p.wave_depth;
-  a.stream_loads = static_cast<double>(heads) * n_keys * head_dim * (dtype == TIS_BF16 ? 2 : 4) >
-                   static_cast<double>(tis::kStreamLoadBytes);
+  a.stream_loads = 1;  // K is read once: streaming loads, whatever its size
   a.top_rows = 1;
   for (int l = 2; l < p.root_level; ++l) a.top_rows *= branching;
   a.wave_leaves = 1;
@@ -1265,5 +1264,31 @@ tis_status tis_tree_decode_threshold(const void *Q, const void *K, const void *V
 const char *tis_last_error(void) { return g_err; }
 
 const char *tis_version(void) { return "tis 0.1.0 gfx950"; }
+
+// ------------------------------------------------- measurement probes --
+
+tis_status tis_probe_read(const void *buf, size_t bytes, int nontemporal, uint32_t *sink,
+                          void *stream) {
+  if (!buf || !sink) return fail(TIS_E_NULL, "tis_probe_read: buf and sink are required");
+  if (!aligned(buf, 16) || !aligned(sink, 4))
+    return fail(TIS_E_ALIGN, "tis_probe_read: buf needs 16-byte alignment, sink 4-byte");
+  if (bytes == 0 || bytes % 16 != 0)
+    return fail(TIS_E_SHAPE, "tis_probe_read: bytes %zu is not a positive multiple of 16", bytes);
+  return hip_status(tis::launch_probe_read(buf, bytes, nontemporal != 0, sink,
+                                           static_cast<hipStream_t>(stream)),
+                    "tis_probe_read launch");
+}
+
+tis_status tis_probe_chase(const uint32_t *next, size_t n_elems, uint32_t start, int hops,
+                           uint32_t *out, void *stream) {
+  if (!next || !out) return fail(TIS_E_NULL, "tis_probe_chase: next and out are required");
+  if (!aligned(next, 4) || !aligned(out, 4))
+    return fail(TIS_E_ALIGN, "tis_probe_chase: next and out need 4-byte alignment");
+  if (n_elems == 0 || n_elems > 0xffffffffull || hops < 0)
+    return fail(TIS_E_SHAPE, "tis_probe_chase: need 1 <= n_elems < 2^32 and hops >= 0");
+  return hip_status(tis::launch_probe_chase(next, n_elems, start, hops, out,
+                                            static_cast<hipStream_t>(stream)),
+                    "tis_probe_chase launch");
+}
 
 }  // extern "C"

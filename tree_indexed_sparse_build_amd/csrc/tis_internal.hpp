@@ -22,7 +22,7 @@ enum class Dt : int { F32 = 0, BF16 = 1, FP8 = 2 };  // FP8: summaries only
 // workspace and one small kernel per level computes levels r-1 .. 1.
 constexpr int kMaxWaveDepth = 3;
 constexpr size_t kTopLdsBytes = 64 * 1024;     // LDS budget of the one-launch top levels
-constexpr size_t kStreamLoadBytes = 384u << 20;  // K larger than this: streaming loads
+constexpr size_t kStageLdsBytes = 64 * 1024;   // LDS budget of the build's staged rows
 
 struct BuildArgs {
   const void *K;
@@ -37,6 +37,8 @@ struct BuildArgs {
   int wave_depth;        // kw
   uint32_t pow2_levels;  // bit l set: M_l = N / n_l is a power of two
   int stream_loads;      // nonzero: K loads carry the non-temporal hint
+  int stage;             // nonzero: the wave-level summary rows wait in LDS
+                         // and leave in one burst after the last K load
   int64_t top_rows;      // b^(r-2): level r-1 nodes under one level-1 node
   int64_t n_at[kMaxLevels + 1];            // b^l
   int64_t chunks_at_level[kMaxLevels + 1]; // B*Hkv*b^l
@@ -56,6 +58,7 @@ struct BuildPlan {
   size_t workspace_bytes;
 };
 
+int64_t stage_rows(int64_t nw, int64_t branching, int kw);
 bool plan_build(int64_t heads, int head_dim, int branching, int leaf_block, int levels,
                 BuildPlan *plan);
 // dt: type of K; sdt: type the summaries are stored in
@@ -275,5 +278,11 @@ hipError_t launch_prefill(Dt dt, Dt sdt, int head_dim, const RouteArgs &ra, cons
 int prefill_tile_heads(int group, int beam, int head_dim, int elem_bytes);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ------------------------------------------------- measurement probes --
+hipError_t launch_probe_read(const void *buf, uint64_t bytes, bool nontemporal, uint32_t *sink,
+                             hipStream_t s);
+hipError_t launch_probe_chase(const uint32_t *next, uint64_t n, uint32_t start, int hops,
+                              uint32_t *out, hipStream_t s);
 
 }  // namespace tis
