@@ -225,15 +225,26 @@ def trace_summary(db_path: str, out_path: str, title: str, command: str,
              "min | max |",
              "|---|---|---|---|---|---|---|---|---|"]
     order = {n: i for i, n in enumerate(["-"] + names)}
+    # "{workload}" in out_path: one file per workload segment
+    outs = {n: out_path.replace("{workload}", n) for n in names} if "{workload}" in out_path \
+        else None
+    body = {}
     for (seg, short, wgs, wx, before), ds in sorted(
             groups.items(), key=lambda kv: (order.get(kv[0][0], 99), -sum(kv[1]))):
         if not (short.startswith("k_") or "probe" in short):
             continue
-        lines.append(f"| {seg} | `{short}` | {wgs} x {wx} | {before} | {len(ds)} | "
-                     f"{statistics.fmean(ds):.2f} | {statistics.median(ds):.2f} | {min(ds):.2f} | "
-                     f"{max(ds):.2f} |")
-    with open(out_path, "w") as f:
-        f.write("\n".join(lines) + "\n")
+        body.setdefault(seg, []).append(
+            f"| {seg} | `{short}` | {wgs} x {wx} | {before} | {len(ds)} | "
+            f"{statistics.fmean(ds):.2f} | {statistics.median(ds):.2f} | {min(ds):.2f} | "
+            f"{max(ds):.2f} |")
+    if outs is None:
+        with open(out_path, "w") as f:
+            f.write("\n".join(lines + [r for seg in body for r in body[seg]]) + "\n")
+        return
+    for n, path in outs.items():
+        head = [ln.replace(title, f"{title}: {n}") if ln == f"# {title}" else ln for ln in lines]
+        with open(path, "w") as f:
+            f.write("\n".join(head + body.get(n, [])) + "\n")
 
 
 # --------------------------------------------------------------- probes --
