@@ -30,6 +30,21 @@ template <typename T, int D> struct AttendGeom {
 
 constexpr int kPartHeader = 4;  // m, l, two pad words: keeps acc 16-byte aligned
 
+// fp32 dot product of the 8 bf16 values of a and of b (16 bytes each, pairs
+// in dwords): four dot2 instructions, each adding two bf16 x bf16 products
+// (exact in fp32) to the running fp32 sum, with no unpacking of the operands.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ inline float dot8_bf16(uint4 a, uint4 b) {
+  float s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.x),
+                                            __builtin_bit_cast(bf16x2_t, b.x), 0.f, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.y),
+                                      __builtin_bit_cast(bf16x2_t, b.y), s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.z),
+                                      __builtin_bit_cast(bf16x2_t, b.z), s, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.w),
+                                         __builtin_bit_cast(bf16x2_t, b.w), s, false);
+}
+
 // MW: the most waves of the workgroups that use it
 template <typename T, int D, int MW = kAttendMaxWaves> struct AttendShared {
   float p[MW][AttendGeom<T, D>::RB];
@@ -130,12 +145,17 @@ __device__ void attend_query(const AttendArgs &a, AttendShared<T, D, MW> &sh, in
       float part[U];
 #pragma unroll
       for (int i = 0; i < U; ++i) {
-        float k[E];
-        Vec16<T>::unpack(kv[i], k);
-        float dot = 0.f;
+        if constexpr (__is_same(T, bf16_bits)) {
+          // bf16 keys and query: the pairs as stored, into gfx950's dot2
+          part[i] = dot8_bf16(kv[i], qraw);
+        } else {
+          float k[E];
+          Vec16<T>::unpack(kv[i], k);
+          float dot = 0.f;
 #pragma unroll
-        for (int e = 0; e < E; ++e) dot = fmaf(q[e], k[e], dot);
-        part[i] = dot;
+          for (int e = 0; e < E; ++e) dot = fmaf(q[e], k[e], dot);
+          part[i] = dot;
+        }
       }
       sc = group_transpose_reduce<U, LPR>(part, lane);
     }
