@@ -43,10 +43,16 @@
  *   device workspace (16-byte aligned) of at least the size the matching
  *   *_workspace_bytes query returns.  A size of 0 means none is needed and
  *   NULL is accepted.  The build keeps fp64 node sums there when its second
- *   kernel runs.  Attend and decode keep partial softmax states there when a
- *   query is split over several workgroups (few queries, long key sets).
- *   Contents on entry never matter.  Calls that share a workspace must be
- *   ordered (same stream or synchronised).
+ *   kernel runs; their contents on entry never matter.  Attend and decode
+ *   use theirs when a query is split over several workgroups (few queries,
+ *   long key sets): the first 1,024 bytes hold one arrival counter per query
+ *   (the last workgroup of a query to finish merges the parts), the partial
+ *   softmax states follow.  Those 1,024 bytes must be zero before a
+ *   workspace's first attend or decode (allocate it zeroed, or clear it
+ *   once); every call that completes leaves them zero, whatever its shape,
+ *   so one workspace serves any sequence of calls.  The rest never matters
+ *   on entry.  Calls that share a workspace must be ordered (same stream or
+ *   synchronised).
  */
 #ifndef TIS_H_
 #define TIS_H_
@@ -223,7 +229,9 @@ size_t tis_decode_workspace_bytes(int batch, int q_heads, int head_dim, int beam
  * is enqueued.  All calls on one GPU share its scratch, whatever their
  * stream: calls that may overlap on one GPU race and give undefined
  * results, so order them (one stream, or synchronise between them).  The
- * scratch holds what the last call left; no call depends on its contents.
+ * scratch is laid out as a workspace (see Workspaces): its arrival counters
+ * are zero when the library is loaded and every call leaves them zero; the
+ * rest holds what the last call left and no call depends on it.
  * The first call on a device looks up the scratch's address there (no
  * allocation); a failure of that lookup returns TIS_E_HIP.
  */

@@ -77,11 +77,14 @@ def test_workspace_bytes(lib):
     # attend and decode: 128 queries run one workgroup each, no workspace
     assert lib.tis_attend_workspace_bytes(4, 32, 128, 8, 64) == 0
     assert lib.tis_decode_workspace_bytes(4, 32, 128, 8, 64) == 0
-    # 32 queries with 512 keys each: still one workgroup per query
-    assert lib.tis_attend_workspace_bytes(1, 32, 128, 16, 32) == 0
-    # 32 queries with 64 x 64 keys each: 8 workgroups per query keep partial states
-    assert lib.tis_attend_workspace_bytes(1, 32, 128, 64, 64) == 32 * 8 * (128 + 4) * 4
-    assert lib.tis_decode_workspace_bytes(1, 32, 128, 64, 64) == 32 * 8 * (128 + 4) * 4
+    # 32 queries with 512 keys each: 8 workgroups per query
+    assert lib.tis_attend_workspace_bytes(1, 32, 128, 16, 32) == 1024 + 32 * 8 * (128 + 4) * 4
+    # 32 queries with 256 keys each: one workgroup per query
+    assert lib.tis_attend_workspace_bytes(1, 32, 128, 8, 32) == 0
+    # 32 queries with 64 x 64 keys each: 8 workgroups per query keep partial
+    # states after the 1 KiB of arrival counters
+    assert lib.tis_attend_workspace_bytes(1, 32, 128, 64, 64) == 1024 + 32 * 8 * (128 + 4) * 4
+    assert lib.tis_decode_workspace_bytes(1, 32, 128, 64, 64) == 1024 + 32 * 8 * (128 + 4) * 4
     # a short key set is never split
     assert lib.tis_attend_workspace_bytes(1, 4, 64, 2, 16) == 0
 

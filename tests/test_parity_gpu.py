@@ -298,22 +298,36 @@ def test_full_size_workload(tis, name):
 
 def test_workspace_reuse_across_geometries(tis):
     """One cached workspace serves calls of different shapes in turn, and
-    contents left by earlier calls never leak into later results."""
+    contents left by earlier calls never leak into later results: beyond the
+    arrival counters of split queries (the first 1 KiB, zero between calls)
+    nothing in a workspace matters on entry, and every call leaves those
+    counters zero whatever its shape."""
     cases = [
         _custom("ws_a", "bf16", 4, 16, 4, 16, Hkv=2, G=2, seed=21),   # few queries, wide beam
         _custom("ws_b", "bf16", 4, 16, 4, 8, Hkv=2, G=16, seed=22),   # many queries
         _custom("ws_c", "bf16", 2, 8, 8, 4, d=64, Hkv=1, G=4, seed=23),  # deep: build climbs
         _custom("ws_d", "bf16", 8, 8, 3, 16, Hkv=4, G=8, seed=24),
+        _custom("ws_split", "bf16", 4, 64, 4, 64, Hkv=2, G=3, seed=26),  # 6 queries, split
         _custom("ws_a2", "bf16", 4, 16, 4, 16, Hkv=2, G=2, seed=25),
     ]
+    splits_seen = 0
     for w in cases:
         for ws in tis.ops._workspaces.values():
             ws.fill_(0x7F)  # garbage (large finite doubles) must not matter
+            ws[:1024].zero_()
+        splits_seen += tis.ops.lib().tis_decode_workspace_bytes(
+            w.batch, w.q_heads, w.head_dim, w.beam, w.leaf_block) > 0
         check_case(tis, w)
+        torch.cuda.synchronize()
+        for kind in ("attend", "decode"):
+            for (_, k), ws in tis.ops._workspaces.items():
+                if k == kind and ws.numel() >= 1024:
+                    assert not ws[:1024].any(), f"{w.name}: {kind} counters left nonzero"
+    assert splits_seen >= 1
 
 
 GRAPH_CASES = [
-    _custom("graph_split", "bf16", 4, 64, 4, 64, Hkv=2, G=3, seed=31),   # split + combine
+    _custom("graph_split", "bf16", 4, 64, 4, 64, Hkv=2, G=3, seed=31),   # split, merged in the kernel
     _custom("graph_deep", "bf16", 2, 4, 9, 6, d=64, Hkv=3, G=1, seed=32),  # per-level build kernels
     workloads.small("deep_planted", levels=4, kv_heads=2),                # top-level build kernel
 ]

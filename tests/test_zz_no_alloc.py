@@ -45,7 +45,7 @@ def _w(name, b, L, lv, W, B, Hkv, G, seed):
 CALLS = [
     (_w("noalloc_split_big", 4, 64, 4, 64, B=2, Hkv=2, G=3, seed=41), True),    # 12 queries
     (_w("noalloc_split_small", 4, 64, 3, 64, B=1, Hkv=1, G=2, seed=42), True),  # 2 queries
-    (_w("noalloc_unsplit", 8, 64, 2, 8, B=2, Hkv=2, G=4, seed=43), False),
+    (_w("noalloc_unsplit", 8, 64, 2, 4, B=2, Hkv=2, G=4, seed=43), False),
 ]
 
 

@@ -5,11 +5,10 @@
 // exact softmax restricted to the tokens of the chosen blocks).
 //
 // One workgroup per query (or, when few queries would leave most CUs idle,
-// `splits` workgroups per query, each on a share of the slots, followed by a
-// small log-sum-exp combine kernel): it reads the query's slot list, applies
-// the slot rules (repeats count once, negatives are empty, out-of-range gives
-// NaN) and runs attend_query.  Parts meet through a kernel boundary, never
-// through atomics or device-scope fences.
+// `splits` workgroups per query, each on a share of the slots, the last of
+// them to finish merging the parts' states): it reads the query's slot
+// list, applies the slot rules (repeats count once, negatives are empty,
+// out-of-range gives NaN) and runs attend_query.
 #include "attend_query.hpp"
 
 namespace tis {
@@ -48,6 +47,7 @@ __global__ void __launch_bounds__(kAttendMaxWaves * 64) k_attend(AttendArgs a) {
                     ? a.part + (static_cast<int64_t>(qi) * a.splits + sp) * (D + kPartHeader)
                     : nullptr;
   attend_query<T, D>(a, sh, qi, qraw, s_idx + s0, s_use + s0, s1 - s0, s_bad != 0, part);
+  if (a.splits > 1) merge_parts<D>(a, qi);
 }
 
 }  // namespace
@@ -63,10 +63,12 @@ int attend_waves(int head_dim, Dt dt, int beam, int leaf_block) {
 }
 
 int attend_splits(int64_t queries, int beam, int leaf_block) {
-  // A split costs one more launch (~4.5 us on MI355X) and pays only when a
-  // query's own gather is long: >= 4096 keys (>= 1 MB of K and V at d = 128
-  // in bf16) and too few queries to give every CU a workgroup.
-  if (queries >= 128 || static_cast<int64_t>(beam) * leaf_block < 4096) return 1;
+  // A split query pays three dependent memory round trips at its end
+  // (the parts' stores, the arrival count, the merge's loads: ~1 us on
+  // MI355X).  Measured on decodes of 128 queries with 512 keys each, that is
+  // more than the gather on the idle half of the CUs saves; at 64 queries
+  // with 1,024 keys it saves 12% of the decode, at 32 with 512 keys 3%.
+  if (queries >= 128 || static_cast<int64_t>(beam) * leaf_block < 512) return 1;
   int s = 1;
   while (s * 2 <= beam && queries * s * 2 <= 256) s *= 2;
   return s;
@@ -74,16 +76,8 @@ int attend_splits(int64_t queries, int beam, int leaf_block) {
 
 size_t attend_workspace(int64_t queries, int head_dim, int splits) {
   if (splits <= 1) return 0;
-  return static_cast<size_t>(queries) * splits * (head_dim + kPartHeader) * sizeof(float);
-}
-
-hipError_t launch_combine(int head_dim, const AttendArgs &a, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(a.queries));
-  if (head_dim == 128)
-    hipLaunchKernelGGL((k_combine<128>), grid, dim3(128), 0, s, a.part, a.O, a.splits);
-  else
-    hipLaunchKernelGGL((k_combine<64>), grid, dim3(64), 0, s, a.part, a.O, a.splits);
-  return hipGetLastError();
+  return kArriveBytes +
+         static_cast<size_t>(queries) * splits * (head_dim + kPartHeader) * sizeof(float);
 }
 
 hipError_t launch_attend(Dt dt, int head_dim, const AttendArgs &a, hipStream_t s) {
@@ -100,9 +94,7 @@ hipError_t launch_attend(Dt dt, int head_dim, const AttendArgs &a, hipStream_t s
     hipLaunchKernelGGL((k_attend<float, 64>), grid, block, 0, s, a);
   else
     return hipErrorInvalidValue;
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.splits <= 1) return e;
-  return launch_combine(head_dim, a, s);
+  return hipGetLastError();
 }
 
 }  // namespace tis

@@ -45,6 +45,18 @@ __device__ inline float dot8_bf16(uint4 a, uint4 b) {
                                          __builtin_bit_cast(bf16x2_t, b.w), s, false);
 }
 
+// Agent-scope (device-coherent) float stores and loads, for the partial
+// states of split queries, which another XCD may read.
+__device__ inline void store_coherent(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline float load_coherent(const float *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// s_waitcnt vmcnt(0): this wave's vector memory operations, the coherent
+// stores included, have completed
+__device__ inline void wait_vector_memory() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // MW: the most waves of the workgroups that use it
 template <typename T, int D, int MW = kAttendMaxWaves> struct AttendShared {
   float p[MW][AttendGeom<T, D>::RB];
@@ -234,10 +246,11 @@ __device__ void attend_query(const AttendArgs &a, AttendShared<T, D, MW> &sh, in
       }
     }
     if (part) {
-      part[kPartHeader + c] = num;
+      // device-coherent stores: the part that merges may run on another XCD
+      store_coherent(part + kPartHeader + c, num);
       if (c == 0) {
-        part[0] = mx;
-        part[1] = bad ? NAN : den;
+        store_coherent(part, mx);
+        store_coherent(part + 1, bad ? NAN : den);
       }
     } else {
       float r = mx == -INFINITY ? 0.f : num / den;
@@ -247,32 +260,78 @@ __device__ void attend_query(const AttendArgs &a, AttendShared<T, D, MW> &sh, in
   }
 }
 
-// Log-sum-exp merge of each query's `splits` partial states into row qi of
-// O: o = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s, M = max_s m_s;
-// zero if no part saw a key, NaN if any part is NaN.
-template <int D> __global__ void __launch_bounds__(D) k_combine(const float *part, float *O,
-                                                                 int splits) {
-  const int64_t qi = blockIdx.x;
-  const int c = threadIdx.x;
-  const float *pq = part + qi * splits * (D + kPartHeader);
-  float mx = -INFINITY;
-  bool bad = false;
-  for (int s = 0; s < splits; ++s) {
-    mx = fmaxf(mx, pq[s * (D + kPartHeader)]);
-    bad |= isnan(pq[s * (D + kPartHeader) + 1]);
+// The end of a split query's part, run by every thread of the part's
+// workgroup after attend_query has written the part's state: the part that
+// arrives last merges the query's `splits` states into row qi of O,
+// o = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s with M = max_s m_s
+// (zero if no part saw a key, NaN if any part is NaN), and sets the query's
+// arrival counter back to zero for the next call.
+//
+// The states travel through device-coherent (agent-scope) stores and loads,
+// which bypass the XCDs' private L2 state, so no L2 write-back or invalidate
+// is needed (a release fence at agent scope would write back the whole L2;
+// measured, that costs more than the split saves).  What orders a part's
+// stores before its arrival is the wait for their completion before the
+// barrier; the counter is an agent-scope atomic, and the last arriver's
+// loads are issued only after it has seen the count.  The merge issues the
+// loads of up to 8 parts at once: one memory round trip per 8 parts.
+template <int D> __device__ void merge_parts(const AttendArgs &a, int qi) {
+  constexpr int PB = 8;  // parts whose loads are in flight together
+  __shared__ int s_last;
+  const int tid = threadIdx.x;
+  if (tid < D) wait_vector_memory();  // the threads that stored the state
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned before = __hip_atomic_fetch_add(a.arrive + qi, 1u, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+    s_last = before == static_cast<unsigned>(a.splits - 1);
   }
-  float r = 0.f;
-  if (mx != -INFINITY) {
-    float num = 0.f, den = 0.f;
-    for (int s = 0; s < splits; ++s) {
-      const float *ps = pq + s * (D + kPartHeader);
-      const float ws = exp2f(ps[0] - mx);
-      den = fmaf(ws, ps[1], den);
-      num = fmaf(ws, ps[kPartHeader + c], num);
+  __syncthreads();
+  if (!s_last) return;
+  if (tid == 0) __hip_atomic_store(a.arrive + qi, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const float *pq = a.part + static_cast<int64_t>(qi) * a.splits * (D + kPartHeader);
+  for (int c = tid; c < D; c += blockDim.x) {
+    float M = -INFINITY, num = 0.f, den = 0.f;
+    bool bad = false;
+    for (int s0 = 0; s0 < a.splits; s0 += PB) {
+      float m[PB], l[PB], v[PB];
+#pragma unroll
+      for (int j = 0; j < PB; ++j) {
+        // parts past the last re-read the last one and are masked
+        const float *ps = pq + min(s0 + j, a.splits - 1) * (D + kPartHeader);
+        m[j] = load_coherent(ps);
+        l[j] = load_coherent(ps + 1);
+        v[j] = load_coherent(ps + kPartHeader + c);
+      }
+      float mb = M;
+#pragma unroll
+      for (int j = 0; j < PB; ++j) {
+        if (s0 + j >= a.splits) {
+          m[j] = -INFINITY;
+          l[j] = 0.f;
+          v[j] = 0.f;
+        }
+        bad |= isnan(l[j]);
+        mb = fmaxf(mb, m[j]);
+      }
+      if (mb != -INFINITY) {
+        // earlier batches' sums move to the new reference (2^-inf = 0 when
+        // there were none)
+        const float r = __builtin_amdgcn_exp2f(M - mb);
+        num *= r;
+        den *= r;
+#pragma unroll
+        for (int j = 0; j < PB; ++j) {
+          const float w = __builtin_amdgcn_exp2f(m[j] - mb);  // 0 for parts that saw no key
+          den = fmaf(w, l[j], den);
+          num = fmaf(w, v[j], num);
+        }
+        M = mb;
+      }
     }
-    r = num / den;
+    const float r = M == -INFINITY ? 0.f : num / den;
+    a.O[static_cast<int64_t>(qi) * D + c] = bad ? NAN : r;
   }
-  O[qi * D + c] = bad ? NAN : r;
 }
 
 }  // namespace tis

@@ -7,8 +7,8 @@
 // goes through memory and the step pays for one launch instead of two.  The
 // leaves are also written out (ascending) when the caller asks for them.
 // With few queries each query gets `splits` workgroups that all walk the
-// tree and each attend over a share of the kept leaves; a small combine
-// kernel merges their partial softmax states.
+// tree and each attend over a share of the kept leaves; the last of them to
+// finish merges their partial softmax states.
 //
 // Fused one-key append + decode over a growing cache (k_decode_append).
 // Adding key t = n0 to the tree changes one node per height: the node that
@@ -51,6 +51,7 @@ __device__ inline void decode_attend(const RouteArgs &ra, const AttendArgs &aa,
                     ? aa.part + (static_cast<int64_t>(qi) * aa.splits + sp) * (D + kPartHeader)
                     : nullptr;
   attend_query<T, D, CACHE>(aa, ash, qi, qraw, rsh.front + s0, nullptr, s1 - s0, false, part);
+  if (aa.splits > 1) merge_parts<D>(aa, qi);
 }
 
 template <typename T, typename S, int D, bool CACHE>
@@ -234,8 +235,7 @@ hipError_t launch_decode_append(Dt dt, Dt sdt, int head_dim, const RouteArgs &ra
   else
     e = sdt == Dt::BF16 ? launch_decode_append_ts<float, bf16_bits>(head_dim, ra, aa, ap, s)
                         : launch_decode_append_ts<float, float>(head_dim, ra, aa, ap, s);
-  if (e != hipSuccess || aa.splits <= 1) return e;
-  return launch_combine(head_dim, aa, s);
+  return e;
 }
 
 hipError_t launch_decode(Dt dt, Dt sdt, int head_dim, const RouteArgs &ra,
@@ -252,8 +252,7 @@ hipError_t launch_decode(Dt dt, Dt sdt, int head_dim, const RouteArgs &ra,
     e = sdt == Dt::BF16 ? launch_decode_ts<float, bf16_bits>(head_dim, ra, aa, s)
                         : launch_decode_ts<float, float>(head_dim, ra, aa, s);
   }
-  if (e != hipSuccess || aa.splits <= 1) return e;
-  return launch_combine(head_dim, aa, s);
+  return e;
 }
 
 }  // namespace tis

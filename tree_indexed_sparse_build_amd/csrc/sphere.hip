@@ -352,6 +352,7 @@ __global__ void __launch_bounds__(kThreshDecodeWaves * 64)
                     : nullptr;
   attend_query<T, D, false, true>(aa, ash, qi, qraw, sh.front[buf] + s0, nullptr, s1 - s0,
                                   kept < 0, part, static_cast<double>(sa.tau[qi]));
+  if (aa.splits > 1) merge_parts<D>(aa, qi);
 }
 
 // ------------------------------------------------------------- launches --
@@ -431,8 +432,7 @@ hipError_t launch_decode_threshold(Dt dt, Dt sdt, int head_dim, const RouteArgs 
   else
     e = sdt == Dt::BF16 ? launch_decode_threshold_ts<float, bf16_bits>(head_dim, ra, sa, aa, s)
                         : launch_decode_threshold_ts<float, float>(head_dim, ra, sa, aa, s);
-  if (e != hipSuccess || aa.splits <= 1) return e;
-  return launch_combine(head_dim, aa, s);
+  return e;
 }
 
 }  // namespace tis

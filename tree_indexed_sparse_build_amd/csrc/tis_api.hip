@@ -312,6 +312,7 @@ static tis_status plan_split(const char *who, int64_t queries, int head_dim, int
                              tis::AttendArgs *a) {
   a->splits = tis::attend_splits(queries, beam, leaf_block);
   a->part = nullptr;
+  a->arrive = nullptr;
   const size_t need = tis::attend_workspace(queries, head_dim, a->splits);
   if (need == 0) return TIS_OK;
   if (!workspace)
@@ -321,7 +322,8 @@ static tis_status plan_split(const char *who, int64_t queries, int head_dim, int
   if (workspace_bytes < need)
     return fail(TIS_E_WORKSPACE, "%s: workspace %zu bytes < %zu required", who, workspace_bytes,
                 need);
-  a->part = static_cast<float *>(workspace);
+  a->arrive = static_cast<unsigned *>(workspace);
+  a->part = reinterpret_cast<float *>(static_cast<unsigned char *>(workspace) + tis::kArriveBytes);
   return TIS_OK;
 }
 
@@ -1025,6 +1027,7 @@ tis_status tis_causal_prefill(const void *Q, const void *K, const void *V, tis_d
   aa.O = O;
   aa.splits = 1;
   aa.part = nullptr;
+  aa.arrive = nullptr;
   aa.queries = static_cast<int>(pq);
   aa.n_keys = tree->n_keys;
   aa.key_stride = tree->capacity;

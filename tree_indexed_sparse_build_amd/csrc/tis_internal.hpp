@@ -104,6 +104,7 @@ struct AttendArgs {
   const int32_t *indices;
   float *O;
   float *part;           // [queries][splits][d + 4] partial states when splits > 1
+  unsigned *arrive;      // [queries] parts of each query done so far (zero between calls)
   int splits;            // workgroups per query (1: no split, no workspace)
   int queries;           // B * Hq (< 2^31, checked by the host)
   int64_t n_keys;        // keys in use per head (leaf j holds [jL, min((j+1)L, n_keys)))
@@ -116,11 +117,16 @@ struct AttendArgs {
 
 int attend_waves(int head_dim, Dt dt, int beam, int leaf_block);
 // Workgroups per query: more than one only when few queries would leave most
-// CUs idle and each query gathers enough keys to share out.
+// CUs idle and each query gathers enough keys to share out.  A split call
+// has fewer than kSplitMaxQueries queries.
+constexpr int kSplitMaxQueries = 256;
 int attend_splits(int64_t queries, int beam, int leaf_block);
+// The workspace of a split call: the arrival counters of kSplitMaxQueries
+// queries (1 KiB, at offset 0 whatever the geometry, so that one workspace
+// serves calls of any shape), then the partial states.
+constexpr size_t kArriveBytes = kSplitMaxQueries * sizeof(unsigned);
 size_t attend_workspace(int64_t queries, int head_dim, int splits);
 hipError_t launch_attend(Dt dt, int head_dim, const AttendArgs &a, hipStream_t s);
-hipError_t launch_combine(int head_dim, const AttendArgs &a, hipStream_t s);
 
 // ---------------------------------------------------------------- decode --
 // Route and attend of each query in one workgroup (one launch).

@@ -62,7 +62,9 @@ def _stream(device: torch.device) -> int:
 
 
 # Workspaces, one per (device, kind), grown on demand and reused: calls are
-# ordered on the caller's stream, and no call expects particular contents.
+# ordered on the caller's stream.  They start zeroed: a split attend or
+# decode needs its arrival counters (the first 1 KiB) at zero on first use,
+# and every call leaves them so.
 _workspaces: Dict[Tuple[int, str], torch.Tensor] = {}
 
 
@@ -70,7 +72,7 @@ def _workspace(device: torch.device, kind: str, nbytes: int) -> torch.Tensor:
     key = (device.index if device.index is not None else torch.cuda.current_device(), kind)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
 
@@ -396,10 +398,10 @@ class DecodePlan:
         self.ws_build = (torch.empty(wsb, dtype=torch.uint8, device=K.device) if wsb
                          else None)
         wsa = L.tis_attend_workspace_bytes(B, Hq, d, beam, leaf_block)
-        self.ws_attend = (torch.empty(wsa, dtype=torch.uint8, device=K.device) if wsa
+        self.ws_attend = (torch.zeros(wsa, dtype=torch.uint8, device=K.device) if wsa
                           else None)
         wsd = L.tis_decode_workspace_bytes(B, Hq, d, beam, leaf_block)
-        self.ws_decode = (torch.empty(wsd, dtype=torch.uint8, device=K.device) if wsd
+        self.ws_decode = (torch.zeros(wsd, dtype=torch.uint8, device=K.device) if wsd
                           else None)
         self.indices = torch.empty((B, Hq, beam), dtype=torch.int32, device=K.device)
         self.out = torch.empty((B, Hq, d), dtype=torch.float32, device=K.device)
