@@ -42,17 +42,17 @@
  *   tis_tree_build, tis_tree_attend and tis_tree_decode take a caller-owned
  *   device workspace (16-byte aligned) of at least the size the matching
  *   *_workspace_bytes query returns.  A size of 0 means none is needed and
- *   NULL is accepted.  The build keeps fp64 node sums there when its second
- *   kernel runs; their contents on entry never matter.  Attend and decode
- *   use theirs when a query is split over several workgroups (few queries,
- *   long key sets): the first 1,024 bytes hold one arrival counter per query
- *   (the last workgroup of a query to finish merges the parts), the partial
- *   softmax states follow.  Those 1,024 bytes must be zero before a
- *   workspace's first attend or decode (allocate it zeroed, or clear it
- *   once); every call that completes leaves them zero, whatever its shape,
- *   so one workspace serves any sequence of calls.  The rest never matters
- *   on entry.  Calls that share a workspace must be ordered (same stream or
- *   synchronised).
+ *   NULL is accepted.  A workspace starts with arrival counters: the build's
+ *   first 16,384 bytes count the finished chunks of each level-1 subtree
+ *   (the last chunk of a subtree to finish climbs to level 1), attend's and
+ *   decode's first 1,024 bytes count the finished parts of each split query
+ *   (few queries, long key sets: the last part to finish merges them).  The
+ *   build's fp64 node sums and the split queries' partial softmax states
+ *   follow.  Those counter bytes must be zero before a workspace's first
+ *   call (allocate it zeroed, or clear it once); every call that completes
+ *   leaves them zero, whatever its shape, so one workspace serves any
+ *   sequence of calls of its kind.  The rest never matters on entry.  Calls
+ *   that share a workspace must be ordered (same stream or synchronised).
  */
 #ifndef TIS_H_
 #define TIS_H_

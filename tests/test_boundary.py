@@ -65,11 +65,12 @@ def test_workspace_bytes(lib):
     # the build keeps fp64 sums of levels 2..r, r = the level of its chunk roots
     # 32K keys, 4 x 8 heads: chunks are level-1 nodes (8 leaves per wave, 8 waves)
     assert lib.tis_build_workspace_bytes(4, 8, 32768, 128, 8, 64, 3) == 0
-    # 256K keys, 2 x 8 heads: chunks at level 2
-    assert lib.tis_build_workspace_bytes(2, 8, 262144, 128, 8, 64, 4) == 16 * 64 * 128 * 8
+    # 256K keys, 2 x 8 heads: chunks at level 2 (16 KiB of arrival counters
+    # come first)
+    assert lib.tis_build_workspace_bytes(2, 8, 262144, 128, 8, 64, 4) == 16384 + 16 * 64 * 128 * 8
     # 1M keys, 8 heads: chunks at level 3 (8 leaves per wave, 8 waves per workgroup:
     # the deepest plan whose wave-level rows fit the LDS staging), sums of levels 2, 3
-    assert lib.tis_build_workspace_bytes(1, 8, 1 << 20, 128, 8, 32, 5) == 8 * (64 + 512) * 128 * 8
+    assert lib.tis_build_workspace_bytes(1, 8, 1 << 20, 128, 8, 32, 5) == 16384 + 8 * (64 + 512) * 128 * 8
     # a single-level tree needs none
     assert lib.tis_build_workspace_bytes(1, 1, 64, 128, 16, 4, 1) == 0
     # invalid geometry -> 0

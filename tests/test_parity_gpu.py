@@ -129,11 +129,12 @@ EDGE = [
     _custom("full_beam", "f32", 2, 8, 4, 16, d=64),
     # long leaf blocks (several batches of rows per wave)
     _custom("long_leaf", "bf16", 2, 200, 2, 2),
-    # deep binary tree: the levels above the chunk roots take the small
-    # per-level kernels
+    # deep binary tree: the last chunk of each level-1 subtree climbs 4
+    # levels above the chunk roots
     _custom("deep_binary", "bf16", 2, 4, 9, 6, d=64, Hkv=3, G=1),
     # the deepest tree the library takes: 16 levels (binary, leaf blocks of
-    # one key, 65,536 keys)
+    # one key, 65,536 keys); a level-1 subtree too wide for the build's LDS,
+    # so the levels above the chunk roots take one small launch each
     _custom("max_levels_16", "f32", 2, 1, 16, 3, d=64, Hkv=1, G=2),
     # many heads, GQA group 8, batch 3
     _custom("gqa8_batch3", "bf16", 4, 32, 3, 6, B=3, Hkv=2, G=8),
@@ -230,7 +231,7 @@ def test_errors_through_binding(tis):
 # -------------------------------------------------------------- full size --
 # bfloat16 summaries: the build rounds every mean straight from fp64 and the
 # walk reads 8 summary elements per 16-byte load (both head dims, the
-# single-launch, top-level and per-level builds, splits)
+# single-launch builds, builds that climb above the chunk roots, splits)
 BF16_SUMMARY_CASES = [
     workloads.small("gqa_32k", levels=2, kv_heads=2),
     workloads.small("deep_planted", levels=4, kv_heads=2),
@@ -249,8 +250,8 @@ def test_bf16_summaries(tis, w):
 
 
 # fp8 summaries (full tree): per-row scales from a wave-wide max in the
-# build's leaf and node stores, the LDS levels, the top-level and per-level
-# kernels; the walk reads 8 codes a lane and scales each row's partial dot
+# build's leaf and node stores, the LDS levels and the climb above the chunk
+# roots; the walk reads 8 codes a lane and scales each row's partial dot
 FP8_SUMMARY_CASES = [
     workloads.small("gqa_32k", levels=2, kv_heads=2),
     workloads.small("deep_planted", levels=4, kv_heads=2),
@@ -299,9 +300,9 @@ def test_full_size_workload(tis, name):
 def test_workspace_reuse_across_geometries(tis):
     """One cached workspace serves calls of different shapes in turn, and
     contents left by earlier calls never leak into later results: beyond the
-    arrival counters of split queries (the first 1 KiB, zero between calls)
-    nothing in a workspace matters on entry, and every call leaves those
-    counters zero whatever its shape."""
+    arrival counters (the first 16 KiB of a build workspace, 1 KiB of an
+    attend or decode one, zero between calls) nothing in a workspace matters
+    on entry, and every call leaves those counters zero whatever its shape."""
     cases = [
         _custom("ws_a", "bf16", 4, 16, 4, 16, Hkv=2, G=2, seed=21),   # few queries, wide beam
         _custom("ws_b", "bf16", 4, 16, 4, 8, Hkv=2, G=16, seed=22),   # many queries
@@ -310,26 +311,30 @@ def test_workspace_reuse_across_geometries(tis):
         _custom("ws_split", "bf16", 4, 64, 4, 64, Hkv=2, G=3, seed=26),  # 6 queries, split
         _custom("ws_a2", "bf16", 4, 16, 4, 16, Hkv=2, G=2, seed=25),
     ]
-    splits_seen = 0
+    counters = {"build": 16384, "attend": 1024, "decode": 1024}
+    splits_seen = climbs_seen = 0
     for w in cases:
-        for ws in tis.ops._workspaces.values():
+        for (_, kind), ws in tis.ops._workspaces.items():
             ws.fill_(0x7F)  # garbage (large finite doubles) must not matter
-            ws[:1024].zero_()
-        splits_seen += tis.ops.lib().tis_decode_workspace_bytes(
+            ws[:counters.get(kind, 0)].zero_()
+        lib = tis.ops.lib()
+        splits_seen += lib.tis_decode_workspace_bytes(
             w.batch, w.q_heads, w.head_dim, w.beam, w.leaf_block) > 0
+        climbs_seen += lib.tis_build_workspace_bytes(
+            w.batch, w.kv_heads, w.n_keys, w.head_dim, w.branching, w.leaf_block, w.levels) > 0
         check_case(tis, w)
         torch.cuda.synchronize()
-        for kind in ("attend", "decode"):
-            for (_, k), ws in tis.ops._workspaces.items():
-                if k == kind and ws.numel() >= 1024:
-                    assert not ws[:1024].any(), f"{w.name}: {kind} counters left nonzero"
-    assert splits_seen >= 1
+        for (_, kind), ws in tis.ops._workspaces.items():
+            n = min(counters.get(kind, 0), ws.numel())
+            assert not ws[:n].any(), f"{w.name}: {kind} counters left nonzero"
+    assert splits_seen >= 1 and climbs_seen >= 1
 
 
 GRAPH_CASES = [
     _custom("graph_split", "bf16", 4, 64, 4, 64, Hkv=2, G=3, seed=31),   # split, merged in the kernel
-    _custom("graph_deep", "bf16", 2, 4, 9, 6, d=64, Hkv=3, G=1, seed=32),  # per-level build kernels
-    workloads.small("deep_planted", levels=4, kv_heads=2),                # top-level build kernel
+    _custom("graph_deep", "bf16", 2, 4, 9, 6, d=64, Hkv=3, G=1, seed=32),  # build climbs 4 levels
+    workloads.small("deep_planted", levels=4, kv_heads=2),                # build climbs
+    _custom("graph_per_level", "f32", 2, 1, 16, 3, d=64, Hkv=1, G=2, seed=33),  # per-level kernels
 ]
 
 

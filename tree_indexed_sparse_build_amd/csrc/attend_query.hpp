@@ -45,18 +45,6 @@ __device__ inline float dot8_bf16(uint4 a, uint4 b) {
                                          __builtin_bit_cast(bf16x2_t, b.w), s, false);
 }
 
-// Agent-scope (device-coherent) float stores and loads, for the partial
-// states of split queries, which another XCD may read.
-__device__ inline void store_coherent(float *p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline float load_coherent(const float *p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// s_waitcnt vmcnt(0): this wave's vector memory operations, the coherent
-// stores included, have completed
-__device__ inline void wait_vector_memory() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
 // MW: the most waves of the workgroups that use it
 template <typename T, int D, int MW = kAttendMaxWaves> struct AttendShared {
   float p[MW][AttendGeom<T, D>::RB];

@@ -8,10 +8,14 @@
 // each summary row is written once.  Sums are carried in fp64 in a fixed
 // order and rounded once to the summary type (float32 or bfloat16).  A wave
 // reduces a subtree of b^kw leaves (a stack of open node sums in registers);
-// a workgroup of b^kg waves finishes its chunk's inner levels in LDS.  When the chunk roots sit below
-// level 1, a second small kernel climbs from their fp64 sums (one launch
-// while a level-1 subtree fits in LDS, else one launch per level): kernel
-// boundaries instead of device-scope fences between workgroups.  K is read
+// a workgroup of b^kg waves finishes its chunk's inner levels in LDS.  When
+// the chunk roots sit below level 1, their fp64 sums go to the workspace and
+// the last chunk of each level-1 subtree to finish climbs the subtree's
+// levels above the chunk roots in the same launch (an agent-scope arrival
+// count per subtree; the sums travel through device-coherent stores and
+// loads, no cache-wide fence).  A level-1 subtree too wide for the
+// workgroup's LDS, or more subtrees than the workspace has counters for,
+// take one small launch per level instead.  K is read
 // exactly once, so its loads carry the streaming (non-temporal) hint:
 // measured on MI355X, cold builds run 6-12% faster with it (a K rebuilt back
 // to back, partly left in the Infinity Cache by the previous build, runs a
@@ -115,7 +119,89 @@ template <int CPL> __device__ inline void stage_cols(bf16_bits *dst, const doubl
 }
 template <int CPL> __device__ inline void stage_cols(fp8_bits *, const double *) {}
 
-template <typename T, typename S, int D>
+// fp8 rows of nn nodes of level l whose fp64 sums sit in LDS (rows of D),
+// the first being node `node0` of the level (head included): one wave a row.
+template <int D>
+__device__ inline void top_rows_fp8(const BuildArgs &a, fp8_bits *summ, const double *sums,
+                                    int nn, int64_t node0, int l) {
+  constexpr int C = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int nw = blockDim.x >> 6;
+  for (int r = threadIdx.x >> 6; r < nn; r += nw) {
+    double m[C];
+    int cols[C];
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      cols[j] = lane + 64 * j;
+      m[j] = node_mean(a, l, sums[r * D + cols[j]]);
+    }
+    store_row_fp8<C>(summ + a.summ_off[l] + (node0 + r) * D, a.scales + a.summ_off[l] / D + node0 + r,
+                     m, cols, lane);
+  }
+}
+
+// Levels r-1 .. 1 of the subtree of level-1 node n1 of `head`: the b^(r-2)
+// nodes of level r-1 in it sum their children's fp64 sums from the
+// workspace (all loads independent; agent-scope loads, since the chunks
+// that stored those sums may have run on other XCDs), the levels above are
+// summed in LDS (2 b^(r-2) rows of D doubles at `lds`).  Every thread of the
+// workgroup takes part.
+template <typename S, int D>
+__device__ void climb_subtree(const BuildArgs &a, int64_t head, int64_t n1, double *lds) {
+  S *const summ = static_cast<S *>(a.summ);
+  const int tid = threadIdx.x;
+  const int b = a.branching;
+  int nn = static_cast<int>(a.top_rows);  // b^(r-2) nodes of level r-1 in the subtree
+  int64_t first = n1 * nn;                // their first index within level r-1
+  int l = a.root_level - 1;
+  double *cur = lds;
+  double *nxt = lds + nn * D;
+  for (int i = tid; i < nn * D; i += blockDim.x) {
+    const int n = i / D;
+    const int t = i - n * D;
+    const int64_t node = head * a.n_at[l] + first + n;
+    const double *child = a.ws_sum + a.ws_off[l + 1] + node * b * D + t;
+    // the children's sums, 8 loads in flight at a time, added in child order
+    double s = 0.0;
+    for (int c0 = 0; c0 < b; c0 += 8) {
+      double v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        v[j] = c0 + j < b ? load_coherent(child + static_cast<int64_t>(c0 + j) * D) : 0.0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (c0 + j < b) s += v[j];
+    }
+    cur[i] = s;
+    if constexpr (!kIsFp8<S>) SummaryType<S>::put(summ + a.summ_off[l] + node * D + t, node_mean(a, l, s));
+  }
+  __syncthreads();
+  if constexpr (kIsFp8<S>) top_rows_fp8<D>(a, summ, cur, nn, head * a.n_at[l] + first, l);
+  for (--l; l >= 1; --l) {
+    nn /= b;
+    first /= b;
+    for (int i = tid; i < nn * D; i += blockDim.x) {
+      const int n = i / D;
+      const int t = i - n * D;
+      double s = 0.0;
+      for (int c = 0; c < b; ++c) s += cur[(n * b + c) * D + t];
+      nxt[i] = s;
+      if constexpr (!kIsFp8<S>)
+        SummaryType<S>::put(summ + a.summ_off[l] + (head * a.n_at[l] + first + n) * D + t,
+                            node_mean(a, l, s));
+    }
+    __syncthreads();
+    if constexpr (kIsFp8<S>) top_rows_fp8<D>(a, summ, nxt, nn, head * a.n_at[l] + first, l);
+    double *tmp = cur;
+    cur = nxt;
+    nxt = tmp;
+  }
+}
+
+// CLIMB: the last chunk of each level-1 subtree climbs the levels above the
+// chunk roots (a compile-time variant, so builds that end at the chunk
+// roots run the kernel without that tail)
+template <typename T, typename S, int D, bool CLIMB>
 __global__ void __launch_bounds__(1024) k_build(BuildArgs a) {
   using G = RowGeom<T, D>;
   constexpr int E = G::kElemsPerLane;
@@ -359,10 +445,30 @@ __global__ void __launch_bounds__(1024) k_build(BuildArgs a) {
     nxt = t;
   }
 
-  // ---- the chunk root: its fp64 sum feeds the levels above (later kernels)
+  // ---- the chunk root: its fp64 sum feeds the levels above
   if (lvl >= 2) {
     double *mine = a.ws_sum + a.ws_off[lvl] + (head * a.n_at[lvl] + base) * D;
-    for (int i = tid; i < D; i += blockDim.x) mine[i] = cur[i];
+    for (int i = tid; i < D; i += blockDim.x) store_coherent(mine + i, cur[i]);
+    if constexpr (CLIMB) {
+      // the last chunk of its level-1 subtree to get here climbs the
+      // subtree's levels r-1 .. 1 and sets the subtree's counter back to
+      // zero; the others are done
+      __shared__ int s_last;
+      if (tid < D) wait_vector_memory();  // the threads that stored the root's sums
+      __syncthreads();
+      const int64_t n1 = chunk / a.chunks_per_l1;
+      unsigned *cnt = a.arrive + head * b + n1;
+      if (tid == 0) {
+        const unsigned before = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT);
+        s_last = before == static_cast<unsigned>(a.chunks_per_l1 - 1);
+      }
+      __syncthreads();
+      if (s_last) {
+        if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        climb_subtree<S, D>(a, head, n1, lds);  // the LDS rows of this chunk are no longer read
+      }
+    }
   }
 }
 
@@ -379,8 +485,16 @@ __global__ void __launch_bounds__(256) k_build_level(BuildArgs a, int l) {
   const int t = static_cast<int>(item - node * D);
   const int b = a.branching;
   const double *child = a.ws_sum + a.ws_off[l + 1] + node * b * D + t;
+  // 8 loads in flight at a time, added in child order
   double s = 0.0;
-  for (int c = 0; c < b; ++c) s += child[static_cast<int64_t>(c) * D];
+  for (int c0 = 0; c0 < b; c0 += 8) {
+    double v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = c0 + j < b ? child[static_cast<int64_t>(c0 + j) * D] : 0.0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (c0 + j < b) s += v[j];
+  }
   SummaryType<S>::put(static_cast<S *>(a.summ) + a.summ_off[l] + node * D + t, node_mean(a, l, s));
   if (l >= 2) a.ws_sum[a.ws_off[l] + node * D + t] = s;
 }
@@ -407,77 +521,6 @@ template <int D> __global__ void __launch_bounds__(256) k_build_level_fp8(BuildA
   }
   store_row_fp8<C>(static_cast<fp8_bits *>(a.summ) + a.summ_off[l] + node * D,
                    a.scales + a.summ_off[l] / D + node, m, cols, lane);
-}
-
-// fp8 rows of nn nodes of level l whose fp64 sums sit in LDS (rows of D),
-// the first being node `node0` of the level (head included): one wave a row.
-template <int D>
-__device__ inline void top_rows_fp8(const BuildArgs &a, fp8_bits *summ, const double *sums,
-                                    int nn, int64_t node0, int l) {
-  constexpr int C = D / 64;
-  const int lane = threadIdx.x & 63;
-  const int nw = blockDim.x >> 6;
-  for (int r = threadIdx.x >> 6; r < nn; r += nw) {
-    double m[C];
-    int cols[C];
-#pragma unroll
-    for (int j = 0; j < C; ++j) {
-      cols[j] = lane + 64 * j;
-      m[j] = node_mean(a, l, sums[r * D + cols[j]]);
-    }
-    store_row_fp8<C>(summ + a.summ_off[l] + (node0 + r) * D, a.scales + a.summ_off[l] / D + node0 + r,
-                     m, cols, lane);
-  }
-}
-
-// Levels r-1 .. 1 in one launch, one workgroup per (head, level-1 node): the
-// b^(r-2) nodes of level r-1 in its subtree sum their children's fp64 sums
-// from the workspace (all loads independent), the levels above are summed in
-// LDS.  Used when the subtree's level r-1 fits in LDS.
-template <typename S, int D> __global__ void __launch_bounds__(256) k_build_top(BuildArgs a) {
-  extern __shared__ double lds[];
-  S *const summ = static_cast<S *>(a.summ);
-  const int tid = threadIdx.x;
-  const int b = a.branching;
-  const int r = a.root_level;
-  const int64_t head = blockIdx.x / b;
-  const int64_t n1 = blockIdx.x - head * b;
-  int nn = static_cast<int>(a.top_rows);  // b^(r-2) nodes of level r-1 in the subtree
-  int64_t first = n1 * nn;                // their first index within level r-1
-  int l = r - 1;
-  double *cur = lds;
-  double *nxt = lds + nn * D;
-  for (int i = tid; i < nn * D; i += blockDim.x) {
-    const int n = i / D;
-    const int t = i - n * D;
-    const int64_t node = head * a.n_at[l] + first + n;
-    const double *child = a.ws_sum + a.ws_off[l + 1] + node * b * D + t;
-    double s = 0.0;
-    for (int c = 0; c < b; ++c) s += child[static_cast<int64_t>(c) * D];
-    cur[i] = s;
-    if constexpr (!kIsFp8<S>) SummaryType<S>::put(summ + a.summ_off[l] + node * D + t, node_mean(a, l, s));
-  }
-  __syncthreads();
-  if constexpr (kIsFp8<S>) top_rows_fp8<D>(a, summ, cur, nn, head * a.n_at[l] + first, l);
-  for (--l; l >= 1; --l) {
-    nn /= b;
-    first /= b;
-    for (int i = tid; i < nn * D; i += blockDim.x) {
-      const int n = i / D;
-      const int t = i - n * D;
-      double s = 0.0;
-      for (int c = 0; c < b; ++c) s += cur[(n * b + c) * D + t];
-      nxt[i] = s;
-      if constexpr (!kIsFp8<S>)
-        SummaryType<S>::put(summ + a.summ_off[l] + (head * a.n_at[l] + first + n) * D + t,
-                            node_mean(a, l, s));
-    }
-    __syncthreads();
-    if constexpr (kIsFp8<S>) top_rows_fp8<D>(a, summ, nxt, nn, head * a.n_at[l] + first, l);
-    double *tmp = cur;
-    cur = nxt;
-    nxt = tmp;
-  }
 }
 
 }  // namespace
@@ -552,7 +595,7 @@ bool plan_build(int64_t heads, int head_dim, int branching, int leaf_block, int 
     if (l >= 2) sum += static_cast<size_t>(heads * n) * head_dim;
   }
   p->sum_elems = sum;
-  p->workspace_bytes = sum * sizeof(double);
+  p->workspace_bytes = sum > 0 ? kBuildArriveBytes + sum * sizeof(double) : 0;
   return true;
 }
 
@@ -572,15 +615,18 @@ hipError_t launch_build_t(int64_t heads, const BuildArgs &args, const BuildPlan 
       static_cast<size_t>(stage_rows(p.waves, a.branching, p.wave_depth)) * D * sizeof(S);
   a.stage = !kIsFp8<S> && stage_bytes <= kStageLdsBytes;
   if (a.stage) lds += stage_bytes;
-  hipLaunchKernelGGL((k_build<T, S, D>), grid, block, lds, s, a);
+  // chunk roots at level 2 or below: the last chunk of each level-1 subtree
+  // climbs it in the same launch when its rows fit the LDS the kernel already
+  // has (2 b^(r-2) <= 2 nw rows) and the counters fit the workspace's
+  a.fuse_top = p.root_level >= 2 && a.top_rows <= p.waves &&
+               heads * a.branching <= kBuildArriveMax;
+  if (a.fuse_top)
+    hipLaunchKernelGGL((k_build<T, S, D, true>), grid, block, lds, s, a);
+  else
+    hipLaunchKernelGGL((k_build<T, S, D, false>), grid, block, lds, s, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.root_level < 2) return e;
-  if (a.top_rows * D * sizeof(double) * 2 <= kTopLdsBytes) {
-    const dim3 g(static_cast<unsigned>(heads * a.branching));
-    const size_t lds = static_cast<size_t>(a.top_rows) * D * sizeof(double) * 2;
-    hipLaunchKernelGGL((k_build_top<S, D>), g, dim3(256), lds, s, a);
-    return hipGetLastError();
-  }
+  if (e != hipSuccess || p.root_level < 2 || a.fuse_top) return e;
+  // otherwise one small launch per level above the chunk roots
   for (int l = p.root_level - 1; e == hipSuccess && l >= 1; --l) {
     if constexpr (kIsFp8<S>) {
       const dim3 g(static_cast<unsigned>((a.chunks_at_level[l] + 3) / 4));

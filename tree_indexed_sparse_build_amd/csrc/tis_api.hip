@@ -211,7 +211,11 @@ tis_status tis_tree_build(const void *K, tis_dtype dtype, int batch, int kv_head
   if (tree->summary_dtype == TIS_FP8_E4M3)
     a.scales = reinterpret_cast<float *>(static_cast<char *>(tree->summaries) +
                                          fp8_scales_offset(g.summ_elems / head_dim, head_dim));
-  a.ws_sum = static_cast<double *>(workspace);
+  // the arrival counters of the level-1 subtrees, then the fp64 node sums
+  a.arrive = p.workspace_bytes > 0 ? static_cast<unsigned *>(workspace) : nullptr;
+  a.ws_sum = p.workspace_bytes > 0
+                 ? reinterpret_cast<double *>(static_cast<char *>(workspace) + tis::kBuildArriveBytes)
+                 : nullptr;
   a.n_keys = n_keys;
   a.chunks = p.chunks;
   a.branching = branching;
@@ -222,6 +226,8 @@ tis_status tis_tree_build(const void *K, tis_dtype dtype, int batch, int kv_head
   a.stream_loads = 1;  // K is read once: streaming loads, whatever its size
   a.top_rows = 1;
   for (int l = 2; l < p.root_level; ++l) a.top_rows *= branching;
+  a.chunks_per_l1 = 1;
+  for (int l = 2; l <= p.root_level; ++l) a.chunks_per_l1 *= branching;
   a.wave_leaves = 1;
   for (int i = 0; i < p.wave_depth; ++i) a.wave_leaves *= branching;
   a.pow2_levels = 0;

@@ -343,4 +343,22 @@ __device__ inline void store_row_fp8(fp8_bits *row, float *scale, const double (
   if (lane == 0) *scale = static_cast<float>(pow2_double(e));
 }
 
+// ---- data handed between workgroups of one launch ----------------------
+// Agent-scope (device-coherent) stores and loads: they bypass the XCDs'
+// private L2 state, so a workgroup on another XCD reads what was stored
+// without an L2 write-back or invalidate (a release or acquire fence at
+// agent scope would do both, over the whole L2).  A producer stores with
+// store_coherent, waits for the stores to complete (wait_vector_memory) and
+// only then counts itself in on an agent-scope atomic; the consumer that
+// reads the count issues its load_coherent loads after it.
+template <typename F> __device__ inline void store_coherent(F *p, F v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename F> __device__ inline F load_coherent(const F *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// s_waitcnt vmcnt(0): this wave's vector memory operations, the coherent
+// stores included, have completed
+__device__ inline void wait_vector_memory() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 }  // namespace tis

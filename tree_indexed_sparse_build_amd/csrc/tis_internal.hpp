@@ -21,14 +21,22 @@ enum class Dt : int { F32 = 0, BF16 = 1, FP8 = 2 };  // FP8: summaries only
 // levels in LDS.  When r >= 2 the chunk roots leave fp64 sums in the
 // workspace and one small kernel per level computes levels r-1 .. 1.
 constexpr int kMaxWaveDepth = 3;
-constexpr size_t kTopLdsBytes = 64 * 1024;     // LDS budget of the one-launch top levels
 constexpr size_t kStageLdsBytes = 64 * 1024;   // LDS budget of the build's staged rows
+// A build workspace (when the build needs one) starts with the arrival
+// counters of up to kBuildArriveMax level-1 subtrees, at offset 0 whatever
+// the geometry; the fp64 node sums follow.
+constexpr int64_t kBuildArriveMax = 4096;
+constexpr size_t kBuildArriveBytes = kBuildArriveMax * sizeof(unsigned);
 
 struct BuildArgs {
   const void *K;
   void *summ;            // float, bf16 bits or fp8 codes (the summary type)
   float *scales;         // fp8 only: a power-of-two scale per node, level-major
   double *ws_sum;        // fp64 node sums of levels 2..r
+  unsigned *arrive;      // [heads * b] chunks of each level-1 subtree done (zero between calls)
+  int fuse_top;          // nonzero: the last chunk of each level-1 subtree climbs
+                         // its levels r-1 .. 1 (no second kernel)
+  int64_t chunks_per_l1; // b^(r-1): chunks under one level-1 node
   int64_t n_keys;        // N
   int64_t chunks;        // b^r chunks per head
   int64_t wave_leaves;   // b^kw

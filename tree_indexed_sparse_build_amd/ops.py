@@ -62,9 +62,9 @@ def _stream(device: torch.device) -> int:
 
 
 # Workspaces, one per (device, kind), grown on demand and reused: calls are
-# ordered on the caller's stream.  They start zeroed: a split attend or
-# decode needs its arrival counters (the first 1 KiB) at zero on first use,
-# and every call leaves them so.
+# ordered on the caller's stream.  They start zeroed: the arrival counters at
+# the start of a build, attend or decode workspace must be zero on first
+# use, and every call leaves them so.
 _workspaces: Dict[Tuple[int, str], torch.Tensor] = {}
 
 
@@ -395,7 +395,7 @@ class DecodePlan:
             raise _lib.TisError(_lib.TIS_E_SHAPE, "invalid tree geometry")
         self.summaries = torch.empty(nbytes // tdt.itemsize, dtype=tdt, device=K.device)
         wsb = L.tis_build_workspace_bytes(*self.geom)
-        self.ws_build = (torch.empty(wsb, dtype=torch.uint8, device=K.device) if wsb
+        self.ws_build = (torch.zeros(wsb, dtype=torch.uint8, device=K.device) if wsb
                          else None)
         wsa = L.tis_attend_workspace_bytes(B, Hq, d, beam, leaf_block)
         self.ws_attend = (torch.zeros(wsa, dtype=torch.uint8, device=K.device) if wsa
