@@ -535,19 +535,23 @@ int64_t stage_rows(int64_t nw, int64_t branching, int kw) {
 
 bool plan_build(int64_t heads, int head_dim, int branching, int leaf_block, int levels,
                 BuildPlan *p) {
-  (void)leaf_block;
   // Choose the wave subtree depth kw (b^kw leaves per wave) and the
-  // workgroup depth kg (b^kg <= 16 waves).  Each level left above the chunk
-  // roots costs one more small launch (~5 us), so: (1) a plan that finishes
-  // in the first kernel (r <= 1) wins if it still has >= 2048 waves;
-  // (2) otherwise plans with >= 4096 waves and >= 512 workgroups (enough
-  // loads in flight on 256 CUs), fewest levels left first; (3) otherwise the
-  // most waves.  Within a tier, plans whose wave-level rows fit the LDS
-  // staging budget (as float32 rows, so the plan is the same for every
-  // summary type) come first: writing those rows in one burst after the
-  // last K load, instead of one row at a time between loads, measured 4-10%
-  // faster on cold builds.  Ties go to bigger workgroups.
-  struct Cand { int kw, kg, r; int64_t waves, wgs; bool stage; };
+  // workgroup depth kg (b^kg <= 16 waves), by tiers measured on MI355X
+  // (every plan gives the same summaries, bit for bit): (0) a plan that
+  // needs no level above the chunk roots (r <= 1) and has >= 2048 waves;
+  // (1) a plan whose waves all run at once (2048 to 4096 waves: the kernel
+  // keeps 16 waves a CU on 256 CUs) in >= 512 workgroups, each wave
+  // streaming at most 1,024 keys (measured on 262,144-key heads with
+  // b = 4: 7% faster than the 8,192 waves of tier 2, run in two rounds);
+  // (2) plans with >= 4096 waves and >= 512 workgroups (enough loads in
+  // flight on 256 CUs), fewest levels left first; (3) otherwise the most
+  // waves.  Within a tier, plans whose wave-level rows fit the LDS staging
+  // budget (as float32 rows, so the plan is the same for every summary
+  // type) come first: writing those rows in one burst after the last K
+  // load, instead of one row at a time between loads, measured 4-10% faster
+  // on cold builds.  Ties go to bigger workgroups.
+  constexpr int64_t kOneRoundWaves = 256 * 16;
+  struct Cand { int kw, kg, r; int64_t waves, wgs; bool stage; int64_t wave_keys; };
   auto ipow = [](int64_t x, int e) {
     int64_t v = 1;
     for (int i = 0; i < e; ++i) v *= x;
@@ -555,15 +559,17 @@ bool plan_build(int64_t heads, int head_dim, int branching, int leaf_block, int 
   };
   auto tier = [](const Cand &c) {
     if (c.r <= 1 && c.waves >= 2048) return 0;
-    if (c.waves >= 4096 && c.wgs >= 512) return 1;
-    return 2;
+    if (c.waves >= 2048 && c.waves <= kOneRoundWaves && c.wgs >= 512 && c.wave_keys <= 1024)
+      return 1;
+    if (c.waves >= 4096 && c.wgs >= 512) return 2;
+    return 3;
   };
   auto better = [&](const Cand &c, const Cand &o) {
     const int tc = tier(c), to = tier(o);
     if (tc != to) return tc < to;
     if (c.stage != o.stage) return c.stage;
     if (tc == 0) return c.waves > o.waves || (c.waves == o.waves && c.kg > o.kg);
-    if (tc == 1) return c.r < o.r || (c.r == o.r && c.kg > o.kg);
+    if (tc == 1 || tc == 2) return c.r < o.r || (c.r == o.r && c.kg > o.kg);
     return c.waves > o.waves || (c.waves == o.waves && c.r < o.r);
   };
   bool have = false;
@@ -575,7 +581,7 @@ bool plan_build(int64_t heads, int head_dim, int branching, int leaf_block, int 
       const int r = levels - kw - kg;
       const bool stage = stage_rows(nw, branching, kw) * head_dim * sizeof(float) <= kStageLdsBytes;
       const Cand c{kw, kg, r, heads * ipow(branching, levels - kw), heads * ipow(branching, r),
-                   stage};
+                   stage, ipow(branching, kw) * leaf_block};
       if (c.wgs > 0x7fffffffLL) continue;
       if (!have || better(c, best)) best = c;
       have = true;
