@@ -83,7 +83,11 @@ def distinct_bytes(tis, w, Q, K):
     the rows of every scored level's candidates (from the route's trace; the
     first level that cuts scores all of its nodes, later ones the children of
     the nodes the group kept), the K and V rows of the distinct kept leaves,
-    and each query's own row, kept leaves and output."""
+    and each query's own row, kept leaves and output.  Also returns the leaf
+    union fraction: distinct kept leaves per (batch, KV head), summed, over
+    the queries' kept leaves (1.0: the G query heads of a group share none;
+    1 / G: all keep the same), the most that gathering each leaf of a
+    group's union once could save of the gather's bytes."""
     import numpy as np
     tree = tis.tree_build(K, w.branching, w.leaf_block, w.levels)
     idx, tr = tis.tree_route(Q, tree, w.beam, trace=True)
@@ -103,7 +107,9 @@ def distinct_bytes(tis, w, Q, K):
                 rows += len(kept) * b
             blocks += len(np.unique(idx[bb, h * G:(h + 1) * G]))
     per_query = d * w.elem_bytes + 4 * W + 4 * d
-    return rows * d * 4 + blocks * w.leaf_block * d * w.elem_bytes * 2 + w.queries * per_query
+    kept = int((idx >= 0).sum())
+    return (rows * d * 4 + blocks * w.leaf_block * d * w.elem_bytes * 2 + w.queries * per_query,
+            blocks / max(kept, 1))
 
 
 def _source_digest() -> str:
@@ -486,10 +492,18 @@ def measure_workload(tis, torch, probes, w, ceil_gbs, hop_us, reps, headline=Fal
                     "cold_frac": by["build"] / (bc * 1e3) / HBM_PEAK_GBS,
                     "warm_us": graph_time(torch, plan.build, per_graph=5, replays=3)}
     res["build"]["warm_frac"] = by["build"] / (res["build"]["warm_us"] * 1e3) / HBM_PEAK_GBS
+    # the same bytes as the build's K, streamed by the read probe (cold): the
+    # read ceiling at this size, ramp and tail included
+    kread = graph_diff(torch, probes.flush, lambda: probes.read(K_, nontemporal=True),
+                       per_graph=max(5, min(K, 20)), replays=3)
+    kbytes = K_.numel() * K_.element_size()
+    res["build"]["k_read_cold_us"] = kread
+    res["build"]["k_read_cold_gbs"] = kbytes / (kread * 1e3)
+    res["build"]["frac_of_k_read"] = kread / bc
     dr = decode_regimes(torch, probes, plan)
-    dist = distinct_bytes(tis, w, Q, K_)
+    dist, union = distinct_bytes(tis, w, Q, K_)
     floor = decode_floor(w, ceil_gbs, hop_us, dec_bytes)
-    dec = {"regimes": dr, "bytes_distinct": dist, "floor_us": floor,
+    dec = {"regimes": dr, "bytes_distinct": dist, "leaf_union_fraction": union, "floor_us": floor,
            "floor_model": f"{w.levels - first_cut(w) + 2} dependent HBM round trips + "
                           "per-query-sum bytes at the read ceiling"}
     for r in ("cold", "steady", "warm"):
@@ -503,7 +517,9 @@ def measure_workload(tis, torch, probes, w, ceil_gbs, hop_us, reps, headline=Fal
     if step is not None:
         res["step"] = step
     log(f"{w.name}: build cold {bc:.1f} us ({res['build']['cold_frac']:.1%} of 8 TB/s on "
-        f"{by['build'] / 1e6:.1f} MB), warm {res['build']['warm_us']:.1f} us; decode cold "
+        f"{by['build'] / 1e6:.1f} MB; {kread / bc:.1%} of a cold streaming read of K, "
+        f"{kread:.1f} us), warm {res['build']['warm_us']:.1f} us; leaf union "
+        f"{union:.2f}; decode cold "
         f"{dr['cold_us']:.2f} / steady {dr['steady_us']:.2f} / warm {dr['warm_us']:.2f} us "
         f"({dec['cold']['frac']:.1%} / {dec['steady']['frac']:.1%} / {dec['warm']['frac']:.1%} "
         f"on {dec_bytes / 1e6:.2f} MB per-query sum; {dec['cold']['frac_distinct']:.1%} cold on "
@@ -824,7 +840,8 @@ def main(argv=None):
                      "traffic": load_traffic(w.name), "regime": "cold (caches emptied first)",
                      "launch_us_mean": head["build"]["cold_us"],
                      "warm_frac": head["build"]["warm_frac"],
-                     "read_ceiling_frac": build_gbs / ceil_gbs},
+                     "read_ceiling_frac": build_gbs / ceil_gbs,
+                     "frac_of_k_read": head["build"]["frac_of_k_read"]},
         "decode": {"queries_per_s_cold": d["cold"]["queries_per_s"],
                    "queries_per_s_steady": d["steady"]["queries_per_s"],
                    "queries_per_s_warm": d["warm"]["queries_per_s"],
