@@ -228,6 +228,42 @@ def test_errors_through_binding(tis):
     torch.cuda.synchronize()
 
 
+# ------------------------------------------------------ random geometries --
+def _random_geometries(n=24, seed=2024):
+    """Seeded small geometries across branching, depth, leaf size, beam, head
+    dim, input type and GQA group, kept small enough for the oracle: they
+    reach the build's single-kernel and climbing plans, unscored levels,
+    beams from 1 to every leaf, and split and unsplit attention."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        b = int(rng.choice([2, 3, 4, 5, 8]))
+        lv = int(rng.integers(1, 6))
+        L = int(rng.choice([1, 3, 4, 8, 16, 32, 64, 96]))
+        leaves = b ** lv
+        if leaves * L > (1 << 15) or leaves > 4096:
+            continue
+        W = int(rng.integers(1, min(leaves, 256 // b) + 1))
+        d = int(rng.choice([64, 128]))
+        dtype = str(rng.choice(["f32", "bf16"]))
+        B = int(rng.integers(1, 3))
+        Hkv = int(rng.integers(1, 4))
+        G = int(rng.choice([1, 2, 4, 8]))
+        name = f"rand{len(out)}_b{b}_lv{lv}_L{L}_W{W}_d{d}_{dtype}_B{B}_{Hkv}x{G}"
+        out.append(workloads.Workload(name, dtype, B, Hkv * G, Hkv, d, b, L, lv, W, "normal",
+                                      seed=100 + len(out)))
+    return out
+
+
+RANDOM = _random_geometries()
+
+
+@pytest.mark.parametrize("w", RANDOM, ids=[w.name for w in RANDOM])
+def test_random_geometry(tis, w):
+    check_case(tis, w)
+
+
 # -------------------------------------------------------------- full size --
 # bfloat16 summaries: the build rounds every mean straight from fp64 and the
 # walk reads 8 summary elements per 16-byte load (both head dims, the
