@@ -436,6 +436,26 @@ def decode_regimes(torch, probes, plan):
             "warm_us": graph_time(torch, plan.decode)}
 
 
+def attend_comparison(torch, probes, plan):
+    """The attention alone over the routed leaves, per query (tree_attend)
+    and with the query heads of a KV head together (tree_attend_grouped),
+    cold and warm (us); the grouped output's largest difference from the
+    per-query one."""
+    plan.route()
+    plan.attend()
+    torch.cuda.synchronize()
+    ref = plan.out.clone()
+    res = {"per_query_cold_us": graph_diff(torch, probes.flush, plan.attend, replays=3),
+           "per_query_warm_us": graph_time(torch, plan.attend, replays=3)}
+    if plan.ws_grouped is not None:
+        plan.attend_grouped()
+        torch.cuda.synchronize()
+        res["grouped_max_abs_diff"] = float((plan.out - ref).abs().max().item())
+        res["grouped_cold_us"] = graph_diff(torch, probes.flush, plan.attend_grouped, replays=3)
+        res["grouped_warm_us"] = graph_time(torch, plan.attend_grouped, replays=3)
+    return res
+
+
 def decode_floor(w, ceil_gbs, hop_us, dec_bytes):
     """Latency floor of one decode: the scored levels and the gather form a
     chain of dependent round trips (the first level's rows, each later
@@ -514,6 +534,7 @@ def measure_workload(tis, torch, probes, w, ceil_gbs, hop_us, reps, headline=Fal
                   "frac_distinct": dist / (t * 1e3) / HBM_PEAK_GBS,
                   "floor_ratio": t / floor}
     res["decode"] = dec
+    res["attend_only"] = attend_comparison(torch, probes, plan)
     if step is not None:
         res["step"] = step
     log(f"{w.name}: build cold {bc:.1f} us ({res['build']['cold_frac']:.1%} of 8 TB/s on "
@@ -523,7 +544,9 @@ def measure_workload(tis, torch, probes, w, ceil_gbs, hop_us, reps, headline=Fal
         f"{dr['cold_us']:.2f} / steady {dr['steady_us']:.2f} / warm {dr['warm_us']:.2f} us "
         f"({dec['cold']['frac']:.1%} / {dec['steady']['frac']:.1%} / {dec['warm']['frac']:.1%} "
         f"on {dec_bytes / 1e6:.2f} MB per-query sum; {dec['cold']['frac_distinct']:.1%} cold on "
-        f"{dist / 1e6:.2f} MB distinct); floor {floor:.2f} us")
+        f"{dist / 1e6:.2f} MB distinct); floor {floor:.2f} us; attend alone cold per query "
+        f"{res['attend_only']['per_query_cold_us']:.2f} us, grouped "
+        f"{res['attend_only'].get('grouped_cold_us', float('nan')):.2f} us")
     return res, (x, Q, K_, V, plan)
 
 

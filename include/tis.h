@@ -39,14 +39,16 @@
  *   status of the calling thread.  No C++ exception crosses this interface.
  *
  * Workspaces
- *   tis_tree_build, tis_tree_attend and tis_tree_decode take a caller-owned
+ *   tis_tree_build, tis_tree_attend, tis_tree_attend_grouped and
+ *   tis_tree_decode take a caller-owned
  *   device workspace (16-byte aligned) of at least the size the matching
  *   *_workspace_bytes query returns.  A size of 0 means none is needed and
  *   NULL is accepted.  A workspace starts with arrival counters: the build's
  *   first 16,384 bytes count the finished chunks of each level-1 subtree
  *   (the last chunk of a subtree to finish climbs to level 1), attend's and
  *   decode's first 1,024 bytes count the finished parts of each split query
- *   (few queries, long key sets: the last part to finish merges them).  The
+ *   (few queries, long key sets: the last part to finish merges them), the
+ *   grouped attend's those of each split group of query heads.  The
  *   build's fp64 node sums and the split queries' partial softmax states
  *   follow.  Those counter bytes must be zero before a workspace's first
  *   call (allocate it zeroed, or clear it once); every call that completes
@@ -186,6 +188,34 @@ tis_status tis_tree_attend(const void *Q, const void *K, const void *V, tis_dtyp
                            int head_dim, int leaf_block, const int32_t *indices,
                            int beam, float scale, float *O, void *workspace,
                            size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace tis_tree_attend_grouped needs for this geometry (0: none). */
+size_t tis_attend_grouped_workspace_bytes(int batch, int q_heads, int kv_heads, int head_dim,
+                                          int beam);
+
+/*
+ * tis_tree_attend_grouped -- tis_tree_attend with the G = q_heads / kv_heads
+ * query heads that share a KV head contracted together on the matrix cores
+ * (the attention of the ZHA abstract and of the NSA / InfLLMv2 abstract, as
+ * for tis_tree_attend; the grouping is an order of work, not a change of
+ * what is computed).  Every leaf block kept by any head of a group is read
+ * once for the whole group; each head still attends over exactly its own
+ * blocks (masked per head).
+ *
+ * Arguments, layouts, slot rules (negative = empty, repeats count once,
+ * >= N / L makes the head's row NaN, an empty set gives a zero row), scale
+ * and O exactly as tis_tree_attend; results agree with it to fp32 rounding
+ * (weights and sums in fp32, another summation order).
+ * workspace, workspace_bytes: see Workspaces
+ * (tis_attend_grouped_workspace_bytes; counters in the first 1,024 bytes).
+ * Requires N % L == 0, beam >= 1, G <= 64 and G * beam <= 512
+ * (TIS_E_UNSUPPORTED otherwise).
+ */
+tis_status tis_tree_attend_grouped(const void *Q, const void *K, const void *V, tis_dtype dtype,
+                                   int batch, int q_heads, int kv_heads, int n_keys,
+                                   int head_dim, int leaf_block, const int32_t *indices,
+                                   int beam, float scale, float *O, void *workspace,
+                                   size_t workspace_bytes, void *stream);
 
 /*
  * tis_tree_decode -- one decode step: tis_tree_route and tis_tree_attend for

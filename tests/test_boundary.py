@@ -203,6 +203,53 @@ def test_attend_rejects(lib, kw, status):
     assert lib.tis_last_error().decode()
 
 
+def _attend_grouped(lib, **kw):
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, dt=_lib.TIS_BF16, B=1, Hq=4, Hkv=2, N=256, d=128, L=16,
+             idx=FAKE, beam=4, scale=0.0, O=FAKE, ws=FAKE, wsb=1 << 20)
+    a.update(kw)
+    return lib.tis_tree_attend_grouped(a["Q"], a["K"], a["V"], a["dt"], a["B"], a["Hq"], a["Hkv"],
+                                       a["N"], a["d"], a["L"], a["idx"], a["beam"], a["scale"],
+                                       a["O"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(V=None), _lib.TIS_E_NULL),
+    (dict(idx=None), _lib.TIS_E_NULL),
+    (dict(dt=-1), _lib.TIS_E_DTYPE),
+    (dict(Hq=3), _lib.TIS_E_SHAPE),
+    (dict(N=250), _lib.TIS_E_SHAPE),
+    (dict(beam=0), _lib.TIS_E_SHAPE),
+    (dict(d=32), _lib.TIS_E_UNSUPPORTED),
+    (dict(scale=float("nan")), _lib.TIS_E_SHAPE),
+    (dict(K=FAKE + 8), _lib.TIS_E_ALIGN),
+    (dict(idx=FAKE + 2), _lib.TIS_E_ALIGN),
+    # 65 query heads per KV head, or 576 slots in a group
+    (dict(Hq=130, Hkv=2), _lib.TIS_E_UNSUPPORTED),
+    (dict(Hq=64, Hkv=1, beam=9), _lib.TIS_E_UNSUPPORTED),
+    # 2 groups: split, so a workspace is needed
+    (dict(ws=None), _lib.TIS_E_NULL),
+    (dict(wsb=100), _lib.TIS_E_WORKSPACE),
+    (dict(ws=FAKE + 8), _lib.TIS_E_ALIGN),
+])
+def test_attend_grouped_rejects(lib, kw, status):
+    assert _attend_grouped(lib, **kw) == status
+    assert lib.tis_last_error().decode()
+
+
+def test_attend_grouped_workspace_bytes(lib):
+    part = (128 + 4) * 4
+    # 32 groups of 4 heads, beam 8: 8 parts per group
+    assert lib.tis_attend_grouped_workspace_bytes(4, 32, 8, 128, 8) == 1024 + 32 * 8 * 4 * part
+    # 8 groups of 16 heads: 16 parts (16 x 16 states for the last part to merge)
+    assert lib.tis_attend_grouped_workspace_bytes(1, 128, 8, 128, 8) == 1024 + 8 * 16 * 16 * part
+    # no more parts than the group has slots
+    assert lib.tis_attend_grouped_workspace_bytes(1, 2, 2, 128, 1) == 0
+    assert lib.tis_attend_grouped_workspace_bytes(1, 2, 1, 128, 1) == 1024 + 2 * 2 * part
+    # 256 groups: one workgroup each, no workspace
+    assert lib.tis_attend_grouped_workspace_bytes(64, 8, 4, 128, 2) == 0
+    assert lib.tis_attend_grouped_workspace_bytes(1, 3, 2, 128, 8) == 0  # 3 heads over 2
+
+
 def _decode(lib, Q=FAKE, K=FAKE, V=FAKE, dt=_lib.TIS_BF16, Hq=2, tree=None, beam=2, scale=0.0,
             O=FAKE, idx=None, ws=None, wsb=0):
     t = tree if tree is not None else _tree(H=1)

@@ -39,6 +39,12 @@ def tis():
     return t
 
 
+def grouped_supported(w) -> bool:
+    """The grouped attend takes up to 64 query heads per KV head and 512
+    slots per group."""
+    return w.group <= 64 and w.group * w.beam <= 512
+
+
 def run_gpu(t, w, x, oracle_idx=None, summary_dtype="f32"):
     dev = "cuda"
     K = t.from_storage(x["K"], w.dtype, dev)
@@ -52,9 +58,14 @@ def run_gpu(t, w, x, oracle_idx=None, summary_dtype="f32"):
         oi = torch.from_numpy(np.ascontiguousarray(oracle_idx, dtype=np.int32)).to(dev)
         res["out_oracle_idx"] = t.tree_attend(Q, K, V, oi, w.leaf_block)
     res["fused_out"], res["fused_idx"] = t.tree_decode(Q, K, V, tree, w.beam, return_indices=True)
+    if grouped_supported(w):
+        res["grouped_out"] = t.tree_attend_grouped(Q, K, V, idx, w.leaf_block)
+    else:
+        with pytest.raises(t.TisError, match="TIS_E_UNSUPPORTED"):
+            t.tree_attend_grouped(Q, K, V, idx, w.leaf_block)
     torch.cuda.synchronize()
     res["levels"] = [tree.level(l).float().cpu().numpy() for l in range(1, w.levels + 1)]
-    for k in ("idx", "trace", "out", "out_oracle_idx", "fused_out", "fused_idx"):
+    for k in ("idx", "trace", "out", "out_oracle_idx", "fused_out", "fused_idx", "grouped_out"):
         if k in res:
             res[k] = res[k].cpu().numpy()
     return res
@@ -85,9 +96,13 @@ def check_case(t, w, x=None, label="", summary_dtype="f32", max_excused=None):
     # the fused decode keeps the same leaves and attends over them
     assert np.array_equal(g["fused_idx"], g["idx"]), "fused decode kept other leaves"
     err3 = parity.compare_outputs(g["fused_out"], o_g, w.dtype)
+    # the grouped attend over the same leaves
+    err4 = (parity.compare_outputs(g["grouped_out"], o_g, w.dtype)
+            if "grouped_out" in g else float("nan"))
     _say(f"{label or w.name}: summaries bit-equal {eq}/{tot} (worst {worst} ulp); "
          f"indices exact {exact}/{nq}, tie-exposed mismatches {tie}; "
-         f"attend max-abs {err1:.2e} (oracle idx) {err2:.2e} (gpu idx) {err3:.2e} (fused); "
+         f"attend max-abs {err1:.2e} (oracle idx) {err2:.2e} (gpu idx) {err3:.2e} (fused) "
+         f"{err4:.2e} (grouped); "
          f"min cut gap {float(np.min(orr['gap'])):.2e}; {time.time() - t0:.1f}s")
     return x, ob, orr, g
 
@@ -189,6 +204,50 @@ def test_attend_slot_rules(tis):
         assert np.max(np.abs(out[0, r] - want[0, r])) <= parity.ATTEND_TOL["bf16"]
     assert np.all(out[0, 1] == 0.0)
     assert np.all(np.isnan(out[0, 3]))
+
+
+def test_grouped_attend_slot_rules(tis):
+    """The grouped attend applies the slot rules per head: a leaf kept by
+    several heads of the group, repeats and negatives within a head, an
+    empty head, an out-of-range block in one head only."""
+    w = _custom("slots_grouped", "bf16", 4, 16, 2, 4, Hkv=1, G=6)
+    x = workloads.generate(w)
+    n_blocks = w.n_keys // w.leaf_block
+    idx = np.array([[[3, 3, 7, -1],
+                     [-1, -1, -1, -1],
+                     [0, 1, 2, 15],
+                     [5, n_blocks, 1, 2],
+                     [9, -5, 9, 9],
+                     [15, 14, 13, 12]]], dtype=np.int32)
+    K = tis.from_storage(x["K"], w.dtype)
+    V = tis.from_storage(x["V"], w.dtype)
+    Q = tis.from_storage(x["Q"], w.dtype)
+    out = tis.tree_attend_grouped(Q, K, V, torch.from_numpy(idx).cuda(),
+                                  w.leaf_block).cpu().numpy()
+    safe = idx.copy()
+    safe[0, 3] = -1
+    want = O.tree_attend(x["Q"], x["K"], x["V"], w.dtype, safe, w.leaf_block)
+    for r in (0, 2, 4, 5):
+        assert np.max(np.abs(out[0, r] - want[0, r])) <= parity.ATTEND_TOL["bf16"]
+    assert np.all(out[0, 1] == 0.0)
+    assert np.all(np.isnan(out[0, 3]))
+
+
+GROUPED_CASES = [
+    # 32 and 48 heads per KV head: two and four blocks of 16 heads
+    _custom("grouped_g32", "bf16", 4, 32, 2, 4, Hkv=1, G=32),
+    _custom("grouped_g48_f32", "f32", 4, 16, 3, 8, d=64, Hkv=2, G=48),
+    # 16 heads, ragged leaf blocks (not a multiple of 16 keys)
+    _custom("grouped_g16_ragged", "bf16", 8, 24, 2, 8, Hkv=2, G=16),
+    # 256 groups: one workgroup per group, no split
+    _custom("grouped_unsplit", "bf16", 2, 16, 2, 2, B=64, Hkv=4, G=2),
+    _custom("grouped_unsplit_f32", "f32", 2, 32, 2, 2, d=64, B=32, Hkv=8, G=3),
+]
+
+
+@pytest.mark.parametrize("w", GROUPED_CASES, ids=[w.name for w in GROUPED_CASES])
+def test_grouped_geometry(tis, w):
+    check_case(tis, w)
 
 
 def test_deterministic(tis):

@@ -16,8 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libtis.so")
-SOURCES = ["tis_api.hip", "build.hip", "route.hip", "attend.hip", "decode.hip", "cache.hip",
-           "sphere.hip", "prefill.hip", "probe.hip"]
+SOURCES = ["tis_api.hip", "build.hip", "route.hip", "attend.hip", "attend_group.hip", "decode.hip",
+           "cache.hip", "sphere.hip", "prefill.hip", "probe.hip"]
 ARCH = "gfx950"
 
 

@@ -385,6 +385,82 @@ tis_status tis_tree_attend(const void *Q, const void *K, const void *V, tis_dtyp
                     "tis_tree_attend launch");
 }
 
+size_t tis_attend_grouped_workspace_bytes(int batch, int q_heads, int kv_heads, int head_dim,
+                                          int beam) {
+  if (batch < 1 || kv_heads < 1 || q_heads < 1 || q_heads % kv_heads != 0 ||
+      (head_dim != 64 && head_dim != 128) || beam < 1)
+    return 0;
+  const int group = q_heads / kv_heads;
+  const int64_t groups = static_cast<int64_t>(batch) * kv_heads;
+  return tis::attend_group_workspace(groups, group, head_dim,
+                                     tis::attend_group_splits(groups, group, beam));
+}
+
+tis_status tis_tree_attend_grouped(const void *Q, const void *K, const void *V, tis_dtype dtype,
+                                   int batch, int q_heads, int kv_heads, int n_keys,
+                                   int head_dim, int leaf_block, const int32_t *indices,
+                                   int beam, float scale, float *O, void *workspace,
+                                   size_t workspace_bytes, void *stream) {
+  const char *who = "tis_tree_attend_grouped";
+  if (!Q || !K || !V || !indices || !O)
+    return fail(TIS_E_NULL, "%s: Q, K, V, indices and O are required", who);
+  tis_status st = check_dtype(dtype);
+  if (st != TIS_OK) return st;
+  if (batch < 1 || kv_heads < 1 || q_heads < 1 || q_heads % kv_heads != 0)
+    return fail(TIS_E_SHAPE, "%s: need batch, kv_heads >= 1 and q_heads a multiple of kv_heads",
+                who);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(head_dim < 1 ? TIS_E_SHAPE : TIS_E_UNSUPPORTED,
+                "%s: head_dim %d: only 64 and 128 are compiled", who, head_dim);
+  if (leaf_block < 1 || n_keys < 1 || n_keys % leaf_block != 0)
+    return fail(TIS_E_SHAPE, "%s: n_keys %d is not a positive multiple of leaf_block %d", who,
+                n_keys, leaf_block);
+  if (beam < 1) return fail(TIS_E_SHAPE, "%s: beam %d < 1", who, beam);
+  const int group = q_heads / kv_heads;
+  if (group > tis::kGroupMaxHeads || group * static_cast<int64_t>(beam) > tis::kGroupMaxEntries)
+    return fail(TIS_E_UNSUPPORTED, "%s: %d heads per KV head x beam %d: at most %d heads and %d slots per group",
+                who, group, beam, tis::kGroupMaxHeads, tis::kGroupMaxEntries);
+  if (!(scale == scale) || isinf(scale)) return fail(TIS_E_SHAPE, "%s: scale must be finite", who);
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) ||
+      !aligned(indices, 4))
+    return fail(TIS_E_ALIGN, "%s: Q, K, V and O need 16-byte alignment, indices 4-byte", who);
+  const int64_t queries = static_cast<int64_t>(batch) * q_heads;
+  if (queries > 0x7fffffffLL) return fail(TIS_E_UNSUPPORTED, "%s: too many queries", who);
+
+  const double sc = scale > 0.f ? static_cast<double>(scale) : 1.0 / sqrt(static_cast<double>(head_dim));
+  tis::AttendArgs a{};
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.indices = indices;
+  a.O = O;
+  a.queries = static_cast<int>(queries);
+  a.n_keys = n_keys;
+  a.key_stride = n_keys;
+  a.q_heads = q_heads;
+  a.kv_heads = kv_heads;
+  a.group = group;
+  a.leaf_block = leaf_block;
+  a.beam = beam;
+  a.n_blocks = n_keys / leaf_block;
+  a.scale_log2 = static_cast<float>(sc * 1.4426950408889634);
+  const int64_t groups = static_cast<int64_t>(batch) * kv_heads;
+  a.splits = tis::attend_group_splits(groups, group, beam);
+  const size_t need = tis::attend_group_workspace(groups, group, head_dim, a.splits);
+  if (need > 0) {
+    if (!workspace) return fail(TIS_E_NULL, "%s: a workspace of %zu bytes is required", who, need);
+    if (!aligned(workspace, 16)) return fail(TIS_E_ALIGN, "%s: workspace must be 16-byte aligned", who);
+    if (workspace_bytes < need)
+      return fail(TIS_E_WORKSPACE, "%s: workspace %zu bytes < %zu required", who, workspace_bytes,
+                  need);
+    a.arrive = static_cast<unsigned *>(workspace);
+    a.part = reinterpret_cast<float *>(static_cast<unsigned char *>(workspace) + tis::kArriveBytes);
+  }
+  const tis::Dt dt = dtype == TIS_BF16 ? tis::Dt::BF16 : tis::Dt::F32;
+  return hip_status(tis::launch_attend_group(dt, head_dim, a, static_cast<hipStream_t>(stream)),
+                    "tis_tree_attend_grouped launch");
+}
+
 }  // extern "C"
 
 namespace {

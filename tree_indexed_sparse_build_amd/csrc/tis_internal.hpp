@@ -136,6 +136,15 @@ constexpr size_t kArriveBytes = kSplitMaxQueries * sizeof(unsigned);
 size_t attend_workspace(int64_t queries, int head_dim, int splits);
 hipError_t launch_attend(Dt dt, int head_dim, const AttendArgs &a, hipStream_t s);
 
+// Grouped attend: the G query heads of a KV head together (splits = parts
+// per group; a split call has fewer than kSplitMaxQueries groups, whose
+// arrival counters sit where the attend's are).
+constexpr int kGroupMaxHeads = 64;     // heads per group (one 64-bit mask)
+constexpr int kGroupMaxEntries = 512;  // slots per group, G * beam
+int attend_group_splits(int64_t groups, int group, int beam);
+size_t attend_group_workspace(int64_t groups, int group, int head_dim, int splits);
+hipError_t launch_attend_group(Dt dt, int head_dim, const AttendArgs &a, hipStream_t s);
+
 // ---------------------------------------------------------------- decode --
 // Route and attend of each query in one workgroup (one launch).
 hipError_t launch_decode(Dt dt, Dt sdt, int head_dim, const RouteArgs &ra,

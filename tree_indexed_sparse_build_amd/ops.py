@@ -205,6 +205,37 @@ def tree_attend(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, indices: torc
     return O
 
 
+def tree_attend_grouped(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
+                        indices: torch.Tensor, leaf_block: int,
+                        scale: Optional[float] = None) -> torch.Tensor:
+    """tree_attend with the query heads that share a KV head attended
+    together (each shared leaf read once per group, scores and P V on the
+    matrix cores).  Same arguments and result as tree_attend, to fp32
+    rounding."""
+    _need_device(Q, K, V, indices)
+    if indices.dtype != torch.int32:
+        raise TypeError("indices must be int32")
+    if K.dtype != Q.dtype or V.dtype != Q.dtype:
+        raise TypeError("Q, K and V must share one dtype")
+    B, Hq, d = Q.shape
+    _, Hkv, N, _ = K.shape
+    if tuple(V.shape) != tuple(K.shape) or K.shape[0] != B or K.shape[3] != d:
+        raise ValueError("shape mismatch between Q, K and V")
+    if indices.dim() != 3 or indices.shape[0] != B or indices.shape[1] != Hq:
+        raise ValueError("indices must be [B, Hq, W]")
+    W = indices.shape[2]
+    O = torch.empty((B, Hq, d), dtype=torch.float32, device=Q.device)
+    L = lib()
+    wsb = L.tis_attend_grouped_workspace_bytes(B, Hq, Hkv, d, W)
+    ws = _workspace(Q.device, "attend", wsb) if wsb else None
+    check(L.tis_tree_attend_grouped(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q), B,
+                                    Hq, Hkv, N, d, leaf_block, indices.data_ptr(), W,
+                                    0.0 if scale is None else float(scale), O.data_ptr(),
+                                    ws.data_ptr() if ws is not None else None,
+                                    ws.numel() if ws is not None else 0, _stream(Q.device)))
+    return O
+
+
 def tree_decode(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, tree: Tree, beam: int,
                 scale: Optional[float] = None, return_indices: bool = False):
     """Route and attend every query in one launch.  Returns O (float32
@@ -403,6 +434,10 @@ class DecodePlan:
         wsd = L.tis_decode_workspace_bytes(B, Hq, d, beam, leaf_block)
         self.ws_decode = (torch.zeros(wsd, dtype=torch.uint8, device=K.device) if wsd
                           else None)
+        G = Hq // H
+        wsg = L.tis_attend_grouped_workspace_bytes(B, Hq, H, d, beam)
+        self.ws_grouped = (torch.zeros(max(wsg, 256), dtype=torch.uint8, device=K.device)
+                           if G <= 64 and G * beam <= 512 else None)
         self.indices = torch.empty((B, Hq, beam), dtype=torch.int32, device=K.device)
         self.out = torch.empty((B, Hq, d), dtype=torch.float32, device=K.device)
         self.tree_c = TisTree(0, 0, 0, 0, 0, 0, 0, code, self.summaries.data_ptr())
@@ -431,6 +466,17 @@ class DecodePlan:
                                         else self.ws_attend.data_ptr(),
                                         0 if self.ws_attend is None
                                         else self.ws_attend.numel(), _stream(self.device)))
+
+    def attend_grouped(self) -> None:
+        """attend() with the query heads of each KV head attended together
+        (tree_attend_grouped) over the routed indices, into self.out."""
+        B, H, N, d, b, Lb, lv = self.geom
+        if self.ws_grouped is None:
+            raise RuntimeError("this geometry has no grouped attend (G > 64 or G * beam > 512)")
+        check(self._lib.tis_tree_attend_grouped(
+            self.Q.data_ptr(), self.K.data_ptr(), self.V.data_ptr(), self.dt, B, self.q_heads, H,
+            N, d, Lb, self.indices.data_ptr(), self.beam, self.scale, self.out.data_ptr(),
+            self.ws_grouped.data_ptr(), self.ws_grouped.numel(), _stream(self.device)))
 
     def decode(self) -> None:
         """Route and attend in one launch (indices not written)."""
