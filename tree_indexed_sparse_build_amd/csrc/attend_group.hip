@@ -7,25 +7,25 @@
 // its own blocks; what changes is the order of work: a leaf that several
 // heads of a group kept is loaded once for all of them.
 //
-// A workgroup takes a share of one group's leaves (the group = one (batch,
-// KV head) and its G query heads):
-//   * it loads the group's G x W slot lists and forms their union in LDS,
-//     ascending, each leaf with a G-bit mask of the heads that kept it
-//     (slot rules as tree_attend: negatives are empty, a repeat counts once,
-//     an entry >= N / L makes that head's row NaN);
-//   * `splits` workgroups share the union in equal runs of leaves; within
-//     one, each wave takes tiles of 16 keys in turn, the loads of up to 4
-//     tiles (2 for fp32) issued before the first computes; it computes the 16 keys x
-//     16 heads scores on MFMA (S^T = K Q^T, fp32 accumulation), masks each
-//     head to its own leaves, keeps an online softmax per head, and adds
-//     P V on MFMA (bf16: each weight in three bf16 parts, fp32 precision;
-//     V goes through a per-wave LDS tile, whose rows are read back 4 keys
-//     of one dim per lane, the operand order of the product);
-//   * the waves' states meet in LDS (log-sum-exp factors, then a fixed
-//     pairwise sum), and the workgroup writes O, or its partial state when
-//     the group is split: the last workgroup of the group to finish merges
-//     the partial states (device-coherent stores and loads, an agent-scope
-//     arrival count, as in the split attend).
+// The group is one (batch, KV head) and its G query heads, its slot list
+// the G x W entries of its heads (head-major).  `splits` workgroups share
+// it, part p owning the entries [p n / S, (p + 1) n / S):
+//   * the part loads the whole list and, for each entry it owns, finds
+//     whether an earlier entry holds the same leaf and which heads hold it
+//     (a 64-bit mask); it attends over the leaves whose first entry it owns,
+//     for all their heads (slot rules as tree_attend: negatives are empty, a
+//     repeat counts once, an entry >= N / L makes that head's row NaN);
+//   * each wave takes tiles of 16 keys in turn: 16 keys x 16 heads scores on
+//     MFMA (S^T = K Q^T, fp32 accumulation), each head masked to its own
+//     leaves, an online softmax per head, and P V on MFMA (bf16: each weight
+//     in three bf16 parts, fp32 precision; V goes through a per-wave LDS
+//     tile whose rows are read back 4 keys of one dim per lane, the operand
+//     order of the product);
+//   * the waves' states meet in LDS in one round and are combined by
+//     log-sum-exp in wave order; the workgroup writes O, or its partial
+//     state when the group is split, and the last part of the group to
+//     finish merges the partial states (device-coherent stores and loads,
+//     an agent-scope arrival count, as in the split attend).
 // More than 16 heads (up to 64) take 2 or 4 row blocks of 16, a wave per
 // block per tile.
 #include "attend_query.hpp"
@@ -195,13 +195,11 @@ __global__ void __launch_bounds__(GroupWaves<T>::NW * 64) k_attend_group(AttendA
   };
   using KReg = typename TM::KReg;
   using VReg = typename TM::VReg;
-  // loads of tile t (past the end, or not a first entry: leaf 0, unused)
+  // loads of tile t (one with rows: a first entry's leaf)
   const auto fetch = [&](int t, KReg &kr, uint4 *vr) {
-    const int tt = t < T_ ? t : 0;
-    const int u = tt / tpl;
-    const int kt = (tt - u * tpl) * 16;
-    const int leaf = t < T_ && s_own[u] >= 0 ? s_own[u] : 0;
-    const int64_t base = static_cast<int64_t>(leaf) * L;
+    const int u = t / tpl;
+    const int kt = (t - u * tpl) * 16;
+    const int64_t base = static_cast<int64_t>(s_own[u]) * L;
     TM::load_k(kr, kh + (base + min(kt + r, L - 1)) * D, g);
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
@@ -264,20 +262,15 @@ __global__ void __launch_bounds__(GroupWaves<T>::NW * 64) k_attend_group(AttendA
     __builtin_amdgcn_wave_barrier();
   };
 
-  // passes of up to MT tiles (t, t + NS, ...): every load of a pass is
-  // issued before its first tile computes
-  constexpr int MT = ES == 2 ? 4 : 2;
-  for (int t0 = st; t0 < T_; t0 += NS * MT) {
-    KReg kr[MT];
-    uint4 vr[MT][VPT];
-#pragma unroll
-    for (int j = 0; j < MT; ++j) fetch(t0 + j * NS, kr[j], vr[j]);
-#pragma unroll
-    for (int j = 0; j < MT; ++j) {
-      const int t = t0 + j * NS;
-      const unsigned rows = t < T_ ? rows_of(t) : 0u;
-      if (rows != 0u) compute(t, rows, kr[j], vr[j]);
-    }
+  // tiles t, t + NS, ...: one at a time (measured: issuing the loads of 2
+  // or 4 tiles before the first computes was 2-13% slower, warm)
+  for (int t = st; t < T_; t += NS) {
+    const unsigned rows = rows_of(t);
+    if (rows == 0u) continue;
+    KReg kr;
+    uint4 vr[VPT];
+    fetch(t, kr, vr);
+    compute(t, rows, kr, vr);
   }
 
   // ---- the waves' states meet in LDS: per head reference and sum, and
