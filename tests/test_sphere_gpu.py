@@ -129,6 +129,12 @@ CASES = [
     (_custom("sph_single_level", "bf16", 16, 8, 1), (4, 60), "f32"),
     (_custom("sph_clustered", "bf16", 8, 64, 2, B=2, Hkv=2, G=4, gen="mixture",
              clusters=32), (32, 100, 200), "f32"),
+    # whole-wave leaf blocks (32, 64 and 96 keys: several row batches a
+    # leaf), 1 to 8 levels, both head dims and summary types
+    (_custom("sph_l32_d64", "bf16", 4, 32, 4, d=64), (1, 17, 90), "f32"),
+    (_custom("sph_l64_lv6_bf16s", "bf16", 2, 64, 6), (1, 33), "bf16"),
+    (_custom("sph_l96_lv8", "bf16", 2, 96, 8, d=64, Hkv=1, G=2), (2, 40), "f32"),
+    (_custom("sph_l32_lv1", "bf16", 16, 32, 1, B=2), (3, 50), "f32"),
 ]
 
 
