@@ -96,8 +96,10 @@ __global__ void __launch_bounds__(GroupWaves<T>::NW * 64) k_attend_group(AttendA
   constexpr int VBYTES = NW * VT::BYTES;     // every wave's V tile
   // slot entries, padded to whole 4-entry reads of every lane's slice
   __shared__ __align__(16) int s_ent[kGroupMaxEntries + 256];
-  __shared__ int s_own[kGroupMaxEntries];    // this part's entries: their leaf if the
-  __shared__ unsigned long long s_omask[kGroupMaxEntries];  // first of it, else -1
+  // this part's entries: the leaf, if the entry is the leaf's first in the
+  // list (else -1), and the heads whose entries hold it
+  __shared__ int s_own[kGroupMaxEntries];
+  __shared__ unsigned long long s_omask[kGroupMaxEntries];
   __shared__ float s_m[NW][16], s_l[NW][16];
   __shared__ unsigned long long s_bad;
   __shared__ int s_last;
