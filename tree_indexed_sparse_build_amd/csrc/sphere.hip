@@ -18,6 +18,10 @@
 //    subtraction and an FMA per key element and level).  The ancestors'
 //    summaries go through LDS; only the nodes that change are reloaded, and
 //    the next leaf's own centre is fetched ahead of its rows.
+//  * k_radius_quad: the same maxima for leaf blocks of at least 64 keys and
+//    trees of up to 8 levels: 4 lanes a key, 4 keys a lane sharing each
+//    widened centre value, a running maximum per level reduced across the
+//    wave only when the level's node ends.
 //  * k_radius_finish: radius = smallest float32 r with r * r >= the maximum
 //    (r * r is exact in fp64, so the test is exact).
 //  * threshold walk: one workgroup per query; level by level, the children
@@ -181,6 +185,193 @@ __global__ void __launch_bounds__(kRadiusWaves * 64) k_radius(RadiusArgs a) {
 }
 
 // Smallest float32 r >= 0 with r * r >= D, from the reduced maxima.
+// The same maxima for leaf blocks of at least 64 keys and trees of up to 8
+// levels: a wave takes 64 keys of one leaf at a time, a lane a quarter of 4
+// keys (keys s, s + 16, s + 32, s + 48 of the batch for lane slot s; 64
+// contiguous bytes a load round across a key's 4 lanes).  Each centre
+// value is widened once and serves the lane's 4 keys, a key's squared
+// distance needs only the two in-quad exchanges (DPP, no LDS swizzle), and
+// each lane keeps a running maximum per level that is reduced across the
+// wave only when that level's node ends.  (k_radius sums a key across 16
+// lanes, widens each centre value for every 4 keys and takes a wave
+// maximum every 16 keys; measured on the 32K-key GQA workload, its VALU
+// and its loads did not overlap.)  Centres and owner lanes as in k_radius.
+template <typename T, typename S, int D, int LV>
+__global__ void __launch_bounds__(kRadiusWaves * 64) k_radius_quad(RadiusArgs a) {
+  constexpr int ES = static_cast<int>(sizeof(T));
+  constexpr int NL = D * ES / 64;  // 16-byte loads a lane per key (a quarter key)
+  constexpr int EPL = 16 / ES;     // elements a load
+  constexpr int KPL = 4;           // keys a lane
+  __shared__ float ctr[kRadiusWaves][LV][D];  // this leaf's ancestors' centres
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int64_t gw = static_cast<int64_t>(blockIdx.x) * kRadiusWaves + w;
+  const int64_t head = gw / a.waves_per_head;
+  if (head >= a.heads) return;  // whole wave: no barrier below spans waves
+  const int64_t n_leaves = a.n_at[LV];
+  const int64_t leaf0 = (gw - head * a.waves_per_head) * a.leaves_per_wave;
+  const int64_t leaf1 = min(leaf0 + a.leaves_per_wave, n_leaves);
+  const int L = a.leaf_block;
+  const int ks = lane >> 2;   // this lane's key slot within the batch
+  const int part = lane & 3;  // and its quarter: bytes part * 16 + 64 i
+  const T *kh = static_cast<const T *>(a.K) + head * a.n_keys * D;
+  const S *summ = static_cast<const S *>(a.summ);
+  float (*cw)[D] = ctr[w];
+
+  // the centres of `leaf`'s ancestors, this lane's columns lane + 64 j
+  // (fetched a leaf ahead, written to LDS when the leaf starts)
+  constexpr int CPL = D / 64;
+  const auto fetch_centres = [&](int64_t leaf, float (&f)[LV][CPL]) {
+#pragma unroll
+    for (int l = 1; l <= LV; ++l) {
+      const S *row = summ + a.summ_off[l] + (head * a.n_at[l] + leaf / a.span[l]) * D;
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        const int c = lane + 64 * j;
+        if constexpr (sizeof(S) == 4)
+          f[l - 1][j] = reinterpret_cast<const float *>(row)[c];
+        else
+          f[l - 1][j] = __uint_as_float(
+              static_cast<uint32_t>(reinterpret_cast<const bf16_bits *>(row)[c].v) << 16);
+      }
+    }
+  };
+  const auto enter = [&](const float (&f)[LV][CPL]) {
+#pragma unroll
+    for (int l = 0; l < LV; ++l)
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) cw[l][lane + 64 * j] = f[l][j];
+    // LDS accesses of one wave are performed in order: the rows written
+    // above are what the lanes read below
+    __builtin_amdgcn_wave_barrier();
+  };
+  // the finished nodes' maxima: a wave maximum of the lanes' running
+  // maxima, taken by the level's owner lane (l - 1) to the node's slot
+  double run[LV];
+#pragma unroll
+  for (int l = 0; l < LV; ++l) run[l] = 0.0;
+  const auto finish = [&](int64_t leaf, bool last) {
+#pragma unroll
+    for (int l = 1; l <= LV; ++l) {
+      const int64_t node = leaf / a.span[l];
+      if (!last && node == (leaf + 1) / a.span[l]) continue;  // the node goes on
+      const double m = wave_max_d(run[l - 1]);
+      if (lane == l - 1)
+        atomicMax(a.d2 + a.node_off[l] + head * a.n_at[l] + node,
+                  static_cast<unsigned long long>(__double_as_longlong(m)));
+      run[l - 1] = 0.0;
+    }
+  };
+  // load round i of the batch at row r0 of `leaf`: 16 bytes of each of the
+  // lane's keys (rows past the block read its last row and are masked)
+  const auto load_round = [&](int64_t leaf, int r0, int i, uint4 (&kv)[KPL]) {
+#pragma unroll
+    for (int k = 0; k < KPL; ++k) {
+      const int row = min(r0 + ks + 16 * k, L - 1);
+      kv[k] = load16(reinterpret_cast<const unsigned char *>(kh + (leaf * L + row) * D) +
+                     part * 16 + i * 64);
+    }
+  };
+  // one stream of load rounds over the wave's leaves, batches and rounds,
+  // the next round's loads (and at a leaf's last round the next leaf's
+  // centres) in flight while this one computes
+  if (leaf0 >= leaf1) return;
+  {
+    float f[LV][CPL];
+    fetch_centres(leaf0, f);
+    enter(f);
+  }
+  int64_t leaf = leaf0;
+  int r0 = 0, i = 0;
+  uint4 cur[KPL], nxt[KPL];
+  float pre[LV][CPL];
+  load_round(leaf, r0, i, cur);
+  double sq[KPL][LV];
+#pragma unroll
+  for (int k = 0; k < KPL; ++k)
+#pragma unroll
+    for (int l = 0; l < LV; ++l) sq[k][l] = 0.0;
+  for (;;) {
+    // the next round
+    int64_t nleaf = leaf;
+    int nr0 = r0, ni = i + 1;
+    if (ni == NL) {
+      ni = 0;
+      nr0 += 16 * KPL;
+      if (nr0 >= L) {
+        nr0 = 0;
+        ++nleaf;
+      }
+    }
+    const bool more = nleaf < leaf1;
+    if (more) load_round(nleaf, nr0, ni, nxt);
+    const bool new_leaf = more && nleaf != leaf;
+    if (new_leaf) fetch_centres(nleaf, pre);
+    double kd[KPL][EPL];  // this round's elements of the lane's keys, widened
+#pragma unroll
+    for (int k = 0; k < KPL; ++k) {
+      float fv[EPL];
+      Vec16<T>::unpack(cur[k], fv);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) kd[k][e] = static_cast<double>(fv[e]);
+    }
+#pragma unroll
+    for (int l = 0; l < LV; ++l) {
+      const float *c = cw[l] + (part * 16 + i * 64) / ES;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const double cd = static_cast<double>(c[e]);
+#pragma unroll
+        for (int k = 0; k < KPL; ++k) {
+          const double diff = kd[k][e] - cd;  // exact: both are float32 values
+          sq[k][l] = fma(diff, diff, sq[k][l]);
+        }
+      }
+    }
+    if (i == NL - 1) {  // the batch's keys are complete
+#pragma unroll
+      for (int k = 0; k < KPL; ++k) {
+        const bool valid = r0 + ks + 16 * k < L;
+#pragma unroll
+        for (int l = 0; l < LV; ++l) {
+          double d = sq[k][l];
+          d += xor_lane<1>(d, lane);
+          d += xor_lane<2>(d, lane);  // the key's squared distance, in its 4 lanes
+          run[l] = fmax(run[l], valid ? d : 0.0);
+          sq[k][l] = 0.0;
+        }
+      }
+    }
+    if (!more || new_leaf) {
+      finish(leaf, !more);
+      if (!more) break;
+      __builtin_amdgcn_wave_barrier();  // this leaf's centre reads come first
+      enter(pre);
+    }
+    leaf = nleaf;
+    r0 = nr0;
+    i = ni;
+#pragma unroll
+    for (int k = 0; k < KPL; ++k) cur[k] = nxt[k];
+  }
+}
+
+template <typename T, typename S, int D>
+bool launch_radius_quad(const RadiusArgs &a, dim3 grid, hipStream_t s) {
+  const dim3 block(kRadiusWaves * 64);
+  switch (a.levels) {
+    case 1: hipLaunchKernelGGL((k_radius_quad<T, S, D, 1>), grid, block, 0, s, a); return true;
+    case 2: hipLaunchKernelGGL((k_radius_quad<T, S, D, 2>), grid, block, 0, s, a); return true;
+    case 3: hipLaunchKernelGGL((k_radius_quad<T, S, D, 3>), grid, block, 0, s, a); return true;
+    case 4: hipLaunchKernelGGL((k_radius_quad<T, S, D, 4>), grid, block, 0, s, a); return true;
+    case 5: hipLaunchKernelGGL((k_radius_quad<T, S, D, 5>), grid, block, 0, s, a); return true;
+    case 6: hipLaunchKernelGGL((k_radius_quad<T, S, D, 6>), grid, block, 0, s, a); return true;
+    case 7: hipLaunchKernelGGL((k_radius_quad<T, S, D, 7>), grid, block, 0, s, a); return true;
+    case 8: hipLaunchKernelGGL((k_radius_quad<T, S, D, 8>), grid, block, 0, s, a); return true;
+    default: return false;
+  }
+}
+
 __global__ void __launch_bounds__(256) k_radius_finish(const unsigned long long *d2,
                                                        float *radii, int64_t n) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -360,12 +551,19 @@ template <typename T, typename S>
 hipError_t launch_radii_ts(int head_dim, const RadiusArgs &a, int64_t waves, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>((waves + kRadiusWaves - 1) / kRadiusWaves));
   const dim3 block(kRadiusWaves * 64);
-  if (head_dim == 128)
-    hipLaunchKernelGGL((k_radius<T, S, 128>), grid, block, 0, s, a);
-  else if (head_dim == 64)
-    hipLaunchKernelGGL((k_radius<T, S, 64>), grid, block, 0, s, a);
-  else
-    return hipErrorInvalidValue;
+  // leaf blocks of 64 keys or more, up to 8 levels: 4 lanes a key, 4 keys
+  // a lane; otherwise 16 lanes a key
+  bool quad = false;
+  if (head_dim != 128 && head_dim != 64) return hipErrorInvalidValue;
+  if (a.leaf_block >= 64)
+    quad = head_dim == 128 ? launch_radius_quad<T, S, 128>(a, grid, s)
+                           : launch_radius_quad<T, S, 64>(a, grid, s);
+  if (!quad) {
+    if (head_dim == 128)
+      hipLaunchKernelGGL((k_radius<T, S, 128>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((k_radius<T, S, 64>), grid, block, 0, s, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 g2(static_cast<unsigned>((a.total_nodes + 255) / 256));
