@@ -135,6 +135,9 @@ CASES = [
     (_custom("sph_l64_lv6_bf16s", "bf16", 2, 64, 6), (1, 33), "bf16"),
     (_custom("sph_l96_lv8", "bf16", 2, 96, 8, d=64, Hkv=1, G=2), (2, 40), "f32"),
     (_custom("sph_l32_lv1", "bf16", 16, 32, 1, B=2), (3, 50), "f32"),
+    # float32 keys in leaf blocks of 64 keys or more (4 lanes a key, 4 keys a lane)
+    (_custom("sph_f32_l64_d128", "f32", 4, 64, 3), (1, 20, 100), "f32"),
+    (_custom("sph_f32_l128_d64_bf16s", "f32", 2, 128, 4, d=64), (2, 70), "bf16"),
 ]
 
 
