@@ -253,6 +253,44 @@ def trace_summary(db_path: str, out_path: str, title: str, command: str,
             f.write("\n".join(head + body.get(n, [])) + "\n")
 
 
+def counters_summary(csv_path: str, out_path: str, title: str, command: str,
+                     kernels: str) -> None:
+    """Writes a markdown summary of a rocprofv3 --pmc counter file: for each
+    kernel whose name holds one of `kernels` (comma-separated), by grid and
+    workgroup size, the dispatches and the mean of every counter per
+    dispatch."""
+    import csv
+    keys = [k for k in kernels.split(",") if k]
+    vals = {}
+    counters = []
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"]
+            if not any(k in name for k in keys):
+                continue
+            short = name.replace("(anonymous namespace)::", "").replace("tis::", "")
+            short = short.replace("void ", "", 1).split("(")[0]
+            c = r["Counter_Name"]
+            if c not in counters:
+                counters.append(c)
+            key = (short, r.get("Grid_Size", "?"), r.get("Workgroup_Size", "?"))
+            vals.setdefault(key, {}).setdefault(c, []).append(float(r["Counter_Value"]))
+    lines = [f"# {title}", "", "Command (run from the repository root):", "", "```", command,
+             "```", "", "Mean per dispatch of each counter (rocprofv3 --pmc).", "",
+             "| kernel | grid x workgroup (threads) | dispatches | " + " | ".join(counters) + " |",
+             "|---|---|---|" + "---|" * len(counters)]
+    for (short, g, w), cs in sorted(vals.items()):
+        n = max(len(v) for v in cs.values())
+        cells = []
+        for c in counters:
+            xs = cs.get(c, [])
+            m = sum(xs) / len(xs) if xs else float("nan")
+            cells.append(f"{m:.4g}" if abs(m) < 1e6 else f"{m:.4e}")
+        lines.append(f"| `{short}` | {g} x {w} | {n} | " + " | ".join(cells) + " |")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 # --------------------------------------------------------------- probes --
 
 class Probes:
@@ -741,7 +779,14 @@ def main(argv=None):
                     metavar=("DB", "OUT_MD", "TITLE", "COMMAND", "SEGMENTS"),
                     help="write a markdown kernel-trace summary of a rocprofv3 database (its "
                          "workload segments named by SEGMENTS, comma-separated) and exit")
+    ap.add_argument("--counters-from", nargs=5,
+                    metavar=("CSV", "OUT_MD", "TITLE", "COMMAND", "KERNELS"),
+                    help="write a markdown summary of a rocprofv3 --pmc counter file for the "
+                         "kernels named by KERNELS (comma-separated substrings) and exit")
     args = ap.parse_args(argv)
+    if args.counters_from:
+        counters_summary(*args.counters_from)
+        return 0
     if args.traffic_from:
         print(json.dumps(traffic_from_counters(args.workload, *args.traffic_from)))
         return 0

@@ -282,9 +282,11 @@ __global__ void __launch_bounds__(1024) k_build(BuildArgs a) {
     const int r0 = lb * U * R;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int row = r0 + u * R + rsub;
-      const T *p = kl + static_cast<int64_t>(row) * D;
-      v[u] = row >= L ? make_uint4(0u, 0u, 0u, 0u) : a.stream_loads ? load16_stream(p) : load16(p);
+      // rows past the leaf load its last row again (added as zero): every
+      // load is issued unconditionally, so the wait before a batch is used
+      // counts only the loads issued before it
+      const int row = min(r0 + u * R + rsub, L - 1);
+      v[u] = load16_stream(kl + static_cast<int64_t>(row) * D);
     }
     if (++lb == nb) {
       lb = 0;
@@ -294,11 +296,17 @@ __global__ void __launch_bounds__(1024) k_build(BuildArgs a) {
   double acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.0;
+  const bool ragged = L % (U * R) != 0;
   auto consume = [&](const uint4 (&v)[U]) {
+    const int rc = cb * U * R + rsub;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float f[E];
       Vec16<T>::unpack(v[u], f);
+      if (ragged && rc + u * R >= L) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) f[e] = 0.0f;
+      }
 #pragma unroll
       for (int e = 0; e < E; ++e) acc[e] += static_cast<double>(f[e]);
     }
@@ -322,7 +330,7 @@ __global__ void __launch_bounds__(1024) k_build(BuildArgs a) {
       } else if (a.stage) {
         stage_cols<CPL>(stage + (w * a.wave_leaves + (cc - 1)) * D + colf, m);  // leaf cc - 1
       } else {
-        store_cols<CPL>(summ + a.summ_off[lv] + node * D + colf, m, a.stream_loads != 0);
+        store_cols<CPL>(summ + a.summ_off[lv] + node * D + colf, m, a.through_stores != 0);
       }
     }
     double carry[CPL];
@@ -356,7 +364,7 @@ __global__ void __launch_bounds__(1024) k_build(BuildArgs a) {
           const int row = stage_base(k + 1) + w * per + static_cast<int>(nid[k] - wnode * per);
           stage_cols<CPL>(stage + static_cast<int64_t>(row) * D + colf, m);
         } else {
-          store_cols<CPL>(summ + a.summ_off[lvl] + node * D + colf, m, a.stream_loads != 0);
+          store_cols<CPL>(summ + a.summ_off[lvl] + node * D + colf, m, a.through_stores != 0);
         }
       }
 #pragma unroll
@@ -368,17 +376,25 @@ __global__ void __launch_bounds__(1024) k_build(BuildArgs a) {
       ++nid[k];
     }
   };
+  // The steady-state loop issues both buffers unconditionally, so the
+  // compiler's wait before a batch is used leaves the other batch's loads in
+  // flight (a load issued under a condition makes it wait for every load).
   uint4 va[U], vb[U];
   issue(va);
-  while (true) {
-    bool more = lc < a.wave_leaves;
-    if (more) issue(vb);
+  int64_t left = a.wave_leaves * nb - 1;  // batches still to issue
+  while (left >= 2) {
+    issue(vb);
     consume(va);
-    if (!more) break;
-    more = lc < a.wave_leaves;
-    if (more) issue(va);
+    issue(va);
     consume(vb);
-    if (!more) break;
+    left -= 2;
+  }
+  if (left == 1) {
+    issue(vb);
+    consume(va);
+    consume(vb);
+  } else {
+    consume(va);
   }
 
   // ---- the workgroup's inner levels, from the waves' fp64 root sums in LDS

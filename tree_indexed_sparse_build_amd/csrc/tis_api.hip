@@ -223,7 +223,7 @@ tis_status tis_tree_build(const void *K, tis_dtype dtype, int batch, int kv_head
   a.levels = levels;
   a.root_level = p.root_level;
   a.wave_depth = p.wave_depth;
-  a.stream_loads = 1;  // K is read once: streaming loads, whatever its size
+  a.through_stores = 1;  // K is streamed once, whatever its size
   a.top_rows = 1;
   for (int l = 2; l < p.root_level; ++l) a.top_rows *= branching;
   a.chunks_per_l1 = 1;

@@ -44,7 +44,8 @@ struct BuildArgs {
   int root_level;        // r
   int wave_depth;        // kw
   uint32_t pow2_levels;  // bit l set: M_l = N / n_l is a power of two
-  int stream_loads;      // nonzero: K loads carry the non-temporal hint
+  int through_stores;    // nonzero: rows written between K loads use device-coherent
+                         // stores (K loads always carry the non-temporal hint)
   int stage;             // nonzero: the wave-level summary rows wait in LDS
                          // and leave in one burst after the last K load
   int64_t top_rows;      // b^(r-2): level r-1 nodes under one level-1 node
