@@ -170,3 +170,23 @@ def test_trace_summary_groups_by_cache_state(tmp_path):
     assert any("`k_decode" in ln and "probe read of the summaries | 1 | 18.00" in ln for ln in rows2)
     assert not any("`k_build" in ln for ln in rows2)
     assert "cmd" in first and first.startswith("# T: first")
+
+
+def test_counters_summary_means_per_kernel(tmp_path):
+    csv_path = tmp_path / "c.csv"
+    grp = "void tis::(anonymous namespace)::k_attend_group<bf16_bits, 128, 1>(tis::AttendArgs)"
+    att = "void tis::(anonymous namespace)::k_attend<bf16_bits, 128>(tis::AttendArgs)"
+    rows = ["Dispatch_Id,Kernel_Name,Grid_Size,Workgroup_Size,Counter_Name,Counter_Value"]
+    for i, (name, util) in enumerate([(grp, 1.5), (grp, 2.5), (att, 0.0)]):
+        rows.append(f'{i},"{name}",65536,512,MfmaUtil,{util}')
+        rows.append(f'{i},"{name}",65536,512,SQ_INSTS_VALU,{1000 * (i + 1)}')
+    rows.append('9,"at::native::fill",1,1,MfmaUtil,7')
+    csv_path.write_text("\n".join(rows) + "\n")
+    out = tmp_path / "c.md"
+    bench.counters_summary(str(csv_path), str(out), "T", "cmd", "k_attend")
+    text = out.read_text()
+    lines = [ln for ln in text.splitlines() if ln.startswith("| `")]
+    assert len(lines) == 2 and not any("fill" in ln for ln in lines)
+    g = [ln for ln in lines if "k_attend_group" in ln][0]
+    assert "| 65536 x 512 | 2 | 2 | 1500 |" in g      # means over the two dispatches
+    assert "| MfmaUtil | SQ_INSTS_VALU |" in text and text.startswith("# T")
