@@ -23,7 +23,7 @@ __global__ void __launch_bounds__(kAttendMaxWaves * 64) k_attend(AttendArgs a) {
   const int tid = threadIdx.x;
   // part sp of query qi; the parts of a query are queries apart in the grid,
   // so with a multiple of 8 queries they land on one XCD and share its L2
-  const int sp = blockIdx.x / a.queries;
+  const int sp = div_u(static_cast<int>(blockIdx.x), a.queries);
   const int qi = query_of_slot(blockIdx.x - sp * a.queries, a.queries, a.group);
   const int W = a.beam;
 
@@ -35,14 +35,16 @@ __global__ void __launch_bounds__(kAttendMaxWaves * 64) k_attend(AttendArgs a) {
   for (int s = tid; s < W; s += blockDim.x) {
     const int idx = s_idx[s];
     const bool bad = idx >= a.n_blocks;
-    bool use = idx >= 0 && !bad;
-    for (int j = 0; j < s && use; ++j) use = s_idx[j] != idx;
-    s_use[s] = use;
+    // a repeat of an earlier slot counts once: the earlier slots are read
+    // without an early exit, so their LDS reads do not wait on each other
+    bool seen = false;
+    for (int j = 0; j < s; ++j) seen |= s_idx[j] == idx;
+    s_use[s] = idx >= 0 && !bad && !seen;
     if (bad) s_bad = 1;
   }
   __syncthreads();
-  const int s0 = sp * W / a.splits;
-  const int s1 = (sp + 1) * W / a.splits;
+  const int s0 = div_u(sp * W, a.splits);
+  const int s1 = div_u((sp + 1) * W, a.splits);
   float *part = a.splits > 1
                     ? a.part + (static_cast<int64_t>(qi) * a.splits + sp) * (D + kPartHeader)
                     : nullptr;

@@ -84,9 +84,9 @@ __device__ void attend_query(const AttendArgs &a, AttendShared<T, D, MW> &sh, in
   const int nw = blockDim.x >> 6;
   const int L = a.leaf_block;
   const int hr = PREFILL ? hrow : qi;
-  const int bi = hr / a.q_heads;
+  const int bi = div_u(hr, a.q_heads);
   const int hq = hr - bi * a.q_heads;
-  const int64_t head = static_cast<int64_t>(bi) * a.kv_heads + hq / a.group;
+  const int64_t head = static_cast<int64_t>(bi) * a.kv_heads + div_u(hq, a.group);
   const int col = (lane % LPR) * E;
   const int rsub = lane / LPR;
   const int64_t n_keys = PREFILL ? nk : a.n_keys;
@@ -104,7 +104,7 @@ __device__ void attend_query(const AttendArgs &a, AttendShared<T, D, MW> &sh, in
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
 
   for (int u = w; u < units; u += nw) {
-    const int s = u / nc;
+    const int s = div_u(u, nc);
     if (use && !use[s]) continue;
     const int r0 = (u - s * nc) * RB;
     const int64_t blk0 = static_cast<int64_t>(slots[s]) * L;

@@ -45,8 +45,8 @@ __device__ inline void decode_attend(const RouteArgs &ra, const AttendArgs &aa,
     for (int k = kept + static_cast<int>(threadIdx.x); k < ra.beam; k += kDecodeWaves * 64)
       out[k] = -1;
   }
-  const int s0 = sp * kept / aa.splits;
-  const int s1 = (sp + 1) * kept / aa.splits;
+  const int s0 = div_u(sp * kept, aa.splits);
+  const int s1 = div_u((sp + 1) * kept, aa.splits);
   float *part = aa.splits > 1
                     ? aa.part + (static_cast<int64_t>(qi) * aa.splits + sp) * (D + kPartHeader)
                     : nullptr;
@@ -59,7 +59,7 @@ __global__ void __launch_bounds__(kDecodeWaves * 64) k_decode(RouteArgs ra, Atte
   __shared__ RouteShared<kDecodeWaves> rsh;
   __shared__ AttendShared<T, D> ash;
   // part sp of query qi (see k_attend: a query's parts share an XCD)
-  const int sp = blockIdx.x / aa.queries;
+  const int sp = div_u(static_cast<int>(blockIdx.x), aa.queries);
   const int qi = query_of_slot(blockIdx.x - sp * aa.queries, aa.queries, aa.group);
   const uint4 qraw = attend_q_raw<T, D>(aa, qi);  // in flight during the walk
   // every part walks the tree (the repeated summary reads hit the XCD's L2)
@@ -94,9 +94,9 @@ template <typename T, typename S, int D> struct OpenNodes {
 
   __device__ OpenNodes(const RouteArgs &r, const AppendArgs &a, int q, uint64_t *k, double *os)
       : ra(r), ap(a), keys(k), open_score(os), qi(q) {
-    const int bi = q / ra.q_heads;
+    const int bi = div_u(q, ra.q_heads);
     const int hq = q - bi * ra.q_heads;
-    head = static_cast<int64_t>(bi) * ra.kv_heads + hq / ra.group;
+    head = static_cast<int64_t>(bi) * ra.kv_heads + div_u(hq, ra.group);
   }
 
   // pw: this wave among the NP; every lane of the wave calls it (the
@@ -178,7 +178,7 @@ __global__ void __launch_bounds__(kDecodeWaves * 64)
     append_one<T, S, D>(ap, static_cast<int64_t>(blockIdx.x) - nq);
     return;
   }
-  const int sp = blockIdx.x / aa.queries;
+  const int sp = div_u(static_cast<int>(blockIdx.x), aa.queries);
   const int qi = query_of_slot(blockIdx.x - sp * aa.queries, aa.queries, aa.group);
   const uint4 qraw = attend_q_raw<T, D>(aa, qi);
   const OpenNodes<T, S, D> open(ra, ap, qi, rsh.keys, open_score);

@@ -128,7 +128,7 @@ template <int LAYOUT> struct LevelCursor {
     cl = c;
     b = ra.branching;
     l = l0;
-    heads = static_cast<int64_t>(ra.queries / ra.q_heads) * ra.kv_heads;
+    heads = static_cast<int64_t>(div_u(ra.queries, ra.q_heads)) * ra.kv_heads;
     if constexpr (LAYOUT == 0) {
       // full tree: level l has b^l nodes, levels 1 .. l-1 come first
       int64_t n = 1;
@@ -299,9 +299,9 @@ __device__ int route_walk(const RouteArgs &a, RouteShared<NW, SMAXC> &sh, int qi
   const int w = tid >> 6;
   // (batch, query head) row of the query: qi itself, or given (prefill)
   const int hr = LAYOUT == 2 ? hrow : qi;
-  const int bi = hr / a.q_heads;
+  const int bi = div_u(hr, a.q_heads);
   const int hq = hr - bi * a.q_heads;
-  const int64_t head = static_cast<int64_t>(bi) * a.kv_heads + hq / a.group;
+  const int64_t head = static_cast<int64_t>(bi) * a.kv_heads + div_u(hq, a.group);
   const int b = a.branching;
   const int W = a.beam;
   const int lv = LAYOUT == 2 ? cl->levels : a.levels;

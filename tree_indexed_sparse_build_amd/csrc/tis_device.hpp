@@ -143,6 +143,20 @@ __device__ inline uint4 load16_stream(const void *p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// x / d and x % d for x >= 0 and a divisor d >= 1 that is the same for the
+// whole wave (a head count, a group size, a split count).  A 32-bit division
+// by a runtime value is a chain of some 25 scalar and vector instructions,
+// and the scalar ones go through the one scalar unit that all waves of a CU
+// share, so a 16-wave workgroup that divides on its critical path waits for
+// the whole CU's share of them.  Power-of-two divisors (every geometry of
+// the usual workloads) take a shift and a mask instead.
+__device__ inline int div_u(int x, int d) {
+  return (d & (d - 1)) == 0 ? x >> __builtin_ctz(static_cast<unsigned>(d)) : x / d;
+}
+__device__ inline int mod_u(int x, int d) {
+  return (d & (d - 1)) == 0 ? x & (d - 1) : x % d;
+}
+
 // Query served by workgroup slot s (0 <= s < queries).  Workgroups are
 // dispatched to the 8 XCDs in turn, so slots s = x (mod 8) share XCD x and
 // its L2.  When queries is a multiple of 8 * group, the group queries that
@@ -152,10 +166,10 @@ __device__ inline uint4 load16_stream(const void *p) {
 // the identity.  The map is a bijection either way; only locality depends
 // on it.
 __device__ inline int query_of_slot(int s, int queries, int group) {
-  if (group == 1 || queries % (8 * group) != 0) return s;
+  if (group == 1 || mod_u(queries, 8 * group) != 0) return s;
   const int x = s & 7;
   const int t = s >> 3;
-  return ((t / group) * 8 + x) * group + t % group;
+  return (div_u(t, group) * 8 + x) * group + mod_u(t, group);
 }
 
 // Row geometry for a wave reading rows of D elements of T, 16 bytes per lane:
