@@ -494,6 +494,56 @@ def attend_comparison(torch, probes, plan):
     return res
 
 
+TIMELINE_SLOTS, TIMELINE_WAVES = 24, 16
+
+
+def timeline_phases(st, khz: int, scored: int) -> dict:
+    """Phase times (us from the launch's first wave entry) of one decode's
+    timeline st [workgroups, 16 waves, 24 slots]: for each phase the median
+    and the latest over the waves that passed it (the walking waves for the
+    levels).  'K arrived' and 'V used' are each wave's first unit."""
+    import numpy as np
+    st = st.astype(np.int64)
+    t0 = st[:, :, 0][st[:, :, 0] > 0].min()
+    names = [(0, "entry", None)]
+    for j in range(min(scored, 8)):
+        names += [(8 + 2 * j, f"level {j + 1} scored", 8), (9 + 2 * j, f"level {j + 1} ranked", 8)]
+    names += [(1, "descent done", None), (2, "first K load issued", None),
+              (3, "K arrived", None), (4, "V used", None), (5, "units done", None),
+              (6, "partials merged", None), (7, "end", None)]
+    out = {}
+    for k, nm, waves in names:
+        v = st[:, :waves, k] if waves else st[:, :, k]
+        v = v[v > 0]
+        if v.size:
+            us = (v - t0) * 1e3 / khz
+            out[nm] = {"median_us": float(np.median(us)), "max_us": float(us.max())}
+    return out
+
+
+def decode_timeline(torch, probes, plan, w) -> dict:
+    """Where a decode's time goes: the instrumented decode's phase stamps
+    after a cache flush (cold) and right after two decodes (warm)."""
+    lib = plan._lib
+    khz = int(lib.tis_wall_clock_khz(torch.cuda.current_device()))
+    if khz <= 0 or plan.summary_dtype == "fp8":
+        return {}
+    tl = torch.zeros(plan.timeline_bytes() // 8, dtype=torch.int64, device=plan.device)
+    scored = w.levels - first_cut(w) + 1
+    res = {"clock_khz": khz}
+    for regime in ("cold", "warm"):
+        plan.decode()
+        plan.decode()
+        if regime == "cold":
+            probes.flush()
+        tl.zero_()
+        plan.decode_timeline(tl)
+        torch.cuda.synchronize()
+        st = tl.cpu().numpy().reshape(-1, TIMELINE_WAVES, TIMELINE_SLOTS)
+        res[regime] = timeline_phases(st, khz, scored)
+    return res
+
+
 def decode_floor(w, ceil_gbs, hop_us, dec_bytes):
     """Latency floor of one decode: the scored levels and the gather form a
     chain of dependent round trips (the first level's rows, each later
@@ -571,6 +621,7 @@ def measure_workload(tis, torch, probes, w, ceil_gbs, hop_us, reps, headline=Fal
                   "gbs_distinct": dist / (t * 1e3),
                   "frac_distinct": dist / (t * 1e3) / HBM_PEAK_GBS,
                   "floor_ratio": t / floor}
+    dec["timeline"] = decode_timeline(torch, probes, plan, w)
     res["decode"] = dec
     res["attend_only"] = attend_comparison(torch, probes, plan)
     if step is not None:
@@ -585,6 +636,10 @@ def measure_workload(tis, torch, probes, w, ceil_gbs, hop_us, reps, headline=Fal
         f"{dist / 1e6:.2f} MB distinct); floor {floor:.2f} us; attend alone cold per query "
         f"{res['attend_only']['per_query_cold_us']:.2f} us, grouped "
         f"{res['attend_only'].get('grouped_cold_us', float('nan')):.2f} us")
+    tlc = dec["timeline"].get("cold", {})
+    if tlc:
+        log(f"{w.name}: cold decode timeline (median / latest wave, us): " + "; ".join(
+            f"{k} {v['median_us']:.2f}/{v['max_us']:.2f}" for k, v in tlc.items()))
     return res, (x, Q, K_, V, plan)
 
 

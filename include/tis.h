@@ -370,6 +370,42 @@ tis_status tis_probe_read(const void *buf, size_t bytes, int nontemporal, uint32
 tis_status tis_probe_chase(const uint32_t *next, size_t n_elems, uint32_t start, int hops,
                            uint32_t *out, void *stream);
 
+/* Bytes of the timeline tis_probe_decode_timeline writes for this shape
+ * (one 24-slot record per wave of every workgroup; 0 for invalid sizes). */
+size_t tis_probe_decode_timeline_bytes(int batch, int q_heads, int beam, int leaf_block);
+
+/* tis_tree_decode (same arguments, same results in O, indices not written)
+ * run by an instrumented copy of its kernel that also records where each
+ * workgroup's time goes: the descent level by level and the gather that
+ * follows it ("Subquadratic Attention with a Hierarchical Tree-Structured
+ * Indexer", Abstract: a query's cost is its descent plus the attention at
+ * the end).  A measurement, not a path of its own.
+ *
+ * timeline: device uint64, 8-byte aligned, at least
+ * tis_probe_decode_timeline_bytes() bytes, laid out
+ * [workgroup][16 waves][24 slots]; workgroup g = part * (batch * q_heads) +
+ * slot of a query (a query with several parts has several workgroups).
+ * Slot k of a wave receives the GPU's constant-rate wall clock (ticks of
+ * hipDeviceAttributeWallClockRate kHz) when the wave's first lane passed
+ * phase k: 0 entry; 1 descent done; 2 its first K load about to issue; 3 that
+ * unit's keys loaded and scored; 4 its values used; 5 all its units done;
+ * 6 the workgroup's partial states merged (barrier passed); 7 end; 8 + 2j
+ * its rows of scored level j done, 9 + 2j level j ranked (j < 8, counted
+ * from the first level that cuts).  Slots a wave does not pass keep their
+ * old contents, so clear the buffer first.  Float32 or bfloat16 summaries
+ * (TIS_E_UNSUPPORTED for fp8); TIS_E_NULL without a timeline, TIS_E_ALIGN,
+ * TIS_E_WORKSPACE when it is too small; every tis_tree_decode check
+ * applies. */
+tis_status tis_probe_decode_timeline(const void *Q, const void *K, const void *V,
+                                     tis_dtype dtype, int q_heads, const tis_tree *tree, int beam,
+                                     float scale, float *O, void *workspace,
+                                     size_t workspace_bytes, uint64_t *timeline,
+                                     size_t timeline_bytes, void *stream);
+
+/* The GPU's wall-clock rate in kHz (the clock of the decode timeline), or 0
+ * if the device cannot be queried. */
+int tis_wall_clock_khz(int device);
+
 /* Message for the last non-OK status returned on the calling thread. */
 const char *tis_last_error(void);
 

@@ -6,6 +6,8 @@ them."""
 from __future__ import annotations
 
 import json
+
+import numpy as np
 import sqlite3
 
 import pytest
@@ -190,3 +192,24 @@ def test_counters_summary_means_per_kernel(tmp_path):
     g = [ln for ln in lines if "k_attend_group" in ln][0]
     assert "| 65536 x 512 | 2 | 2 | 1500 |" in g      # means over the two dispatches
     assert "| MfmaUtil | SQ_INSTS_VALU |" in text and text.startswith("# T")
+
+
+def test_timeline_phases_from_stamps():
+    """The decode timeline summary: times from the launch's first entry, the
+    level phases over the 8 walking waves only, unpassed phases left out."""
+    st = np.zeros((2, 16, 24), dtype=np.int64)
+    st[:, :, 0] = 1000
+    st[0, 0, 0] = 900                      # the launch's first entry
+    st[:, :8, 8] = 1100                    # level 1 scored by the walking waves
+    st[:, 8:, 8] = 5000                    # the other waves' stamps are not counted
+    st[:, :8, 9] = 1200
+    st[:, :, 1] = 1300
+    st[:, :, 7] = 2000
+    st[1, 3, 7] = 2500
+    ph = bench.timeline_phases(st, 100_000, 1)  # 100 MHz: 100 ticks a microsecond
+    assert ph["entry"]["median_us"] == pytest.approx(1.0)
+    assert ph["level 1 scored"] == {"median_us": pytest.approx(2.0), "max_us": pytest.approx(2.0)}
+    assert ph["level 1 ranked"]["max_us"] == pytest.approx(3.0)
+    assert ph["descent done"]["median_us"] == pytest.approx(4.0)
+    assert ph["end"]["max_us"] == pytest.approx(16.0)
+    assert "K arrived" not in ph and "level 2 scored" not in ph

@@ -281,6 +281,38 @@ def test_decode_rejects(lib, kw, status):
     assert lib.tis_last_error().decode()
 
 
+def _decode_timeline(lib, Q=FAKE, K=FAKE, V=FAKE, dt=_lib.TIS_BF16, Hq=2, tree=None, beam=2,
+                     scale=0.0, O=FAKE, ws=None, wsb=0, tl=FAKE, tlb=1 << 20):
+    t = tree if tree is not None else _tree(H=1)
+    return lib.tis_probe_decode_timeline(Q, K, V, dt, Hq, ctypes.byref(t), beam, scale, O, ws,
+                                         wsb, tl, tlb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(tl=None), _lib.TIS_E_NULL),
+    (dict(K=None), _lib.TIS_E_NULL),
+    (dict(beam=0), _lib.TIS_E_SHAPE),
+    (dict(tl=FAKE + 4), _lib.TIS_E_ALIGN),
+    (dict(tlb=2 * 16 * 24 * 8 - 8), _lib.TIS_E_WORKSPACE),
+    (dict(tree=_tree(H=1, sd=_lib.TIS_FP8_E4M3)), _lib.TIS_E_UNSUPPORTED),
+    # a split decode still needs its workspace
+    (dict(tree=_tree(b=4, lv=4, L=64, d=128), beam=64, Hq=2), _lib.TIS_E_NULL),
+])
+def test_decode_timeline_rejects(lib, kw, status):
+    assert _decode_timeline(lib, **kw) == status
+    assert lib.tis_last_error().decode()
+
+
+def test_decode_timeline_bytes(lib):
+    # one record of 24 eight-byte slots per wave, 16 waves per workgroup
+    assert lib.tis_probe_decode_timeline_bytes(1, 2, 2, 16) == 2 * 16 * 24 * 8
+    # 2 queries with beam 64 over 64-key leaves split into 64 parts each
+    assert lib.tis_probe_decode_timeline_bytes(1, 2, 64, 64) == 2 * 64 * 16 * 24 * 8
+    assert lib.tis_probe_decode_timeline_bytes(4, 32, 8, 64) == 128 * 16 * 24 * 8
+    assert lib.tis_probe_decode_timeline_bytes(0, 2, 2, 16) == 0
+    assert lib.tis_probe_decode_timeline_bytes(1, 2, 0, 16) == 0
+
+
 def _decode_noalloc(lib, Q=FAKE, K=FAKE, V=FAKE, dt=_lib.TIS_BF16, Hq=2, tree=None, beam=2,
                     scale=0.0, O=FAKE, idx=None):
     t = tree if tree is not None else _tree(H=1)

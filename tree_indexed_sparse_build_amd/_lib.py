@@ -100,6 +100,11 @@ SIGNATURES = {
                                     _c_int, _c_float, _vp, _vp, _vp, _c_size, _vp]),
     "tis_probe_read": (_c_int, [_vp, _c_size, _c_int, _vp, _vp]),
     "tis_probe_chase": (_c_int, [_vp, _c_size, ctypes.c_uint32, _c_int, _vp, _vp]),
+    "tis_probe_decode_timeline_bytes": (_c_size, [_c_int] * 4),
+    "tis_probe_decode_timeline": (_c_int, [_vp, _vp, _vp, _c_int, _c_int,
+                                           ctypes.POINTER(TisTree), _c_int, _c_float, _vp, _vp,
+                                           _c_size, _vp, _c_size, _vp]),
+    "tis_wall_clock_khz": (_c_int, [_c_int]),
     "tis_last_error": (ctypes.c_char_p, []),
     "tis_version": (ctypes.c_char_p, []),
 }

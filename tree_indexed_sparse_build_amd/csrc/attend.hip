@@ -20,6 +20,7 @@ __global__ void __launch_bounds__(kAttendMaxWaves * 64) k_attend(AttendArgs a) {
   __shared__ int s_idx[kMaxCandidates];
   __shared__ int s_use[kMaxCandidates];
   __shared__ int s_bad;
+  prefetch_kernargs<sizeof(AttendArgs)>();
   const int tid = threadIdx.x;
   // part sp of query qi; the parts of a query are queries apart in the grid,
   // so with a multiple of 8 queries they land on one XCD and share its L2

@@ -75,7 +75,7 @@ template <typename T, int D, bool RAGGED = false, bool THRESH = false, bool PREF
 __device__ void attend_query(const AttendArgs &a, AttendShared<T, D, MW> &sh, int qi,
                              uint4 qraw, const int *slots, const int *use, int nslots,
                              bool bad, float *part, double tau = 0.0, int hrow = 0,
-                             int64_t nk = 0) {
+                             int64_t nk = 0, unsigned long long *tl = nullptr) {
   using AG = AttendGeom<T, D>;
   constexpr int E = AG::E, LPR = AG::LPR, R = AG::R, U = AG::U, RB = AG::RB, REP = AG::REP;
   const int tid = threadIdx.x;
@@ -113,6 +113,7 @@ __device__ void attend_query(const AttendArgs &a, AttendShared<T, D, MW> &sh, in
     const int len = RAGGED ? static_cast<int>(min(static_cast<int64_t>(L), n_keys - blk0)) : L;
     if (RAGGED && r0 >= len) continue;
     uint4 kv[U], vv[U];
+    if (u == w) tl_stamp(tl, 2);
 #pragma unroll
     for (int i = 0; i < U; ++i) {
       const int row = r0 + i * R + rsub;
@@ -159,6 +160,10 @@ __device__ void attend_query(const AttendArgs &a, AttendShared<T, D, MW> &sh, in
       }
       sc = group_transpose_reduce<U, LPR>(part, lane);
     }
+    if (u == w) {
+      tl_after(tl, sc);
+      tl_stamp(tl, 3);
+    }
     // lane holds the score of row r0 + kk * R + rsub
     const int kk = (lane % LPR) / REP;
     const bool valid = r0 + kk * R + rsub < len && pass;
@@ -188,7 +193,13 @@ __device__ void attend_query(const AttendArgs &a, AttendShared<T, D, MW> &sh, in
 #pragma unroll
       for (int e = 0; e < E; ++e) acc[e] = fmaf(pr[i], v[e], acc[e]);
     }
+    if (u == w) {
+      tl_after(tl, acc[0]);
+      tl_stamp(tl, 4);
+    }
   }
+  tl_after(tl, acc[0]);
+  tl_stamp(tl, 5);
   // rows were spread over the R lane groups of the wave
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = group_sum<LPR, 32>(acc[e], lane);
@@ -201,6 +212,7 @@ __device__ void attend_query(const AttendArgs &a, AttendShared<T, D, MW> &sh, in
     sh.l[w] = l;
   }
   __syncthreads();
+  tl_stamp(tl, 6);
 
   // ---- log-sum-exp merge of the waves' partials, one column per thread.
   // Every read has a compile-time offset and all are issued before the

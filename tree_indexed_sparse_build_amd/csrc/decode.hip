@@ -38,7 +38,8 @@ constexpr int kDecodeWalkWaves = 8;  // waves that walk the tree (see route_walk
 template <typename T, int D, bool CACHE>
 __device__ inline void decode_attend(const RouteArgs &ra, const AttendArgs &aa,
                                      RouteShared<kDecodeWaves> &rsh, AttendShared<T, D> &ash,
-                                     int qi, int sp, uint4 qraw, int kept) {
+                                     int qi, int sp, uint4 qraw, int kept,
+                                     unsigned long long *tl = nullptr) {
   if (ra.indices && sp == 0) {
     int32_t *out = ra.indices + static_cast<int64_t>(qi) * ra.beam;
     write_ascending<kDecodeWaves * 64>(rsh.front, kept, out);
@@ -50,7 +51,8 @@ __device__ inline void decode_attend(const RouteArgs &ra, const AttendArgs &aa,
   float *part = aa.splits > 1
                     ? aa.part + (static_cast<int64_t>(qi) * aa.splits + sp) * (D + kPartHeader)
                     : nullptr;
-  attend_query<T, D, CACHE>(aa, ash, qi, qraw, rsh.front + s0, nullptr, s1 - s0, false, part);
+  attend_query<T, D, CACHE>(aa, ash, qi, qraw, rsh.front + s0, nullptr, s1 - s0, false, part,
+                            0.0, 0, 0, tl);
   if (aa.splits > 1) merge_parts<D>(aa, qi);
 }
 
@@ -58,6 +60,7 @@ template <typename T, typename S, int D, bool CACHE>
 __global__ void __launch_bounds__(kDecodeWaves * 64) k_decode(RouteArgs ra, AttendArgs aa) {
   __shared__ RouteShared<kDecodeWaves> rsh;
   __shared__ AttendShared<T, D> ash;
+  prefetch_kernargs<sizeof(RouteArgs) + sizeof(AttendArgs)>();
   // part sp of query qi (see k_attend: a query's parts share an XCD)
   const int sp = div_u(static_cast<int>(blockIdx.x), aa.queries);
   const int qi = query_of_slot(blockIdx.x - sp * aa.queries, aa.queries, aa.group);
@@ -65,6 +68,27 @@ __global__ void __launch_bounds__(kDecodeWaves * 64) k_decode(RouteArgs ra, Atte
   // every part walks the tree (the repeated summary reads hit the XCD's L2)
   const int kept = route_walk<T, S, D, kDecodeWaves, kDecodeWalkWaves, CACHE>(ra, rsh, qi);
   decode_attend<T, D, CACHE>(ra, aa, rsh, ash, qi, sp, qraw, kept);
+}
+
+// k_decode with a phase timeline (see tl_stamp): the same walk and gather,
+// the same results, plus a wall-clock stamp per wave at each phase.  A
+// measurement of where a decode's time goes, not a path of its own.
+template <typename T, typename S, int D>
+__global__ void __launch_bounds__(kDecodeWaves * 64)
+    k_decode_timeline(RouteArgs ra, AttendArgs aa, unsigned long long *tl) {
+  __shared__ RouteShared<kDecodeWaves> rsh;
+  __shared__ AttendShared<T, D> ash;
+  tl_stamp(tl, 0);
+  prefetch_kernargs<sizeof(RouteArgs) + sizeof(AttendArgs)>();
+  const int sp = div_u(static_cast<int>(blockIdx.x), aa.queries);
+  const int qi = query_of_slot(blockIdx.x - sp * aa.queries, aa.queries, aa.group);
+  const uint4 qraw = attend_q_raw<T, D>(aa, qi);
+  const int kept = route_walk<T, S, D, kDecodeWaves, kDecodeWalkWaves, 0>(
+      ra, rsh, qi, nullptr, nullptr, -1, static_cast<const NoPrep *>(nullptr), nullptr, tl);
+  tl_stamp(tl, 1);
+  decode_attend<T, D, false>(ra, aa, rsh, ash, qi, sp, qraw, kept, tl);
+  __syncthreads();
+  tl_stamp(tl, 7);
 }
 
 template <typename T> __device__ inline float widen1(const T *p);
@@ -173,6 +197,7 @@ __global__ void __launch_bounds__(kDecodeWaves * 64)
   __shared__ RouteShared<kDecodeWaves> rsh;
   __shared__ AttendShared<T, D> ash;
   __shared__ double open_score[kMaxLevels + 1];
+  prefetch_kernargs<sizeof(RouteArgs) + sizeof(AttendArgs) + sizeof(AppendArgs)>();
   const int nq = aa.queries * aa.splits;
   if (static_cast<int>(blockIdx.x) >= nq) {
     append_one<T, S, D>(ap, static_cast<int64_t>(blockIdx.x) - nq);
@@ -223,7 +248,31 @@ hipError_t launch_decode_append_ts(int head_dim, const RouteArgs &ra, const Atte
   return hipGetLastError();
 }
 
+template <typename T, typename S>
+hipError_t launch_decode_timeline_ts(int head_dim, const RouteArgs &ra, const AttendArgs &aa,
+                                     unsigned long long *tl, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(ra.queries) * static_cast<unsigned>(aa.splits));
+  const dim3 block(kDecodeWaves * 64);
+  if (head_dim == 128)
+    hipLaunchKernelGGL((k_decode_timeline<T, S, 128>), grid, block, 0, s, ra, aa, tl);
+  else if (head_dim == 64)
+    hipLaunchKernelGGL((k_decode_timeline<T, S, 64>), grid, block, 0, s, ra, aa, tl);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_decode_timeline(Dt dt, Dt sdt, int head_dim, const RouteArgs &ra,
+                                  const AttendArgs &aa, unsigned long long *tl, hipStream_t s) {
+  if (sdt == Dt::FP8 || ra.cache) return hipErrorInvalidValue;  // float32 / bfloat16, full tree
+  if (dt == Dt::BF16)
+    return sdt == Dt::BF16 ? launch_decode_timeline_ts<bf16_bits, bf16_bits>(head_dim, ra, aa, tl, s)
+                           : launch_decode_timeline_ts<bf16_bits, float>(head_dim, ra, aa, tl, s);
+  return sdt == Dt::BF16 ? launch_decode_timeline_ts<float, bf16_bits>(head_dim, ra, aa, tl, s)
+                         : launch_decode_timeline_ts<float, float>(head_dim, ra, aa, tl, s);
+}
 
 hipError_t launch_decode_append(Dt dt, Dt sdt, int head_dim, const RouteArgs &ra,
                                 const AttendArgs &aa, const AppendArgs &ap, hipStream_t s) {

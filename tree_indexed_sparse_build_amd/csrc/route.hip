@@ -14,6 +14,7 @@ constexpr int kRouteWaves = 8;
 template <typename T, typename S, int D, bool CACHE>
 __global__ void __launch_bounds__(kRouteWaves * 64) k_route(RouteArgs a) {
   __shared__ RouteShared<kRouteWaves> sh;
+  prefetch_kernargs<sizeof(RouteArgs)>();
   const int qi = query_of_slot(blockIdx.x, a.queries, a.group);
   const int kept = route_walk<T, S, D, kRouteWaves, kRouteWaves, CACHE>(a, sh, qi);
   int32_t *out = a.indices + static_cast<int64_t>(qi) * a.beam;

@@ -278,7 +278,8 @@ template <typename T, typename S, int D, int NW, int NRW, int LAYOUT,
 __device__ int route_walk(const RouteArgs &a, RouteShared<NW, SMAXC> &sh, int qi,
                           const CausalLevels *cl = nullptr, const void *open_summ = nullptr,
                           int hrow = -1, const Prep *prep = nullptr,
-                          const double *open_score = nullptr) {
+                          const double *open_score = nullptr,
+                          unsigned long long *tl = nullptr) {
   constexpr bool CACHE = LAYOUT != 0;  // nodes past the last key may be missing
   constexpr bool OPEN = !__is_same(Prep, NoPrep);
   static_assert(!kIsFp8<S> || LAYOUT == 0, "fp8 summaries: full tree only");
@@ -399,6 +400,7 @@ __device__ int route_walk(const RouteArgs &a, RouteShared<NW, SMAXC> &sh, int qi
         else
           score_rows<T, S, D, 8, CACHE>(row_of, C, node_of, emit, qr, NRW, w, lane, scale_of);
       }
+      if (l - l0 < 8) tl_stamp(tl, 8 + 2 * (l - l0));
       __syncthreads();
       // rank of candidate i = number of candidates with a larger key.  Each
       // candidate has a group of g adjacent lanes (g <= 8); lane p of the
@@ -472,6 +474,7 @@ __device__ int route_walk(const RouteArgs &a, RouteShared<NW, SMAXC> &sh, int qi
       }
     }
     __syncthreads();
+    if (live > W && l - l0 < 8) tl_stamp(tl, 9 + 2 * (l - l0));
     cur ^= 1;
     nf = keep;
     if (l < lv) lc.down(D);

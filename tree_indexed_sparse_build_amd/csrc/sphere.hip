@@ -521,6 +521,7 @@ __global__ void __launch_bounds__(kThreshDecodeWaves * 64)
     k_decode_threshold(RouteArgs ra, SphereArgs sa, AttendArgs aa) {
   __shared__ ThreshShared<kThreshDecodeWaves> sh;
   __shared__ AttendShared<T, D> ash;
+  prefetch_kernargs<sizeof(RouteArgs) + sizeof(SphereArgs) + sizeof(AttendArgs)>();
   const int sp = div_u(static_cast<int>(blockIdx.x), aa.queries);
   const int qi = query_of_slot(blockIdx.x - sp * aa.queries, aa.queries, aa.group);
   const uint4 qraw = attend_q_raw<T, D>(aa, qi);

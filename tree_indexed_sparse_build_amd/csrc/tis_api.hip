@@ -503,7 +503,9 @@ tis_status scratch_address(const char *who, void **out) {
 tis_status decode_full_tree(const char *who, const void *Q, const void *K, const void *V,
                             tis_dtype dtype, int q_heads, const tis_tree *tree, int beam,
                             float scale, float *O, int32_t *indices, void *workspace,
-                            size_t workspace_bytes, bool noalloc, void *stream) {
+                            size_t workspace_bytes, bool noalloc, void *stream,
+                            unsigned long long *timeline = nullptr,
+                            size_t timeline_bytes = 0) {
   if (!Q || !K || !V || !tree || !tree->summaries || !O)
     return fail(TIS_E_NULL, "%s: Q, K, V, tree, tree->summaries and O are required", who);
   tis_status st = check_dtype(dtype);
@@ -570,6 +572,21 @@ tis_status decode_full_tree(const char *who, const void *Q, const void *K, const
                   workspace_bytes, &aa);
   if (st != TIS_OK) return st;
   const tis::Dt dt = dtype == TIS_BF16 ? tis::Dt::BF16 : tis::Dt::F32;
+  if (timeline) {
+    if (tree->summary_dtype == TIS_FP8_E4M3)
+      return fail(TIS_E_UNSUPPORTED, "%s: float32 or bfloat16 summaries only", who);
+    const size_t need = static_cast<size_t>(queries) * aa.splits * tis::kTimelineWaves *
+                        tis::kTimelineSlots * sizeof(unsigned long long);
+    if (!aligned(timeline, 8))
+      return fail(TIS_E_ALIGN, "%s: timeline needs 8-byte alignment", who);
+    if (timeline_bytes < need)
+      return fail(TIS_E_WORKSPACE, "%s: timeline %zu bytes < %zu required", who, timeline_bytes,
+                  need);
+    return hip_status(tis::launch_decode_timeline(dt, to_dt(tree->summary_dtype), tree->head_dim,
+                                                  ra, aa, timeline,
+                                                  static_cast<hipStream_t>(stream)),
+                      who);
+  }
   return hip_status(tis::launch_decode(dt, to_dt(tree->summary_dtype), tree->head_dim, ra, aa,
                                       static_cast<hipStream_t>(stream)),
                     who);
@@ -585,6 +602,31 @@ tis_status tis_tree_decode(const void *Q, const void *K, const void *V, tis_dtyp
                            void *stream) {
   return decode_full_tree("tis_tree_decode", Q, K, V, dtype, q_heads, tree, beam, scale, O,
                           indices, workspace, workspace_bytes, false, stream);
+}
+
+size_t tis_probe_decode_timeline_bytes(int batch, int q_heads, int beam, int leaf_block) {
+  if (batch < 1 || q_heads < 1 || beam < 1 || leaf_block < 1) return 0;
+  const int64_t queries = static_cast<int64_t>(batch) * q_heads;
+  return static_cast<size_t>(queries) * tis::attend_splits(queries, beam, leaf_block) *
+         tis::kTimelineWaves * tis::kTimelineSlots * sizeof(unsigned long long);
+}
+
+tis_status tis_probe_decode_timeline(const void *Q, const void *K, const void *V,
+                                     tis_dtype dtype, int q_heads, const tis_tree *tree, int beam,
+                                     float scale, float *O, void *workspace,
+                                     size_t workspace_bytes, uint64_t *timeline,
+                                     size_t timeline_bytes, void *stream) {
+  if (!timeline)
+    return fail(TIS_E_NULL, "tis_probe_decode_timeline: timeline is required");
+  return decode_full_tree("tis_probe_decode_timeline", Q, K, V, dtype, q_heads, tree, beam, scale,
+                          O, nullptr, workspace, workspace_bytes, false, stream,
+                          reinterpret_cast<unsigned long long *>(timeline), timeline_bytes);
+}
+
+int tis_wall_clock_khz(int device) {
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeWallClockRate, device) != hipSuccess) return 0;
+  return v;
 }
 
 tis_status tis_tree_decode_noalloc(const void *Q, const void *K, const void *V, tis_dtype dtype,

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "tis_internal.hpp"
+
 namespace tis {
 
 // Storage element of a bf16 tensor: its 16-bit pattern.
@@ -355,6 +357,47 @@ __device__ inline void store_row_fp8(fp8_bits *row, float *scale, const double (
 #pragma unroll
   for (int j = 0; j < C; ++j) row[cols[j]].v = static_cast<uint8_t>(e4m3_from_double(m[j] * inv));
   if (lane == 0) *scale = static_cast<float>(pow2_double(e));
+}
+
+// ---- kernel arguments ----------------------------------------------------
+// Brings the first BYTES of the launch's argument block into the scalar
+// cache with one scalar load per 64-byte line, all issued before any is
+// waited for.  The scalar cache starts a launch empty, and the compiler
+// fetches arguments where the code first needs them: in the decode kernels
+// that was three dependent rounds before the first summary row could be
+// requested, each a memory round trip.  Called first thing in a kernel, it
+// makes that one round; the compiler's own argument loads then hit.
+template <size_t BYTES> __device__ inline void prefetch_kernargs() {
+  typedef const __attribute__((address_space(4))) uint32_t kword;
+  constexpr int N = static_cast<int>((BYTES + 63) / 64);
+  kword *p = (kword *)__builtin_amdgcn_kernarg_segment_ptr();
+  uint32_t v[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = p[i * 16];
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" ::"s"(v[i]));
+}
+
+// ---- phase timeline of the fused decode (measurement only) --------------
+// Slot k of wave w of workgroup g is tl[(g * kTimelineWaves + w) *
+// kTimelineSlots + k]: the value of the GPU's constant-rate wall clock
+// (s_memrealtime) when lane 0 of the wave passed phase k.  Phases: 0 entry;
+// 1 walk done; 2 first K load about to issue; 3 first unit's K arrived and
+// scored; 4 first unit's V used; 5 the wave's units done; 6 waves' partials
+// merged in LDS (barrier passed); 7 end; 8 + 2j scored level j of the walk
+// (this wave's rows, before the barrier), 9 + 2j level j ranked (after the
+// barrier), j < 8.  Unrecorded slots keep what the caller put there.  With
+// tl == nullptr (a constant in every kernel but the timeline one) nothing is
+// recorded and the call compiles away.
+__device__ inline void tl_stamp(unsigned long long *tl, int slot) {
+  if (tl && (threadIdx.x & 63) == 0)
+    tl[(static_cast<size_t>(blockIdx.x) * kTimelineWaves + (threadIdx.x >> 6)) * kTimelineSlots +
+       slot] = __builtin_amdgcn_s_memrealtime();
+}
+// Holds back a stamp until v has been computed (so the stamp after a load's
+// first use waits for the load).
+template <typename V> __device__ inline void tl_after(unsigned long long *tl, const V &v) {
+  if (tl) asm volatile("" ::"v"(v));
 }
 
 // ---- data handed between workgroups of one launch ----------------------

@@ -11,6 +11,10 @@ namespace tis {
 constexpr int kMaxLevels = 16;
 constexpr int kMaxCandidates = 256;   // beam * branching scored per level
 constexpr int kMaxBranching = 64;
+// Phase timeline of the fused decode: slots per wave, waves per workgroup
+// (see tl_stamp).
+constexpr int kTimelineSlots = 24;
+constexpr int kTimelineWaves = 16;
 
 enum class Dt : int { F32 = 0, BF16 = 1, FP8 = 2 };  // FP8: summaries only
 
@@ -150,6 +154,10 @@ hipError_t launch_attend_group(Dt dt, int head_dim, const AttendArgs &a, hipStre
 // Route and attend of each query in one workgroup (one launch).
 hipError_t launch_decode(Dt dt, Dt sdt, int head_dim, const RouteArgs &ra,
                          const AttendArgs &aa, hipStream_t s);
+// The same decode with a per-wave phase timeline in tl (float32 or bfloat16
+// summaries over a full tree; see tl_stamp for the layout).
+hipError_t launch_decode_timeline(Dt dt, Dt sdt, int head_dim, const RouteArgs &ra,
+                                  const AttendArgs &aa, unsigned long long *tl, hipStream_t s);
 
 // ------------------------------------------------------- growing cache --
 // Append keys [n0, n1) of a cache of `capacity` keys per head to its tree:

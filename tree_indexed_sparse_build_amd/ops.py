@@ -488,6 +488,25 @@ class DecodePlan:
                                         None if ws is None else ws.data_ptr(),
                                         0 if ws is None else ws.numel(), _stream(self.device)))
 
+    def timeline_bytes(self) -> int:
+        """Bytes of the buffer decode_timeline() fills."""
+        B, H, N, d, b, Lb, lv = self.geom
+        return int(self._lib.tis_probe_decode_timeline_bytes(B, self.q_heads, self.beam, Lb))
+
+    def decode_timeline(self, timeline: torch.Tensor) -> None:
+        """decode() by the instrumented kernel (tis_probe_decode_timeline):
+        the same output in self.out, plus a wall-clock stamp per wave and
+        phase in `timeline` (int64, timeline_bytes() bytes, cleared by the
+        caller)."""
+        B, H, N, d, b, Lb, lv = self.geom
+        ws = self.ws_decode
+        check(self._lib.tis_probe_decode_timeline(
+            self.Q.data_ptr(), self.K.data_ptr(), self.V.data_ptr(), self.dt, self.q_heads,
+            ctypes.byref(self.tree_c), self.beam, self.scale, self.out.data_ptr(),
+            None if ws is None else ws.data_ptr(), 0 if ws is None else ws.numel(),
+            timeline.data_ptr(), timeline.numel() * timeline.element_size(),
+            _stream(self.device)))
+
     def tree(self) -> Tree:
         B, H, N, d, b, Lb, lv = self.geom
         return Tree(self.summaries, B, H, N, d, b, Lb, lv)
