@@ -445,18 +445,22 @@ def graph_diff(torch, prep, fn, per_graph=10, replays=5):
     ga, gb = capture(both), capture(prep)
     e0, e1 = _events(torch, 2)
 
-    def timed(g):
+    def once(g):
+        e0.record()
         g.replay()
+        e1.record()
         torch.cuda.synchronize()
-        ts = []
-        for _ in range(replays):
-            e0.record()
-            g.replay()
-            e1.record()
-            torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1) * 1e3)
-        return float(np.median(ts))
-    t = (timed(ga) - timed(gb)) / per_graph
+        return e0.elapsed_time(e1) * 1e3
+    ga.replay()
+    gb.replay()
+    torch.cuda.synchronize()
+    # the two graphs alternate, so a drift of the clock or of the memory
+    # system's state over the measurement falls on both alike
+    ta, tb = [], []
+    for _ in range(replays):
+        ta.append(once(ga))
+        tb.append(once(gb))
+    t = (float(np.median(ta)) - float(np.median(tb))) / per_graph
     del ga, gb
     return t
 
@@ -469,8 +473,10 @@ def decode_regimes(torch, probes, plan):
     def steady_prep():
         probes.flush()
         probes.read(plan.summaries)
-    return {"cold_us": graph_diff(torch, probes.flush, plan.decode),
-            "steady_us": graph_diff(torch, steady_prep, plan.decode),
+    # the decode is short beside the flush (about 190 us), so its cold
+    # figures take more launches a graph and more replays than the rest
+    return {"cold_us": graph_diff(torch, probes.flush, plan.decode, per_graph=20, replays=9),
+            "steady_us": graph_diff(torch, steady_prep, plan.decode, per_graph=20, replays=9),
             "warm_us": graph_time(torch, plan.decode)}
 
 
@@ -483,13 +489,15 @@ def attend_comparison(torch, probes, plan):
     plan.attend()
     torch.cuda.synchronize()
     ref = plan.out.clone()
-    res = {"per_query_cold_us": graph_diff(torch, probes.flush, plan.attend, replays=3),
+    res = {"per_query_cold_us": graph_diff(torch, probes.flush, plan.attend, per_graph=20,
+                                           replays=9),
            "per_query_warm_us": graph_time(torch, plan.attend, replays=3)}
     if plan.ws_grouped is not None:
         plan.attend_grouped()
         torch.cuda.synchronize()
         res["grouped_max_abs_diff"] = float((plan.out - ref).abs().max().item())
-        res["grouped_cold_us"] = graph_diff(torch, probes.flush, plan.attend_grouped, replays=3)
+        res["grouped_cold_us"] = graph_diff(torch, probes.flush, plan.attend_grouped,
+                                            per_graph=20, replays=9)
         res["grouped_warm_us"] = graph_time(torch, plan.attend_grouped, replays=3)
     return res
 
@@ -587,7 +595,7 @@ def measure_workload(tis, torch, probes, w, ceil_gbs, hop_us, reps, headline=Fal
         step_us = graph_diff(torch, probes.flush, step_fn, per_graph=K, replays=3)
         h1 = time.perf_counter()
         step = {"steps": K, "step_us_mean": step_us, "region_wall_s": h1 - h0}
-    bc = graph_diff(torch, probes.flush, plan.build, per_graph=max(5, min(K, 20)), replays=3)
+    bc = graph_diff(torch, probes.flush, plan.build, per_graph=max(5, min(K, 20)), replays=7)
     if not headline:
         # the build then one decode, back to back (the decode finds the tree
         # the build just wrote): the literal sequence of the 1M-key workload
@@ -603,7 +611,7 @@ def measure_workload(tis, torch, probes, w, ceil_gbs, hop_us, reps, headline=Fal
     # the same bytes as the build's K, streamed by the read probe (cold): the
     # read ceiling at this size, ramp and tail included
     kread = graph_diff(torch, probes.flush, lambda: probes.read(K_, nontemporal=True),
-                       per_graph=max(5, min(K, 20)), replays=3)
+                       per_graph=max(5, min(K, 20)), replays=7)
     kbytes = K_.numel() * K_.element_size()
     res["build"]["k_read_cold_us"] = kread
     res["build"]["k_read_cold_gbs"] = kbytes / (kread * 1e3)
