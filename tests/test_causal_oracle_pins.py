@@ -117,3 +117,19 @@ def test_bf16_summaries_follow_the_same_definition():
     Q, K, V = _rand(1, 2, 1, 40, 8, seed=9)
     a = C.causal_prefill(Q, K, V, "f32", 2, 4, beam=40 // 4, summary_dtype="bf16")
     np.testing.assert_allclose(a["out"], _dense_causal(Q, K, V), rtol=1e-12, atol=1e-12)
+
+
+def test_gap_is_the_smallest_level_gap():
+    """A hand-worked prefix: d = 1, q = 1, b = 2, L = 1, beam 1, keys
+    4, 0, 1, 1.  At position 3 (all 4 keys, two levels) level 1 compares the
+    means 2 and 1 (relative gap (2 - 1) / 2 = 1/2) and keeps node 0; level 2
+    compares its leaves 4 and 0 (gap (4 - 0) / 4 = 1).  At position 2 the
+    second node holds key 2 alone (mean 1): the gaps are 1/2 and 1 again.
+    At position 1 (keys 4, 0, one level) the only gap is 1, and at position 0
+    nothing is cut (+inf).  The reported gap is the smallest level's."""
+    K = np.array([4, 0, 1, 1], dtype=np.float32).reshape(1, 1, 4, 1)
+    V = np.arange(4, dtype=np.float32).reshape(1, 1, 4, 1)
+    Q = np.ones((1, 1, 4, 1), dtype=np.float32)
+    r = C.causal_prefill(Q, K, V, "f32", 2, 1, 1)
+    assert r["gap"][0, 0].tolist() == [np.inf, 1.0, 0.5, 0.5]
+    assert r["indices"][0, 0, :, 0].tolist() == [0, 0, 0, 0]

@@ -1,11 +1,14 @@
 """The oracle's pins catch plausible mistakes planted in the oracle (CPU).
 
-Each mutant of tests/oracle_mutants.py edits one place of
-oracle/tis_oracle.py (a tie order, a sign, a child or row index, a GQA map,
-a scale, the tie measure's pair or denominator, an accumulation or rounding
-mode, the bf16 widening) and runs the pins that do not compare with stored
-oracle outputs.  The unmutated oracle must pass them and every mutant must
-fail at least one.
+Each mutant of tests/oracle_mutants.py edits one place of one oracle module
+(the full tree: a tie order, a sign, a child or row index, a GQA map, a
+scale, the tie measure's pair or denominator, an accumulation or rounding
+mode, the bf16 widening; the growing cache: depth, open-node means, existing
+nodes, blocks cut at n; the spheres: max radius, the bound's |q| and r,
+strict comparisons, overflow; the causal prefill: the prefix length, the
+query's position, keys read, the tie measure) and runs that module's pins
+that do not compare with stored oracle outputs.  The unmutated oracles must
+pass them and every mutant must fail at least one.
 """
 from __future__ import annotations
 
@@ -31,14 +34,15 @@ def _run(name: str) -> str:
     return f"NO RESULT (rc {r.returncode}): {(r.stdout + r.stderr)[-400:]}"
 
 
-def test_unmutated_oracle_passes_the_pins():
-    assert _run("none") == "PASSED"
+@pytest.mark.parametrize("module", sorted(oracle_mutants.PIN_FILES))
+def test_unmutated_oracle_passes_the_pins(module):
+    assert _run(f"none:{module}") == "PASSED"
 
 
 @pytest.mark.timeout(900)
 def test_every_mutant_fails_a_pin():
     names = sorted(oracle_mutants.MUTANTS)
-    assert len(names) >= 20
+    assert len(names) >= 40
     with ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
         results = dict(zip(names, ex.map(_run, names)))
     missed = {n: r for n, r in results.items() if r != "FAILED"}

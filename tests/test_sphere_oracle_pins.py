@@ -148,7 +148,7 @@ def test_survivors_match_a_per_leaf_formulation():
     reaches tau (written leaf by leaf here, not level by level)."""
     b, L, lv = 2, 3, 5
     K, V, Q, tree, rad = _case(b, L, lv, 6, seed=9)
-    qn = S.query_norm(Q, "f32")
+    qn = np.linalg.norm(Q.astype(np.float64), axis=-1)  # numpy's norm, not the oracle's
     for k_rank in (1, 5, 30):
         tau = _tau_between_scores(Q, K, k_rank, G=2)
         r = S.threshold_route(Q, "f32", tree["stored"], rad["stored"], b, tau, b ** lv)
@@ -216,6 +216,18 @@ def test_overflow_is_reported():
     assert np.all(r["counts"] == -1) and np.all(r["indices"] == -1)
     a = S.threshold_attend(Q, K, V, "f32", r["indices"], r["counts"], L, lo)
     assert np.all(np.isnan(a["out"]))
+
+
+def test_query_norm_closed_forms():
+    """|q| of Pythagorean rows: (3, 4) -> 5, (2, 3, 6) -> 7, (1, 4, 8) -> 9,
+    and a bf16 row (the pattern 0x4040 is 3.0, 0x4080 is 4.0) -> 5."""
+    Q = np.zeros((1, 3, 3), dtype=np.float32)
+    Q[0, 0, :2] = [3, 4]
+    Q[0, 1] = [2, 3, 6]
+    Q[0, 2] = [1, 4, 8]
+    assert S.query_norm(Q, "f32").tolist() == [[5.0, 7.0, 9.0]]
+    Qb = np.array([[[0x4040, 0x4080]]], dtype=np.uint16)
+    assert S.query_norm(Qb, "bf16").tolist() == [[5.0]]
 
 
 def test_radius_zero_leaves_prune_exactly():
