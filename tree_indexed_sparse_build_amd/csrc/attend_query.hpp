@@ -52,32 +52,28 @@ template <typename T, int D, int MW = kAttendMaxWaves> struct AttendShared {
   float acc[MW][D];
 };
 
-// The rows of K and V of the KV head that query row hr reads (row 0 of the
-// head; the lane's columns are added where they are used).
-template <typename T> struct HeadRows {
-  const T *k, *v;
-};
-template <typename T, int D>
-__device__ inline HeadRows<T> head_rows(const AttendArgs &a, int hr) {
+// Element offset, in K and in V, of row 0 of the KV head that query row hr
+// reads (the lane's columns are added where it is used).
+template <int D> __device__ inline int64_t head_offset(const AttendArgs &a, int hr) {
   const int bi = div_u(hr, a.q_heads);
   const int hq = hr - bi * a.q_heads;
   const int64_t head = static_cast<int64_t>(bi) * a.kv_heads + div_u(hq, a.group);
-  return {static_cast<const T *>(a.K) + head * a.key_stride * D,
-          static_cast<const T *>(a.V) + head * a.key_stride * D};
+  return head * a.key_stride * D;
 }
 
-// HeadRows computed where the caller stands, held there: the empty asm takes
-// the pointers as opaque values, so the compiler cannot move their scalar
-// arithmetic (and its argument loads) down to where they are used.  The
-// fused decode computes them before its walk, in the shadow of the first
-// level's loads, instead of after it, where all 16 waves of the workgroup
-// would queue on the CU's one scalar unit for them at once.
-template <typename T, int D>
-__device__ inline HeadRows<T> head_rows_early(const AttendArgs &a, int hr) {
-  HeadRows<T> r = head_rows<T, D>(a, hr);
-  uint64_t k = reinterpret_cast<uint64_t>(r.k), v = reinterpret_cast<uint64_t>(r.v);
-  asm volatile("" : "+s"(k), "+s"(v));
-  return {reinterpret_cast<const T *>(k), reinterpret_cast<const T *>(v)};
+// head_offset computed where the caller stands, held there: the empty asm
+// takes it as an opaque value, so the compiler cannot move its scalar
+// arithmetic (and its argument loads) down to where it is used.  The fused
+// decode computes it before its walk, in the shadow of the first level's
+// loads, instead of after it, where all 16 waves of the workgroup would
+// queue on the CU's one scalar unit for it at once.  Only the offset is held
+// opaque: the K and V pointers still come from the kernel's arguments, so
+// the compiler keeps the gather's loads global rather than generic (flat)
+// ones, which would also count against the LDS wait counter.
+template <int D> __device__ inline int64_t head_offset_early(const AttendArgs &a, int hr) {
+  int64_t off = head_offset<D>(a, hr);
+  asm volatile("" : "+s"(off));
+  return off;
 }
 
 // This lane's part of the query row in the attend layout (E elements).
@@ -104,7 +100,7 @@ __device__ void attend_query(const AttendArgs &a, AttendShared<T, D, MW> &sh, in
                              uint4 qraw, const int *slots, const int *use, int nslots,
                              bool bad, float *part, double tau = 0.0, int hrow = 0,
                              int64_t nk = 0, unsigned long long *tl = nullptr,
-                             const HeadRows<T> *pre = nullptr) {
+                             const int64_t *pre_off = nullptr) {
   using AG = AttendGeom<T, D>;
   constexpr int E = AG::E, LPR = AG::LPR, R = AG::R, U = AG::U, RB = AG::RB, REP = AG::REP;
   const int tid = threadIdx.x;
@@ -113,15 +109,15 @@ __device__ void attend_query(const AttendArgs &a, AttendShared<T, D, MW> &sh, in
   const int nw = blockDim.x >> 6;
   const int L = a.leaf_block;
   const int hr = PREFILL ? hrow : qi;
-  const HeadRows<T> rows = pre ? *pre : head_rows<T, D>(a, hr);
+  const int64_t hoff = pre_off ? *pre_off : head_offset<D>(a, hr);
   const int col = (lane % LPR) * E;
   const int rsub = lane / LPR;
   const int64_t n_keys = PREFILL ? nk : a.n_keys;
 
   float q[E];
   Vec16<T>::unpack(qraw, q);
-  const T *kh = rows.k + col;
-  const T *vh = rows.v + col;
+  const T *kh = static_cast<const T *>(a.K) + hoff + col;
+  const T *vh = static_cast<const T *>(a.V) + hoff + col;
   const int nc = (L + RB - 1) / RB;
   const int units = nslots * nc;
 

@@ -39,7 +39,7 @@ template <typename T, int D, bool CACHE>
 __device__ inline void decode_attend(const RouteArgs &ra, const AttendArgs &aa,
                                      RouteShared<kDecodeWaves> &rsh, AttendShared<T, D> &ash,
                                      int qi, int sp, uint4 qraw, int kept,
-                                     const HeadRows<T> &rows, unsigned long long *tl = nullptr) {
+                                     int64_t hoff, unsigned long long *tl = nullptr) {
   if (ra.indices && sp == 0) {
     int32_t *out = ra.indices + static_cast<int64_t>(qi) * ra.beam;
     write_ascending<kDecodeWaves * 64>(rsh.front, kept, out);
@@ -52,7 +52,7 @@ __device__ inline void decode_attend(const RouteArgs &ra, const AttendArgs &aa,
                     ? aa.part + (static_cast<int64_t>(qi) * aa.splits + sp) * (D + kPartHeader)
                     : nullptr;
   attend_query<T, D, CACHE>(aa, ash, qi, qraw, rsh.front + s0, nullptr, s1 - s0, false, part,
-                            0.0, 0, 0, tl, &rows);
+                            0.0, 0, 0, tl, &hoff);
   if (aa.splits > 1) merge_parts<D>(aa, qi);
 }
 
@@ -65,10 +65,10 @@ __global__ void __launch_bounds__(kDecodeWaves * 64) k_decode(RouteArgs ra, Atte
   const int sp = div_u(static_cast<int>(blockIdx.x), aa.queries);
   const int qi = query_of_slot(blockIdx.x - sp * aa.queries, aa.queries, aa.group);
   const uint4 qraw = attend_q_raw<T, D>(aa, qi);  // in flight during the walk
-  const HeadRows<T> rows = head_rows_early<T, D>(aa, qi);
+  const int64_t hoff = head_offset_early<D>(aa, qi);
   // every part walks the tree (the repeated summary reads hit the XCD's L2)
   const int kept = route_walk<T, S, D, kDecodeWaves, kDecodeWalkWaves, CACHE>(ra, rsh, qi);
-  decode_attend<T, D, CACHE>(ra, aa, rsh, ash, qi, sp, qraw, kept, rows);
+  decode_attend<T, D, CACHE>(ra, aa, rsh, ash, qi, sp, qraw, kept, hoff);
 }
 
 // k_decode with a phase timeline (see tl_stamp): the same walk and gather,
@@ -84,11 +84,11 @@ __global__ void __launch_bounds__(kDecodeWaves * 64)
   const int sp = div_u(static_cast<int>(blockIdx.x), aa.queries);
   const int qi = query_of_slot(blockIdx.x - sp * aa.queries, aa.queries, aa.group);
   const uint4 qraw = attend_q_raw<T, D>(aa, qi);
-  const HeadRows<T> rows = head_rows_early<T, D>(aa, qi);
+  const int64_t hoff = head_offset_early<D>(aa, qi);
   const int kept = route_walk<T, S, D, kDecodeWaves, kDecodeWalkWaves, 0>(
       ra, rsh, qi, nullptr, nullptr, -1, static_cast<const NoPrep *>(nullptr), nullptr, tl);
   tl_stamp(tl, 1);
-  decode_attend<T, D, false>(ra, aa, rsh, ash, qi, sp, qraw, kept, rows, tl);
+  decode_attend<T, D, false>(ra, aa, rsh, ash, qi, sp, qraw, kept, hoff, tl);
   __syncthreads();
   tl_stamp(tl, 7);
 }
@@ -208,11 +208,11 @@ __global__ void __launch_bounds__(kDecodeWaves * 64)
   const int sp = div_u(static_cast<int>(blockIdx.x), aa.queries);
   const int qi = query_of_slot(blockIdx.x - sp * aa.queries, aa.queries, aa.group);
   const uint4 qraw = attend_q_raw<T, D>(aa, qi);
-  const HeadRows<T> rows = head_rows_early<T, D>(aa, qi);
+  const int64_t hoff = head_offset_early<D>(aa, qi);
   const OpenNodes<T, S, D> open(ra, ap, qi, rsh.keys, open_score);
   const int kept = route_walk<T, S, D, kDecodeWaves, kDecodeWalkWaves, 1>(
       ra, rsh, qi, nullptr, nullptr, -1, &open, open_score);
-  decode_attend<T, D, true>(ra, aa, rsh, ash, qi, sp, qraw, kept, rows);
+  decode_attend<T, D, true>(ra, aa, rsh, ash, qi, sp, qraw, kept, hoff);
 }
 
 template <typename T, typename S, bool CACHE>
